@@ -1,0 +1,218 @@
+"""NVFP4 paged-KV attention for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI in ``include/nvfp4_attn.h``.  PyTorch supplies
+device memory and the current stream; every step of the computation runs in the
+HIP library (``libnvfp4_attn.so``).  The names follow the C entry points:
+``quantize_kv``, ``Plan`` (``nvfp4_plan_*``), ``batch_decode``, ``batch_prefill``
+and ``merge_states``.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+from ._lib import (EXPORTS, STATUS, WORK_FIELDS, KVPoolStruct, NVFP4Error, PlanInfoStruct,
+                   check, lib)
+
+__all__ = ["KVPool", "Plan", "quantize_kv", "batch_decode", "batch_prefill", "merge_states",
+           "NVFP4Error", "lib", "version", "EXPORTS"]
+
+
+def version() -> str:
+    return lib.nvfp4_version().decode()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+class KVPool:
+    """One paged NVFP4 pool (K or V).
+
+    ``data`` is uint8 ``[pages, H, P, D/2]`` (layout "HND") or ``[pages, P, H, D/2]``
+    ("NHD"); ``sf`` has the same leading dims and ``D/16`` scale bytes.  Any strides
+    are allowed as long as the last dimension is contiguous.
+    """
+
+    def __init__(self, data: torch.Tensor, sf: torch.Tensor, *, head_dim: int, layout="HND",
+                 global_scale: float = 1.0):
+        if data.dtype != torch.uint8 or sf.dtype != torch.uint8:
+            raise TypeError("pool data and scales must be uint8 tensors")
+        if data.dim() != 4 or sf.dim() != 4:
+            raise ValueError("pool tensors must be 4-D")
+        if layout not in ("HND", "NHD"):
+            raise ValueError(f"layout must be HND or NHD, got {layout!r}")
+        if data.stride(-1) != 1 or sf.stride(-1) != 1:
+            raise ValueError("the last pool dimension must be contiguous")
+        self.data, self.sf, self.layout = data, sf, layout
+        self.head_dim = int(head_dim)
+        self.global_scale = float(global_scale)
+        self.num_pages = data.shape[0]
+        if layout == "HND":
+            self.num_kv_heads, self.page_size = data.shape[1], data.shape[2]
+        else:
+            self.page_size, self.num_kv_heads = data.shape[1], data.shape[2]
+        if data.shape[-1] != head_dim // 2 or sf.shape[-1] != head_dim // 16:
+            raise ValueError("pool last dims must be head_dim/2 (data) and head_dim/16 (scales)")
+
+    @classmethod
+    def empty(cls, num_pages: int, num_kv_heads: int, page_size: int, head_dim: int,
+              layout="HND", device="cuda", global_scale: float = 1.0) -> "KVPool":
+        if layout == "HND":
+            shape = (num_pages, num_kv_heads, page_size)
+        else:
+            shape = (num_pages, page_size, num_kv_heads)
+        data = torch.empty(shape + (head_dim // 2,), dtype=torch.uint8, device=device)
+        sf = torch.empty(shape + (head_dim // 16,), dtype=torch.uint8, device=device)
+        return cls(data, sf, head_dim=head_dim, layout=layout, global_scale=global_scale)
+
+    def struct(self) -> KVPoolStruct:
+        d, s = self.data.stride(), self.sf.stride()
+        if self.layout == "HND":
+            dp, dh, dt = d[0], d[1], d[2]
+            sp, sh, st = s[0], s[1], s[2]
+        else:
+            dp, dt, dh = d[0], d[1], d[2]
+            sp, st, sh = s[0], s[1], s[2]
+        return KVPoolStruct(self.data.data_ptr(), dp, dh, dt, self.sf.data_ptr(), sp, sh, st,
+                            self.num_pages, self.page_size, self.num_kv_heads, self.head_dim,
+                            self.global_scale)
+
+
+def quantize_kv(k: Optional[torch.Tensor], v: Optional[torch.Tensor], slot_mapping: torch.Tensor,
+                k_pool: Optional[KVPool], v_pool: Optional[KVPool], stream=None) -> None:
+    """Quantise bf16 K/V rows ``[n_tokens, H, D]`` into their pools at ``slot_mapping``
+    (int64 ``page * page_size + offset``; negative = skip)."""
+    n = (k if k is not None else v).shape[0]
+    for t in (k, v):
+        if t is not None and (t.dtype != torch.bfloat16 or t.dim() != 3 or t.stride(-1) != 1):
+            raise ValueError("K/V sources must be bf16 [n_tokens, heads, head_dim], last dim contiguous")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.numel() < n:
+        raise ValueError("slot_mapping must be int64 with one entry per token")
+    ks = k_pool.struct() if k_pool is not None else None
+    vs = v_pool.struct() if v_pool is not None else None
+    check(lib.nvfp4_quantize_kv(
+        _ptr(k), k.stride(0) if k is not None else 0, k.stride(1) if k is not None else 0,
+        _ptr(v), v.stride(0) if v is not None else 0, v.stride(1) if v is not None else 0,
+        n, _ptr(slot_mapping),
+        ctypes.byref(ks) if ks is not None else None, ctypes.byref(vs) if vs is not None else None,
+        _stream(stream)))
+
+
+class Plan:
+    """Host-side split of one batch into work items (``nvfp4_plan_create``).
+
+    Decode when ``qo_indptr`` is None (one query per request), else prefill.
+    """
+
+    def __init__(self, kv_lens: Sequence[int], *, num_qo_heads: int, num_kv_heads: int,
+                 head_dim_qk: int, head_dim_vo: Optional[int] = None, page_size: int = 16,
+                 qo_indptr: Optional[Sequence[int]] = None, causal: bool = False,
+                 kv_chunk_tokens: int = 0, num_cus: int = 0):
+        head_dim_vo = head_dim_qk if head_dim_vo is None else head_dim_vo
+        self._kv = np.ascontiguousarray(np.asarray(kv_lens, dtype=np.int32))
+        self._ind = None if qo_indptr is None else np.ascontiguousarray(
+            np.asarray(qo_indptr, dtype=np.int32))
+        self._h = ctypes.c_void_p()
+        self.batch = len(self._kv)
+        self.num_qo_heads, self.num_kv_heads = num_qo_heads, num_kv_heads
+        self.head_dim_qk, self.head_dim_vo, self.page_size = head_dim_qk, head_dim_vo, page_size
+        self.causal = causal
+        check(lib.nvfp4_plan_create(
+            self._kv.ctypes.data_as(ctypes.c_void_p) if self.batch else None,
+            self._ind.ctypes.data_as(ctypes.c_void_p) if self._ind is not None else None,
+            self.batch, num_qo_heads, num_kv_heads, head_dim_qk, head_dim_vo, page_size,
+            int(bool(causal)), kv_chunk_tokens, num_cus, ctypes.byref(self._h)))
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            lib.nvfp4_plan_destroy(h)
+            self._h = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    @property
+    def workspace_bytes(self) -> int:
+        return int(lib.nvfp4_plan_workspace_bytes(self._h))
+
+    def info(self) -> dict:
+        s = PlanInfoStruct()
+        check(lib.nvfp4_plan_get_info(self._h, ctypes.byref(s)))
+        return {f: getattr(s, f) for f, _ in PlanInfoStruct._fields_}
+
+    def work(self) -> np.ndarray:
+        n = self.info()["num_work_items"]
+        out = np.zeros((max(n, 1), len(WORK_FIELDS)), dtype=np.int32)
+        check(lib.nvfp4_plan_get_work(self._h, out.ctypes.data_as(ctypes.c_void_p), n))
+        return out[:n]
+
+    def new_workspace(self, device="cuda") -> torch.Tensor:
+        return torch.empty(self.workspace_bytes, dtype=torch.uint8, device=device)
+
+    def upload(self, workspace: torch.Tensor, stream=None) -> None:
+        check(lib.nvfp4_plan_upload(self._h, _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def _attn(fn, plan: Plan, q, page_table, k_pool, v_pool, sm_scale, workspace, out, lse, stream):
+    rows = q.shape[0]
+    if q.dtype != torch.bfloat16 or q.dim() != 3 or q.stride(-1) != 1:
+        raise ValueError("q must be bf16 [rows, num_qo_heads, head_dim_qk], last dim contiguous")
+    if page_table.dtype != torch.int32 or page_table.dim() != 2 or page_table.stride(1) != 1:
+        raise ValueError("page_table must be int32 [batch, max_pages] with contiguous rows")
+    if out is None:
+        out = torch.empty((rows, plan.num_qo_heads, plan.head_dim_vo), dtype=torch.float32,
+                          device=q.device)
+    if lse is None:
+        lse = torch.empty((rows, plan.num_qo_heads), dtype=torch.float32, device=q.device)
+    if out.dtype != torch.float32 or out.stride(-1) != 1 or lse.dtype != torch.float32 \
+            or not lse.is_contiguous():
+        raise ValueError("out must be fp32 with a contiguous last dim; lse fp32 contiguous")
+    ks, vs = k_pool.struct(), v_pool.struct()
+    check(fn(plan.handle, _ptr(q), q.stride(0), q.stride(1), _ptr(page_table), page_table.stride(0),
+             ctypes.byref(ks), ctypes.byref(vs), float(sm_scale), _ptr(workspace),
+             workspace.numel(), _ptr(out), out.stride(0), out.stride(1), _ptr(lse), _stream(stream)))
+    return out, lse
+
+
+def batch_decode(plan: Plan, q: torch.Tensor, page_table: torch.Tensor, k_pool: KVPool,
+                 v_pool: KVPool, sm_scale: float, workspace: torch.Tensor,
+                 out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                 stream=None):
+    """Decode attention; returns (O fp32 [batch, Hq, Dv], LSE fp32 [batch, Hq])."""
+    return _attn(lib.nvfp4_batch_decode, plan, q, page_table, k_pool, v_pool, sm_scale,
+                 workspace, out, lse, stream)
+
+
+def batch_prefill(plan: Plan, q: torch.Tensor, page_table: torch.Tensor, k_pool: KVPool,
+                  v_pool: KVPool, sm_scale: float, workspace: torch.Tensor,
+                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                  stream=None):
+    """Prefill / extend attention; returns (O fp32 [total_q, Hq, Dv], LSE fp32 [total_q, Hq])."""
+    return _attn(lib.nvfp4_batch_prefill, plan, q, page_table, k_pool, v_pool, sm_scale,
+                 workspace, out, lse, stream)
+
+
+def merge_states(o_parts: torch.Tensor, lse_parts: torch.Tensor, out=None, lse=None, stream=None):
+    """Merge partial states: o_parts fp32 [rows, n, H, D], lse_parts fp32 [rows, n, H]."""
+    if not (o_parts.is_contiguous() and lse_parts.is_contiguous()):
+        raise ValueError("o_parts and lse_parts must be contiguous")
+    rows, n, h, d = o_parts.shape
+    if out is None:
+        out = torch.empty((rows, h, d), dtype=torch.float32, device=o_parts.device)
+    if lse is None:
+        lse = torch.empty((rows, h), dtype=torch.float32, device=o_parts.device)
+    check(lib.nvfp4_merge_states(_ptr(o_parts), _ptr(lse_parts), rows, n, h, d, _ptr(out),
+                                 _ptr(lse), _stream(stream)))
+    return out, lse

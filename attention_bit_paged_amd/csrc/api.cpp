@@ -1,0 +1,633 @@
+// Host side of the C ABI: argument validation, the split-KV planner, workspace
+// layout and kernel launches.  No device memory is allocated here.
+//
+// [PF] "Re-enable split-KV for NVFP4 KV cache in prefill path":
+//   * commit "Re-enable split-KV...": reject a tile that does not fit on-chip memory
+//     at plan time instead of failing at launch;
+//   * commit "Gate split-KV off when kv_data_type is NVFP4", follow-up: the split of
+//     the KV range uses 16-token-aligned chunk boundaries;
+//   * commits on unequal K/V strides: either support them or reject them loudly
+//     (supported everywhere here);
+//   * last commit: NVFP4 needs its scale tensors (a null scale pointer is rejected);
+//   * commit on JIT scalars: errors name the offending argument.
+// [XQA] "Support NVFP4 KV cache decode on SM120", review: check the capability of
+// the device the call runs on, not of a default device.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <numeric>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+using namespace nvfp4;
+
+namespace {
+
+thread_local std::string g_error;
+
+nvfp4_status fail(nvfp4_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return st;
+}
+
+nvfp4_status ok() {
+  g_error.clear();
+  return NVFP4_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+int log2i(int64_t x) {
+  int s = 0;
+  while ((int64_t(1) << s) < x) ++s;
+  return s;
+}
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// ---- device check: gfx950 only, cached per device ordinal
+std::mutex g_dev_mu;
+int g_dev_state[64];  // 0 unknown, 1 gfx950, 2 other
+
+nvfp4_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+    return fail(NVFP4_E_DEVICE, "no HIP device is current");
+  if (dev >= 64) return fail(NVFP4_E_DEVICE, "device ordinal %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if (g_dev_state[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+      return fail(NVFP4_E_DEVICE, "hipGetDeviceProperties failed for device %d", dev);
+    g_dev_state[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    if (g_dev_state[dev] == 2)
+      return fail(NVFP4_E_DEVICE, "device %d is %s, this library needs gfx950", dev,
+                  prop.gcnArchName);
+  }
+  if (g_dev_state[dev] != 1) return fail(NVFP4_E_DEVICE, "device %d is not gfx950", dev);
+  return NVFP4_OK;
+}
+
+bool head_dim_ok(int d) { return d == 64 || d == 128 || d == 256 || d == 512; }
+
+// Validates one pool against the expected head dim and shared page geometry.
+nvfp4_status check_pool(const nvfp4_kv_pool* p, const char* name, int head_dim,
+                        int num_kv_heads, int page_size) {
+  if (!p) return fail(NVFP4_E_INVALID, "%s pool is NULL", name);
+  if (!p->data) return fail(NVFP4_E_INVALID, "%s.data is NULL", name);
+  if (!p->sf) return fail(NVFP4_E_INVALID, "%s.sf is NULL: NVFP4 needs its scale factors", name);
+  if (p->head_dim != head_dim)
+    return fail(NVFP4_E_SHAPE, "%s.head_dim is %d, expected %d", name, p->head_dim, head_dim);
+  if (num_kv_heads >= 0 && p->num_kv_heads != num_kv_heads)
+    return fail(NVFP4_E_SHAPE, "%s.num_kv_heads is %d, expected %d", name, p->num_kv_heads,
+                num_kv_heads);
+  if (page_size >= 0 && p->page_size != page_size)
+    return fail(NVFP4_E_SHAPE, "%s.page_size is %d, expected %d", name, p->page_size, page_size);
+  if (!is_pow2(p->page_size) || p->page_size > 256)
+    return fail(NVFP4_E_UNSUPPORTED, "%s.page_size %d is not a power of two in [1, 256]", name,
+                p->page_size);
+  if (p->num_pages < 1) return fail(NVFP4_E_INVALID, "%s.num_pages must be >= 1", name);
+  if (p->num_kv_heads < 1) return fail(NVFP4_E_INVALID, "%s.num_kv_heads must be >= 1", name);
+  if (!(p->global_scale > 0.f) || !std::isfinite(p->global_scale))
+    return fail(NVFP4_E_INVALID, "%s.global_scale must be finite and > 0", name);
+  const int64_t da = head_dim >= 128 ? 16 : head_dim / 8;
+  const int64_t sa = std::min(head_dim / 16, 8);
+  if (!aligned(p->data, da) || p->stride_page % da || p->stride_head % da || p->stride_token % da)
+    return fail(NVFP4_E_SHAPE, "%s data pointer and strides must be multiples of %lld bytes", name,
+                (long long)da);
+  if (!aligned(p->sf, sa) || p->sf_stride_page % sa || p->sf_stride_head % sa ||
+      p->sf_stride_token % sa)
+    return fail(NVFP4_E_SHAPE, "%s sf pointer and strides must be multiples of %lld bytes", name,
+                (long long)sa);
+  if (p->stride_page < 0 || p->stride_head < 0 || p->stride_token < 0 || p->sf_stride_page < 0 ||
+      p->sf_stride_head < 0 || p->sf_stride_token < 0)
+    return fail(NVFP4_E_SHAPE, "%s strides must be non-negative", name);
+  return NVFP4_OK;
+}
+
+PoolArgs pool_args(const nvfp4_kv_pool* p, int num_pages) {
+  PoolArgs a;
+  a.data = static_cast<const uint8_t*>(p->data);
+  a.s_page = p->stride_page;
+  a.s_head = p->stride_head;
+  a.s_tok = p->stride_token;
+  a.sf = static_cast<const uint8_t*>(p->sf);
+  a.sf_page = p->sf_stride_page;
+  a.sf_head = p->sf_stride_head;
+  a.sf_tok = p->sf_stride_token;
+  a.num_pages = num_pages;
+  return a;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------- plan
+struct nvfp4_plan {
+  int prefill = 0;
+  int batch = 0, num_qo_heads = 0, num_kv_heads = 0, group = 0;
+  int head_dim_qk = 0, head_dim_vo = 0, page_size = 0, causal = 0;
+  int chunk = 0;           // chunk length used when splitting (0: no split)
+  int rows_per_item = 0;   // decode: 16 heads; prefill: rows of a tile
+  int rows_per_slot = 0;
+  int64_t total_q = 0;
+  std::vector<int32_t> work;    // kWorkFields per item
+  std::vector<int32_t> merges;  // kMergeFields per merge
+  std::vector<int32_t> kv_lens, qo_indptr;
+  int num_partials = 0;
+  // workspace layout (byte offsets)
+  size_t off_work = 0, off_merge = 0, off_kvlens = 0, off_indptr = 0, off_part_o = 0,
+         off_part_lse = 0, ws_bytes = 0;
+  void* uploaded_to = nullptr;
+};
+
+extern "C" {
+
+const char* nvfp4_last_error(void) { return g_error.c_str(); }
+
+const char* nvfp4_version(void) { return "nvfp4_attn 0.1 (gfx950)"; }
+
+nvfp4_status nvfp4_plan_create(const int32_t* kv_lens, const int32_t* qo_indptr, int32_t batch,
+                               int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim_qk,
+                               int32_t head_dim_vo, int32_t page_size, int32_t causal,
+                               int32_t kv_chunk_tokens, int32_t num_cus, nvfp4_plan** out) {
+  if (!out) return fail(NVFP4_E_INVALID, "out is NULL");
+  *out = nullptr;
+  if (batch < 0) return fail(NVFP4_E_INVALID, "batch must be >= 0");
+  if (batch > 0 && !kv_lens) return fail(NVFP4_E_INVALID, "kv_lens is NULL");
+  if (num_qo_heads < 1 || num_kv_heads < 1)
+    return fail(NVFP4_E_INVALID, "num_qo_heads and num_kv_heads must be >= 1");
+  if (num_qo_heads % num_kv_heads)
+    return fail(NVFP4_E_SHAPE, "num_qo_heads %d is not a multiple of num_kv_heads %d",
+                num_qo_heads, num_kv_heads);
+  if (!head_dim_ok(head_dim_qk) || !head_dim_ok(head_dim_vo))
+    return fail(NVFP4_E_UNSUPPORTED, "head dims (qk %d, vo %d): each must be 64, 128, 256 or 512",
+                head_dim_qk, head_dim_vo);
+  const bool prefill = qo_indptr != nullptr;
+  if (prefill ? !prefill_supported(head_dim_qk, head_dim_vo)
+              : !decode_supported(head_dim_qk, head_dim_vo))
+    return fail(NVFP4_E_UNSUPPORTED, "head dims (qk %d, vo %d) not supported (need vo <= qk)",
+                head_dim_qk, head_dim_vo);
+  if (head_dim_qk == 512 && head_dim_vo == 512)
+    return fail(NVFP4_E_LDS_BUDGET,
+                "head dims (512, 512): the per-wave tile does not fit the register file");
+  if (!is_pow2(page_size) || page_size > 256)
+    return fail(NVFP4_E_UNSUPPORTED, "page_size %d is not a power of two in [1, 256]", page_size);
+  if (kv_chunk_tokens > 0 && kv_chunk_tokens % 16)
+    return fail(NVFP4_E_INVALID, "kv_chunk_tokens %d is not a multiple of 16", kv_chunk_tokens);
+  if (num_cus < 0) return fail(NVFP4_E_INVALID, "num_cus must be >= 0");
+  const int group = num_qo_heads / num_kv_heads;
+  if (!prefill && group > 4 * kDecodeHeads)
+    return fail(NVFP4_E_UNSUPPORTED, "decode supports at most %d qo heads per kv head, got %d",
+                4 * kDecodeHeads, group);
+  int rows_item = prefill ? prefill_rows_per_item(head_dim_qk, head_dim_vo, group) : kDecodeHeads;
+  if (prefill && group > rows_item)
+    return fail(NVFP4_E_UNSUPPORTED, "prefill supports at most %d qo heads per kv head, got %d",
+                rows_item, group);
+  if (prefill && prefill_lds_bytes(head_dim_qk, head_dim_vo) > 160 * 1024)
+    return fail(NVFP4_E_LDS_BUDGET, "prefill tile for (%d, %d) exceeds 160 KiB of LDS",
+                head_dim_qk, head_dim_vo);
+
+  for (int b = 0; b < batch; ++b) {
+    if (kv_lens[b] < 0) return fail(NVFP4_E_INVALID, "kv_lens[%d] = %d is negative", b, kv_lens[b]);
+  }
+  int64_t total_q = batch;
+  if (prefill) {
+    if (qo_indptr[0] != 0) return fail(NVFP4_E_SHAPE, "qo_indptr[0] must be 0");
+    for (int b = 0; b < batch; ++b) {
+      const int q = qo_indptr[b + 1] - qo_indptr[b];
+      if (q < 0) return fail(NVFP4_E_SHAPE, "qo_indptr is not non-decreasing at %d", b);
+      if (q > kv_lens[b])
+        return fail(NVFP4_E_SHAPE, "request %d has %d queries but only %d keys", b, q, kv_lens[b]);
+    }
+    total_q = qo_indptr[batch];
+  }
+
+  if (num_cus == 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        cus > 0)
+      num_cus = cus;
+    else
+      num_cus = 256;
+    (void)hipGetLastError();
+  }
+
+  auto* plan = new nvfp4_plan();
+  plan->prefill = prefill;
+  plan->batch = batch;
+  plan->num_qo_heads = num_qo_heads;
+  plan->num_kv_heads = num_kv_heads;
+  plan->group = group;
+  plan->head_dim_qk = head_dim_qk;
+  plan->head_dim_vo = head_dim_vo;
+  plan->page_size = page_size;
+  plan->causal = prefill ? (causal != 0) : 0;
+  plan->total_q = total_q;
+  plan->kv_lens.assign(kv_lens, kv_lens + batch);
+  if (prefill) plan->qo_indptr.assign(qo_indptr, qo_indptr + batch + 1);
+
+  // Row groups: decode -> (b, kv head, head block of <= 16 heads) over [0, L);
+  // prefill -> (b, kv head, query tile) over the tile's visible key range.
+  struct RowGroup {
+    int b, kvh, row0, rows, kv_end;
+  };
+  std::vector<RowGroup> groups;
+  if (!prefill) {
+    const int nhb = (group + kDecodeHeads - 1) / kDecodeHeads;
+    for (int b = 0; b < batch; ++b)
+      for (int g = 0; g < num_kv_heads; ++g)
+        for (int hb = 0; hb < nhb; ++hb)
+          groups.push_back({b, g, hb * kDecodeHeads, std::min(kDecodeHeads, group - hb * kDecodeHeads),
+                            kv_lens[b]});
+    plan->rows_per_item = kDecodeHeads;
+    plan->rows_per_slot = kDecodeHeads;
+  } else {
+    const int tq = rows_item / group;  // queries per tile
+    for (int b = 0; b < batch; ++b) {
+      const int qlen = qo_indptr[b + 1] - qo_indptr[b];
+      const int L = kv_lens[b];
+      for (int g = 0; g < num_kv_heads; ++g)
+        for (int q0 = 0; q0 < qlen; q0 += tq) {
+          const int qn = std::min(tq, qlen - q0);
+          const int end = plan->causal ? std::min(L, q0 + qn - 1 + (L - qlen) + 1) : L;
+          groups.push_back({b, g, q0, qn, end});
+        }
+    }
+    plan->rows_per_item = tq * group;
+    plan->rows_per_slot = tq * group;
+  }
+
+  // Chunk length: explicit, never, or chosen so that the work items fill the device.
+  int chunk = 0;
+  if (kv_chunk_tokens > 0) {
+    chunk = kv_chunk_tokens;
+  } else if (kv_chunk_tokens == 0) {
+    // Items one CU should hold at once: decode items are single waves, prefill items
+    // workgroups of four.
+    const int64_t target = (int64_t)num_cus * (prefill ? 2 : 8);
+    if ((int64_t)groups.size() < target) {
+      int64_t total = 0;
+      int max_len = 0;
+      for (const auto& g : groups) {
+        total += g.kv_end;
+        max_len = std::max(max_len, g.kv_end);
+      }
+      int64_t c = (total + target - 1) / std::max<int64_t>(target, 1);
+      c = std::max<int64_t>(c, prefill ? 128 : 256);
+      c = (c + 31) / 32 * 32;
+      if (c < max_len) chunk = (int)c;
+    }
+  }
+  plan->chunk = chunk;
+
+  struct Item {
+    int32_t f[kWorkFields];
+    int len;
+  };
+  std::vector<Item> items;
+  std::vector<int32_t> merges;
+  int next_slot = 0;
+  for (const auto& g : groups) {
+    const int L = g.kv_end;
+    const int nchunks = (chunk > 0 && L > chunk) ? (L + chunk - 1) / chunk : 1;
+    if (nchunks == 1) {
+      items.push_back({{g.b, g.kvh, g.row0, g.rows, 0, L, -1, -1}, L});
+      continue;
+    }
+    const int mi = (int)(merges.size() / kMergeFields);
+    const int32_t rec[kMergeFields] = {g.b, g.kvh, g.row0, g.rows, next_slot, nchunks, 0, 0};
+    merges.insert(merges.end(), rec, rec + kMergeFields);
+    for (int c = 0; c < nchunks; ++c) {
+      const int a = c * chunk, e = std::min(L, (c + 1) * chunk);
+      items.push_back({{g.b, g.kvh, g.row0, g.rows, a, e, next_slot + c, mi}, e - a});
+    }
+    next_slot += nchunks;
+  }
+  // Longest first, so the tail of the grid holds the short items.
+  std::stable_sort(items.begin(), items.end(),
+                   [](const Item& x, const Item& y) { return x.len > y.len; });
+  plan->work.reserve(items.size() * kWorkFields);
+  for (const auto& it : items) plan->work.insert(plan->work.end(), it.f, it.f + kWorkFields);
+  plan->merges = std::move(merges);
+  plan->num_partials = next_slot;
+
+  // Workspace: [work | merges | kv_lens | qo_indptr | partial O | partial LSE]
+  size_t off = 0;
+  plan->off_work = off;
+  off = align_up(off + plan->work.size() * sizeof(int32_t));
+  plan->off_merge = off;
+  off = align_up(off + plan->merges.size() * sizeof(int32_t));
+  plan->off_kvlens = off;
+  off = align_up(off + (size_t)batch * sizeof(int32_t));
+  plan->off_indptr = off;
+  off = align_up(off + (size_t)(batch + 1) * sizeof(int32_t));
+  plan->off_part_o = off;
+  off = align_up(off + (size_t)plan->num_partials * plan->rows_per_slot * head_dim_vo * sizeof(float));
+  plan->off_part_lse = off;
+  off = align_up(off + (size_t)plan->num_partials * plan->rows_per_slot * sizeof(float));
+  plan->ws_bytes = std::max<size_t>(off, kAlign);
+  *out = plan;
+  return ok();
+}
+
+void nvfp4_plan_destroy(nvfp4_plan* plan) { delete plan; }
+
+size_t nvfp4_plan_workspace_bytes(const nvfp4_plan* plan) { return plan ? plan->ws_bytes : 0; }
+
+nvfp4_status nvfp4_plan_get_info(const nvfp4_plan* plan, nvfp4_plan_info* info) {
+  if (!plan || !info) return fail(NVFP4_E_INVALID, "plan or info is NULL");
+  info->num_work_items = (int32_t)(plan->work.size() / kWorkFields);
+  info->num_partials = plan->num_partials;
+  info->num_merges = (int32_t)(plan->merges.size() / kMergeFields);
+  info->kv_chunk_tokens = plan->chunk;
+  info->rows_per_item = plan->rows_per_item;
+  info->is_prefill = plan->prefill;
+  info->workspace_bytes = (int64_t)plan->ws_bytes;
+  return ok();
+}
+
+nvfp4_status nvfp4_plan_get_work(const nvfp4_plan* plan, int32_t* out, int64_t capacity) {
+  if (!plan || !out) return fail(NVFP4_E_INVALID, "plan or out is NULL");
+  const int64_t n = (int64_t)(plan->work.size() / kWorkFields);
+  if (capacity < n) return fail(NVFP4_E_INVALID, "capacity %lld < %lld work items",
+                                (long long)capacity, (long long)n);
+  std::memcpy(out, plan->work.data(), plan->work.size() * sizeof(int32_t));
+  return ok();
+}
+
+nvfp4_status nvfp4_plan_upload(nvfp4_plan* plan, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  if (!plan) return fail(NVFP4_E_INVALID, "plan is NULL");
+  if (!workspace) return fail(NVFP4_E_WORKSPACE, "workspace is NULL");
+  if (!aligned(workspace, kAlign)) return fail(NVFP4_E_WORKSPACE, "workspace is not 256-byte aligned");
+  if (workspace_bytes < plan->ws_bytes)
+    return fail(NVFP4_E_WORKSPACE, "workspace has %zu bytes, plan needs %zu", workspace_bytes,
+                plan->ws_bytes);
+  if (nvfp4_status st = check_device()) return st;
+  // One host staging buffer for the tables, then one copy.
+  std::vector<uint8_t> host(plan->off_part_o, 0);
+  auto put = [&](size_t off, const std::vector<int32_t>& v) {
+    if (!v.empty()) std::memcpy(host.data() + off, v.data(), v.size() * sizeof(int32_t));
+  };
+  put(plan->off_work, plan->work);
+  put(plan->off_merge, plan->merges);
+  put(plan->off_kvlens, plan->kv_lens);
+  put(plan->off_indptr, plan->qo_indptr);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!host.empty()) {
+    hipError_t e = hipMemcpyAsync(workspace, host.data(), host.size(), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return fail(NVFP4_E_HIP, "plan upload failed: %s", hipGetErrorString(e));
+  }
+  plan->uploaded_to = workspace;
+  return ok();
+}
+
+}  // extern "C"
+
+namespace {
+
+nvfp4_status check_run(const nvfp4_plan* plan, bool prefill, const void* q, int64_t q_s_row,
+                       int64_t q_s_head, const int32_t* page_table, int64_t pt_stride,
+                       const nvfp4_kv_pool* k, const nvfp4_kv_pool* v, float sm_scale,
+                       void* ws, size_t ws_bytes, float* o, int64_t o_s_row, int64_t o_s_head,
+                       float* lse) {
+  if (!plan) return fail(NVFP4_E_INVALID, "plan is NULL");
+  if (plan->prefill != (int)prefill)
+    return fail(NVFP4_E_SHAPE, "plan was made for %s, called for %s",
+                plan->prefill ? "prefill" : "decode", prefill ? "prefill" : "decode");
+  if (nvfp4_status st = check_pool(k, "k_pool", plan->head_dim_qk, plan->num_kv_heads,
+                                   plan->page_size))
+    return st;
+  if (nvfp4_status st = check_pool(v, "v_pool", plan->head_dim_vo, plan->num_kv_heads,
+                                   plan->page_size))
+    return st;
+  if (!std::isfinite(sm_scale)) return fail(NVFP4_E_INVALID, "sm_scale is not finite");
+  const bool any_rows = plan->total_q > 0;
+  if (any_rows) {
+    if (!q) return fail(NVFP4_E_INVALID, "q is NULL");
+    if (!o) return fail(NVFP4_E_INVALID, "o is NULL");
+    if (!lse) return fail(NVFP4_E_INVALID, "lse is NULL");
+    if (!page_table) return fail(NVFP4_E_INVALID, "page_table is NULL");
+  }
+  if (!aligned(q, 16) || q_s_row % 8 || q_s_head % 8 || q_s_row < 0 || q_s_head < 0)
+    return fail(NVFP4_E_SHAPE, "q rows must be 16-byte aligned (strides multiples of 8 elements)");
+  if (!aligned(o, 16) || o_s_row % 4 || o_s_head % 4 || o_s_row < 0 || o_s_head < 0)
+    return fail(NVFP4_E_SHAPE, "o rows must be 16-byte aligned (strides multiples of 4 elements)");
+  if (!aligned(lse, 4)) return fail(NVFP4_E_SHAPE, "lse must be 4-byte aligned");
+  int max_pages = 0;
+  for (int b = 0; b < plan->batch; ++b)
+    max_pages = std::max(max_pages, (plan->kv_lens[b] + plan->page_size - 1) / plan->page_size);
+  if (pt_stride < max_pages)
+    return fail(NVFP4_E_SHAPE, "pt_stride %lld is smaller than the %d pages of the longest request",
+                (long long)pt_stride, max_pages);
+  if (!ws) return fail(NVFP4_E_WORKSPACE, "workspace is NULL");
+  if (ws_bytes < plan->ws_bytes)
+    return fail(NVFP4_E_WORKSPACE, "workspace has %zu bytes, plan needs %zu", ws_bytes,
+                plan->ws_bytes);
+  if (plan->uploaded_to != ws)
+    return fail(NVFP4_E_WORKSPACE, "the plan was not uploaded to this workspace (nvfp4_plan_upload)");
+  return check_device();
+}
+
+AttnArgs make_args(const nvfp4_plan* plan, const void* q, int64_t q_s_row, int64_t q_s_head,
+                   const int32_t* page_table, int64_t pt_stride, const nvfp4_kv_pool* k,
+                   const nvfp4_kv_pool* v, float sm_scale, void* ws, float* o, int64_t o_s_row,
+                   int64_t o_s_head, float* lse) {
+  AttnArgs a;
+  std::memset(&a, 0, sizeof(a));
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  const int num_pages = std::min(k->num_pages, v->num_pages);
+  a.q = static_cast<const uint16_t*>(q);
+  a.q_s_row = q_s_row;
+  a.q_s_head = q_s_head;
+  a.page_table = page_table;
+  a.pt_stride = pt_stride;
+  a.k = pool_args(k, num_pages);
+  a.v = pool_args(v, num_pages);
+  a.score_scale = sm_scale * 1.4426950408889634f * k->global_scale;
+  a.out_scale = v->global_scale;
+  a.work = reinterpret_cast<const int32_t*>(w + plan->off_work);
+  a.n_work = (int32_t)(plan->work.size() / kWorkFields);
+  a.kv_lens = reinterpret_cast<const int32_t*>(w + plan->off_kvlens);
+  a.qo_indptr = reinterpret_cast<const int32_t*>(w + plan->off_indptr);
+  a.o = o;
+  a.o_s_row = o_s_row;
+  a.o_s_head = o_s_head;
+  a.lse = lse;
+  a.part_o = reinterpret_cast<float*>(w + plan->off_part_o);
+  a.part_lse = reinterpret_cast<float*>(w + plan->off_part_lse);
+  a.num_qo_heads = plan->num_qo_heads;
+  a.group = plan->group;
+  a.page_shift = log2i(plan->page_size);
+  a.rows_per_slot = plan->rows_per_slot;
+  a.causal = plan->causal;
+  return a;
+}
+
+MergeArgs make_merge(const nvfp4_plan* plan, const AttnArgs& a, void* ws) {
+  MergeArgs m;
+  std::memset(&m, 0, sizeof(m));
+  m.merges = reinterpret_cast<const int32_t*>(static_cast<uint8_t*>(ws) + plan->off_merge);
+  m.n_merges = (int32_t)(plan->merges.size() / kMergeFields);
+  m.part_o = a.part_o;
+  m.part_lse = a.part_lse;
+  m.rows_per_slot = plan->rows_per_slot;
+  m.head_dim = plan->head_dim_vo;
+  m.o = a.o;
+  m.o_s_row = a.o_s_row;
+  m.o_s_head = a.o_s_head;
+  m.lse = a.lse;
+  m.num_qo_heads = plan->num_qo_heads;
+  m.group = plan->group;
+  m.prefill = plan->prefill;
+  m.qo_indptr = a.qo_indptr;
+  return m;
+}
+
+nvfp4_status run(const nvfp4_plan* plan, bool prefill, const void* q, int64_t q_s_row,
+                 int64_t q_s_head, const int32_t* page_table, int64_t pt_stride,
+                 const nvfp4_kv_pool* k, const nvfp4_kv_pool* v, float sm_scale, void* ws,
+                 size_t ws_bytes, float* o, int64_t o_s_row, int64_t o_s_head, float* lse,
+                 void* stream) {
+  if (nvfp4_status st = check_run(plan, prefill, q, q_s_row, q_s_head, page_table, pt_stride, k,
+                                  v, sm_scale, ws, ws_bytes, o, o_s_row, o_s_head, lse))
+    return st;
+  if (plan->work.empty()) return ok();
+  const AttnArgs a = make_args(plan, q, q_s_row, q_s_head, page_table, pt_stride, k, v, sm_scale,
+                               ws, o, o_s_row, o_s_head, lse);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = prefill
+                     ? launch_prefill(plan->head_dim_qk, plan->head_dim_vo, a.page_shift, a,
+                                      plan->rows_per_item, s)
+                     : launch_decode(plan->head_dim_qk, plan->head_dim_vo, a.page_shift, a, s);
+  if (e != hipSuccess)
+    return fail(NVFP4_E_HIP, "%s launch failed: %s", prefill ? "prefill" : "decode",
+                hipGetErrorString(e));
+  if (!plan->merges.empty()) {
+    e = launch_merge_partials(make_merge(plan, a, ws), s);
+    if (e != hipSuccess) return fail(NVFP4_E_HIP, "merge launch failed: %s", hipGetErrorString(e));
+  }
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+nvfp4_status nvfp4_batch_decode(const nvfp4_plan* plan, const void* q, int64_t q_stride_req,
+                                int64_t q_stride_head, const int32_t* page_table, int64_t pt_stride,
+                                const nvfp4_kv_pool* k_pool, const nvfp4_kv_pool* v_pool,
+                                float sm_scale, void* workspace, size_t workspace_bytes, float* o,
+                                int64_t o_stride_req, int64_t o_stride_head, float* lse,
+                                void* stream) {
+  return run(plan, false, q, q_stride_req, q_stride_head, page_table, pt_stride, k_pool, v_pool,
+             sm_scale, workspace, workspace_bytes, o, o_stride_req, o_stride_head, lse, stream);
+}
+
+nvfp4_status nvfp4_batch_prefill(const nvfp4_plan* plan, const void* q, int64_t q_stride_tok,
+                                 int64_t q_stride_head, const int32_t* page_table,
+                                 int64_t pt_stride, const nvfp4_kv_pool* k_pool,
+                                 const nvfp4_kv_pool* v_pool, float sm_scale, void* workspace,
+                                 size_t workspace_bytes, float* o, int64_t o_stride_tok,
+                                 int64_t o_stride_head, float* lse, void* stream) {
+  return run(plan, true, q, q_stride_tok, q_stride_head, page_table, pt_stride, k_pool, v_pool,
+             sm_scale, workspace, workspace_bytes, o, o_stride_tok, o_stride_head, lse, stream);
+}
+
+nvfp4_status nvfp4_merge_states(const float* o_parts, const float* lse_parts, int64_t rows,
+                                int32_t num_parts, int32_t heads, int32_t head_dim, float* o,
+                                float* lse, void* stream) {
+  if (rows < 0) return fail(NVFP4_E_INVALID, "rows must be >= 0");
+  if (num_parts < 1) return fail(NVFP4_E_INVALID, "num_parts must be >= 1");
+  if (heads < 1) return fail(NVFP4_E_INVALID, "heads must be >= 1");
+  if (head_dim < 4 || head_dim % 4 || head_dim > 1024)
+    return fail(NVFP4_E_UNSUPPORTED, "head_dim %d must be a multiple of 4 in [4, 1024]", head_dim);
+  if (rows == 0) return ok();
+  if (!o_parts || !lse_parts || !o || !lse)
+    return fail(NVFP4_E_INVALID, "o_parts, lse_parts, o and lse must be non-NULL");
+  if (!aligned(o_parts, 16) || !aligned(o, 16) || !aligned(lse_parts, 4) || !aligned(lse, 4))
+    return fail(NVFP4_E_SHAPE, "o_parts and o must be 16-byte aligned");
+  if (nvfp4_status st = check_device()) return st;
+  hipError_t e = launch_merge_states(o_parts, lse_parts, rows, num_parts, heads, head_dim, o, lse,
+                                     static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(NVFP4_E_HIP, "merge launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+nvfp4_status nvfp4_quantize_kv(const void* k_src, int64_t k_stride_token, int64_t k_stride_head,
+                               const void* v_src, int64_t v_stride_token, int64_t v_stride_head,
+                               int64_t n_tokens, const int64_t* slot_mapping,
+                               const nvfp4_kv_pool* k_pool, const nvfp4_kv_pool* v_pool,
+                               void* stream) {
+  if (n_tokens < 0) return fail(NVFP4_E_INVALID, "n_tokens must be >= 0");
+  const bool do_k = k_src || k_pool;
+  const bool do_v = v_src || v_pool;
+  if (!do_k && !do_v) return fail(NVFP4_E_INVALID, "nothing to quantise: K and V are both NULL");
+  if (do_k && (!k_src || !k_pool)) return fail(NVFP4_E_INVALID, "k_src and k_pool must both be set");
+  if (do_v && (!v_src || !v_pool)) return fail(NVFP4_E_INVALID, "v_src and v_pool must both be set");
+  if (do_k) {
+    if (nvfp4_status st = check_pool(k_pool, "k_pool", k_pool->head_dim, -1, -1)) return st;
+    if (!head_dim_ok(k_pool->head_dim))
+      return fail(NVFP4_E_UNSUPPORTED, "k_pool.head_dim %d unsupported", k_pool->head_dim);
+  }
+  if (do_v) {
+    if (nvfp4_status st = check_pool(v_pool, "v_pool", v_pool->head_dim, -1, -1)) return st;
+    if (!head_dim_ok(v_pool->head_dim))
+      return fail(NVFP4_E_UNSUPPORTED, "v_pool.head_dim %d unsupported", v_pool->head_dim);
+  }
+  if (do_k && do_v && k_pool->page_size != v_pool->page_size)
+    return fail(NVFP4_E_SHAPE, "k_pool and v_pool page sizes differ");
+  if (do_k && (!aligned(k_src, 16) || k_stride_token % 8 || k_stride_head % 8 ||
+               k_stride_token < 0 || k_stride_head < 0))
+    return fail(NVFP4_E_SHAPE, "k_src rows must be 16-byte aligned (strides multiples of 8)");
+  if (do_v && (!aligned(v_src, 16) || v_stride_token % 8 || v_stride_head % 8 ||
+               v_stride_token < 0 || v_stride_head < 0))
+    return fail(NVFP4_E_SHAPE, "v_src rows must be 16-byte aligned (strides multiples of 8)");
+  if (n_tokens == 0) return ok();
+  if (!slot_mapping) return fail(NVFP4_E_INVALID, "slot_mapping is NULL");
+  if (nvfp4_status st = check_device()) return st;
+  auto qa = [](const void* src, int64_t st, int64_t sh, const nvfp4_kv_pool* p) {
+    QuantArgs a;
+    a.src = static_cast<const uint16_t*>(src);
+    a.s_tok = st;
+    a.s_head = sh;
+    a.data = static_cast<uint8_t*>(p->data);
+    a.d_page = p->stride_page;
+    a.d_head = p->stride_head;
+    a.d_tok = p->stride_token;
+    a.sf = static_cast<uint8_t*>(p->sf);
+    a.sf_page = p->sf_stride_page;
+    a.sf_head = p->sf_stride_head;
+    a.sf_tok = p->sf_stride_token;
+    a.num_slots = (int64_t)p->num_pages * p->page_size;
+    a.page_shift = log2i(p->page_size);
+    a.num_heads = p->num_kv_heads;
+    a.head_dim = p->head_dim;
+    a.gscale = (double)p->global_scale;
+    return a;
+  };
+  QuantArgs ka, va;
+  if (do_k) ka = qa(k_src, k_stride_token, k_stride_head, k_pool);
+  if (do_v) va = qa(v_src, v_stride_token, v_stride_head, v_pool);
+  hipError_t e = launch_quantize(do_k ? &ka : nullptr, do_v ? &va : nullptr, n_tokens,
+                                 slot_mapping, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(NVFP4_E_HIP, "quantize launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,294 @@
+// One 32-token step of paged NVFP4 attention for one wave, shared by the decode and
+// prefill kernels.
+//
+// Layout (gfx950 wave64, 16x16x32 fp16 MFMA; lane l = 16j + n):
+//   * S^T = K Q^T: K rows (tokens) on M, query rows on N.  Two token tiles per step:
+//     tile A row m is token 8*(m/4) + m%4 of the step, tile B row m is that token + 4.
+//     The accumulator layout (lane (j, n) holds rows 4j..4j+3 of column n) then gives
+//     lane (j, n) the scores of tokens 8j..8j+7 for query row n.
+//   * O^T += V^T P^T: value dims on M, tokens on K, query rows on N.  Lane (j, n)'s
+//     k-slots are tokens 8j..8j+7, the same tokens it holds scores for, so P needs no
+//     lane exchange.  Lane (j, m) reads for those 8 tokens the m-th 1/16 slice of the
+//     V row; nibble e of the slice is value dim m*DV/16 + e and feeds PV tile e.
+//   * The K contraction runs over each lane's contiguous quarter row: k-step s takes
+//     dword s of the quarter row; Q is laid out with the same (lane, slot) order.
+// Page sources: [XQA] "Support NVFP4 KV cache decode on SM120" (packed K/V and scale
+// factors streamed from a page table); [PF] "Re-enable split-KV for NVFP4 KV cache in
+// prefill path" (K and V through independent strides).
+#pragma once
+
+#include "fp4_common.h"
+#include "internal.h"
+
+namespace nvfp4 {
+
+template <int DK, int DV>
+struct StepShape {
+  static constexpr int NS = DK / 32;     // QK k-steps; also dwords of a lane's K quarter-row
+  static constexpr int KB = DK / 8;      // K bytes per lane per token
+  static constexpr int KSF = DK / 64;    // K scale bytes per lane per token
+  static constexpr int KSFW = (KSF + 3) / 4;
+  static constexpr int KPAIRS = (KSF + 1) / 2;
+  static constexpr int VB = DV / 32;     // V bytes per lane per token
+  static constexpr int VW = (VB + 3) / 4;
+  static constexpr int NT = DV / 16;     // PV tiles
+  static constexpr int VSFB = DV >= 512 ? 2 : 1;  // V scale bytes per lane per token
+  static constexpr int QW = DK / 8;      // dwords of a lane's bf16 Q quarter-row
+};
+
+template <int DK, int DV>
+struct StepRaw {
+  using S = StepShape<DK, DV>;
+  uint32_t ka[S::NS], kb[S::NS];
+  uint32_t ksa[S::KSFW], ksb[S::KSFW];
+  uint32_t vd[8][S::VW];
+  uint32_t vs[8];
+};
+
+// Per-wave view of one request's K/V pools for one kv head.
+template <int DK, int DV, bool PAGE16>
+struct PagedView {
+  using S = StepShape<DK, DV>;
+  const int32_t* pt_row;
+  int page_shift, page_mask, num_pages;
+  const uint8_t* kdat;
+  const uint8_t* ksf;
+  const uint8_t* vdat;
+  const uint8_t* vsf;
+  int64_t k_page, k_tok, ksf_page, ksf_tok, v_page, v_tok, vsf_page, vsf_tok;
+  int j, n;
+  uint32_t bad;
+
+  __device__ __forceinline__ void init(const AttnArgs& a, int b, int kvh, int lane) {
+    j = lane >> 4;
+    n = lane & 15;
+    pt_row = a.page_table + (int64_t)b * a.pt_stride;
+    page_shift = a.page_shift;
+    page_mask = (1 << a.page_shift) - 1;
+    num_pages = a.k.num_pages;
+    kdat = a.k.data + (int64_t)kvh * a.k.s_head + j * S::KB;
+    ksf = a.k.sf + (int64_t)kvh * a.k.sf_head + j * S::KSF;
+    vdat = a.v.data + (int64_t)kvh * a.v.s_head + n * S::VB;
+    vsf = a.v.sf + (int64_t)kvh * a.v.sf_head + (n * DV / 16) / 16;
+    k_page = a.k.s_page; k_tok = a.k.s_tok; ksf_page = a.k.sf_page; ksf_tok = a.k.sf_tok;
+    v_page = a.v.s_page; v_tok = a.v.s_tok; vsf_page = a.v.sf_page; vsf_tok = a.v.sf_tok;
+    bad = 0;
+  }
+
+  __device__ __forceinline__ int page_of(int t) {
+    int pg = pt_row[t >> page_shift];
+    if ((unsigned)pg >= (unsigned)num_pages) {
+      bad = 1;
+      pg = 0;
+    }
+    return pg;
+  }
+
+  // Raw bytes of the step starting at token t0 (a multiple of 16); tokens past tlast are
+  // clamped to tlast so that every read stays inside the request's pages.
+  __device__ __forceinline__ void load(StepRaw<DK, DV>& r, int t0, int tlast) {
+    const int ta = min(t0 + 8 * (n >> 2) + (n & 3), tlast);
+    const int tb = min(t0 + 8 * (n >> 2) + (n & 3) + 4, tlast);
+    int pga, pgb, pgv[8], tv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tv[i] = min(t0 + 8 * j + i, tlast);
+    if constexpr (PAGE16) {
+      const int pg0 = page_of(t0);
+      const int pg1 = page_of(min(t0 + 16, tlast));
+      pga = (ta - t0) < 16 ? pg0 : pg1;
+      pgb = (tb - t0) < 16 ? pg0 : pg1;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pgv[i] = (tv[i] - t0) < 16 ? pg0 : pg1;
+    } else {
+      pga = page_of(ta);
+      pgb = page_of(tb);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pgv[i] = page_of(tv[i]);
+    }
+    load_bytes<S::KB>(kdat + (int64_t)pga * k_page + (int64_t)(ta & page_mask) * k_tok, r.ka);
+    load_bytes<S::KB>(kdat + (int64_t)pgb * k_page + (int64_t)(tb & page_mask) * k_tok, r.kb);
+    load_bytes<S::KSF>(ksf + (int64_t)pga * ksf_page + (int64_t)(ta & page_mask) * ksf_tok, r.ksa);
+    load_bytes<S::KSF>(ksf + (int64_t)pgb * ksf_page + (int64_t)(tb & page_mask) * ksf_tok, r.ksb);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      load_bytes<S::VB>(vdat + (int64_t)pgv[i] * v_page + (int64_t)(tv[i] & page_mask) * v_tok,
+                        r.vd[i]);
+      load_bytes<S::VSFB>(vsf + (int64_t)pgv[i] * vsf_page + (int64_t)(tv[i] & page_mask) * vsf_tok,
+                          &r.vs[i]);
+    }
+  }
+};
+
+// Q quarter-row of one query row as fp16 MFMA operands, prescaled by a power of two
+// that puts the row's largest magnitude in [2^14, 2^15) (exact for bf16 inputs in
+// fp16's range).  Returns the factor that undoes the prescale on the scores.
+template <int DK>
+__device__ __forceinline__ float load_q_operand(const uint16_t* qrow, bool valid, int j,
+                                                f16x8 (&qf)[DK / 32]) {
+  constexpr int QW = DK / 8;
+  uint32_t qraw[QW];
+  if (valid) {
+    load_bytes<DK / 2>(reinterpret_cast<const uint8_t*>(qrow + j * (DK / 4)), qraw);
+  } else {
+#pragma unroll
+    for (int i = 0; i < QW; ++i) qraw[i] = 0u;
+  }
+  float qmax = 0.f;
+#pragma unroll
+  for (int i = 0; i < QW; ++i)
+    qmax = fmaxf(qmax, fmaxf(fabsf(bf16f(qraw[i] & 0xFFFF)), fabsf(bf16f(qraw[i] >> 16))));
+  qmax = max_over_groups(qmax);
+  int qexp = 0;
+  if (qmax > 0.f) (void)frexpf(qmax, &qexp);
+  const float qmul = ldexpf(1.f, 15 - qexp);
+#pragma unroll
+  for (int s = 0; s < DK / 32; ++s) {
+    f16x2 p[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t w = qraw[4 * s + t];
+      p[t] = f16x2{(_Float16)(bf16f(w & 0xFFFF) * qmul), (_Float16)(bf16f(w >> 16) * qmul)};
+    }
+    qf[s] = pack8(p[0], p[1], p[2], p[3]);
+  }
+  return ldexpf(1.f, qexp - 15);
+}
+
+// Dequantised K operands of the two token tiles of a step.
+template <int DK, int DV>
+__device__ __forceinline__ void k_operands(const StepRaw<DK, DV>& r, f16x8 (&ka)[DK / 32],
+                                           f16x8 (&kb)[DK / 32]) {
+  using S = StepShape<DK, DV>;
+  f16x2 kpa[S::KPAIRS], kpb[S::KPAIRS];
+#pragma unroll
+  for (int w = 0; w < S::KPAIRS; ++w) {
+    kpa[w] = (w & 1) ? fp8x2_to_f16<true>(r.ksa[w >> 1]) : fp8x2_to_f16<false>(r.ksa[w >> 1]);
+    kpb[w] = (w & 1) ? fp8x2_to_f16<true>(r.ksb[w >> 1]) : fp8x2_to_f16<false>(r.ksb[w >> 1]);
+  }
+#pragma unroll
+  for (int s = 0; s < S::NS; ++s) {
+    const int bi = s >> 1;  // scale byte of this dword within the lane's quarter-row
+    const f16x2 sca = (bi & 1) ? splat_hi(kpa[bi >> 1]) : splat_lo(kpa[bi >> 1]);
+    const f16x2 scb = (bi & 1) ? splat_hi(kpb[bi >> 1]) : splat_lo(kpb[bi >> 1]);
+    ka[s] = dequant8(r.ka[s], sca);
+    kb[s] = dequant8(r.kb[s], scb);
+  }
+}
+
+// Dequantised V^T operands of a step: vt[e] holds value dim m*DV/16 + e (m = lane%16)
+// for tokens 8j..8j+7.  Tokens after tlast get scale 0 (their bytes may be anything).
+template <int DK, int DV>
+__device__ __forceinline__ void v_operands(const StepRaw<DK, DV>& r, int t0, int tlast, int j,
+                                           f16x8 (&vt)[DV / 16]) {
+  using S = StepShape<DK, DV>;
+  uint32_t sw[S::VSFB][2];
+#pragma unroll
+  for (int h = 0; h < S::VSFB; ++h) {
+    uint32_t bytes[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      bytes[i] = (t0 + 8 * j + i > tlast) ? 0u : ((r.vs[i] >> (8 * h)) & 0xFF);
+    sw[h][0] = bytes[0] | (bytes[1] << 8) | (bytes[2] << 16) | (bytes[3] << 24);
+    sw[h][1] = bytes[4] | (bytes[5] << 8) | (bytes[6] << 16) | (bytes[7] << 24);
+  }
+  f16x2 vp[S::NT][4];
+#pragma unroll
+  for (int q = 0; q < S::VW; ++q) {
+    const int h = (q * 8) / 16 < S::VSFB ? (q * 8) / 16 : 0;  // scale block of this dword
+    const f16x2 sp[4] = {fp8x2_to_f16<false>(sw[h][0]), fp8x2_to_f16<true>(sw[h][0]),
+                         fp8x2_to_f16<false>(sw[h][1]), fp8x2_to_f16<true>(sw[h][1])};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t w0 = r.vd[2 * p][q];
+      const uint32_t w1 = r.vd[2 * p + 1][q];
+      // byte k of lo: nibble 2k of token 2p (low) and of token 2p+1 (high); hi: nibble 2k+1
+      const uint32_t lo = (w0 & 0x0F0F0F0Fu) | ((w1 << 4) & 0xF0F0F0F0u);
+      const uint32_t hi = ((w0 >> 4) & 0x0F0F0F0Fu) | (w1 & 0xF0F0F0F0u);
+      constexpr int NB = S::VB < 4 ? S::VB : 4;  // bytes of the slice in this dword
+      if constexpr (NB > 0) { vp[8 * q + 0][p] = fp4x2_to_f16<0>(lo) * sp[p]; vp[8 * q + 1][p] = fp4x2_to_f16<0>(hi) * sp[p]; }
+      if constexpr (NB > 1) { vp[8 * q + 2][p] = fp4x2_to_f16<1>(lo) * sp[p]; vp[8 * q + 3][p] = fp4x2_to_f16<1>(hi) * sp[p]; }
+      if constexpr (NB > 2) { vp[8 * q + 4][p] = fp4x2_to_f16<2>(lo) * sp[p]; vp[8 * q + 5][p] = fp4x2_to_f16<2>(hi) * sp[p]; }
+      if constexpr (NB > 3) { vp[8 * q + 6][p] = fp4x2_to_f16<3>(lo) * sp[p]; vp[8 * q + 7][p] = fp4x2_to_f16<3>(hi) * sp[p]; }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < S::NT; ++e) vt[e] = pack8(vp[e][0], vp[e][1], vp[e][2], vp[e][3]);
+}
+
+// Online-softmax state of one 16-row group (base-2 scores).
+template <int NT>
+struct RowState {
+  f32x4 acc[NT];
+  float m, l;
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int e = 0; e < NT; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m = -INFINITY;
+    l = 0.f;
+  }
+
+  // Scores of tokens t0 + 8j + i (i < 8) for this lane's row: sa (i < 4), sb (i >= 4).
+  // Keys after `last` are masked.  Returns the P operand.
+  __device__ __forceinline__ f16x8 softmax(f32x4 sa, f32x4 sb, float c, int t0, int j, int last) {
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = sa[i] * c;
+      x[4 + i] = sb[i] * c;
+    }
+    float bm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (t0 + 8 * j + i > last) x[i] = -INFINITY;
+      bm = fmaxf(bm, x[i]);
+    }
+    bm = max_over_groups(bm);
+    const float m_new = fmaxf(m, bm);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m - m_use);
+    float psum = 0.f;
+    f16x2 pp[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p0 = fast_exp2(x[2 * i] - m_use);
+      const float p1 = fast_exp2(x[2 * i + 1] - m_use);
+      psum += p0 + p1;
+      pp[i] = f16x2{(_Float16)p0, (_Float16)p1};
+    }
+    l = l * alpha + psum;
+    m = m_new;
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int e = 0; e < NT; ++e) acc[e] *= alpha;
+    }
+    return pack8(pp[0], pp[1], pp[2], pp[3]);
+  }
+
+  __device__ __forceinline__ void pv(const f16x8 (&vt)[NT], f16x8 p) {
+#pragma unroll
+    for (int e = 0; e < NT; ++e) acc[e] = mfma16x16x32(vt[e], p, acc[e]);
+  }
+
+  // Normalise and store this lane's part of the row: value dims (4j+i)*NT + e.
+  // Row sums are completed over the four lanes of the row first.
+  __device__ __forceinline__ void store(float* dst, float* lse_dst, bool valid, bool bad,
+                                        float out_scale, int j) {
+    const float l_tot = sum_over_groups(l);
+    const bool empty = !(l_tot > 0.f);
+    const float inv = bad ? NAN : (empty ? 0.f : out_scale / l_tot);
+    const float lse_v =
+        bad ? NAN : (empty ? -INFINITY : (m + fast_log2(l_tot)) * 0.69314718055994531f);
+    if (!valid) return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float4* row = reinterpret_cast<float4*>(dst + (4 * j + i) * NT);
+#pragma unroll
+      for (int e = 0; e < NT; e += 4)
+        row[e / 4] = make_float4(acc[e][i] * inv, acc[e + 1][i] * inv, acc[e + 2][i] * inv,
+                                 acc[e + 3][i] * inv);
+    }
+    if (j == 0) *lse_dst = lse_v;
+  }
+};
+
+}  // namespace nvfp4

@@ -1,0 +1,109 @@
+// Internal declarations shared by the host library and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nvfp4_attn.h"
+
+namespace nvfp4 {
+
+// Work-item record: eight int32 fields (see nvfp4_plan_get_work).
+enum WorkField {
+  W_REQ = 0,    // request index b
+  W_KVH = 1,    // kv head
+  W_ROW0 = 2,   // first qo head within the group (decode) / first query row of the tile (prefill)
+  W_ROWS = 3,   // qo heads (decode) / query rows (prefill) covered
+  W_KV0 = 4,    // first key of the chunk
+  W_KV1 = 5,    // one past the last key of the chunk
+  W_SLOT = 6,   // partial slot, or -1 when the item owns the whole row range
+  W_MERGE = 7,  // merge entry, or -1
+};
+constexpr int kWorkFields = 8;
+
+// Merge record: {req, kv_head, row0, rows, first_partial, num_parts, 0, 0}.
+constexpr int kMergeFields = 8;
+
+// Decode: one wave handles at most this many qo heads of one kv head.
+constexpr int kDecodeHeads = 16;
+// Tokens one decode wave consumes per step (two 16-row MFMA tiles).
+constexpr int kDecodeStep = 32;
+
+struct PoolArgs {
+  const uint8_t* data;
+  int64_t s_page, s_head, s_tok;
+  const uint8_t* sf;
+  int64_t sf_page, sf_head, sf_tok;
+  int32_t num_pages;
+};
+
+struct AttnArgs {
+  const uint16_t* q;        // bf16 bits
+  int64_t q_s_row, q_s_head;
+  const int32_t* page_table;
+  int64_t pt_stride;
+  PoolArgs k, v;
+  float score_scale;        // sm_scale * log2(e) * global_scale(K)
+  float out_scale;          // global_scale(V)
+  const int32_t* work;      // device work records
+  int32_t n_work;
+  const int32_t* qo_indptr; // device, [batch + 1] (prefill)
+  const int32_t* kv_lens;   // device, [batch]
+  float* o;
+  int64_t o_s_row, o_s_head;
+  float* lse;               // [rows, num_qo_heads]
+  float* part_o;            // [slots, rows_per_slot, head_dim_vo]
+  float* part_lse;          // [slots, rows_per_slot]
+  int32_t num_qo_heads;
+  int32_t group;            // qo heads per kv head
+  int32_t page_shift;       // log2(page_size)
+  int32_t rows_per_slot;
+  int32_t causal;
+};
+
+struct MergeArgs {
+  const int32_t* merges;
+  int32_t n_merges;
+  const float* part_o;
+  const float* part_lse;
+  int32_t rows_per_slot;
+  int32_t head_dim;
+  float* o;
+  int64_t o_s_row, o_s_head;
+  float* lse;
+  int32_t num_qo_heads;
+  int32_t group;
+  int32_t prefill;
+  const int32_t* qo_indptr;
+};
+
+struct QuantArgs {
+  const uint16_t* src;      // bf16 bits
+  int64_t s_tok, s_head;    // elements
+  uint8_t* data;
+  int64_t d_page, d_head, d_tok;
+  uint8_t* sf;
+  int64_t sf_page, sf_head, sf_tok;
+  int64_t num_slots;        // num_pages * page_size
+  int32_t page_shift;
+  int32_t num_heads;
+  int32_t head_dim;
+  double gscale;
+};
+
+// Launchers (defined in the .hip files).  Return the hipGetLastError() status of the launch.
+hipError_t launch_quantize(const QuantArgs* k, const QuantArgs* v, int64_t n_tokens,
+                           const int64_t* slots, hipStream_t stream);
+hipError_t launch_decode(int dk, int dv, int page_shift, const AttnArgs& a, hipStream_t stream);
+bool decode_supported(int dk, int dv);
+hipError_t launch_prefill(int dk, int dv, int page_shift, const AttnArgs& a, int rows_per_item,
+                          hipStream_t stream);
+bool prefill_supported(int dk, int dv);
+int prefill_rows_per_item(int dk, int dv, int group);
+size_t prefill_lds_bytes(int dk, int dv);
+hipError_t launch_merge_partials(const MergeArgs& m, hipStream_t stream);
+hipError_t launch_merge_states(const float* o_parts, const float* lse_parts, int64_t rows,
+                               int32_t num_parts, int32_t heads, int32_t head_dim, float* o,
+                               float* lse, hipStream_t stream);
+
+}  // namespace nvfp4

@@ -1,0 +1,64 @@
+"""Device-side set-up of a paged NVFP4 cache for a synthetic workload.
+
+Draws the workload's Q/K/V on the device, allocates separate K and V pools (with
+their scale pools) in the requested layout, fills every slot with random bytes and
+NaN scales, then writes each request's tokens with ``quantize_kv``.  Used by the
+benchmark and by the full-size tests.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import KVPool, Plan, quantize_kv, synth
+
+
+@dataclasses.dataclass
+class PagedCase:
+    w: synth.Workload
+    q: torch.Tensor
+    k: torch.Tensor          # bf16 source rows (kept for sampling by tests)
+    v: torch.Tensor
+    k_pool: KVPool
+    v_pool: KVPool
+    page_table: torch.Tensor
+    page_table_np: np.ndarray
+    slots: torch.Tensor
+    qo_indptr: np.ndarray
+
+
+def poison_pool(pool: KVPool, seed: int) -> None:
+    g = torch.Generator(device=pool.data.device)
+    g.manual_seed(seed)
+    pool.data.copy_(torch.randint(0, 256, pool.data.shape, generator=g, dtype=torch.uint8,
+                                  device=pool.data.device))
+    pool.sf.fill_(synth.SF_POISON)
+
+
+def build_case(w: synth.Workload, device="cuda", layout="HND", poison=True,
+               keep_sources=True) -> PagedCase:
+    q, k, v = synth.draw_qkv(w, device=device)
+    k_pool = KVPool.empty(w.pool_pages, w.num_kv_heads, w.page_size, w.head_dim_qk, layout, device)
+    v_pool = KVPool.empty(w.pool_pages, w.num_kv_heads, w.page_size, w.head_dim_vo, layout, device)
+    if poison:
+        poison_pool(k_pool, w.value_seed + 11)
+        poison_pool(v_pool, w.value_seed + 12)
+    pt = synth.page_table(w)
+    slots = torch.from_numpy(synth.token_slots(w, pt)).to(device)
+    quantize_kv(k, v, slots, k_pool, v_pool)
+    ind = synth.indptr(w.qo_lens)
+    if not keep_sources:
+        k = v = None
+    return PagedCase(w, q, k, v, k_pool, v_pool, torch.from_numpy(pt).to(device), pt, slots, ind)
+
+
+def make_plan(case: PagedCase, num_cus: int = 0, kv_chunk_tokens: Optional[int] = None) -> Plan:
+    w = case.w
+    chunk = w.kv_chunk_tokens if kv_chunk_tokens is None else kv_chunk_tokens
+    return Plan(w.kv_lens, num_qo_heads=w.num_qo_heads, num_kv_heads=w.num_kv_heads,
+                head_dim_qk=w.head_dim_qk, head_dim_vo=w.head_dim_vo, page_size=w.page_size,
+                qo_indptr=None if w.decode else case.qo_indptr.tolist(), causal=w.causal,
+                kv_chunk_tokens=chunk, num_cus=num_cus)

@@ -1,0 +1,228 @@
+/*
+ * nvfp4_attn.h -- C ABI for batched attention over a paged KV cache stored as
+ * NVFP4, on AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages; cited by title and section):
+ *   [PF]  "Re-enable split-KV for NVFP4 KV cache in prefill path"
+ *         (jethac/flashinfer pull request 1, a series of commit messages)
+ *   [XQA] "Support NVFP4 KV cache decode on SM120"
+ *         (flashinfer-ai/flashinfer pull request 2520)
+ *   [FIX] "fix(attention): correct SM120 NVFP4 qk_correction layout, row-sum
+ *         reduction, and lse" (flashinfer-ai/flashinfer pull request 3838)
+ *
+ * Storage format ([PF] commit "Gate split-KV off when kv_data_type is NVFP4";
+ * [XQA] changelog): every K or V row of one token and one kv head is packed
+ * uint8, two e2m1 values per byte (element 2j in the low nibble of byte j,
+ * element 2j+1 in the high nibble), with one FP8 e4m3fn scale byte per 16
+ * consecutive head-dim elements.  dequantised value = e2m1 * e4m3 * global_scale.
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers named "device" are device memory the caller owns (for example
+ *     allocated through PyTorch).  The library never allocates device memory and
+ *     never frees caller memory.  Pointers named "host" are host memory.
+ *   - Every call that takes `stream` (a hipStream_t; NULL = the null stream) is
+ *     asynchronous on that stream unless stated otherwise.
+ *   - All strides are in the units stated next to them (bytes for the packed
+ *     pools, elements for bf16 and fp32 tensors).
+ *   - A call that returns anything but NVFP4_OK has launched nothing and written
+ *     no output ([PF] commit "Re-enable split-KV...": reject a configuration
+ *     cleanly instead of failing later).  nvfp4_last_error() then names the
+ *     offending argument.
+ *   - Kernels treat a page-table entry outside [0, num_pages) as corrupt input:
+ *     they read nothing through it and write NaN to the affected output rows.
+ */
+#ifndef NVFP4_ATTN_H
+#define NVFP4_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NVFP4_OK = 0,
+  NVFP4_E_INVALID = 1,     /* an argument has an invalid value (null pointer, bad size) */
+  NVFP4_E_SHAPE = 2,       /* shapes, strides or alignment inconsistent; plan/run mismatch */
+  NVFP4_E_UNSUPPORTED = 3, /* head dim, group size or page size outside the supported set */
+  NVFP4_E_LDS_BUDGET = 4,  /* a kernel tile for this shape does not fit in LDS */
+  NVFP4_E_WORKSPACE = 5,   /* workspace null, too small, misaligned or not uploaded */
+  NVFP4_E_DEVICE = 6,      /* current device is not gfx950 */
+  NVFP4_E_HIP = 7          /* a HIP runtime call failed */
+} nvfp4_status;
+
+/* Text of the last error on the calling thread ("" if none).  Never NULL. */
+const char* nvfp4_last_error(void);
+
+/* Library version string. */
+const char* nvfp4_version(void);
+
+/*
+ * One paged pool: K or V.  K and V have independent pools and independent stride
+ * families ([PF] commits on unequal K/V strides: "support-or-reject" contract; this
+ * library supports them on every path).  Byte address of packed row
+ * (page p, kv head h, token slot t) = data + p*stride_page + h*stride_head +
+ * t*stride_token; that row holds head_dim/2 bytes.  Its scale row (head_dim/16
+ * bytes) starts at sf + p*sf_stride_page + h*sf_stride_head + t*sf_stride_token.
+ * HND and NHD layouts are both expressed through these strides ([XQA] changelog:
+ * scale tensors follow the data layout; container strides count bytes).
+ * Alignment: data and every data stride must be multiples of 16 bytes when
+ * head_dim >= 128, of head_dim/8 bytes otherwise; sf and every sf stride multiples
+ * of min(head_dim/16, 8) bytes.
+ */
+typedef struct {
+  void* data;              /* device, packed e2m1 pairs (uint8) */
+  int64_t stride_page;     /* bytes */
+  int64_t stride_head;     /* bytes */
+  int64_t stride_token;    /* bytes */
+  void* sf;                /* device, e4m3fn scale bytes; required ([PF] last commit: scales
+                              are required for NVFP4; [XQA] review: assert scales present) */
+  int64_t sf_stride_page;  /* bytes */
+  int64_t sf_stride_head;  /* bytes */
+  int64_t sf_stride_token; /* bytes */
+  int32_t num_pages;       /* pages in the pool; page-table entries must be < num_pages */
+  int32_t page_size;       /* tokens per page: a power of two, 1..256 */
+  int32_t num_kv_heads;
+  int32_t head_dim;        /* 64, 128, 256 or 512 */
+  float global_scale;      /* > 0; multiplies every dequantised value */
+} nvfp4_kv_pool;
+
+/*
+ * Append (quantise and scatter) K and V rows into their pools ([PF] commit on
+ * unequal strides: bf16 sources quantised by the in-tree NVFP4 KV quantisation
+ * kernel; [XQA] changelog: to_nvfp4 with a global scale).
+ *   k_src, v_src: device bf16 [n_tokens, num_kv_heads, head_dim] with the given
+ *     element strides (the last dimension is contiguous and 16-byte aligned).
+ *     Either (src, pool) pair may be NULL to quantise only the other.
+ *   slot_mapping: device int64 [n_tokens]; token i goes to page slot/page_size,
+ *     in-page slot slot%page_size.  A negative slot skips the token; a slot at or
+ *     past num_pages*page_size is skipped too.
+ * Per 16-element block: s = RNE_e4m3(amax / (6*g)) saturated to 448; element code =
+ * RNE_e2m1(|x| / (s*g)), ties to the even code, saturated to 6, sign bit copied
+ * from x; s == 0 gives magnitude code 0.  Decisions are exact (no rounding of the
+ * quotients affects them).  Inputs must be finite.
+ */
+nvfp4_status nvfp4_quantize_kv(const void* k_src, int64_t k_stride_token, int64_t k_stride_head,
+                               const void* v_src, int64_t v_stride_token, int64_t v_stride_head,
+                               int64_t n_tokens, const int64_t* slot_mapping,
+                               const nvfp4_kv_pool* k_pool, const nvfp4_kv_pool* v_pool,
+                               void* stream);
+
+/*
+ * Plan: host-only partition of one batch's attention into work items
+ * ([PF] commit "Gate split-KV off...", follow-up: split the KV range with
+ * 16-token-aligned chunk boundaries; plan()/run() split of the prefill wrappers;
+ * [PF] commits on the smem probe: plan rejects tiles that do not fit).
+ *   kv_lens:   host int32 [batch], total keys of each request (>= 0).
+ *   qo_indptr: host int32 [batch+1] ragged query offsets for prefill, or NULL for
+ *              decode (one query per request).  Prefill requires q_b <= kv_len_b.
+ *   causal:    prefill only: query row i of request b sees keys
+ *              j <= i + kv_len_b - q_b (bottom-right aligned, prefix extend).
+ *   kv_chunk_tokens: 0 = choose the split to fill the device; < 0 = never split;
+ *              otherwise a multiple of 16: split every request's KV range into
+ *              chunks of that many tokens.  Every chunk boundary except the end of
+ *              a request is a multiple of 16 tokens.
+ *   num_cus:   compute units to fill; 0 = query the current device (256 if none).
+ * The plan owns host memory only.  It is immutable after creation, except for the
+ * record of the workspace it was last uploaded to.
+ */
+typedef struct nvfp4_plan nvfp4_plan;
+
+nvfp4_status nvfp4_plan_create(const int32_t* kv_lens, const int32_t* qo_indptr, int32_t batch,
+                               int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim_qk,
+                               int32_t head_dim_vo, int32_t page_size, int32_t causal,
+                               int32_t kv_chunk_tokens, int32_t num_cus, nvfp4_plan** out);
+
+void nvfp4_plan_destroy(nvfp4_plan* plan);
+
+/* Device workspace bytes the runs of this plan need (256-byte aligned). */
+size_t nvfp4_plan_workspace_bytes(const nvfp4_plan* plan);
+
+typedef struct {
+  int32_t num_work_items;  /* kernel work items (one wave or workgroup each) */
+  int32_t num_partials;    /* partial (O, LSE) slots written by split work items */
+  int32_t num_merges;      /* row groups merged from partials */
+  int32_t kv_chunk_tokens; /* chunk length used (0 when nothing is split) */
+  int32_t rows_per_item;   /* query rows x heads covered by one work item (upper bound) */
+  int32_t is_prefill;
+  int64_t workspace_bytes;
+} nvfp4_plan_info;
+
+nvfp4_status nvfp4_plan_get_info(const nvfp4_plan* plan, nvfp4_plan_info* info);
+
+/*
+ * Copy the work items as int32 records of 8 fields into host memory `out`
+ * (capacity in records): {request, kv_head, row_begin, row_count, kv_begin,
+ * kv_end, partial_slot (-1 = written directly), merge_index (-1 = none)}.
+ * row_begin/row_count count qo heads within the group (decode) or query rows
+ * (prefill).  For tests and tools.
+ */
+nvfp4_status nvfp4_plan_get_work(const nvfp4_plan* plan, int32_t* out, int64_t capacity);
+
+/*
+ * Copy the plan's tables into the workspace (device, >= workspace_bytes, 256-byte
+ * aligned) and wait for the copy to finish.  Runs must use a workspace the plan
+ * was uploaded to; distinct concurrent runs need distinct workspaces.
+ */
+nvfp4_status nvfp4_plan_upload(nvfp4_plan* plan, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
+ * Decode: one query per request ([XQA] walkthrough: xqa(q, k_cache, v_cache,
+ * k_sf_cache, v_sf_cache, page_table, seq_lens, output); [PF] commit on decode
+ * strides: K and V addressed through their own strides).
+ *   q: device bf16 [batch, num_qo_heads, head_dim_qk], element strides
+ *      (last dim contiguous, 16-byte aligned rows).
+ *   page_table: device int32 [batch, pt_stride]; entry (b, i) is the page of
+ *      tokens [i*page_size, (i+1)*page_size) of request b.
+ *   o: device fp32 [batch, num_qo_heads, head_dim_vo] with element strides
+ *      (last dim contiguous, 16-byte aligned rows) -- the output is sized by
+ *      head_dim_vo ([PF] commits "output sized by VO" / out_head_dim gate).
+ *   lse: device fp32 [batch, num_qo_heads] contiguous, natural log, always written
+ *      ([PF] commit zeroing lse; [FIX] second commit: ln-sum-exp of the scaled
+ *      scores).  A request with kv_len 0 gets O = 0 and LSE = -inf.
+ * Split work items write partial states into the workspace; a merge kernel on the
+ * same stream then combines them by LSE ([XQA] changelog: mergeAndSaveOutTile).
+ */
+nvfp4_status nvfp4_batch_decode(const nvfp4_plan* plan, const void* q, int64_t q_stride_req,
+                                int64_t q_stride_head, const int32_t* page_table, int64_t pt_stride,
+                                const nvfp4_kv_pool* k_pool, const nvfp4_kv_pool* v_pool,
+                                float sm_scale, void* workspace, size_t workspace_bytes, float* o,
+                                int64_t o_stride_req, int64_t o_stride_head, float* lse,
+                                void* stream);
+
+/*
+ * Prefill / extend over the paged cache ([PF] commits on asymmetric heads and
+ * "Gate split-KV off...": prefix-cache extend, qo_len << kv_len; causal runs).
+ *   q: device bf16 [total_q, num_qo_heads, head_dim_qk] ragged by the plan's
+ *      qo_indptr; o: device fp32 [total_q, num_qo_heads, head_dim_vo];
+ *   lse: device fp32 [total_q, num_qo_heads] contiguous.
+ * Other arguments as for nvfp4_batch_decode.
+ */
+nvfp4_status nvfp4_batch_prefill(const nvfp4_plan* plan, const void* q, int64_t q_stride_tok,
+                                 int64_t q_stride_head, const int32_t* page_table,
+                                 int64_t pt_stride, const nvfp4_kv_pool* k_pool,
+                                 const nvfp4_kv_pool* v_pool, float sm_scale, void* workspace,
+                                 size_t workspace_bytes, float* o, int64_t o_stride_tok,
+                                 int64_t o_stride_head, float* lse, void* stream);
+
+/*
+ * Merge partial attention states by their LSE ([XQA] changelog: merge of the
+ * split-KV partial tiles).
+ *   o_parts: device fp32 [rows, num_parts, heads, head_dim] contiguous;
+ *   lse_parts: device fp32 [rows, num_parts, heads] contiguous (natural log);
+ *   o: device fp32 [rows, heads, head_dim]; lse: device fp32 [rows, heads].
+ * lse = M + ln sum_c exp(lse_c - M), M = max_c lse_c; o = sum_c exp(lse_c - lse) o_c.
+ * Parts with lse = -inf contribute nothing; all -inf gives o = 0, lse = -inf.
+ * head_dim: a multiple of 4, at most 1024.
+ */
+nvfp4_status nvfp4_merge_states(const float* o_parts, const float* lse_parts, int64_t rows,
+                                int32_t num_parts, int32_t heads, int32_t head_dim, float* o,
+                                float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_ATTN_H */

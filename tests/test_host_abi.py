@@ -1,0 +1,136 @@
+"""The C-ABI library loads, exports every symbol the header declares, and rejects bad
+arguments before launching anything (these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import attention_bit_paged_amd as nv
+from attention_bit_paged_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "nvfp4_attn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"\b(nvfp4_[a-z_]+)\s*\(", text)
+
+
+def test_every_declared_symbol_is_exported():
+    names = header_functions()
+    assert len(names) == len(set(names)) == len(_lib.EXPORTS)
+    assert set(names) == set(_lib.EXPORTS)
+    so = ctypes.CDLL(_lib.LIB_PATH)
+    for n in names:
+        assert hasattr(so, n), n
+
+
+def test_version_and_empty_error():
+    assert "gfx950" in nv.version()
+    assert nv.lib.nvfp4_last_error() is not None
+
+
+def test_status_codes_match_header():
+    text = open(os.path.join(ROOT, "include", "nvfp4_attn.h")).read()
+    for name, code in re.findall(r"(NVFP4_(?:OK|E_[A-Z_]+))\s*=\s*(\d+)", text):
+        assert _lib.STATUS[int(code)] == name
+
+
+def _plan_status(**kw):
+    args = dict(kv_lens=[32], num_qo_heads=4, num_kv_heads=1, head_dim_qk=128, num_cus=256)
+    args.update(kw)
+    try:
+        nv.Plan(**args)
+    except nv.NVFP4Error as e:
+        return e.status, str(e)
+    return "NVFP4_OK", ""
+
+
+@pytest.mark.parametrize("kw,status,word", [
+    (dict(num_qo_heads=6, num_kv_heads=4), "NVFP4_E_SHAPE", "multiple"),
+    (dict(head_dim_qk=96), "NVFP4_E_UNSUPPORTED", "head dims"),
+    (dict(head_dim_qk=128, head_dim_vo=256), "NVFP4_E_UNSUPPORTED", "vo <= qk"),
+    (dict(head_dim_qk=512, head_dim_vo=512), "NVFP4_E_LDS_BUDGET", "512"),
+    (dict(page_size=12), "NVFP4_E_UNSUPPORTED", "page_size"),
+    (dict(kv_chunk_tokens=40), "NVFP4_E_INVALID", "multiple of 16"),
+    (dict(kv_lens=[-1]), "NVFP4_E_INVALID", "negative"),
+    (dict(kv_lens=[10], qo_indptr=[0, 11]), "NVFP4_E_SHAPE", "queries"),
+    (dict(kv_lens=[10, 10], qo_indptr=[0, 5, 3]), "NVFP4_E_SHAPE", "non-decreasing"),
+    (dict(num_qo_heads=128, num_kv_heads=1), "NVFP4_E_UNSUPPORTED", "qo heads per kv head"),
+])
+def test_plan_rejections(kw, status, word):
+    st, msg = _plan_status(**kw)
+    assert st == status and word in msg, msg
+
+
+def _fake_pool(head_dim=128, page_size=16, heads=1, pages=8, sf=0x2000, data=0x1000,
+               align_shift=0):
+    row = head_dim // 2
+    return _lib.KVPoolStruct(data + align_shift, pages * 0 + heads * page_size * row, page_size * row,
+                             row, sf, heads * page_size * head_dim // 16, page_size * head_dim // 16,
+                             head_dim // 16, pages, page_size, heads, head_dim, 1.0)
+
+
+def _decode(plan, **over):
+    args = dict(q=0x10000, q_s_row=512, q_s_head=128, pt=0x20000, pt_stride=8,
+                k=_fake_pool(), v=_fake_pool(), sm=0.1, ws=0x40000,
+                ws_bytes=plan.workspace_bytes, o=0x80000, o_s_row=512, o_s_head=128, lse=0x90000)
+    args.update(over)
+    st = nv.lib.nvfp4_batch_decode(plan.handle, args["q"], args["q_s_row"], args["q_s_head"],
+                                   args["pt"], args["pt_stride"], ctypes.byref(args["k"]),
+                                   ctypes.byref(args["v"]), args["sm"], args["ws"], args["ws_bytes"],
+                                   args["o"], args["o_s_row"], args["o_s_head"], args["lse"], None)
+    return _lib.STATUS[st], nv.lib.nvfp4_last_error().decode()
+
+
+def test_run_rejections_never_launch():
+    plan = nv.Plan([100], num_qo_heads=4, num_kv_heads=1, head_dim_qk=128, num_cus=256)
+    cases = [
+        (dict(k=_fake_pool(sf=0)), "NVFP4_E_INVALID", "scale"),
+        (dict(v=_fake_pool(head_dim=64)), "NVFP4_E_SHAPE", "head_dim"),
+        (dict(k=_fake_pool(page_size=32)), "NVFP4_E_SHAPE", "page_size"),
+        (dict(k=_fake_pool(heads=2)), "NVFP4_E_SHAPE", "num_kv_heads"),
+        (dict(k=_fake_pool(align_shift=8)), "NVFP4_E_SHAPE", "multiples"),
+        (dict(q=0x10004), "NVFP4_E_SHAPE", "q rows"),
+        (dict(o_s_head=130), "NVFP4_E_SHAPE", "o rows"),
+        (dict(pt_stride=3), "NVFP4_E_SHAPE", "pt_stride"),
+        (dict(ws=0), "NVFP4_E_WORKSPACE", "NULL"),
+        (dict(ws_bytes=16), "NVFP4_E_WORKSPACE", "needs"),
+        (dict(), "NVFP4_E_WORKSPACE", "uploaded"),   # never uploaded
+        (dict(q=0), "NVFP4_E_INVALID", "q is NULL"),
+        (dict(sm=float("nan")), "NVFP4_E_INVALID", "sm_scale"),
+    ]
+    for over, status, word in cases:
+        st, msg = _decode(plan, **over)
+        assert st == status and word in msg, (over, st, msg)
+
+
+def test_prefill_plan_used_for_decode_is_rejected():
+    plan = nv.Plan([100], qo_indptr=[0, 10], num_qo_heads=4, num_kv_heads=1, head_dim_qk=128,
+                   num_cus=256)
+    st, msg = _decode(plan)
+    assert st == "NVFP4_E_SHAPE" and "prefill" in msg
+
+
+def test_merge_states_rejections():
+    f = nv.lib.nvfp4_merge_states
+    assert _lib.STATUS[f(0x1000, 0x2000, 4, 0, 2, 64, 0x3000, 0x4000, None)] == "NVFP4_E_INVALID"
+    assert _lib.STATUS[f(0x1000, 0x2000, 4, 2, 2, 66, 0x3000, 0x4000, None)] == "NVFP4_E_UNSUPPORTED"
+    assert _lib.STATUS[f(0, 0x2000, 4, 2, 2, 64, 0x3000, 0x4000, None)] == "NVFP4_E_INVALID"
+    assert _lib.STATUS[f(0x1000, 0x2000, 0, 2, 2, 64, 0x3000, 0x4000, None)] == "NVFP4_OK"
+
+
+def test_quantize_rejections():
+    q = nv.lib.nvfp4_quantize_kv
+    k = _fake_pool()
+    st = q(None, 0, 0, None, 0, 0, 4, 0x5000, None, None, None)
+    assert _lib.STATUS[st] == "NVFP4_E_INVALID"
+    st = q(0x10000, 1024, 128, None, 0, 0, 4, 0x5000, ctypes.byref(_fake_pool(sf=0)), None, None)
+    assert _lib.STATUS[st] == "NVFP4_E_INVALID"
+    st = q(0x10002, 1024, 128, None, 0, 0, 4, 0x5000, ctypes.byref(k), None, None)
+    assert _lib.STATUS[st] == "NVFP4_E_SHAPE"
+    st = q(0x10000, 1024, 128, None, 0, 0, 0, 0, ctypes.byref(k), None, None)
+    assert _lib.STATUS[st] == "NVFP4_OK"   # zero tokens: nothing to do
