@@ -10,7 +10,9 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libnvfp4_attn.so")
+# NVFP4_ATTN_LIB selects another build of the same library (for example a copy built
+# with different compile flags); by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("NVFP4_ATTN_LIB") or os.path.join(_HERE, "libnvfp4_attn.so")
 
 STATUS = {
     0: "NVFP4_OK", 1: "NVFP4_E_INVALID", 2: "NVFP4_E_SHAPE", 3: "NVFP4_E_UNSUPPORTED",

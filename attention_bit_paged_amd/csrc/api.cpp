@@ -115,6 +115,11 @@ nvfp4_status check_pool(const nvfp4_kv_pool* p, const char* name, int head_dim,
   if (p->stride_page < 0 || p->stride_head < 0 || p->stride_token < 0 || p->sf_stride_page < 0 ||
       p->sf_stride_head < 0 || p->sf_stride_token < 0)
     return fail(NVFP4_E_SHAPE, "%s strides must be non-negative", name);
+  const int64_t kMaxStride = (int64_t(1) << 31) - 1;  // kernels multiply strides in 32 bits
+  if (p->stride_page > kMaxStride || p->stride_head > kMaxStride || p->stride_token > kMaxStride ||
+      p->sf_stride_page > kMaxStride || p->sf_stride_head > kMaxStride ||
+      p->sf_stride_token > kMaxStride)
+    return fail(NVFP4_E_SHAPE, "%s strides must be below 2^31 bytes", name);
   return NVFP4_OK;
 }
 
@@ -148,8 +153,8 @@ struct nvfp4_plan {
   std::vector<int32_t> kv_lens, qo_indptr;
   int num_partials = 0;
   // workspace layout (byte offsets)
-  size_t off_work = 0, off_merge = 0, off_kvlens = 0, off_indptr = 0, off_part_o = 0,
-         off_part_lse = 0, ws_bytes = 0;
+  size_t off_work = 0, off_merge = 0, off_kvlens = 0, off_indptr = 0,
+         off_part_o = 0, off_part_lse = 0, ws_bytes = 0;
   void* uploaded_to = nullptr;
 };
 
@@ -176,13 +181,13 @@ nvfp4_status nvfp4_plan_create(const int32_t* kv_lens, const int32_t* qo_indptr,
     return fail(NVFP4_E_UNSUPPORTED, "head dims (qk %d, vo %d): each must be 64, 128, 256 or 512",
                 head_dim_qk, head_dim_vo);
   const bool prefill = qo_indptr != nullptr;
+  if (head_dim_qk == 512 && head_dim_vo == 512)
+    return fail(NVFP4_E_LDS_BUDGET,
+                "head dims (512, 512): the per-wave tile does not fit the register file");
   if (prefill ? !prefill_supported(head_dim_qk, head_dim_vo)
               : !decode_supported(head_dim_qk, head_dim_vo))
     return fail(NVFP4_E_UNSUPPORTED, "head dims (qk %d, vo %d) not supported (need vo <= qk)",
                 head_dim_qk, head_dim_vo);
-  if (head_dim_qk == 512 && head_dim_vo == 512)
-    return fail(NVFP4_E_LDS_BUDGET,
-                "head dims (512, 512): the per-wave tile does not fit the register file");
   if (!is_pow2(page_size) || page_size > 256)
     return fail(NVFP4_E_UNSUPPORTED, "page_size %d is not a power of two in [1, 256]", page_size);
   if (kv_chunk_tokens > 0 && kv_chunk_tokens % 16)
@@ -271,28 +276,33 @@ nvfp4_status nvfp4_plan_create(const int32_t* kv_lens, const int32_t* qo_indptr,
     plan->rows_per_slot = tq * group;
   }
 
-  // Chunk length: explicit, never, or chosen so that the work items fill the device.
+  // Chunk length.  Decode: keys per wave; a work item (one workgroup of four waves)
+  // covers four consecutive chunks of a row group, or the whole row split evenly over
+  // its waves when nothing is split.  Prefill: keys per work item.  Explicit, never, or
+  // chosen so that the device is filled: decode aims at 8 waves per CU, prefill at 2
+  // workgroups per CU.
   int chunk = 0;
+  int64_t total = 0;
+  int max_len = 0;
+  for (const auto& g : groups) {
+    total += g.kv_end;
+    max_len = std::max(max_len, g.kv_end);
+  }
+  const int per_item = prefill ? 1 : 4;  // chunks per work item
   if (kv_chunk_tokens > 0) {
     chunk = kv_chunk_tokens;
   } else if (kv_chunk_tokens == 0) {
-    // Items one CU should hold at once: decode items are single waves, prefill items
-    // workgroups of four.
-    const int64_t target = (int64_t)num_cus * (prefill ? 2 : 8);
-    if ((int64_t)groups.size() < target) {
-      int64_t total = 0;
-      int max_len = 0;
-      for (const auto& g : groups) {
-        total += g.kv_end;
-        max_len = std::max(max_len, g.kv_end);
-      }
+    const int64_t target = (int64_t)num_cus * (prefill ? 2 : 8);   // items (prefill) / waves (decode)
+    const int64_t have = (int64_t)groups.size() * (prefill ? 1 : 4);
+    if (have < target) {
       int64_t c = (total + target - 1) / std::max<int64_t>(target, 1);
-      c = std::max<int64_t>(c, prefill ? 128 : 256);
+      c = std::max<int64_t>(c, prefill ? 128 : 64);
       c = (c + 31) / 32 * 32;
-      if (c < max_len) chunk = (int)c;
+      if (c * per_item < max_len) chunk = (int)c;
     }
   }
   plan->chunk = chunk;
+  const int64_t item_span = chunk > 0 ? (int64_t)chunk * per_item : 0;
 
   struct Item {
     int32_t f[kWorkFields];
@@ -303,19 +313,19 @@ nvfp4_status nvfp4_plan_create(const int32_t* kv_lens, const int32_t* qo_indptr,
   int next_slot = 0;
   for (const auto& g : groups) {
     const int L = g.kv_end;
-    const int nchunks = (chunk > 0 && L > chunk) ? (L + chunk - 1) / chunk : 1;
-    if (nchunks == 1) {
+    const int nitems = (item_span > 0 && L > item_span) ? (int)((L + item_span - 1) / item_span) : 1;
+    if (nitems == 1) {
       items.push_back({{g.b, g.kvh, g.row0, g.rows, 0, L, -1, -1}, L});
       continue;
     }
     const int mi = (int)(merges.size() / kMergeFields);
-    const int32_t rec[kMergeFields] = {g.b, g.kvh, g.row0, g.rows, next_slot, nchunks, 0, 0};
+    const int32_t rec[kMergeFields] = {g.b, g.kvh, g.row0, g.rows, next_slot, nitems, 0, 0};
     merges.insert(merges.end(), rec, rec + kMergeFields);
-    for (int c = 0; c < nchunks; ++c) {
-      const int a = c * chunk, e = std::min(L, (c + 1) * chunk);
+    for (int c = 0; c < nitems; ++c) {
+      const int a = (int)(c * item_span), e = (int)std::min<int64_t>(L, (c + 1) * item_span);
       items.push_back({{g.b, g.kvh, g.row0, g.rows, a, e, next_slot + c, mi}, e - a});
     }
-    next_slot += nchunks;
+    next_slot += nitems;
   }
   // Longest first, so the tail of the grid holds the short items.
   std::stable_sort(items.begin(), items.end(),
@@ -325,7 +335,8 @@ nvfp4_status nvfp4_plan_create(const int32_t* kv_lens, const int32_t* qo_indptr,
   plan->merges = std::move(merges);
   plan->num_partials = next_slot;
 
-  // Workspace: [work | merges | kv_lens | qo_indptr | partial O | partial LSE]
+  // Workspace: [work | merges | kv_lens | qo_indptr | partial O | partial LSE]; everything
+  // before the partials is uploaded.
   size_t off = 0;
   plan->off_work = off;
   off = align_up(off + plan->work.size() * sizeof(int32_t));
@@ -416,7 +427,8 @@ nvfp4_status check_run(const nvfp4_plan* plan, bool prefill, const void* q, int6
   if (nvfp4_status st = check_pool(v, "v_pool", plan->head_dim_vo, plan->num_kv_heads,
                                    plan->page_size))
     return st;
-  if (!std::isfinite(sm_scale)) return fail(NVFP4_E_INVALID, "sm_scale is not finite");
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.f))
+    return fail(NVFP4_E_INVALID, "sm_scale must be finite and > 0");
   const bool any_rows = plan->total_q > 0;
   if (any_rows) {
     if (!q) return fail(NVFP4_E_INVALID, "q is NULL");
@@ -476,27 +488,9 @@ AttnArgs make_args(const nvfp4_plan* plan, const void* q, int64_t q_s_row, int64
   a.page_shift = log2i(plan->page_size);
   a.rows_per_slot = plan->rows_per_slot;
   a.causal = plan->causal;
+  a.wave_chunk = plan->prefill ? 0 : plan->chunk;
+  a.merges = reinterpret_cast<const int32_t*>(w + plan->off_merge);
   return a;
-}
-
-MergeArgs make_merge(const nvfp4_plan* plan, const AttnArgs& a, void* ws) {
-  MergeArgs m;
-  std::memset(&m, 0, sizeof(m));
-  m.merges = reinterpret_cast<const int32_t*>(static_cast<uint8_t*>(ws) + plan->off_merge);
-  m.n_merges = (int32_t)(plan->merges.size() / kMergeFields);
-  m.part_o = a.part_o;
-  m.part_lse = a.part_lse;
-  m.rows_per_slot = plan->rows_per_slot;
-  m.head_dim = plan->head_dim_vo;
-  m.o = a.o;
-  m.o_s_row = a.o_s_row;
-  m.o_s_head = a.o_s_head;
-  m.lse = a.lse;
-  m.num_qo_heads = plan->num_qo_heads;
-  m.group = plan->group;
-  m.prefill = plan->prefill;
-  m.qo_indptr = a.qo_indptr;
-  return m;
 }
 
 nvfp4_status run(const nvfp4_plan* plan, bool prefill, const void* q, int64_t q_s_row,
@@ -518,8 +512,9 @@ nvfp4_status run(const nvfp4_plan* plan, bool prefill, const void* q, int64_t q_
   if (e != hipSuccess)
     return fail(NVFP4_E_HIP, "%s launch failed: %s", prefill ? "prefill" : "decode",
                 hipGetErrorString(e));
-  if (!plan->merges.empty()) {
-    e = launch_merge_partials(make_merge(plan, a, ws), s);
+  const int n_merges = (int)(plan->merges.size() / kMergeFields);
+  if (n_merges > 0) {
+    e = launch_merge_partials(a, n_merges, plan->head_dim_vo, plan->prefill, s);
     if (e != hipSuccess) return fail(NVFP4_E_HIP, "merge launch failed: %s", hipGetErrorString(e));
   }
   return ok();

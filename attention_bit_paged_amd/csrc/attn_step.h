@@ -13,7 +13,7 @@
 //   * The K contraction runs over each lane's contiguous quarter row: k-step s takes
 //     dword s of the quarter row; Q is laid out with the same (lane, slot) order.
 // Page sources: [XQA] "Support NVFP4 KV cache decode on SM120" (packed K/V and scale
-// factors streamed from a page table); [PF] "Re-enable split-KV for NVFP4 KV cache in
+// factors streamed through a page table); [PF] "Re-enable split-KV for NVFP4 KV cache in
 // prefill path" (K and V through independent strides).
 #pragma once
 
@@ -21,6 +21,10 @@
 #include "internal.h"
 
 namespace nvfp4 {
+
+// Softmax reference point moves only when a row's maximum exceeds it by this much
+// (base-2 units); until then exp2(x - ref) <= 2^8 and the accumulators stay untouched.
+constexpr float kRescaleSlack = 8.f;
 
 template <int DK, int DV>
 struct StepShape {
@@ -46,6 +50,12 @@ struct StepRaw {
 };
 
 // Per-wave view of one request's K/V pools for one kv head.
+//
+// PAGE16 (page_size >= 16): the two 16-token halves of a step each lie inside one page,
+// so a step needs two page-table entries (uniform, scalar loads) and every lane's byte
+// offset inside a half is fixed for the whole loop.  A half that starts after the
+// last key reuses the first half's page: its reads stay inside a valid page and are
+// masked.  Otherwise (page_size < 16) every token is looked up on its own.
 template <int DK, int DV, bool PAGE16>
 struct PagedView {
   using S = StepShape<DK, DV>;
@@ -56,6 +66,10 @@ struct PagedView {
   const uint8_t* vdat;
   const uint8_t* vsf;
   int64_t k_page, k_tok, ksf_page, ksf_tok, v_page, v_tok, vsf_page, vsf_tok;
+  // PAGE16: lane offsets inside a 16-token half
+  uint32_t ka_off, kb_off, ksa_off, ksb_off;
+  uint32_t v_off[8], vs_off[8];
+  bool k_hi, v_hi;
   int j, n;
   uint32_t bad;
 
@@ -66,17 +80,33 @@ struct PagedView {
     page_shift = a.page_shift;
     page_mask = (1 << a.page_shift) - 1;
     num_pages = a.k.num_pages;
-    kdat = a.k.data + (int64_t)kvh * a.k.s_head + j * S::KB;
-    ksf = a.k.sf + (int64_t)kvh * a.k.sf_head + j * S::KSF;
-    vdat = a.v.data + (int64_t)kvh * a.v.s_head + n * S::VB;
-    vsf = a.v.sf + (int64_t)kvh * a.v.sf_head + (n * DV / 16) / 16;
+    kdat = a.k.data + (int64_t)kvh * a.k.s_head;
+    ksf = a.k.sf + (int64_t)kvh * a.k.sf_head;
+    vdat = a.v.data + (int64_t)kvh * a.v.s_head;
+    vsf = a.v.sf + (int64_t)kvh * a.v.sf_head;
     k_page = a.k.s_page; k_tok = a.k.s_tok; ksf_page = a.k.sf_page; ksf_tok = a.k.sf_tok;
     v_page = a.v.s_page; v_tok = a.v.s_tok; vsf_page = a.v.sf_page; vsf_tok = a.v.sf_tok;
     bad = 0;
+    const int da = 8 * (n >> 2) + (n & 3);  // token of tile A row n inside the step
+    k_hi = da >= 16;
+    v_hi = j >= 2;
+    if constexpr (PAGE16) {
+      const int sa = da & 15, sb = (da + 4) & 15;
+      ka_off = (uint32_t)(sa * k_tok) + j * S::KB;
+      kb_off = (uint32_t)(sb * k_tok) + j * S::KB;
+      ksa_off = (uint32_t)(sa * ksf_tok) + j * S::KSF;
+      ksb_off = (uint32_t)(sb * ksf_tok) + j * S::KSF;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int t = 8 * (j & 1) + i;
+        v_off[i] = (uint32_t)(t * v_tok) + n * S::VB;
+        vs_off[i] = (uint32_t)(t * vsf_tok) + (n * DV / 16) / 16;
+      }
+    }
   }
 
-  __device__ __forceinline__ int page_of(int t) {
-    int pg = pt_row[t >> page_shift];
+  __device__ __forceinline__ int page_of(int idx) {
+    int pg = pt_row[idx];
     if ((unsigned)pg >= (unsigned)num_pages) {
       bad = 1;
       pg = 0;
@@ -84,37 +114,52 @@ struct PagedView {
     return pg;
   }
 
-  // Raw bytes of the step starting at token t0 (a multiple of 16); tokens past tlast are
-  // clamped to tlast so that every read stays inside the request's pages.
+  // Raw bytes of the step starting at token t0 (a multiple of 16).  Keys after tlast
+  // are never used; their reads stay inside the request's pages.
   __device__ __forceinline__ void load(StepRaw<DK, DV>& r, int t0, int tlast) {
-    const int ta = min(t0 + 8 * (n >> 2) + (n & 3), tlast);
-    const int tb = min(t0 + 8 * (n >> 2) + (n & 3) + 4, tlast);
-    int pga, pgb, pgv[8], tv[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) tv[i] = min(t0 + 8 * j + i, tlast);
     if constexpr (PAGE16) {
-      const int pg0 = page_of(t0);
-      const int pg1 = page_of(min(t0 + 16, tlast));
-      pga = (ta - t0) < 16 ? pg0 : pg1;
-      pgb = (tb - t0) < 16 ? pg0 : pg1;
+      const int pg0 = page_of(t0 >> page_shift);
+      const int64_t s0 = t0 & page_mask;
+      const bool h1 = t0 + 16 <= tlast;
+      const int pg1 = h1 ? page_of((t0 + 16) >> page_shift) : pg0;
+      const int64_t s1 = h1 ? ((t0 + 16) & page_mask) : s0;
+      const uint8_t* kb0 = kdat + pg0 * k_page + s0 * k_tok;
+      const uint8_t* kb1 = kdat + pg1 * k_page + s1 * k_tok;
+      const uint8_t* ks0 = ksf + pg0 * ksf_page + s0 * ksf_tok;
+      const uint8_t* ks1 = ksf + pg1 * ksf_page + s1 * ksf_tok;
+      const uint8_t* vb0 = vdat + pg0 * v_page + s0 * v_tok;
+      const uint8_t* vb1 = vdat + pg1 * v_page + s1 * v_tok;
+      const uint8_t* vs0 = vsf + pg0 * vsf_page + s0 * vsf_tok;
+      const uint8_t* vs1 = vsf + pg1 * vsf_page + s1 * vsf_tok;
+      const uint8_t* kb = k_hi ? kb1 : kb0;
+      const uint8_t* ks = k_hi ? ks1 : ks0;
+      const uint8_t* vb = v_hi ? vb1 : vb0;
+      const uint8_t* vs = v_hi ? vs1 : vs0;
+      load_bytes<S::KB>(kb + ka_off, r.ka);
+      load_bytes<S::KB>(kb + kb_off, r.kb);
+      load_bytes<S::KSF>(ks + ksa_off, r.ksa);
+      load_bytes<S::KSF>(ks + ksb_off, r.ksb);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pgv[i] = (tv[i] - t0) < 16 ? pg0 : pg1;
+      for (int i = 0; i < 8; ++i) {
+        load_bytes<S::VB>(vb + v_off[i], r.vd[i]);
+        load_bytes<S::VSFB>(vs + vs_off[i], &r.vs[i]);
+      }
     } else {
-      pga = page_of(ta);
-      pgb = page_of(tb);
+      const int ta = min(t0 + 8 * (n >> 2) + (n & 3), tlast);
+      const int tb = min(t0 + 8 * (n >> 2) + (n & 3) + 4, tlast);
+      const int pga = page_of(ta >> page_shift), pgb = page_of(tb >> page_shift);
+      load_bytes<S::KB>(kdat + pga * k_page + (int64_t)(ta & page_mask) * k_tok + j * S::KB, r.ka);
+      load_bytes<S::KB>(kdat + pgb * k_page + (int64_t)(tb & page_mask) * k_tok + j * S::KB, r.kb);
+      load_bytes<S::KSF>(ksf + pga * ksf_page + (int64_t)(ta & page_mask) * ksf_tok + j * S::KSF, r.ksa);
+      load_bytes<S::KSF>(ksf + pgb * ksf_page + (int64_t)(tb & page_mask) * ksf_tok + j * S::KSF, r.ksb);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pgv[i] = page_of(tv[i]);
-    }
-    load_bytes<S::KB>(kdat + (int64_t)pga * k_page + (int64_t)(ta & page_mask) * k_tok, r.ka);
-    load_bytes<S::KB>(kdat + (int64_t)pgb * k_page + (int64_t)(tb & page_mask) * k_tok, r.kb);
-    load_bytes<S::KSF>(ksf + (int64_t)pga * ksf_page + (int64_t)(ta & page_mask) * ksf_tok, r.ksa);
-    load_bytes<S::KSF>(ksf + (int64_t)pgb * ksf_page + (int64_t)(tb & page_mask) * ksf_tok, r.ksb);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      load_bytes<S::VB>(vdat + (int64_t)pgv[i] * v_page + (int64_t)(tv[i] & page_mask) * v_tok,
-                        r.vd[i]);
-      load_bytes<S::VSFB>(vsf + (int64_t)pgv[i] * vsf_page + (int64_t)(tv[i] & page_mask) * vsf_tok,
-                          &r.vs[i]);
+      for (int i = 0; i < 8; ++i) {
+        const int t = min(t0 + 8 * j + i, tlast);
+        const int pg = page_of(t >> page_shift);
+        const int64_t sl = t & page_mask;
+        load_bytes<S::VB>(vdat + pg * v_page + sl * v_tok + n * S::VB, r.vd[i]);
+        load_bytes<S::VSFB>(vsf + pg * vsf_page + sl * vsf_tok + (n * DV / 16) / 16, &r.vs[i]);
+      }
     }
   }
 };
@@ -176,8 +221,9 @@ __device__ __forceinline__ void k_operands(const StepRaw<DK, DV>& r, f16x8 (&ka)
 }
 
 // Dequantised V^T operands of a step: vt[e] holds value dim m*DV/16 + e (m = lane%16)
-// for tokens 8j..8j+7.  Tokens after tlast get scale 0 (their bytes may be anything).
-template <int DK, int DV>
+// for tokens 8j..8j+7.  With MASK, tokens after tlast get scale 0 (their bytes may be
+// anything, NaN scales included).
+template <int DK, int DV, bool MASK>
 __device__ __forceinline__ void v_operands(const StepRaw<DK, DV>& r, int t0, int tlast, int j,
                                            f16x8 (&vt)[DV / 16]) {
   using S = StepShape<DK, DV>;
@@ -186,8 +232,10 @@ __device__ __forceinline__ void v_operands(const StepRaw<DK, DV>& r, int t0, int
   for (int h = 0; h < S::VSFB; ++h) {
     uint32_t bytes[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      bytes[i] = (t0 + 8 * j + i > tlast) ? 0u : ((r.vs[i] >> (8 * h)) & 0xFF);
+    for (int i = 0; i < 8; ++i) {
+      bytes[i] = (r.vs[i] >> (8 * h)) & 0xFF;
+      if constexpr (MASK) bytes[i] = (t0 + 8 * j + i > tlast) ? 0u : bytes[i];
+    }
     sw[h][0] = bytes[0] | (bytes[1] << 8) | (bytes[2] << 16) | (bytes[3] << 24);
     sw[h][1] = bytes[4] | (bytes[5] << 8) | (bytes[6] << 16) | (bytes[7] << 24);
   }
@@ -215,7 +263,10 @@ __device__ __forceinline__ void v_operands(const StepRaw<DK, DV>& r, int t0, int
   for (int e = 0; e < S::NT; ++e) vt[e] = pack8(vp[e][0], vp[e][1], vp[e][2], vp[e][3]);
 }
 
-// Online-softmax state of one 16-row group (base-2 scores).
+// Online-softmax state of one 16-row group (base-2 scores).  `m` is a reference point,
+// not necessarily the running maximum: it is raised only when a row's maximum exceeds
+// it by kRescaleSlack, so p = exp2(x - m) <= 2^8.  O = acc / l and LSE = m + log2(l)
+// hold for any reference point.
 template <int NT>
 struct RowState {
   f32x4 acc[NT];
@@ -228,39 +279,50 @@ struct RowState {
   }
 
   // Scores of tokens t0 + 8j + i (i < 8) for this lane's row: sa (i < 4), sb (i >= 4).
-  // Keys after `last` are masked.  Returns the P operand.
+  // With MASK, keys after `last` are dropped.  Returns the P operand.
+  template <bool MASK>
   __device__ __forceinline__ f16x8 softmax(f32x4 sa, f32x4 sb, float c, int t0, int j, int last) {
+    // raw scores; x = s * c is formed inside the exponent's fma.  c > 0 (the host
+    // rejects other scales), so the largest raw score gives the largest x.
     float x[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      x[i] = sa[i] * c;
-      x[4 + i] = sb[i] * c;
+      x[i] = sa[i];
+      x[4 + i] = sb[i];
     }
-    float bm = -INFINITY;
+    if constexpr (MASK) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (t0 + 8 * j + i > last) x[i] = -INFINITY;
-      bm = fmaxf(bm, x[i]);
+      for (int i = 0; i < 8; ++i)
+        if (t0 + 8 * j + i > last) x[i] = -INFINITY;
     }
-    bm = max_over_groups(bm);
-    const float m_new = fmaxf(m, bm);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m - m_use);
+    float bm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                     fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    bm = max_over_groups(bm) * c;
+    const bool raise = bm > m + kRescaleSlack;
+    if (__any(raise)) {
+      // Rare.  The multiplies are done in place (tied asm operands): as plain code the
+      // branch either gets if-converted into 4*NT multiplies every step or makes the
+      // register allocator copy every accumulator at the join.
+      const float m_new = raise ? bm : m;
+      const float alpha = fast_exp2(m - m_new);  // 0 when m was -inf
+      l *= alpha;
+#pragma unroll
+      for (int e = 0; e < NT; ++e)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) asm volatile("v_mul_f32 %0, %0, %1" : "+v"(acc[e][i]) : "v"(alpha));
+      m = m_new;
+    }
+    const float m_use = m == -INFINITY ? 0.f : m;
     float psum = 0.f;
     f16x2 pp[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float p0 = fast_exp2(x[2 * i] - m_use);
-      const float p1 = fast_exp2(x[2 * i + 1] - m_use);
+      const float p0 = fast_exp2(fmaf(x[2 * i], c, -m_use));
+      const float p1 = fast_exp2(fmaf(x[2 * i + 1], c, -m_use));
       psum += p0 + p1;
       pp[i] = f16x2{(_Float16)p0, (_Float16)p1};
     }
-    l = l * alpha + psum;
-    m = m_new;
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-      for (int e = 0; e < NT; ++e) acc[e] *= alpha;
-    }
+    l += psum;
     return pack8(pp[0], pp[1], pp[2], pp[3]);
   }
 
@@ -269,8 +331,21 @@ struct RowState {
     for (int e = 0; e < NT; ++e) acc[e] = mfma16x16x32(vt[e], p, acc[e]);
   }
 
-  // Normalise and store this lane's part of the row: value dims (4j+i)*NT + e.
-  // Row sums are completed over the four lanes of the row first.
+  // Fold another state of the same rows into this one (same lane layout).
+  __device__ __forceinline__ void combine(float m2, float l2, const float* acc2) {
+    const float mx = fmaxf(m, m2);
+    const float mu = mx == -INFINITY ? 0.f : mx;
+    const float f1 = fast_exp2(m - mu), f2 = fast_exp2(m2 - mu);
+#pragma unroll
+    for (int e = 0; e < NT; ++e)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[e][i] = acc[e][i] * f1 + acc2[4 * e + i] * f2;
+    l = l * f1 + l2 * f2;
+    m = mx;
+  }
+
+  // Normalise and store this lane's part of the row: value dims (4j+i)*NT + e.  The row
+  // sum is first completed over the four lanes of the row.
   __device__ __forceinline__ void store(float* dst, float* lse_dst, bool valid, bool bad,
                                         float out_scale, int j) {
     const float l_tot = sum_over_groups(l);

@@ -1,85 +1,221 @@
-// Paged NVFP4 decode: one query per request, all qo heads of one kv head per wave.
+// Paged NVFP4 decode: one query per request, all qo heads of one kv head together.
 //
 // [XQA] "Support NVFP4 KV cache decode on SM120", walkthrough: packed K/V and their
-// scale factors are streamed from the page table, unpacked, scaled and fed to the
-// matrix units; split partials are merged afterwards.  [PF] "Re-enable split-KV for
-// NVFP4 KV cache in prefill path", commit "Gate split-KV off when kv_data_type is
-// NVFP4" and its follow-up: decode splits the KV range into 16-token-aligned chunks
-// whose partial states are merged by LSE.  [FIX] "fix(attention): correct SM120 NVFP4
-// qk_correction layout, row-sum reduction, and lse", commits 1-2: the row sum reduces
-// over exactly the lanes of one row; lse is ln of the sum of exp of the scaled scores.
+// scale factors are streamed through the page table, unpacked, scaled and fed to the
+// matrix units; split partials are merged.  [PF] "Re-enable split-KV for NVFP4 KV cache
+// in prefill path", commit "Gate split-KV off when kv_data_type is NVFP4" and its
+// follow-up: decode splits the KV range into 16-token-aligned chunks whose partial
+// states are merged by LSE.  [FIX] "fix(attention): correct SM120 NVFP4 qk_correction
+// layout, row-sum reduction, and lse", commits 1-2: a row sum reduces over exactly the
+// lanes of that row; lse is ln of the sum of exp of the scaled scores.
 //
-// A work item (request b, kv head g, up to 16 qo heads, chunk [kv0, kv1)) is one wave;
-// four independent items share a 256-thread workgroup.  The qo heads of the group are
-// the N dimension of the MFMAs (padded to 16), so the K/V bytes of the chunk are read
-// once for all of them.  The next step's bytes are loaded before the current step is
-// computed.
-#include "attn_step.h"
+// A work item is one workgroup of four waves over one key range of one (request,
+// kv head, block of <= 16 qo heads).  Wave w takes the w-th chunk of the range (the
+// plan's chunk length, or an even 16-aligned quarter), streams it in 32-token steps with
+// several steps' bytes in flight, and the four states are combined through LDS.  When a
+// row group is split over several workgroups, each writes a partial state and a merge
+// kernel on the same stream combines them by LSE (a fence-and-counter merge inside this
+// kernel was measured slower: each agent-scope release writes back the L2).
+#include "kv_ring.h"
 
 namespace nvfp4 {
 
 namespace {
 
-template <int DK, int DV, bool PAGE16>
-__global__ __launch_bounds__(256) void decode_kernel(AttnArgs a) {
+// Epilogue shared by both decode kernels: combine the four waves' states in wave 0,
+// then store the row group directly, or as a partial for the merge kernel.
+template <int DV>
+__device__ __forceinline__ void decode_epilogue(const AttnArgs& a, RowState<DV / 16>& st,
+                                                float* xch_mem, bool bad_w, int wave, int lane,
+                                                int b, int head, int n, int j, bool head_valid,
+                                                int slot) {
+  constexpr int NT = DV / 16;
+  constexpr int NX = NT * 4 + 3;  // per-lane state: accumulators, m, l, bad
+  float (*xch)[NX][64] = reinterpret_cast<float (*)[NX][64]>(xch_mem);
+  if (wave > 0) {
+#pragma unroll
+    for (int e = 0; e < NT; ++e)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xch[wave - 1][4 * e + i][lane] = st.acc[e][i];
+    xch[wave - 1][NX - 3][lane] = st.m;
+    xch[wave - 1][NX - 2][lane] = st.l;
+    xch[wave - 1][NX - 1][lane] = bad_w ? 1.f : 0.f;
+  }
+  __syncthreads();
+  if (wave > 0) return;
+  float bad_any = bad_w ? 1.f : 0.f;
+#pragma unroll
+  for (int w = 0; w < 3; ++w) {
+    const float m2 = xch[w][NX - 3][lane];
+    const float mx = fmaxf(st.m, m2);
+    const float mu = mx == -INFINITY ? 0.f : mx;
+    const float f1 = fast_exp2(st.m - mu), f2 = fast_exp2(m2 - mu);
+#pragma unroll
+    for (int e = 0; e < NT; ++e)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st.acc[e][i] = st.acc[e][i] * f1 + xch[w][4 * e + i][lane] * f2;
+    st.l = st.l * f1 + xch[w][NX - 2][lane] * f2;
+    st.m = mx;
+    bad_any = fmaxf(bad_any, xch[w][NX - 1][lane]);
+  }
+  const bool bad = bad_any != 0.f;
+
+  float* o_dst = a.o + (int64_t)b * a.o_s_row + (int64_t)head * a.o_s_head;
+  float* lse_dst = a.lse + (int64_t)b * a.num_qo_heads + head;
+  if (slot < 0) {
+    st.store(o_dst, lse_dst, head_valid, bad, a.out_scale, j);
+  } else {
+    st.store(a.part_o + ((int64_t)slot * a.rows_per_slot + n) * DV,
+             a.part_lse + (int64_t)slot * a.rows_per_slot + n, head_valid, bad, a.out_scale, j);
+  }
+}
+
+// One 32-token step: dequantise K, S^T = K Q^T, online softmax, dequantise V, O^T += V^T P^T.
+template <int DK, int DV>
+__device__ __forceinline__ void decode_step(const StepRaw<DK, DV>& r, int t0, int w1, int j,
+                                            const f16x8 (&qf)[DK / 32], float score_c,
+                                            RowState<DV / 16>& st) {
   using S = StepShape<DK, DV>;
+  const int tlast = w1 - 1;
+  f16x8 ka[S::NS], kb[S::NS];
+  k_operands<DK, DV>(r, ka, kb);
+  f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < S::NS; ++s) {
+    sa = mfma16x16x32(ka[s], qf[s], sa);
+    sb = mfma16x16x32(kb[s], qf[s], sb);
+  }
+  f16x8 vt[S::NT];
+  f16x8 p;
+  if (t0 + kDecodeStep > w1) {  // the wave's last, partial step
+    p = st.template softmax<true>(sa, sb, score_c, t0, j, tlast);
+    v_operands<DK, DV, true>(r, t0, tlast, j, vt);
+  } else {
+    p = st.template softmax<false>(sa, sb, score_c, t0, j, tlast);
+    v_operands<DK, DV, false>(r, t0, tlast, j, vt);
+  }
+  st.pv(vt, p);
+}
+
+// Work record, this wave's key range [w0, w1) and the Q operand: common to both kernels.
+struct DecodeItem {
+  int b, kvh, h0, hn, kv0, kv1, slot, merge, w0, w1, head;
+  bool head_valid;
+};
+
+__device__ __forceinline__ DecodeItem decode_item(const AttnArgs& a, int wave, int n) {
+  const int32_t* rec = a.work + (int64_t)blockIdx.x * kWorkFields;
+  DecodeItem it;
+  it.b = rec[W_REQ]; it.kvh = rec[W_KVH]; it.h0 = rec[W_ROW0]; it.hn = rec[W_ROWS];
+  it.kv0 = rec[W_KV0]; it.kv1 = rec[W_KV1]; it.slot = rec[W_SLOT]; it.merge = rec[W_MERGE];
+  const int sub =
+      a.wave_chunk > 0 ? a.wave_chunk : (((it.kv1 - it.kv0 + 3) / 4 + 15) / 16) * 16;
+  it.w0 = min(it.kv1, it.kv0 + wave * sub);
+  it.w1 = min(it.kv1, it.w0 + sub);
+  it.head_valid = n < it.hn;
+  it.head = it.kvh * a.group + it.h0 + n;
+  return it;
+}
+
+// page_size >= 16: the chunk streams through a per-wave LDS ring several steps deep.
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void decode_ring_kernel(AttnArgs a) {
+  using S = StepShape<DK, DV>;
+  using R = RingShape<DK, DV>;
+  constexpr int XCH_BYTES = 3 * (S::NT * 4 + 3) * 64 * 4;
+  constexpr int SMEM = 4 * R::WAVE_BYTES > XCH_BYTES ? 4 * R::WAVE_BYTES : XCH_BYTES;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int item = blockIdx.x * 4 + wave;
-  if (item >= a.n_work) return;
   const int lane = threadIdx.x & 63;
   const int j = lane >> 4;
   const int n = lane & 15;
-  const int32_t* rec = a.work + (int64_t)item * kWorkFields;
-  const int b = rec[W_REQ], kvh = rec[W_KVH], h0 = rec[W_ROW0], hn = rec[W_ROWS];
-  const int kv0 = rec[W_KV0], kv1 = rec[W_KV1], slot = rec[W_SLOT];
-  const bool head_valid = n < hn;
-  const int head = kvh * a.group + h0 + n;
+  const DecodeItem it = decode_item(a, wave, n);
 
   f16x8 qf[S::NS];
-  const float score_c =
-      a.score_scale * load_q_operand<DK>(a.q + (int64_t)b * a.q_s_row + (int64_t)head * a.q_s_head,
-                                         head_valid, j, qf);
+  const float score_c = a.score_scale *
+      load_q_operand<DK>(a.q + (int64_t)it.b * a.q_s_row + (int64_t)it.head * a.q_s_head,
+                         it.head_valid, j, qf);
 
-  PagedView<DK, DV, PAGE16> view;
-  view.init(a, b, kvh, lane);
-  const int tlast = kv1 - 1;
+  PagedView<DK, DV, true> view;
+  view.init(a, it.b, it.kvh, lane);
+  RingPlan<DK, DV> rp;
+  rp.init(lane, view.k_tok, view.v_tok, view.ksf_tok, view.vsf_tok);
+  uint8_t* ring = smem + wave * R::WAVE_BYTES;
+  const uint32_t ring_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)ring);
+  const int tlast = it.w1 - 1;
+  const int nsteps = (it.w1 - it.w0 + kDecodeStep - 1) / kDecodeStep;
+  uint32_t bad = 0;
 
   RowState<S::NT> st;
   st.init();
-  StepRaw<DK, DV> cur, nxt;
-  if (kv0 < kv1) view.load(cur, kv0, tlast);
-  for (int t0 = kv0; t0 < kv1; t0 += kDecodeStep) {
-    if (t0 + kDecodeStep < kv1) view.load(nxt, t0 + kDecodeStep, tlast);
-    f16x8 ka[S::NS], kb[S::NS];
-    k_operands<DK, DV>(cur, ka, kb);
-    f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < S::NS; ++s) {
-      sa = mfma16x16x32(ka[s], qf[s], sa);
-      sb = mfma16x16x32(kb[s], qf[s], sb);
+  for (int s = 0; s < R::NST - 1; ++s)
+    if (s < nsteps)
+      ring_issue<DK, DV>(rp, ring_lds + s * R::STAGE, view, it.w0 + s * kDecodeStep, tlast, bad);
+  // unrolled by the ring depth so that every stage offset is a compile-time constant
+  for (int i0 = 0; i0 < nsteps; i0 += R::NST) {
+#pragma unroll
+    for (int s = 0; s < R::NST; ++s) {
+      const int i = i0 + s;
+      if (i < nsteps) {
+        const int ahead = i + R::NST - 1;
+        if (ahead < nsteps)
+          ring_issue<DK, DV>(rp, ring_lds + ((s + R::NST - 1) % R::NST) * R::STAGE, view,
+                             it.w0 + ahead * kDecodeStep, tlast, bad);
+        const uint32_t zero = wait_steps<R::NDMA, R::NST>(min(nsteps - 1 - i, R::NST - 1));
+        StepRaw<DK, DV> raw;
+        ring_read<DK, DV>(ring + s * R::STAGE + zero, j, n, raw);
+        decode_step<DK, DV>(raw, it.w0 + i * kDecodeStep, it.w1, j, qf, score_c, st);
+      }
     }
-    const f16x8 p = st.softmax(sa, sb, score_c, t0, j, tlast);
-    f16x8 vt[S::NT];
-    v_operands<DK, DV>(cur, t0, tlast, j, vt);
-    st.pv(vt, p);
-    cur = nxt;
   }
+  const bool bad_w = __any(bad != 0);
+  __syncthreads();  // every wave is done with its ring: the exchange reuses that memory
+  decode_epilogue<DV>(a, st, reinterpret_cast<float*>(smem), bad_w, wave, lane, it.b, it.head, n,
+                      j, it.head_valid, it.slot);
+}
 
-  const bool bad = __any(view.bad != 0);
-  float* dst = slot < 0 ? a.o + (int64_t)b * a.o_s_row + (int64_t)head * a.o_s_head
-                        : a.part_o + ((int64_t)slot * a.rows_per_slot + n) * DV;
-  float* lse_dst = slot < 0 ? a.lse + (int64_t)b * a.num_qo_heads + head
-                            : a.part_lse + (int64_t)slot * a.rows_per_slot + n;
-  st.store(dst, lse_dst, head_valid, bad, a.out_scale, j);
+// page_size < 16: every token is looked up on its own; the next step is held in registers.
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void decode_regs_kernel(AttnArgs a) {
+  using S = StepShape<DK, DV>;
+  __shared__ float xch[3 * (S::NT * 4 + 3) * 64];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int j = lane >> 4;
+  const int n = lane & 15;
+  const DecodeItem it = decode_item(a, wave, n);
+
+  f16x8 qf[S::NS];
+  const float score_c = a.score_scale *
+      load_q_operand<DK>(a.q + (int64_t)it.b * a.q_s_row + (int64_t)it.head * a.q_s_head,
+                         it.head_valid, j, qf);
+  PagedView<DK, DV, false> view;
+  view.init(a, it.b, it.kvh, lane);
+  const int tlast = it.w1 - 1;
+  RowState<S::NT> st;
+  st.init();
+  StepRaw<DK, DV> r0, r1;
+  if (it.w0 < it.w1) view.load(r0, it.w0, tlast);
+  for (int t0 = it.w0; t0 < it.w1; t0 += 2 * kDecodeStep) {
+    const int t1 = t0 + kDecodeStep;
+    if (t1 < it.w1) view.load(r1, t1, tlast);
+    decode_step<DK, DV>(r0, t0, it.w1, j, qf, score_c, st);
+    if (t1 >= it.w1) break;
+    if (t1 + kDecodeStep < it.w1) view.load(r0, t1 + kDecodeStep, tlast);
+    decode_step<DK, DV>(r1, t1, it.w1, j, qf, score_c, st);
+  }
+  const bool bad_w = __any(view.bad != 0);
+  decode_epilogue<DV>(a, st, xch, bad_w, wave, lane, it.b, it.head, n, j, it.head_valid, it.slot);
 }
 
 template <int DK, int DV>
 hipError_t launch_dk_dv(int page_shift, const AttnArgs& a, hipStream_t stream) {
-  const dim3 grid((a.n_work + 3) / 4);
+  const dim3 grid(a.n_work);
   if (page_shift >= 4)
-    hipLaunchKernelGGL((decode_kernel<DK, DV, true>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((decode_ring_kernel<DK, DV>), grid, dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((decode_kernel<DK, DV, false>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((decode_regs_kernel<DK, DV>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -88,7 +224,7 @@ hipError_t launch_dk_dv(int page_shift, const AttnArgs& a, hipStream_t stream) {
 bool decode_supported(int dk, int dv) {
   const bool okk = dk == 64 || dk == 128 || dk == 256 || dk == 512;
   const bool okv = dv == 64 || dv == 128 || dv == 256 || dv == 512;
-  return okk && okv && dv <= dk;
+  return okk && okv && dv <= dk && !(dk == 512 && dv == 512);
 }
 
 hipError_t launch_decode(int dk, int dv, int page_shift, const AttnArgs& a, hipStream_t stream) {
@@ -104,7 +240,6 @@ hipError_t launch_decode(int dk, int dv, int page_shift, const AttnArgs& a, hipS
   NVFP4_DECODE_CASE(512, 64)
   NVFP4_DECODE_CASE(512, 128)
   NVFP4_DECODE_CASE(512, 256)
-  NVFP4_DECODE_CASE(512, 512)
 #undef NVFP4_DECODE_CASE
   return hipErrorInvalidValue;
 }

@@ -59,22 +59,8 @@ struct AttnArgs {
   int32_t page_shift;       // log2(page_size)
   int32_t rows_per_slot;
   int32_t causal;
-};
-
-struct MergeArgs {
-  const int32_t* merges;
-  int32_t n_merges;
-  const float* part_o;
-  const float* part_lse;
-  int32_t rows_per_slot;
-  int32_t head_dim;
-  float* o;
-  int64_t o_s_row, o_s_head;
-  float* lse;
-  int32_t num_qo_heads;
-  int32_t group;
-  int32_t prefill;
-  const int32_t* qo_indptr;
+  int32_t wave_chunk;       // decode: keys per wave (0: split the item evenly over 4 waves)
+  const int32_t* merges;    // merge records
 };
 
 struct QuantArgs {
@@ -101,7 +87,8 @@ hipError_t launch_prefill(int dk, int dv, int page_shift, const AttnArgs& a, int
 bool prefill_supported(int dk, int dv);
 int prefill_rows_per_item(int dk, int dv, int group);
 size_t prefill_lds_bytes(int dk, int dv);
-hipError_t launch_merge_partials(const MergeArgs& m, hipStream_t stream);
+hipError_t launch_merge_partials(const AttnArgs& a, int n_merges, int dv, int prefill,
+                                 hipStream_t stream);
 hipError_t launch_merge_states(const float* o_parts, const float* lse_parts, int64_t rows,
                                int32_t num_parts, int32_t heads, int32_t head_dim, float* o,
                                float* lse, hipStream_t stream);

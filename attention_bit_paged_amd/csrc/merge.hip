@@ -4,57 +4,70 @@
 // partial tiles are combined by mergeAndSaveOutTile.  For parts c with
 // (O_c, lse_c): lse = M + ln sum_c exp(lse_c - M) with M = max_c lse_c and
 // O = sum_c exp(lse_c - lse) O_c; a part with lse = -inf adds nothing.
-#include "internal.h"
+#include "attn_step.h"
 
 namespace nvfp4 {
 
 namespace {
 
-// Partials written by the decode / prefill kernels for one split row group.
-__global__ __launch_bounds__(256) void merge_partials_kernel(MergeArgs m) {
-  const int32_t* rec = m.merges + (int64_t)blockIdx.x * kMergeFields;
-  const int b = rec[0], kvh = rec[1], row0 = rec[2], nrows_in = rec[3];
-  const int first = rec[4], np = rec[5];
-  const int nrows = m.prefill ? nrows_in * m.group : nrows_in;
-  const int c4 = m.head_dim / 4;
-  const int total = nrows * c4;
-  for (int idx = threadIdx.x; idx < total; idx += blockDim.x) {
-    const int r = idx / c4;
-    const int c = idx - r * c4;
-    float mx = -INFINITY;
-    for (int p = 0; p < np; ++p) mx = fmaxf(mx, m.part_lse[(int64_t)(first + p) * m.rows_per_slot + r]);
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    float wsum = 0.f;
-    if (mx > -INFINITY) {
-      for (int p = 0; p < np; ++p) {
-        const int64_t prow = (int64_t)(first + p) * m.rows_per_slot + r;
-        const float l = m.part_lse[prow];
-        const float w = l > -INFINITY ? __expf(l - mx) : 0.f;
-        if (w > 0.f) {
-          const float4 v = reinterpret_cast<const float4*>(m.part_o + prow * m.head_dim)[c];
-          acc.x += w * v.x;
-          acc.y += w * v.y;
-          acc.z += w * v.z;
-          acc.w += w * v.w;
-        }
-        wsum += w;
-      }
-    }
-    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-    int64_t orow;
-    int head;
-    if (m.prefill) {
-      const int qi = r / m.group;
-      head = kvh * m.group + (r - qi * m.group);
-      orow = (int64_t)m.qo_indptr[b] + row0 + qi;
-    } else {
-      head = kvh * m.group + row0 + r;
-      orow = b;
-    }
-    float4* dst = reinterpret_cast<float4*>(m.o + orow * m.o_s_row + (int64_t)head * m.o_s_head);
-    dst[c] = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-    if (c == 0) m.lse[orow * m.num_qo_heads + head] = wsum > 0.f ? mx + __logf(wsum) : -INFINITY;
+// Partials of split row groups, after the attention kernel: one wave per (merge
+// record, row).  A row is one qo head of the group (decode) or one (query, qo head) pair
+// of a query tile (prefill); each partial holds a normalised O row and its LSE.
+template <int DV>
+__global__ __launch_bounds__(256) void merge_partials_kernel(AttnArgs a, int n_merges, int prefill) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int64_t task = (int64_t)blockIdx.x * 4 + wave;
+  const int rows_per_merge = a.rows_per_slot;
+  if (task >= (int64_t)n_merges * rows_per_merge) return;
+  const int mi = (int)(task / rows_per_merge);
+  const int r = (int)(task - (int64_t)mi * rows_per_merge);
+  const int32_t* rec = a.merges + (int64_t)mi * kMergeFields;
+  const int b = rec[0], kvh = rec[1], row0 = rec[2], nrow = rec[3], first = rec[4], np = rec[5];
+  int64_t orow;
+  int head;
+  if (prefill) {
+    // rows are (query, head) pairs, query major
+    if (r >= nrow * a.group) return;
+    const int qi = r / a.group;
+    head = kvh * a.group + (r - qi * a.group);
+    orow = (int64_t)a.qo_indptr[b] + row0 + qi;
+  } else {
+    if (r >= nrow) return;
+    head = kvh * a.group + row0 + r;
+    orow = b;
   }
+  // lane covers value dims [lane * DV/64, (lane+1) * DV/64)
+  constexpr int PER = DV / 64;
+  float mx = -INFINITY;
+  bool any_nan = false;
+  for (int p = 0; p < np; ++p) {
+    const float lp = a.part_lse[(int64_t)(first + p) * a.rows_per_slot + r];
+    any_nan |= lp != lp;
+    mx = fmaxf(mx, lp);
+  }
+  float acc[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) acc[k] = 0.f;
+  float wsum = 0.f;
+  if (mx > -INFINITY) {
+    for (int p = 0; p < np; ++p) {
+      const int64_t prow = (int64_t)(first + p) * a.rows_per_slot + r;
+      const float lp = a.part_lse[prow];
+      const float w = lp > -INFINITY ? __expf(lp - mx) : 0.f;
+      wsum += w;
+      const float* src = a.part_o + prow * DV + lane * PER;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) acc[k] += w * src[k];
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  float* dst = a.o + orow * a.o_s_row + (int64_t)head * a.o_s_head + lane * PER;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) dst[k] = any_nan ? NAN : acc[k] * inv;
+  if (lane == 0)
+    a.lse[orow * a.num_qo_heads + head] =
+        any_nan ? NAN : (wsum > 0.f ? mx + __logf(wsum) : -INFINITY);
 }
 
 // Standalone merge: o_parts [rows, np, heads, D], lse_parts [rows, np, heads].
@@ -108,9 +121,18 @@ __global__ __launch_bounds__(256) void merge_states_kernel(const float* __restri
 
 }  // namespace
 
-hipError_t launch_merge_partials(const MergeArgs& m, hipStream_t stream) {
-  if (m.n_merges <= 0) return hipSuccess;
-  hipLaunchKernelGGL(merge_partials_kernel, dim3(m.n_merges), dim3(256), 0, stream, m);
+hipError_t launch_merge_partials(const AttnArgs& a, int n_merges, int dv, int prefill,
+                                 hipStream_t stream) {
+  if (n_merges <= 0) return hipSuccess;
+  const int64_t tasks = (int64_t)n_merges * a.rows_per_slot;
+  const dim3 grid((unsigned)((tasks + 3) / 4));
+  switch (dv) {
+    case 64: hipLaunchKernelGGL(merge_partials_kernel<64>, grid, dim3(256), 0, stream, a, n_merges, prefill); break;
+    case 128: hipLaunchKernelGGL(merge_partials_kernel<128>, grid, dim3(256), 0, stream, a, n_merges, prefill); break;
+    case 256: hipLaunchKernelGGL(merge_partials_kernel<256>, grid, dim3(256), 0, stream, a, n_merges, prefill); break;
+    case 512: hipLaunchKernelGGL(merge_partials_kernel<512>, grid, dim3(256), 0, stream, a, n_merges, prefill); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

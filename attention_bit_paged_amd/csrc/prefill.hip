@@ -11,9 +11,9 @@
 // A work item is one workgroup of four waves: (request b, kv head g, query tile,
 // chunk [kv0, kv1)).  The tile's rows are (query, qo head of the group) pairs, query
 // major, so the heads that share a kv head share every K/V byte read.  Each wave owns
-// NR groups of 16 rows and streams the chunk in 32-token steps with the shared step
-// machinery; the dequantised K and V^T operands of a step are reused by the wave's
-// row groups.
+// NR groups of 16 rows and streams the chunk in 32-token steps with the next step's
+// bytes in flight; the dequantised K and V^T operands of a step serve all the wave's
+// row groups.  A split tile's partial states are merged by a separate kernel.
 #include "attn_step.h"
 
 namespace nvfp4 {
@@ -39,7 +39,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a) {
   const int G = a.group;
   const int R = qn * G;
   const int row_base = wave * NR * 16;
-  if (row_base >= R) return;  // no rows for this wave (no barriers in this kernel)
+  const bool wave_has_rows = row_base < R;  // uniform; rowless waves still meet the barriers
   const int qstart = a.qo_indptr[b];
   const int qlen = a.qo_indptr[b + 1] - qstart;
   const int off = a.kv_lens[b] - qlen;
@@ -65,11 +65,15 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a) {
                                 rv[rg], j, qf[rg]);
   }
   // keys this wave needs: up to the last visible key of its last valid row
-  int wave_end = kv1;
-  if (a.causal) {
+  int wave_end = wave_has_rows ? kv1 : kv0;
+  if (a.causal && wave_has_rows) {
     const int r_last = min(R - 1, row_base + NR * 16 - 1);
     wave_end = min(kv1, q0 + r_last / G + off + 1);
   }
+  // steps that may hold a masked key: the chunk's tail and, for causal rows, any step
+  // past the first visible-key limit of the wave's first row
+  int mask_from = kv1 - kDecodeStep;
+  if (a.causal) mask_from = min(mask_from, q0 + row_base / G + off + 1 - kDecodeStep);
 
   PagedView<DK, DV, PAGE16> view;
   view.init(a, b, kvh, lane);
@@ -78,12 +82,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a) {
   RowState<S::NT> st[NR];
 #pragma unroll
   for (int rg = 0; rg < NR; ++rg) st[rg].init();
-  StepRaw<DK, DV> cur, nxt;
-  if (kv0 < wave_end) view.load(cur, kv0, tlast);
-  for (int t0 = kv0; t0 < wave_end; t0 += kDecodeStep) {
-    if (t0 + kDecodeStep < wave_end) view.load(nxt, t0 + kDecodeStep, tlast);
+
+  auto step = [&](const StepRaw<DK, DV>& r, int t0) {
     f16x8 ka[S::NS], kb[S::NS];
-    k_operands<DK, DV>(cur, ka, kb);
+    k_operands<DK, DV>(r, ka, kb);
+    const bool masked = t0 > mask_from;
     f16x8 p[NR];
 #pragma unroll
     for (int rg = 0; rg < NR; ++rg) {
@@ -93,24 +96,46 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a) {
         sa = mfma16x16x32(ka[s], qf[rg][s], sa);
         sb = mfma16x16x32(kb[s], qf[rg][s], sb);
       }
-      p[rg] = st[rg].softmax(sa, sb, sc[rg], t0, j, last[rg]);
+      p[rg] = masked ? st[rg].template softmax<true>(sa, sb, sc[rg], t0, j, last[rg])
+                     : st[rg].template softmax<false>(sa, sb, sc[rg], t0, j, last[rg]);
     }
     f16x8 vt[S::NT];
-    v_operands<DK, DV>(cur, t0, tlast, j, vt);
+    if (t0 + kDecodeStep > kv1)
+      v_operands<DK, DV, true>(r, t0, tlast, j, vt);
+    else
+      v_operands<DK, DV, false>(r, t0, tlast, j, vt);
 #pragma unroll
     for (int rg = 0; rg < NR; ++rg) st[rg].pv(vt, p[rg]);
-    cur = nxt;
+  };
+
+  StepRaw<DK, DV> r0, r1;
+  if (kv0 < wave_end) view.load(r0, kv0, tlast);
+  for (int t0 = kv0; t0 < wave_end; t0 += 2 * kDecodeStep) {
+    const int t1 = t0 + kDecodeStep;
+    if (t1 < wave_end) view.load(r1, t1, tlast);
+    step(r0, t0);
+    if (t1 >= wave_end) break;
+    if (t1 + kDecodeStep < wave_end) view.load(r0, t1 + kDecodeStep, tlast);
+    step(r1, t1);
   }
 
   const bool bad = __any(view.bad != 0);
+  if (slot < 0) {
+    if (wave_has_rows) {
 #pragma unroll
-  for (int rg = 0; rg < NR; ++rg) {
-    const int r = row_base + rg * 16 + n;
-    float* dst = slot < 0 ? a.o + tokrow[rg] * a.o_s_row + (int64_t)headi[rg] * a.o_s_head
-                          : a.part_o + ((int64_t)slot * a.rows_per_slot + r) * DV;
-    float* lse_dst = slot < 0 ? a.lse + tokrow[rg] * a.num_qo_heads + headi[rg]
-                              : a.part_lse + (int64_t)slot * a.rows_per_slot + r;
-    st[rg].store(dst, lse_dst, rv[rg], bad, a.out_scale, j);
+      for (int rg = 0; rg < NR; ++rg)
+        st[rg].store(a.o + tokrow[rg] * a.o_s_row + (int64_t)headi[rg] * a.o_s_head,
+                     a.lse + tokrow[rg] * a.num_qo_heads + headi[rg], rv[rg], bad, a.out_scale, j);
+    }
+    return;
+  }
+  if (wave_has_rows) {
+#pragma unroll
+    for (int rg = 0; rg < NR; ++rg) {
+      const int r = row_base + rg * 16 + n;
+      st[rg].store(a.part_o + ((int64_t)slot * a.rows_per_slot + r) * DV,
+                   a.part_lse + (int64_t)slot * a.rows_per_slot + r, rv[rg], bad, a.out_scale, j);
+    }
   }
 }
 
@@ -129,7 +154,7 @@ hipError_t launch_dk_dv(int page_shift, const AttnArgs& a, hipStream_t stream) {
 bool prefill_supported(int dk, int dv) {
   const bool okk = dk == 64 || dk == 128 || dk == 256 || dk == 512;
   const bool okv = dv == 64 || dv == 128 || dv == 256 || dv == 512;
-  return okk && okv && dv <= dk;
+  return okk && okv && dv <= dk && !(dk == 512 && dv == 512);
 }
 
 int prefill_rows_per_item(int dk, int /*dv*/, int /*group*/) { return 64 * (dk >= 512 ? 1 : 2); }
@@ -150,7 +175,6 @@ hipError_t launch_prefill(int dk, int dv, int page_shift, const AttnArgs& a, int
   NVFP4_PREFILL_CASE(512, 64)
   NVFP4_PREFILL_CASE(512, 128)
   NVFP4_PREFILL_CASE(512, 256)
-  NVFP4_PREFILL_CASE(512, 512)
 #undef NVFP4_PREFILL_CASE
   return hipErrorInvalidValue;
 }

@@ -43,7 +43,8 @@ def check_plan(plan, kv_lens, group, qo_lens=None, causal=False):
             assert all(w[W["partial_slot"]] >= 0 for w in items)
             assert len({w[W["merge_index"]] for w in items}) == 1
             if plan.info()["kv_chunk_tokens"]:
-                c = plan.info()["kv_chunk_tokens"]
+                # a decode item is one workgroup of four waves, one chunk per wave
+                c = plan.info()["kv_chunk_tokens"] * (1 if info["is_prefill"] else 4)
                 assert all(w[W["kv_end"]] - w[W["kv_begin"]] <= c for w in items)
     assert nmerge == info["num_merges"]
     return by_group
@@ -79,14 +80,14 @@ def test_batch_decode_config_plan():
     check_plan(plan, list(w.kv_lens), 4)
     info = plan.info()
     assert info["kv_chunk_tokens"] == 256
-    assert info["num_work_items"] == sum(8 * -(-l // 256) for l in w.kv_lens)
+    assert info["num_work_items"] == sum(8 * -(-l // 1024) for l in w.kv_lens)
 
 
 def test_auto_split_fills_the_device_for_long_context():
     plan = nv.Plan([131072] * 8, num_qo_heads=32, num_kv_heads=8, head_dim_qk=128, num_cus=256)
     info = plan.info()
     assert info["kv_chunk_tokens"] % 32 == 0 and info["kv_chunk_tokens"] > 0
-    assert info["num_work_items"] >= 256 * 4
+    assert info["num_work_items"] * 4 >= 256 * 8      # four waves per decode item
     check_plan(plan, [131072] * 8, 4)
     # short batch that already fills the device is not split
     plan2 = nv.Plan([300] * 512, num_qo_heads=32, num_kv_heads=8, head_dim_qk=128, num_cus=256)
