@@ -123,6 +123,9 @@ class Plan:
         self._ind = None if qo_indptr is None else np.ascontiguousarray(
             np.asarray(qo_indptr, dtype=np.int32))
         self._h = ctypes.c_void_p()
+        # held on the instance: module globals may already be gone when a plan is
+        # collected at interpreter exit
+        self._destroy = lib.nvfp4_plan_destroy
         self.batch = len(self._kv)
         self.num_qo_heads, self.num_kv_heads = num_qo_heads, num_kv_heads
         self.head_dim_qk, self.head_dim_vo, self.page_size = head_dim_qk, head_dim_vo, page_size
@@ -135,8 +138,9 @@ class Plan:
 
     def __del__(self):
         h = getattr(self, "_h", None)
-        if h is not None and h.value:
-            lib.nvfp4_plan_destroy(h)
+        destroy = getattr(self, "_destroy", None)
+        if h is not None and h.value and destroy is not None:
+            destroy(h)
             self._h = None
 
     @property

@@ -279,8 +279,8 @@ nvfp4_status nvfp4_plan_create(const int32_t* kv_lens, const int32_t* qo_indptr,
   // Chunk length.  Decode: keys per wave; a work item (one workgroup of four waves)
   // covers four consecutive chunks of a row group, or the whole row split evenly over
   // its waves when nothing is split.  Prefill: keys per work item.  Explicit, never, or
-  // chosen so that the device is filled: decode aims at 8 waves per CU, prefill at 2
-  // workgroups per CU.
+  // chosen so that the device is filled: decode aims at as many waves per CU as its
+  // kernel keeps resident for this shape, prefill at 2 workgroups per CU.
   int chunk = 0;
   int64_t total = 0;
   int max_len = 0;
@@ -292,7 +292,9 @@ nvfp4_status nvfp4_plan_create(const int32_t* kv_lens, const int32_t* qo_indptr,
   if (kv_chunk_tokens > 0) {
     chunk = kv_chunk_tokens;
   } else if (kv_chunk_tokens == 0) {
-    const int64_t target = (int64_t)num_cus * (prefill ? 2 : 8);   // items (prefill) / waves (decode)
+    // items (prefill) / waves (decode)
+    const int64_t target =
+        (int64_t)num_cus * (prefill ? 2 : 4 * decode_wgs_per_cu(head_dim_qk, head_dim_vo));
     const int64_t have = (int64_t)groups.size() * (prefill ? 1 : 4);
     if (have < target) {
       int64_t c = (total + target - 1) / std::max<int64_t>(target, 1);

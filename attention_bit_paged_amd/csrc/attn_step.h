@@ -263,11 +263,34 @@ __device__ __forceinline__ void v_operands(const StepRaw<DK, DV>& r, int t0, int
   for (int e = 0; e < S::NT; ++e) vt[e] = pack8(vp[e][0], vp[e][1], vp[e][2], vp[e][3]);
 }
 
+// Multiplies 16 accumulators by alpha on the lanes of a wave whose `raised` mask is
+// non-zero.  The test and the multiplies sit in one asm statement, so the accumulators
+// keep their registers whether or not the multiplies run (as C++ control flow, the
+// join of the two paths copies every accumulator each step).  The leading nops cover
+// the MFMA-result-to-VALU distance, the trailing ones the VALU-to-MFMA operand one.
+__device__ __forceinline__ void scale16_if(f32x4& a, f32x4& b, f32x4& c, f32x4& d, float alpha,
+                                           uint64_t raised) {
+  asm volatile(
+      "s_cmp_eq_u64 %16, 0\n\ts_cbranch_scc1 1f\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\t"
+      "v_mul_f32 %0, %0, %17\n\tv_mul_f32 %1, %1, %17\n\tv_mul_f32 %2, %2, %17\n\t"
+      "v_mul_f32 %3, %3, %17\n\tv_mul_f32 %4, %4, %17\n\tv_mul_f32 %5, %5, %17\n\t"
+      "v_mul_f32 %6, %6, %17\n\tv_mul_f32 %7, %7, %17\n\tv_mul_f32 %8, %8, %17\n\t"
+      "v_mul_f32 %9, %9, %17\n\tv_mul_f32 %10, %10, %17\n\tv_mul_f32 %11, %11, %17\n\t"
+      "v_mul_f32 %12, %12, %17\n\tv_mul_f32 %13, %13, %17\n\tv_mul_f32 %14, %14, %17\n\t"
+      "v_mul_f32 %15, %15, %17\n\ts_nop 4\n1:"
+      : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]),
+        "+v"(b[3]), "+v"(c[0]), "+v"(c[1]), "+v"(c[2]), "+v"(c[3]), "+v"(d[0]), "+v"(d[1]),
+        "+v"(d[2]), "+v"(d[3])
+      : "s"(raised), "v"(alpha)
+      : "scc");
+}
+
 // Online-softmax state of one 16-row group (base-2 scores).  `m` is a reference point,
 // not necessarily the running maximum: it is raised only when a row's maximum exceeds
 // it by kRescaleSlack, so p = exp2(x - m) <= 2^8.  O = acc / l and LSE = m + log2(l)
-// hold for any reference point.
-template <int NT>
+// hold for any reference point.  VGPR_ACC: the accumulators live in ordinary VGPRs
+// and are rescaled in place (scale16_if); otherwise by plain code.
+template <int NT, bool VGPR_ACC>
 struct RowState {
   f32x4 acc[NT];
   float m, l;
@@ -279,7 +302,8 @@ struct RowState {
   }
 
   // Scores of tokens t0 + 8j + i (i < 8) for this lane's row: sa (i < 4), sb (i >= 4).
-  // With MASK, keys after `last` are dropped.  Returns the P operand.
+  // With MASK, keys after `last` are dropped; without it every key is valid, so the
+  // reference point is finite once this step has been folded in.  Returns the P operand.
   template <bool MASK>
   __device__ __forceinline__ f16x8 softmax(f32x4 sa, f32x4 sb, float c, int t0, int j, int last) {
     // raw scores; x = s * c is formed inside the exponent's fma.  c > 0 (the host
@@ -295,24 +319,37 @@ struct RowState {
       for (int i = 0; i < 8; ++i)
         if (t0 + 8 * j + i > last) x[i] = -INFINITY;
     }
-    float bm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                     fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-    bm = max_over_groups(bm) * c;
+    const float b1 = fmaxf(fmaxf(x[0], x[1]), x[2]);
+    const float b2 = fmaxf(fmaxf(x[3], x[4]), x[5]);
+    const float b3 = fmaxf(fmaxf(x[6], x[7]), b1);
+    const float bm = max_over_groups(fmaxf(b3, b2)) * c;
     const bool raise = bm > m + kRescaleSlack;
-    if (__any(raise)) {
-      // Rare.  The multiplies are done in place (tied asm operands): as plain code the
-      // branch either gets if-converted into 4*NT multiplies every step or makes the
-      // register allocator copy every accumulator at the join.
-      const float m_new = raise ? bm : m;
-      const float alpha = fast_exp2(m - m_new);  // 0 when m was -inf
-      l *= alpha;
+    const float m_new = raise ? bm : m;
+    if constexpr (VGPR_ACC) {
+      const uint64_t raised = __ballot(raise);
+      // alpha = exp2(m - m_new) on raising lanes (0 when m was -inf), 1 elsewhere; only
+      // computed when some lane raises
+      float alpha;
+      asm volatile(
+          "s_cmp_eq_u64 %2, 0\n\ts_cbranch_scc1 1f\n\tv_sub_f32 %0, %3, %4\n\t"
+          "v_cndmask_b32_e64 %0, 0, %0, %2\n\tv_exp_f32 %0, %0\n\ts_nop 1\n\t"
+          "v_mul_f32 %1, %1, %0\n1:"
+          : "=&v"(alpha), "+v"(l)
+          : "s"(raised), "v"(m), "v"(m_new)
+          : "scc");
 #pragma unroll
-      for (int e = 0; e < NT; ++e)
+      for (int e = 0; e < NT; e += 4)
+        scale16_if(acc[e], acc[e + 1], acc[e + 2], acc[e + 3], alpha, raised);
+    } else {
+      if (__any(raise)) {
+        const float alpha = fast_exp2(m - m_new);  // 0 when m was -inf
+        l *= alpha;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) asm volatile("v_mul_f32 %0, %0, %1" : "+v"(acc[e][i]) : "v"(alpha));
-      m = m_new;
+        for (int e = 0; e < NT; ++e) acc[e] *= alpha;
+      }
     }
-    const float m_use = m == -INFINITY ? 0.f : m;
+    m = m_new;
+    const float m_use = MASK ? (m == -INFINITY ? 0.f : m) : m;
     float psum = 0.f;
     f16x2 pp[4];
 #pragma unroll

@@ -22,10 +22,23 @@ namespace nvfp4 {
 
 namespace {
 
+// Workgroups (of four waves) one CU holds at once, by design.  Registers: 512 VGPRs
+// per SIMD lane are shared by the waves on a SIMD, and the kernels of each shape are
+// held to the budget of this many waves (amdgpu_waves_per_eu).  LDS: 160 KiB per CU,
+// and each wave's ring needs two stages at least.
+template <int DK, int DV>
+struct DecodeOcc {
+  static constexpr int STAGE = 16 * DK + 16 * DV + (2 * DK + 2 * DV + 255) / 256 * 256;
+  static constexpr int BY_REGS = DK <= 128 ? 4 : (DK == 256 && DV <= 128 ? 3 : 2);
+  static constexpr int BY_LDS = (160 * 1024) / (4 * 2 * STAGE);
+  static constexpr int WGS = BY_REGS < BY_LDS ? BY_REGS : (BY_LDS > 0 ? BY_LDS : 1);
+  static constexpr int WAVE_LDS = (160 * 1024) / (4 * WGS);  // one wave's ring budget
+};
+
 // Epilogue shared by both decode kernels: combine the four waves' states in wave 0,
 // then store the row group directly, or as a partial for the merge kernel.
 template <int DV>
-__device__ __forceinline__ void decode_epilogue(const AttnArgs& a, RowState<DV / 16>& st,
+__device__ __forceinline__ void decode_epilogue(const AttnArgs& a, RowState<DV / 16, true>& st,
                                                 float* xch_mem, bool bad_w, int wave, int lane,
                                                 int b, int head, int n, int j, bool head_valid,
                                                 int slot) {
@@ -71,12 +84,12 @@ __device__ __forceinline__ void decode_epilogue(const AttnArgs& a, RowState<DV /
 }
 
 // One 32-token step: dequantise K, S^T = K Q^T, online softmax, dequantise V, O^T += V^T P^T.
-template <int DK, int DV>
-__device__ __forceinline__ void decode_step(const StepRaw<DK, DV>& r, int t0, int w1, int j,
+// MASK: the step may hold keys after tlast.
+template <int DK, int DV, bool MASK>
+__device__ __forceinline__ void decode_step(const StepRaw<DK, DV>& r, int t0, int tlast, int j,
                                             const f16x8 (&qf)[DK / 32], float score_c,
-                                            RowState<DV / 16>& st) {
+                                            RowState<DV / 16, true>& st) {
   using S = StepShape<DK, DV>;
-  const int tlast = w1 - 1;
   f16x8 ka[S::NS], kb[S::NS];
   k_operands<DK, DV>(r, ka, kb);
   f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
@@ -85,15 +98,9 @@ __device__ __forceinline__ void decode_step(const StepRaw<DK, DV>& r, int t0, in
     sa = mfma16x16x32(ka[s], qf[s], sa);
     sb = mfma16x16x32(kb[s], qf[s], sb);
   }
+  const f16x8 p = st.template softmax<MASK>(sa, sb, score_c, t0, j, tlast);
   f16x8 vt[S::NT];
-  f16x8 p;
-  if (t0 + kDecodeStep > w1) {  // the wave's last, partial step
-    p = st.template softmax<true>(sa, sb, score_c, t0, j, tlast);
-    v_operands<DK, DV, true>(r, t0, tlast, j, vt);
-  } else {
-    p = st.template softmax<false>(sa, sb, score_c, t0, j, tlast);
-    v_operands<DK, DV, false>(r, t0, tlast, j, vt);
-  }
+  v_operands<DK, DV, MASK>(r, t0, tlast, j, vt);
   st.pv(vt, p);
 }
 
@@ -119,9 +126,11 @@ __device__ __forceinline__ DecodeItem decode_item(const AttnArgs& a, int wave, i
 
 // page_size >= 16: the chunk streams through a per-wave LDS ring several steps deep.
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void decode_ring_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DecodeOcc<DK, DV>::WGS)))
+void decode_ring_kernel(AttnArgs a) {
   using S = StepShape<DK, DV>;
-  using R = RingShape<DK, DV>;
+  constexpr int WL = DecodeOcc<DK, DV>::WAVE_LDS;
+  using R = RingShape<DK, DV, WL>;
   constexpr int XCH_BYTES = 3 * (S::NT * 4 + 3) * 64 * 4;
   constexpr int SMEM = 4 * R::WAVE_BYTES > XCH_BYTES ? 4 * R::WAVE_BYTES : XCH_BYTES;
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
@@ -138,36 +147,48 @@ __global__ __launch_bounds__(256) void decode_ring_kernel(AttnArgs a) {
 
   PagedView<DK, DV, true> view;
   view.init(a, it.b, it.kvh, lane);
-  RingPlan<DK, DV> rp;
+  RingPlan<DK, DV, WL> rp;
   rp.init(lane, view.k_tok, view.v_tok, view.ksf_tok, view.vsf_tok);
   uint8_t* ring = smem + wave * R::WAVE_BYTES;
   const uint32_t ring_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)ring);
   const int tlast = it.w1 - 1;
-  const int nsteps = (it.w1 - it.w0 + kDecodeStep - 1) / kDecodeStep;
   uint32_t bad = 0;
 
-  RowState<S::NT> st;
+  RowState<S::NT, true> st;
   st.init();
+  RingLanes lanes = ring_lanes<DK, DV, WL>(ring_lds, j, n);
+  const int len = it.w1 - it.w0;
+  const int nsteps = (len + kDecodeStep - 1) / kDecodeStep;
+  const int nfull = len / kDecodeStep;  // steps whose 32 keys are all in range
 #pragma unroll
   for (int s = 0; s < R::NST - 1; ++s)
     if (s < nsteps)
-      ring_issue<DK, DV>(rp, ring_lds + s * R::STAGE, view, it.w0 + s * kDecodeStep, tlast, bad);
-  // unrolled by the ring depth so that every stage offset is a compile-time constant
-  for (int i0 = 0; i0 < nsteps; i0 += R::NST) {
+      ring_issue<DK, DV, WL>(rp, ring_lds + s * R::STAGE, view, it.w0 + s * kDecodeStep, tlast,
+                             bad);
+  // Full steps, unrolled by the ring depth so that every stage offset is a constant.
+  // Step i issues step i + NST - 1 (when it exists) into the stage step i - 1 used,
+  // then waits until at most NST - 1 steps are newer than its own.
+  for (int i0 = 0; i0 < nfull; i0 += R::NST) {
 #pragma unroll
     for (int s = 0; s < R::NST; ++s) {
       const int i = i0 + s;
-      if (i < nsteps) {
-        const int ahead = i + R::NST - 1;
-        if (ahead < nsteps)
-          ring_issue<DK, DV>(rp, ring_lds + ((s + R::NST - 1) % R::NST) * R::STAGE, view,
-                             it.w0 + ahead * kDecodeStep, tlast, bad);
-        const uint32_t zero = wait_steps<R::NDMA, R::NST>(min(nsteps - 1 - i, R::NST - 1));
-        StepRaw<DK, DV> raw;
-        ring_read<DK, DV>(ring + s * R::STAGE + zero, j, n, raw);
-        decode_step<DK, DV>(raw, it.w0 + i * kDecodeStep, it.w1, j, qf, score_c, st);
-      }
+      if (i >= nfull) break;
+      const int ahead = i + R::NST - 1;
+      const bool more = ahead < nsteps;
+      if (more)
+        ring_issue<DK, DV, WL>(rp, ring_lds + ((s + R::NST - 1) % R::NST) * R::STAGE, view,
+                           it.w0 + ahead * kDecodeStep, tlast, bad);
+      ring_wait_sel<(R::NST - 1) * R::NDMA>(lanes, more);
+      StepRaw<DK, DV> raw;
+      ring_read<DK, DV>(lanes, s * R::STAGE, raw);
+      decode_step<DK, DV, false>(raw, it.w0 + i * kDecodeStep, tlast, j, qf, score_c, st);
     }
+  }
+  if (nfull < nsteps) {  // the last step is partial; it was issued already
+    ring_wait<0>(lanes);
+    StepRaw<DK, DV> raw;
+    ring_read<DK, DV>(lanes, (uint32_t)(nfull % R::NST) * R::STAGE, raw);
+    decode_step<DK, DV, true>(raw, it.w0 + nfull * kDecodeStep, tlast, j, qf, score_c, st);
   }
   const bool bad_w = __any(bad != 0);
   __syncthreads();  // every wave is done with its ring: the exchange reuses that memory
@@ -193,17 +214,27 @@ __global__ __launch_bounds__(256) void decode_regs_kernel(AttnArgs a) {
   PagedView<DK, DV, false> view;
   view.init(a, it.b, it.kvh, lane);
   const int tlast = it.w1 - 1;
-  RowState<S::NT> st;
+  RowState<S::NT, true> st;
   st.init();
+  const int len = it.w1 - it.w0;
+  const int nsteps = (len + kDecodeStep - 1) / kDecodeStep;
+  const int nfull = len / kDecodeStep;
+  auto t_of = [&](int i) { return it.w0 + i * kDecodeStep; };
+  // r0 holds step i at the top of every iteration; full steps in pairs, unmasked
   StepRaw<DK, DV> r0, r1;
-  if (it.w0 < it.w1) view.load(r0, it.w0, tlast);
-  for (int t0 = it.w0; t0 < it.w1; t0 += 2 * kDecodeStep) {
-    const int t1 = t0 + kDecodeStep;
-    if (t1 < it.w1) view.load(r1, t1, tlast);
-    decode_step<DK, DV>(r0, t0, it.w1, j, qf, score_c, st);
-    if (t1 >= it.w1) break;
-    if (t1 + kDecodeStep < it.w1) view.load(r0, t1 + kDecodeStep, tlast);
-    decode_step<DK, DV>(r1, t1, it.w1, j, qf, score_c, st);
+  if (nsteps > 0) view.load(r0, t_of(0), tlast);
+  int i = 0;
+  for (; i + 1 < nfull; i += 2) {
+    view.load(r1, t_of(i + 1), tlast);
+    decode_step<DK, DV, false>(r0, t_of(i), tlast, j, qf, score_c, st);
+    if (i + 2 < nsteps) view.load(r0, t_of(i + 2), tlast);
+    decode_step<DK, DV, false>(r1, t_of(i + 1), tlast, j, qf, score_c, st);
+  }
+  // at most two steps are left, the second one partial
+  if (i < nsteps) {
+    if (i + 1 < nsteps) view.load(r1, t_of(i + 1), tlast);
+    decode_step<DK, DV, true>(r0, t_of(i), tlast, j, qf, score_c, st);
+    if (i + 1 < nsteps) decode_step<DK, DV, true>(r1, t_of(i + 1), tlast, j, qf, score_c, st);
   }
   const bool bad_w = __any(view.bad != 0);
   decode_epilogue<DV>(a, st, xch, bad_w, wave, lane, it.b, it.head, n, j, it.head_valid, it.slot);
@@ -225,6 +256,22 @@ bool decode_supported(int dk, int dv) {
   const bool okk = dk == 64 || dk == 128 || dk == 256 || dk == 512;
   const bool okv = dv == 64 || dv == 128 || dv == 256 || dv == 512;
   return okk && okv && dv <= dk && !(dk == 512 && dv == 512);
+}
+
+int decode_wgs_per_cu(int dk, int dv) {
+#define NVFP4_DECODE_CASE(K, V) \
+  if (dk == K && dv == V) return DecodeOcc<K, V>::WGS;
+  NVFP4_DECODE_CASE(64, 64)
+  NVFP4_DECODE_CASE(128, 64)
+  NVFP4_DECODE_CASE(128, 128)
+  NVFP4_DECODE_CASE(256, 64)
+  NVFP4_DECODE_CASE(256, 128)
+  NVFP4_DECODE_CASE(256, 256)
+  NVFP4_DECODE_CASE(512, 64)
+  NVFP4_DECODE_CASE(512, 128)
+  NVFP4_DECODE_CASE(512, 256)
+#undef NVFP4_DECODE_CASE
+  return 2;
 }
 
 hipError_t launch_decode(int dk, int dv, int page_shift, const AttnArgs& a, hipStream_t stream) {

@@ -58,15 +58,43 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 // Max / sum over the four lanes l, l^16, l^32, l^48 (the four k-groups of one column).
+// gfx950's permlane swaps exchange 16-lane rows (odd rows of the first operand with
+// even rows of the second) and 32-lane halves; with both operands holding v, the two
+// results hold {v[l], v[l^16]} (resp. {v[l], v[l^32]}) in some order on every lane.
+// The results are copied out as plain integers before the bit casts: a bit cast of a
+// vector element directly reads element 0 whatever the index.
+__device__ __forceinline__ void swap16(float v, float& a, float& b) {
+  const uint32_t x = __builtin_bit_cast(uint32_t, v);
+  const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  const uint32_t r0 = r[0], r1 = r[1];
+  a = __builtin_bit_cast(float, r0);
+  b = __builtin_bit_cast(float, r1);
+}
+__device__ __forceinline__ void swap32(float v, float& a, float& b) {
+  const uint32_t x = __builtin_bit_cast(uint32_t, v);
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  const uint32_t r0 = r[0], r1 = r[1];
+  a = __builtin_bit_cast(float, r0);
+  b = __builtin_bit_cast(float, r1);
+}
+// v_max_f32 as is: fmaxf on values the compiler cannot prove canonical adds a
+// quieting v_max of each input first.
+__device__ __forceinline__ float max_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 __device__ __forceinline__ float max_over_groups(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+  float a, b;
+  swap16(v, a, b);
+  swap32(max_raw(a, b), a, b);
+  return max_raw(a, b);
 }
 __device__ __forceinline__ float sum_over_groups(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+  float a, b;
+  swap16(v, a, b);
+  swap32(a + b, a, b);
+  return a + b;
 }
 
 // Unaligned-size loads of N bytes (N in {1, 2, 4, 8, 16}) into dwords.

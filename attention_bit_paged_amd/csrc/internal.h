@@ -82,6 +82,8 @@ hipError_t launch_quantize(const QuantArgs* k, const QuantArgs* v, int64_t n_tok
                            const int64_t* slots, hipStream_t stream);
 hipError_t launch_decode(int dk, int dv, int page_shift, const AttnArgs& a, hipStream_t stream);
 bool decode_supported(int dk, int dv);
+// Decode workgroups (four waves each) one CU runs at once for this shape.
+int decode_wgs_per_cu(int dk, int dv);
 hipError_t launch_prefill(int dk, int dv, int page_shift, const AttnArgs& a, int rows_per_item,
                           hipStream_t stream);
 bool prefill_supported(int dk, int dv);

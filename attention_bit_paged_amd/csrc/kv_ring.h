@@ -4,19 +4,25 @@
 // scales, each token-major.  The bytes are copied by gfx950's direct global-to-LDS
 // loads (64 lanes x 16 or 4 bytes per instruction, placed in lane order at the LDS
 // address held in m0), so several steps are in flight without spending registers.
-// The copies are issued through inline assembly and waited for with explicit vmcnt
-// counts: inside the streaming loop they are the wave's only vector-memory
-// operations, so "the newest n steps may still be in flight" is an exact count.
+// Every copy takes its 64-bit base from SGPRs and a loop-invariant 32-bit offset per
+// lane, so issuing a step costs no vector instructions: a copy whose lanes fall into
+// several (pool, 16-token half) groups is issued once per group under an exec mask.
+// The copies are waited for with explicit vmcnt counts: inside the streaming loop they
+// are the wave's only vector-memory operations, so "the newest n steps may still be in
+// flight" is an exact count.
 // [XQA] "Support NVFP4 KV cache decode on SM120", changelog: packed K/V and their
 // scale factors are staged on chip before the unpack (there through shared memory
 // with grain-sized copies; here through this ring).
 #pragma once
 
+#include <utility>
+
 #include "attn_step.h"
 
 namespace nvfp4 {
 
-template <int DK, int DV>
+// WAVE_LDS: LDS bytes available to one wave's ring; the ring is 2..4 stages deep.
+template <int DK, int DV, int WAVE_LDS>
 struct RingShape {
   static constexpr int KD = 16 * DK;  // 32 tokens x DK/2 bytes
   static constexpr int VD = 16 * DV;
@@ -30,93 +36,179 @@ struct RingShape {
   static constexpr int N_KD = KD / 1024;  // 16-byte-per-lane copies
   static constexpr int N_VD = VD / 1024;
   static constexpr int N_SF = SFP / 256;  // 4-byte-per-lane copies
-  static constexpr int NDMA = N_KD + N_VD + N_SF;
-  // stages per wave: as many as fit 76 KiB per workgroup of four waves, 2..4
-  static constexpr int NST_RAW = (76 * 1024) / (4 * STAGE);
-  static constexpr int NST = NST_RAW < 2 ? 2 : (NST_RAW > 4 ? 4 : NST_RAW);
-  static constexpr int WAVE_BYTES = NST * STAGE;
+  static constexpr int NCOPY = N_KD + N_VD + N_SF;
   static_assert(KD % 1024 == 0 && VD % 1024 == 0, "ring shape");
+
+  // Group of the bytes lane `lane` moves in copy c: 0/1 K rows of token half 0/1,
+  // 2/3 V rows, 4/5 K scales, 6/7 V scales; -1 for padding lanes (not issued).
+  static constexpr int group(int c, int lane) {
+    if (c < N_KD) return (c * 1024 + lane * 16) / (DK / 2) >= 16 ? 1 : 0;
+    if (c < N_KD + N_VD) return ((c - N_KD) * 1024 + lane * 16) / (DV / 2) >= 16 ? 3 : 2;
+    int byte = (c - N_KD - N_VD) * 256 + lane * 4;
+    if (byte >= KS + VS) return -1;
+    if (byte < KS) return byte / (DK / 16) >= 16 ? 5 : 4;
+    byte -= KS;
+    return byte / (DV / 16) >= 16 ? 7 : 6;
+  }
+  static constexpr uint64_t mask(int c, int g) {
+    uint64_t m = 0;
+    for (int l = 0; l < 64; ++l)
+      if (group(c, l) == g) m |= uint64_t(1) << l;
+    return m;
+  }
+  static constexpr int ndma() {
+    int n = 0;
+    for (int c = 0; c < NCOPY; ++c)
+      for (int g = 0; g < 8; ++g) n += mask(c, g) != 0;
+    return n;
+  }
+  static constexpr int lds_off(int c) {
+    return c < N_KD ? OFF_KD + c * 1024
+                    : (c < N_KD + N_VD ? OFF_VD + (c - N_KD) * 1024
+                                       : OFF_SF + (c - N_KD - N_VD) * 256);
+  }
+  static constexpr int NDMA = ndma();  // copy instructions per stage
+  static constexpr int NST_RAW = WAVE_LDS / STAGE;
+  static constexpr int NST = NST_RAW > 4 ? 4 : NST_RAW;
+  static_assert(NST >= 2, "LDS budget below two stages");
+  static constexpr int WAVE_BYTES = NST * STAGE;
   static_assert(NDMA * (NST - 1) <= 63, "vmcnt range");
 };
 
-// The copies are not declared to touch memory: they only write this wave's ring, which
-// is read after an explicit wait whose result (a zero) feeds the read addresses, so the
-// compiler cannot hoist those reads above it.  Keeping the global view unclobbered lets
-// the page-table reads stay scalar loads.
-__device__ __forceinline__ void dma16(uint32_t lds_addr, const uint8_t* src) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :: "s"(lds_addr), "v"(src));
+// m0 must be written one instruction ahead of the copy that reads it.  The copies are
+// not declared to touch memory: they only write this wave's ring, whose reads take
+// their addresses from the wait below, so the compiler cannot move them above it.
+// Keeping the global view unclobbered lets the page-table reads stay scalar loads.
+template <bool X4>
+__device__ __forceinline__ void dma(uint32_t m0, uint32_t voff, const uint8_t* sbase) {
+  if constexpr (X4)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(m0), "v"(voff), "s"(sbase));
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+                 :: "s"(m0), "v"(voff), "s"(sbase));
 }
-__device__ __forceinline__ void dma4(uint32_t lds_addr, const uint8_t* src) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
-               :: "s"(lds_addr), "v"(src));
+// The same copy for the lanes in (LO, HI) only; exec is restored inside the statement.
+template <bool X4, int LO, int HI>
+__device__ __forceinline__ void dma_masked(uint32_t m0, uint32_t voff, const uint8_t* sbase) {
+  uint64_t save;
+  if constexpr (X4)
+    asm volatile("s_mov_b64 %0, exec\n\ts_mov_b32 exec_lo, %4\n\ts_mov_b32 exec_hi, %5\n\t"
+                 "s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3\n\t"
+                 "s_mov_b64 exec, %0"
+                 : "=&s"(save) : "s"(m0), "v"(voff), "s"(sbase), "n"(LO), "n"(HI));
+  else
+    asm volatile("s_mov_b64 %0, exec\n\ts_mov_b32 exec_lo, %4\n\ts_mov_b32 exec_hi, %5\n\t"
+                 "s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, %3\n\t"
+                 "s_mov_b64 exec, %0"
+                 : "=&s"(save) : "s"(m0), "v"(voff), "s"(sbase), "n"(LO), "n"(HI));
 }
+
+// LDS byte addresses of this lane's reads in stage 0 of its wave's ring.  They pass
+// through every wait (tied asm operands), which both orders the reads after the wait
+// and lets each read use one base register plus an immediate offset.
+struct RingLanes {
+  uint32_t k, ks, v, vs;
+};
+
 template <int N>
-__device__ __forceinline__ uint32_t wait_vm() {
-  uint32_t zero;
-  asm volatile("s_waitcnt vmcnt(%1)\n\ts_mov_b32 %0, 0" : "=s"(zero) : "n"(N));
-  return zero;
+__device__ __forceinline__ void ring_wait(RingLanes& b) {
+  asm volatile("s_waitcnt vmcnt(%4)" : "+v"(b.k), "+v"(b.ks), "+v"(b.v), "+v"(b.vs) : "n"(N));
 }
-// Wait until at most `newer` steps of NDMA copies each are still in flight.  Returns 0.
-template <int NDMA, int NST>
-__device__ __forceinline__ uint32_t wait_steps(int newer) {
-  if (NST > 3 && newer >= 3) return wait_vm<NDMA * 3 <= 63 ? NDMA * 3 : 63>();
-  if (NST > 2 && newer >= 2) return wait_vm<NDMA * 2 <= 63 ? NDMA * 2 : 63>();
-  if (newer >= 1) return wait_vm<NDMA <= 63 ? NDMA : 63>();
-  return wait_vm<0>();
+// Waits for vmcnt(N) when `newer` is set (wave-uniform), else for vmcnt(0).
+template <int N>
+__device__ __forceinline__ void ring_wait_sel(RingLanes& b, uint32_t newer) {
+  asm volatile("s_cmp_eq_u32 %4, 0\n\ts_cbranch_scc1 1f\n\ts_waitcnt vmcnt(%5)\n\ts_branch 2f\n"
+               "1:\n\ts_waitcnt vmcnt(0)\n2:"
+               : "+v"(b.k), "+v"(b.ks), "+v"(b.v), "+v"(b.vs)
+               : "s"(__builtin_amdgcn_readfirstlane(newer)), "n"(N)
+               : "scc");
 }
 
-// Per-lane copy plan of one stage: for every copy instruction, which pool, which
-// 16-token half and which byte offset inside that half this lane fetches.
-template <int DK, int DV>
+// Per-lane copy offsets of one stage, relative to the lane's group base.
+template <int DK, int DV, int WAVE_LDS>
 struct RingPlan {
-  using R = RingShape<DK, DV>;
-  uint32_t off[R::NDMA];     // byte offset from the half's base
-  uint32_t sel[R::NDMA];     // bit 0: second half; bit 1: V pool (scale copies only)
+  using R = RingShape<DK, DV, WAVE_LDS>;
+  uint32_t off[R::NCOPY];
 
-  // token strides in bytes: k_tok/v_tok (data), ks_tok/vs_tok (scales)
+  // token strides in bytes: k_tok/v_tok (data), ks_tok/vs_tok (scales); the host
+  // keeps 16 token strides plus a row inside 32 bits
   __device__ __forceinline__ void init(int lane, int64_t k_tok, int64_t v_tok, int64_t ks_tok,
                                        int64_t vs_tok) {
 #pragma unroll
     for (int i = 0; i < R::N_KD; ++i) {
       const int byte = i * 1024 + lane * 16;
       const int t = byte / (DK / 2), in_row = byte % (DK / 2);
-      off[i] = (uint32_t)((t & 15) * k_tok) + in_row;
-      sel[i] = t >= 16;
+      off[i] = (uint32_t)(t & 15) * (uint32_t)k_tok + in_row;
     }
 #pragma unroll
     for (int i = 0; i < R::N_VD; ++i) {
       const int byte = i * 1024 + lane * 16;
       const int t = byte / (DV / 2), in_row = byte % (DV / 2);
-      off[R::N_KD + i] = (uint32_t)((t & 15) * v_tok) + in_row;
-      sel[R::N_KD + i] = t >= 16;
+      off[R::N_KD + i] = (uint32_t)(t & 15) * (uint32_t)v_tok + in_row;
     }
 #pragma unroll
     for (int i = 0; i < R::N_SF; ++i) {
       int byte = i * 256 + lane * 4;
-      if (byte >= R::KS + R::VS) {  // padding: re-read a valid dword, land past the scales
-        off[R::N_KD + R::N_VD + i] = 0;
-        sel[R::N_KD + R::N_VD + i] = 0;
-        continue;
+      uint32_t o = 0;
+      if (byte < R::KS) {
+        o = (uint32_t)((byte / (DK / 16)) & 15) * (uint32_t)ks_tok + byte % (DK / 16);
+      } else if (byte < R::KS + R::VS) {
+        byte -= R::KS;
+        o = (uint32_t)((byte / (DV / 16)) & 15) * (uint32_t)vs_tok + byte % (DV / 16);
       }
-      const bool vpool = byte >= R::KS;
-      if (vpool) byte -= R::KS;
-      const int row = vpool ? DV / 16 : DK / 16;
-      const int t = byte / row, in_row = byte % row;
-      off[R::N_KD + R::N_VD + i] = (uint32_t)((t & 15) * (vpool ? vs_tok : ks_tok)) + in_row;
-      sel[R::N_KD + R::N_VD + i] = (t >= 16 ? 1u : 0u) | (vpool ? 2u : 0u);
+      off[R::N_KD + R::N_VD + i] = o;
     }
   }
 };
 
+namespace ring_detail {
+
+template <int DK, int DV, int WL, int C, int G>
+__device__ __forceinline__ void issue_group(uint32_t m0, uint32_t voff,
+                                            const uint8_t* const (&base)[8]) {
+  using R = RingShape<DK, DV, WL>;
+  constexpr uint64_t M = R::mask(C, G);
+  constexpr bool X4 = C < R::N_KD + R::N_VD;
+  if constexpr (M == ~uint64_t(0)) {
+    dma<X4>(m0, voff, base[G]);
+  } else if constexpr (M != 0) {
+    dma_masked<X4, (int)(uint32_t)M, (int)(uint32_t)(M >> 32)>(m0, voff, base[G]);
+  }
+}
+
+template <int DK, int DV, int WL, int C>
+__device__ __forceinline__ void issue_copy(uint32_t stage_lds, const RingPlan<DK, DV, WL>& rp,
+                                           const uint8_t* const (&base)[8]) {
+  using R = RingShape<DK, DV, WL>;
+  const uint32_t m0 = stage_lds + R::lds_off(C);
+  issue_group<DK, DV, WL, C, 0>(m0, rp.off[C], base);
+  issue_group<DK, DV, WL, C, 1>(m0, rp.off[C], base);
+  issue_group<DK, DV, WL, C, 2>(m0, rp.off[C], base);
+  issue_group<DK, DV, WL, C, 3>(m0, rp.off[C], base);
+  issue_group<DK, DV, WL, C, 4>(m0, rp.off[C], base);
+  issue_group<DK, DV, WL, C, 5>(m0, rp.off[C], base);
+  issue_group<DK, DV, WL, C, 6>(m0, rp.off[C], base);
+  issue_group<DK, DV, WL, C, 7>(m0, rp.off[C], base);
+}
+
+template <int DK, int DV, int WL, int... Cs>
+__device__ __forceinline__ void issue_all(std::integer_sequence<int, Cs...>, uint32_t stage_lds,
+                                          const RingPlan<DK, DV, WL>& rp,
+                                          const uint8_t* const (&base)[8]) {
+  (issue_copy<DK, DV, WL, Cs>(stage_lds, rp, base), ...);
+}
+
+}  // namespace ring_detail
+
 // Issues the copies of the step starting at token t0 into the stage at lds_stage.
 // Bases of the two 16-token halves come from two page-table entries; a half that
 // starts after tlast reuses the first half's page (its bytes are never used).
-template <int DK, int DV>
-__device__ __forceinline__ void ring_issue(const RingPlan<DK, DV>& rp, uint32_t lds_stage,
+template <int DK, int DV, int WL>
+__device__ __forceinline__ void ring_issue(const RingPlan<DK, DV, WL>& rp, uint32_t lds_stage,
                                            const PagedView<DK, DV, true>& pv, int t0, int tlast,
                                            uint32_t& bad) {
-  using R = RingShape<DK, DV>;
+  using R = RingShape<DK, DV, WL>;
   // The page table is read-only while the kernel runs: reading it through the
   // constant address space keeps these uniform reads scalar loads.
   const __attribute__((address_space(4))) int32_t* pt =
@@ -138,48 +230,77 @@ __device__ __forceinline__ void ring_issue(const RingPlan<DK, DV>& rp, uint32_t 
   auto at = [](const uint8_t* base, int pg, int sl, int64_t page_stride, int64_t tok_stride) {
     return base + (int64_t)pg * (int32_t)page_stride + (int64_t)sl * (int32_t)tok_stride;
   };
-  const uint8_t* kb[2] = {at(pv.kdat, pg0, s0, pv.k_page, pv.k_tok), at(pv.kdat, pg1, s1, pv.k_page, pv.k_tok)};
-  const uint8_t* vb[2] = {at(pv.vdat, pg0, s0, pv.v_page, pv.v_tok), at(pv.vdat, pg1, s1, pv.v_page, pv.v_tok)};
-  const uint8_t* ksb[2] = {at(pv.ksf, pg0, s0, pv.ksf_page, pv.ksf_tok),
-                           at(pv.ksf, pg1, s1, pv.ksf_page, pv.ksf_tok)};
-  const uint8_t* vsb[2] = {at(pv.vsf, pg0, s0, pv.vsf_page, pv.vsf_tok),
-                           at(pv.vsf, pg1, s1, pv.vsf_page, pv.vsf_tok)};
+  const uint8_t* const base[8] = {
+      at(pv.kdat, pg0, s0, pv.k_page, pv.k_tok),     at(pv.kdat, pg1, s1, pv.k_page, pv.k_tok),
+      at(pv.vdat, pg0, s0, pv.v_page, pv.v_tok),     at(pv.vdat, pg1, s1, pv.v_page, pv.v_tok),
+      at(pv.ksf, pg0, s0, pv.ksf_page, pv.ksf_tok),  at(pv.ksf, pg1, s1, pv.ksf_page, pv.ksf_tok),
+      at(pv.vsf, pg0, s0, pv.vsf_page, pv.vsf_tok),  at(pv.vsf, pg1, s1, pv.vsf_page, pv.vsf_tok)};
   // the previous reads of this stage were consumed already; make sure they completed
   asm volatile("s_waitcnt lgkmcnt(0)");
+  ring_detail::issue_all<DK, DV, WL>(std::make_integer_sequence<int, R::NCOPY>{}, lds_stage, rp,
+                                      base);
+}
+
+// LDS addresses of this lane's reads in stage 0 of the ring at ring_lds.
+template <int DK, int DV, int WL>
+__device__ __forceinline__ RingLanes ring_lanes(uint32_t ring_lds, int j, int n) {
+  using R = RingShape<DK, DV, WL>;
+  using S = StepShape<DK, DV>;
+  const int ta = 8 * (n >> 2) + (n & 3);
+  RingLanes b;
+  b.k = ring_lds + R::OFF_KD + ta * (DK / 2) + j * S::KB;
+  b.ks = ring_lds + R::OFF_SF + ta * (DK / 16) + j * S::KSF;
+  b.v = ring_lds + R::OFF_VD + 8 * j * (DV / 2) + n * S::VB;
+  b.vs = ring_lds + R::OFF_SF + R::KS + 8 * j * (DV / 16) + (n * DV / 16) / 16;
+  return b;
+}
+
+template <int N>
+__device__ __forceinline__ void lds_load(uint32_t addr, uint32_t* out) {
+  typedef __attribute__((address_space(3))) const uint8_t* lds_u8;
+  typedef __attribute__((address_space(3))) const uint16_t* lds_u16;
+  typedef __attribute__((address_space(3))) const uint32_t* lds_u32;
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  typedef __attribute__((address_space(3))) const u32x2* lds_u64;
+  typedef __attribute__((address_space(3))) const u32x4* lds_u128;
+  if constexpr (N == 1) {
+    out[0] = *(lds_u8)(size_t)addr;
+  } else if constexpr (N == 2) {
+    out[0] = *(lds_u16)(size_t)addr;
+  } else if constexpr (N == 4) {
+    out[0] = *(lds_u32)(size_t)addr;
+  } else if constexpr (N == 8) {
+    const u32x2 v = *(lds_u64)(size_t)addr;
+    out[0] = v[0];
+    out[1] = v[1];
+  } else {
+    static_assert(N % 16 == 0, "load size");
 #pragma unroll
-  for (int i = 0; i < R::N_KD; ++i)
-    dma16(lds_stage + R::OFF_KD + i * 1024, (rp.sel[i] ? kb[1] : kb[0]) + rp.off[i]);
-#pragma unroll
-  for (int i = 0; i < R::N_VD; ++i) {
-    const int c = R::N_KD + i;
-    dma16(lds_stage + R::OFF_VD + i * 1024, (rp.sel[c] ? vb[1] : vb[0]) + rp.off[c]);
-  }
-#pragma unroll
-  for (int i = 0; i < R::N_SF; ++i) {
-    const int c = R::N_KD + R::N_VD + i;
-    const uint32_t s = rp.sel[c];
-    const uint8_t* base = (s & 2) ? ((s & 1) ? vsb[1] : vsb[0]) : ((s & 1) ? ksb[1] : ksb[0]);
-    dma4(lds_stage + R::OFF_SF + i * 256, base + rp.off[c]);
+    for (int i = 0; i < N / 16; ++i) {
+      const u32x4 v = *(lds_u128)(size_t)(addr + 16 * i);
+      out[4 * i + 0] = v[0];
+      out[4 * i + 1] = v[1];
+      out[4 * i + 2] = v[2];
+      out[4 * i + 3] = v[3];
+    }
   }
 }
 
-// Reads a step's raw bytes for this lane from an LDS stage, in the register layout the
-// step helpers expect (the same as a direct load from the pool).
+// Reads a step's raw bytes for this lane from the stage `stage_off` bytes past the
+// lane addresses, in the register layout the step helpers expect (the same as a
+// direct load from the pool).
 template <int DK, int DV>
-__device__ __forceinline__ void ring_read(const uint8_t* stage, int j, int n, StepRaw<DK, DV>& r) {
-  using R = RingShape<DK, DV>;
+__device__ __forceinline__ void ring_read(const RingLanes& b, uint32_t stage_off,
+                                          StepRaw<DK, DV>& r) {
   using S = StepShape<DK, DV>;
-  const int ta = 8 * (n >> 2) + (n & 3);
-  const int tb = ta + 4;
-  load_bytes<S::KB>(stage + R::OFF_KD + ta * (DK / 2) + j * S::KB, r.ka);
-  load_bytes<S::KB>(stage + R::OFF_KD + tb * (DK / 2) + j * S::KB, r.kb);
-  load_bytes<S::KSF>(stage + R::OFF_SF + ta * (DK / 16) + j * S::KSF, r.ksa);
-  load_bytes<S::KSF>(stage + R::OFF_SF + tb * (DK / 16) + j * S::KSF, r.ksb);
+  lds_load<S::KB>(b.k + stage_off, r.ka);
+  lds_load<S::KB>(b.k + stage_off + 4 * (DK / 2), r.kb);
+  lds_load<S::KSF>(b.ks + stage_off, r.ksa);
+  lds_load<S::KSF>(b.ks + stage_off + 4 * (DK / 16), r.ksb);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int t = 8 * j + i;
-    load_bytes<S::VB>(stage + R::OFF_VD + t * (DV / 2) + n * S::VB, r.vd[i]);
-    load_bytes<S::VSFB>(stage + R::OFF_SF + R::KS + t * (DV / 16) + (n * DV / 16) / 16, &r.vs[i]);
+    lds_load<S::VB>(b.v + stage_off + i * (DV / 2), r.vd[i]);
+    lds_load<S::VSFB>(b.vs + stage_off + i * (DV / 16), &r.vs[i]);
   }
 }
 

@@ -10,9 +10,22 @@ namespace nvfp4 {
 
 namespace {
 
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
 // Partials of split row groups, after the attention kernel: one wave per (merge
 // record, row).  A row is one qo head of the group (decode) or one (query, qo head) pair
-// of a query tile (prefill); each partial holds a normalised O row and its LSE.
+// of a query tile (prefill); each partial holds a normalised O row and its LSE.  The
+// partials' LSEs are read by the lanes in parallel (64 partials at a time); each
+// lane then sums its DV/64 value dims over the partials, several loads in flight.
 template <int DV>
 __global__ __launch_bounds__(256) void merge_partials_kernel(AttnArgs a, int n_merges, int prefill) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -37,29 +50,62 @@ __global__ __launch_bounds__(256) void merge_partials_kernel(AttnArgs a, int n_m
     head = kvh * a.group + row0 + r;
     orow = b;
   }
-  // lane covers value dims [lane * DV/64, (lane+1) * DV/64)
-  constexpr int PER = DV / 64;
+  constexpr int PER = DV / 64;  // lane covers value dims [lane * PER, (lane + 1) * PER)
+  const int64_t rps = a.rows_per_slot;
+  const int64_t row_of_first = (int64_t)first * rps + r;  // partial p: row_of_first + p * rps
+  auto lse_of = [&](int p) { return p < np ? a.part_lse[row_of_first + (int64_t)p * rps] : -INFINITY; };
+
   float mx = -INFINITY;
-  bool any_nan = false;
-  for (int p = 0; p < np; ++p) {
-    const float lp = a.part_lse[(int64_t)(first + p) * a.rows_per_slot + r];
-    any_nan |= lp != lp;
+  bool nan = false;
+  for (int p0 = 0; p0 < np; p0 += 64) {
+    const float lp = lse_of(p0 + lane);
+    nan |= lp != lp;
     mx = fmaxf(mx, lp);
   }
+  mx = wave_max(mx);
+  const bool any_nan = __any(nan);
+
   float acc[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) acc[k] = 0.f;
   float wsum = 0.f;
   if (mx > -INFINITY) {
-    for (int p = 0; p < np; ++p) {
-      const int64_t prow = (int64_t)(first + p) * a.rows_per_slot + r;
-      const float lp = a.part_lse[prow];
-      const float w = lp > -INFINITY ? __expf(lp - mx) : 0.f;
+    for (int p0 = 0; p0 < np; p0 += 64) {
+      const float lp = lse_of(p0 + lane);
+      const float w = lp > -INFINITY ? __expf(lp - mx) : 0.f;  // weight of partial p0 + lane
       wsum += w;
-      const float* src = a.part_o + prow * DV + lane * PER;
+      const int cnt = min(64, np - p0);
+      const float* src = a.part_o + (row_of_first + (int64_t)p0 * rps) * DV + lane * PER;
+      const int64_t step = rps * DV;
+      auto add = [&](int q) {
+        const float wq = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), q));
+        const float* s = src + q * step;
+        if constexpr (PER == 1) {
+          acc[0] += wq * s[0];
+        } else if constexpr (PER == 2) {
+          const float2 v = *reinterpret_cast<const float2*>(s);
+          acc[0] += wq * v.x;
+          acc[1] += wq * v.y;
+        } else {
 #pragma unroll
-      for (int k = 0; k < PER; ++k) acc[k] += w * src[k];
+          for (int k = 0; k < PER; k += 4) {
+            const float4 v = *reinterpret_cast<const float4*>(s + k);
+            acc[k] += wq * v.x;
+            acc[k + 1] += wq * v.y;
+            acc[k + 2] += wq * v.z;
+            acc[k + 3] += wq * v.w;
+          }
+        }
+      };
+      int q = 0;
+      for (; q + 8 <= cnt; q += 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) add(q + u);
+      }
+      for (; q < cnt; ++q) add(q);
     }
+    wsum = wave_sum(wsum);
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   float* dst = a.o + orow * a.o_s_row + (int64_t)head * a.o_s_head + lane * PER;

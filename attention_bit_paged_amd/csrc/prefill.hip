@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a) {
   view.init(a, b, kvh, lane);
   const int tlast = kv1 - 1;
 
-  RowState<S::NT> st[NR];
+  RowState<S::NT, false> st[NR];
 #pragma unroll
   for (int rg = 0; rg < NR; ++rg) st[rg].init();
 
