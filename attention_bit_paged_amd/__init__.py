@@ -17,8 +17,8 @@ import torch
 from ._lib import (EXPORTS, STATUS, WORK_FIELDS, KVPoolStruct, NVFP4Error, PlanInfoStruct,
                    check, lib)
 
-__all__ = ["KVPool", "Plan", "quantize_kv", "batch_decode", "batch_prefill", "merge_states",
-           "NVFP4Error", "lib", "version", "EXPORTS"]
+__all__ = ["KVPool", "Plan", "Prepared", "quantize_kv", "batch_decode", "batch_prefill",
+           "merge_partials", "merge_states", "NVFP4Error", "lib", "version", "EXPORTS"]
 
 
 def version() -> str:
@@ -76,6 +76,12 @@ class KVPool:
         return cls(data, sf, head_dim=head_dim, layout=layout, global_scale=global_scale)
 
     def struct(self) -> KVPoolStruct:
+        """The C view of this pool (built once: the tensors of a pool never change)."""
+        if getattr(self, "_struct", None) is None:
+            self._struct = self._make_struct()
+        return self._struct
+
+    def _make_struct(self) -> KVPoolStruct:
         d, s = self.data.stride(), self.sf.stride()
         if self.layout == "HND":
             dp, dh, dt = d[0], d[1], d[2]
@@ -88,8 +94,22 @@ class KVPool:
                             self.global_scale)
 
 
+class Prepared:
+    """One library call with its arguments marshalled once (``prepare=True`` on the
+    calls below).  Calling it launches again on the same stream with the same tensors,
+    whose contents may change between calls but whose storage must stay alive; it
+    keeps references to them.  For launch loops where per-call Python work matters."""
+
+    def __init__(self, fn, args, keep):
+        self._fn, self._args, self._keep = fn, args, keep
+
+    def __call__(self) -> None:
+        check(self._fn(*self._args))
+
+
 def quantize_kv(k: Optional[torch.Tensor], v: Optional[torch.Tensor], slot_mapping: torch.Tensor,
-                k_pool: Optional[KVPool], v_pool: Optional[KVPool], stream=None) -> None:
+                k_pool: Optional[KVPool], v_pool: Optional[KVPool], stream=None,
+                prepare: bool = False):
     """Quantise bf16 K/V rows ``[n_tokens, H, D]`` into their pools at ``slot_mapping``
     (int64 ``page * page_size + offset``; negative = skip)."""
     n = (k if k is not None else v).shape[0]
@@ -100,12 +120,14 @@ def quantize_kv(k: Optional[torch.Tensor], v: Optional[torch.Tensor], slot_mappi
         raise ValueError("slot_mapping must be int64 with one entry per token")
     ks = k_pool.struct() if k_pool is not None else None
     vs = v_pool.struct() if v_pool is not None else None
-    check(lib.nvfp4_quantize_kv(
-        _ptr(k), k.stride(0) if k is not None else 0, k.stride(1) if k is not None else 0,
-        _ptr(v), v.stride(0) if v is not None else 0, v.stride(1) if v is not None else 0,
-        n, _ptr(slot_mapping),
-        ctypes.byref(ks) if ks is not None else None, ctypes.byref(vs) if vs is not None else None,
-        _stream(stream)))
+    args = (_ptr(k), k.stride(0) if k is not None else 0, k.stride(1) if k is not None else 0,
+            _ptr(v), v.stride(0) if v is not None else 0, v.stride(1) if v is not None else 0,
+            n, _ptr(slot_mapping),
+            ctypes.byref(ks) if ks is not None else None,
+            ctypes.byref(vs) if vs is not None else None, _stream(stream))
+    if prepare:
+        return Prepared(lib.nvfp4_quantize_kv, args, (k, v, slot_mapping, k_pool, v_pool, ks, vs))
+    check(lib.nvfp4_quantize_kv(*args))
 
 
 class Plan:
@@ -168,8 +190,13 @@ class Plan:
     def upload(self, workspace: torch.Tensor, stream=None) -> None:
         check(lib.nvfp4_plan_upload(self._h, _ptr(workspace), workspace.numel(), _stream(stream)))
 
+    def set_deferred_merge(self, deferred: bool = True) -> None:
+        """Runs leave split rows' partials for ``merge_partials`` (nvfp4_plan_set_deferred_merge)."""
+        check(lib.nvfp4_plan_set_deferred_merge(self._h, int(bool(deferred))))
 
-def _attn(fn, plan: Plan, q, page_table, k_pool, v_pool, sm_scale, workspace, out, lse, stream):
+
+def _attn(fn, plan: Plan, q, page_table, k_pool, v_pool, sm_scale, workspace, out, lse, stream,
+          prepare=False):
     rows = q.shape[0]
     if q.dtype != torch.bfloat16 or q.dim() != 3 or q.stride(-1) != 1:
         raise ValueError("q must be bf16 [rows, num_qo_heads, head_dim_qk], last dim contiguous")
@@ -184,28 +211,47 @@ def _attn(fn, plan: Plan, q, page_table, k_pool, v_pool, sm_scale, workspace, ou
             or not lse.is_contiguous():
         raise ValueError("out must be fp32 with a contiguous last dim; lse fp32 contiguous")
     ks, vs = k_pool.struct(), v_pool.struct()
-    check(fn(plan.handle, _ptr(q), q.stride(0), q.stride(1), _ptr(page_table), page_table.stride(0),
-             ctypes.byref(ks), ctypes.byref(vs), float(sm_scale), _ptr(workspace),
-             workspace.numel(), _ptr(out), out.stride(0), out.stride(1), _ptr(lse), _stream(stream)))
+    args = (plan.handle, _ptr(q), q.stride(0), q.stride(1), _ptr(page_table), page_table.stride(0),
+            ctypes.byref(ks), ctypes.byref(vs), float(sm_scale), _ptr(workspace),
+            workspace.numel(), _ptr(out), out.stride(0), out.stride(1), _ptr(lse), _stream(stream))
+    if prepare:
+        return Prepared(fn, args, (plan, q, page_table, k_pool, v_pool, ks, vs, workspace, out, lse))
+    check(fn(*args))
     return out, lse
 
 
 def batch_decode(plan: Plan, q: torch.Tensor, page_table: torch.Tensor, k_pool: KVPool,
                  v_pool: KVPool, sm_scale: float, workspace: torch.Tensor,
                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                 stream=None):
-    """Decode attention; returns (O fp32 [batch, Hq, Dv], LSE fp32 [batch, Hq])."""
+                 stream=None, prepare: bool = False):
+    """Decode attention; returns (O fp32 [batch, Hq, Dv], LSE fp32 [batch, Hq]), or a
+    ``Prepared`` call with ``prepare=True``."""
     return _attn(lib.nvfp4_batch_decode, plan, q, page_table, k_pool, v_pool, sm_scale,
-                 workspace, out, lse, stream)
+                 workspace, out, lse, stream, prepare)
 
 
 def batch_prefill(plan: Plan, q: torch.Tensor, page_table: torch.Tensor, k_pool: KVPool,
                   v_pool: KVPool, sm_scale: float, workspace: torch.Tensor,
                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                  stream=None):
-    """Prefill / extend attention; returns (O fp32 [total_q, Hq, Dv], LSE fp32 [total_q, Hq])."""
+                  stream=None, prepare: bool = False):
+    """Prefill / extend attention; returns (O fp32 [total_q, Hq, Dv], LSE fp32 [total_q, Hq]),
+    or a ``Prepared`` call with ``prepare=True``."""
     return _attn(lib.nvfp4_batch_prefill, plan, q, page_table, k_pool, v_pool, sm_scale,
-                 workspace, out, lse, stream)
+                 workspace, out, lse, stream, prepare)
+
+
+def merge_partials(plan: Plan, workspace: torch.Tensor, out: torch.Tensor, lse: torch.Tensor,
+                   stream=None, prepare: bool = False):
+    """Write the split rows of a deferred-merge run into out / lse (nvfp4_merge_partials)."""
+    if out.dtype != torch.float32 or out.dim() != 3 or out.stride(-1) != 1 \
+            or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("out must be fp32 [rows, heads, Dv] with a contiguous last dim; lse fp32")
+    args = (plan.handle, _ptr(workspace), workspace.numel(), _ptr(out), out.stride(0),
+            out.stride(1), _ptr(lse), _stream(stream))
+    if prepare:
+        return Prepared(lib.nvfp4_merge_partials, args, (plan, workspace, out, lse))
+    check(lib.nvfp4_merge_partials(*args))
+    return out, lse
 
 
 def merge_states(o_parts: torch.Tensor, lse_parts: torch.Tensor, out=None, lse=None, stream=None):

@@ -1,8 +1,9 @@
 """ctypes view of ``include/nvfp4_attn.h``: struct layouts, signatures and errors.
 
 Argument marshalling only; every computation happens in the HIP library.  The
-library must have been built (``python -m attention_bit_paged_amd.build``); a
-missing library raises ImportError instead of falling back to anything else.
+library must have been built (``python attention_bit_paged_amd/build.py``); a missing
+library, or one without every entry point, raises ImportError instead of falling
+back to anything else.
 """
 from __future__ import annotations
 
@@ -25,7 +26,7 @@ EXPORTS = (
     "nvfp4_last_error", "nvfp4_version", "nvfp4_quantize_kv", "nvfp4_plan_create",
     "nvfp4_plan_destroy", "nvfp4_plan_workspace_bytes", "nvfp4_plan_get_info",
     "nvfp4_plan_get_work", "nvfp4_plan_upload", "nvfp4_batch_decode", "nvfp4_batch_prefill",
-    "nvfp4_merge_states",
+    "nvfp4_plan_set_deferred_merge", "nvfp4_merge_partials", "nvfp4_merge_states",
 )
 
 WORK_FIELDS = ("request", "kv_head", "row_begin", "row_count", "kv_begin", "kv_end",
@@ -73,7 +74,7 @@ class NVFP4Error(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing; build it with `python -m attention_bit_paged_amd.build`")
+            f"{LIB_PATH} is missing; build it with `python attention_bit_paged_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
                              ctypes.c_size_t)
@@ -93,9 +94,14 @@ def _load():
                                               vp, i64, i64, vp, vp]),
         "nvfp4_batch_prefill": (ctypes.c_int, [vp, vp, i64, i64, vp, i64, pool_p, pool_p, f32, vp, sz,
                                                vp, i64, i64, vp, vp]),
+        "nvfp4_plan_set_deferred_merge": (ctypes.c_int, [vp, i32]),
+        "nvfp4_merge_partials": (ctypes.c_int, [vp, vp, sz, vp, i64, i64, vp, vp]),
         "nvfp4_merge_states": (ctypes.c_int, [vp, vp, i64, i32, i32, i32, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
+        if not hasattr(lib, name):
+            raise ImportError(f"{LIB_PATH} does not export {name}; rebuild it with "
+                              "`python attention_bit_paged_amd/build.py`")
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args

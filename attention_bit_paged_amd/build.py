@@ -1,7 +1,8 @@
 """Build the gfx950 shared library ``libnvfp4_attn.so`` in-tree with hipcc.
 
-Usage: ``python -m attention_bit_paged_amd.build`` (or ``build()`` from Python).
-Every call compiles all sources (objects under ``_build/``) and relinks.
+Usage: ``python attention_bit_paged_amd/build.py`` (run by path: importing the package
+loads the library this script builds).  Every call compiles all sources (objects
+under ``_build/``) and relinks.
 """
 from __future__ import annotations
 

@@ -120,6 +120,11 @@ nvfp4_status check_pool(const nvfp4_kv_pool* p, const char* name, int head_dim,
       p->sf_stride_page > kMaxStride || p->sf_stride_head > kMaxStride ||
       p->sf_stride_token > kMaxStride)
     return fail(NVFP4_E_SHAPE, "%s strides must be below 2^31 bytes", name);
+  // the streaming copies address 16 consecutive token slots from one base with a 32-bit
+  // offset per lane
+  const int64_t kMaxTokStride = int64_t(1) << 27;
+  if (p->stride_token >= kMaxTokStride || p->sf_stride_token >= kMaxTokStride)
+    return fail(NVFP4_E_SHAPE, "%s token strides must be below 2^27 bytes", name);
   return NVFP4_OK;
 }
 
@@ -156,6 +161,7 @@ struct nvfp4_plan {
   size_t off_work = 0, off_merge = 0, off_kvlens = 0, off_indptr = 0,
          off_part_o = 0, off_part_lse = 0, ws_bytes = 0;
   void* uploaded_to = nullptr;
+  int defer_merge = 0;  // runs leave split rows' partials for nvfp4_merge_partials
 };
 
 extern "C" {
@@ -515,7 +521,7 @@ nvfp4_status run(const nvfp4_plan* plan, bool prefill, const void* q, int64_t q_
     return fail(NVFP4_E_HIP, "%s launch failed: %s", prefill ? "prefill" : "decode",
                 hipGetErrorString(e));
   const int n_merges = (int)(plan->merges.size() / kMergeFields);
-  if (n_merges > 0) {
+  if (n_merges > 0 && !plan->defer_merge) {
     e = launch_merge_partials(a, n_merges, plan->head_dim_vo, plan->prefill, s);
     if (e != hipSuccess) return fail(NVFP4_E_HIP, "merge launch failed: %s", hipGetErrorString(e));
   }
@@ -544,6 +550,51 @@ nvfp4_status nvfp4_batch_prefill(const nvfp4_plan* plan, const void* q, int64_t 
                                  int64_t o_stride_head, float* lse, void* stream) {
   return run(plan, true, q, q_stride_tok, q_stride_head, page_table, pt_stride, k_pool, v_pool,
              sm_scale, workspace, workspace_bytes, o, o_stride_tok, o_stride_head, lse, stream);
+}
+
+nvfp4_status nvfp4_plan_set_deferred_merge(nvfp4_plan* plan, int32_t deferred) {
+  if (!plan) return fail(NVFP4_E_INVALID, "plan is NULL");
+  plan->defer_merge = deferred != 0;
+  return ok();
+}
+
+nvfp4_status nvfp4_merge_partials(const nvfp4_plan* plan, void* workspace, size_t workspace_bytes,
+                                  float* o, int64_t o_stride_row, int64_t o_stride_head, float* lse,
+                                  void* stream) {
+  if (!plan) return fail(NVFP4_E_INVALID, "plan is NULL");
+  const int n_merges = (int)(plan->merges.size() / kMergeFields);
+  if (n_merges == 0) return ok();
+  if (!workspace) return fail(NVFP4_E_WORKSPACE, "workspace is NULL");
+  if (workspace_bytes < plan->ws_bytes)
+    return fail(NVFP4_E_WORKSPACE, "workspace has %zu bytes, plan needs %zu", workspace_bytes,
+                plan->ws_bytes);
+  if (plan->uploaded_to != workspace)
+    return fail(NVFP4_E_WORKSPACE, "the plan was not uploaded to this workspace (nvfp4_plan_upload)");
+  if (!o) return fail(NVFP4_E_INVALID, "o is NULL");
+  if (!lse) return fail(NVFP4_E_INVALID, "lse is NULL");
+  if (!aligned(o, 16) || o_stride_row % 4 || o_stride_head % 4 || o_stride_row < 0 ||
+      o_stride_head < 0)
+    return fail(NVFP4_E_SHAPE, "o rows must be 16-byte aligned (strides multiples of 4 elements)");
+  if (!aligned(lse, 4)) return fail(NVFP4_E_SHAPE, "lse must be 4-byte aligned");
+  if (nvfp4_status st = check_device()) return st;
+  AttnArgs a;
+  std::memset(&a, 0, sizeof(a));
+  uint8_t* w = static_cast<uint8_t*>(workspace);
+  a.qo_indptr = reinterpret_cast<const int32_t*>(w + plan->off_indptr);
+  a.o = o;
+  a.o_s_row = o_stride_row;
+  a.o_s_head = o_stride_head;
+  a.lse = lse;
+  a.part_o = reinterpret_cast<float*>(w + plan->off_part_o);
+  a.part_lse = reinterpret_cast<float*>(w + plan->off_part_lse);
+  a.num_qo_heads = plan->num_qo_heads;
+  a.group = plan->group;
+  a.rows_per_slot = plan->rows_per_slot;
+  a.merges = reinterpret_cast<const int32_t*>(w + plan->off_merge);
+  const hipError_t e = launch_merge_partials(a, n_merges, plan->head_dim_vo, plan->prefill,
+                                             static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(NVFP4_E_HIP, "merge launch failed: %s", hipGetErrorString(e));
+  return ok();
 }
 
 nvfp4_status nvfp4_merge_states(const float* o_parts, const float* lse_parts, int64_t rows,

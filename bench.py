@@ -4,28 +4,45 @@
 Default workload: batch decode (64 requests, kv_len ~ U[512, 8192], 32 qo / 8 kv heads,
 head dim 128, page size 16, 40k-page pool in a seeded random permutation, split-KV
 with 256-token chunks).  One step = append the step's new K/V token of every request
-(NVFP4 quantise into its slot) + the decode over the paged cache (split chunks merged
-by LSE).  The plan is built once (the lengths do not change between steps) and its
-host time is reported separately.  Inputs are resident in HBM before timing starts;
-three independent pool sets are rotated so that the 256 MB Infinity Cache cannot
-serve a step from the previous one.
+(NVFP4 quantise into its slot) + the attention pass over the paged cache + the LSE
+merge of the split rows.  The plan is built once (the lengths do not change between
+steps) and its host time is reported separately.  Inputs are resident in HBM before
+timing starts; three independent pool sets are rotated so that the 256 MB Infinity
+Cache cannot serve a step from the previous one.
 
-Prints one JSON line.  ``value`` is the decode's KV GB/s (packed e2m1 bytes plus e4m3
-scale bytes of every visible K and V row, divided by the step time).
+Prints one JSON line.  ``value`` is the decode's KV GB/s: packed e2m1 bytes plus e4m3
+scale bytes of every visible K and V row, divided by the step time.  ``roofline`` is
+the attention kernel's own figure: its algorithmic bytes (KV + Q + O + LSE) over its
+average duration, timed with HIP events around each launch inside the timed steps
+(events created without the system-scope fence, which would add to every launch).
+
+Other modes (profiling support, see the design doc for the commands):
+  --pmc-run                a short program for rocprofv3 counter passes: a 1 GiB copy
+                           (counter calibration) and a few steps of the workload;
+  --summarize-trace DIR    summarise a rocprofv3 --kernel-trace --stats output dir;
+  --summarize-pmc DIR ...  summarise FETCH_SIZE / WRITE_SIZE counter dirs into the
+                           traffic record read back by the benchmark.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
-import math
 import os
 import sys
 import time
 
 import numpy as np
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
+PROFILES = os.path.join(ROOT, "profiles")
+# sources whose change invalidates recorded counters of the decode kernel
+DECODE_SOURCES = ("decode.hip", "kv_ring.h", "attn_step.h", "fp4_common.h", "internal.h")
+CALIB_BYTES = 1 << 30
 
 
 def parse():
@@ -38,20 +55,75 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true", help="skip the other workloads' lines")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--pmc-run", action="store_true")
+    p.add_argument("--summarize-trace", metavar="DIR")
+    p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    p.add_argument("--command", default="", help="command line recorded in a summary")
+    p.add_argument("--out", default="", help="summary file to write")
     return p.parse_args()
 
 
-def time_events(torch, fn, iters):
-    """Average duration (ms) of fn() over iters launches, HIP events on the current stream."""
-    s = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(iters)]
-    for a, b in ev:
-        a.record(s)
-        fn()
-        b.record(s)
-    torch.cuda.synchronize()
-    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+def sources_digest():
+    h = hashlib.sha256()
+    for name in DECODE_SOURCES:
+        with open(os.path.join(ROOT, "attention_bit_paged_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record_path(workload):
+    return os.path.join(PROFILES, f"decode_ring_kernel.{workload}.traffic.txt")
+
+
+def recorded_traffic(workload):
+    """HBM bytes per launch of the decode kernel from the committed counter record, or
+    None when there is none or the kernel sources changed since it was taken."""
+    path = traffic_record_path(workload)
+    if not os.path.exists(path):
+        return None
+    rec = None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("{"):
+                rec = json.loads(line)
+    if not rec or rec.get("source_digest") != sources_digest():
+        return None
+    return rec["bytes_per_launch"]
+
+
+class HipEvents:
+    """Timing events created directly through HIP, without the system-scope fence a
+    default event performs when it is recorded (that fence adds several microseconds
+    to every bracketed launch)."""
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.pool = []
+
+    def new(self):
+        e = self.ct.c_void_p()
+        if self.hip.hipEventCreateWithFlags(self.ct.byref(e),
+                                            self.ct.c_uint(self.DISABLE_SYSTEM_FENCE)) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        self.pool.append(e)
+        return e
+
+    def record(self, e, stream):
+        if self.hip.hipEventRecord(e, self.ct.c_void_p(stream.cuda_stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def ms(self, a, b):
+        out = self.ct.c_float()
+        if self.hip.hipEventElapsedTime(self.ct.byref(out), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return out.value
+
+    def __del__(self):
+        for e in self.pool:
+            self.hip.hipEventDestroy(e)
 
 
 def decode_bytes(w):
@@ -60,7 +132,7 @@ def decode_bytes(w):
     return w.kv_bytes(), q + o
 
 
-def cpu_baseline(torch, case, budget_s):
+def cpu_baseline(case, budget_s):
     """The oracle on a bounded sample of the same decode workload (one BLAS thread)."""
     from threadpoolctl import threadpool_limits
     from oracle import nvfp4_ref as ref
@@ -88,121 +160,263 @@ def cpu_baseline(torch, case, budget_s):
                       f"tokens x {w.num_kv_heads} kv heads), numpy float64, {dt:.1f} s"}
 
 
+def timed_passes(torch, nv, run, merge, iters):
+    """Per-launch HIP-event durations (ms) of the attention pass and the merge."""
+    s = torch.cuda.current_stream()
+    he = HipEvents()
+    ev = [[he.new() for _ in range(3)] for _ in range(iters)]
+    for e in ev:
+        he.record(e[0], s)
+        run()
+        he.record(e[1], s)
+        merge()
+        he.record(e[2], s)
+    torch.cuda.synchronize()
+    return (float(np.mean([he.ms(a, b) for a, b, _ in ev])),
+            float(np.mean([he.ms(b, c) for _, b, c in ev])))
+
+
 def extra_decode(torch, nv, paged, synth, name, iters=20):
     w = synth.workload(name)
     case = paged.build_case(w, keep_sources=False)
     plan = paged.make_plan(case)
+    plan.set_deferred_merge(True)
     ws = plan.new_workspace()
     plan.upload(ws)
     o = torch.empty((w.batch, w.num_qo_heads, w.head_dim_vo), device="cuda")
     lse = torch.empty((w.batch, w.num_qo_heads), device="cuda")
-    fn = lambda: nv.batch_decode(plan, case.q, case.page_table, case.k_pool, case.v_pool,
-                                 w.sm_scale, ws, out=o, lse=lse)
+    run = nv.batch_decode(plan, case.q, case.page_table, case.k_pool, case.v_pool, w.sm_scale,
+                          ws, out=o, lse=lse, prepare=True)
+    merge = nv.merge_partials(plan, ws, o, lse, prepare=True)
     for _ in range(3):
-        fn()
-    ms = time_events(torch, fn, iters)
-    kv, _ = decode_bytes(w)
+        run()
+        merge()
+    run_ms, merge_ms = timed_passes(torch, nv, run, merge, iters)
+    del run, merge
+    kv, qo = decode_bytes(w)
     info = plan.info()
     del case, ws
     torch.cuda.empty_cache()
-    return {"workload": name, "kv_GBs": round(kv / ms / 1e6, 1),
-            "frac_hbm": round(kv / ms / 1e6 / HBM_PEAK_GBS, 4), "ms": round(ms, 4),
-            "kv_bytes": kv, "chunk": info["kv_chunk_tokens"], "work_items": info["num_work_items"]}
+    return {"workload": name, "kv_GBs": round(kv / (run_ms + merge_ms) / 1e6, 1),
+            "kernel_GBs": round((kv + qo) / run_ms / 1e6, 1),
+            "kernel_frac_hbm": round((kv + qo) / run_ms / 1e6 / HBM_PEAK_GBS, 4),
+            "attn_ms": round(run_ms, 4), "merge_ms": round(merge_ms, 4), "kv_bytes": kv,
+            "chunk": info["kv_chunk_tokens"], "work_items": info["num_work_items"]}
 
 
 def extra_prefill(torch, nv, paged, synth, name, iters=10):
     w = synth.workload(name)
     case = paged.build_case(w, keep_sources=False)
     plan = paged.make_plan(case)
+    plan.set_deferred_merge(True)
     ws = plan.new_workspace()
     plan.upload(ws)
     o = torch.empty((w.total_q, w.num_qo_heads, w.head_dim_vo), device="cuda")
     lse = torch.empty((w.total_q, w.num_qo_heads), device="cuda")
-    fn = lambda: nv.batch_prefill(plan, case.q, case.page_table, case.k_pool, case.v_pool,
-                                  w.sm_scale, ws, out=o, lse=lse)
+    run = nv.batch_prefill(plan, case.q, case.page_table, case.k_pool, case.v_pool, w.sm_scale,
+                           ws, out=o, lse=lse, prepare=True)
+    merge = nv.merge_partials(plan, ws, o, lse, prepare=True)
     for _ in range(3):
-        fn()
-    ms = time_events(torch, fn, iters)
+        run()
+        merge()
+    run_ms, merge_ms = timed_passes(torch, nv, run, merge, iters)
+    del run, merge
     fl = w.flops()
     info = plan.info()
     del case, ws
     torch.cuda.empty_cache()
-    return {"workload": name, "TFLOPs": round(fl / ms / 1e9, 2),
-            "frac_mfma_f16": round(fl / ms / 1e9 / MFMA_F16_PEAK_TFLOPS, 4), "ms": round(ms, 4),
-            "flops": fl, "work_items": info["num_work_items"], "chunk": info["kv_chunk_tokens"]}
+    return {"workload": name, "TFLOPs": round(fl / (run_ms + merge_ms) / 1e9, 2),
+            "kernel_TFLOPs": round(fl / run_ms / 1e9, 2),
+            "kernel_frac_mfma_f16": round(fl / run_ms / 1e9 / MFMA_F16_PEAK_TFLOPS, 4),
+            "attn_ms": round(run_ms, 4), "merge_ms": round(merge_ms, 4), "flops": fl,
+            "work_items": info["num_work_items"], "chunk": info["kv_chunk_tokens"]}
+
+
+class Decoder:
+    """The timed decode step of one workload over rotated pool sets."""
+
+    def __init__(self, torch, nv, paged, synth, name, pool_sets):
+        self.torch, self.nv = torch, nv
+        w = self.w = synth.workload(name)
+        if not w.decode:
+            raise SystemExit("the timed step is a decode workload; prefill runs as an extra line")
+        self.sets = [paged.build_case(w, keep_sources=(i == 0)) for i in range(pool_sets)]
+        t0 = time.perf_counter()
+        self.plan = paged.make_plan(self.sets[0])
+        self.plan_us = (time.perf_counter() - t0) * 1e6
+        self.plan.set_deferred_merge(True)
+        self.ws = self.plan.new_workspace()
+        self.plan.upload(self.ws)
+        # the step's new token of every request: its K/V rows and the slot of token L_b - 1
+        g = torch.Generator(device="cuda")
+        g.manual_seed(w.value_seed + 500)
+        self.new_k = torch.randn((w.batch, w.num_kv_heads, w.head_dim_qk), generator=g,
+                                 device="cuda").bfloat16()
+        self.new_v = torch.randn((w.batch, w.num_kv_heads, w.head_dim_vo), generator=g,
+                                 device="cuda").bfloat16()
+        last = np.cumsum(w.kv_lens) - 1
+        self.new_slots = self.sets[0].slots[torch.tensor(last, device="cuda")]
+        self.o = torch.empty((w.batch, w.num_qo_heads, w.head_dim_vo), device="cuda")
+        self.lse = torch.empty((w.batch, w.num_qo_heads), device="cuda")
+        # the three calls of a step, marshalled once per pool set
+        self.calls = [(nv.quantize_kv(self.new_k, self.new_v, self.new_slots, c.k_pool, c.v_pool,
+                                      prepare=True),
+                       nv.batch_decode(self.plan, c.q, c.page_table, c.k_pool, c.v_pool,
+                                       w.sm_scale, self.ws, out=self.o, lse=self.lse,
+                                       prepare=True),
+                       nv.merge_partials(self.plan, self.ws, self.o, self.lse, prepare=True))
+                      for c in self.sets]
+
+    def step(self, i, ev=None, he=None):
+        quant, attn, merge = self.calls[i % len(self.calls)]
+        if ev is None:
+            quant()
+            attn()
+            merge()
+            return
+        s = self.torch.cuda.current_stream()
+        he.record(ev[0], s)
+        quant()
+        he.record(ev[1], s)
+        attn()
+        he.record(ev[2], s)
+        merge()
+        he.record(ev[3], s)
+
+
+def pmc_run(args):
+    """Short program for counter passes: calibration copy, then a few decode steps."""
+    import torch
+    import attention_bit_paged_amd as nv
+    from attention_bit_paged_amd import paged, synth
+    x = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda")
+    x.fill_(1)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    del x, y
+    d = Decoder(torch, nv, paged, synth, args.workload, 1)
+    for i in range(5):
+        d.step(i)
+    torch.cuda.synchronize()
+    print(json.dumps({"pmc_run": args.workload, "info": d.plan.info()}), flush=True)
+
+
+def _kernel_rows(path_glob):
+    files = glob.glob(path_glob, recursive=True)
+    if not files:
+        raise SystemExit(f"no file matches {path_glob}")
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def _short(name):
+    name = name.replace("void ", "").replace("nvfp4::(anonymous namespace)::", "")
+    return name.split("(")[0][:70]
+
+
+def summarize_trace(args):
+    rows = _kernel_rows(os.path.join(args.summarize_trace, "**", "*kernel_stats.csv"))
+    lines = [f"# rocprofv3 kernel trace summary, workload {args.workload}",
+             f"# command: {args.command}", "",
+             f"{'kernel':72s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>6s}"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append(f"{_short(r['Name']):72s} {int(r['Calls']):6d} {float(r['AverageNs'])/1e3:10.2f} "
+                     f"{float(r['MinNs'])/1e3:10.2f} {float(r['MaxNs'])/1e3:10.2f} "
+                     f"{float(r['Percentage']):6.2f}")
+    text = "\n".join(lines) + "\n"
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(text)
+    print(text)
+
+
+def summarize_pmc(args):
+    """FETCH_SIZE / WRITE_SIZE per dispatch of the decode kernel and of the 1 GiB copy
+    (its calibration), into the traffic record the benchmark reads back."""
+    fetch_dir, write_dir = args.summarize_pmc
+
+    def per_kernel(d, counter):
+        out = {}
+        rows = _kernel_rows(os.path.join(d, "**", "*counter_collection.csv"))
+        for r in sorted(rows, key=lambda r: int(r["Dispatch_Id"])):
+            if r["Counter_Name"] != counter:
+                continue
+            out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return out
+
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    dec = [k for k in fetch if "decode_ring_kernel" in k]
+    cpy = [k for k in fetch if "copyBuffer" in k]
+    if not dec or not cpy:
+        raise SystemExit(f"kernels not found: {list(fetch)}")
+    # --pmc-run starts with three copies of CALIB_BYTES: the first three copy dispatches
+    dk, ck = dec[0], cpy[0]
+    kib = CALIB_BYTES / 1024
+    f_scale = kib / float(np.mean(fetch[ck][:3]))
+    w_scale = kib / float(np.mean(write[ck][:3]))
+    f_dec, w_dec = float(np.mean(fetch[dk])), float(np.mean(write[dk]))
+    nbytes = (f_dec * f_scale + w_dec * w_scale) * 1024
+    rec = {"kernel": _short(dk), "workload": args.workload,
+           "fetch_kib_per_dispatch": round(f_dec, 1), "write_kib_per_dispatch": round(w_dec, 1),
+           "copy_fetch_kib": round(float(np.mean(fetch[ck][:3])), 1),
+           "copy_write_kib": round(float(np.mean(write[ck][:3])), 1),
+           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+           "bytes_per_launch": round(nbytes), "source_digest": sources_digest()}
+    text = "\n".join([
+        f"# HBM traffic of the decode kernel, workload {args.workload}",
+        f"# commands: {args.command}",
+        f"# calibration: {_short(ck)} copies {CALIB_BYTES} bytes; FETCH_SIZE reads "
+        f"{rec['copy_fetch_kib']} KiB and WRITE_SIZE {rec['copy_write_kib']} KiB for it, so the "
+        f"scales are {rec['fetch_scale']} and {rec['write_scale']}",
+        f"# decode kernel {rec['kernel']}: FETCH_SIZE {rec['fetch_kib_per_dispatch']} KiB, "
+        f"WRITE_SIZE {rec['write_kib_per_dispatch']} KiB per dispatch "
+        f"({len(fetch[dk])} dispatches) -> {rec['bytes_per_launch']} bytes per launch",
+        json.dumps(rec)]) + "\n"
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(text)
+    print(text)
 
 
 def main():
     args = parse()
+    if args.summarize_trace:
+        return summarize_trace(args)
+    if args.summarize_pmc:
+        return summarize_pmc(args)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path shards by request or kv head with no exchange; see DESIGN.md)",
               file=sys.stderr)
         sys.exit(2)
+    if args.pmc_run:
+        return pmc_run(args)
     import torch
     import attention_bit_paged_amd as nv
     from attention_bit_paged_amd import paged, synth
 
-    w = synth.workload(args.workload)
-    if not w.decode:
-        raise SystemExit("the timed step is the decode workload; prefill runs as an extra line")
-    sets = [paged.build_case(w, keep_sources=(i == 0)) for i in range(args.pool_sets)]
-    case0 = sets[0]
-    t0 = time.perf_counter()
-    plan = paged.make_plan(case0)
-    plan_us = (time.perf_counter() - t0) * 1e6
-    ws = plan.new_workspace()
-    plan.upload(ws)
-    info = plan.info()
-
-    # the step's new token of every request: its K/V rows and the slot of token L_b - 1
-    g = torch.Generator(device="cuda")
-    g.manual_seed(w.value_seed + 500)
-    new_k = torch.randn((w.batch, w.num_kv_heads, w.head_dim_qk), generator=g, device="cuda").bfloat16()
-    new_v = torch.randn((w.batch, w.num_kv_heads, w.head_dim_vo), generator=g, device="cuda").bfloat16()
-    last = []
-    pos = 0
-    for L in w.kv_lens:
-        pos += L
-        last.append(pos - 1)
-    new_slots = case0.slots[torch.tensor(last, device="cuda")]
-    o = torch.empty((w.batch, w.num_qo_heads, w.head_dim_vo), device="cuda")
-    lse = torch.empty((w.batch, w.num_qo_heads), device="cuda")
-
-    def step(i):
-        c = sets[i % len(sets)]
-        nv.quantize_kv(new_k, new_v, new_slots, c.k_pool, c.v_pool)
-        nv.batch_decode(plan, c.q, c.page_table, c.k_pool, c.v_pool, w.sm_scale, ws, out=o, lse=lse)
-
+    d = Decoder(torch, nv, paged, synth, args.workload, args.pool_sets)
+    w, info = d.w, d.plan.info()
     for i in range(args.warmup):
-        step(i)
+        d.step(i)
     torch.cuda.synchronize()
+    he = HipEvents()
+    ev = [[he.new() for _ in range(4)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i)
+        d.step(i, ev[i], he)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     ms_step = dt * 1e3 / args.steps
-
-    # per-kernel HIP-event timing on the launch stream (same rotation as the steps)
-    ctr = [0]
-
-    def dec():
-        c = sets[ctr[0] % len(sets)]
-        ctr[0] += 1
-        nv.batch_decode(plan, c.q, c.page_table, c.k_pool, c.v_pool, w.sm_scale, ws, out=o, lse=lse)
-
-    def quant():
-        c = sets[ctr[0] % len(sets)]
-        ctr[0] += 1
-        nv.quantize_kv(new_k, new_v, new_slots, c.k_pool, c.v_pool)
-
-    dec_ms = time_events(torch, dec, max(args.steps, 20))
-    quant_ms = time_events(torch, quant, max(args.steps, 20))
+    quant_ms = float(np.mean([he.ms(e[0], e[1]) for e in ev]))
+    attn_ms = float(np.mean([he.ms(e[1], e[2]) for e in ev]))
+    merge_ms = float(np.mean([he.ms(e[2], e[3]) for e in ev]))
 
     kv, qo = decode_bytes(w)
     value = kv / (ms_step * 1e-3) / 1e9
-    achieved = (kv + qo) / (dec_ms * 1e-3) / 1e9
+    achieved = (kv + qo) / (attn_ms * 1e-3) / 1e9
     out = {
         "metric": "NVFP4 paged decode KV GB/s (% HBM peak); prefill TFLOP/s (% MFMA peak)",
         "value": round(value, 1),
@@ -214,30 +428,36 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "nvfp4 KV (e2m1 + e4m3), fp16 MFMA, fp32 accumulate",
-        "data": "synthetic (seeded N(0,1) bf16 Q/K/V, NVFP4-quantised in-kernel)",
-        "config": {"workload": w.name, "batch": w.batch, "kv_len": "U[512,8192] seeded",
+        "dtype": "f16",
+        "data": "synthetic (seeded N(0,1) bf16 Q/K/V, K/V NVFP4-quantised on the GPU)",
+        "config": {"workload": w.name, "batch": w.batch,
+                   "kv_len": (str(w.kv_lens[0]) if min(w.kv_lens) == max(w.kv_lens)
+                              else f"{min(w.kv_lens)}..{max(w.kv_lens)} (seeded uniform)"),
                    "num_qo_heads": w.num_qo_heads, "num_kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim_qk, "page_size": w.page_size, "pool_pages": w.pool_pages,
                    "kv_chunk_tokens": info["kv_chunk_tokens"], "work_items": info["num_work_items"],
-                   "total_kv_tokens": w.total_kv, "pool_sets_rotated": len(sets)},
+                   "total_kv_tokens": w.total_kv, "pool_sets_rotated": len(d.sets)},
         "frac_hbm": round(value / HBM_PEAK_GBS, 4),
-        "roofline": {"bound": "hbm", "kernel": "decode (decode_kernel + merge_partials_kernel)",
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "bytes_per_launch": kv + qo, "avg_launch_ms": round(dec_ms, 5)},
-        "quantize_append_ms": round(quant_ms, 5),
-        "plan_host_us": round(plan_us, 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic(w.name),
+                     "kernel": f"decode_ring_kernel<{w.head_dim_qk}, {w.head_dim_vo}>",
+                     "bytes_per_launch": kv + qo, "avg_launch_ms": round(attn_ms, 5)},
+        "step_breakdown_ms": {"quantize_append": round(quant_ms, 5), "attention": round(attn_ms, 5),
+                              "merge": round(merge_ms, 5)},
+        "plan_host_us": round(d.plan_us, 1),
     }
     if not args.no_extra:
-        extras = []
-        for name in ("long_decode", "asym_decode"):
-            extras.append(extra_decode(torch, nv, paged, synth, name))
-        for name in ("prefill_extend", "asym_prefill"):
-            extras.append(extra_prefill(torch, nv, paged, synth, name))
+        del d
+        torch.cuda.empty_cache()
+        extras = [extra_decode(torch, nv, paged, synth, n) for n in ("long_decode", "asym_decode")]
+        extras += [extra_prefill(torch, nv, paged, synth, n) for n in ("prefill_extend", "asym_prefill")]
         out["other_workloads"] = extras
+        case0 = paged.build_case(w, keep_sources=True)
+    else:
+        case0 = d.sets[0]
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(torch, case0, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(case0, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

@@ -69,7 +69,8 @@ const char* nvfp4_version(void);
  * scale tensors follow the data layout; container strides count bytes).
  * Alignment: data and every data stride must be multiples of 16 bytes when
  * head_dim >= 128, of head_dim/8 bytes otherwise; sf and every sf stride multiples
- * of min(head_dim/16, 8) bytes.
+ * of min(head_dim/16, 8) bytes.  Strides are non-negative and below 2^31 bytes;
+ * token strides (data and sf) below 2^27 bytes.
  */
 typedef struct {
   void* data;              /* device, packed e2m1 pairs (uint8) */
@@ -122,7 +123,9 @@ nvfp4_status nvfp4_quantize_kv(const void* k_src, int64_t k_stride_token, int64_
  *   kv_chunk_tokens: 0 = choose the split to fill the device; < 0 = never split;
  *              otherwise a multiple of 16: split every request's KV range into
  *              chunks of that many tokens.  Every chunk boundary except the end of
- *              a request is a multiple of 16 tokens.
+ *              a request is a multiple of 16 tokens.  A decode work item covers
+ *              four consecutive chunks (one per wave, combined on chip), a prefill
+ *              work item one chunk; split items are merged by LSE.
  *   num_cus:   compute units to fill; 0 = query the current device (256 if none).
  * The plan owns host memory only.  It is immutable after creation, except for the
  * record of the workspace it was last uploaded to.
@@ -182,8 +185,11 @@ nvfp4_status nvfp4_plan_upload(nvfp4_plan* plan, void* workspace, size_t workspa
  *   lse: device fp32 [batch, num_qo_heads] contiguous, natural log, always written
  *      ([PF] commit zeroing lse; [FIX] second commit: ln-sum-exp of the scaled
  *      scores).  A request with kv_len 0 gets O = 0 and LSE = -inf.
+ *   sm_scale: finite and > 0; scores are sm_scale * q.k (times the K pool's
+ *      global scale).
  * Split work items write partial states into the workspace; a merge kernel on the
- * same stream then combines them by LSE ([XQA] changelog: mergeAndSaveOutTile).
+ * same stream then combines them by LSE ([XQA] changelog: mergeAndSaveOutTile),
+ * unless the plan defers it (nvfp4_plan_set_deferred_merge).
  */
 nvfp4_status nvfp4_batch_decode(const nvfp4_plan* plan, const void* q, int64_t q_stride_req,
                                 int64_t q_stride_head, const int32_t* page_table, int64_t pt_stride,
@@ -206,6 +212,22 @@ nvfp4_status nvfp4_batch_prefill(const nvfp4_plan* plan, const void* q, int64_t 
                                  const nvfp4_kv_pool* v_pool, float sm_scale, void* workspace,
                                  size_t workspace_bytes, float* o, int64_t o_stride_tok,
                                  int64_t o_stride_head, float* lse, void* stream);
+
+/*
+ * Deferred merge ([XQA] changelog: the split-KV partial tiles are merged after the
+ * attention pass).  With deferred != 0, nvfp4_batch_decode / nvfp4_batch_prefill
+ * runs of this plan write the rows that were not split and leave the split rows'
+ * partial states in the workspace; nvfp4_merge_partials then writes those rows'
+ * O and LSE (same o, strides and lse as the run), on its stream, after the run.
+ * Until it has run, the split rows of o and lse hold nothing meaningful.  Lets a
+ * caller place the merge elsewhere on its streams or time the two passes apart.
+ * Default: 0 (runs merge by themselves).
+ */
+nvfp4_status nvfp4_plan_set_deferred_merge(nvfp4_plan* plan, int32_t deferred);
+
+nvfp4_status nvfp4_merge_partials(const nvfp4_plan* plan, void* workspace, size_t workspace_bytes,
+                                  float* o, int64_t o_stride_row, int64_t o_stride_head, float* lse,
+                                  void* stream);
 
 /*
  * Merge partial attention states by their LSE ([XQA] changelog: merge of the

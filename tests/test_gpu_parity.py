@@ -225,3 +225,65 @@ def test_merge_states_matches_oracle():
     o_ref, lse_ref = ref.merge_states(np.moveaxis(o_parts, 1, 0), np.moveaxis(lse_parts, 1, 0))
     gh.assert_attention_close(o.cpu().double().numpy(), lse.cpu().double().numpy(), o_ref, lse_ref)
     assert np.abs(o.cpu().numpy() - o_ref).max() < 1e-5
+
+
+@pytest.mark.parametrize("decode", [True, False])
+def test_deferred_merge_matches_default(decode):
+    """A deferred-merge run followed by nvfp4_merge_partials writes exactly what a
+    default run writes (same kernels, same order of operations)."""
+    if decode:
+        w = synth.custom("defer_d", kv_lens=[700, 33, 1500, 0, 260], num_qo_heads=8,
+                         num_kv_heads=2, seed=31)
+        chunk = 64
+    else:
+        w = synth.custom("defer_p", kv_lens=[300, 90], qo_lens=[40, 90], num_qo_heads=8,
+                         num_kv_heads=2, causal=True, seed=32)
+        chunk = 64
+    c = gh.build_oracle_case(w)
+    plan = gh.make_plan(w, chunk)
+    assert plan.info()["num_merges"] > 0
+    o_ref, lse_ref = gh.run_gpu(c, plan)
+    plan2 = gh.make_plan(w, chunk)
+    plan2.set_deferred_merge(True)
+    ws = plan2.new_workspace(c.q.device)
+    plan2.upload(ws)
+    rows = c.q.shape[0]
+    o = torch.full((rows, w.num_qo_heads, w.head_dim_vo), float("nan"), device=c.q.device)
+    lse = torch.full((rows, w.num_qo_heads), float("nan"), device=c.q.device)
+    fn = nv.batch_decode if decode else nv.batch_prefill
+    fn(plan2, c.q, c.page_table, c.k_pool, c.v_pool, w.sm_scale, ws, out=o, lse=lse)
+    nv.merge_partials(plan2, ws, o, lse)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(o.cpu().double().numpy(), o_ref)
+    np.testing.assert_array_equal(lse.cpu().double().numpy(), lse_ref)
+
+
+def test_prepared_calls_match_direct_calls():
+    """Prepared (pre-marshalled) quantise and decode calls launch the same work."""
+    w = synth.custom("prepared", kv_lens=[300, 1200, 45], num_qo_heads=8, num_kv_heads=2, seed=33)
+    c = gh.build_oracle_case(w)
+    plan = gh.make_plan(w, 64)
+    o_ref, lse_ref = gh.run_gpu(c, plan)
+    ws = plan.new_workspace(c.q.device)
+    plan.upload(ws)
+    o = torch.full((w.batch, w.num_qo_heads, w.head_dim_vo), float("nan"), device=c.q.device)
+    lse = torch.full((w.batch, w.num_qo_heads), float("nan"), device=c.q.device)
+    call = nv.batch_decode(plan, c.q, c.page_table, c.k_pool, c.v_pool, w.sm_scale, ws, out=o,
+                           lse=lse, prepare=True)
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(o.cpu().double().numpy(), o_ref)
+    np.testing.assert_array_equal(lse.cpu().double().numpy(), lse_ref)
+    # a prepared quantise call writes the same bytes as a direct one
+    src = torch.randn((4, w.num_kv_heads, w.head_dim_qk), device="cuda").bfloat16()
+    slots = torch.tensor([0, 17, 33, 2], dtype=torch.int64, device="cuda")
+    a = nv.KVPool.empty(4, w.num_kv_heads, 16, w.head_dim_qk)
+    b = nv.KVPool.empty(4, w.num_kv_heads, 16, w.head_dim_qk)
+    for p in (a, b):
+        p.data.zero_()
+        p.sf.zero_()
+    nv.quantize_kv(src, None, slots, a, None)
+    nv.quantize_kv(src, None, slots, b, None, prepare=True)()
+    torch.cuda.synchronize()
+    assert torch.equal(a.data, b.data) and torch.equal(a.sf, b.sf)

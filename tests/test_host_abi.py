@@ -134,3 +134,22 @@ def test_quantize_rejections():
     assert _lib.STATUS[st] == "NVFP4_E_SHAPE"
     st = q(0x10000, 1024, 128, None, 0, 0, 0, 0, ctypes.byref(k), None, None)
     assert _lib.STATUS[st] == "NVFP4_OK"   # zero tokens: nothing to do
+
+
+def test_deferred_merge_entry_points():
+    f = nv.lib.nvfp4_merge_partials
+    assert _lib.STATUS[nv.lib.nvfp4_plan_set_deferred_merge(None, 1)] == "NVFP4_E_INVALID"
+    assert _lib.STATUS[f(None, 0x4000, 1 << 20, 0x8000, 512, 128, 0x9000, None)] == "NVFP4_E_INVALID"
+    split = nv.Plan([3000], num_qo_heads=4, num_kv_heads=1, head_dim_qk=128, kv_chunk_tokens=64,
+                    num_cus=256)
+    split.set_deferred_merge(True)
+    assert split.info()["num_merges"] == 1
+    # the plan was never uploaded to this workspace: rejected before any launch
+    st = f(split.handle, 0x40000, split.workspace_bytes, 0x80000, 512, 128, 0x90000, None)
+    assert _lib.STATUS[st] == "NVFP4_E_WORKSPACE" and "uploaded" in nv.lib.nvfp4_last_error().decode()
+    st = f(split.handle, 0x40000, 16, 0x80000, 512, 128, 0x90000, None)
+    assert _lib.STATUS[st] == "NVFP4_E_WORKSPACE"
+    # nothing split: nothing to do
+    whole = nv.Plan([3000], num_qo_heads=4, num_kv_heads=1, head_dim_qk=128, kv_chunk_tokens=-1,
+                    num_cus=256)
+    assert _lib.STATUS[f(whole.handle, 0, 0, 0, 0, 0, 0, None)] == "NVFP4_OK"
