@@ -33,9 +33,10 @@ def flags():
             "-Wall", "-Wno-unused-function"]
 
 
-# Per-file extras.  decode: MFMA accumulators in ordinary VGPRs, so the softmax can
-# rescale them in place instead of copying them out of AGPRs every step.
-EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-file extras.  MFMA accumulators in ordinary VGPRs, so the softmax can rescale
+# them in place instead of copying them out of AGPRs every step.
+EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+         "prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str) -> str:

@@ -203,7 +203,8 @@ nvfp4_status nvfp4_plan_create(const int32_t* kv_lens, const int32_t* qo_indptr,
   if (!prefill && group > 4 * kDecodeHeads)
     return fail(NVFP4_E_UNSUPPORTED, "decode supports at most %d qo heads per kv head, got %d",
                 4 * kDecodeHeads, group);
-  int rows_item = prefill ? prefill_rows_per_item(head_dim_qk, head_dim_vo, group) : kDecodeHeads;
+  int rows_item =
+      prefill ? prefill_rows_per_item(head_dim_qk, head_dim_vo, group, page_size) : kDecodeHeads;
   if (prefill && group > rows_item)
     return fail(NVFP4_E_UNSUPPORTED, "prefill supports at most %d qo heads per kv head, got %d",
                 rows_item, group);

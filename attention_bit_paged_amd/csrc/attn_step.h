@@ -285,12 +285,32 @@ __device__ __forceinline__ void scale16_if(f32x4& a, f32x4& b, f32x4& c, f32x4& 
       : "scc");
 }
 
+// The same for accumulators held in AGPRs (MFMA results left in the accumulation
+// registers): each value is read out, scaled and written back, all inside the
+// skipped block.
+__device__ __forceinline__ void scale4_if_agpr(f32x4& a, float alpha, uint64_t raised) {
+  float t;
+  asm volatile(
+      "s_cmp_eq_u64 %5, 0\n\ts_cbranch_scc1 1f\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\t"
+      "v_accvgpr_read_b32 %4, %0\n\ts_nop 1\n\tv_mul_f32 %4, %4, %6\n\tv_accvgpr_write_b32 %0, %4\n\t"
+      "v_accvgpr_read_b32 %4, %1\n\ts_nop 1\n\tv_mul_f32 %4, %4, %6\n\tv_accvgpr_write_b32 %1, %4\n\t"
+      "v_accvgpr_read_b32 %4, %2\n\ts_nop 1\n\tv_mul_f32 %4, %4, %6\n\tv_accvgpr_write_b32 %2, %4\n\t"
+      "v_accvgpr_read_b32 %4, %3\n\ts_nop 1\n\tv_mul_f32 %4, %4, %6\n\tv_accvgpr_write_b32 %3, %4\n\t"
+      "s_nop 4\n1:"
+      : "+a"(a[0]), "+a"(a[1]), "+a"(a[2]), "+a"(a[3]), "=&v"(t)
+      : "s"(raised), "v"(alpha)
+      : "scc");
+}
+
+// Where the accumulators of a RowState live and how the rare rescale reaches them.
+enum class AccForm { VGPR, AGPR, PLAIN };
+
 // Online-softmax state of one 16-row group (base-2 scores).  `m` is a reference point,
 // not necessarily the running maximum: it is raised only when a row's maximum exceeds
 // it by kRescaleSlack, so p = exp2(x - m) <= 2^8.  O = acc / l and LSE = m + log2(l)
-// hold for any reference point.  VGPR_ACC: the accumulators live in ordinary VGPRs
-// and are rescaled in place (scale16_if); otherwise by plain code.
-template <int NT, bool VGPR_ACC>
+// hold for any reference point.  FORM: accumulators in VGPRs or AGPRs, rescaled in
+// place by one asm statement (scale16_if / scale4_if_agpr), or left to plain code.
+template <int NT, AccForm FORM>
 struct RowState {
   f32x4 acc[NT];
   float m, l;
@@ -325,7 +345,7 @@ struct RowState {
     const float bm = max_over_groups(fmaxf(b3, b2)) * c;
     const bool raise = bm > m + kRescaleSlack;
     const float m_new = raise ? bm : m;
-    if constexpr (VGPR_ACC) {
+    if constexpr (FORM != AccForm::PLAIN) {
       const uint64_t raised = __ballot(raise);
       // alpha = exp2(m - m_new) on raising lanes (0 when m was -inf), 1 elsewhere; only
       // computed when some lane raises
@@ -337,9 +357,14 @@ struct RowState {
           : "=&v"(alpha), "+v"(l)
           : "s"(raised), "v"(m), "v"(m_new)
           : "scc");
+      if constexpr (FORM == AccForm::VGPR) {
 #pragma unroll
-      for (int e = 0; e < NT; e += 4)
-        scale16_if(acc[e], acc[e + 1], acc[e + 2], acc[e + 3], alpha, raised);
+        for (int e = 0; e < NT; e += 4)
+          scale16_if(acc[e], acc[e + 1], acc[e + 2], acc[e + 3], alpha, raised);
+      } else {
+#pragma unroll
+        for (int e = 0; e < NT; ++e) scale4_if_agpr(acc[e], alpha, raised);
+      }
     } else {
       if (__any(raise)) {
         const float alpha = fast_exp2(m - m_new);  // 0 when m was -inf

@@ -38,7 +38,7 @@ struct DecodeOcc {
 // Epilogue shared by both decode kernels: combine the four waves' states in wave 0,
 // then store the row group directly, or as a partial for the merge kernel.
 template <int DV>
-__device__ __forceinline__ void decode_epilogue(const AttnArgs& a, RowState<DV / 16, true>& st,
+__device__ __forceinline__ void decode_epilogue(const AttnArgs& a, RowState<DV / 16, AccForm::VGPR>& st,
                                                 float* xch_mem, bool bad_w, int wave, int lane,
                                                 int b, int head, int n, int j, bool head_valid,
                                                 int slot) {
@@ -88,7 +88,7 @@ __device__ __forceinline__ void decode_epilogue(const AttnArgs& a, RowState<DV /
 template <int DK, int DV, bool MASK>
 __device__ __forceinline__ void decode_step(const StepRaw<DK, DV>& r, int t0, int tlast, int j,
                                             const f16x8 (&qf)[DK / 32], float score_c,
-                                            RowState<DV / 16, true>& st) {
+                                            RowState<DV / 16, AccForm::VGPR>& st) {
   using S = StepShape<DK, DV>;
   f16x8 ka[S::NS], kb[S::NS];
   k_operands<DK, DV>(r, ka, kb);
@@ -154,7 +154,7 @@ void decode_ring_kernel(AttnArgs a) {
   const int tlast = it.w1 - 1;
   uint32_t bad = 0;
 
-  RowState<S::NT, true> st;
+  RowState<S::NT, AccForm::VGPR> st;
   st.init();
   RingLanes lanes = ring_lanes<DK, DV, WL>(ring_lds, j, n);
   const int len = it.w1 - it.w0;
@@ -214,7 +214,7 @@ __global__ __launch_bounds__(256) void decode_regs_kernel(AttnArgs a) {
   PagedView<DK, DV, false> view;
   view.init(a, it.b, it.kvh, lane);
   const int tlast = it.w1 - 1;
-  RowState<S::NT, true> st;
+  RowState<S::NT, AccForm::VGPR> st;
   st.init();
   const int len = it.w1 - it.w0;
   const int nsteps = (len + kDecodeStep - 1) / kDecodeStep;

@@ -87,7 +87,7 @@ int decode_wgs_per_cu(int dk, int dv);
 hipError_t launch_prefill(int dk, int dv, int page_shift, const AttnArgs& a, int rows_per_item,
                           hipStream_t stream);
 bool prefill_supported(int dk, int dv);
-int prefill_rows_per_item(int dk, int dv, int group);
+int prefill_rows_per_item(int dk, int dv, int group, int page_size);
 size_t prefill_lds_bytes(int dk, int dv);
 hipError_t launch_merge_partials(const AttnArgs& a, int n_merges, int dv, int prefill,
                                  hipStream_t stream);

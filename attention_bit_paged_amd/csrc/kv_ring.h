@@ -56,10 +56,12 @@ struct RingShape {
       if (group(c, l) == g) m |= uint64_t(1) << l;
     return m;
   }
-  static constexpr int ndma() {
+  // copy instructions per stage for the pools in the bit set `pools` (bit 0 K rows,
+  // 1 V rows, 2 K scales, 3 V scales)
+  static constexpr int ndma(int pools = 0xF) {
     int n = 0;
     for (int c = 0; c < NCOPY; ++c)
-      for (int g = 0; g < 8; ++g) n += mask(c, g) != 0;
+      for (int g = 0; g < 8; ++g) n += ((pools >> (g / 2)) & 1) && mask(c, g) != 0;
     return n;
   }
   static constexpr int lds_off(int c) {
@@ -67,7 +69,7 @@ struct RingShape {
                     : (c < N_KD + N_VD ? OFF_VD + (c - N_KD) * 1024
                                        : OFF_SF + (c - N_KD - N_VD) * 256);
   }
-  static constexpr int NDMA = ndma();  // copy instructions per stage
+  static constexpr int NDMA = ndma(0xF);  // copy instructions per stage
   static constexpr int NST_RAW = WAVE_LDS / STAGE;
   static constexpr int NST = NST_RAW > 4 ? 4 : NST_RAW;
   static_assert(NST >= 2, "LDS budget below two stages");
@@ -164,11 +166,11 @@ struct RingPlan {
 
 namespace ring_detail {
 
-template <int DK, int DV, int WL, int C, int G>
+template <int DK, int DV, int WL, int POOLS, int C, int G>
 __device__ __forceinline__ void issue_group(uint32_t m0, uint32_t voff,
                                             const uint8_t* const (&base)[8]) {
   using R = RingShape<DK, DV, WL>;
-  constexpr uint64_t M = R::mask(C, G);
+  constexpr uint64_t M = ((POOLS >> (G / 2)) & 1) ? R::mask(C, G) : 0;
   constexpr bool X4 = C < R::N_KD + R::N_VD;
   if constexpr (M == ~uint64_t(0)) {
     dma<X4>(m0, voff, base[G]);
@@ -177,34 +179,35 @@ __device__ __forceinline__ void issue_group(uint32_t m0, uint32_t voff,
   }
 }
 
-template <int DK, int DV, int WL, int C>
+template <int DK, int DV, int WL, int POOLS, int C>
 __device__ __forceinline__ void issue_copy(uint32_t stage_lds, const RingPlan<DK, DV, WL>& rp,
                                            const uint8_t* const (&base)[8]) {
   using R = RingShape<DK, DV, WL>;
   const uint32_t m0 = stage_lds + R::lds_off(C);
-  issue_group<DK, DV, WL, C, 0>(m0, rp.off[C], base);
-  issue_group<DK, DV, WL, C, 1>(m0, rp.off[C], base);
-  issue_group<DK, DV, WL, C, 2>(m0, rp.off[C], base);
-  issue_group<DK, DV, WL, C, 3>(m0, rp.off[C], base);
-  issue_group<DK, DV, WL, C, 4>(m0, rp.off[C], base);
-  issue_group<DK, DV, WL, C, 5>(m0, rp.off[C], base);
-  issue_group<DK, DV, WL, C, 6>(m0, rp.off[C], base);
-  issue_group<DK, DV, WL, C, 7>(m0, rp.off[C], base);
+  issue_group<DK, DV, WL, POOLS, C, 0>(m0, rp.off[C], base);
+  issue_group<DK, DV, WL, POOLS, C, 1>(m0, rp.off[C], base);
+  issue_group<DK, DV, WL, POOLS, C, 2>(m0, rp.off[C], base);
+  issue_group<DK, DV, WL, POOLS, C, 3>(m0, rp.off[C], base);
+  issue_group<DK, DV, WL, POOLS, C, 4>(m0, rp.off[C], base);
+  issue_group<DK, DV, WL, POOLS, C, 5>(m0, rp.off[C], base);
+  issue_group<DK, DV, WL, POOLS, C, 6>(m0, rp.off[C], base);
+  issue_group<DK, DV, WL, POOLS, C, 7>(m0, rp.off[C], base);
 }
 
-template <int DK, int DV, int WL, int... Cs>
+template <int DK, int DV, int WL, int POOLS, int... Cs>
 __device__ __forceinline__ void issue_all(std::integer_sequence<int, Cs...>, uint32_t stage_lds,
                                           const RingPlan<DK, DV, WL>& rp,
                                           const uint8_t* const (&base)[8]) {
-  (issue_copy<DK, DV, WL, Cs>(stage_lds, rp, base), ...);
+  (issue_copy<DK, DV, WL, POOLS, Cs>(stage_lds, rp, base), ...);
 }
 
 }  // namespace ring_detail
 
-// Issues the copies of the step starting at token t0 into the stage at lds_stage.
-// Bases of the two 16-token halves come from two page-table entries; a half that
-// starts after tlast reuses the first half's page (its bytes are never used).
-template <int DK, int DV, int WL>
+// Issues the copies of the step starting at token t0 into the stage at lds_stage, for
+// the pools in the bit set POOLS (see RingShape::ndma).  Bases of the two 16-token
+// halves come from two page-table entries; a half that starts after tlast reuses the
+// first half's page (its bytes are never used).
+template <int DK, int DV, int WL, int POOLS = 0xF>
 __device__ __forceinline__ void ring_issue(const RingPlan<DK, DV, WL>& rp, uint32_t lds_stage,
                                            const PagedView<DK, DV, true>& pv, int t0, int tlast,
                                            uint32_t& bad) {
@@ -237,8 +240,8 @@ __device__ __forceinline__ void ring_issue(const RingPlan<DK, DV, WL>& rp, uint3
       at(pv.vsf, pg0, s0, pv.vsf_page, pv.vsf_tok),  at(pv.vsf, pg1, s1, pv.vsf_page, pv.vsf_tok)};
   // the previous reads of this stage were consumed already; make sure they completed
   asm volatile("s_waitcnt lgkmcnt(0)");
-  ring_detail::issue_all<DK, DV, WL>(std::make_integer_sequence<int, R::NCOPY>{}, lds_stage, rp,
-                                      base);
+  ring_detail::issue_all<DK, DV, WL, POOLS>(std::make_integer_sequence<int, R::NCOPY>{},
+                                             lds_stage, rp, base);
 }
 
 // LDS addresses of this lane's reads in stage 0 of the ring at ring_lds.

@@ -10,11 +10,24 @@
 //
 // A work item is one workgroup of four waves: (request b, kv head g, query tile,
 // chunk [kv0, kv1)).  The tile's rows are (query, qo head of the group) pairs, query
-// major, so the heads that share a kv head share every K/V byte read.  Each wave owns
-// NR groups of 16 rows and streams the chunk in 32-token steps with the next step's
-// bytes in flight; the dequantised K and V^T operands of a step serve all the wave's
-// row groups.  A split tile's partial states are merged by a separate kernel.
-#include "attn_step.h"
+// major, so the heads that share a kv head share every K/V byte read.
+//
+// Cooperative kernel (page_size >= 16, head dims up to 256): the workgroup streams
+// the chunk in 32-token steps.  The raw packed bytes of a step arrive in a shared LDS
+// ring by direct global-to-LDS copies (each wave issues one pool's copies, three
+// steps deep); the four waves then dequantise the step together into fp16 MFMA
+// operands, stored lane-major in an LDS operand buffer (double-buffered, one barrier
+// per step), and every wave computes its four groups of 16 rows from those operands,
+// held in registers for the step.  The K/V dequantisation and the LDS reads are thus
+// shared by the 256 rows of the tile.
+//
+// Register kernel (any page size, any head dims): each wave owns its rows and loads
+// and dequantises every step itself, the next step's bytes held in registers.
+//
+// A split tile's partial states are merged by a separate kernel.
+#include <type_traits>
+
+#include "kv_ring.h"
 
 namespace nvfp4 {
 
@@ -26,7 +39,7 @@ constexpr int prefill_nr() {
 }
 
 template <int DK, int DV, bool PAGE16>
-__global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256) void prefill_regs_kernel(AttnArgs a) {
   using S = StepShape<DK, DV>;
   constexpr int NR = prefill_nr<DK>();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -79,7 +92,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a) {
   view.init(a, b, kvh, lane);
   const int tlast = kv1 - 1;
 
-  RowState<S::NT, false> st[NR];
+  RowState<S::NT, AccForm::PLAIN> st[NR];
 #pragma unroll
   for (int rg = 0; rg < NR; ++rg) st[rg].init();
 
@@ -139,13 +152,289 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ cooperative --
+
+template <int DK, int DV>
+struct CoopShape {
+  using S = StepShape<DK, DV>;
+  static constexpr bool OK = DK <= 256 && DV <= 256;
+  // head dims up to 128: eight waves of two row groups (two waves per SIMD hide each
+  // other's latencies); larger: four waves of two row groups (one per SIMD)
+  static constexpr int NW = DK <= 128 && DV <= 128 ? 8 : 4;
+  static constexpr int NR = 2;                    // row groups of 16 per wave
+  static constexpr int ROWS = NW * NR * 16;       // rows per work item
+  static constexpr int NOP = 2 * S::NS + S::NT;   // operand vectors per step
+  static constexpr int OPB = NOP * 64 * 16;       // bytes of one operand buffer
+  static constexpr int RAW_STAGE = 16 * DK + 16 * DV + (2 * DK + 2 * DV + 255) / 256 * 256;
+  using R = RingShape<DK, DV, 3 * RAW_STAGE>;     // three raw stages
+  static constexpr int LDS = 3 * RAW_STAGE + 2 * OPB;
+  static constexpr int KE = (2 * S::NS + NW - 1) / NW;  // K operand entries per lane
+  static constexpr int VH = NW / 4;               // V tiles split in this many parts
+  static constexpr int VPART = S::NT / VH;        // V tiles per part
+  static_assert(R::NST == 3, "raw ring depth");
+  static_assert(S::NT % VH == 0, "V split");
+};
+
+// Dequantises one raw stage into an operand buffer.  Operand o < 2*NS is K tile o/NS
+// (token tile A or B), k-step o%NS; operand 2*NS + e is V^T tile e.  Entry (o, lane) is
+// the 16 bytes lane `lane` loads for operand o.  K entries: wave w makes entries
+// (w + NW*r, lane).  V: lane L of the workgroup makes, for the operand lane
+// c = L / (4*VH), the token pair p = L%4 of the V tiles of part (L/4)%VH.
+template <int DK, int DV>
+__device__ __forceinline__ void coop_dequant(uint32_t raw, uint32_t opb, int wave, int lane,
+                                             int t0, int tlast) {
+  using S = StepShape<DK, DV>;
+  using C = CoopShape<DK, DV>;
+  using R = typename C::R;
+  typedef __attribute__((address_space(3))) uint8_t* lds_p;
+  const int j = lane >> 4, n = lane & 15;
+  // K entries
+#pragma unroll
+  for (int r = 0; r < C::KE; ++r) {
+    const int o = wave + C::NW * r;  // wave-uniform
+    if (o < 2 * S::NS) {
+      const int tile = o / S::NS, s = o % S::NS;
+      const int tok = 8 * (n >> 2) + (n & 3) + 4 * tile;
+      uint32_t w, sc;
+      lds_load<4>(raw + R::OFF_KD + tok * (DK / 2) + j * S::KB + 4 * s, &w);
+      lds_load<1>(raw + R::OFF_SF + tok * (DK / 16) + j * S::KSF + (s >> 1), &sc);
+      if (t0 + tok > tlast) sc = 0;  // keys past the chunk: finite zeros
+      const f16x8 v = dequant8(w, splat_lo(fp8x2_to_f16<false>(sc)));
+      *(__attribute__((address_space(3))) f16x8*)(lds_p)(size_t)(opb + (o * 64 + lane) * 16) = v;
+    }
+  }
+  // V entries
+  const int L = wave * 64 + lane;
+  const int c = L / (4 * C::VH), p = L & 3, part = (L >> 2) % C::VH;
+  const int jj = c >> 4, m = c & 15;
+  const int ta = 8 * jj + 2 * p;
+  uint32_t sa, sb;
+  const int blk = (m * (DV / 16)) / 16;
+  lds_load<1>(raw + R::OFF_SF + R::KS + ta * (DV / 16) + blk, &sa);
+  lds_load<1>(raw + R::OFF_SF + R::KS + (ta + 1) * (DV / 16) + blk, &sb);
+  if (t0 + ta > tlast) sa = 0;
+  if (t0 + ta + 1 > tlast) sb = 0;
+  const f16x2 sp = fp8x2_to_f16<false>(sa | (sb << 8));
+  constexpr int NB = S::VB < 4 ? S::VB : 4;   // bytes of the slice per dword
+  constexpr int EPD = 2 * NB;                 // V tiles per slice dword
+#pragma unroll
+  for (int q = 0; q < S::VW; ++q) {
+    // a part covers VPART consecutive tiles: whole dwords, or half of one
+    if (C::VH > 1 && C::VPART >= EPD && (q * EPD) / C::VPART != part) continue;
+    uint32_t w0, w1;
+    lds_load<NB>(raw + R::OFF_VD + ta * (DV / 2) + m * S::VB + 4 * q, &w0);
+    lds_load<NB>(raw + R::OFF_VD + (ta + 1) * (DV / 2) + m * S::VB + 4 * q, &w1);
+    // byte k of lo: nibble 2k of token ta (low) and of token ta+1 (high); hi: nibble 2k+1
+    const uint32_t lo = (w0 & 0x0F0F0F0Fu) | ((w1 << 4) & 0xF0F0F0F0u);
+    const uint32_t hi = ((w0 >> 4) & 0x0F0F0F0Fu) | (w1 & 0xF0F0F0F0u);
+#pragma unroll
+    for (int k = 0; k < EPD; ++k) {
+      const int e = EPD * q + k;
+      if (C::VH > 1 && C::VPART < EPD && k / C::VPART != part) continue;
+      const uint32_t src = (k & 1) ? hi : lo;
+      f16x2 v;
+      switch (k >> 1) {
+        case 0: v = fp4x2_to_f16<0>(src); break;
+        case 1: v = fp4x2_to_f16<1>(src); break;
+        case 2: v = fp4x2_to_f16<2>(src); break;
+        default: v = fp4x2_to_f16<3>(src); break;
+      }
+      v = v * sp;
+      *(__attribute__((address_space(3))) uint32_t*)(lds_p)(size_t)(
+          opb + ((2 * S::NS + e) * 64 + c) * 16 + 4 * p) = f16x2_bits(v);
+    }
+  }
+}
+
+// Waits until this wave's copies of all but the newest issued step are done (or all
+// of them).  Waves 0..3 each copy one pool; the others copy nothing.
+template <int DK, int DV>
+__device__ __forceinline__ void coop_wait(int wave, bool one_newer) {
+  using R = typename CoopShape<DK, DV>::R;
+  constexpr int N0 = R::ndma(1), N1 = R::ndma(2), N2 = R::ndma(4), N3 = R::ndma(8);
+  if (wave > 3) return;
+  if (!one_newer) {
+    asm volatile("s_waitcnt vmcnt(0)");
+  } else if (wave == 0) {
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N0));
+  } else if (wave == 1) {
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N1));
+  } else if (wave == 2) {
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N2));
+  } else {
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N3));
+  }
+}
+
+template <int DK, int DV>
+__device__ __forceinline__ void coop_issue(int wave, const RingPlan<DK, DV, 3 * CoopShape<DK, DV>::RAW_STAGE>& rp,
+                                           uint32_t stage, const PagedView<DK, DV, true>& view,
+                                           int t0, int tlast, uint32_t& bad) {
+  constexpr int WL = 3 * CoopShape<DK, DV>::RAW_STAGE;
+  if (wave == 0) ring_issue<DK, DV, WL, 1>(rp, stage, view, t0, tlast, bad);
+  else if (wave == 1) ring_issue<DK, DV, WL, 2>(rp, stage, view, t0, tlast, bad);
+  else if (wave == 2) ring_issue<DK, DV, WL, 4>(rp, stage, view, t0, tlast, bad);
+  else if (wave == 3) ring_issue<DK, DV, WL, 8>(rp, stage, view, t0, tlast, bad);
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__((CoopShape<DK, DV>::NW * 64)) void prefill_coop_kernel(AttnArgs a) {
+  using S = StepShape<DK, DV>;
+  using C = CoopShape<DK, DV>;
+  using R = typename C::R;
+  constexpr int NR = C::NR;
+  constexpr int WL = 3 * C::RAW_STAGE;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int j = lane >> 4;
+  const int n = lane & 15;
+  const int32_t* rec = a.work + (int64_t)blockIdx.x * kWorkFields;
+  const int b = rec[W_REQ], kvh = rec[W_KVH], q0 = rec[W_ROW0], qn = rec[W_ROWS];
+  const int kv0 = rec[W_KV0], kv1 = rec[W_KV1], slot = rec[W_SLOT];
+  const int G = a.group;
+  const int Rn = qn * G;
+  const int row_base = wave * NR * 16;
+  const int qstart = a.qo_indptr[b];
+  const int qlen = a.qo_indptr[b + 1] - qstart;
+  const int off = a.kv_lens[b] - qlen;
+
+  f16x8 qf[NR][S::NS];
+  float sc[NR];
+  int last[NR];
+  bool rv[NR];
+  int64_t tokrow[NR];
+  int headi[NR];
+#pragma unroll
+  for (int rg = 0; rg < NR; ++rg) {
+    const int r = row_base + rg * 16 + n;
+    rv[rg] = r < Rn;
+    const int qi = r / G;
+    const int gh = r - qi * G;
+    const int qpos = q0 + qi;
+    tokrow[rg] = (int64_t)qstart + qpos;
+    headi[rg] = kvh * G + gh;
+    last[rg] = a.causal ? min(kv1 - 1, qpos + off) : kv1 - 1;
+    sc[rg] = a.score_scale *
+             load_q_operand<DK>(a.q + tokrow[rg] * a.q_s_row + (int64_t)headi[rg] * a.q_s_head,
+                                rv[rg], j, qf[rg]);
+  }
+  // keys the tile needs: up to the last visible key of its last row
+  const int tile_end = a.causal ? min(kv1, q0 + (Rn - 1) / G + off + 1) : kv1;
+  const int tlast = kv1 - 1;
+  const int nsteps = tile_end > kv0 ? (tile_end - kv0 + kDecodeStep - 1) / kDecodeStep : 0;
+
+  PagedView<DK, DV, true> view;
+  view.init(a, b, kvh, lane);
+  RingPlan<DK, DV, WL> rp;
+  rp.init(lane, view.k_tok, view.v_tok, view.ksf_tok, view.vsf_tok);
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
+  const uint32_t raw0 = lds0, opb0 = lds0 + 3 * C::RAW_STAGE;
+  uint32_t bad = 0;
+
+  // One wave per SIMD (wide heads): the Q operands are only ever MFMA sources, so they
+  // are kept in AGPRs, leaving the VGPRs to the accumulators and the step's operands.
+  // Two waves per SIMD: everything fits the 256 VGPRs of a wave.
+  if constexpr (C::NW == 4) {
+#pragma unroll
+    for (int rg = 0; rg < NR; ++rg)
+#pragma unroll
+      for (int s = 0; s < S::NS; ++s) asm volatile("" : "+a"(qf[rg][s]));
+  }
+
+  RowState<S::NT, AccForm::VGPR> st[NR];
+#pragma unroll
+  for (int rg = 0; rg < NR; ++rg) st[rg].init();
+
+  auto t_of = [&](int i) { return kv0 + i * kDecodeStep; };
+  // One step: wait for the next raw step, refill the ring, dequantise the next step
+  // and compute this one.  MASK: some key of the step is past some row's limit.
+  auto step = [&](int i, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const bool next = i + 1 < nsteps;
+    // raw step i+1 landed (only step i+2 may still be in flight); operands of step i
+    // are visible; nobody reads operand buffer (i+1)%2 or raw stage i%3 any more
+    if (next) coop_wait<DK, DV>(wave, i + 2 < nsteps);
+    __syncthreads();
+    if (i + 3 < nsteps)
+      coop_issue<DK, DV>(wave, rp, raw0 + (i % 3) * C::RAW_STAGE, view, t_of(i + 3), tlast, bad);
+    if (next)
+      coop_dequant<DK, DV>(raw0 + ((i + 1) % 3) * C::RAW_STAGE, opb0 + ((i + 1) & 1) * C::OPB,
+                           wave, lane, t_of(i + 1), tlast);
+    const uint32_t ob = opb0 + (i & 1) * C::OPB;
+    f16x8 ka[S::NS], kb[S::NS], vt[S::NT];
+#pragma unroll
+    for (int s = 0; s < S::NS; ++s) {
+      lds_load<16>(ob + (s * 64 + lane) * 16, reinterpret_cast<uint32_t*>(&ka[s]));
+      lds_load<16>(ob + ((S::NS + s) * 64 + lane) * 16, reinterpret_cast<uint32_t*>(&kb[s]));
+    }
+#pragma unroll
+    for (int e = 0; e < S::NT; ++e)
+      lds_load<16>(ob + ((2 * S::NS + e) * 64 + lane) * 16, reinterpret_cast<uint32_t*>(&vt[e]));
+    const int t0 = t_of(i);
+#pragma unroll
+    for (int rg = 0; rg < NR; ++rg) {
+      f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < S::NS; ++s) {
+        sa = mfma16x16x32(ka[s], qf[rg][s], sa);
+        sb = mfma16x16x32(kb[s], qf[rg][s], sb);
+      }
+      const f16x8 p = st[rg].template softmax<MASK>(sa, sb, sc[rg], t0, j, last[rg]);
+      st[rg].pv(vt, p);
+    }
+  };
+  // prologue: three steps in flight, step 0 dequantised
+  for (int i = 0; i < 3 && i < nsteps; ++i)
+    coop_issue<DK, DV>(wave, rp, raw0 + i * C::RAW_STAGE, view, t_of(i), tlast, bad);
+  if (nsteps > 0) {
+    coop_wait<DK, DV>(wave, false);
+    __syncthreads();
+    coop_dequant<DK, DV>(raw0, opb0, wave, lane, t_of(0), tlast);
+  }
+  // steps whose 32 keys are visible to every row of the tile, then the rest
+  const int tile_min_last = a.causal ? min(kv1 - 1, q0 + off) : kv1 - 1;
+  const int n_full = min(nsteps, max(0, (tile_min_last - kv0 + 1) / kDecodeStep));
+  int i = 0;
+  for (; i < n_full; ++i) step(i, std::false_type{});
+  for (; i < nsteps; ++i) step(i, std::true_type{});
+
+  const bool badw = __any(bad != 0);
+  // the four waves saw different copies: any bad page poisons the whole tile
+  __shared__ uint32_t bad_flag;
+  if (threadIdx.x == 0) bad_flag = 0;
+  __syncthreads();
+  if (badw && lane == 0) atomicOr(&bad_flag, 1u);
+  __syncthreads();
+  const bool bad_any = bad_flag != 0;
+  if (row_base >= Rn) return;
+#pragma unroll
+  for (int rg = 0; rg < NR; ++rg) {
+    if (slot < 0) {
+      st[rg].store(a.o + tokrow[rg] * a.o_s_row + (int64_t)headi[rg] * a.o_s_head,
+                   a.lse + tokrow[rg] * a.num_qo_heads + headi[rg], rv[rg], bad_any, a.out_scale, j);
+    } else {
+      const int r = row_base + rg * 16 + n;
+      st[rg].store(a.part_o + ((int64_t)slot * a.rows_per_slot + r) * DV,
+                   a.part_lse + (int64_t)slot * a.rows_per_slot + r, rv[rg], bad_any, a.out_scale, j);
+    }
+  }
+}
+
 template <int DK, int DV>
 hipError_t launch_dk_dv(int page_shift, const AttnArgs& a, hipStream_t stream) {
   const dim3 grid(a.n_work);
+  if constexpr (CoopShape<DK, DV>::OK) {
+    if (page_shift >= 4) {
+      hipLaunchKernelGGL((prefill_coop_kernel<DK, DV>), grid, dim3(CoopShape<DK, DV>::NW * 64), 0,
+                         stream, a);
+      return hipGetLastError();
+    }
+  }
   if (page_shift >= 4)
-    hipLaunchKernelGGL((prefill_kernel<DK, DV, true>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((prefill_regs_kernel<DK, DV, true>), grid, dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((prefill_kernel<DK, DV, false>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((prefill_regs_kernel<DK, DV, false>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -157,7 +446,11 @@ bool prefill_supported(int dk, int dv) {
   return okk && okv && dv <= dk && !(dk == 512 && dv == 512);
 }
 
-int prefill_rows_per_item(int dk, int /*dv*/, int /*group*/) { return 64 * (dk >= 512 ? 1 : 2); }
+int prefill_rows_per_item(int dk, int dv, int /*group*/, int page_size) {
+  if (page_size >= 16 && dk <= 256 && dv <= 256)  // cooperative kernel: waves x 2 x 16 rows
+    return dk <= 128 && dv <= 128 ? 256 : 128;
+  return 64 * (dk >= 512 ? 1 : 2);
+}
 
 size_t prefill_lds_bytes(int /*dk*/, int /*dv*/) { return 0; }
 
