@@ -268,9 +268,12 @@ __device__ __forceinline__ void v_operands(const StepRaw<DK, DV>& r, int t0, int
 // keep their registers whether or not the multiplies run (as C++ control flow, the
 // join of the two paths copies every accumulator each step).  The leading nops cover
 // the MFMA-result-to-VALU distance, the trailing ones the VALU-to-MFMA operand one.
+// The statements are not volatile: their operands order them, and a volatile
+// statement would end the scheduling region, keeping the matrix products of other
+// row groups from being interleaved with the softmax.
 __device__ __forceinline__ void scale16_if(f32x4& a, f32x4& b, f32x4& c, f32x4& d, float alpha,
                                            uint64_t raised) {
-  asm volatile(
+  asm(
       "s_cmp_eq_u64 %16, 0\n\ts_cbranch_scc1 1f\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\t"
       "v_mul_f32 %0, %0, %17\n\tv_mul_f32 %1, %1, %17\n\tv_mul_f32 %2, %2, %17\n\t"
       "v_mul_f32 %3, %3, %17\n\tv_mul_f32 %4, %4, %17\n\tv_mul_f32 %5, %5, %17\n\t"
@@ -290,7 +293,7 @@ __device__ __forceinline__ void scale16_if(f32x4& a, f32x4& b, f32x4& c, f32x4& 
 // skipped block.
 __device__ __forceinline__ void scale4_if_agpr(f32x4& a, float alpha, uint64_t raised) {
   float t;
-  asm volatile(
+  asm(
       "s_cmp_eq_u64 %5, 0\n\ts_cbranch_scc1 1f\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\t"
       "v_accvgpr_read_b32 %4, %0\n\ts_nop 1\n\tv_mul_f32 %4, %4, %6\n\tv_accvgpr_write_b32 %0, %4\n\t"
       "v_accvgpr_read_b32 %4, %1\n\ts_nop 1\n\tv_mul_f32 %4, %4, %6\n\tv_accvgpr_write_b32 %1, %4\n\t"
@@ -350,7 +353,7 @@ struct RowState {
       // alpha = exp2(m - m_new) on raising lanes (0 when m was -inf), 1 elsewhere; only
       // computed when some lane raises
       float alpha;
-      asm volatile(
+      asm(
           "s_cmp_eq_u64 %2, 0\n\ts_cbranch_scc1 1f\n\tv_sub_f32 %0, %3, %4\n\t"
           "v_cndmask_b32_e64 %0, 0, %0, %2\n\tv_exp_f32 %0, %0\n\ts_nop 1\n\t"
           "v_mul_f32 %1, %1, %0\n1:"

@@ -158,10 +158,13 @@ template <int DK, int DV>
 struct CoopShape {
   using S = StepShape<DK, DV>;
   static constexpr bool OK = DK <= 256 && DV <= 256;
-  // head dims up to 128: eight waves of two row groups (two waves per SIMD hide each
-  // other's latencies); larger: four waves of two row groups (one per SIMD)
-  static constexpr int NW = DK <= 128 && DV <= 128 ? 8 : 4;
-  static constexpr int NR = 2;                    // row groups of 16 per wave
+  // Four waves per workgroup.  Head dims up to 128: three row groups per wave and two
+  // workgroups per CU (two waves per SIMD hide each other's latencies, and the two
+  // workgroups' barriers are independent); larger: two row groups, one wave per SIMD.
+  static constexpr bool SMALL = DK <= 128 && DV <= 128;
+  static constexpr int NW = 4;
+  static constexpr int NR = SMALL ? 3 : 2;        // row groups of 16 per wave
+  static constexpr int WGS_PER_CU = SMALL ? 2 : 1;
   static constexpr int ROWS = NW * NR * 16;       // rows per work item
   static constexpr int NOP = 2 * S::NS + S::NT;   // operand vectors per step
   static constexpr int OPB = NOP * 64 * 16;       // bytes of one operand buffer
@@ -175,62 +178,89 @@ struct CoopShape {
   static_assert(S::NT % VH == 0, "V split");
 };
 
-// Dequantises one raw stage into an operand buffer.  Operand o < 2*NS is K tile o/NS
-// (token tile A or B), k-step o%NS; operand 2*NS + e is V^T tile e.  Entry (o, lane) is
-// the 16 bytes lane `lane` loads for operand o.  K entries: wave w makes entries
-// (w + NW*r, lane).  V: lane L of the workgroup makes, for the operand lane
-// c = L / (4*VH), the token pair p = L%4 of the V tiles of part (L/4)%VH.
+// Per-lane LDS offsets of the cooperative dequantisation (constant for the kernel).
+// Operand o < 2*NS is K tile o/NS (token tile A or B), k-step o%NS; operand 2*NS + e is
+// V^T tile e.  Entry (o, lane) is the 16 bytes lane `lane` loads for operand o.  K
+// entries: wave w makes entries (w + NW*r, lane).  V: lane L of the workgroup makes,
+// for the operand lane c = L / (4*VH), the token pair p = L%4 of the V tiles of part
+// (L/4)%VH.
 template <int DK, int DV>
-__device__ __forceinline__ void coop_dequant(uint32_t raw, uint32_t opb, int wave, int lane,
-                                             int t0, int tlast) {
+struct CoopLanes {
   using S = StepShape<DK, DV>;
   using C = CoopShape<DK, DV>;
   using R = typename C::R;
+  uint32_t k_raw[C::KE], k_sc[C::KE], k_dst[C::KE];
+  int k_tok[C::KE];
+  uint32_t v_raw, v_sc, v_dst;
+  int v_tok, part;
+
+  __device__ __forceinline__ void init(int wave, int lane) {
+    const int j = lane >> 4, n = lane & 15;
+#pragma unroll
+    for (int r = 0; r < C::KE; ++r) {
+      const int o = min(wave + C::NW * r, 2 * S::NS - 1);  // clamped: unused when past the end
+      const int tile = o / S::NS, s = o % S::NS;
+      k_tok[r] = 8 * (n >> 2) + (n & 3) + 4 * tile;
+      k_raw[r] = R::OFF_KD + k_tok[r] * (DK / 2) + j * S::KB + 4 * s;
+      k_sc[r] = R::OFF_SF + k_tok[r] * (DK / 16) + j * S::KSF + (s >> 1);
+      k_dst[r] = (o * 64 + lane) * 16;
+    }
+    const int L = wave * 64 + lane;
+    const int c = L / (4 * C::VH), p = L & 3;
+    part = (L >> 2) % C::VH;
+    const int jj = c >> 4, m = c & 15;
+    v_tok = 8 * jj + 2 * p;
+    v_raw = R::OFF_VD + v_tok * (DV / 2) + m * S::VB;
+    v_sc = R::OFF_SF + R::KS + v_tok * (DV / 16) + (m * (DV / 16)) / 16;
+    v_dst = (2 * S::NS * 64 + c) * 16 + 4 * p;
+  }
+};
+
+// Dequantises the raw stage at `raw` into the operand buffer at `opb`.  MASK: keys past
+// `kleft` (tokens of the step after the chunk's last key) get scale 0, so that their
+// bytes, whatever they hold, dequantise to finite zeros.
+template <int DK, int DV, bool MASK>
+__device__ __forceinline__ void coop_dequant(uint32_t raw, uint32_t opb, int wave,
+                                             const CoopLanes<DK, DV>& cl, int kleft) {
+  using S = StepShape<DK, DV>;
+  using C = CoopShape<DK, DV>;
   typedef __attribute__((address_space(3))) uint8_t* lds_p;
-  const int j = lane >> 4, n = lane & 15;
-  // K entries
 #pragma unroll
   for (int r = 0; r < C::KE; ++r) {
-    const int o = wave + C::NW * r;  // wave-uniform
-    if (o < 2 * S::NS) {
-      const int tile = o / S::NS, s = o % S::NS;
-      const int tok = 8 * (n >> 2) + (n & 3) + 4 * tile;
+    if (wave + C::NW * r < 2 * S::NS) {  // wave-uniform
       uint32_t w, sc;
-      lds_load<4>(raw + R::OFF_KD + tok * (DK / 2) + j * S::KB + 4 * s, &w);
-      lds_load<1>(raw + R::OFF_SF + tok * (DK / 16) + j * S::KSF + (s >> 1), &sc);
-      if (t0 + tok > tlast) sc = 0;  // keys past the chunk: finite zeros
+      lds_load<4>(raw + cl.k_raw[r], &w);
+      lds_load<1>(raw + cl.k_sc[r], &sc);
+      if (MASK && cl.k_tok[r] > kleft) sc = 0;
       const f16x8 v = dequant8(w, splat_lo(fp8x2_to_f16<false>(sc)));
-      *(__attribute__((address_space(3))) f16x8*)(lds_p)(size_t)(opb + (o * 64 + lane) * 16) = v;
+      *(__attribute__((address_space(3))) f16x8*)(lds_p)(size_t)(opb + cl.k_dst[r]) = v;
     }
   }
-  // V entries
-  const int L = wave * 64 + lane;
-  const int c = L / (4 * C::VH), p = L & 3, part = (L >> 2) % C::VH;
-  const int jj = c >> 4, m = c & 15;
-  const int ta = 8 * jj + 2 * p;
   uint32_t sa, sb;
-  const int blk = (m * (DV / 16)) / 16;
-  lds_load<1>(raw + R::OFF_SF + R::KS + ta * (DV / 16) + blk, &sa);
-  lds_load<1>(raw + R::OFF_SF + R::KS + (ta + 1) * (DV / 16) + blk, &sb);
-  if (t0 + ta > tlast) sa = 0;
-  if (t0 + ta + 1 > tlast) sb = 0;
+  const uint32_t vs = raw + cl.v_sc;
+  lds_load<1>(vs, &sa);
+  lds_load<1>(vs + DV / 16, &sb);
+  if (MASK && cl.v_tok > kleft) sa = 0;
+  if (MASK && cl.v_tok + 1 > kleft) sb = 0;
   const f16x2 sp = fp8x2_to_f16<false>(sa | (sb << 8));
   constexpr int NB = S::VB < 4 ? S::VB : 4;   // bytes of the slice per dword
   constexpr int EPD = 2 * NB;                 // V tiles per slice dword
+  const uint32_t vr = raw + cl.v_raw;
+  const uint32_t vd = opb + cl.v_dst;
 #pragma unroll
   for (int q = 0; q < S::VW; ++q) {
-    // a part covers VPART consecutive tiles: whole dwords, or half of one
-    if (C::VH > 1 && C::VPART >= EPD && (q * EPD) / C::VPART != part) continue;
+    // a part covers VPART consecutive tiles: whole dwords, or a share of one
+    if (C::VH > 1 && C::VPART >= EPD && (q * EPD) / C::VPART != cl.part) continue;
     uint32_t w0, w1;
-    lds_load<NB>(raw + R::OFF_VD + ta * (DV / 2) + m * S::VB + 4 * q, &w0);
-    lds_load<NB>(raw + R::OFF_VD + (ta + 1) * (DV / 2) + m * S::VB + 4 * q, &w1);
+    lds_load<NB>(vr + 4 * q, &w0);
+    lds_load<NB>(vr + DV / 2 + 4 * q, &w1);
     // byte k of lo: nibble 2k of token ta (low) and of token ta+1 (high); hi: nibble 2k+1
     const uint32_t lo = (w0 & 0x0F0F0F0Fu) | ((w1 << 4) & 0xF0F0F0F0u);
     const uint32_t hi = ((w0 >> 4) & 0x0F0F0F0Fu) | (w1 & 0xF0F0F0F0u);
 #pragma unroll
     for (int k = 0; k < EPD; ++k) {
       const int e = EPD * q + k;
-      if (C::VH > 1 && C::VPART < EPD && k / C::VPART != part) continue;
+      if (C::VH > 1 && C::VPART < EPD && k / C::VPART != cl.part) continue;
       const uint32_t src = (k & 1) ? hi : lo;
       f16x2 v;
       switch (k >> 1) {
@@ -240,8 +270,7 @@ __device__ __forceinline__ void coop_dequant(uint32_t raw, uint32_t opb, int wav
         default: v = fp4x2_to_f16<3>(src); break;
       }
       v = v * sp;
-      *(__attribute__((address_space(3))) uint32_t*)(lds_p)(size_t)(
-          opb + ((2 * S::NS + e) * 64 + c) * 16 + 4 * p) = f16x2_bits(v);
+      *(__attribute__((address_space(3))) uint32_t*)(lds_p)(size_t)(vd + e * 1024) = f16x2_bits(v);
     }
   }
 }
@@ -278,7 +307,9 @@ __device__ __forceinline__ void coop_issue(int wave, const RingPlan<DK, DV, 3 * 
 }
 
 template <int DK, int DV>
-__global__ __launch_bounds__((CoopShape<DK, DV>::NW * 64)) void prefill_coop_kernel(AttnArgs a) {
+__global__ __launch_bounds__((CoopShape<DK, DV>::NW * 64))
+__attribute__((amdgpu_waves_per_eu(CoopShape<DK, DV>::WGS_PER_CU)))
+void prefill_coop_kernel(AttnArgs a) {
   using S = StepShape<DK, DV>;
   using C = CoopShape<DK, DV>;
   using R = typename C::R;
@@ -330,12 +361,14 @@ __global__ __launch_bounds__((CoopShape<DK, DV>::NW * 64)) void prefill_coop_ker
   rp.init(lane, view.k_tok, view.v_tok, view.ksf_tok, view.vsf_tok);
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
   const uint32_t raw0 = lds0, opb0 = lds0 + 3 * C::RAW_STAGE;
+  CoopLanes<DK, DV> cl;
+  cl.init(wave, lane);
   uint32_t bad = 0;
 
   // One wave per SIMD (wide heads): the Q operands are only ever MFMA sources, so they
   // are kept in AGPRs, leaving the VGPRs to the accumulators and the step's operands.
   // Two waves per SIMD: everything fits the 256 VGPRs of a wave.
-  if constexpr (C::NW == 4) {
+  if constexpr (C::WGS_PER_CU == 1) {
 #pragma unroll
     for (int rg = 0; rg < NR; ++rg)
 #pragma unroll
@@ -358,29 +391,43 @@ __global__ __launch_bounds__((CoopShape<DK, DV>::NW * 64)) void prefill_coop_ker
     __syncthreads();
     if (i + 3 < nsteps)
       coop_issue<DK, DV>(wave, rp, raw0 + (i % 3) * C::RAW_STAGE, view, t_of(i + 3), tlast, bad);
-    if (next)
-      coop_dequant<DK, DV>(raw0 + ((i + 1) % 3) * C::RAW_STAGE, opb0 + ((i + 1) & 1) * C::OPB,
-                           wave, lane, t_of(i + 1), tlast);
+    if (next) {
+      const uint32_t rs = raw0 + ((i + 1) % 3) * C::RAW_STAGE, ob1 = opb0 + ((i + 1) & 1) * C::OPB;
+      if (t_of(i + 1) + kDecodeStep - 1 > tlast)
+        coop_dequant<DK, DV, true>(rs, ob1, wave, cl, tlast - t_of(i + 1));
+      else
+        coop_dequant<DK, DV, false>(rs, ob1, wave, cl, 0);
+    }
+    // S = K Q^T for every row group first (the K operands are then dead), then per row
+    // group the softmax and O^T += V^T P^T; the PV products of group g can run beside
+    // the softmax of group g+1.
     const uint32_t ob = opb0 + (i & 1) * C::OPB;
+    const int t0 = t_of(i);
+    const uint32_t obl = ob + lane * 16;  // this lane's entry of operand 0
     f16x8 ka[S::NS], kb[S::NS], vt[S::NT];
 #pragma unroll
     for (int s = 0; s < S::NS; ++s) {
-      lds_load<16>(ob + (s * 64 + lane) * 16, reinterpret_cast<uint32_t*>(&ka[s]));
-      lds_load<16>(ob + ((S::NS + s) * 64 + lane) * 16, reinterpret_cast<uint32_t*>(&kb[s]));
+      lds_load<16>(obl + s * 1024, reinterpret_cast<uint32_t*>(&ka[s]));
+      lds_load<16>(obl + (S::NS + s) * 1024, reinterpret_cast<uint32_t*>(&kb[s]));
     }
-#pragma unroll
-    for (int e = 0; e < S::NT; ++e)
-      lds_load<16>(ob + ((2 * S::NS + e) * 64 + lane) * 16, reinterpret_cast<uint32_t*>(&vt[e]));
-    const int t0 = t_of(i);
-#pragma unroll
-    for (int rg = 0; rg < NR; ++rg) {
-      f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+    f32x4 sa[NR], sb[NR];
+    auto qk = [&](int rg) {
+      sa[rg] = f32x4{0.f, 0.f, 0.f, 0.f};
+      sb[rg] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < S::NS; ++s) {
-        sa = mfma16x16x32(ka[s], qf[rg][s], sa);
-        sb = mfma16x16x32(kb[s], qf[rg][s], sb);
+        sa[rg] = mfma16x16x32(ka[s], qf[rg][s], sa[rg]);
+        sb[rg] = mfma16x16x32(kb[s], qf[rg][s], sb[rg]);
       }
-      const f16x8 p = st[rg].template softmax<MASK>(sa, sb, sc[rg], t0, j, last[rg]);
+    };
+#pragma unroll
+    for (int rg = 0; rg < NR; ++rg) qk(rg);
+#pragma unroll
+    for (int e = 0; e < S::NT; ++e)
+      lds_load<16>(obl + (2 * S::NS + e) * 1024, reinterpret_cast<uint32_t*>(&vt[e]));
+#pragma unroll
+    for (int rg = 0; rg < NR; ++rg) {
+      const f16x8 p = st[rg].template softmax<MASK>(sa[rg], sb[rg], sc[rg], t0, j, last[rg]);
       st[rg].pv(vt, p);
     }
   };
@@ -390,7 +437,7 @@ __global__ __launch_bounds__((CoopShape<DK, DV>::NW * 64)) void prefill_coop_ker
   if (nsteps > 0) {
     coop_wait<DK, DV>(wave, false);
     __syncthreads();
-    coop_dequant<DK, DV>(raw0, opb0, wave, lane, t_of(0), tlast);
+    coop_dequant<DK, DV, true>(raw0, opb0, wave, cl, tlast - t_of(0));
   }
   // steps whose 32 keys are visible to every row of the tile, then the rest
   const int tile_min_last = a.causal ? min(kv1 - 1, q0 + off) : kv1 - 1;
@@ -447,8 +494,8 @@ bool prefill_supported(int dk, int dv) {
 }
 
 int prefill_rows_per_item(int dk, int dv, int /*group*/, int page_size) {
-  if (page_size >= 16 && dk <= 256 && dv <= 256)  // cooperative kernel: waves x 2 x 16 rows
-    return dk <= 128 && dv <= 128 ? 256 : 128;
+  if (page_size >= 16 && dk <= 256 && dv <= 256)  // cooperative kernel: 4 waves x NR x 16 rows
+    return dk <= 128 && dv <= 128 ? 192 : 128;
   return 64 * (dk >= 512 ? 1 : 2);
 }
 
