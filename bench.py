@@ -16,7 +16,10 @@ the attention kernel's own figure: its algorithmic bytes (KV + Q + O + LSE) over
 average duration, timed with HIP events around each launch inside the timed steps
 (events created without the system-scope fence, which would add to every launch).
 
-Other modes (profiling support, see the design doc for the commands):
+With --workload naming a prefill workload, the timed step is that prefill's attention
+pass and merge instead (TFLOP/s; used to profile the prefill kernel).
+
+Other modes (profiling support):
   --pmc-run                a short program for rocprofv3 counter passes: a 1 GiB copy
                            (counter calibration) and a few steps of the workload;
   --summarize-trace DIR    summarise a rocprofv3 --kernel-trace --stats output dir;
@@ -380,6 +383,47 @@ def summarize_pmc(args):
     print(text)
 
 
+def prefill_main(args, torch, nv, paged, synth):
+    """A prefill workload as the timed step (for profiling the prefill kernel): the
+    attention pass and the merge of its split rows, prepared once."""
+    w = synth.workload(args.workload)
+    case = paged.build_case(w, keep_sources=False)
+    plan = paged.make_plan(case)
+    plan.set_deferred_merge(True)
+    ws = plan.new_workspace()
+    plan.upload(ws)
+    o = torch.empty((w.total_q, w.num_qo_heads, w.head_dim_vo), device="cuda")
+    lse = torch.empty((w.total_q, w.num_qo_heads), device="cuda")
+    run = nv.batch_prefill(plan, case.q, case.page_table, case.k_pool, case.v_pool, w.sm_scale,
+                           ws, out=o, lse=lse, prepare=True)
+    merge = nv.merge_partials(plan, ws, o, lse, prepare=True)
+    for _ in range(args.warmup):
+        run()
+        merge()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run_ms, merge_ms = timed_passes(torch, nv, run, merge, args.steps)
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    fl = w.flops()
+    info = plan.info()
+    out = {"metric": "NVFP4 paged prefill TFLOP/s (% MFMA peak)",
+           "value": round(fl / (ms_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+           "data": "synthetic (seeded N(0,1) bf16 Q/K/V, K/V NVFP4-quantised on the GPU)",
+           "config": {"workload": w.name, "batch": w.batch, "num_qo_heads": w.num_qo_heads,
+                      "num_kv_heads": w.num_kv_heads, "head_dim_qk": w.head_dim_qk,
+                      "head_dim_vo": w.head_dim_vo, "causal": w.causal,
+                      "work_items": info["num_work_items"]},
+           "roofline": {"bound": "mfma", "achieved": round(fl / run_ms / 1e9, 2),
+                        "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(fl / run_ms / 1e9 / MFMA_F16_PEAK_TFLOPS, 4),
+                        "traffic": None, "flops_per_launch": fl,
+                        "avg_launch_ms": round(run_ms, 5)},
+           "step_breakdown_ms": {"attention": round(run_ms, 5), "merge": round(merge_ms, 5)}}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.summarize_trace:
@@ -388,7 +432,7 @@ def main():
         return summarize_pmc(args)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards by request or kv head with no exchange; see DESIGN.md)",
+              "(the path shards by request or kv head with no exchange between GPUs)",
               file=sys.stderr)
         sys.exit(2)
     if args.pmc_run:
@@ -397,6 +441,8 @@ def main():
     import attention_bit_paged_amd as nv
     from attention_bit_paged_amd import paged, synth
 
+    if not synth.workload(args.workload).decode:
+        return prefill_main(args, torch, nv, paged, synth)
     d = Decoder(torch, nv, paged, synth, args.workload, args.pool_sets)
     w, info = d.w, d.plan.info()
     for i in range(args.warmup):
