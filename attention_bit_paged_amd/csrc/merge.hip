@@ -23,19 +23,26 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 // Partials of split row groups, after the attention kernel: one wave per (merge
 // record, row).  A row is one qo head of the group (decode) or one (query, qo head) pair
-// of a query tile (prefill); each partial holds a normalised O row and its LSE.  The
-// partials' LSEs are read by the lanes in parallel (64 partials at a time); each
-// lane then sums its DV/64 value dims over the partials, several loads in flight.
+// of a query tile (prefill); each partial holds a normalised O row and its LSE.  Lane
+// p reads partial p's LSE; each lane sums its DV/64 value dims over the partials.  With
+// at most FAST partials every load is issued at once, before any weight is known, so
+// the merge costs one memory round trip after the record; more partials are taken 64
+// LSEs at a time with eight row loads in flight.
 template <int DV>
 __global__ __launch_bounds__(256) void merge_partials_kernel(AttnArgs a, int n_merges, int prefill) {
+  constexpr int FAST = 8;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int64_t task = (int64_t)blockIdx.x * 4 + wave;
+  // the host keeps merges x rows below 2^31
+  const int task = (int)blockIdx.x * 4 + wave;
   const int rows_per_merge = a.rows_per_slot;
-  if (task >= (int64_t)n_merges * rows_per_merge) return;
-  const int mi = (int)(task / rows_per_merge);
-  const int r = (int)(task - (int64_t)mi * rows_per_merge);
-  const int32_t* rec = a.merges + (int64_t)mi * kMergeFields;
+  if (task >= n_merges * rows_per_merge) return;
+  const int mi = task / rows_per_merge;
+  const int r = task - mi * rows_per_merge;
+  // the whole record in one scalar load (records are 32-byte aligned)
+  typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+  static_assert(kMergeFields == 8, "merge record");
+  const i32x8 rec = *reinterpret_cast<const i32x8*>(a.merges + (int64_t)mi * kMergeFields);
   const int b = rec[0], kvh = rec[1], row0 = rec[2], nrow = rec[3], first = rec[4], np = rec[5];
   int64_t orow;
   int head;
@@ -53,59 +60,88 @@ __global__ __launch_bounds__(256) void merge_partials_kernel(AttnArgs a, int n_m
   constexpr int PER = DV / 64;  // lane covers value dims [lane * PER, (lane + 1) * PER)
   const int64_t rps = a.rows_per_slot;
   const int64_t row_of_first = (int64_t)first * rps + r;  // partial p: row_of_first + p * rps
+  const float* src = a.part_o + row_of_first * DV + lane * PER;
+  const int64_t step = rps * DV;
   auto lse_of = [&](int p) { return p < np ? a.part_lse[row_of_first + (int64_t)p * rps] : -INFINITY; };
-
-  float mx = -INFINITY;
-  bool nan = false;
-  for (int p0 = 0; p0 < np; p0 += 64) {
-    const float lp = lse_of(p0 + lane);
-    nan |= lp != lp;
-    mx = fmaxf(mx, lp);
-  }
-  mx = wave_max(mx);
-  const bool any_nan = __any(nan);
+  auto load_row = [&](const float* s, float (&v)[PER]) {
+    if constexpr (PER == 1) {
+      v[0] = s[0];
+    } else if constexpr (PER == 2) {
+      const float2 x = *reinterpret_cast<const float2*>(s);
+      v[0] = x.x;
+      v[1] = x.y;
+    } else {
+#pragma unroll
+      for (int k = 0; k < PER; k += 4) {
+        const float4 x = *reinterpret_cast<const float4*>(s + k);
+        v[k] = x.x;
+        v[k + 1] = x.y;
+        v[k + 2] = x.z;
+        v[k + 3] = x.w;
+      }
+    }
+  };
+  auto lane_weight = [&](float w, int q) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), q));
+  };
 
   float acc[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) acc[k] = 0.f;
-  float wsum = 0.f;
-  if (mx > -INFINITY) {
+  float mx, wsum = 0.f;
+  bool any_nan;
+  if (np <= FAST) {
+    const float lp = lse_of(lane);
+    float v[FAST][PER];
+#pragma unroll
+    for (int q = 0; q < FAST; ++q) load_row(src + (q < np ? q : 0) * step, v[q]);  // in bounds
+    any_nan = __any(lp != lp);
+    mx = wave_max(lp);
+    if (mx > -INFINITY) {
+      const float w = lp > -INFINITY ? __expf(lp - mx) : 0.f;  // 0 on lanes >= np
+      wsum = wave_sum(w);
+#pragma unroll
+      for (int q = 0; q < FAST; ++q) {
+        if (q < np) {
+          const float wq = lane_weight(w, q);
+#pragma unroll
+          for (int k = 0; k < PER; ++k) acc[k] += wq * v[q][k];
+        }
+      }
+    }
+  } else {
+    mx = -INFINITY;
+    bool nan = false;
     for (int p0 = 0; p0 < np; p0 += 64) {
       const float lp = lse_of(p0 + lane);
-      const float w = lp > -INFINITY ? __expf(lp - mx) : 0.f;  // weight of partial p0 + lane
-      wsum += w;
-      const int cnt = min(64, np - p0);
-      const float* src = a.part_o + (row_of_first + (int64_t)p0 * rps) * DV + lane * PER;
-      const int64_t step = rps * DV;
-      auto add = [&](int q) {
-        const float wq = __builtin_bit_cast(
-            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), q));
-        const float* s = src + q * step;
-        if constexpr (PER == 1) {
-          acc[0] += wq * s[0];
-        } else if constexpr (PER == 2) {
-          const float2 v = *reinterpret_cast<const float2*>(s);
-          acc[0] += wq * v.x;
-          acc[1] += wq * v.y;
-        } else {
-#pragma unroll
-          for (int k = 0; k < PER; k += 4) {
-            const float4 v = *reinterpret_cast<const float4*>(s + k);
-            acc[k] += wq * v.x;
-            acc[k + 1] += wq * v.y;
-            acc[k + 2] += wq * v.z;
-            acc[k + 3] += wq * v.w;
-          }
-        }
-      };
-      int q = 0;
-      for (; q + 8 <= cnt; q += 8) {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) add(q + u);
-      }
-      for (; q < cnt; ++q) add(q);
+      nan |= lp != lp;
+      mx = fmaxf(mx, lp);
     }
-    wsum = wave_sum(wsum);
+    mx = wave_max(mx);
+    any_nan = __any(nan);
+    if (mx > -INFINITY) {
+      for (int p0 = 0; p0 < np; p0 += 64) {
+        const float lp = lse_of(p0 + lane);
+        const float w = lp > -INFINITY ? __expf(lp - mx) : 0.f;  // weight of partial p0 + lane
+        wsum += w;
+        const int cnt = min(64, np - p0);
+        const float* base = src + (int64_t)p0 * step;
+        auto add = [&](int q) {
+          const float wq = lane_weight(w, q);
+          float v[PER];
+          load_row(base + q * step, v);
+#pragma unroll
+          for (int k = 0; k < PER; ++k) acc[k] += wq * v[k];
+        };
+        int q = 0;
+        for (; q + 8 <= cnt; q += 8) {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) add(q + u);
+        }
+        for (; q < cnt; ++q) add(q);
+      }
+      wsum = wave_sum(wsum);
+    }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   float* dst = a.o + orow * a.o_s_row + (int64_t)head * a.o_s_head + lane * PER;
@@ -171,6 +207,7 @@ hipError_t launch_merge_partials(const AttnArgs& a, int n_merges, int dv, int pr
                                  hipStream_t stream) {
   if (n_merges <= 0) return hipSuccess;
   const int64_t tasks = (int64_t)n_merges * a.rows_per_slot;
+  if (tasks + 4 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;  // 32-bit task index
   const dim3 grid((unsigned)((tasks + 3) / 4));
   switch (dv) {
     case 64: hipLaunchKernelGGL(merge_partials_kernel<64>, grid, dim3(256), 0, stream, a, n_merges, prefill); break;
