@@ -263,56 +263,39 @@ __device__ __forceinline__ void v_operands(const StepRaw<DK, DV>& r, int t0, int
   for (int e = 0; e < S::NT; ++e) vt[e] = pack8(vp[e][0], vp[e][1], vp[e][2], vp[e][3]);
 }
 
-// Multiplies 16 accumulators by alpha on the lanes of a wave whose `raised` mask is
-// non-zero.  The test and the multiplies sit in one asm statement, so the accumulators
-// keep their registers whether or not the multiplies run (as C++ control flow, the
-// join of the two paths copies every accumulator each step).  The leading nops cover
-// the MFMA-result-to-VALU distance, the trailing ones the VALU-to-MFMA operand one.
-// The statements are not volatile: their operands order them, and a volatile
-// statement would end the scheduling region, keeping the matrix products of other
-// row groups from being interleaved with the softmax.
-__device__ __forceinline__ void scale16_if(f32x4& a, f32x4& b, f32x4& c, f32x4& d, float alpha,
-                                           uint64_t raised) {
+// Multiplies 16 accumulators by alpha in place.  One asm statement whose operands are
+// the accumulators themselves: under a branch, the registers stay where they are (as
+// C++ arithmetic, the join of the two paths copies every accumulator).  The leading
+// nops cover the MFMA-result-to-VALU distance, the trailing ones the VALU-to-MFMA
+// operand one.  Not volatile: the operands order it, and a volatile statement would
+// end the scheduling region around it.
+__device__ __forceinline__ void scale16(f32x4& a, f32x4& b, f32x4& c, f32x4& d, float alpha) {
   asm(
-      "s_cmp_eq_u64 %16, 0\n\ts_cbranch_scc1 1f\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\t"
-      "v_mul_f32 %0, %0, %17\n\tv_mul_f32 %1, %1, %17\n\tv_mul_f32 %2, %2, %17\n\t"
-      "v_mul_f32 %3, %3, %17\n\tv_mul_f32 %4, %4, %17\n\tv_mul_f32 %5, %5, %17\n\t"
-      "v_mul_f32 %6, %6, %17\n\tv_mul_f32 %7, %7, %17\n\tv_mul_f32 %8, %8, %17\n\t"
-      "v_mul_f32 %9, %9, %17\n\tv_mul_f32 %10, %10, %17\n\tv_mul_f32 %11, %11, %17\n\t"
-      "v_mul_f32 %12, %12, %17\n\tv_mul_f32 %13, %13, %17\n\tv_mul_f32 %14, %14, %17\n\t"
-      "v_mul_f32 %15, %15, %17\n\ts_nop 4\n1:"
+      "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\t"
+      "v_mul_f32 %0, %0, %16\n\tv_mul_f32 %1, %1, %16\n\tv_mul_f32 %2, %2, %16\n\t"
+      "v_mul_f32 %3, %3, %16\n\tv_mul_f32 %4, %4, %16\n\tv_mul_f32 %5, %5, %16\n\t"
+      "v_mul_f32 %6, %6, %16\n\tv_mul_f32 %7, %7, %16\n\tv_mul_f32 %8, %8, %16\n\t"
+      "v_mul_f32 %9, %9, %16\n\tv_mul_f32 %10, %10, %16\n\tv_mul_f32 %11, %11, %16\n\t"
+      "v_mul_f32 %12, %12, %16\n\tv_mul_f32 %13, %13, %16\n\tv_mul_f32 %14, %14, %16\n\t"
+      "v_mul_f32 %15, %15, %16\n\ts_nop 4"
       : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]),
         "+v"(b[3]), "+v"(c[0]), "+v"(c[1]), "+v"(c[2]), "+v"(c[3]), "+v"(d[0]), "+v"(d[1]),
         "+v"(d[2]), "+v"(d[3])
-      : "s"(raised), "v"(alpha)
-      : "scc");
+      : "v"(alpha));
 }
 
-// The same for accumulators held in AGPRs (MFMA results left in the accumulation
-// registers): each value is read out, scaled and written back, all inside the
-// skipped block.
-__device__ __forceinline__ void scale4_if_agpr(f32x4& a, float alpha, uint64_t raised) {
-  float t;
-  asm(
-      "s_cmp_eq_u64 %5, 0\n\ts_cbranch_scc1 1f\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\t"
-      "v_accvgpr_read_b32 %4, %0\n\ts_nop 1\n\tv_mul_f32 %4, %4, %6\n\tv_accvgpr_write_b32 %0, %4\n\t"
-      "v_accvgpr_read_b32 %4, %1\n\ts_nop 1\n\tv_mul_f32 %4, %4, %6\n\tv_accvgpr_write_b32 %1, %4\n\t"
-      "v_accvgpr_read_b32 %4, %2\n\ts_nop 1\n\tv_mul_f32 %4, %4, %6\n\tv_accvgpr_write_b32 %2, %4\n\t"
-      "v_accvgpr_read_b32 %4, %3\n\ts_nop 1\n\tv_mul_f32 %4, %4, %6\n\tv_accvgpr_write_b32 %3, %4\n\t"
-      "s_nop 4\n1:"
-      : "+a"(a[0]), "+a"(a[1]), "+a"(a[2]), "+a"(a[3]), "=&v"(t)
-      : "s"(raised), "v"(alpha)
-      : "scc");
-}
-
-// Where the accumulators of a RowState live and how the rare rescale reaches them.
-enum class AccForm { VGPR, AGPR, PLAIN };
+// Where the accumulators of a RowState live: VGPRs rescaled in place by scale16, or
+// left to plain code.
+enum class AccForm { VGPR, PLAIN };
 
 // Online-softmax state of one 16-row group (base-2 scores).  `m` is a reference point,
 // not necessarily the running maximum: it is raised only when a row's maximum exceeds
 // it by kRescaleSlack, so p = exp2(x - m) <= 2^8.  O = acc / l and LSE = m + log2(l)
-// hold for any reference point.  FORM: accumulators in VGPRs or AGPRs, rescaled in
-// place by one asm statement (scale16_if / scale4_if_agpr), or left to plain code.
+// hold for any reference point; `l` is this lane's share of the row sum (its 8 keys of
+// every step), completed over the row's four lanes at the end.  A step forms the
+// row-wide maximum (a cross-lane exchange) only when some lane of the wave holds a key
+// more than the slack above the reference, which is rare once the reference has
+// settled; the other lanes of its row can only be lower.
 template <int NT, AccForm FORM>
 struct RowState {
   f32x4 acc[NT];
@@ -342,71 +325,48 @@ struct RowState {
       for (int i = 0; i < 8; ++i)
         if (t0 + 8 * j + i > last) x[i] = -INFINITY;
     }
+    // this lane's largest raw score of the step.  Plain fmaxf: the scores come straight
+    // from the matrix unit, and only compiler-generated code gets the wait states a
+    // VALU read of an MFMA result needs (an asm statement would hide the read).
     const float b1 = fmaxf(fmaxf(x[0], x[1]), x[2]);
     const float b2 = fmaxf(fmaxf(x[3], x[4]), x[5]);
     const float b3 = fmaxf(fmaxf(x[6], x[7]), b1);
-    const float bm = max_over_groups(fmaxf(b3, b2)) * c;
-    const bool raise = bm > m + kRescaleSlack;
-    const float m_new = raise ? bm : m;
-    if constexpr (FORM != AccForm::PLAIN) {
-      const uint64_t raised = __ballot(raise);
-      // alpha = exp2(m - m_new) on raising lanes (0 when m was -inf), 1 elsewhere; only
-      // computed when some lane raises
-      float alpha;
-      asm(
-          "s_cmp_eq_u64 %2, 0\n\ts_cbranch_scc1 1f\n\tv_sub_f32 %0, %3, %4\n\t"
-          "v_cndmask_b32_e64 %0, 0, %0, %2\n\tv_exp_f32 %0, %0\n\ts_nop 1\n\t"
-          "v_mul_f32 %1, %1, %0\n1:"
-          : "=&v"(alpha), "+v"(l)
-          : "s"(raised), "v"(m), "v"(m_new)
-          : "scc");
+    const float bm = fmaxf(b3, b2);
+    // bm * c - m is +inf while m is -inf (any key raises), NaN when both are -inf (the
+    // lane has no key yet: nothing to raise)
+    if (__ballot(fmaf(bm, c, -m) > kRescaleSlack) != 0) {
+      const float bmr = max_over_groups(bm) * c;  // the row's largest scaled score
+      const bool raise = bmr > m + kRescaleSlack;
+      const float m_new = raise ? bmr : m;
+      const float alpha = raise ? fast_exp2(m - m_new) : 1.f;  // 0 when m was -inf
       if constexpr (FORM == AccForm::VGPR) {
 #pragma unroll
-        for (int e = 0; e < NT; e += 4)
-          scale16_if(acc[e], acc[e + 1], acc[e + 2], acc[e + 3], alpha, raised);
+        for (int e = 0; e < NT; e += 4) scale16(acc[e], acc[e + 1], acc[e + 2], acc[e + 3], alpha);
       } else {
-#pragma unroll
-        for (int e = 0; e < NT; ++e) scale4_if_agpr(acc[e], alpha, raised);
-      }
-    } else {
-      if (__any(raise)) {
-        const float alpha = fast_exp2(m - m_new);  // 0 when m was -inf
-        l *= alpha;
 #pragma unroll
         for (int e = 0; e < NT; ++e) acc[e] *= alpha;
       }
+      l *= alpha;
+      m = m_new;
     }
-    m = m_new;
     const float m_use = MASK ? (m == -INFINITY ? 0.f : m) : m;
-    float psum = 0.f;
     f16x2 pp[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float p0 = fast_exp2(fmaf(x[2 * i], c, -m_use));
       const float p1 = fast_exp2(fmaf(x[2 * i + 1], c, -m_use));
-      psum += p0 + p1;
       pp[i] = f16x2{(_Float16)p0, (_Float16)p1};
     }
-    l += psum;
+    // the row sum takes the fp16 values the PV product uses
+    const f16x2 one2 = {(_Float16)1.f, (_Float16)1.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) l = __builtin_amdgcn_fdot2(pp[i], one2, l, false);
     return pack8(pp[0], pp[1], pp[2], pp[3]);
   }
 
   __device__ __forceinline__ void pv(const f16x8 (&vt)[NT], f16x8 p) {
 #pragma unroll
     for (int e = 0; e < NT; ++e) acc[e] = mfma16x16x32(vt[e], p, acc[e]);
-  }
-
-  // Fold another state of the same rows into this one (same lane layout).
-  __device__ __forceinline__ void combine(float m2, float l2, const float* acc2) {
-    const float mx = fmaxf(m, m2);
-    const float mu = mx == -INFINITY ? 0.f : mx;
-    const float f1 = fast_exp2(m - mu), f2 = fast_exp2(m2 - mu);
-#pragma unroll
-    for (int e = 0; e < NT; ++e)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[e][i] = acc[e][i] * f1 + acc2[4 * e + i] * f2;
-    l = l * f1 + l2 * f2;
-    m = mx;
   }
 
   // Normalise and store this lane's part of the row: value dims (4j+i)*NT + e.  The row
