@@ -57,24 +57,28 @@ __device__ __forceinline__ uint32_t e2m1_code(double a, double sg) {
   return c;
 }
 
+// One thread per 16-element block.  IDX: the index type, 32-bit whenever the block
+// count allows (64-bit division is a long software sequence on the GPU).
+template <typename IDX>
 __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs ka, QuantArgs va,
                                                        int64_t n_tokens,
                                                        const int64_t* __restrict__ slots) {
   const QuantArgs& a = blockIdx.y == 0 ? ka : va;
   const int blocks_per_row = a.head_dim / 16;
-  const int64_t total = n_tokens * a.num_heads * blocks_per_row;
-  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
-       idx += (int64_t)gridDim.x * blockDim.x) {
+  const IDX total = (IDX)(n_tokens * a.num_heads * blocks_per_row);
+  for (IDX idx = (IDX)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (IDX)gridDim.x * blockDim.x) {
     const int blk = (int)(idx % blocks_per_row);
-    const int64_t th = idx / blocks_per_row;
+    const IDX th = idx / blocks_per_row;
     const int head = (int)(th % a.num_heads);
-    const int64_t tok = th / a.num_heads;
-    const int64_t slot = slots[tok];
-    if (slot < 0 || slot >= a.num_slots) continue;
+    const int64_t tok = (int64_t)(th / a.num_heads);
+    // the source row and the slot are loaded together (one memory round trip)
     const uint4* src = reinterpret_cast<const uint4*>(a.src + tok * a.s_tok + head * a.s_head +
                                                       blk * 16);
+    const int64_t slot = slots[tok];
     const uint4 u0 = src[0];
     const uint4 u1 = src[1];
+    if (slot < 0 || slot >= a.num_slots) continue;
     const uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
     float amax = 0.f;
 #pragma unroll
@@ -114,8 +118,12 @@ hipError_t launch_quantize(const QuantArgs* k, const QuantArgs* v, int64_t n_tok
   int64_t nb = (per + 255) / 256;
   if (nb > 65535 * 8) nb = 65535 * 8;
   if (nb < 1) nb = 1;
-  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)nb, ny), dim3(256), 0, stream, first, second,
-                     n_tokens, slots);
+  if (per + (int64_t)nb * 256 < ((int64_t)1 << 31))
+    hipLaunchKernelGGL(quantize_kernel<int32_t>, dim3((unsigned)nb, ny), dim3(256), 0, stream,
+                       first, second, n_tokens, slots);
+  else
+    hipLaunchKernelGGL(quantize_kernel<int64_t>, dim3((unsigned)nb, ny), dim3(256), 0, stream,
+                       first, second, n_tokens, slots);
   return hipGetLastError();
 }
 
