@@ -17,7 +17,8 @@ import torch
 from ._lib import (EXPORTS, STATUS, WORK_FIELDS, KVPoolStruct, NVFP4Error, PlanInfoStruct,
                    check, lib)
 
-__all__ = ["KVPool", "Plan", "Prepared", "quantize_kv", "batch_decode", "batch_prefill",
+__all__ = ["KVPool", "Plan", "Prepared", "quantize_kv", "batch_decode", "batch_decode_append",
+           "batch_prefill",
            "merge_partials", "merge_states", "NVFP4Error", "lib", "version", "EXPORTS"]
 
 
@@ -228,6 +229,43 @@ def batch_decode(plan: Plan, q: torch.Tensor, page_table: torch.Tensor, k_pool: 
     ``Prepared`` call with ``prepare=True``."""
     return _attn(lib.nvfp4_batch_decode, plan, q, page_table, k_pool, v_pool, sm_scale,
                  workspace, out, lse, stream, prepare)
+
+
+def batch_decode_append(plan: Plan, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                        page_table: torch.Tensor, k_pool: KVPool, v_pool: KVPool, sm_scale: float,
+                        workspace: torch.Tensor, out: Optional[torch.Tensor] = None,
+                        lse: Optional[torch.Tensor] = None, stream=None, prepare: bool = False):
+    """Decode with the step's new token appended (nvfp4_batch_decode_append): k_new / v_new
+    bf16 [batch, Hkv, Dk / Dv] go to token kv_len-1 of each request, then attention as
+    ``batch_decode``."""
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if t.dtype != torch.bfloat16 or t.dim() != 3 or t.stride(-1) != 1:
+            raise ValueError(f"{name} must be bf16 [batch, num_kv_heads, head_dim], last dim contiguous")
+    rows = q.shape[0]
+    if q.dtype != torch.bfloat16 or q.dim() != 3 or q.stride(-1) != 1:
+        raise ValueError("q must be bf16 [rows, num_qo_heads, head_dim_qk], last dim contiguous")
+    if page_table.dtype != torch.int32 or page_table.dim() != 2 or page_table.stride(1) != 1:
+        raise ValueError("page_table must be int32 [batch, max_pages] with contiguous rows")
+    if out is None:
+        out = torch.empty((rows, plan.num_qo_heads, plan.head_dim_vo), dtype=torch.float32,
+                          device=q.device)
+    if lse is None:
+        lse = torch.empty((rows, plan.num_qo_heads), dtype=torch.float32, device=q.device)
+    if out.dtype != torch.float32 or out.stride(-1) != 1 or lse.dtype != torch.float32 \
+            or not lse.is_contiguous():
+        raise ValueError("out must be fp32 with a contiguous last dim; lse fp32 contiguous")
+    ks, vs = k_pool.struct(), v_pool.struct()
+    args = (plan.handle, _ptr(q), q.stride(0), q.stride(1), _ptr(k_new), k_new.stride(0),
+            k_new.stride(1), _ptr(v_new), v_new.stride(0), v_new.stride(1), _ptr(page_table),
+            page_table.stride(0), ctypes.byref(ks), ctypes.byref(vs), float(sm_scale),
+            _ptr(workspace), workspace.numel(), _ptr(out), out.stride(0), out.stride(1),
+            _ptr(lse), _stream(stream))
+    if prepare:
+        return Prepared(lib.nvfp4_batch_decode_append, args,
+                        (plan, q, k_new, v_new, page_table, k_pool, v_pool, ks, vs, workspace,
+                         out, lse))
+    check(lib.nvfp4_batch_decode_append(*args))
+    return out, lse
 
 
 def batch_prefill(plan: Plan, q: torch.Tensor, page_table: torch.Tensor, k_pool: KVPool,

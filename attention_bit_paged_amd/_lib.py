@@ -25,7 +25,8 @@ STATUS_CODE = {v: k for k, v in STATUS.items()}
 EXPORTS = (
     "nvfp4_last_error", "nvfp4_version", "nvfp4_quantize_kv", "nvfp4_plan_create",
     "nvfp4_plan_destroy", "nvfp4_plan_workspace_bytes", "nvfp4_plan_get_info",
-    "nvfp4_plan_get_work", "nvfp4_plan_upload", "nvfp4_batch_decode", "nvfp4_batch_prefill",
+    "nvfp4_plan_get_work", "nvfp4_plan_upload", "nvfp4_batch_decode",
+    "nvfp4_batch_decode_append", "nvfp4_set_timing_events", "nvfp4_batch_prefill",
     "nvfp4_plan_set_deferred_merge", "nvfp4_merge_partials", "nvfp4_merge_states",
 )
 
@@ -92,6 +93,10 @@ def _load():
         "nvfp4_plan_upload": (ctypes.c_int, [vp, vp, sz, vp]),
         "nvfp4_batch_decode": (ctypes.c_int, [vp, vp, i64, i64, vp, i64, pool_p, pool_p, f32, vp, sz,
                                               vp, i64, i64, vp, vp]),
+        "nvfp4_batch_decode_append": (ctypes.c_int, [vp, vp, i64, i64, vp, i64, i64, vp, i64, i64,
+                                                     vp, i64, pool_p, pool_p, f32, vp, sz,
+                                                     vp, i64, i64, vp, vp]),
+        "nvfp4_set_timing_events": (ctypes.c_int, [vp, vp]),
         "nvfp4_batch_prefill": (ctypes.c_int, [vp, vp, i64, i64, vp, i64, pool_p, pool_p, f32, vp, sz,
                                                vp, i64, i64, vp, vp]),
         "nvfp4_plan_set_deferred_merge": (ctypes.c_int, [vp, i32]),

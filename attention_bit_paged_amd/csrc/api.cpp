@@ -28,6 +28,11 @@
 
 using namespace nvfp4;
 
+nvfp4::LaunchEvents& nvfp4::launch_events() {
+  static thread_local LaunchEvents ev;
+  return ev;
+}
+
 namespace {
 
 thread_local std::string g_error;
@@ -543,6 +548,59 @@ nvfp4_status nvfp4_batch_decode(const nvfp4_plan* plan, const void* q, int64_t q
              sm_scale, workspace, workspace_bytes, o, o_stride_req, o_stride_head, lse, stream);
 }
 
+nvfp4_status nvfp4_batch_decode_append(const nvfp4_plan* plan, const void* q,
+                                       int64_t q_stride_req, int64_t q_stride_head,
+                                       const void* k_new, int64_t k_new_stride_req,
+                                       int64_t k_new_stride_head, const void* v_new,
+                                       int64_t v_new_stride_req, int64_t v_new_stride_head,
+                                       const int32_t* page_table, int64_t pt_stride,
+                                       const nvfp4_kv_pool* k_pool, const nvfp4_kv_pool* v_pool,
+                                       float sm_scale, void* workspace, size_t workspace_bytes,
+                                       float* o, int64_t o_stride_req, int64_t o_stride_head,
+                                       float* lse, void* stream) {
+  // the checks of the new rows come first (they need no device)
+  if (plan && !plan->prefill && plan->page_size < 16)
+    return fail(NVFP4_E_UNSUPPORTED,
+                "page_size %d: the in-place append needs pages of at least 16 tokens "
+                "(use nvfp4_quantize_kv, then nvfp4_batch_decode)", plan->page_size);
+  bool any_keys = false;
+  if (plan)
+    for (int b = 0; b < plan->batch; ++b) any_keys |= plan->kv_lens[b] > 0;
+  if (any_keys && (!k_new || !v_new)) return fail(NVFP4_E_INVALID, "k_new and v_new must be set");
+  if (!aligned(k_new, 16) || k_new_stride_req % 8 || k_new_stride_head % 8 ||
+      k_new_stride_req < 0 || k_new_stride_head < 0)
+    return fail(NVFP4_E_SHAPE, "k_new rows must be 16-byte aligned (strides multiples of 8)");
+  if (!aligned(v_new, 16) || v_new_stride_req % 8 || v_new_stride_head % 8 ||
+      v_new_stride_req < 0 || v_new_stride_head < 0)
+    return fail(NVFP4_E_SHAPE, "v_new rows must be 16-byte aligned (strides multiples of 8)");
+  if (nvfp4_status st = check_run(plan, false, q, q_stride_req, q_stride_head, page_table,
+                                  pt_stride, k_pool, v_pool, sm_scale, workspace,
+                                  workspace_bytes, o, o_stride_req, o_stride_head, lse))
+    return st;
+  if (plan->work.empty()) return ok();
+  AttnArgs a = make_args(plan, q, q_stride_req, q_stride_head, page_table, pt_stride, k_pool,
+                         v_pool, sm_scale, workspace, o, o_stride_req, o_stride_head, lse);
+  if (any_keys) {
+    a.k_new = static_cast<const uint16_t*>(k_new);
+    a.kn_s_req = k_new_stride_req;
+    a.kn_s_head = k_new_stride_head;
+    a.v_new = static_cast<const uint16_t*>(v_new);
+    a.vn_s_req = v_new_stride_req;
+    a.vn_s_head = v_new_stride_head;
+    a.k_gscale = (double)k_pool->global_scale;
+    a.v_gscale = (double)v_pool->global_scale;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_decode(plan->head_dim_qk, plan->head_dim_vo, a.page_shift, a, s);
+  if (e != hipSuccess) return fail(NVFP4_E_HIP, "decode launch failed: %s", hipGetErrorString(e));
+  const int n_merges = (int)(plan->merges.size() / kMergeFields);
+  if (n_merges > 0 && !plan->defer_merge) {
+    e = launch_merge_partials(a, n_merges, plan->head_dim_vo, 0, s);
+    if (e != hipSuccess) return fail(NVFP4_E_HIP, "merge launch failed: %s", hipGetErrorString(e));
+  }
+  return ok();
+}
+
 nvfp4_status nvfp4_batch_prefill(const nvfp4_plan* plan, const void* q, int64_t q_stride_tok,
                                  int64_t q_stride_head, const int32_t* page_table,
                                  int64_t pt_stride, const nvfp4_kv_pool* k_pool,
@@ -551,6 +609,13 @@ nvfp4_status nvfp4_batch_prefill(const nvfp4_plan* plan, const void* q, int64_t 
                                  int64_t o_stride_head, float* lse, void* stream) {
   return run(plan, true, q, q_stride_tok, q_stride_head, page_table, pt_stride, k_pool, v_pool,
              sm_scale, workspace, workspace_bytes, o, o_stride_tok, o_stride_head, lse, stream);
+}
+
+nvfp4_status nvfp4_set_timing_events(void* start_event, void* stop_event) {
+  LaunchEvents& ev = launch_events();
+  ev.start = static_cast<hipEvent_t>(start_event);
+  ev.stop = static_cast<hipEvent_t>(stop_event);
+  return ok();
 }
 
 nvfp4_status nvfp4_plan_set_deferred_merge(nvfp4_plan* plan, int32_t deferred) {

@@ -16,6 +16,7 @@
 // row group is split over several workgroups, each writes a partial state and a merge
 // kernel on the same stream combines them by LSE (a fence-and-counter merge inside this
 // kernel was measured slower: each agent-scope release writes back the L2).
+#include "fp4_quant.h"
 #include "kv_ring.h"
 
 namespace nvfp4 {
@@ -124,8 +125,88 @@ __device__ __forceinline__ DecodeItem decode_item(const AttnArgs& a, int wave, i
   return it;
 }
 
-// page_size >= 16: the chunk streams through a per-wave LDS ring several steps deep.
+// The step's new token, appended by the wave whose keys end at the request's last key.
+// The concatenated K and V rows are quantised four elements per lane: quarter q goes to
+// lane q % 64, slot q / 64, and the four lanes of a 16-element block share its largest
+// magnitude through two lane exchanges (the arithmetic is the append kernel's).  The
+// codes are written to the pools at once and stay in registers until the wave's last
+// step, where they replace the token's bytes in the ring: the ring never depends on
+// the pool write being visible to the copies.
 template <int DK, int DV>
+struct NewToken {
+  static constexpr int QK = DK / 4;          // quarters of the K row
+  static constexpr int QT = (DK + DV) / 4;   // quarters of both rows
+  static constexpr int RQ = (QT + 63) / 64;  // per lane
+  uint32_t codes[RQ];                        // 16 bits: four e2m1 codes
+  uint32_t sc[RQ];                           // the block's e4m3 scale code
+
+  __device__ __forceinline__ void quantise(const AttnArgs& a, int b, int kvh, int lane) {
+    const uint16_t* krow = a.k_new + (int64_t)b * a.kn_s_req + (int64_t)kvh * a.kn_s_head;
+    const uint16_t* vrow = a.v_new + (int64_t)b * a.vn_s_req + (int64_t)kvh * a.vn_s_head;
+#pragma unroll
+    for (int r = 0; r < RQ; ++r) {
+      const int q = lane + 64 * r;
+      uint2 u = make_uint2(0u, 0u);
+      if (q < QT) u = *reinterpret_cast<const uint2*>(q < QK ? krow + 4 * q : vrow + 4 * (q - QK));
+      float amax = quant::amax4(u.x, u.y);
+      amax = fmaxf(amax, __shfl_xor(amax, 1));
+      amax = fmaxf(amax, __shfl_xor(amax, 2));
+      const double gs = q < QK ? a.k_gscale : a.v_gscale;
+      sc[r] = quant::scale_code(amax, gs);
+      codes[r] = quant::codes4(u.x, u.y, sc[r], gs);
+    }
+  }
+
+  // Writes the token (step token tt) into the ring stage at byte address `stage`.
+  template <int WL>
+  __device__ __forceinline__ void inject(uint32_t stage, int tt, int lane) const {
+    using R = RingShape<DK, DV, WL>;
+    typedef __attribute__((address_space(3))) uint16_t* lds_u16;
+    typedef __attribute__((address_space(3))) uint8_t* lds_u8;
+#pragma unroll
+    for (int r = 0; r < RQ; ++r) {
+      const int q = lane + 64 * r;
+      if (q >= QT) continue;
+      const bool isk = q < QK;
+      const int e = isk ? q : q - QK;  // quarter within its row
+      const uint32_t row = isk ? R::OFF_KD + tt * (DK / 2) : R::OFF_VD + tt * (DV / 2);
+      const uint32_t sf = isk ? R::OFF_SF + tt * (DK / 16) : R::OFF_SF + R::KS + tt * (DV / 16);
+      *(lds_u16)(size_t)(stage + row + 2 * e) = (uint16_t)codes[r];
+      if ((e & 3) == 0) *(lds_u8)(size_t)(stage + sf + (e >> 2)) = (uint8_t)sc[r];
+    }
+  }
+
+  // Writes the token (key `tok` of the request) to the pools; an out-of-range page
+  // writes nothing (the request's outputs are NaN then).
+  __device__ __forceinline__ void store(const PagedView<DK, DV, true>& v, int tok, int lane) const {
+    const int pg = v.pt_row[tok >> v.page_shift];
+    if ((unsigned)pg >= (unsigned)v.num_pages) return;
+    const int64_t sl = tok & v.page_mask;
+    uint8_t* kd = const_cast<uint8_t*>(v.kdat) + pg * v.k_page + sl * v.k_tok;
+    uint8_t* ks = const_cast<uint8_t*>(v.ksf) + pg * v.ksf_page + sl * v.ksf_tok;
+    uint8_t* vd = const_cast<uint8_t*>(v.vdat) + pg * v.v_page + sl * v.v_tok;
+    uint8_t* vs = const_cast<uint8_t*>(v.vsf) + pg * v.vsf_page + sl * v.vsf_tok;
+#pragma unroll
+    for (int r = 0; r < RQ; ++r) {
+      const int q = lane + 64 * r;
+      // separate guarded blocks for K and V (an if/else pair gets merged into one store
+      // through a stack table of pointers)
+      if (q < QK) {
+        *reinterpret_cast<uint16_t*>(kd + 2 * q) = (uint16_t)codes[r];
+        if ((q & 3) == 0) ks[q >> 2] = (uint8_t)sc[r];
+      }
+      const int e = q - QK;
+      if (e >= 0 && q < QT) {
+        *reinterpret_cast<uint16_t*>(vd + 2 * e) = (uint16_t)codes[r];
+        if ((e & 3) == 0) vs[e >> 2] = (uint8_t)sc[r];
+      }
+    }
+  }
+};
+
+// page_size >= 16: the chunk streams through a per-wave LDS ring several steps deep.
+// APPEND: the launch also appends the step's new token (AttnArgs::k_new).
+template <int DK, int DV, bool APPEND>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DecodeOcc<DK, DV>::WGS)))
 void decode_ring_kernel(AttnArgs a) {
   using S = StepShape<DK, DV>;
@@ -140,11 +221,6 @@ void decode_ring_kernel(AttnArgs a) {
   const int n = lane & 15;
   const DecodeItem it = decode_item(a, wave, n);
 
-  f16x8 qf[S::NS];
-  const float score_c = a.score_scale *
-      load_q_operand<DK>(a.q + (int64_t)it.b * a.q_s_row + (int64_t)it.head * a.q_s_head,
-                         it.head_valid, j, qf);
-
   PagedView<DK, DV, true> view;
   view.init(a, it.b, it.kvh, lane);
   RingPlan<DK, DV, WL> rp;
@@ -154,17 +230,34 @@ void decode_ring_kernel(AttnArgs a) {
   const int tlast = it.w1 - 1;
   uint32_t bad = 0;
 
-  RowState<S::NT, AccForm::VGPR> st;
-  st.init();
   RingLanes lanes = ring_lanes<DK, DV, WL>(ring_lds, j, n);
   const int len = it.w1 - it.w0;
   const int nsteps = (len + kDecodeStep - 1) / kDecodeStep;
-  const int nfull = len / kDecodeStep;  // steps whose 32 keys are all in range
+  // the wave holding the request's last key appends the step's new token; its last
+  // step is then always taken by the peeled (masked) code
+  const bool appender = APPEND && len > 0 && it.w1 == a.kv_lens[it.b];
+  const int nfull = appender ? nsteps - 1 : len / kDecodeStep;  // steps of the unrolled loop
 #pragma unroll
   for (int s = 0; s < R::NST - 1; ++s)
     if (s < nsteps)
       ring_issue<DK, DV, WL>(rp, ring_lds + s * R::STAGE, view, it.w0 + s * kDecodeStep, tlast,
                              bad);
+  // Q (and the new token's rows) after the first copies, so that their loads overlap
+  f16x8 qf[S::NS];
+  const float score_c = a.score_scale *
+      load_q_operand<DK>(a.q + (int64_t)it.b * a.q_s_row + (int64_t)it.head * a.q_s_head,
+                         it.head_valid, j, qf);
+  NewToken<DK, DV> nt;
+  if (appender) {
+    nt.quantise(a, it.b, it.kvh, lane);
+    // Written to the pools now, overlapping the stream.  The stores join the wave's
+    // vmcnt queue ahead of later copies, which only makes the ring's waits stronger;
+    // the ring itself takes the token's bytes from registers (below).
+    nt.store(view, tlast, lane);
+  }
+
+  RowState<S::NT, AccForm::VGPR> st;
+  st.init();
   // Full steps, unrolled by the ring depth so that every stage offset is a constant.
   // Step i issues step i + NST - 1 (when it exists) into the stage step i - 1 used,
   // then waits until at most NST - 1 steps are newer than its own.
@@ -184,11 +277,18 @@ void decode_ring_kernel(AttnArgs a) {
       decode_step<DK, DV, false>(raw, it.w0 + i * kDecodeStep, tlast, j, qf, score_c, st);
     }
   }
-  if (nfull < nsteps) {  // the last step is partial; it was issued already
+  if (nfull < nsteps) {  // the last step: partial, or the appender's; it was issued already
     ring_wait<0>(lanes);
+    const uint32_t stage_off = (uint32_t)(nfull % R::NST) * R::STAGE;
+    const int t0 = it.w0 + nfull * kDecodeStep;
+    if (appender) {
+      uint32_t stage = ring_lds + stage_off;
+      asm volatile("" : "+v"(stage));  // after the wait: the copies have landed
+      nt.template inject<WL>(stage, tlast - t0, lane);
+    }
     StepRaw<DK, DV> raw;
-    ring_read<DK, DV>(lanes, (uint32_t)(nfull % R::NST) * R::STAGE, raw);
-    decode_step<DK, DV, true>(raw, it.w0 + nfull * kDecodeStep, tlast, j, qf, score_c, st);
+    ring_read<DK, DV>(lanes, stage_off, raw);
+    decode_step<DK, DV, true>(raw, t0, tlast, j, qf, score_c, st);
   }
   const bool bad_w = __any(bad != 0);
   __syncthreads();  // every wave is done with its ring: the exchange reuses that memory
@@ -243,10 +343,14 @@ __global__ __launch_bounds__(256) void decode_regs_kernel(AttnArgs a) {
 template <int DK, int DV>
 hipError_t launch_dk_dv(int page_shift, const AttnArgs& a, hipStream_t stream) {
   const dim3 grid(a.n_work);
-  if (page_shift >= 4)
-    hipLaunchKernelGGL((decode_ring_kernel<DK, DV>), grid, dim3(256), 0, stream, a);
+  if (page_shift >= 4 && a.k_new)
+    launch_attention(decode_ring_kernel<DK, DV, true>, grid, dim3(256), stream, a);
+  else if (page_shift >= 4)
+    launch_attention(decode_ring_kernel<DK, DV, false>, grid, dim3(256), stream, a);
+  else if (!a.k_new)
+    launch_attention(decode_regs_kernel<DK, DV>, grid, dim3(256), stream, a);
   else
-    hipLaunchKernelGGL((decode_regs_kernel<DK, DV>), grid, dim3(256), 0, stream, a);
+    return hipErrorInvalidValue;  // the append needs the ring kernel (page_size >= 16)
   return hipGetLastError();
 }
 

@@ -1,6 +1,7 @@
 // Internal declarations shared by the host library and the HIP kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -61,6 +62,14 @@ struct AttnArgs {
   int32_t causal;
   int32_t wave_chunk;       // decode: keys per wave (0: split the item evenly over 4 waves)
   const int32_t* merges;    // merge records
+  // Decode with append: the step's new K/V rows (bf16 [batch, kv heads, dim], element
+  // strides), quantised into the slot of token kv_len-1 of their request by the work
+  // item that ends there; k_new is null when the call appends nothing.
+  const uint16_t* k_new;
+  int64_t kn_s_req, kn_s_head;
+  const uint16_t* v_new;
+  int64_t vn_s_req, vn_s_head;
+  double k_gscale, v_gscale;  // the pools' global scales (the quantiser's divisor)
 };
 
 struct QuantArgs {
@@ -76,6 +85,25 @@ struct QuantArgs {
   int32_t head_dim;
   double gscale;
 };
+
+// Timing events of the attention launches (nvfp4_set_timing_events): while set, the
+// decode and prefill kernels are launched with them, so that the dispatch itself
+// timestamps the kernel's start and end.  Per host thread.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchEvents& launch_events();
+
+// Launches an attention kernel, with the thread's timing events when they are set.
+template <typename K>
+inline void launch_attention(K kernel, dim3 grid, dim3 block, hipStream_t stream,
+                             const AttnArgs& a) {
+  const LaunchEvents& ev = launch_events();
+  if (ev.start || ev.stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, ev.start, ev.stop, 0u, a);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, a);
+}
 
 // Launchers (defined in the .hip files).  Return the hipGetLastError() status of the launch.
 hipError_t launch_quantize(const QuantArgs* k, const QuantArgs* v, int64_t n_tokens,

@@ -473,15 +473,15 @@ hipError_t launch_dk_dv(int page_shift, const AttnArgs& a, hipStream_t stream) {
   const dim3 grid(a.n_work);
   if constexpr (CoopShape<DK, DV>::OK) {
     if (page_shift >= 4) {
-      hipLaunchKernelGGL((prefill_coop_kernel<DK, DV>), grid, dim3(CoopShape<DK, DV>::NW * 64), 0,
-                         stream, a);
+      launch_attention(prefill_coop_kernel<DK, DV>, grid, dim3(CoopShape<DK, DV>::NW * 64), stream,
+                       a);
       return hipGetLastError();
     }
   }
   if (page_shift >= 4)
-    hipLaunchKernelGGL((prefill_regs_kernel<DK, DV, true>), grid, dim3(256), 0, stream, a);
+    launch_attention(prefill_regs_kernel<DK, DV, true>, grid, dim3(256), stream, a);
   else
-    hipLaunchKernelGGL((prefill_regs_kernel<DK, DV, false>), grid, dim3(256), 0, stream, a);
+    launch_attention(prefill_regs_kernel<DK, DV, false>, grid, dim3(256), stream, a);
   return hipGetLastError();
 }
 

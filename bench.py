@@ -4,17 +4,20 @@
 Default workload: batch decode (64 requests, kv_len ~ U[512, 8192], 32 qo / 8 kv heads,
 head dim 128, page size 16, 40k-page pool in a seeded random permutation, split-KV
 with 256-token chunks).  One step = append the step's new K/V token of every request
-(NVFP4 quantise into its slot) + the attention pass over the paged cache + the LSE
-merge of the split rows.  The plan is built once (the lengths do not change between
-steps) and its host time is reported separately.  Inputs are resident in HBM before
+(NVFP4 quantise into the slot of its last key) + the attention pass over the paged
+cache, both in one launch (nvfp4_batch_decode_append), + the LSE merge of the split
+rows.  The same step with the append as its own launch is timed for the breakdown.
+The plan is built once (the lengths do not change between steps) and its host time
+is reported separately.  Inputs are resident in HBM before
 timing starts; three independent pool sets are rotated so that the 256 MB Infinity
 Cache cannot serve a step from the previous one.
 
 Prints one JSON line.  ``value`` is the decode's KV GB/s: packed e2m1 bytes plus e4m3
 scale bytes of every visible K and V row, divided by the step time.  ``roofline`` is
-the attention kernel's own figure: its algorithmic bytes (KV + Q + O + LSE) over its
-average duration, timed with HIP events around each launch inside the timed steps
-(events created without the system-scope fence, which would add to every launch).
+the attention kernel's own figure: its algorithmic bytes (KV + Q + O + LSE + the new
+token's rows) over its average duration, timed inside the timed steps with HIP events
+that the kernel's dispatch itself timestamps (nvfp4_set_timing_events), so that no
+event packet is added to the queue.
 
 With --workload naming a prefill workload, the timed step is that prefill's attention
 pass and merge instead (TFLOP/s; used to profile the prefill kernel).
@@ -44,7 +47,8 @@ HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
 PROFILES = os.path.join(ROOT, "profiles")
 # sources whose change invalidates recorded counters of the decode kernel
-DECODE_SOURCES = ("decode.hip", "kv_ring.h", "attn_step.h", "fp4_common.h", "internal.h")
+DECODE_SOURCES = ("decode.hip", "kv_ring.h", "attn_step.h", "fp4_common.h", "fp4_quant.h",
+                  "internal.h")
 CALIB_BYTES = 1 << 30
 
 
@@ -118,6 +122,12 @@ class HipEvents:
         if self.hip.hipEventRecord(e, self.ct.c_void_p(stream.cuda_stream)) != 0:
             raise RuntimeError("hipEventRecord failed")
 
+    @staticmethod
+    def time_launches(nv, start, stop):
+        """Attention launches from now on carry (start, stop), timestamped by the dispatch
+        itself (nvfp4_set_timing_events); None, None stops."""
+        nv.check(nv.lib.nvfp4_set_timing_events(start, stop))
+
     def ms(self, a, b):
         out = self.ct.c_float()
         if self.hip.hipEventElapsedTime(self.ct.byref(out), a, b) != 0:
@@ -129,10 +139,16 @@ class HipEvents:
             self.hip.hipEventDestroy(e)
 
 
-def decode_bytes(w):
+def decode_bytes(w, append=False):
+    """(KV bytes, other bytes) of one decode launch: Q read, O and LSE written, and with
+    ``append`` the new token's bf16 rows read and their NVFP4 bytes written."""
     q = w.batch * w.num_qo_heads * w.head_dim_qk * 2
     o = w.batch * w.num_qo_heads * (w.head_dim_vo * 4 + 4)
-    return w.kv_bytes(), q + o
+    new = 0
+    if append:
+        dk, dv = w.head_dim_qk, w.head_dim_vo
+        new = w.batch * w.num_kv_heads * (2 * (dk + dv) + dk // 2 + dk // 16 + dv // 2 + dv // 16)
+    return w.kv_bytes(), q + o + new
 
 
 def cpu_baseline(case, budget_s):
@@ -164,19 +180,21 @@ def cpu_baseline(case, budget_s):
 
 
 def timed_passes(torch, nv, run, merge, iters):
-    """Per-launch HIP-event durations (ms) of the attention pass and the merge."""
+    """Per-launch durations (ms) of the attention kernel (events carried by its dispatch)
+    and of the merge (events recorded around it)."""
     s = torch.cuda.current_stream()
     he = HipEvents()
-    ev = [[he.new() for _ in range(3)] for _ in range(iters)]
+    ev = [[he.new() for _ in range(4)] for _ in range(iters)]
     for e in ev:
-        he.record(e[0], s)
+        he.time_launches(nv, e[0], e[1])
         run()
-        he.record(e[1], s)
-        merge()
+        he.time_launches(nv, None, None)
         he.record(e[2], s)
+        merge()
+        he.record(e[3], s)
     torch.cuda.synchronize()
-    return (float(np.mean([he.ms(a, b) for a, b, _ in ev])),
-            float(np.mean([he.ms(b, c) for _, b, c in ev])))
+    return (float(np.mean([he.ms(e[0], e[1]) for e in ev])),
+            float(np.mean([he.ms(e[2], e[3]) for e in ev])))
 
 
 def extra_decode(torch, nv, paged, synth, name, iters=20):
@@ -261,30 +279,63 @@ class Decoder:
         self.new_slots = self.sets[0].slots[torch.tensor(last, device="cuda")]
         self.o = torch.empty((w.batch, w.num_qo_heads, w.head_dim_vo), device="cuda")
         self.lse = torch.empty((w.batch, w.num_qo_heads), device="cuda")
-        # the three calls of a step, marshalled once per pool set
-        self.calls = [(nv.quantize_kv(self.new_k, self.new_v, self.new_slots, c.k_pool, c.v_pool,
-                                      prepare=True),
-                       nv.batch_decode(self.plan, c.q, c.page_table, c.k_pool, c.v_pool,
-                                       w.sm_scale, self.ws, out=self.o, lse=self.lse,
-                                       prepare=True),
+        # the two calls of a step (append + attention in one launch, then the merge of the
+        # split rows), marshalled once per pool set
+        self.calls = [(nv.batch_decode_append(self.plan, c.q, self.new_k, self.new_v,
+                                              c.page_table, c.k_pool, c.v_pool, w.sm_scale,
+                                              self.ws, out=self.o, lse=self.lse, prepare=True),
                        nv.merge_partials(self.plan, self.ws, self.o, self.lse, prepare=True))
                       for c in self.sets]
+        # the same step with a separate append launch (for the breakdown line)
+        self.unfused = [(nv.quantize_kv(self.new_k, self.new_v, self.new_slots, c.k_pool,
+                                        c.v_pool, prepare=True),
+                         nv.batch_decode(self.plan, c.q, c.page_table, c.k_pool, c.v_pool,
+                                         w.sm_scale, self.ws, out=self.o, lse=self.lse,
+                                         prepare=True),
+                         nv.merge_partials(self.plan, self.ws, self.o, self.lse, prepare=True))
+                        for c in self.sets]
 
     def step(self, i, ev=None, he=None):
-        quant, attn, merge = self.calls[i % len(self.calls)]
+        """One step; with ``ev`` (two events) the attention launch carries them: the
+        dispatch timestamps the kernel's start and end, adding no packet to the queue."""
+        attn, merge = self.calls[i % len(self.calls)]
         if ev is None:
-            quant()
             attn()
             merge()
             return
-        s = self.torch.cuda.current_stream()
-        he.record(ev[0], s)
-        quant()
-        he.record(ev[1], s)
+        he.time_launches(self.nv, ev[0], ev[1])
         attn()
-        he.record(ev[2], s)
+        he.time_launches(self.nv, None, None)
         merge()
-        he.record(ev[3], s)
+
+    def merge_ms(self, iters):
+        """Mean duration of the merge launch (outside the timed steps)."""
+        s = self.torch.cuda.current_stream()
+        he = HipEvents()
+        ev = [(he.new(), he.new()) for _ in range(iters)]
+        for i, (a, b) in enumerate(ev):
+            attn, merge = self.calls[i % len(self.calls)]
+            attn()
+            he.record(a, s)
+            merge()
+            he.record(b, s)
+        self.torch.cuda.synchronize()
+        return float(np.mean([he.ms(a, b) for a, b in ev]))
+
+    def unfused_step_ms(self, iters):
+        """Mean GPU time of the step with the append as its own launch."""
+        s = self.torch.cuda.current_stream()
+        he = HipEvents()
+        ev = [(he.new(), he.new()) for _ in range(iters)]
+        for i, (a, b) in enumerate(ev):
+            quant, attn, merge = self.unfused[i % len(self.unfused)]
+            he.record(a, s)
+            quant()
+            attn()
+            merge()
+            he.record(b, s)
+        self.torch.cuda.synchronize()
+        return float(np.mean([he.ms(a, b) for a, b in ev]))
 
 
 def pmc_run(args):
@@ -350,7 +401,7 @@ def summarize_pmc(args):
         return out
 
     fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
-    dec = [k for k in fetch if "decode_ring_kernel" in k]
+    dec = [k for k in fetch if "decode_ring_kernel" in k and "true" in k]
     cpy = [k for k in fetch if "copyBuffer" in k]
     if not dec or not cpy:
         raise SystemExit(f"kernels not found: {list(fetch)}")
@@ -449,18 +500,19 @@ def main():
         d.step(i)
     torch.cuda.synchronize()
     he = HipEvents()
-    ev = [[he.new() for _ in range(4)] for _ in range(args.steps)]
+    ev = [[he.new() for _ in range(2)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
         d.step(i, ev[i], he)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     ms_step = dt * 1e3 / args.steps
-    quant_ms = float(np.mean([he.ms(e[0], e[1]) for e in ev]))
-    attn_ms = float(np.mean([he.ms(e[1], e[2]) for e in ev]))
-    merge_ms = float(np.mean([he.ms(e[2], e[3]) for e in ev]))
+    attn_ms = float(np.mean([he.ms(e[0], e[1]) for e in ev]))
+    # breakdown, after the timed steps
+    merge_ms = d.merge_ms(max(args.steps // 2, 3))
+    unfused_ms = d.unfused_step_ms(max(args.steps // 2, 3))
 
-    kv, qo = decode_bytes(w)
+    kv, qo = decode_bytes(w, append=True)
     value = kv / (ms_step * 1e-3) / 1e9
     achieved = (kv + qo) / (attn_ms * 1e-3) / 1e9
     out = {
@@ -487,10 +539,11 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic(w.name),
-                     "kernel": f"decode_ring_kernel<{w.head_dim_qk}, {w.head_dim_vo}>",
+                     "kernel": f"decode_ring_kernel<{w.head_dim_qk}, {w.head_dim_vo}, true>",
                      "bytes_per_launch": kv + qo, "avg_launch_ms": round(attn_ms, 5)},
-        "step_breakdown_ms": {"quantize_append": round(quant_ms, 5), "attention": round(attn_ms, 5),
-                              "merge": round(merge_ms, 5)},
+        "step_breakdown_ms": {"append_and_attention": round(attn_ms, 5),
+                              "merge": round(merge_ms, 5),
+                              "unfused_step_gpu": round(unfused_ms, 5)},
         "plan_host_us": round(d.plan_us, 1),
     }
     if not args.no_extra:

@@ -199,6 +199,42 @@ nvfp4_status nvfp4_batch_decode(const nvfp4_plan* plan, const void* q, int64_t q
                                 void* stream);
 
 /*
+ * Decode with the step's new token appended in the same launch.  For every request b
+ * with kv_len_b >= 1, the rows k_new[b] and v_new[b] (device bf16 [batch,
+ * num_kv_heads, head_dim_qk / head_dim_vo], element strides, last dim contiguous,
+ * 16-byte aligned rows) are quantised exactly as nvfp4_quantize_kv does and written
+ * to the slot of token kv_len_b - 1 (its page from the page table), and this call's
+ * attention uses them as that key.  The result equals nvfp4_quantize_kv into those
+ * slots followed by nvfp4_batch_decode, with one launch less: serving loops append
+ * one token per request and attend to it at once ([PF] commit "Gate split-KV off..."
+ * and its follow-up describe decode over the growing cache; [XQA] changelog: the
+ * tests quantise the cache with to_nvfp4 before decoding).  Requests with kv_len 0
+ * append nothing.  Requires page_size >= 16 (NVFP4_E_UNSUPPORTED otherwise).  Other
+ * arguments, outputs and errors as for nvfp4_batch_decode.
+ */
+nvfp4_status nvfp4_batch_decode_append(const nvfp4_plan* plan, const void* q,
+                                       int64_t q_stride_req, int64_t q_stride_head,
+                                       const void* k_new, int64_t k_new_stride_req,
+                                       int64_t k_new_stride_head, const void* v_new,
+                                       int64_t v_new_stride_req, int64_t v_new_stride_head,
+                                       const int32_t* page_table, int64_t pt_stride,
+                                       const nvfp4_kv_pool* k_pool, const nvfp4_kv_pool* v_pool,
+                                       float sm_scale, void* workspace, size_t workspace_bytes,
+                                       float* o, int64_t o_stride_req, int64_t o_stride_head,
+                                       float* lse, void* stream);
+
+/*
+ * Kernel timing for benchmarks and profilers.  While set, every decode and prefill
+ * attention launch made by the calling host thread is dispatched with these HIP
+ * events (hipEvent_t, cast to void*), which the dispatch itself timestamps when the
+ * kernel starts and when it ends (hipExtLaunchKernel), so that their elapsed time is
+ * the kernel's own duration without extra queue packets.  The merge and append
+ * kernels are not timed.  NULL, NULL stops.  The events belong to the caller and must
+ * stay valid while set.  Never fails.
+ */
+nvfp4_status nvfp4_set_timing_events(void* start_event, void* stop_event);
+
+/*
  * Prefill / extend over the paged cache ([PF] commits on asymmetric heads and
  * "Gate split-KV off...": prefix-cache extend, qo_len << kv_len; causal runs).
  *   q: device bf16 [total_q, num_qo_heads, head_dim_qk] ragged by the plan's

@@ -287,3 +287,134 @@ def test_prepared_calls_match_direct_calls():
     nv.quantize_kv(src, None, slots, b, None, prepare=True)()
     torch.cuda.synchronize()
     assert torch.equal(a.data, b.data) and torch.equal(a.sf, b.sf)
+
+
+# ------------------------------------------------------------ decode + append ----
+
+def _clone_view(t):
+    base = t._base if t._base is not None else t
+    nb = base.clone()
+    return nb.as_strided(t.size(), t.stride(), t.storage_offset())
+
+
+def _clone_pool(p):
+    return nv.KVPool(_clone_view(p.data), _clone_view(p.sf), head_dim=p.head_dim,
+                     layout=p.layout, global_scale=p.global_scale)
+
+
+def _slot_rows(pool, page, off):
+    """(data, sf) rows of one slot for every kv head."""
+    if pool.layout == "HND":
+        return pool.data[page, :, off], pool.sf[page, :, off]
+    return pool.data[page, off], pool.sf[page, off]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("lens,hq,hkv,dk,dv,page,chunk,layout,gs,defer", [
+    ([1, 32, 33, 100, 517], 8, 2, 128, 128, 16, None, "HND", (1.0, 1.0), False),
+    ([1, 32, 33, 100, 517], 8, 2, 128, 128, 16, 32, "HND", (1.0, 1.0), False),
+    ([0, 64, 65, 300], 4, 1, 128, 128, 16, 64, "NHD", (0.75, 1.25), True),
+    ([200, 31], 32, 1, 128, 128, 16, None, "HND", (1.0, 1.0), False),
+    ([97, 1000], 8, 2, 64, 64, 32, 64, "HND", (1.0, 1.0), False),
+    ([129, 700], 8, 1, 512, 256, 16, 128, "HND", (1.0, 1.0), False),
+    ([40, 1025], 8, 2, 256, 128, 64, None, "NHD", (1.0, 1.0), False),
+])
+def test_decode_append_matches_quantize_then_decode(lens, hq, hkv, dk, dv, page, chunk, layout,
+                                                    gs, defer):
+    """The fused append writes the oracle quantiser's bytes to the slot of every request's
+    last key, and its outputs equal, bit for bit, quantize_kv into those slots followed by
+    batch_decode; both match the oracle."""
+    w = synth.custom("append", kv_lens=lens, num_qo_heads=hq, num_kv_heads=hkv, head_dim_qk=dk,
+                     head_dim_vo=dv, page_size=page, seed=41)
+    c = gh.build_oracle_case(w, layout=layout, k_global=gs[0], v_global=gs[1])
+    _, k, v = synth.draw_qkv(w, device="cpu")
+    last = np.cumsum(w.kv_lens) - 1
+    have = np.array(w.kv_lens) > 0
+    slots = synth.token_slots(w, c.pt)
+    # the new rows of every request ([batch, Hkv, D]; zero rows where nothing is appended)
+    k_new = torch.zeros((w.batch, hkv, dk), dtype=torch.bfloat16)
+    v_new = torch.zeros((w.batch, hkv, dv), dtype=torch.bfloat16)
+    k_new[have] = k[last[have]]
+    v_new[have] = v[last[have]]
+    k_new, v_new = k_new.cuda(), v_new.cuda()
+    # poison the slots the appends will write
+    rng = np.random.default_rng(5)
+    for b in np.nonzero(have)[0]:
+        s = int(slots[last[b]])
+        for pool in (c.k_pool, c.v_pool):
+            d, f = _slot_rows(pool, s // page, s % page)
+            d.copy_(torch.from_numpy(rng.integers(0, 256, tuple(d.shape), dtype=np.uint8)))
+            f.fill_(synth.SF_POISON)
+    plan = gh.make_plan(w, chunk)
+    plan.set_deferred_merge(defer)
+    outs = []
+    pools = []
+    for fused in (False, True):
+        kp, vp = _clone_pool(c.k_pool), _clone_pool(c.v_pool)
+        ws = plan.new_workspace()
+        plan.upload(ws)
+        o = torch.full((w.batch, hq, dv), float("nan"), device="cuda")
+        lse = torch.full((w.batch, hq), float("nan"), device="cuda")
+        if fused:
+            nv.batch_decode_append(plan, c.q, k_new, v_new, c.page_table, kp, vp, w.sm_scale, ws,
+                                   out=o, lse=lse)
+        else:
+            sl = torch.from_numpy(np.where(have, slots[np.maximum(last, 0)], -1)).cuda()
+            nv.quantize_kv(k_new, v_new, sl, kp, vp)
+            nv.batch_decode(plan, c.q, c.page_table, kp, vp, w.sm_scale, ws, out=o, lse=lse)
+        if defer:
+            nv.merge_partials(plan, ws, o, lse)
+        torch.cuda.synchronize()
+        outs.append((o.cpu().numpy(), lse.cpu().numpy()))
+        pools.append((kp, vp))
+    (oa, la), (ob, lb) = outs
+    assert np.array_equal(oa, ob, equal_nan=True) and np.array_equal(la, lb, equal_nan=True)
+    for pa, pb, ref_pool in ((pools[0][0], pools[1][0], "k"), (pools[0][1], pools[1][1], "v")):
+        assert torch.equal(pa.data, pb.data) and torch.equal(pa.sf, pb.sf), ref_pool
+    # the appended slots hold the oracle quantiser's bytes (the case was built from them)
+    kd, ksf = c.k_np
+    vd, vsf = c.v_np
+    for b in np.nonzero(have)[0]:
+        s = int(slots[last[b]])
+        for pool, (dref, sref) in ((pools[1][0], (kd, ksf)), (pools[1][1], (vd, vsf))):
+            d, f = _slot_rows(pool, s // page, s % page)
+            if layout == "HND":
+                dr, fr = dref[s // page, :, s % page], sref[s // page, :, s % page]
+            else:
+                dr, fr = dref[s // page, s % page], sref[s // page, s % page]
+            assert np.array_equal(d.cpu().numpy(), dr) and np.array_equal(f.cpu().numpy(), fr)
+    o_ref, lse_ref = gh.oracle_reference(c)
+    gh.assert_attention_close(ob.astype(np.float64), lb.astype(np.float64), o_ref, lse_ref,
+                              "decode_append")
+
+
+@pytest.mark.gpu
+def test_timing_events_bracket_the_kernel():
+    """Launches made while timing events are set carry them; the elapsed time is positive
+    and within the host's wall time of the call; the outputs are unchanged."""
+    import ctypes
+    import time
+    hip = ctypes.CDLL("libamdhip64.so")
+    ev = [ctypes.c_void_p(), ctypes.c_void_p()]
+    for e in ev:
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+    try:
+        w = synth.custom("timing", kv_lens=[700, 64, 3000], num_qo_heads=8, num_kv_heads=2, seed=16)
+        c = gh.build_oracle_case(w)
+        plan = gh.make_plan(w)
+        o0, l0 = gh.run_gpu(c, plan)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        nv.check(nv.lib.nvfp4_set_timing_events(ev[0], ev[1]))
+        try:
+            o1, l1 = gh.run_gpu(c, plan)
+        finally:
+            nv.check(nv.lib.nvfp4_set_timing_events(None, None))
+        wall_ms = (time.perf_counter() - t0) * 1e3
+        ms = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(ms), ev[0], ev[1]) == 0
+        assert 0.0 < ms.value <= wall_ms
+        assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+    finally:
+        for e in ev:
+            hip.hipEventDestroy(e)

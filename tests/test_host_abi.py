@@ -153,3 +153,32 @@ def test_deferred_merge_entry_points():
     whole = nv.Plan([3000], num_qo_heads=4, num_kv_heads=1, head_dim_qk=128, kv_chunk_tokens=-1,
                     num_cus=256)
     assert _lib.STATUS[f(whole.handle, 0, 0, 0, 0, 0, 0, None)] == "NVFP4_OK"
+
+
+def test_decode_append_rejections_never_launch():
+    f = nv.lib.nvfp4_batch_decode_append
+
+    def call(plan, k_new=0x50000, v_new=0x60000, kn_s=(256, 128), **over):
+        args = dict(q=0x10000, pt=0x20000, pt_stride=8, k=_fake_pool(), v=_fake_pool(), ws=0x40000)
+        args.update(over)
+        st = f(plan.handle, args["q"], 512, 128, k_new, kn_s[0], kn_s[1], v_new, 256, 128,
+               args["pt"], args["pt_stride"], ctypes.byref(args["k"]), ctypes.byref(args["v"]),
+               0.1, args["ws"], plan.workspace_bytes, 0x80000, 512, 128, 0x90000, None)
+        return _lib.STATUS[st], nv.lib.nvfp4_last_error().decode()
+
+    plan = nv.Plan([100], num_qo_heads=4, num_kv_heads=1, head_dim_qk=128, num_cus=256)
+    assert call(plan, k_new=0)[0] == "NVFP4_E_INVALID"
+    st, msg = call(plan, v_new=0x60002)
+    assert st == "NVFP4_E_SHAPE" and "v_new" in msg
+    st, msg = call(plan, kn_s=(250, 128))
+    assert st == "NVFP4_E_SHAPE" and "k_new" in msg
+    st, msg = call(plan)  # valid rows: the usual decode checks follow (never uploaded)
+    assert st == "NVFP4_E_WORKSPACE" and "uploaded" in msg
+    small = nv.Plan([100], num_qo_heads=4, num_kv_heads=1, head_dim_qk=128, page_size=8,
+                    num_cus=256)
+    st, msg = call(small, k=_fake_pool(page_size=8), v=_fake_pool(page_size=8))
+    assert st == "NVFP4_E_UNSUPPORTED" and "page_size" in msg
+    prefill = nv.Plan([100], qo_indptr=[0, 10], num_qo_heads=4, num_kv_heads=1, head_dim_qk=128,
+                      num_cus=256)
+    st, msg = call(prefill)
+    assert st == "NVFP4_E_SHAPE" and "prefill" in msg
