@@ -157,11 +157,14 @@ __global__ __launch_bounds__(256) void prefill_regs_kernel(AttnArgs a) {
 template <int DK, int DV>
 struct CoopShape {
   using S = StepShape<DK, DV>;
-  static constexpr bool OK = DK <= 256 && DV <= 256;
+  static constexpr bool OK = (DK <= 256 && DV <= 256) || (DK == 512 && DV <= 256);
   // Four waves per workgroup.  Head dims up to 128: three row groups per wave and two
   // workgroups per CU (two waves per SIMD hide each other's latencies, and the two
   // workgroups' barriers are independent); larger: two row groups, one wave per SIMD.
   static constexpr bool SMALL = DK <= 128 && DV <= 128;
+  // DK = 512: the K operands of a step (a quarter of the register file) are read one
+  // k-step at a time and the V operands one tile at a time.
+  static constexpr bool WIDE = DK > 256;
   static constexpr int NW = 4;
   static constexpr int NR = SMALL ? 3 : 2;        // row groups of 16 per wave
   static constexpr int WGS_PER_CU = SMALL ? 2 : 1;
@@ -225,35 +228,50 @@ __device__ __forceinline__ void coop_dequant(uint32_t raw, uint32_t opb, int wav
   using S = StepShape<DK, DV>;
   using C = CoopShape<DK, DV>;
   typedef __attribute__((address_space(3))) uint8_t* lds_p;
+  constexpr int NB = S::VB < 4 ? S::VB : 4;   // bytes of the V slice per dword
+  constexpr int EPD = 2 * NB;                 // V tiles per slice dword
+  // Every raw read first: the operand stores below may not move above them (the
+  // compiler cannot tell the raw stage from the operand buffer), so reads issued after
+  // a store would each wait for their own round trip.
+  uint32_t kw[C::KE], ksc[C::KE];
 #pragma unroll
   for (int r = 0; r < C::KE; ++r) {
-    if (wave + C::NW * r < 2 * S::NS) {  // wave-uniform
-      uint32_t w, sc;
-      lds_load<4>(raw + cl.k_raw[r], &w);
-      lds_load<1>(raw + cl.k_sc[r], &sc);
-      if (MASK && cl.k_tok[r] > kleft) sc = 0;
-      const f16x8 v = dequant8(w, splat_lo(fp8x2_to_f16<false>(sc)));
-      *(__attribute__((address_space(3))) f16x8*)(lds_p)(size_t)(opb + cl.k_dst[r]) = v;
+    // wave-uniform; always true when the K entries divide evenly among the waves
+    if ((2 * S::NS) % C::NW == 0 || wave + C::NW * r < 2 * S::NS) {
+      lds_load<4>(raw + cl.k_raw[r], &kw[r]);
+      lds_load<1>(raw + cl.k_sc[r], &ksc[r]);
     }
   }
   uint32_t sa, sb;
   const uint32_t vs = raw + cl.v_sc;
   lds_load<1>(vs, &sa);
   lds_load<1>(vs + DV / 16, &sb);
+  const uint32_t vr = raw + cl.v_raw;
+  uint32_t vw0[S::VW], vw1[S::VW];
+#pragma unroll
+  for (int q = 0; q < S::VW; ++q) {
+    if (C::VH > 1 && C::VPART >= EPD && (q * EPD) / C::VPART != cl.part) continue;
+    lds_load<NB>(vr + 4 * q, &vw0[q]);
+    lds_load<NB>(vr + DV / 2 + 4 * q, &vw1[q]);
+  }
+#pragma unroll
+  for (int r = 0; r < C::KE; ++r) {
+    if ((2 * S::NS) % C::NW == 0 || wave + C::NW * r < 2 * S::NS) {
+      uint32_t sc = ksc[r];
+      if (MASK && cl.k_tok[r] > kleft) sc = 0;
+      const f16x8 v = dequant8(kw[r], splat_lo(fp8x2_to_f16<false>(sc)));
+      *(__attribute__((address_space(3))) f16x8*)(lds_p)(size_t)(opb + cl.k_dst[r]) = v;
+    }
+  }
   if (MASK && cl.v_tok > kleft) sa = 0;
   if (MASK && cl.v_tok + 1 > kleft) sb = 0;
   const f16x2 sp = fp8x2_to_f16<false>(sa | (sb << 8));
-  constexpr int NB = S::VB < 4 ? S::VB : 4;   // bytes of the slice per dword
-  constexpr int EPD = 2 * NB;                 // V tiles per slice dword
-  const uint32_t vr = raw + cl.v_raw;
   const uint32_t vd = opb + cl.v_dst;
 #pragma unroll
   for (int q = 0; q < S::VW; ++q) {
     // a part covers VPART consecutive tiles: whole dwords, or a share of one
     if (C::VH > 1 && C::VPART >= EPD && (q * EPD) / C::VPART != cl.part) continue;
-    uint32_t w0, w1;
-    lds_load<NB>(vr + 4 * q, &w0);
-    lds_load<NB>(vr + DV / 2 + 4 * q, &w1);
+    const uint32_t w0 = vw0[q], w1 = vw1[q];
     // byte k of lo: nibble 2k of token ta (low) and of token ta+1 (high); hi: nibble 2k+1
     const uint32_t lo = (w0 & 0x0F0F0F0Fu) | ((w1 << 4) & 0xF0F0F0F0u);
     const uint32_t hi = ((w0 >> 4) & 0x0F0F0F0Fu) | (w1 & 0xF0F0F0F0u);
@@ -404,6 +422,51 @@ void prefill_coop_kernel(AttnArgs a) {
     const uint32_t ob = opb0 + (i & 1) * C::OPB;
     const int t0 = t_of(i);
     const uint32_t obl = ob + lane * 16;  // this lane's entry of operand 0
+    if constexpr (C::WIDE) {
+      f32x4 sa[NR], sb[NR];
+#pragma unroll
+      for (int rg = 0; rg < NR; ++rg) {
+        sa[rg] = f32x4{0.f, 0.f, 0.f, 0.f};
+        sb[rg] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      // K operands two k-steps ahead of their products (one wave per SIMD: nothing
+      // else hides the LDS latency)
+      constexpr int PF = 3;
+      f16x8 ka[PF], kb[PF];
+      auto kload = [&](int s) {
+        lds_load<16>(obl + s * 1024, reinterpret_cast<uint32_t*>(&ka[s % PF]));
+        lds_load<16>(obl + (S::NS + s) * 1024, reinterpret_cast<uint32_t*>(&kb[s % PF]));
+      };
+      kload(0);
+      kload(1);
+#pragma unroll
+      for (int s = 0; s < S::NS; ++s) {
+        if (s + 2 < S::NS) kload(s + 2);
+#pragma unroll
+        for (int rg = 0; rg < NR; ++rg) {
+          sa[rg] = mfma16x16x32(ka[s % PF], qf[rg][s], sa[rg]);
+          sb[rg] = mfma16x16x32(kb[s % PF], qf[rg][s], sb[rg]);
+        }
+      }
+      f16x8 p[NR];
+#pragma unroll
+      for (int rg = 0; rg < NR; ++rg)
+        p[rg] = st[rg].template softmax<MASK>(sa[rg], sb[rg], sc[rg], t0, j, last[rg]);
+      f16x8 vt[PF];
+      auto vload = [&](int e) {
+        lds_load<16>(obl + (2 * S::NS + e) * 1024, reinterpret_cast<uint32_t*>(&vt[e % PF]));
+      };
+      vload(0);
+      vload(1);
+#pragma unroll
+      for (int e = 0; e < S::NT; ++e) {
+        if (e + 2 < S::NT) vload(e + 2);
+#pragma unroll
+        for (int rg = 0; rg < NR; ++rg)
+          st[rg].acc[e] = mfma16x16x32(vt[e % PF], p[rg], st[rg].acc[e]);
+      }
+      return;
+    }
     f16x8 ka[S::NS], kb[S::NS], vt[S::NT];
 #pragma unroll
     for (int s = 0; s < S::NS; ++s) {
@@ -494,8 +557,8 @@ bool prefill_supported(int dk, int dv) {
 }
 
 int prefill_rows_per_item(int dk, int dv, int /*group*/, int page_size) {
-  if (page_size >= 16 && dk <= 256 && dv <= 256)  // cooperative kernel: 4 waves x NR x 16 rows
-    return dk <= 128 && dv <= 128 ? 192 : 128;
+  if (page_size >= 16 && ((dk <= 256 && dv <= 256) || (dk == 512 && dv <= 256)))
+    return dk <= 128 && dv <= 128 ? 192 : 128;  // cooperative kernel: 4 waves x NR x 16 rows
   return 64 * (dk >= 512 ? 1 : 2);
 }
 

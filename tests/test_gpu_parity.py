@@ -187,7 +187,7 @@ def test_prefill_extend(causal, chunk):
 
 
 @pytest.mark.parametrize("dk,dv,hq,hkv", [(512, 256, 8, 1), (256, 128, 8, 2), (64, 64, 4, 4),
-                                          (128, 128, 32, 8)])
+                                          (128, 128, 32, 8), (512, 128, 4, 1), (512, 64, 8, 2)])
 def test_prefill_head_dims(dk, dv, hq, hkv):
     w = synth.custom(f"pdims{dk}x{dv}", kv_lens=[90, 200], qo_lens=[90, 37], num_qo_heads=hq,
                      num_kv_heads=hkv, head_dim_qk=dk, head_dim_vo=dv, causal=True, seed=dk)
