@@ -292,7 +292,8 @@ nvfp4_status nvfp4_plan_create(const int32_t* kv_lens, const int32_t* qo_indptr,
   // covers four consecutive chunks of a row group, or the whole row split evenly over
   // its waves when nothing is split.  Prefill: keys per work item.  Explicit, never, or
   // chosen so that the device is filled: decode aims at as many waves per CU as its
-  // kernel keeps resident for this shape, prefill at 2 workgroups per CU.
+  // kernel keeps resident for this shape, prefill at as many workgroups per CU as its
+  // kernel keeps resident.
   int chunk = 0;
   int64_t total = 0;
   int max_len = 0;
@@ -305,12 +306,17 @@ nvfp4_status nvfp4_plan_create(const int32_t* kv_lens, const int32_t* qo_indptr,
     chunk = kv_chunk_tokens;
   } else if (kv_chunk_tokens == 0) {
     // items (prefill) / waves (decode)
+    // prefill: one and a half rounds of the resident workgroups, so that the tail
+    // round is made of the short chunks
     const int64_t target =
-        (int64_t)num_cus * (prefill ? 2 : 4 * decode_wgs_per_cu(head_dim_qk, head_dim_vo));
+        prefill ? (int64_t)num_cus * prefill_wgs_per_cu(head_dim_qk, head_dim_vo) * 3 / 2
+                : (int64_t)num_cus * 4 * decode_wgs_per_cu(head_dim_qk, head_dim_vo);
     const int64_t have = (int64_t)groups.size() * (prefill ? 1 : 4);
     if (have < target) {
       int64_t c = (total + target - 1) / std::max<int64_t>(target, 1);
-      c = std::max<int64_t>(c, prefill ? 128 : 64);
+      // a prefill chunk amortises its tile's set-up (Q, pipeline fill, partial store
+      // and merge) over at least 16 steps
+      c = std::max<int64_t>(c, prefill ? 512 : 64);
       c = (c + 31) / 32 * 32;
       if (c * per_item < max_len) chunk = (int)c;
     }

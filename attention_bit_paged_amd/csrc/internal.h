@@ -116,6 +116,8 @@ hipError_t launch_prefill(int dk, int dv, int page_shift, const AttnArgs& a, int
                           hipStream_t stream);
 bool prefill_supported(int dk, int dv);
 int prefill_rows_per_item(int dk, int dv, int group, int page_size);
+// Prefill workgroups one CU runs at once for this shape.
+int prefill_wgs_per_cu(int dk, int dv);
 size_t prefill_lds_bytes(int dk, int dv);
 hipError_t launch_merge_partials(const AttnArgs& a, int n_merges, int dv, int prefill,
                                  hipStream_t stream);

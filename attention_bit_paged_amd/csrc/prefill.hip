@@ -158,15 +158,16 @@ template <int DK, int DV>
 struct CoopShape {
   using S = StepShape<DK, DV>;
   static constexpr bool OK = (DK <= 256 && DV <= 256) || (DK == 512 && DV <= 256);
-  // Four waves per workgroup.  Head dims up to 128: three row groups per wave and two
-  // workgroups per CU (two waves per SIMD hide each other's latencies, and the two
-  // workgroups' barriers are independent); larger: two row groups, one wave per SIMD.
+  // Head dims up to 128: four waves of three row groups, two workgroups per CU (two
+  // waves per SIMD hide each other's latencies, and the two workgroups' barriers are
+  // independent); up to 256: four waves of two row groups, one wave per SIMD.
   static constexpr bool SMALL = DK <= 128 && DV <= 128;
   // DK = 512: the K operands of a step (a quarter of the register file) are read one
-  // k-step at a time and the V operands one tile at a time.
+  // k-step at a time and the V operands one tile at a time; eight waves of one row
+  // group each, two per SIMD, so that one wave's LDS reads overlap the other's products.
   static constexpr bool WIDE = DK > 256;
-  static constexpr int NW = 4;
-  static constexpr int NR = SMALL ? 3 : 2;        // row groups of 16 per wave
+  static constexpr int NW = WIDE ? 8 : 4;
+  static constexpr int NR = SMALL ? 3 : (WIDE ? 1 : 2);  // row groups of 16 per wave
   static constexpr int WGS_PER_CU = SMALL ? 2 : 1;
   static constexpr int ROWS = NW * NR * 16;       // rows per work item
   static constexpr int NOP = 2 * S::NS + S::NT;   // operand vectors per step
@@ -555,6 +556,8 @@ bool prefill_supported(int dk, int dv) {
   const bool okv = dv == 64 || dv == 128 || dv == 256 || dv == 512;
   return okk && okv && dv <= dk && !(dk == 512 && dv == 512);
 }
+
+int prefill_wgs_per_cu(int dk, int dv) { return dk <= 128 && dv <= 128 ? 2 : 1; }
 
 int prefill_rows_per_item(int dk, int dv, int /*group*/, int page_size) {
   if (page_size >= 16 && ((dk <= 256 && dv <= 256) || (dk == 512 && dv <= 256)))
