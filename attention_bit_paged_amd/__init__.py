@@ -196,13 +196,28 @@ class Plan:
         check(lib.nvfp4_plan_set_deferred_merge(self._h, int(bool(deferred))))
 
 
+def _check_rows(plan: Plan, q, page_table, out, lse):
+    """Shapes the C library cannot see (it takes pointers): q, page table and outputs
+    must cover the plan's rows, or the kernels would read or write past them."""
+    rows = plan.batch if plan._ind is None else int(plan._ind[-1])
+    if q.dtype != torch.bfloat16 or q.dim() != 3 or q.stride(-1) != 1 \
+            or tuple(q.shape) != (rows, plan.num_qo_heads, plan.head_dim_qk):
+        raise ValueError(f"q must be bf16 [{rows}, {plan.num_qo_heads}, {plan.head_dim_qk}] "
+                         "with a contiguous last dim")
+    if page_table.dtype != torch.int32 or page_table.dim() != 2 or page_table.stride(1) != 1 \
+            or page_table.shape[0] < plan.batch:
+        raise ValueError(f"page_table must be int32 [>= {plan.batch}, max_pages] with "
+                         "contiguous rows")
+    for name, t, shape in (("out", out, (rows, plan.num_qo_heads, plan.head_dim_vo)),
+                           ("lse", lse, (rows, plan.num_qo_heads))):
+        if t is not None and tuple(t.shape) != shape:
+            raise ValueError(f"{name} must have shape {shape}")
+    return rows
+
+
 def _attn(fn, plan: Plan, q, page_table, k_pool, v_pool, sm_scale, workspace, out, lse, stream,
           prepare=False):
-    rows = q.shape[0]
-    if q.dtype != torch.bfloat16 or q.dim() != 3 or q.stride(-1) != 1:
-        raise ValueError("q must be bf16 [rows, num_qo_heads, head_dim_qk], last dim contiguous")
-    if page_table.dtype != torch.int32 or page_table.dim() != 2 or page_table.stride(1) != 1:
-        raise ValueError("page_table must be int32 [batch, max_pages] with contiguous rows")
+    rows = _check_rows(plan, q, page_table, out, lse)
     if out is None:
         out = torch.empty((rows, plan.num_qo_heads, plan.head_dim_vo), dtype=torch.float32,
                           device=q.device)
@@ -238,14 +253,12 @@ def batch_decode_append(plan: Plan, q: torch.Tensor, k_new: torch.Tensor, v_new:
     """Decode with the step's new token appended (nvfp4_batch_decode_append): k_new / v_new
     bf16 [batch, Hkv, Dk / Dv] go to token kv_len-1 of each request, then attention as
     ``batch_decode``."""
-    for name, t in (("k_new", k_new), ("v_new", v_new)):
-        if t.dtype != torch.bfloat16 or t.dim() != 3 or t.stride(-1) != 1:
-            raise ValueError(f"{name} must be bf16 [batch, num_kv_heads, head_dim], last dim contiguous")
-    rows = q.shape[0]
-    if q.dtype != torch.bfloat16 or q.dim() != 3 or q.stride(-1) != 1:
-        raise ValueError("q must be bf16 [rows, num_qo_heads, head_dim_qk], last dim contiguous")
-    if page_table.dtype != torch.int32 or page_table.dim() != 2 or page_table.stride(1) != 1:
-        raise ValueError("page_table must be int32 [batch, max_pages] with contiguous rows")
+    for name, t, d in (("k_new", k_new, plan.head_dim_qk), ("v_new", v_new, plan.head_dim_vo)):
+        if t.dtype != torch.bfloat16 or t.dim() != 3 or t.stride(-1) != 1 \
+                or tuple(t.shape) != (plan.batch, plan.num_kv_heads, d):
+            raise ValueError(f"{name} must be bf16 [{plan.batch}, {plan.num_kv_heads}, {d}] "
+                             "with a contiguous last dim")
+    rows = _check_rows(plan, q, page_table, out, lse)
     if out is None:
         out = torch.empty((rows, plan.num_qo_heads, plan.head_dim_vo), dtype=torch.float32,
                           device=q.device)

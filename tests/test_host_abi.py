@@ -182,3 +182,24 @@ def test_decode_append_rejections_never_launch():
                       num_cus=256)
     st, msg = call(prefill)
     assert st == "NVFP4_E_SHAPE" and "prefill" in msg
+
+
+def test_binding_checks_shapes_against_the_plan():
+    """The C library takes pointers; the binding rejects tensors that do not cover the
+    plan's rows before any launch."""
+    import torch
+    plan = nv.Plan([100, 30], num_qo_heads=4, num_kv_heads=1, head_dim_qk=128, num_cus=256)
+    pt = torch.zeros((2, 8), dtype=torch.int32)
+    pool = nv.KVPool.empty(16, 1, 16, 128, device="cpu")
+    ws = torch.zeros(plan.workspace_bytes, dtype=torch.uint8)
+    bad_q = torch.zeros((1, 4, 128), dtype=torch.bfloat16)           # one request short
+    with pytest.raises(ValueError, match="q must be"):
+        nv.batch_decode(plan, bad_q, pt, pool, pool, 0.1, ws)
+    q = torch.zeros((2, 4, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="page_table"):
+        nv.batch_decode(plan, q, pt[:1], pool, pool, 0.1, ws)
+    with pytest.raises(ValueError, match="out must"):
+        nv.batch_decode(plan, q, pt, pool, pool, 0.1, ws, out=torch.zeros((2, 4, 64)))
+    kn = torch.zeros((2, 1, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="v_new"):
+        nv.batch_decode_append(plan, q, kn, kn[:1], pt, pool, pool, 0.1, ws)
