@@ -288,12 +288,12 @@ nvfp4_status nvfp4_plan_create(const int32_t* kv_lens, const int32_t* qo_indptr,
     plan->rows_per_slot = tq * group;
   }
 
-  // Chunk length.  Decode: keys per wave; a work item (one workgroup of four waves)
-  // covers four consecutive chunks of a row group, or the whole row split evenly over
-  // its waves when nothing is split.  Prefill: keys per work item.  Explicit, never, or
-  // chosen so that the device is filled: decode aims at as many waves per CU as its
-  // kernel keeps resident for this shape, prefill at as many workgroups per CU as its
-  // kernel keeps resident.
+  // Chunk length.  Decode: keys per wave of a whole work item; a work item (one
+  // workgroup of four waves) covers four consecutive chunks of a row group, or the
+  // whole row when nothing is split, spread evenly over its waves.  Prefill: keys per
+  // work item.  Explicit, never, or chosen so that the device is filled: decode aims at
+  // as many waves per CU as its kernel keeps resident for this shape, prefill at one
+  // and a half rounds of the workgroups its kernel keeps resident.
   int chunk = 0;
   int64_t total = 0;
   int max_len = 0;
@@ -508,7 +508,6 @@ AttnArgs make_args(const nvfp4_plan* plan, const void* q, int64_t q_s_row, int64
   a.page_shift = log2i(plan->page_size);
   a.rows_per_slot = plan->rows_per_slot;
   a.causal = plan->causal;
-  a.wave_chunk = plan->prefill ? 0 : plan->chunk;
   a.merges = reinterpret_cast<const int32_t*>(w + plan->off_merge);
   return a;
 }

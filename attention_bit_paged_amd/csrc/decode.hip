@@ -10,8 +10,8 @@
 // lanes of that row; lse is ln of the sum of exp of the scaled scores.
 //
 // A work item is one workgroup of four waves over one key range of one (request,
-// kv head, block of <= 16 qo heads).  Wave w takes the w-th chunk of the range (the
-// plan's chunk length, or an even 16-aligned quarter), streams it in 32-token steps with
+// kv head, block of <= 16 qo heads).  Wave w takes the w-th 16-aligned quarter of the
+// range (one chunk of a full item), streams it in 32-token steps with
 // several steps' bytes in flight, and the four states are combined through LDS.  When a
 // row group is split over several workgroups, each writes a partial state and a merge
 // kernel on the same stream combines them by LSE (a fence-and-counter merge inside this
@@ -116,8 +116,9 @@ __device__ __forceinline__ DecodeItem decode_item(const AttnArgs& a, int wave, i
   DecodeItem it;
   it.b = rec[W_REQ]; it.kvh = rec[W_KVH]; it.h0 = rec[W_ROW0]; it.hn = rec[W_ROWS];
   it.kv0 = rec[W_KV0]; it.kv1 = rec[W_KV1]; it.slot = rec[W_SLOT]; it.merge = rec[W_MERGE];
-  const int sub =
-      a.wave_chunk > 0 ? a.wave_chunk : (((it.kv1 - it.kv0 + 3) / 4 + 15) / 16) * 16;
+  // the item's keys spread evenly over its four waves, in 16-aligned parts (a full
+  // item gives each wave one chunk; a request's shorter last item keeps all four busy)
+  const int sub = (((it.kv1 - it.kv0 + 3) / 4 + 15) / 16) * 16;
   it.w0 = min(it.kv1, it.kv0 + wave * sub);
   it.w1 = min(it.kv1, it.w0 + sub);
   it.head_valid = n < it.hn;

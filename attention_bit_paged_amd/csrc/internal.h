@@ -60,7 +60,6 @@ struct AttnArgs {
   int32_t page_shift;       // log2(page_size)
   int32_t rows_per_slot;
   int32_t causal;
-  int32_t wave_chunk;       // decode: keys per wave (0: split the item evenly over 4 waves)
   const int32_t* merges;    // merge records
   // Decode with append: the step's new K/V rows (bf16 [batch, kv heads, dim], element
   // strides), quantised into the slot of token kv_len-1 of their request by the work

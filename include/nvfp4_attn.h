@@ -124,8 +124,10 @@ nvfp4_status nvfp4_quantize_kv(const void* k_src, int64_t k_stride_token, int64_
  *              otherwise a multiple of 16: split every request's KV range into
  *              chunks of that many tokens.  Every chunk boundary except the end of
  *              a request is a multiple of 16 tokens.  A decode work item covers
- *              four consecutive chunks (one per wave, combined on chip), a prefill
- *              work item one chunk; split items are merged by LSE.
+ *              four consecutive chunks, spread evenly over its four waves in
+ *              16-aligned parts (one chunk each when the item is whole) and combined
+ *              on chip; a prefill work item covers one chunk; split items are merged
+ *              by LSE.
  *   num_cus:   compute units to fill; 0 = query the current device (256 if none).
  * The plan owns host memory only.  It is immutable after creation, except for the
  * record of the workspace it was last uploaded to.
