@@ -347,9 +347,15 @@ nvfp4_status nvfp4_plan_create(const int32_t* kv_lens, const int32_t* qo_indptr,
     }
     next_slot += nitems;
   }
-  // Longest first, so the tail of the grid holds the short items.
-  std::stable_sort(items.begin(), items.end(),
-                   [](const Item& x, const Item& y) { return x.len > y.len; });
+  // Longest first, so the tail of the grid holds the short items; equal lengths by
+  // request, key range, then kv head, so that consecutive workgroups read the heads of
+  // the same pages together (a page holds every head's rows in one block).
+  std::stable_sort(items.begin(), items.end(), [](const Item& x, const Item& y) {
+    if (x.len != y.len) return x.len > y.len;
+    if (x.f[W_REQ] != y.f[W_REQ]) return x.f[W_REQ] < y.f[W_REQ];
+    if (x.f[W_KV0] != y.f[W_KV0]) return x.f[W_KV0] < y.f[W_KV0];
+    return x.f[W_KVH] < y.f[W_KVH];
+  });
   plan->work.reserve(items.size() * kWorkFields);
   for (const auto& it : items) plan->work.insert(plan->work.end(), it.f, it.f + kWorkFields);
   plan->merges = std::move(merges);

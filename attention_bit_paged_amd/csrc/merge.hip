@@ -4,6 +4,8 @@
 // partial tiles are combined by mergeAndSaveOutTile.  For parts c with
 // (O_c, lse_c): lse = M + ln sum_c exp(lse_c - M) with M = max_c lse_c and
 // O = sum_c exp(lse_c - lse) O_c; a part with lse = -inf adds nothing.
+#include <algorithm>
+
 #include "attn_step.h"
 
 namespace nvfp4 {
@@ -35,7 +37,8 @@ __global__ __launch_bounds__(256) void merge_partials_kernel(AttnArgs a, int n_m
   const int lane = threadIdx.x & 63;
   // the host keeps merges x rows below 2^31
   const int task = (int)blockIdx.x * 4 + wave;
-  const int rows_per_merge = a.rows_per_slot;
+  // rows a merge can have: a decode merge holds at most one block of qo heads
+  const int rows_per_merge = prefill ? a.rows_per_slot : min(a.group, kDecodeHeads);
   if (task >= n_merges * rows_per_merge) return;
   const int mi = task / rows_per_merge;
   const int r = task - mi * rows_per_merge;
@@ -206,7 +209,8 @@ __global__ __launch_bounds__(256) void merge_states_kernel(const float* __restri
 hipError_t launch_merge_partials(const AttnArgs& a, int n_merges, int dv, int prefill,
                                  hipStream_t stream) {
   if (n_merges <= 0) return hipSuccess;
-  const int64_t tasks = (int64_t)n_merges * a.rows_per_slot;
+  const int64_t tasks =
+      (int64_t)n_merges * (prefill ? a.rows_per_slot : std::min(a.group, kDecodeHeads));
   if (tasks + 4 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;  // 32-bit task index
   const dim3 grid((unsigned)((tasks + 3) / 4));
   switch (dv) {
