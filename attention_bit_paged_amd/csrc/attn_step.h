@@ -312,9 +312,18 @@ struct RowState {
   // reference point is finite once this step has been folded in.  Returns the P operand.
   template <bool MASK>
   __device__ __forceinline__ f16x8 softmax(f32x4 sa, f32x4 sb, float c, int t0, int j, int last) {
-    // raw scores; x = s * c is formed inside the exponent's fma.  c > 0 (the host
-    // rejects other scales), so the largest raw score gives the largest x.
     float x[8];
+    const float bm = scores<MASK>(sa, sb, t0, j, last, x);
+    if (__ballot(wants(bm, c)) != 0) raise(bm, c);
+    return probs<MASK>(x, c);
+  }
+
+  // The softmax in parts, for callers that hold several row groups and keep the rare
+  // rescale branch apart from the exponentials.  scores(): the step's raw scores x (c
+  // times them is the base-2 exponent; c > 0, the host rejects other scales) with
+  // masked keys at -inf, and this lane's largest.
+  template <bool MASK>
+  __device__ __forceinline__ float scores(f32x4 sa, f32x4 sb, int t0, int j, int last, float (&x)[8]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       x[i] = sa[i];
@@ -325,30 +334,41 @@ struct RowState {
       for (int i = 0; i < 8; ++i)
         if (t0 + 8 * j + i > last) x[i] = -INFINITY;
     }
-    // this lane's largest raw score of the step.  Plain fmaxf: the scores come straight
-    // from the matrix unit, and only compiler-generated code gets the wait states a
-    // VALU read of an MFMA result needs (an asm statement would hide the read).
+    // Plain fmaxf: the scores come straight from the matrix unit, and only
+    // compiler-generated code gets the wait states a VALU read of an MFMA result needs
+    // (an asm statement would hide the read).
     const float b1 = fmaxf(fmaxf(x[0], x[1]), x[2]);
     const float b2 = fmaxf(fmaxf(x[3], x[4]), x[5]);
     const float b3 = fmaxf(fmaxf(x[6], x[7]), b1);
-    const float bm = fmaxf(b3, b2);
-    // bm * c - m is +inf while m is -inf (any key raises), NaN when both are -inf (the
-    // lane has no key yet: nothing to raise)
-    if (__ballot(fmaf(bm, c, -m) > kRescaleSlack) != 0) {
-      const float bmr = max_over_groups(bm) * c;  // the row's largest scaled score
-      const bool raise = bmr > m + kRescaleSlack;
-      const float m_new = raise ? bmr : m;
-      const float alpha = raise ? fast_exp2(m - m_new) : 1.f;  // 0 when m was -inf
-      if constexpr (FORM == AccForm::VGPR) {
+    return fmaxf(b3, b2);
+  }
+  // This lane's largest passes the reference by more than the slack.  bm * c - m is
+  // +inf while m is -inf (any key raises) and NaN when both are -inf (the lane has no
+  // key yet: nothing to raise).
+  __device__ __forceinline__ bool wants(float bm, float c) const {
+    return fmaf(bm, c, -m) > kRescaleSlack;
+  }
+  // Under a wave-uniform branch taken when some lane wants it: forms the row-wide
+  // maximum and moves the reference of the rows that passed it by the slack.
+  __device__ __forceinline__ void raise(float bm, float c) {
+    const float bmr = max_over_groups(bm) * c;  // the row's largest scaled score
+    const bool up = bmr > m + kRescaleSlack;
+    const float m_new = up ? bmr : m;
+    const float alpha = up ? fast_exp2(m - m_new) : 1.f;  // 0 when m was -inf
+    if constexpr (FORM == AccForm::VGPR) {
 #pragma unroll
-        for (int e = 0; e < NT; e += 4) scale16(acc[e], acc[e + 1], acc[e + 2], acc[e + 3], alpha);
-      } else {
+      for (int e = 0; e < NT; e += 4) scale16(acc[e], acc[e + 1], acc[e + 2], acc[e + 3], alpha);
+    } else {
 #pragma unroll
-        for (int e = 0; e < NT; ++e) acc[e] *= alpha;
-      }
-      l *= alpha;
-      m = m_new;
+      for (int e = 0; e < NT; ++e) acc[e] *= alpha;
     }
+    l *= alpha;
+    m = m_new;
+  }
+  // P = exp2(x c - m) in fp16, and the lane's row sum, which takes the fp16 values the
+  // PV product uses.
+  template <bool MASK>
+  __device__ __forceinline__ f16x8 probs(const float (&x)[8], float c) {
     const float m_use = MASK ? (m == -INFINITY ? 0.f : m) : m;
     f16x2 pp[4];
 #pragma unroll
@@ -357,7 +377,6 @@ struct RowState {
       const float p1 = fast_exp2(fmaf(x[2 * i + 1], c, -m_use));
       pp[i] = f16x2{(_Float16)p0, (_Float16)p1};
     }
-    // the row sum takes the fp16 values the PV product uses
     const f16x2 one2 = {(_Float16)1.f, (_Float16)1.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) l = __builtin_amdgcn_fdot2(pp[i], one2, l, false);

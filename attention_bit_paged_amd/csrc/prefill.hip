@@ -220,41 +220,47 @@ struct CoopLanes {
   }
 };
 
-// Dequantises the raw stage at `raw` into the operand buffer at `opb`.  MASK: keys past
-// `kleft` (tokens of the step after the chunk's last key) get scale 0, so that their
-// bytes, whatever they hold, dequantise to finite zeros.
-template <int DK, int DV, bool MASK>
-__device__ __forceinline__ void coop_dequant(uint32_t raw, uint32_t opb, int wave,
-                                             const CoopLanes<DK, DV>& cl, int kleft) {
+// The cooperative dequantisation of one raw stage: load() reads this lane's raw bytes
+// and scales, store() writes its fp16 operand entries.  MASK: keys past `kleft` (tokens
+// of the step after the chunk's last key) get scale 0, so that their bytes, whatever
+// they hold, dequantise to finite zeros.
+template <int DK, int DV>
+struct CoopRaw {
   using S = StepShape<DK, DV>;
   using C = CoopShape<DK, DV>;
-  typedef __attribute__((address_space(3))) uint8_t* lds_p;
-  constexpr int NB = S::VB < 4 ? S::VB : 4;   // bytes of the V slice per dword
-  constexpr int EPD = 2 * NB;                 // V tiles per slice dword
-  // Every raw read first: the operand stores below may not move above them (the
-  // compiler cannot tell the raw stage from the operand buffer), so reads issued after
-  // a store would each wait for their own round trip.
-  uint32_t kw[C::KE], ksc[C::KE];
+  static constexpr int NB = S::VB < 4 ? S::VB : 4;   // bytes of the V slice per dword
+  static constexpr int EPD = 2 * NB;                 // V tiles per slice dword
+  uint32_t kw[C::KE], ksc[C::KE], sa, sb, vw0[S::VW], vw1[S::VW];
+
+  __device__ __forceinline__ void load(uint32_t raw, int wave, const CoopLanes<DK, DV>& cl) {
 #pragma unroll
-  for (int r = 0; r < C::KE; ++r) {
-    // wave-uniform; always true when the K entries divide evenly among the waves
-    if ((2 * S::NS) % C::NW == 0 || wave + C::NW * r < 2 * S::NS) {
-      lds_load<4>(raw + cl.k_raw[r], &kw[r]);
-      lds_load<1>(raw + cl.k_sc[r], &ksc[r]);
+    for (int r = 0; r < C::KE; ++r) {
+      // wave-uniform; always true when the K entries divide evenly among the waves
+      if ((2 * S::NS) % C::NW == 0 || wave + C::NW * r < 2 * S::NS) {
+        lds_load<4>(raw + cl.k_raw[r], &kw[r]);
+        lds_load<1>(raw + cl.k_sc[r], &ksc[r]);
+      }
+    }
+    const uint32_t vs = raw + cl.v_sc;
+    lds_load<1>(vs, &sa);
+    lds_load<1>(vs + DV / 16, &sb);
+    const uint32_t vr = raw + cl.v_raw;
+#pragma unroll
+    for (int q = 0; q < S::VW; ++q) {
+      if (C::VH > 1 && C::VPART >= EPD && (q * EPD) / C::VPART != cl.part) continue;
+      lds_load<NB>(vr + 4 * q, &vw0[q]);
+      lds_load<NB>(vr + DV / 2 + 4 * q, &vw1[q]);
     }
   }
-  uint32_t sa, sb;
-  const uint32_t vs = raw + cl.v_sc;
-  lds_load<1>(vs, &sa);
-  lds_load<1>(vs + DV / 16, &sb);
-  const uint32_t vr = raw + cl.v_raw;
-  uint32_t vw0[S::VW], vw1[S::VW];
-#pragma unroll
-  for (int q = 0; q < S::VW; ++q) {
-    if (C::VH > 1 && C::VPART >= EPD && (q * EPD) / C::VPART != cl.part) continue;
-    lds_load<NB>(vr + 4 * q, &vw0[q]);
-    lds_load<NB>(vr + DV / 2 + 4 * q, &vw1[q]);
-  }
+  template <bool MASK>
+  __device__ __forceinline__ void store(uint32_t opb, int wave, const CoopLanes<DK, DV>& cl, int kleft);
+};
+
+template <int DK, int DV>
+template <bool MASK>
+__device__ __forceinline__ void CoopRaw<DK, DV>::store(uint32_t opb, int wave,
+                                                       const CoopLanes<DK, DV>& cl, int kleft) {
+  typedef __attribute__((address_space(3))) uint8_t* lds_p;
 #pragma unroll
   for (int r = 0; r < C::KE; ++r) {
     if ((2 * S::NS) % C::NW == 0 || wave + C::NW * r < 2 * S::NS) {
@@ -292,6 +298,17 @@ __device__ __forceinline__ void coop_dequant(uint32_t raw, uint32_t opb, int wav
       *(__attribute__((address_space(3))) uint32_t*)(lds_p)(size_t)(vd + e * 1024) = f16x2_bits(v);
     }
   }
+}
+
+// Dequantises the raw stage at `raw` into the operand buffer at `opb`.  MASK: keys past
+// `kleft` get scale 0.  Every raw read first: the operand stores may not move above
+// them (the compiler cannot tell the raw stage from the operand buffer).
+template <int DK, int DV, bool MASK>
+__device__ __forceinline__ void coop_dequant(uint32_t raw, uint32_t opb, int wave,
+                                             const CoopLanes<DK, DV>& cl, int kleft) {
+  CoopRaw<DK, DV> r;
+  r.load(raw, wave, cl);
+  r.template store<MASK>(opb, wave, cl, kleft);
 }
 
 // Waits until this wave's copies of all but the newest issued step are done (or all
@@ -410,20 +427,17 @@ void prefill_coop_kernel(AttnArgs a) {
     __syncthreads();
     if (i + 3 < nsteps)
       coop_issue<DK, DV>(wave, rp, raw0 + (i % 3) * C::RAW_STAGE, view, t_of(i + 3), tlast, bad);
-    if (next) {
-      const uint32_t rs = raw0 + ((i + 1) % 3) * C::RAW_STAGE, ob1 = opb0 + ((i + 1) & 1) * C::OPB;
-      if (t_of(i + 1) + kDecodeStep - 1 > tlast)
-        coop_dequant<DK, DV, true>(rs, ob1, wave, cl, tlast - t_of(i + 1));
-      else
-        coop_dequant<DK, DV, false>(rs, ob1, wave, cl, 0);
-    }
-    // S = K Q^T for every row group first (the K operands are then dead), then per row
-    // group the softmax and O^T += V^T P^T; the PV products of group g can run beside
-    // the softmax of group g+1.
     const uint32_t ob = opb0 + (i & 1) * C::OPB;
     const int t0 = t_of(i);
     const uint32_t obl = ob + lane * 16;  // this lane's entry of operand 0
+    const uint32_t rs = raw0 + ((i + 1) % 3) * C::RAW_STAGE, ob1 = opb0 + ((i + 1) & 1) * C::OPB;
     if constexpr (C::WIDE) {
+      if (next) {
+        if (t_of(i + 1) + kDecodeStep - 1 > tlast)
+          coop_dequant<DK, DV, true>(rs, ob1, wave, cl, tlast - t_of(i + 1));
+        else
+          coop_dequant<DK, DV, false>(rs, ob1, wave, cl, 0);
+      }
       f32x4 sa[NR], sb[NR];
 #pragma unroll
       for (int rg = 0; rg < NR; ++rg) {
@@ -468,14 +482,23 @@ void prefill_coop_kernel(AttnArgs a) {
       }
       return;
     }
+    // Two straight-line blocks.  The first reads this step's K operands and the next
+    // step's raw bytes, forms S = K Q^T for every row group and dequantises the next
+    // step beside those products (on the last step: a stale stage, into the operand
+    // buffer nobody reads any more), then takes each row group's largest score.  The
+    // rare rescale sits between the blocks; the second forms P and O^T += V^T P^T for
+    // every row group, each group's PV products beside the next group's exponentials.
     f16x8 ka[S::NS], kb[S::NS], vt[S::NT];
 #pragma unroll
     for (int s = 0; s < S::NS; ++s) {
       lds_load<16>(obl + s * 1024, reinterpret_cast<uint32_t*>(&ka[s]));
       lds_load<16>(obl + (S::NS + s) * 1024, reinterpret_cast<uint32_t*>(&kb[s]));
     }
+    CoopRaw<DK, DV> raw;
+    raw.load(rs, wave, cl);
     f32x4 sa[NR], sb[NR];
-    auto qk = [&](int rg) {
+#pragma unroll
+    for (int rg = 0; rg < NR; ++rg) {
       sa[rg] = f32x4{0.f, 0.f, 0.f, 0.f};
       sb[rg] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -483,17 +506,39 @@ void prefill_coop_kernel(AttnArgs a) {
         sa[rg] = mfma16x16x32(ka[s], qf[rg][s], sa[rg]);
         sb[rg] = mfma16x16x32(kb[s], qf[rg][s], sb[rg]);
       }
-    };
-#pragma unroll
-    for (int rg = 0; rg < NR; ++rg) qk(rg);
+    }
+    raw.template store<true>(ob1, wave, cl, tlast - t_of(i + 1));
 #pragma unroll
     for (int e = 0; e < S::NT; ++e)
       lds_load<16>(obl + (2 * S::NS + e) * 1024, reinterpret_cast<uint32_t*>(&vt[e]));
+    float x[NR][8], bm[NR];
+    bool want = false;
 #pragma unroll
     for (int rg = 0; rg < NR; ++rg) {
-      const f16x8 p = st[rg].template softmax<MASK>(sa[rg], sb[rg], sc[rg], t0, j, last[rg]);
+      bm[rg] = st[rg].template scores<MASK>(sa[rg], sb[rg], t0, j, last[rg], x[rg]);
+      want = want || st[rg].wants(bm[rg], sc[rg]);
+    }
+    if (__ballot(want) != 0) {
+#pragma unroll
+      for (int rg = 0; rg < NR; ++rg)
+        if (__ballot(st[rg].wants(bm[rg], sc[rg])) != 0) st[rg].raise(bm[rg], sc[rg]);
+    }
+#pragma unroll
+    for (int rg = 0; rg < NR; ++rg) {
+      const f16x8 p = st[rg].template probs<MASK>(x[rg], sc[rg]);
       st[rg].pv(vt, p);
     }
+    // order of the second block: group 0's P, then one PV product of group g to three
+    // VALU instructions of group g+1's P, then the last group's products
+    __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);
+#pragma unroll
+    for (int rg = 1; rg < NR; ++rg)
+#pragma unroll
+      for (int e = 0; e < S::NT; ++e) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      }
+    __builtin_amdgcn_sched_group_barrier(0x008, S::NT, 0);
   };
   // prologue: three steps in flight, step 0 dequantised
   for (int i = 0; i < 3 && i < nsteps; ++i)
