@@ -315,8 +315,8 @@ nvfp4_status nvfp4_plan_create(const int32_t* kv_lens, const int32_t* qo_indptr,
     if (have < target) {
       int64_t c = (total + target - 1) / std::max<int64_t>(target, 1);
       // a prefill chunk amortises its tile's set-up (Q, pipeline fill, partial store
-      // and merge) over at least 16 steps
-      c = std::max<int64_t>(c, prefill ? 512 : 64);
+      // and merge) over at least 20 steps
+      c = std::max<int64_t>(c, prefill ? 640 : 64);
       c = (c + 31) / 32 * 32;
       if (c * per_item < max_len) chunk = (int)c;
     }
