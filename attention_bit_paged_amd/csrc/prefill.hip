@@ -17,9 +17,9 @@
 // ring by direct global-to-LDS copies (each wave issues one pool's copies, three
 // steps deep); the four waves then dequantise the step together into fp16 MFMA
 // operands, stored lane-major in an LDS operand buffer (double-buffered, one barrier
-// per step), and every wave computes its four groups of 16 rows from those operands,
-// held in registers for the step.  The K/V dequantisation and the LDS reads are thus
-// shared by the 256 rows of the tile.
+// per step), and every wave computes its groups of 16 rows from those operands, held
+// in registers for the step (three groups per wave for head dims up to 128).  The K/V
+// dequantisation and the LDS reads are thus shared by all rows of the tile.
 //
 // Register kernel (any page size, any head dims): each wave owns its rows and loads
 // and dequantises every step itself, the next step's bytes held in registers.
@@ -452,6 +452,7 @@ void prefill_coop_kernel(AttnArgs a) {
         lds_load<16>(obl + s * 1024, reinterpret_cast<uint32_t*>(&ka[s % PF]));
         lds_load<16>(obl + (S::NS + s) * 1024, reinterpret_cast<uint32_t*>(&kb[s % PF]));
       };
+      __builtin_amdgcn_s_setprio(1);  // the QK products first, as below
       kload(0);
       kload(1);
 #pragma unroll
@@ -463,6 +464,7 @@ void prefill_coop_kernel(AttnArgs a) {
           sb[rg] = mfma16x16x32(kb[s % PF], qf[rg][s], sb[rg]);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
       f16x8 p[NR];
 #pragma unroll
       for (int rg = 0; rg < NR; ++rg)
@@ -489,6 +491,11 @@ void prefill_coop_kernel(AttnArgs a) {
     // rare rescale sits between the blocks; the second forms P and O^T += V^T P^T for
     // every row group, each group's PV products beside the next group's exponentials.
     f16x8 ka[S::NS], kb[S::NS], vt[S::NT];
+    // This block at raised wave priority: of the two workgroups sharing a SIMD, the
+    // wave that is issuing its QK products goes first and the other wave's softmax and
+    // PV work fills the matrix unit's gaps (about 4 % faster than equal priorities;
+    // raising the PV block as well, or the barrier and copy issue, gained nothing).
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int s = 0; s < S::NS; ++s) {
       lds_load<16>(obl + s * 1024, reinterpret_cast<uint32_t*>(&ka[s]));
@@ -508,6 +515,7 @@ void prefill_coop_kernel(AttnArgs a) {
       }
     }
     raw.template store<true>(ob1, wave, cl, tlast - t_of(i + 1));
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int e = 0; e < S::NT; ++e)
       lds_load<16>(obl + (2 * S::NS + e) * 1024, reinterpret_cast<uint32_t*>(&vt[e]));

@@ -27,7 +27,9 @@ Other modes (profiling support):
                            (counter calibration) and a few steps of the workload;
   --summarize-trace DIR    summarise a rocprofv3 --kernel-trace --stats output dir;
   --summarize-pmc DIR ...  summarise FETCH_SIZE / WRITE_SIZE counter dirs into the
-                           traffic record read back by the benchmark.
+                           traffic record read back by the benchmark;
+  --summarize-counters DIR ...  summarise SQ counter passes of one kernel (--kernel
+                           names it): MFMA busy share, instruction mix per wave, waits.
 """
 from __future__ import annotations
 
@@ -65,6 +67,8 @@ def parse():
     p.add_argument("--pmc-run", action="store_true")
     p.add_argument("--summarize-trace", metavar="DIR")
     p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    p.add_argument("--summarize-counters", nargs="+", metavar="DIR")
+    p.add_argument("--kernel", default="prefill_coop_kernel", help="kernel of --summarize-counters")
     p.add_argument("--command", default="", help="command line recorded in a summary")
     p.add_argument("--out", default="", help="summary file to write")
     return p.parse_args()
@@ -434,6 +438,70 @@ def summarize_pmc(args):
     print(text)
 
 
+SIMDS = 256 * 4          # MI355X: 256 CUs of 4 SIMDs
+CLOCK_GHZ = 2.4          # nominal peak engine clock
+
+
+def summarize_counters(args):
+    """Per-dispatch SQ counters of one kernel from rocprofv3 --pmc passes, averaged over
+    its dispatches, with the figures derived from them.  Cycle counters of waves
+    (SQ_WAVE_CYCLES, SQ_WAIT_*, SQ_ACTIVE_INST_*) count in units of 4 cycles;
+    SQ_VALU_MFMA_BUSY_CYCLES in cycles, summed over the SIMDs.  Kernel time comes from
+    the dispatch timestamps; cycles assume the nominal 2.4 GHz clock."""
+    vals, dur, waves = {}, [], None
+    for d in args.summarize_counters:
+        per = {}
+        for r in _kernel_rows(os.path.join(d, "**", "*counter_collection.csv")):
+            if args.kernel not in r["Kernel_Name"]:
+                continue
+            key = (r["Dispatch_Id"], r["Counter_Name"])
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+            dur.append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+            waves = int(r["Grid_Size"]) // 64
+        for (_, c), v in per.items():
+            vals.setdefault(c, []).append(v)
+    if not vals:
+        raise SystemExit(f"no dispatch of {args.kernel} in {args.summarize_counters}")
+    avg = {c: float(np.mean(v)) for c, v in vals.items()}
+    t = float(np.median(dur))
+    cyc = t * CLOCK_GHZ * 1e9
+    lines = [f"# SQ counters of {args.kernel}, workload {args.workload}",
+             f"# command: {args.command}",
+             f"# {len(vals[next(iter(vals))])} dispatches per counter; kernel {t * 1e6:.1f} us "
+             f"(dispatch timestamps, median), {waves} waves", ""]
+    for c in sorted(avg):
+        lines.append(f"{c:32s} {avg[c]:18.0f}")
+    der = {}
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+        der["mfma_busy_share"] = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (SIMDS * cyc)
+    if "SQ_INSTS_VALU_MFMA_MOPS_F16" in avg:
+        der["mfma_f16_tflops_executed"] = avg["SQ_INSTS_VALU_MFMA_MOPS_F16"] * 512 / t / 1e12
+    if "SQ_WAVE_CYCLES" in avg:
+        der["resident_wave_share_of_2_per_simd"] = avg["SQ_WAVE_CYCLES"] * 4 / (2 * SIMDS * cyc)
+    if "SQ_INSTS_MFMA" in avg and waves:
+        mf = avg["SQ_INSTS_MFMA"] / waves
+        der["mfma_per_wave"] = mf
+        if "SQ_INSTS_VALU" in avg:
+            der["other_valu_per_mfma"] = (avg["SQ_INSTS_VALU"] - avg["SQ_INSTS_MFMA"]) / avg["SQ_INSTS_MFMA"]
+        for c in ("SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_INSTS_VALU_TRANS_F32"):
+            if c in avg:
+                der[c.lower() + "_per_mfma"] = avg[c] / avg["SQ_INSTS_MFMA"]
+        for c in ("SQ_WAVE_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_ANY",
+                  "SQ_WAIT_ANY", "SQ_WAIT_INST_LDS"):
+            if c in avg:
+                der[c.lower() + "_cycles_per_mfma"] = avg[c] * 4 / avg["SQ_INSTS_MFMA"]
+    lines += ["", "# derived (per MFMA instruction: 16 busy cycles each for 16x16x32 f16)"]
+    lines += [f"{k:48s} {v:12.4f}" for k, v in der.items()]
+    lines.append(json.dumps({"kernel": args.kernel, "workload": args.workload, "kernel_us": round(t * 1e6, 2),
+                             "counters": {c: round(v) for c, v in avg.items()},
+                             "derived": {k: round(v, 4) for k, v in der.items()}}))
+    text = "\n".join(lines) + "\n"
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(text)
+    print(text)
+
+
 def prefill_main(args, torch, nv, paged, synth):
     """A prefill workload as the timed step (for profiling the prefill kernel): the
     attention pass and the merge of its split rows, prepared once."""
@@ -481,6 +549,8 @@ def main():
         return summarize_trace(args)
     if args.summarize_pmc:
         return summarize_pmc(args)
+    if args.summarize_counters:
+        return summarize_counters(args)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path shards by request or kv head with no exchange between GPUs)",
