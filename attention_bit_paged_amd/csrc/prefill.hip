@@ -193,22 +193,29 @@ struct CoopLanes {
   using S = StepShape<DK, DV>;
   using C = CoopShape<DK, DV>;
   using R = typename C::R;
-  uint32_t k_raw[C::KE], k_sc[C::KE], k_dst[C::KE];
-  int k_tok[C::KE];
+  // Entry r of a lane is operand wave + NW*r.  NW divides NS (or a lane has one entry),
+  // so entry r lies a fixed distance from entry 0 in the raw stage and in the operand
+  // buffer: one per-lane base per pool, the rest immediate offsets of the LDS accesses.
+  static_assert(S::NS % C::NW == 0 || C::KE == 1, "K entry spacing");
+  static constexpr uint32_t k_raw_off(int r) {
+    return (C::NW * r) / S::NS * 4 * (DK / 2) + 4 * ((C::NW * r) % S::NS);
+  }
+  static constexpr uint32_t k_sc_off(int r) {
+    return (C::NW * r) / S::NS * 4 * (DK / 16) + ((C::NW * r) % S::NS) / 2;
+  }
+  static constexpr uint32_t k_dst_off(int r) { return C::NW * r * 64 * 16; }
+  uint32_t k_raw, k_sc, k_dst;  // entry 0
   uint32_t v_raw, v_sc, v_dst;
   int v_tok, part;
 
   __device__ __forceinline__ void init(int wave, int lane) {
     const int j = lane >> 4, n = lane & 15;
-#pragma unroll
-    for (int r = 0; r < C::KE; ++r) {
-      const int o = min(wave + C::NW * r, 2 * S::NS - 1);  // clamped: unused when past the end
-      const int tile = o / S::NS, s = o % S::NS;
-      k_tok[r] = 8 * (n >> 2) + (n & 3) + 4 * tile;
-      k_raw[r] = R::OFF_KD + k_tok[r] * (DK / 2) + j * S::KB + 4 * s;
-      k_sc[r] = R::OFF_SF + k_tok[r] * (DK / 16) + j * S::KSF + (s >> 1);
-      k_dst[r] = (o * 64 + lane) * 16;
-    }
+    const int o = min(wave, 2 * S::NS - 1);  // clamped: unused when past the end
+    const int tile = o / S::NS, s = o % S::NS;
+    const int k_tok = 8 * (n >> 2) + (n & 3) + 4 * tile;
+    k_raw = R::OFF_KD + k_tok * (DK / 2) + j * S::KB + 4 * s;
+    k_sc = R::OFF_SF + k_tok * (DK / 16) + j * S::KSF + (s >> 1);
+    k_dst = (o * 64 + lane) * 16;
     const int L = wave * 64 + lane;
     const int c = L / (4 * C::VH), p = L & 3;
     part = (L >> 2) % C::VH;
@@ -221,9 +228,12 @@ struct CoopLanes {
 };
 
 // The cooperative dequantisation of one raw stage: load() reads this lane's raw bytes
-// and scales, store() writes its fp16 operand entries.  MASK: keys past `kleft` (tokens
-// of the step after the chunk's last key) get scale 0, so that their bytes, whatever
-// they hold, dequantise to finite zeros.
+// and scales, store() writes its fp16 operand entries.  MASK: value rows past `kleft`
+// (tokens of the step after the chunk's last key) get scale 0, so that their bytes,
+// whatever they hold (NaN scales included), dequantise to finite zeros: a NaN there
+// would reach every output through its zero probability.  Key rows past the end are
+// left as they are: a bad key row only spoils its own scores, which the softmax of a
+// step that holds such keys replaces by -inf.
 template <int DK, int DV>
 struct CoopRaw {
   using S = StepShape<DK, DV>;
@@ -237,8 +247,8 @@ struct CoopRaw {
     for (int r = 0; r < C::KE; ++r) {
       // wave-uniform; always true when the K entries divide evenly among the waves
       if ((2 * S::NS) % C::NW == 0 || wave + C::NW * r < 2 * S::NS) {
-        lds_load<4>(raw + cl.k_raw[r], &kw[r]);
-        lds_load<1>(raw + cl.k_sc[r], &ksc[r]);
+        lds_load<4>(raw + cl.k_raw + cl.k_raw_off(r), &kw[r]);
+        lds_load<1>(raw + cl.k_sc + cl.k_sc_off(r), &ksc[r]);
       }
     }
     const uint32_t vs = raw + cl.v_sc;
@@ -264,10 +274,8 @@ __device__ __forceinline__ void CoopRaw<DK, DV>::store(uint32_t opb, int wave,
 #pragma unroll
   for (int r = 0; r < C::KE; ++r) {
     if ((2 * S::NS) % C::NW == 0 || wave + C::NW * r < 2 * S::NS) {
-      uint32_t sc = ksc[r];
-      if (MASK && cl.k_tok[r] > kleft) sc = 0;
-      const f16x8 v = dequant8(kw[r], splat_lo(fp8x2_to_f16<false>(sc)));
-      *(__attribute__((address_space(3))) f16x8*)(lds_p)(size_t)(opb + cl.k_dst[r]) = v;
+      const f16x8 v = dequant8(kw[r], splat_lo(fp8x2_to_f16<false>(ksc[r])));
+      *(__attribute__((address_space(3))) f16x8*)(lds_p)(size_t)(opb + cl.k_dst + cl.k_dst_off(r)) = v;
     }
   }
   if (MASK && cl.v_tok > kleft) sa = 0;
@@ -300,8 +308,8 @@ __device__ __forceinline__ void CoopRaw<DK, DV>::store(uint32_t opb, int wave,
   }
 }
 
-// Dequantises the raw stage at `raw` into the operand buffer at `opb`.  MASK: keys past
-// `kleft` get scale 0.  Every raw read first: the operand stores may not move above
+// Dequantises the raw stage at `raw` into the operand buffer at `opb`.  MASK: value rows
+// past `kleft` get scale 0.  Every raw read first: the operand stores may not move above
 // them (the compiler cannot tell the raw stage from the operand buffer).
 template <int DK, int DV, bool MASK>
 __device__ __forceinline__ void coop_dequant(uint32_t raw, uint32_t opb, int wave,
@@ -427,10 +435,13 @@ void prefill_coop_kernel(AttnArgs a) {
     __syncthreads();
     if (i + 3 < nsteps)
       coop_issue<DK, DV>(wave, rp, raw0 + (i % 3) * C::RAW_STAGE, view, t_of(i + 3), tlast, bad);
-    const uint32_t ob = opb0 + (i & 1) * C::OPB;
+    // Stage and buffer bases as single scalars: left to itself the compiler folds the
+    // modulo's parts into every lane address separately (two vector adds per address).
+    const uint32_t ob = __builtin_amdgcn_readfirstlane(opb0 + (i & 1) * C::OPB);
     const int t0 = t_of(i);
     const uint32_t obl = ob + lane * 16;  // this lane's entry of operand 0
-    const uint32_t rs = raw0 + ((i + 1) % 3) * C::RAW_STAGE, ob1 = opb0 + ((i + 1) & 1) * C::OPB;
+    const uint32_t rs = __builtin_amdgcn_readfirstlane(raw0 + ((i + 1) % 3) * C::RAW_STAGE);
+    const uint32_t ob1 = __builtin_amdgcn_readfirstlane(opb0 + ((i + 1) & 1) * C::OPB);
     if constexpr (C::WIDE) {
       if (next) {
         if (t_of(i + 1) + kDecodeStep - 1 > tlast)
