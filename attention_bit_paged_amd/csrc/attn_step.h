@@ -334,13 +334,15 @@ struct RowState {
       for (int i = 0; i < 8; ++i)
         if (t0 + 8 * j + i > last) x[i] = -INFINITY;
     }
-    // Plain fmaxf: the scores come straight from the matrix unit, and only
-    // compiler-generated code gets the wait states a VALU read of an MFMA result needs
-    // (an asm statement would hide the read).
-    const float b1 = fmaxf(fmaxf(x[0], x[1]), x[2]);
-    const float b2 = fmaxf(fmaxf(x[3], x[4]), x[5]);
-    const float b3 = fmaxf(fmaxf(x[6], x[7]), b1);
-    return fmaxf(b3, b2);
+    // Compiler-generated code, not asm: the scores come straight from the matrix unit,
+    // and only compiler-generated code gets the wait states a VALU read of an MFMA
+    // result needs.  The NaN-propagating maximum (four v_maximum3_f32) rather than
+    // fmaxf, whose IEEE semantics make the compiler quieten some MFMA results first; a
+    // NaN score could only come from a key that is masked above or from NaN inputs.
+    const float b1 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(x[0], x[1]), x[2]);
+    const float b2 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(x[3], x[4]), x[5]);
+    const float b3 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(x[6], x[7]), b1);
+    return __builtin_elementwise_maximum(b3, b2);
   }
   // This lane's largest passes the reference by more than the slack.  bm * c - m is
   // +inf while m is -inf (any key raises) and NaN when both are -inf (the lane has no

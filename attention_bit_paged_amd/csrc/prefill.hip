@@ -531,13 +531,13 @@ void prefill_coop_kernel(AttnArgs a) {
     for (int e = 0; e < S::NT; ++e)
       lds_load<16>(obl + (2 * S::NS + e) * 1024, reinterpret_cast<uint32_t*>(&vt[e]));
     float x[NR][8], bm[NR];
-    bool want = false;
+    uint64_t want = 0;  // the groups' votes, combined as wave masks on the scalar unit
 #pragma unroll
     for (int rg = 0; rg < NR; ++rg) {
       bm[rg] = st[rg].template scores<MASK>(sa[rg], sb[rg], t0, j, last[rg], x[rg]);
-      want = want || st[rg].wants(bm[rg], sc[rg]);
+      want |= __ballot(st[rg].wants(bm[rg], sc[rg]));
     }
-    if (__ballot(want) != 0) {
+    if (want != 0) {
 #pragma unroll
       for (int rg = 0; rg < NR; ++rg)
         if (__ballot(st[rg].wants(bm[rg], sc[rg])) != 0) st[rg].raise(bm[rg], sc[rg]);
