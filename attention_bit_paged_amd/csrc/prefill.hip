@@ -380,20 +380,6 @@ void prefill_coop_kernel(AttnArgs a) {
   bool rv[NR];
   int64_t tokrow[NR];
   int headi[NR];
-#pragma unroll
-  for (int rg = 0; rg < NR; ++rg) {
-    const int r = row_base + rg * 16 + n;
-    rv[rg] = r < Rn;
-    const int qi = r / G;
-    const int gh = r - qi * G;
-    const int qpos = q0 + qi;
-    tokrow[rg] = (int64_t)qstart + qpos;
-    headi[rg] = kvh * G + gh;
-    last[rg] = a.causal ? min(kv1 - 1, qpos + off) : kv1 - 1;
-    sc[rg] = a.score_scale *
-             load_q_operand<DK>(a.q + tokrow[rg] * a.q_s_row + (int64_t)headi[rg] * a.q_s_head,
-                                rv[rg], j, qf[rg]);
-  }
   // keys the tile needs: up to the last visible key of its last row
   const int tile_end = a.causal ? min(kv1, q0 + (Rn - 1) / G + off + 1) : kv1;
   const int tlast = kv1 - 1;
@@ -408,6 +394,25 @@ void prefill_coop_kernel(AttnArgs a) {
   CoopLanes<DK, DV> cl;
   cl.init(wave, lane);
   uint32_t bad = 0;
+
+  // The first three steps' copies go out before Q is read, so that the two memory
+  // latencies of a work item's start overlap.
+  for (int i = 0; i < 3 && i < nsteps; ++i)
+    coop_issue<DK, DV>(wave, rp, raw0 + i * C::RAW_STAGE, view, kv0 + i * kDecodeStep, tlast, bad);
+#pragma unroll
+  for (int rg = 0; rg < NR; ++rg) {
+    const int r = row_base + rg * 16 + n;
+    rv[rg] = r < Rn;
+    const int qi = r / G;
+    const int gh = r - qi * G;
+    const int qpos = q0 + qi;
+    tokrow[rg] = (int64_t)qstart + qpos;
+    headi[rg] = kvh * G + gh;
+    last[rg] = a.causal ? min(kv1 - 1, qpos + off) : kv1 - 1;
+    sc[rg] = a.score_scale *
+             load_q_operand<DK>(a.q + tokrow[rg] * a.q_s_row + (int64_t)headi[rg] * a.q_s_head,
+                                rv[rg], j, qf[rg]);
+  }
 
   // One wave per SIMD (wide heads): the Q operands are only ever MFMA sources, so they
   // are kept in AGPRs, leaving the VGPRs to the accumulators and the step's operands.
@@ -559,9 +564,7 @@ void prefill_coop_kernel(AttnArgs a) {
       }
     __builtin_amdgcn_sched_group_barrier(0x008, S::NT, 0);
   };
-  // prologue: three steps in flight, step 0 dequantised
-  for (int i = 0; i < 3 && i < nsteps; ++i)
-    coop_issue<DK, DV>(wave, rp, raw0 + i * C::RAW_STAGE, view, t_of(i), tlast, bad);
+  // prologue: three steps in flight (issued above), step 0 dequantised
   if (nsteps > 0) {
     coop_wait<DK, DV>(wave, false);
     __syncthreads();
