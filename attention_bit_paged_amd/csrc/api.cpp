@@ -20,9 +20,7 @@
 #include <cstdio>
 #include <cstring>
 #include <mutex>
-#include <functional>
 #include <numeric>
-#include <queue>
 #include <string>
 #include <vector>
 
@@ -147,24 +145,6 @@ PoolArgs pool_args(const nvfp4_kv_pool* p, int num_pages) {
   a.sf_tok = p->sf_stride_token;
   a.num_pages = num_pages;
   return a;
-}
-
-// Finish time of a longest-first list schedule over `slots` identical slots of work
-// items whose costs are given as a histogram (hist[c] items of cost c): the order in
-// which a grid's workgroups take the free workgroup slots when the work items are
-// sorted by decreasing length.  `heap` is scratch.
-int lpt_makespan(const std::vector<int>& hist, int slots, std::vector<int>& heap) {
-  heap.assign((size_t)slots, 0);  // all zero: already a heap
-  int end = 0;
-  for (int c = (int)hist.size() - 1; c > 0; --c) {
-    for (int n = hist[c]; n > 0; --n) {
-      std::pop_heap(heap.begin(), heap.end(), std::greater<int>());
-      heap.back() += c;
-      end = std::max(end, heap.back());
-      std::push_heap(heap.begin(), heap.end(), std::greater<int>());
-    }
-  }
-  return end;
 }
 
 }  // namespace
@@ -344,67 +324,6 @@ nvfp4_status nvfp4_plan_create(const int32_t* kv_lens, const int32_t* qo_indptr,
   plan->chunk = chunk;
   const int64_t item_span = chunk > 0 ? (int64_t)chunk * per_item : 0;
 
-  // Prefill left whole by the rule above (enough tiles for the device): the grid is a
-  // longest-first list schedule of the tiles over the resident workgroups, and a few
-  // long tiles can set its end.  Splitting every tile above a threshold into equal
-  // 32-key parts evens it out at the price of a merge of those tiles' rows.  Model: a
-  // tile costs its 32-key steps plus about three steps of start-up (Q, the pipeline
-  // fill, the stores); a step of one workgroup takes its products' share of about
-  // 900 TFLOP/s over the resident workgroups; the merge streams its partial rows at
-  // about 4 TB/s after a launch of about 3 us (measured on the causal
-  // extend workload: splitting 192 of its 976 tiles took 12-30 us off the attention
-  // kernel and added 14 us of merge).  The thresholds tried are fractions of
-  // the longest tile; the cheapest plan, whole tiles included, is kept.
-  std::vector<int> parts(groups.size(), 1);
-  if (prefill && kv_chunk_tokens == 0 && chunk == 0 && !groups.empty()) {
-    const int slots = num_cus * prefill_wgs_per_cu(head_dim_qk, head_dim_vo);
-    std::vector<int> steps(groups.size());
-    int max_steps = 0;
-    for (size_t i = 0; i < groups.size(); ++i) {
-      steps[i] = (groups[i].kv_end + 31) / 32;
-      max_steps = std::max(max_steps, steps[i]);
-    }
-    constexpr int kStartSteps = 3;
-    constexpr double kDeviceFlops = 9.0e14, kMergeBytesPerUs = 4.0e6, kMergeLaunchUs = 3.0;
-    const double step_us = (double)plan->rows_per_item * 32 * 2 * (head_dim_qk + head_dim_vo) *
-                           slots / kDeviceFlops * 1e6;
-    const double row_bytes = (double)plan->rows_per_item * (head_dim_vo + 1) * 4;
-    std::vector<int> hist, heap;
-    auto cost_us = [&](int x, std::vector<int>* out) {
-      hist.assign((size_t)max_steps + kStartSteps + 1, 0);
-      double merge_bytes = 0;
-      for (size_t i = 0; i < groups.size(); ++i) {
-        const int k = (x > 0 && steps[i] > x) ? (steps[i] + x - 1) / x : 1;
-        if (out) (*out)[i] = k;
-        hist[steps[i] / k + 1 + kStartSteps] += steps[i] % k;
-        hist[steps[i] / k + kStartSteps] += k - steps[i] % k;
-        if (k > 1) merge_bytes += row_bytes * (k + 1);
-      }
-      const double merge_us = merge_bytes > 0 ? kMergeLaunchUs + merge_bytes / kMergeBytesPerUs : 0.0;
-      return lpt_makespan(hist, std::max(slots, 1), heap) * step_us + merge_us;
-    };
-    // whole tiles, then thresholds at 90..50 % of the longest tile, then 5 % either
-    // side of the best of those
-    double best = cost_us(0, nullptr);
-    int best_f = 0;
-    auto consider = [&](int f) {
-      const int x = max_steps * f / 100;
-      if (f <= 0 || f >= 100 || x < 4) return;
-      const double c = cost_us(x, nullptr);
-      if (c < best) {
-        best = c;
-        best_f = f;
-      }
-    };
-    for (int f = 90; f >= 50; f -= 10) consider(f);
-    const int coarse = best_f;
-    if (coarse > 0) {
-      consider(coarse + 5);
-      consider(coarse - 5);
-    }
-    if (best_f > 0) cost_us(max_steps * best_f / 100, &parts);
-  }
-
   struct Item {
     int32_t f[kWorkFields];
     int len;
@@ -412,11 +331,9 @@ nvfp4_status nvfp4_plan_create(const int32_t* kv_lens, const int32_t* qo_indptr,
   std::vector<Item> items;
   std::vector<int32_t> merges;
   int next_slot = 0;
-  for (size_t gi = 0; gi < groups.size(); ++gi) {
-    const auto& g = groups[gi];
+  for (const auto& g : groups) {
     const int L = g.kv_end;
-    const int nitems = (item_span > 0 && L > item_span) ? (int)((L + item_span - 1) / item_span)
-                                                        : parts[gi];
+    const int nitems = (item_span > 0 && L > item_span) ? (int)((L + item_span - 1) / item_span) : 1;
     if (nitems == 1) {
       items.push_back({{g.b, g.kvh, g.row0, g.rows, 0, L, -1, -1}, L});
       continue;
@@ -424,14 +341,8 @@ nvfp4_status nvfp4_plan_create(const int32_t* kv_lens, const int32_t* qo_indptr,
     const int mi = (int)(merges.size() / kMergeFields);
     const int32_t rec[kMergeFields] = {g.b, g.kvh, g.row0, g.rows, next_slot, nitems, 0, 0};
     merges.insert(merges.end(), rec, rec + kMergeFields);
-    // chunks of item_span keys, or (a split prefill tile) equal parts of whole steps
-    const int steps = (L + 31) / 32;
-    auto bound = [&](int c) -> int {
-      if (item_span > 0) return (int)std::min<int64_t>(L, c * item_span);
-      return std::min(L, 32 * (c * (steps / nitems) + std::min(c, steps % nitems)));
-    };
     for (int c = 0; c < nitems; ++c) {
-      const int a = bound(c), e = bound(c + 1);
+      const int a = (int)(c * item_span), e = (int)std::min<int64_t>(L, (c + 1) * item_span);
       items.push_back({{g.b, g.kvh, g.row0, g.rows, a, e, next_slot + c, mi}, e - a});
     }
     next_slot += nitems;

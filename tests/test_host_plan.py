@@ -110,27 +110,3 @@ def test_prefill_plan_covers_every_query(causal, chunk):
             starts = sorted(r0 for (bb, gg, r0) in groups if bb == b and gg == g)
             assert starts == list(range(0, int(q[b]), tq))
 
-
-def test_prefill_extend_plan_splits_only_the_longest_tiles():
-    """The causal extend workload (16 requests, 976 tiles over 512 resident workgroups):
-    the planner's list-schedule model splits the longest tiles, each into equal parts of
-    whole 32-key steps, and no tile shorter than an unsplit one."""
-    from attention_bit_paged_amd import synth
-    w = synth.workload("prefill_extend")
-    ind = synth.indptr(w.qo_lens)
-    plan = nv.Plan(w.kv_lens, qo_indptr=ind.tolist(), num_qo_heads=w.num_qo_heads,
-                   num_kv_heads=w.num_kv_heads, head_dim_qk=128, causal=True, kv_chunk_tokens=0,
-                   num_cus=256)
-    groups = check_plan(plan, w.kv_lens, 4, list(w.qo_lens), True)
-    info = plan.info()
-    assert info["kv_chunk_tokens"] == 0 and info["num_merges"] > 0
-    split, whole = [], []
-    for items in groups.values():
-        items = sorted(items, key=lambda x: x[W["kv_begin"]])
-        end = items[-1][W["kv_end"]]
-        (split if len(items) > 1 else whole).append(end)
-        if len(items) > 1:
-            steps = [(x[W["kv_end"]] - x[W["kv_begin"]] + 31) // 32 for x in items]
-            assert max(steps) - min(steps) <= 1
-            assert all(x[W["kv_begin"]] % 32 == 0 for x in items)
-    assert (max(whole) + 31) // 32 <= (min(split) + 31) // 32
