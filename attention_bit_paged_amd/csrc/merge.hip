@@ -96,8 +96,11 @@ __global__ __launch_bounds__(256) void merge_partials_kernel(AttnArgs a, int n_m
   if (np <= FAST) {
     const float lp = lse_of(lane);
     float v[FAST][PER];
+    // only the partials that exist (np is wave-uniform: scalar branches between loads
+    // that are all in flight together)
 #pragma unroll
-    for (int q = 0; q < FAST; ++q) load_row(src + (q < np ? q : 0) * step, v[q]);  // in bounds
+    for (int q = 0; q < FAST; ++q)
+      if (q < np) load_row(src + q * step, v[q]);
     any_nan = __any(lp != lp);
     mx = wave_max(lp);
     if (mx > -INFINITY) {
