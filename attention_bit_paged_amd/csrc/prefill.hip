@@ -33,6 +33,11 @@ namespace nvfp4 {
 
 namespace {
 
+// Operand registers of the wide-head (DK = 512) cooperative kernel's LDS read pipeline:
+// reads run this many k-steps (V tiles) less one ahead of their products (3 and 5
+// measured alike, 7 slower).
+constexpr int kWidePrefetch = 3;
+
 template <int DK>
 constexpr int prefill_nr() {
   return DK >= 512 ? 1 : 2;
@@ -460,43 +465,50 @@ void prefill_coop_kernel(AttnArgs a) {
         sa[rg] = f32x4{0.f, 0.f, 0.f, 0.f};
         sb[rg] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-      // K operands two k-steps ahead of their products (one wave per SIMD: nothing
-      // else hides the LDS latency)
-      constexpr int PF = 3;
+      // K operands PF - 1 k-steps ahead of their products, the order pinned by
+      // scheduling groups: left to itself the compiler moves every read next to its
+      // product (three operand registers instead of PF) and each pair of products
+      // then waits for the LDS.
+      constexpr int PF = kWidePrefetch;
+      static_assert(NR == 1, "one row group per wave");
       f16x8 ka[PF], kb[PF];
       auto kload = [&](int s) {
         lds_load<16>(obl + s * 1024, reinterpret_cast<uint32_t*>(&ka[s % PF]));
         lds_load<16>(obl + (S::NS + s) * 1024, reinterpret_cast<uint32_t*>(&kb[s % PF]));
       };
       __builtin_amdgcn_s_setprio(1);  // the QK products first, as below
-      kload(0);
-      kload(1);
+#pragma unroll
+      for (int s = 0; s < PF - 1; ++s) kload(s);
 #pragma unroll
       for (int s = 0; s < S::NS; ++s) {
-        if (s + 2 < S::NS) kload(s + 2);
+        if (s + PF - 1 < S::NS) kload(s + PF - 1);
+        sa[0] = mfma16x16x32(ka[s % PF], qf[0][s], sa[0]);
+        sb[0] = mfma16x16x32(kb[s % PF], qf[0][s], sb[0]);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (PF - 1), 0);
 #pragma unroll
-        for (int rg = 0; rg < NR; ++rg) {
-          sa[rg] = mfma16x16x32(ka[s % PF], qf[rg][s], sa[rg]);
-          sb[rg] = mfma16x16x32(kb[s % PF], qf[rg][s], sb[rg]);
-        }
+      for (int s = 0; s < S::NS; ++s) {
+        if (s + PF - 1 < S::NS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       }
       __builtin_amdgcn_s_setprio(0);
-      f16x8 p[NR];
-#pragma unroll
-      for (int rg = 0; rg < NR; ++rg)
-        p[rg] = st[rg].template softmax<MASK>(sa[rg], sb[rg], sc[rg], t0, j, last[rg]);
+      const f16x8 p = st[0].template softmax<MASK>(sa[0], sb[0], sc[0], t0, j, last[0]);
       f16x8 vt[PF];
       auto vload = [&](int e) {
         lds_load<16>(obl + (2 * S::NS + e) * 1024, reinterpret_cast<uint32_t*>(&vt[e % PF]));
       };
-      vload(0);
-      vload(1);
+#pragma unroll
+      for (int e = 0; e < PF - 1; ++e) vload(e);
 #pragma unroll
       for (int e = 0; e < S::NT; ++e) {
-        if (e + 2 < S::NT) vload(e + 2);
+        if (e + PF - 1 < S::NT) vload(e + PF - 1);
+        st[0].acc[e] = mfma16x16x32(vt[e % PF], p, st[0].acc[e]);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, PF - 1, 0);
 #pragma unroll
-        for (int rg = 0; rg < NR; ++rg)
-          st[rg].acc[e] = mfma16x16x32(vt[e % PF], p[rg], st[rg].acc[e]);
+      for (int e = 0; e < S::NT; ++e) {
+        if (e + PF - 1 < S::NT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       }
       return;
     }
