@@ -259,6 +259,15 @@ void decode_ring_kernel(AttnArgs a) {
 
   RowState<S::NT, AccForm::VGPR> st;
   st.init();
+  // Long chunks: wave priority from the steps a wave has left (longest remaining
+  // first).  The waves resident on a CU otherwise share its memory issue oldest first:
+  // with one round of equal chunks (the long-context workload, 64 steps per wave) the
+  // first-dispatched workgroups finished in 114 us and the last in 200, the early ones'
+  // slots idle meanwhile; ranking by the work left evens that out (221 -> 211 us).  Short
+  // chunks (the batch workload, 8 steps per wave, 2.3 rounds of work items) keep equal
+  // priorities: there a second-round item would overtake the ones about to finish, and it
+  // measured 3 % slower.
+  const bool lrpt = nsteps >= 24;
   // Full steps, unrolled by the ring depth so that every stage offset is a constant.
   // Step i issues step i + NST - 1 (when it exists) into the stage step i - 1 used,
   // then waits until at most NST - 1 steps are newer than its own.
@@ -267,6 +276,13 @@ void decode_ring_kernel(AttnArgs a) {
     for (int s = 0; s < R::NST; ++s) {
       const int i = i0 + s;
       if (i >= nfull) break;
+      if (lrpt) {
+        const int rem = nsteps - i;
+        if (rem >= 24) __builtin_amdgcn_s_setprio(3);
+        else if (rem >= 12) __builtin_amdgcn_s_setprio(2);
+        else if (rem >= 4) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
+      }
       const int ahead = i + R::NST - 1;
       const bool more = ahead < nsteps;
       if (more)
