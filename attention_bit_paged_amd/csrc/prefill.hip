@@ -344,15 +344,97 @@ __device__ __forceinline__ void coop_wait(int wave, bool one_newer) {
   }
 }
 
+// The copy offsets of the one pool this wave issues (wave 0: K data, 1: V data, 2 and 3:
+// the scale bytes, whose copies carry both pools' lanes).  The full plan holds every
+// pool's offsets; kept whole in each wave they cost registers the loop needs.
 template <int DK, int DV>
-__device__ __forceinline__ void coop_issue(int wave, const RingPlan<DK, DV, 3 * CoopShape<DK, DV>::RAW_STAGE>& rp,
-                                           uint32_t stage, const PagedView<DK, DV, true>& view,
-                                           int t0, int tlast, uint32_t& bad) {
+struct CoopCopies {
+  using R = RingShape<DK, DV, 3 * CoopShape<DK, DV>::RAW_STAGE>;
+  using Plan = RingPlan<DK, DV, 3 * CoopShape<DK, DV>::RAW_STAGE>;
+  static constexpr int MAXC = R::N_KD > R::N_VD ? (R::N_KD > R::N_SF ? R::N_KD : R::N_SF)
+                                                : (R::N_VD > R::N_SF ? R::N_VD : R::N_SF);
+  uint32_t mine[MAXC];
+
+  __device__ __forceinline__ void init(const Plan& rp, int wave) {
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+      const uint32_t kd = c < R::N_KD ? rp.off[c] : 0u;
+      const uint32_t vd = c < R::N_VD ? rp.off[R::N_KD + c] : 0u;
+      const uint32_t sf = c < R::N_SF ? rp.off[R::N_KD + R::N_VD + c] : 0u;
+      mine[c] = wave == 0 ? kd : (wave == 1 ? vd : sf);
+    }
+  }
+  // a plan holding this wave's offsets in the places of pool P (1, 2, 4 or 8) and zeros
+  // (never read for P) elsewhere
+  template <int P>
+  __device__ __forceinline__ Plan expand() const {
+    Plan r;
+    constexpr int first = P == 1 ? 0 : (P == 2 ? R::N_KD : R::N_KD + R::N_VD);
+    constexpr int count = P == 1 ? R::N_KD : (P == 2 ? R::N_VD : R::N_SF);
+#pragma unroll
+    for (int c = 0; c < R::NCOPY; ++c)
+      r.off[c] = (c >= first && c < first + count) ? mine[c - first] : 0u;
+    return r;
+  }
+};
+
+template <int DK, int DV>
+__device__ __forceinline__ void coop_issue(int wave, const CoopCopies<DK, DV>& cc, uint32_t stage,
+                                           const PagedView<DK, DV, true>& view, int t0, int tlast,
+                                           uint32_t& bad) {
   constexpr int WL = 3 * CoopShape<DK, DV>::RAW_STAGE;
-  if (wave == 0) ring_issue<DK, DV, WL, 1>(rp, stage, view, t0, tlast, bad);
-  else if (wave == 1) ring_issue<DK, DV, WL, 2>(rp, stage, view, t0, tlast, bad);
-  else if (wave == 2) ring_issue<DK, DV, WL, 4>(rp, stage, view, t0, tlast, bad);
-  else if (wave == 3) ring_issue<DK, DV, WL, 8>(rp, stage, view, t0, tlast, bad);
+  if (wave == 0) ring_issue<DK, DV, WL, 1>(cc.template expand<1>(), stage, view, t0, tlast, bad);
+  else if (wave == 1) ring_issue<DK, DV, WL, 2>(cc.template expand<2>(), stage, view, t0, tlast, bad);
+  else if (wave == 2) ring_issue<DK, DV, WL, 4>(cc.template expand<4>(), stage, view, t0, tlast, bad);
+  else if (wave == 3) ring_issue<DK, DV, WL, 8>(cc.template expand<8>(), stage, view, t0, tlast, bad);
+}
+
+// Softmax with the reference point inside the product (head dims up to 256).  Q carries
+// the score factor, and each row group's QK accumulators start at -r, where r is the
+// row's reference point (0 while the row has seen no key): the products then give
+// x = c s - r directly and p = exp2(x), without a multiply-add per score.  A row moves
+// its reference when its largest x passes the slack, and at its first visible key: in
+// a step whose keys every row sees (no mask) that can only be the item's first step,
+// where every row moves; a masked step also moves rows that have no reference yet.
+struct ShiftRef {
+  f32x4 negr;
+  __device__ __forceinline__ void init() { negr = f32x4{0.f, 0.f, 0.f, 0.f}; }
+};
+
+// Under a wave-uniform branch taken when some lane passed its threshold: moves the
+// reference of the rows whose largest score passed it, rescales their accumulators and
+// row sums, and shifts this step's x to the new reference.
+template <int NT>
+__device__ __forceinline__ void raise_shifted(RowState<NT, AccForm::VGPR>& st, ShiftRef& sr,
+                                              float bm, float (&x)[8]) {
+  const float r = -sr.negr[0];
+  const float bmr = max_over_groups(bm) + r;  // the row's largest c s
+  const bool up = bmr > st.m + kRescaleSlack;
+  const float m_new = up ? bmr : st.m;
+  const float alpha = up ? fast_exp2(st.m - m_new) : 1.f;  // 0 when m was -inf
+#pragma unroll
+  for (int e = 0; e < NT; e += 4)
+    scale16(st.acc[e], st.acc[e + 1], st.acc[e + 2], st.acc[e + 3], alpha);
+  st.l *= alpha;
+  st.m = m_new;
+  const float r_new = m_new == -INFINITY ? 0.f : m_new;
+  const float d = r_new - r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] -= d;
+  sr.negr = f32x4{-r_new, -r_new, -r_new, -r_new};
+}
+
+// P = exp2(x) in fp16 and the lane's row sum of those fp16 values.
+template <int NT>
+__device__ __forceinline__ f16x8 probs_shifted(RowState<NT, AccForm::VGPR>& st, const float (&x)[8]) {
+  f16x2 pp[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    pp[i] = f16x2{(_Float16)fast_exp2(x[2 * i]), (_Float16)fast_exp2(x[2 * i + 1])};
+  const f16x2 one2 = {(_Float16)1.f, (_Float16)1.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) st.l = __builtin_amdgcn_fdot2(pp[i], one2, st.l, false);
+  return pack8(pp[0], pp[1], pp[2], pp[3]);
 }
 
 template <int DK, int DV>
@@ -381,7 +463,6 @@ void prefill_coop_kernel(AttnArgs a) {
 
   f16x8 qf[NR][S::NS];
   float sc[NR];
-  int last[NR];
   bool rv[NR];
   int64_t tokrow[NR];
   int headi[NR];
@@ -392,8 +473,12 @@ void prefill_coop_kernel(AttnArgs a) {
 
   PagedView<DK, DV, true> view;
   view.init(a, b, kvh, lane);
-  RingPlan<DK, DV, WL> rp;
-  rp.init(lane, view.k_tok, view.v_tok, view.ksf_tok, view.vsf_tok);
+  CoopCopies<DK, DV> cc;
+  {
+    RingPlan<DK, DV, WL> rp;
+    rp.init(lane, view.k_tok, view.v_tok, view.ksf_tok, view.vsf_tok);
+    cc.init(rp, wave);
+  }
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
   const uint32_t raw0 = lds0, opb0 = lds0 + 3 * C::RAW_STAGE;
   CoopLanes<DK, DV> cl;
@@ -403,7 +488,10 @@ void prefill_coop_kernel(AttnArgs a) {
   // The first three steps' copies go out before Q is read, so that the two memory
   // latencies of a work item's start overlap.
   for (int i = 0; i < 3 && i < nsteps; ++i)
-    coop_issue<DK, DV>(wave, rp, raw0 + i * C::RAW_STAGE, view, kv0 + i * kDecodeStep, tlast, bad);
+    coop_issue<DK, DV>(wave, cc, raw0 + i * C::RAW_STAGE, view, kv0 + i * kDecodeStep, tlast, bad);
+  // Head dims up to 256: Q carries the score factor (see ShiftRef) unless some row of
+  // the wave could overflow fp16; that wave then takes the exact prescaled Q.
+  bool safe = true;
 #pragma unroll
   for (int rg = 0; rg < NR; ++rg) {
     const int r = row_base + rg * 16 + n;
@@ -413,10 +501,19 @@ void prefill_coop_kernel(AttnArgs a) {
     const int qpos = q0 + qi;
     tokrow[rg] = (int64_t)qstart + qpos;
     headi[rg] = kvh * G + gh;
-    last[rg] = a.causal ? min(kv1 - 1, qpos + off) : kv1 - 1;
-    sc[rg] = a.score_scale *
-             load_q_operand<DK>(a.q + tokrow[rg] * a.q_s_row + (int64_t)headi[rg] * a.q_s_head,
-                                rv[rg], j, qf[rg]);
+    const uint16_t* qrow = a.q + tokrow[rg] * a.q_s_row + (int64_t)headi[rg] * a.q_s_head;
+    if constexpr (C::WIDE)
+      sc[rg] = a.score_scale * load_q_operand<DK>(qrow, rv[rg], j, qf[rg]);
+    else
+      safe = load_q_scaled<DK>(qrow, rv[rg], j, a.score_scale, qf[rg]) && safe;
+  }
+  const bool shifted = !C::WIDE && __all(safe);
+  if (!C::WIDE && !shifted) {
+#pragma unroll
+    for (int rg = 0; rg < NR; ++rg)
+      sc[rg] = a.score_scale *
+               load_q_operand<DK>(a.q + tokrow[rg] * a.q_s_row + (int64_t)headi[rg] * a.q_s_head,
+                                  rv[rg], j, qf[rg]);
   }
 
   // One wave per SIMD (wide heads): the Q operands are only ever MFMA sources, so they
@@ -430,21 +527,32 @@ void prefill_coop_kernel(AttnArgs a) {
   }
 
   RowState<S::NT, AccForm::VGPR> st[NR];
+  ShiftRef sr[NR];
 #pragma unroll
-  for (int rg = 0; rg < NR; ++rg) st[rg].init();
+  for (int rg = 0; rg < NR; ++rg) {
+    st[rg].init();
+    sr[rg].init();
+  }
 
   auto t_of = [&](int i) { return kv0 + i * kDecodeStep; };
+  // the last key row group rg may see; recomputed in the (few) masked steps rather than
+  // held in registers for the whole loop
+  auto last_of = [&](int rg) {
+    const int qpos = q0 + (row_base + rg * 16 + n) / G;
+    return a.causal ? min(kv1 - 1, qpos + off) : kv1 - 1;
+  };
   // One step: wait for the next raw step, refill the ring, dequantise the next step
   // and compute this one.  MASK: some key of the step is past some row's limit.
-  auto step = [&](int i, auto mask_tag) {
+  auto step = [&](int i, auto mask_tag, auto shift_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr bool SHIFT = decltype(shift_tag)::value && !C::WIDE;
     const bool next = i + 1 < nsteps;
     // raw step i+1 landed (only step i+2 may still be in flight); operands of step i
     // are visible; nobody reads operand buffer (i+1)%2 or raw stage i%3 any more
     if (next) coop_wait<DK, DV>(wave, i + 2 < nsteps);
     __syncthreads();
     if (i + 3 < nsteps)
-      coop_issue<DK, DV>(wave, rp, raw0 + (i % 3) * C::RAW_STAGE, view, t_of(i + 3), tlast, bad);
+      coop_issue<DK, DV>(wave, cc, raw0 + (i % 3) * C::RAW_STAGE, view, t_of(i + 3), tlast, bad);
     // Stage and buffer bases as single scalars: left to itself the compiler folds the
     // modulo's parts into every lane address separately (two vector adds per address).
     const uint32_t ob = __builtin_amdgcn_readfirstlane(opb0 + (i & 1) * C::OPB);
@@ -492,7 +600,7 @@ void prefill_coop_kernel(AttnArgs a) {
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       }
       __builtin_amdgcn_s_setprio(0);
-      const f16x8 p = st[0].template softmax<MASK>(sa[0], sb[0], sc[0], t0, j, last[0]);
+      const f16x8 p = st[0].template softmax<MASK>(sa[0], sb[0], sc[0], t0, j, MASK ? last_of(0) : 0);
       f16x8 vt[PF];
       auto vload = [&](int e) {
         lds_load<16>(obl + (2 * S::NS + e) * 1024, reinterpret_cast<uint32_t*>(&vt[e % PF]));
@@ -534,8 +642,8 @@ void prefill_coop_kernel(AttnArgs a) {
     f32x4 sa[NR], sb[NR];
 #pragma unroll
     for (int rg = 0; rg < NR; ++rg) {
-      sa[rg] = f32x4{0.f, 0.f, 0.f, 0.f};
-      sb[rg] = f32x4{0.f, 0.f, 0.f, 0.f};
+      sa[rg] = SHIFT ? sr[rg].negr : f32x4{0.f, 0.f, 0.f, 0.f};
+      sb[rg] = sa[rg];
 #pragma unroll
       for (int s = 0; s < S::NS; ++s) {
         sa[rg] = mfma16x16x32(ka[s], qf[rg][s], sa[rg]);
@@ -548,31 +656,46 @@ void prefill_coop_kernel(AttnArgs a) {
     for (int e = 0; e < S::NT; ++e)
       lds_load<16>(obl + (2 * S::NS + e) * 1024, reinterpret_cast<uint32_t*>(&vt[e]));
     float x[NR][8], bm[NR];
+    const bool first = i == 0;  // uniform
+    auto vote = [&](int rg) -> bool {
+      if constexpr (SHIFT)
+        return first || bm[rg] > kRescaleSlack || (MASK && st[rg].m == -INFINITY);
+      else
+        return st[rg].wants(bm[rg], sc[rg]);
+    };
     uint64_t want = 0;  // the groups' votes, combined as wave masks on the scalar unit
 #pragma unroll
     for (int rg = 0; rg < NR; ++rg) {
-      bm[rg] = st[rg].template scores<MASK>(sa[rg], sb[rg], t0, j, last[rg], x[rg]);
-      want |= __ballot(st[rg].wants(bm[rg], sc[rg]));
+      bm[rg] = st[rg].template scores<MASK>(sa[rg], sb[rg], t0, j, MASK ? last_of(rg) : 0, x[rg]);
+      want |= __ballot(vote(rg));
     }
     if (want != 0) {
 #pragma unroll
-      for (int rg = 0; rg < NR; ++rg)
-        if (__ballot(st[rg].wants(bm[rg], sc[rg])) != 0) st[rg].raise(bm[rg], sc[rg]);
+      for (int rg = 0; rg < NR; ++rg) {
+        if (__ballot(vote(rg)) != 0) {
+          if constexpr (SHIFT)
+            raise_shifted(st[rg], sr[rg], bm[rg], x[rg]);
+          else
+            st[rg].raise(bm[rg], sc[rg]);
+        }
+      }
     }
 #pragma unroll
     for (int rg = 0; rg < NR; ++rg) {
-      const f16x8 p = st[rg].template probs<MASK>(x[rg], sc[rg]);
+      const f16x8 p = SHIFT ? probs_shifted(st[rg], x[rg]) : st[rg].template probs<MASK>(x[rg], sc[rg]);
       st[rg].pv(vt, p);
     }
-    // order of the second block: group 0's P, then one PV product of group g to three
-    // VALU instructions of group g+1's P, then the last group's products
-    __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);
+    // order of the second block: group 0's P, then one PV product of group g to a share
+    // of group g+1's P (16 VALU instructions a group shifted, 24 otherwise), then the
+    // last group's products
+    constexpr int PV_VALU = SHIFT ? 2 : 3;
+    __builtin_amdgcn_sched_group_barrier(0x002, SHIFT ? 16 : 20, 0);
 #pragma unroll
     for (int rg = 1; rg < NR; ++rg)
 #pragma unroll
       for (int e = 0; e < S::NT; ++e) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, PV_VALU, 0);
       }
     __builtin_amdgcn_sched_group_barrier(0x008, S::NT, 0);
   };
@@ -586,8 +709,13 @@ void prefill_coop_kernel(AttnArgs a) {
   const int tile_min_last = a.causal ? min(kv1 - 1, q0 + off) : kv1 - 1;
   const int n_full = min(nsteps, max(0, (tile_min_last - kv0 + 1) / kDecodeStep));
   int i = 0;
-  for (; i < n_full; ++i) step(i, std::false_type{});
-  for (; i < nsteps; ++i) step(i, std::true_type{});
+  if (shifted) {
+    for (; i < n_full; ++i) step(i, std::false_type{}, std::true_type{});
+    for (; i < nsteps; ++i) step(i, std::true_type{}, std::true_type{});
+  } else {
+    for (; i < n_full; ++i) step(i, std::false_type{}, std::false_type{});
+    for (; i < nsteps; ++i) step(i, std::true_type{}, std::false_type{});
+  }
 
   const bool badw = __any(bad != 0);
   // the four waves saw different copies: any bad page poisons the whole tile
