@@ -207,6 +207,27 @@ def test_prefill_unequal_strides():
     _run_case(w, k_pad=(1, 1, 3, 16), v_pad=(2, 0, 1, 32), chunk=-1)
 
 
+@pytest.mark.parametrize("dk,dv", [(128, 128), (256, 256), (64, 64)])
+def test_prefill_extreme_q_magnitudes(dk, dv):
+    """Query rows scaled by 2^18 (|q sm_scale log2 e| far above fp16's range: those waves
+    take the exactly prescaled Q) next to rows scaled by 2^-20 (fp16 subnormals once
+    multiplied by the score factor) and ordinary rows.  Powers of two keep Q exact in
+    bf16, so the oracle sees the same values."""
+    w = synth.custom(f"pqmag{dk}", kv_lens=[150, 230], qo_lens=[70, 100], num_qo_heads=8,
+                     num_kv_heads=2, head_dim_qk=dk, head_dim_vo=dv, causal=True, seed=41)
+    c = gh.build_oracle_case(w)
+    scale = np.ones(c.q_np.shape[0])
+    scale[:12] = 2.0 ** 18          # request 0, first queries: one wave's rows and more
+    scale[70:80] = 2.0 ** -20       # request 1, first queries
+    c.q_np = c.q_np * scale[:, None, None]
+    c.q = (c.q.double() * torch.from_numpy(scale).to(c.q.device)[:, None, None]).to(torch.bfloat16)
+    assert np.array_equal(c.q.cpu().double().numpy(), c.q_np)
+    plan = gh.make_plan(w, -1)
+    o, lse = gh.run_gpu(c, plan)
+    o_ref, lse_ref = gh.oracle_reference(c)
+    gh.assert_attention_close(o, lse, o_ref, lse_ref, w.name)
+
+
 def test_prefill_asym_config():
     """The asymmetric-heads causal prefill workload at its full size."""
     _run_case(synth.workload("asym_prefill"), chunk=None)
