@@ -389,6 +389,38 @@ __device__ __forceinline__ void coop_issue(int wave, const CoopCopies<DK, DV>& c
   else if (wave == 3) ring_issue<DK, DV, WL, 8>(cc.template expand<8>(), stage, view, t0, tlast, bad);
 }
 
+// Q quarter-row multiplied by the score factor c (the scores then leave the product in
+// base-2 exponent units) and rounded to fp16, relative error at most 2^-12 per
+// element.  Returns false when the row could overflow fp16 (|q c| >= 2^15, or not
+// finite): the caller then takes the exact prescaled form of load_q_operand.
+template <int DK>
+__device__ __forceinline__ bool load_q_scaled(const uint16_t* qrow, bool valid, int j, float c,
+                                              f16x8 (&qf)[DK / 32]) {
+  constexpr int QW = DK / 8;
+  uint32_t qraw[QW];
+  if (valid) {
+    load_bytes<DK / 2>(reinterpret_cast<const uint8_t*>(qrow + j * (DK / 4)), qraw);
+  } else {
+#pragma unroll
+    for (int i = 0; i < QW; ++i) qraw[i] = 0u;
+  }
+  float qmax = 0.f;
+#pragma unroll
+  for (int i = 0; i < QW; ++i)
+    qmax = fmaxf(qmax, fmaxf(fabsf(bf16f(qraw[i] & 0xFFFF)), fabsf(bf16f(qraw[i] >> 16))));
+#pragma unroll
+  for (int s = 0; s < DK / 32; ++s) {
+    f16x2 p[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t w = qraw[4 * s + t];
+      p[t] = f16x2{(_Float16)(bf16f(w & 0xFFFF) * c), (_Float16)(bf16f(w >> 16) * c)};
+    }
+    qf[s] = pack8(p[0], p[1], p[2], p[3]);
+  }
+  return qmax * c < 32768.f;
+}
+
 // Softmax with the reference point inside the product (head dims up to 256).  Q carries
 // the score factor, and each row group's QK accumulators start at -r, where r is the
 // row's reference point (0 while the row has seen no key): the products then give
