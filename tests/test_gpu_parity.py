@@ -186,6 +186,51 @@ def test_prefill_extend(causal, chunk):
     _run_case(w, chunk=chunk)
 
 
+def test_prefill_request_without_queries():
+    """A request with keys but no queries inside a ragged prefill batch."""
+    w = synth.custom("noq", kv_lens=[40, 120, 75], qo_lens=[10, 0, 75], num_qo_heads=8,
+                     num_kv_heads=2, causal=True, seed=24)
+    _run_case(w, chunk=-1)
+    _run_case(w, chunk=32)
+
+
+@pytest.mark.parametrize("dk,chunk", [(128, -1), (128, 64), (64, -1), (256, -1), (512, -1)])
+def test_prefill_vones_uniform_probe(dk, chunk):
+    """Q = 0 and V = ones in a causal extend: every row's O is exactly the dequantised
+    one (1.03125) and its LSE is ln of its visible keys, i + 1 + L - q for query i."""
+    q = [3, 40, 100]
+    prefix = [0, 17, 260]
+    w = synth.custom(f"pvones{dk}", kv_lens=[a + b for a, b in zip(q, prefix)], qo_lens=q,
+                     num_qo_heads=8, num_kv_heads=2, head_dim_qk=dk,
+                     head_dim_vo=min(dk, 256), causal=True, seed=25)
+    c = gh.build_oracle_case(w)
+    c.q.zero_()
+    dv = w.head_dim_vo
+    vq, vs = ref.quantize(np.ones((1, 2, dv)))
+    slots = synth.token_slots(w, c.pt)
+    pages, offs = slots // 16, slots % 16
+    vd = c.v_pool.data.cpu().numpy()
+    vsf = c.v_pool.sf.cpu().numpy()
+    vd[pages, :, offs] = vq[0]
+    vsf[pages, :, offs] = vs[0]
+    c.v_pool.data.copy_(torch.from_numpy(vd))
+    c.v_pool.sf.copy_(torch.from_numpy(vsf))
+    o, lse = gh.run_gpu(c, gh.make_plan(w, chunk))
+    if chunk == -1:
+        assert np.all(o == 1.03125)
+    else:
+        # split rows pass through the LSE merge, whose fp32 weights are not exact
+        dev = np.abs(o - 1.03125).max()
+        print(f"merged rows: max |O - 1.03125| = {dev:.3e}", flush=True)
+        assert dev <= 8 * 2.0 ** -23
+    row = 0
+    for b, (qb, L) in enumerate(zip(q, w.kv_lens)):
+        for i in range(qb):
+            want = math.log(i + 1 + L - qb)
+            assert np.all(np.abs(lse[row] - want) <= 1e-5 * max(1.0, want)), (b, i)
+            row += 1
+
+
 @pytest.mark.parametrize("dk,dv,hq,hkv", [(512, 256, 8, 1), (256, 128, 8, 2), (64, 64, 4, 4),
                                           (128, 128, 32, 8), (512, 128, 4, 1), (512, 64, 8, 2)])
 def test_prefill_head_dims(dk, dv, hq, hkv):
