@@ -57,8 +57,10 @@ CALIB_BYTES = 1 << 30
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    # defaults: about 50 ms of timed decode steps after the clocks and queues have
+    # reached their steady state (10 warmup steps measured 3-4 % below it)
+    p.add_argument("--steps", type=int, default=500)
+    p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--workload", default="batch_decode")
     p.add_argument("--pool-sets", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -201,7 +203,7 @@ def timed_passes(torch, nv, run, merge, iters):
             float(np.mean([he.ms(e[2], e[3]) for e in ev])))
 
 
-def extra_decode(torch, nv, paged, synth, name, iters=20):
+def extra_decode(torch, nv, paged, synth, name, iters=100, warm=20):
     w = synth.workload(name)
     case = paged.build_case(w, keep_sources=False)
     plan = paged.make_plan(case)
@@ -213,7 +215,7 @@ def extra_decode(torch, nv, paged, synth, name, iters=20):
     run = nv.batch_decode(plan, case.q, case.page_table, case.k_pool, case.v_pool, w.sm_scale,
                           ws, out=o, lse=lse, prepare=True)
     merge = nv.merge_partials(plan, ws, o, lse, prepare=True)
-    for _ in range(3):
+    for _ in range(warm):
         run()
         merge()
     run_ms, merge_ms = timed_passes(torch, nv, run, merge, iters)
@@ -229,7 +231,7 @@ def extra_decode(torch, nv, paged, synth, name, iters=20):
             "chunk": info["kv_chunk_tokens"], "work_items": info["num_work_items"]}
 
 
-def extra_prefill(torch, nv, paged, synth, name, iters=10):
+def extra_prefill(torch, nv, paged, synth, name, iters=40, warm=10):
     w = synth.workload(name)
     case = paged.build_case(w, keep_sources=False)
     plan = paged.make_plan(case)
@@ -241,7 +243,7 @@ def extra_prefill(torch, nv, paged, synth, name, iters=10):
     run = nv.batch_prefill(plan, case.q, case.page_table, case.k_pool, case.v_pool, w.sm_scale,
                            ws, out=o, lse=lse, prepare=True)
     merge = nv.merge_partials(plan, ws, o, lse, prepare=True)
-    for _ in range(3):
+    for _ in range(warm):
         run()
         merge()
     run_ms, merge_ms = timed_passes(torch, nv, run, merge, iters)
@@ -577,7 +579,8 @@ def main():
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     ms_step = dt * 1e3 / args.steps
-    attn_ms = float(np.mean([he.ms(e[0], e[1]) for e in ev]))
+    launch_ms = np.array([he.ms(e[0], e[1]) for e in ev])
+    attn_ms = float(np.mean(launch_ms))
     # breakdown, after the timed steps
     merge_ms = d.merge_ms(max(args.steps // 2, 3))
     unfused_ms = d.unfused_step_ms(max(args.steps // 2, 3))
@@ -611,6 +614,9 @@ def main():
                      "traffic": recorded_traffic(w.name),
                      "kernel": f"decode_ring_kernel<{w.head_dim_qk}, {w.head_dim_vo}, true>",
                      "bytes_per_launch": kv + qo, "avg_launch_ms": round(attn_ms, 5)},
+        "kernel_ms_percentiles": {"p10": round(float(np.percentile(launch_ms, 10)), 5),
+                                  "p50": round(float(np.percentile(launch_ms, 50)), 5),
+                                  "p90": round(float(np.percentile(launch_ms, 90)), 5)},
         "step_breakdown_ms": {"append_and_attention": round(attn_ms, 5),
                               "merge": round(merge_ms, 5),
                               "unfused_step_gpu": round(unfused_ms, 5)},
