@@ -433,9 +433,10 @@ struct ShiftRef {
   __device__ __forceinline__ void init() { negr = f32x4{0.f, 0.f, 0.f, 0.f}; }
 };
 
-// Under a wave-uniform branch taken when some lane passed its threshold: moves the
-// reference of the rows whose largest score passed it, rescales their accumulators and
-// row sums, and shifts this step's x to the new reference.
+// Under a wave-uniform branch taken when some lane of the group voted (see ShiftRef):
+// moves the reference of the rows whose largest score passed the slack, or that had
+// none, rescales their accumulators and row sums, and shifts this step's x to the new
+// reference.
 template <int NT>
 __device__ __forceinline__ void raise_shifted(RowState<NT, AccForm::VGPR>& st, ShiftRef& sr,
                                               float bm, float (&x)[8]) {
