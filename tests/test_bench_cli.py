@@ -55,3 +55,36 @@ def test_traffic_is_scaled_by_the_calibration_copy(tmp_path):
     assert rec["write_scale"] == pytest.approx(1.0)
     assert rec["bytes_per_launch"] == round((1001.0 * 2 + 10.0) * 1024)
     assert rec["kernel"].startswith("decode_ring_kernel<128, 128, true>")
+
+
+def test_counter_summary_derivations(tmp_path):
+    """Derived figures of the SQ counter summary on synthetic passes: a kernel of 1 ms
+    (2.4 M cycles at the nominal clock) on 1024 SIMDs whose MFMAs keep the matrix
+    units busy 25 % of the time."""
+    cyc = 1e-3 * bench.CLOCK_GHZ * 1e9
+    mfma = 1000.0
+    counters = {"SQ_VALU_MFMA_BUSY_CYCLES": 0.25 * bench.SIMDS * cyc, "SQ_INSTS_MFMA": mfma,
+                "SQ_INSTS_VALU": 4 * mfma, "SQ_INSTS_SALU": 2 * mfma,
+                "SQ_WAVE_CYCLES": 18 * mfma}
+    d = tmp_path / "p" / "host"
+    d.mkdir(parents=True)
+    with open(d / "run_counter_collection.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name",
+                                          "Counter_Value", "Start_Timestamp", "End_Timestamp",
+                                          "Grid_Size"])
+        w.writeheader()
+        for c, v in counters.items():
+            w.writerow({"Dispatch_Id": 1, "Kernel_Name": "prefill_coop_kernel<128, 128>",
+                        "Counter_Name": c, "Counter_Value": v, "Start_Timestamp": 0,
+                        "End_Timestamp": 1_000_000, "Grid_Size": 64 * 10})
+    out = tmp_path / "s.txt"
+    args = types.SimpleNamespace(summarize_counters=[str(tmp_path / "p")], kernel="prefill_coop_kernel",
+                                 workload="w", command="synthetic", out=str(out))
+    bench.summarize_counters(args)
+    der = __import__("json").loads(out.read_text().strip().splitlines()[-1])["derived"]
+    assert der["mfma_busy_share"] == pytest.approx(0.25, rel=1e-4)
+    assert der["mfma_per_wave"] == pytest.approx(mfma / 10)
+    assert der["other_valu_per_mfma"] == pytest.approx(3.0)
+    assert der["sq_insts_salu_per_mfma"] == pytest.approx(2.0)
+    # wave cycles count in units of four cycles
+    assert der["sq_wave_cycles_cycles_per_mfma"] == pytest.approx(72.0)
