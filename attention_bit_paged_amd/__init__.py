@@ -30,9 +30,33 @@ def _ptr(t: Optional[torch.Tensor]):
     return ctypes.c_void_p(0 if t is None else t.data_ptr())
 
 
-def _stream(stream) -> ctypes.c_void_p:
+def _device(*tensors) -> torch.device:
+    """The one GPU every given tensor lives on (None entries are skipped).  The kernels
+    dereference these pointers on the device: a host tensor, or one on another GPU,
+    would fault there, so it is refused here, before any library call."""
+    dev = None
+    for t in tensors:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("every tensor passed to the library must be a GPU tensor "
+                             f"(got one on {t.device})")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"tensors on different devices: {dev} and {t.device}")
+    if dev is None:
+        raise ValueError("no GPU tensor given")
+    return dev
+
+
+def _stream(stream, device: Optional[torch.device] = None) -> ctypes.c_void_p:
+    """The stream to launch on: by default the current stream of ``device``; a given
+    stream must belong to ``device``."""
     if stream is None:
-        stream = torch.cuda.current_stream()
+        stream = torch.cuda.current_stream(device)
+    elif device is not None and stream.device != device:
+        raise ValueError(f"stream is on {stream.device}, the tensors on {device}")
     return ctypes.c_void_p(stream.cuda_stream)
 
 
@@ -54,6 +78,10 @@ class KVPool:
             raise ValueError(f"layout must be HND or NHD, got {layout!r}")
         if data.stride(-1) != 1 or sf.stride(-1) != 1:
             raise ValueError("the last pool dimension must be contiguous")
+        if tuple(data.shape[:3]) != tuple(sf.shape[:3]):
+            raise ValueError("pool data and scales must have the same leading dims")
+        if data.device != sf.device:
+            raise ValueError("pool data and scales must be on one device")
         self.data, self.sf, self.layout = data, sf, layout
         self.head_dim = int(head_dim)
         self.global_scale = float(global_scale)
@@ -113,19 +141,32 @@ def quantize_kv(k: Optional[torch.Tensor], v: Optional[torch.Tensor], slot_mappi
                 prepare: bool = False):
     """Quantise bf16 K/V rows ``[n_tokens, H, D]`` into their pools at ``slot_mapping``
     (int64 ``page * page_size + offset``; negative = skip)."""
+    if (k is None) != (k_pool is None) or (v is None) != (v_pool is None):
+        raise ValueError("each source needs its pool and each pool its source")
+    if k is None and v is None:
+        raise ValueError("nothing to quantise")
     n = (k if k is not None else v).shape[0]
-    for t in (k, v):
-        if t is not None and (t.dtype != torch.bfloat16 or t.dim() != 3 or t.stride(-1) != 1):
-            raise ValueError("K/V sources must be bf16 [n_tokens, heads, head_dim], last dim contiguous")
-    if slot_mapping.dtype != torch.int64 or slot_mapping.numel() < n:
-        raise ValueError("slot_mapping must be int64 with one entry per token")
+    for name, t, pool in (("k", k, k_pool), ("v", v, v_pool)):
+        if t is None:
+            continue
+        if t.dtype != torch.bfloat16 or t.dim() != 3 or t.stride(-1) != 1:
+            raise ValueError(f"{name} must be bf16 [n_tokens, heads, head_dim], last dim contiguous")
+        # the kernel reads n_tokens x heads x head_dim elements of each source
+        if tuple(t.shape) != (n, pool.num_kv_heads, pool.head_dim):
+            raise ValueError(f"{name} must have shape ({n}, {pool.num_kv_heads}, {pool.head_dim}) "
+                             f"to match its pool, got {tuple(t.shape)}")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.dim() != 1 \
+            or slot_mapping.numel() != n or not slot_mapping.is_contiguous():
+        raise ValueError("slot_mapping must be a contiguous int64 vector with one entry per token")
+    dev = _device(k, v, slot_mapping, *(p.data for p in (k_pool, v_pool) if p is not None),
+                  *(p.sf for p in (k_pool, v_pool) if p is not None))
     ks = k_pool.struct() if k_pool is not None else None
     vs = v_pool.struct() if v_pool is not None else None
     args = (_ptr(k), k.stride(0) if k is not None else 0, k.stride(1) if k is not None else 0,
             _ptr(v), v.stride(0) if v is not None else 0, v.stride(1) if v is not None else 0,
             n, _ptr(slot_mapping),
             ctypes.byref(ks) if ks is not None else None,
-            ctypes.byref(vs) if vs is not None else None, _stream(stream))
+            ctypes.byref(vs) if vs is not None else None, _stream(stream, dev))
     if prepare:
         return Prepared(lib.nvfp4_quantize_kv, args, (k, v, slot_mapping, k_pool, v_pool, ks, vs))
     check(lib.nvfp4_quantize_kv(*args))
@@ -140,8 +181,14 @@ class Plan:
     def __init__(self, kv_lens: Sequence[int], *, num_qo_heads: int, num_kv_heads: int,
                  head_dim_qk: int, head_dim_vo: Optional[int] = None, page_size: int = 16,
                  qo_indptr: Optional[Sequence[int]] = None, causal: bool = False,
-                 kv_chunk_tokens: int = 0, num_cus: int = 0):
+                 kv_chunk_tokens: int = 0, num_cus: int = 0, device=None):
+        """``num_cus`` 0 fills the compute units of ``device`` (default: the current
+        device when a GPU is present, else the library's default of 256)."""
         head_dim_vo = head_dim_qk if head_dim_vo is None else head_dim_vo
+        if num_cus == 0 and torch.cuda.is_available():
+            num_cus = torch.cuda.get_device_properties(
+                torch.device("cuda") if device is None else torch.device(device)
+            ).multi_processor_count
         self._kv = np.ascontiguousarray(np.asarray(kv_lens, dtype=np.int32))
         self._ind = None if qo_indptr is None else np.ascontiguousarray(
             np.asarray(qo_indptr, dtype=np.int32))
@@ -189,47 +236,87 @@ class Plan:
         return torch.empty(self.workspace_bytes, dtype=torch.uint8, device=device)
 
     def upload(self, workspace: torch.Tensor, stream=None) -> None:
-        check(lib.nvfp4_plan_upload(self._h, _ptr(workspace), workspace.numel(), _stream(stream)))
+        _check_workspace(self, workspace)
+        check(lib.nvfp4_plan_upload(self._h, _ptr(workspace), workspace.numel(),
+                                    _stream(stream, _device(workspace))))
+
+    @property
+    def total_rows(self) -> int:
+        """Query rows of the batch: one per request (decode) or qo_indptr[-1]."""
+        return self.batch if self._ind is None else int(self._ind[-1])
+
+    def max_pages(self) -> int:
+        """Page-table columns the longest request needs."""
+        if self.batch == 0:
+            return 0
+        return int(max(-(-int(l) // self.page_size) for l in self._kv))
 
     def set_deferred_merge(self, deferred: bool = True) -> None:
         """Runs leave split rows' partials for ``merge_partials`` (nvfp4_plan_set_deferred_merge)."""
         check(lib.nvfp4_plan_set_deferred_merge(self._h, int(bool(deferred))))
 
 
+def _check_workspace(plan: Plan, ws: torch.Tensor):
+    if ws.dtype != torch.uint8 or ws.dim() != 1 or not ws.is_contiguous() \
+            or ws.numel() < plan.workspace_bytes:
+        raise ValueError(f"workspace must be a contiguous uint8 vector of at least "
+                         f"{plan.workspace_bytes} bytes")
+
+
+def _check_outputs(plan: Plan, out, lse):
+    """out fp32 [rows, Hq, Dv] with a contiguous last dim, lse fp32 [rows, Hq] contiguous."""
+    rows = plan.total_rows
+    for name, t, shape in (("out", out, (rows, plan.num_qo_heads, plan.head_dim_vo)),
+                           ("lse", lse, (rows, plan.num_qo_heads))):
+        if t is not None and tuple(t.shape) != shape:
+            raise ValueError(f"{name} must have shape {shape}")
+    if out is not None and (out.dtype != torch.float32 or out.stride(-1) != 1):
+        raise ValueError("out must be fp32 with a contiguous last dim")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("lse must be fp32 and contiguous")
+
+
 def _check_rows(plan: Plan, q, page_table, out, lse):
     """Shapes the C library cannot see (it takes pointers): q, page table and outputs
     must cover the plan's rows, or the kernels would read or write past them."""
-    rows = plan.batch if plan._ind is None else int(plan._ind[-1])
+    rows = plan.total_rows
     if q.dtype != torch.bfloat16 or q.dim() != 3 or q.stride(-1) != 1 \
             or tuple(q.shape) != (rows, plan.num_qo_heads, plan.head_dim_qk):
         raise ValueError(f"q must be bf16 [{rows}, {plan.num_qo_heads}, {plan.head_dim_qk}] "
                          "with a contiguous last dim")
     if page_table.dtype != torch.int32 or page_table.dim() != 2 or page_table.stride(1) != 1 \
-            or page_table.shape[0] < plan.batch:
-        raise ValueError(f"page_table must be int32 [>= {plan.batch}, max_pages] with "
-                         "contiguous rows")
-    for name, t, shape in (("out", out, (rows, plan.num_qo_heads, plan.head_dim_vo)),
-                           ("lse", lse, (rows, plan.num_qo_heads))):
-        if t is not None and tuple(t.shape) != shape:
-            raise ValueError(f"{name} must have shape {shape}")
+            or page_table.shape[0] < plan.batch or page_table.shape[1] < plan.max_pages():
+        raise ValueError(f"page_table must be int32 [>= {plan.batch}, >= {plan.max_pages()}] "
+                         "with contiguous rows")
+    _check_outputs(plan, out, lse)
     return rows
+
+
+def _check_pools(plan: Plan, k_pool: "KVPool", v_pool: "KVPool"):
+    for name, p, d in (("k_pool", k_pool, plan.head_dim_qk), ("v_pool", v_pool, plan.head_dim_vo)):
+        if p.head_dim != d or p.num_kv_heads != plan.num_kv_heads or p.page_size != plan.page_size:
+            raise ValueError(f"{name} is (heads {p.num_kv_heads}, page {p.page_size}, dim "
+                             f"{p.head_dim}); the plan needs ({plan.num_kv_heads}, "
+                             f"{plan.page_size}, {d})")
 
 
 def _attn(fn, plan: Plan, q, page_table, k_pool, v_pool, sm_scale, workspace, out, lse, stream,
           prepare=False):
     rows = _check_rows(plan, q, page_table, out, lse)
+    _check_pools(plan, k_pool, v_pool)
+    _check_workspace(plan, workspace)
+    dev = _device(q, page_table, k_pool.data, k_pool.sf, v_pool.data, v_pool.sf, workspace, out,
+                  lse)
     if out is None:
         out = torch.empty((rows, plan.num_qo_heads, plan.head_dim_vo), dtype=torch.float32,
-                          device=q.device)
+                          device=dev)
     if lse is None:
-        lse = torch.empty((rows, plan.num_qo_heads), dtype=torch.float32, device=q.device)
-    if out.dtype != torch.float32 or out.stride(-1) != 1 or lse.dtype != torch.float32 \
-            or not lse.is_contiguous():
-        raise ValueError("out must be fp32 with a contiguous last dim; lse fp32 contiguous")
+        lse = torch.empty((rows, plan.num_qo_heads), dtype=torch.float32, device=dev)
     ks, vs = k_pool.struct(), v_pool.struct()
     args = (plan.handle, _ptr(q), q.stride(0), q.stride(1), _ptr(page_table), page_table.stride(0),
             ctypes.byref(ks), ctypes.byref(vs), float(sm_scale), _ptr(workspace),
-            workspace.numel(), _ptr(out), out.stride(0), out.stride(1), _ptr(lse), _stream(stream))
+            workspace.numel(), _ptr(out), out.stride(0), out.stride(1), _ptr(lse),
+            _stream(stream, dev))
     if prepare:
         return Prepared(fn, args, (plan, q, page_table, k_pool, v_pool, ks, vs, workspace, out, lse))
     check(fn(*args))
@@ -259,20 +346,21 @@ def batch_decode_append(plan: Plan, q: torch.Tensor, k_new: torch.Tensor, v_new:
             raise ValueError(f"{name} must be bf16 [{plan.batch}, {plan.num_kv_heads}, {d}] "
                              "with a contiguous last dim")
     rows = _check_rows(plan, q, page_table, out, lse)
+    _check_pools(plan, k_pool, v_pool)
+    _check_workspace(plan, workspace)
+    dev = _device(q, k_new, v_new, page_table, k_pool.data, k_pool.sf, v_pool.data, v_pool.sf,
+                  workspace, out, lse)
     if out is None:
         out = torch.empty((rows, plan.num_qo_heads, plan.head_dim_vo), dtype=torch.float32,
-                          device=q.device)
+                          device=dev)
     if lse is None:
-        lse = torch.empty((rows, plan.num_qo_heads), dtype=torch.float32, device=q.device)
-    if out.dtype != torch.float32 or out.stride(-1) != 1 or lse.dtype != torch.float32 \
-            or not lse.is_contiguous():
-        raise ValueError("out must be fp32 with a contiguous last dim; lse fp32 contiguous")
+        lse = torch.empty((rows, plan.num_qo_heads), dtype=torch.float32, device=dev)
     ks, vs = k_pool.struct(), v_pool.struct()
     args = (plan.handle, _ptr(q), q.stride(0), q.stride(1), _ptr(k_new), k_new.stride(0),
             k_new.stride(1), _ptr(v_new), v_new.stride(0), v_new.stride(1), _ptr(page_table),
             page_table.stride(0), ctypes.byref(ks), ctypes.byref(vs), float(sm_scale),
             _ptr(workspace), workspace.numel(), _ptr(out), out.stride(0), out.stride(1),
-            _ptr(lse), _stream(stream))
+            _ptr(lse), _stream(stream, dev))
     if prepare:
         return Prepared(lib.nvfp4_batch_decode_append, args,
                         (plan, q, k_new, v_new, page_table, k_pool, v_pool, ks, vs, workspace,
@@ -294,11 +382,13 @@ def batch_prefill(plan: Plan, q: torch.Tensor, page_table: torch.Tensor, k_pool:
 def merge_partials(plan: Plan, workspace: torch.Tensor, out: torch.Tensor, lse: torch.Tensor,
                    stream=None, prepare: bool = False):
     """Write the split rows of a deferred-merge run into out / lse (nvfp4_merge_partials)."""
-    if out.dtype != torch.float32 or out.dim() != 3 or out.stride(-1) != 1 \
-            or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("out must be fp32 [rows, heads, Dv] with a contiguous last dim; lse fp32")
+    if out is None or lse is None:
+        raise ValueError("out and lse are the run's outputs and must be given")
+    _check_outputs(plan, out, lse)
+    _check_workspace(plan, workspace)
+    dev = _device(workspace, out, lse)
     args = (plan.handle, _ptr(workspace), workspace.numel(), _ptr(out), out.stride(0),
-            out.stride(1), _ptr(lse), _stream(stream))
+            out.stride(1), _ptr(lse), _stream(stream, dev))
     if prepare:
         return Prepared(lib.nvfp4_merge_partials, args, (plan, workspace, out, lse))
     check(lib.nvfp4_merge_partials(*args))
@@ -306,14 +396,24 @@ def merge_partials(plan: Plan, workspace: torch.Tensor, out: torch.Tensor, lse: 
 
 
 def merge_states(o_parts: torch.Tensor, lse_parts: torch.Tensor, out=None, lse=None, stream=None):
-    """Merge partial states: o_parts fp32 [rows, n, H, D], lse_parts fp32 [rows, n, H]."""
+    """Merge partial states: o_parts fp32 [rows, n, H, D], lse_parts fp32 [rows, n, H]
+    (both contiguous); out fp32 [rows, H, D] and lse fp32 [rows, H], contiguous."""
+    if o_parts.dim() != 4 or o_parts.dtype != torch.float32 or lse_parts.dtype != torch.float32:
+        raise ValueError("o_parts must be fp32 [rows, n, H, D] and lse_parts fp32 [rows, n, H]")
+    if tuple(lse_parts.shape) != tuple(o_parts.shape[:3]):
+        raise ValueError(f"lse_parts must have shape {tuple(o_parts.shape[:3])}")
     if not (o_parts.is_contiguous() and lse_parts.is_contiguous()):
         raise ValueError("o_parts and lse_parts must be contiguous")
     rows, n, h, d = o_parts.shape
+    for name, t, shape in (("out", out, (rows, h, d)), ("lse", lse, (rows, h))):
+        if t is not None and (tuple(t.shape) != shape or t.dtype != torch.float32
+                              or not t.is_contiguous()):
+            raise ValueError(f"{name} must be contiguous fp32 of shape {shape}")
+    dev = _device(o_parts, lse_parts, out, lse)
     if out is None:
-        out = torch.empty((rows, h, d), dtype=torch.float32, device=o_parts.device)
+        out = torch.empty((rows, h, d), dtype=torch.float32, device=dev)
     if lse is None:
-        lse = torch.empty((rows, h), dtype=torch.float32, device=o_parts.device)
+        lse = torch.empty((rows, h), dtype=torch.float32, device=dev)
     check(lib.nvfp4_merge_states(_ptr(o_parts), _ptr(lse_parts), rows, n, h, d, _ptr(out),
-                                 _ptr(lse), _stream(stream)))
+                                 _ptr(lse), _stream(stream, dev)))
     return out, lse

@@ -53,6 +53,7 @@ nvfp4_status ok() {
 }
 
 constexpr size_t kAlign = 256;
+constexpr size_t kLdsBytesPerCu = 160 * 1024;  // gfx950
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
@@ -63,14 +64,29 @@ int log2i(int64_t x) {
 }
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// ---- device check: gfx950 only, cached per device ordinal
+// ---- device check: gfx950 only, cached per device ordinal.  The device is the one the
+// call's stream belongs to (the null stream: the current device), not whatever device
+// happens to be current ([XQA] review: the capability check must look at the device the
+// tensors are on, not at a default device).
 std::mutex g_dev_mu;
 int g_dev_state[64];  // 0 unknown, 1 gfx950, 2 other
 
-nvfp4_status check_device() {
+nvfp4_status stream_device(void* stream, int* dev) {
+  *dev = -1;
+  hipError_t e = stream ? hipStreamGetDevice(static_cast<hipStream_t>(stream), dev)
+                        : hipGetDevice(dev);
+  if (e != hipSuccess || *dev < 0) {
+    (void)hipGetLastError();
+    return fail(NVFP4_E_DEVICE, stream ? "cannot query the device of the stream: %s"
+                                       : "no HIP device is current: %s",
+                hipGetErrorString(e));
+  }
+  return NVFP4_OK;
+}
+
+nvfp4_status check_device(void* stream) {
   int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0)
-    return fail(NVFP4_E_DEVICE, "no HIP device is current");
+  if (nvfp4_status st = stream_device(stream, &dev)) return st;
   if (dev >= 64) return fail(NVFP4_E_DEVICE, "device ordinal %d out of range", dev);
   std::lock_guard<std::mutex> lk(g_dev_mu);
   if (g_dev_state[dev] == 0) {
@@ -192,15 +208,27 @@ nvfp4_status nvfp4_plan_create(const int32_t* kv_lens, const int32_t* qo_indptr,
     return fail(NVFP4_E_UNSUPPORTED, "head dims (qk %d, vo %d): each must be 64, 128, 256 or 512",
                 head_dim_qk, head_dim_vo);
   const bool prefill = qo_indptr != nullptr;
-  if (head_dim_qk == 512 && head_dim_vo == 512)
-    return fail(NVFP4_E_LDS_BUDGET,
-                "head dims (512, 512): the per-wave tile does not fit the register file");
-  if (prefill ? !prefill_supported(head_dim_qk, head_dim_vo)
-              : !decode_supported(head_dim_qk, head_dim_vo))
-    return fail(NVFP4_E_UNSUPPORTED, "head dims (qk %d, vo %d) not supported (need vo <= qk)",
-                head_dim_qk, head_dim_vo);
   if (!is_pow2(page_size) || page_size > 256)
     return fail(NVFP4_E_UNSUPPORTED, "page_size %d is not a power of two in [1, 256]", page_size);
+  if (head_dim_vo > head_dim_qk)
+    return fail(NVFP4_E_UNSUPPORTED, "head dims (qk %d, vo %d) not supported (need vo <= qk)",
+                head_dim_qk, head_dim_vo);
+  // on-chip budget ([PF] commit "Re-enable split-KV...": a tile that does not fit the
+  // on-chip memory is rejected at plan time): the LDS the resident workgroups of this
+  // shape's kernel need, then the register file
+  const size_t lds = prefill ? prefill_lds_bytes(head_dim_qk, head_dim_vo, page_size)
+                             : decode_lds_bytes(head_dim_qk, head_dim_vo, page_size);
+  if (lds > kLdsBytesPerCu)
+    return fail(NVFP4_E_LDS_BUDGET, "%s tile for head dims (%d, %d) needs %zu bytes of LDS per CU, "
+                "more than the %zu a CU has", prefill ? "prefill" : "decode", head_dim_qk,
+                head_dim_vo, lds, kLdsBytesPerCu);
+  if (head_dim_qk == 512 && head_dim_vo == 512)
+    return fail(NVFP4_E_LDS_BUDGET,
+                "head dims (512, 512): the per-wave decode tile does not fit the register file");
+  if (prefill ? !prefill_supported(head_dim_qk, head_dim_vo)
+              : !decode_supported(head_dim_qk, head_dim_vo))
+    return fail(NVFP4_E_UNSUPPORTED, "head dims (qk %d, vo %d) not supported", head_dim_qk,
+                head_dim_vo);
   if (kv_chunk_tokens > 0 && kv_chunk_tokens % 16)
     return fail(NVFP4_E_INVALID, "kv_chunk_tokens %d is not a multiple of 16", kv_chunk_tokens);
   if (num_cus < 0) return fail(NVFP4_E_INVALID, "num_cus must be >= 0");
@@ -213,9 +241,6 @@ nvfp4_status nvfp4_plan_create(const int32_t* kv_lens, const int32_t* qo_indptr,
   if (prefill && group > rows_item)
     return fail(NVFP4_E_UNSUPPORTED, "prefill supports at most %d qo heads per kv head, got %d",
                 rows_item, group);
-  if (prefill && prefill_lds_bytes(head_dim_qk, head_dim_vo) > 160 * 1024)
-    return fail(NVFP4_E_LDS_BUDGET, "prefill tile for (%d, %d) exceeds 160 KiB of LDS",
-                head_dim_qk, head_dim_vo);
 
   for (int b = 0; b < batch; ++b) {
     if (kv_lens[b] < 0) return fail(NVFP4_E_INVALID, "kv_lens[%d] = %d is negative", b, kv_lens[b]);
@@ -414,7 +439,7 @@ nvfp4_status nvfp4_plan_upload(nvfp4_plan* plan, void* workspace, size_t workspa
   if (workspace_bytes < plan->ws_bytes)
     return fail(NVFP4_E_WORKSPACE, "workspace has %zu bytes, plan needs %zu", workspace_bytes,
                 plan->ws_bytes);
-  if (nvfp4_status st = check_device()) return st;
+  if (nvfp4_status st = check_device(stream)) return st;
   // One host staging buffer for the tables, then one copy.
   std::vector<uint8_t> host(plan->off_part_o, 0);
   auto put = [&](size_t off, const std::vector<int32_t>& v) {
@@ -442,7 +467,7 @@ nvfp4_status check_run(const nvfp4_plan* plan, bool prefill, const void* q, int6
                        int64_t q_s_head, const int32_t* page_table, int64_t pt_stride,
                        const nvfp4_kv_pool* k, const nvfp4_kv_pool* v, float sm_scale,
                        void* ws, size_t ws_bytes, float* o, int64_t o_s_row, int64_t o_s_head,
-                       float* lse) {
+                       float* lse, void* stream) {
   if (!plan) return fail(NVFP4_E_INVALID, "plan is NULL");
   if (plan->prefill != (int)prefill)
     return fail(NVFP4_E_SHAPE, "plan was made for %s, called for %s",
@@ -479,7 +504,7 @@ nvfp4_status check_run(const nvfp4_plan* plan, bool prefill, const void* q, int6
                 plan->ws_bytes);
   if (plan->uploaded_to != ws)
     return fail(NVFP4_E_WORKSPACE, "the plan was not uploaded to this workspace (nvfp4_plan_upload)");
-  return check_device();
+  return check_device(stream);
 }
 
 AttnArgs make_args(const nvfp4_plan* plan, const void* q, int64_t q_s_row, int64_t q_s_head,
@@ -524,7 +549,7 @@ nvfp4_status run(const nvfp4_plan* plan, bool prefill, const void* q, int64_t q_
                  size_t ws_bytes, float* o, int64_t o_s_row, int64_t o_s_head, float* lse,
                  void* stream) {
   if (nvfp4_status st = check_run(plan, prefill, q, q_s_row, q_s_head, page_table, pt_stride, k,
-                                  v, sm_scale, ws, ws_bytes, o, o_s_row, o_s_head, lse))
+                                  v, sm_scale, ws, ws_bytes, o, o_s_row, o_s_head, lse, stream))
     return st;
   if (plan->work.empty()) return ok();
   const AttnArgs a = make_args(plan, q, q_s_row, q_s_head, page_table, pt_stride, k, v, sm_scale,
@@ -586,7 +611,7 @@ nvfp4_status nvfp4_batch_decode_append(const nvfp4_plan* plan, const void* q,
     return fail(NVFP4_E_SHAPE, "v_new rows must be 16-byte aligned (strides multiples of 8)");
   if (nvfp4_status st = check_run(plan, false, q, q_stride_req, q_stride_head, page_table,
                                   pt_stride, k_pool, v_pool, sm_scale, workspace,
-                                  workspace_bytes, o, o_stride_req, o_stride_head, lse))
+                                  workspace_bytes, o, o_stride_req, o_stride_head, lse, stream))
     return st;
   if (plan->work.empty()) return ok();
   AttnArgs a = make_args(plan, q, q_stride_req, q_stride_head, page_table, pt_stride, k_pool,
@@ -653,7 +678,7 @@ nvfp4_status nvfp4_merge_partials(const nvfp4_plan* plan, void* workspace, size_
       o_stride_head < 0)
     return fail(NVFP4_E_SHAPE, "o rows must be 16-byte aligned (strides multiples of 4 elements)");
   if (!aligned(lse, 4)) return fail(NVFP4_E_SHAPE, "lse must be 4-byte aligned");
-  if (nvfp4_status st = check_device()) return st;
+  if (nvfp4_status st = check_device(stream)) return st;
   AttnArgs a;
   std::memset(&a, 0, sizeof(a));
   uint8_t* w = static_cast<uint8_t*>(workspace);
@@ -687,7 +712,7 @@ nvfp4_status nvfp4_merge_states(const float* o_parts, const float* lse_parts, in
     return fail(NVFP4_E_INVALID, "o_parts, lse_parts, o and lse must be non-NULL");
   if (!aligned(o_parts, 16) || !aligned(o, 16) || !aligned(lse_parts, 4) || !aligned(lse, 4))
     return fail(NVFP4_E_SHAPE, "o_parts and o must be 16-byte aligned");
-  if (nvfp4_status st = check_device()) return st;
+  if (nvfp4_status st = check_device(stream)) return st;
   hipError_t e = launch_merge_states(o_parts, lse_parts, rows, num_parts, heads, head_dim, o, lse,
                                      static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(NVFP4_E_HIP, "merge launch failed: %s", hipGetErrorString(e));
@@ -725,7 +750,7 @@ nvfp4_status nvfp4_quantize_kv(const void* k_src, int64_t k_stride_token, int64_
     return fail(NVFP4_E_SHAPE, "v_src rows must be 16-byte aligned (strides multiples of 8)");
   if (n_tokens == 0) return ok();
   if (!slot_mapping) return fail(NVFP4_E_INVALID, "slot_mapping is NULL");
-  if (nvfp4_status st = check_device()) return st;
+  if (nvfp4_status st = check_device(stream)) return st;
   auto qa = [](const void* src, int64_t st, int64_t sh, const nvfp4_kv_pool* p) {
     QuantArgs a;
     a.src = static_cast<const uint16_t*>(src);

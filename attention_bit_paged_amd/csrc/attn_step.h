@@ -52,10 +52,9 @@ struct StepRaw {
 // Per-wave view of one request's K/V pools for one kv head.
 //
 // PAGE16 (page_size >= 16): the two 16-token halves of a step each lie inside one page,
-// so a step needs two page-table entries (uniform, scalar loads) and every lane's byte
-// offset inside a half is fixed for the whole loop.  A half that starts after the
-// last key reuses the first half's page: its reads stay inside a valid page and are
-// masked.  Otherwise (page_size < 16) every token is looked up on its own.
+// so a step needs two page-table entries (uniform, scalar loads); the ring kernels
+// take their copy bases from this view.  Otherwise (page_size < 16) load() looks every
+// token up on its own.
 template <int DK, int DV, bool PAGE16>
 struct PagedView {
   using S = StepShape<DK, DV>;
@@ -66,10 +65,6 @@ struct PagedView {
   const uint8_t* vdat;
   const uint8_t* vsf;
   int64_t k_page, k_tok, ksf_page, ksf_tok, v_page, v_tok, vsf_page, vsf_tok;
-  // PAGE16: lane offsets inside a 16-token half
-  uint32_t ka_off, kb_off, ksa_off, ksb_off;
-  uint32_t v_off[8], vs_off[8];
-  bool k_hi, v_hi;
   int j, n;
   uint32_t bad;
 
@@ -87,24 +82,10 @@ struct PagedView {
     k_page = a.k.s_page; k_tok = a.k.s_tok; ksf_page = a.k.sf_page; ksf_tok = a.k.sf_tok;
     v_page = a.v.s_page; v_tok = a.v.s_tok; vsf_page = a.v.sf_page; vsf_tok = a.v.sf_tok;
     bad = 0;
-    const int da = 8 * (n >> 2) + (n & 3);  // token of tile A row n inside the step
-    k_hi = da >= 16;
-    v_hi = j >= 2;
-    if constexpr (PAGE16) {
-      const int sa = da & 15, sb = (da + 4) & 15;
-      ka_off = (uint32_t)(sa * k_tok) + j * S::KB;
-      kb_off = (uint32_t)(sb * k_tok) + j * S::KB;
-      ksa_off = (uint32_t)(sa * ksf_tok) + j * S::KSF;
-      ksb_off = (uint32_t)(sb * ksf_tok) + j * S::KSF;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int t = 8 * (j & 1) + i;
-        v_off[i] = (uint32_t)(t * v_tok) + n * S::VB;
-        vs_off[i] = (uint32_t)(t * vsf_tok) + (n * DV / 16) / 16;
-      }
-    }
   }
 
+  // A page-table entry; one outside [0, num_pages) marks the view bad and reads page 0
+  // instead, so no address is ever formed from it.
   __device__ __forceinline__ int page_of(int idx) {
     int pg = pt_row[idx];
     if ((unsigned)pg >= (unsigned)num_pages) {
@@ -114,52 +95,24 @@ struct PagedView {
     return pg;
   }
 
-  // Raw bytes of the step starting at token t0 (a multiple of 16).  Keys after tlast
-  // are never used; their reads stay inside the request's pages.
+  // Raw bytes of the step starting at token t0 (page_size < 16), every token looked up
+  // on its own.  Keys after tlast are never used; their reads are clamped to tlast.
   __device__ __forceinline__ void load(StepRaw<DK, DV>& r, int t0, int tlast) {
-    if constexpr (PAGE16) {
-      const int pg0 = page_of(t0 >> page_shift);
-      const int64_t s0 = t0 & page_mask;
-      const bool h1 = t0 + 16 <= tlast;
-      const int pg1 = h1 ? page_of((t0 + 16) >> page_shift) : pg0;
-      const int64_t s1 = h1 ? ((t0 + 16) & page_mask) : s0;
-      const uint8_t* kb0 = kdat + pg0 * k_page + s0 * k_tok;
-      const uint8_t* kb1 = kdat + pg1 * k_page + s1 * k_tok;
-      const uint8_t* ks0 = ksf + pg0 * ksf_page + s0 * ksf_tok;
-      const uint8_t* ks1 = ksf + pg1 * ksf_page + s1 * ksf_tok;
-      const uint8_t* vb0 = vdat + pg0 * v_page + s0 * v_tok;
-      const uint8_t* vb1 = vdat + pg1 * v_page + s1 * v_tok;
-      const uint8_t* vs0 = vsf + pg0 * vsf_page + s0 * vsf_tok;
-      const uint8_t* vs1 = vsf + pg1 * vsf_page + s1 * vsf_tok;
-      const uint8_t* kb = k_hi ? kb1 : kb0;
-      const uint8_t* ks = k_hi ? ks1 : ks0;
-      const uint8_t* vb = v_hi ? vb1 : vb0;
-      const uint8_t* vs = v_hi ? vs1 : vs0;
-      load_bytes<S::KB>(kb + ka_off, r.ka);
-      load_bytes<S::KB>(kb + kb_off, r.kb);
-      load_bytes<S::KSF>(ks + ksa_off, r.ksa);
-      load_bytes<S::KSF>(ks + ksb_off, r.ksb);
+    static_assert(!PAGE16, "page_size >= 16 streams through the LDS rings");
+    const int ta = min(t0 + 8 * (n >> 2) + (n & 3), tlast);
+    const int tb = min(t0 + 8 * (n >> 2) + (n & 3) + 4, tlast);
+    const int pga = page_of(ta >> page_shift), pgb = page_of(tb >> page_shift);
+    load_bytes<S::KB>(kdat + pga * k_page + (int64_t)(ta & page_mask) * k_tok + j * S::KB, r.ka);
+    load_bytes<S::KB>(kdat + pgb * k_page + (int64_t)(tb & page_mask) * k_tok + j * S::KB, r.kb);
+    load_bytes<S::KSF>(ksf + pga * ksf_page + (int64_t)(ta & page_mask) * ksf_tok + j * S::KSF, r.ksa);
+    load_bytes<S::KSF>(ksf + pgb * ksf_page + (int64_t)(tb & page_mask) * ksf_tok + j * S::KSF, r.ksb);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        load_bytes<S::VB>(vb + v_off[i], r.vd[i]);
-        load_bytes<S::VSFB>(vs + vs_off[i], &r.vs[i]);
-      }
-    } else {
-      const int ta = min(t0 + 8 * (n >> 2) + (n & 3), tlast);
-      const int tb = min(t0 + 8 * (n >> 2) + (n & 3) + 4, tlast);
-      const int pga = page_of(ta >> page_shift), pgb = page_of(tb >> page_shift);
-      load_bytes<S::KB>(kdat + pga * k_page + (int64_t)(ta & page_mask) * k_tok + j * S::KB, r.ka);
-      load_bytes<S::KB>(kdat + pgb * k_page + (int64_t)(tb & page_mask) * k_tok + j * S::KB, r.kb);
-      load_bytes<S::KSF>(ksf + pga * ksf_page + (int64_t)(ta & page_mask) * ksf_tok + j * S::KSF, r.ksa);
-      load_bytes<S::KSF>(ksf + pgb * ksf_page + (int64_t)(tb & page_mask) * ksf_tok + j * S::KSF, r.ksb);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int t = min(t0 + 8 * j + i, tlast);
-        const int pg = page_of(t >> page_shift);
-        const int64_t sl = t & page_mask;
-        load_bytes<S::VB>(vdat + pg * v_page + sl * v_tok + n * S::VB, r.vd[i]);
-        load_bytes<S::VSFB>(vsf + pg * vsf_page + sl * vsf_tok + (n * DV / 16) / 16, &r.vs[i]);
-      }
+    for (int i = 0; i < 8; ++i) {
+      const int t = min(t0 + 8 * j + i, tlast);
+      const int pg = page_of(t >> page_shift);
+      const int64_t sl = t & page_mask;
+      load_bytes<S::VB>(vdat + pg * v_page + sl * v_tok + n * S::VB, r.vd[i]);
+      load_bytes<S::VSFB>(vsf + pg * vsf_page + sl * vsf_tok + (n * DV / 16) / 16, &r.vs[i]);
     }
   }
 };

@@ -34,6 +34,14 @@ struct DecodeOcc {
   static constexpr int BY_LDS = (160 * 1024) / (4 * 2 * STAGE);
   static constexpr int WGS = BY_REGS < BY_LDS ? BY_REGS : (BY_LDS > 0 ? BY_LDS : 1);
   static constexpr int WAVE_LDS = (160 * 1024) / (4 * WGS);  // one wave's ring budget
+  // the four waves' states exchanged at the end (accumulators, m, l, bad flag)
+  static constexpr int XCH = 3 * (DV / 16 * 4 + 3) * 64 * 4;
+  // LDS of one workgroup of the ring kernel: the rings, reused for the exchange
+  static constexpr int RING_SMEM = 4 * RingShape<DK, DV, WAVE_LDS>::WAVE_BYTES > XCH
+                                       ? 4 * RingShape<DK, DV, WAVE_LDS>::WAVE_BYTES
+                                       : XCH;
+  static_assert(RING_SMEM * WGS <= 160 * 1024, "resident workgroups exceed the LDS");
+  static_assert(XCH * WGS <= 160 * 1024, "resident workgroups exceed the LDS");
 };
 
 // Epilogue shared by both decode kernels: combine the four waves' states in wave 0,
@@ -213,9 +221,7 @@ void decode_ring_kernel(AttnArgs a) {
   using S = StepShape<DK, DV>;
   constexpr int WL = DecodeOcc<DK, DV>::WAVE_LDS;
   using R = RingShape<DK, DV, WL>;
-  constexpr int XCH_BYTES = 3 * (S::NT * 4 + 3) * 64 * 4;
-  constexpr int SMEM = 4 * R::WAVE_BYTES > XCH_BYTES ? 4 * R::WAVE_BYTES : XCH_BYTES;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[DecodeOcc<DK, DV>::RING_SMEM];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int j = lane >> 4;
@@ -317,7 +323,7 @@ void decode_ring_kernel(AttnArgs a) {
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void decode_regs_kernel(AttnArgs a) {
   using S = StepShape<DK, DV>;
-  __shared__ float xch[3 * (S::NT * 4 + 3) * 64];
+  __shared__ float xch[DecodeOcc<DK, DV>::XCH / 4];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int j = lane >> 4;
@@ -393,6 +399,26 @@ int decode_wgs_per_cu(int dk, int dv) {
   NVFP4_DECODE_CASE(512, 256)
 #undef NVFP4_DECODE_CASE
   return 2;
+}
+
+size_t decode_lds_bytes(int dk, int dv, int page_size) {
+  // per CU: the resident workgroups' rings (page_size >= 16) or exchange buffers
+#define NVFP4_DECODE_CASE(K, V)                                                      \
+  if (dk == K && dv == V)                                                            \
+    return (size_t)DecodeOcc<K, V>::WGS *                                            \
+           (page_size >= 16 ? DecodeOcc<K, V>::RING_SMEM : DecodeOcc<K, V>::XCH);
+  NVFP4_DECODE_CASE(64, 64)
+  NVFP4_DECODE_CASE(128, 64)
+  NVFP4_DECODE_CASE(128, 128)
+  NVFP4_DECODE_CASE(256, 64)
+  NVFP4_DECODE_CASE(256, 128)
+  NVFP4_DECODE_CASE(256, 256)
+  NVFP4_DECODE_CASE(512, 64)
+  NVFP4_DECODE_CASE(512, 128)
+  NVFP4_DECODE_CASE(512, 256)
+  NVFP4_DECODE_CASE(512, 512)
+#undef NVFP4_DECODE_CASE
+  return (size_t)-1;
 }
 
 hipError_t launch_decode(int dk, int dv, int page_shift, const AttnArgs& a, hipStream_t stream) {

@@ -111,13 +111,16 @@ hipError_t launch_decode(int dk, int dv, int page_shift, const AttnArgs& a, hipS
 bool decode_supported(int dk, int dv);
 // Decode workgroups (four waves each) one CU runs at once for this shape.
 int decode_wgs_per_cu(int dk, int dv);
+// LDS one CU's resident decode workgroups use (any head dims of the set 64..512).
+size_t decode_lds_bytes(int dk, int dv, int page_size);
 hipError_t launch_prefill(int dk, int dv, int page_shift, const AttnArgs& a, int rows_per_item,
                           hipStream_t stream);
 bool prefill_supported(int dk, int dv);
 int prefill_rows_per_item(int dk, int dv, int group, int page_size);
 // Prefill workgroups one CU runs at once for this shape.
 int prefill_wgs_per_cu(int dk, int dv);
-size_t prefill_lds_bytes(int dk, int dv);
+// LDS one CU's resident prefill workgroups use (any head dims of the set 64..512).
+size_t prefill_lds_bytes(int dk, int dv, int page_size);
 hipError_t launch_merge_partials(const AttnArgs& a, int n_merges, int dv, int prefill,
                                  hipStream_t stream);
 hipError_t launch_merge_states(const float* o_parts, const float* lse_parts, int64_t rows,

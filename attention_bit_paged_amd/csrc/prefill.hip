@@ -43,7 +43,8 @@ constexpr int prefill_nr() {
   return DK >= 512 ? 1 : 2;
 }
 
-template <int DK, int DV, bool PAGE16>
+// page_size < 16: every token is looked up on its own (PagedView::load).
+template <int DK, int DV>
 __global__ __launch_bounds__(256) void prefill_regs_kernel(AttnArgs a) {
   using S = StepShape<DK, DV>;
   constexpr int NR = prefill_nr<DK>();
@@ -93,7 +94,7 @@ __global__ __launch_bounds__(256) void prefill_regs_kernel(AttnArgs a) {
   int mask_from = kv1 - kDecodeStep;
   if (a.causal) mask_from = min(mask_from, q0 + row_base / G + off + 1 - kDecodeStep);
 
-  PagedView<DK, DV, PAGE16> view;
+  PagedView<DK, DV, false> view;
   view.init(a, b, kvh, lane);
   const int tlast = kv1 - 1;
 
@@ -186,6 +187,8 @@ struct CoopShape {
   static_assert(R::NST == 3, "raw ring depth");
   static_assert(S::NT % VH == 0, "V split");
 };
+
+constexpr int kLdsPerCu = 160 * 1024;
 
 // Per-lane LDS offsets of the cooperative dequantisation (constant for the kernel).
 // Operand o < 2*NS is K tile o/NS (token tile A or B), k-step o%NS; operand 2*NS + e is
@@ -476,9 +479,10 @@ __attribute__((amdgpu_waves_per_eu(CoopShape<DK, DV>::WGS_PER_CU)))
 void prefill_coop_kernel(AttnArgs a) {
   using S = StepShape<DK, DV>;
   using C = CoopShape<DK, DV>;
-  using R = typename C::R;
   constexpr int NR = C::NR;
   constexpr int WL = 3 * C::RAW_STAGE;
+  static_assert(C::OK, "shape has no cooperative kernel");
+  static_assert(C::LDS * C::WGS_PER_CU <= kLdsPerCu, "resident workgroups exceed the LDS");
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -775,17 +779,10 @@ void prefill_coop_kernel(AttnArgs a) {
 template <int DK, int DV>
 hipError_t launch_dk_dv(int page_shift, const AttnArgs& a, hipStream_t stream) {
   const dim3 grid(a.n_work);
-  if constexpr (CoopShape<DK, DV>::OK) {
-    if (page_shift >= 4) {
-      launch_attention(prefill_coop_kernel<DK, DV>, grid, dim3(CoopShape<DK, DV>::NW * 64), stream,
-                       a);
-      return hipGetLastError();
-    }
-  }
   if (page_shift >= 4)
-    launch_attention(prefill_regs_kernel<DK, DV, true>, grid, dim3(256), stream, a);
+    launch_attention(prefill_coop_kernel<DK, DV>, grid, dim3(CoopShape<DK, DV>::NW * 64), stream, a);
   else
-    launch_attention(prefill_regs_kernel<DK, DV, false>, grid, dim3(256), stream, a);
+    launch_attention(prefill_regs_kernel<DK, DV>, grid, dim3(256), stream, a);
   return hipGetLastError();
 }
 
@@ -805,7 +802,25 @@ int prefill_rows_per_item(int dk, int dv, int /*group*/, int page_size) {
   return 64 * (dk >= 512 ? 1 : 2);
 }
 
-size_t prefill_lds_bytes(int /*dk*/, int /*dv*/) { return 0; }
+size_t prefill_lds_bytes(int dk, int dv, int page_size) {
+  if (page_size < 16) return 0;  // the register kernel uses no LDS
+  // one CU holds WGS_PER_CU workgroups of the cooperative kernel; formula for every
+  // pair of head dims, including those the planner then rejects for it
+#define NVFP4_PREFILL_LDS(K, V) \
+  if (dk == K && dv == V) return (size_t)CoopShape<K, V>::LDS * CoopShape<K, V>::WGS_PER_CU;
+  NVFP4_PREFILL_LDS(64, 64)
+  NVFP4_PREFILL_LDS(128, 64)
+  NVFP4_PREFILL_LDS(128, 128)
+  NVFP4_PREFILL_LDS(256, 64)
+  NVFP4_PREFILL_LDS(256, 128)
+  NVFP4_PREFILL_LDS(256, 256)
+  NVFP4_PREFILL_LDS(512, 64)
+  NVFP4_PREFILL_LDS(512, 128)
+  NVFP4_PREFILL_LDS(512, 256)
+  NVFP4_PREFILL_LDS(512, 512)
+#undef NVFP4_PREFILL_LDS
+  return (size_t)-1;
+}
 
 hipError_t launch_prefill(int dk, int dv, int page_shift, const AttnArgs& a, int /*rows*/,
                           hipStream_t stream) {

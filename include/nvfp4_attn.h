@@ -30,6 +30,9 @@
  *     offending argument.
  *   - Kernels treat a page-table entry outside [0, num_pages) as corrupt input:
  *     they read nothing through it and write NaN to the affected output rows.
+ *   - Calls that launch check that the device the stream belongs to (the current
+ *     device for the null stream) is a gfx950; the pointers must be memory of that
+ *     device ([XQA] review: the check must use the tensors' device, not a default).
  */
 #ifndef NVFP4_ATTN_H
 #define NVFP4_ATTN_H
@@ -46,9 +49,11 @@ typedef enum {
   NVFP4_E_INVALID = 1,     /* an argument has an invalid value (null pointer, bad size) */
   NVFP4_E_SHAPE = 2,       /* shapes, strides or alignment inconsistent; plan/run mismatch */
   NVFP4_E_UNSUPPORTED = 3, /* head dim, group size or page size outside the supported set */
-  NVFP4_E_LDS_BUDGET = 4,  /* a kernel tile for this shape does not fit in LDS */
+  NVFP4_E_LDS_BUDGET = 4,  /* a kernel tile for this shape does not fit on chip: the LDS its
+                              resident workgroups need exceeds a CU's 160 KiB, or (head dims
+                              512/512) its decode tile exceeds the register file */
   NVFP4_E_WORKSPACE = 5,   /* workspace null, too small, misaligned or not uploaded */
-  NVFP4_E_DEVICE = 6,      /* current device is not gfx950 */
+  NVFP4_E_DEVICE = 6,      /* the device of the call's stream is not gfx950 */
   NVFP4_E_HIP = 7          /* a HIP runtime call failed */
 } nvfp4_status;
 
@@ -129,6 +134,9 @@ nvfp4_status nvfp4_quantize_kv(const void* k_src, int64_t k_stride_token, int64_
  *              on chip; a prefill work item covers one chunk; split items are merged
  *              by LSE.
  *   num_cus:   compute units to fill; 0 = query the current device (256 if none).
+ * Rejects, with NVFP4_E_LDS_BUDGET, a shape whose kernel's resident workgroups need more
+ * LDS than a CU has ([PF] commits on the shared-memory probe: a tile that does not
+ * fit on chip is refused at plan time, not at launch).
  * The plan owns host memory only.  It is immutable after creation, except for the
  * record of the workspace it was last uploaded to.
  */

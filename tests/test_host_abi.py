@@ -203,3 +203,95 @@ def test_binding_checks_shapes_against_the_plan():
     kn = torch.zeros((2, 1, 128), dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="v_new"):
         nv.batch_decode_append(plan, q, kn, kn[:1], pt, pool, pool, 0.1, ws)
+
+
+def test_lds_budget_is_computed_and_rejects_what_does_not_fit():
+    """The plan's on-chip check uses the kernels' own LDS footprint: the 512/512 prefill
+    tile needs more LDS than a CU has and is refused as such; every supported pair of
+    head dims fits at every page size."""
+    st, msg = _plan_status(kv_lens=[64], qo_indptr=[0, 8], head_dim_qk=512, head_dim_vo=512)
+    assert st == "NVFP4_E_LDS_BUDGET" and "LDS" in msg and "163840" in msg, msg
+    st, msg = _plan_status(kv_lens=[64], head_dim_qk=512, head_dim_vo=512)
+    assert st == "NVFP4_E_LDS_BUDGET", msg
+    for dk in (64, 128, 256, 512):
+        for dv in (64, 128, 256, 512):
+            if dv > dk or (dk, dv) == (512, 512):
+                continue
+            for ps in (1, 4, 16, 64):
+                for ind in (None, [0, 8]):
+                    st, msg = _plan_status(kv_lens=[64], qo_indptr=ind, head_dim_qk=dk,
+                                           head_dim_vo=dv, page_size=ps, num_qo_heads=8,
+                                           num_kv_heads=1)
+                    assert st == "NVFP4_OK", (dk, dv, ps, ind, msg)
+
+
+def test_binding_refuses_host_tensors_before_any_call():
+    """Tensors with the right shapes but on the host would hand host pointers to the
+    kernels; the binding refuses them (and mixed devices) before calling the library."""
+    import torch
+    plan = nv.Plan([100, 30], num_qo_heads=4, num_kv_heads=1, head_dim_qk=128, num_cus=256)
+    pt = torch.zeros((2, 8), dtype=torch.int32)
+    pool = nv.KVPool.empty(16, 1, 16, 128, device="cpu")
+    ws = torch.zeros(plan.workspace_bytes, dtype=torch.uint8)
+    q = torch.zeros((2, 4, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        nv.batch_decode(plan, q, pt, pool, pool, 0.1, ws)
+    kn = torch.zeros((2, 1, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        nv.batch_decode_append(plan, q, kn, kn, pt, pool, pool, 0.1, ws)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        plan.upload(ws)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        nv.quantize_kv(kn[0:1].expand(3, 1, 128).contiguous(), None,
+                       torch.zeros(3, dtype=torch.int64), pool, None)
+    o = torch.zeros((2, 4, 128))
+    lse = torch.zeros((2, 4))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        nv.merge_partials(plan, ws, o, lse)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        nv.merge_states(torch.zeros((2, 3, 4, 64)), torch.zeros((2, 3, 4)))
+    # a pool whose heads or dims do not match the plan
+    pool64 = nv.KVPool.empty(16, 1, 16, 64, device="cpu")
+    with pytest.raises(ValueError, match="k_pool"):
+        nv.batch_decode(plan, q, pt, pool64, pool, 0.1, ws)
+    # a page table with too few columns for the longest request (100 keys: 7 pages)
+    with pytest.raises(ValueError, match="page_table"):
+        nv.batch_decode(plan, q, pt[:, :6], pool, pool, 0.1, ws)
+    with pytest.raises(ValueError, match="workspace"):
+        nv.batch_decode(plan, q, pt, pool, pool, 0.1, ws[:8])
+
+
+def test_binding_checks_sources_and_merge_shapes():
+    """Sources must match their pools, and merge inputs / outputs their shapes and
+    dtype, or the kernels would read or write past the buffers."""
+    import torch
+    kp = nv.KVPool.empty(16, 2, 16, 128, device="cpu")
+    vp = nv.KVPool.empty(16, 2, 16, 64, device="cpu")
+    slots = torch.zeros(5, dtype=torch.int64)
+    k = torch.zeros((5, 2, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="v must have shape"):
+        nv.quantize_kv(k, torch.zeros((4, 2, 64), dtype=torch.bfloat16), slots, kp, vp)
+    with pytest.raises(ValueError, match="v must have shape"):
+        nv.quantize_kv(k, torch.zeros((5, 2, 128), dtype=torch.bfloat16), slots, kp, vp)
+    with pytest.raises(ValueError, match="k must have shape"):
+        nv.quantize_kv(torch.zeros((5, 1, 128), dtype=torch.bfloat16), None, slots, kp, None)
+    with pytest.raises(ValueError, match="slot_mapping"):
+        nv.quantize_kv(k, None, slots[:4], kp, None)
+    with pytest.raises(ValueError, match="pool"):
+        nv.quantize_kv(k, None, slots, None, None)
+    o_parts = torch.zeros((2, 3, 4, 64))
+    with pytest.raises(ValueError, match="fp32"):
+        nv.merge_states(o_parts.double(), torch.zeros((2, 3, 4)))
+    with pytest.raises(ValueError, match="lse_parts must have shape"):
+        nv.merge_states(o_parts, torch.zeros((2, 3, 5)))
+    with pytest.raises(ValueError, match="out must be"):
+        nv.merge_states(o_parts, torch.zeros((2, 3, 4)), out=torch.zeros((2, 4, 32)))
+    with pytest.raises(ValueError, match="lse must be"):
+        nv.merge_states(o_parts, torch.zeros((2, 3, 4)), lse=torch.zeros((4, 2)).t())
+    plan = nv.Plan([3000], num_qo_heads=4, num_kv_heads=1, head_dim_qk=128, kv_chunk_tokens=64,
+                   num_cus=256)
+    ws = torch.zeros(plan.workspace_bytes, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="out must have shape"):
+        nv.merge_partials(plan, ws, torch.zeros((2, 4, 128)), torch.zeros((1, 4)))
+    with pytest.raises(ValueError, match="lse must"):
+        nv.merge_partials(plan, ws, torch.zeros((1, 4, 128)), torch.zeros((1, 4), dtype=torch.float64))

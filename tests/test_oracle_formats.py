@@ -13,15 +13,56 @@ from oracle import nvfp4_ref as ref
 RNG = np.random.default_rng(12345)
 
 
+# ------------------------------------------------------- minifloat fields ----
+
+def minifloat_value(code, ebits, mbits, bias):
+    """Value of a sign / exponent / mantissa code read from its bit fields (OCP FP8 and
+    MX v1.0 layouts): exponent field 0 is subnormal, 2^(1-bias) * m / 2^mbits; any other
+    e is 2^(e-bias) * (1 + m / 2^mbits).  Written from the field definitions, not from
+    the oracle, and pinned on the FP8 formats by torch's own conversions below."""
+    sign = (code >> (ebits + mbits)) & 1
+    e = (code >> mbits) & ((1 << ebits) - 1)
+    m = code & ((1 << mbits) - 1)
+    if e == 0:
+        mag = 2.0 ** (1 - bias) * (m / 2.0 ** mbits)
+    else:
+        mag = 2.0 ** (e - bias) * (1.0 + m / 2.0 ** mbits)
+    return -mag if sign else mag
+
+
+def test_minifloat_fields_match_torch_fp8_formats():
+    # e4m3fn: bias 7, only 0x7F / 0xFF are NaN; e5m2: bias 15, exponent 31 is inf/NaN
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    t43 = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    t52 = codes.view(torch.float8_e5m2).to(torch.float64).numpy()
+    for c in range(256):
+        if (c & 0x7F) != 0x7F:
+            assert minifloat_value(c, 4, 3, 7) == t43[c], c
+        if (c >> 2) & 0x1F != 0x1F:
+            assert minifloat_value(c, 5, 2, 15) == t52[c], c
+
+
+# e2m1 = 1 sign bit (bit 3), 2 exponent bits with bias 1, 1 mantissa bit (OCP MX v1.0)
+E2M1_FROM_FIELDS = np.array([minifloat_value(c, 2, 1, 1) for c in range(8)])
+
+
+def test_e2m1_values_follow_the_bit_fields():
+    for code in range(16):
+        want = minifloat_value(code, 2, 1, 1)
+        got = float(ref.e2m1_value(code))
+        assert got == want and np.signbit(got) == np.signbit(want), (code, got, want)
+
+
 # ----------------------------------------------------------------- e2m1 ----
 
 def brute_e2m1(r):
-    """Nearest of the 8 magnitudes by exhaustive search; ties to the even code."""
+    """Nearest of the 8 magnitudes (from the bit fields) by exhaustive search; ties to
+    the even code."""
     out = []
     for x in np.ravel(r):
         best, best_d = None, None
         for code in range(8):
-            d = abs(x - ref.E2M1_MAGNITUDE[code])
+            d = abs(x - E2M1_FROM_FIELDS[code])
             if best is None or d < best_d or (d == best_d and code % 2 == 0):
                 best, best_d = code, d
         if x > 6.0:
@@ -35,8 +76,8 @@ def test_e2m1_table_roundtrip():
         v = ref.e2m1_value(code)
         assert ref.e2m1_round(abs(v)) == (code & 7)
         assert np.signbit(v) == bool(code & 8) or v == 0
-    assert list(ref.e2m1_value(np.arange(8))) == [0, .5, 1, 1.5, 2, 3, 4, 6]
-    assert list(ref.e2m1_value(np.arange(8, 16))) == [-0.0, -.5, -1, -1.5, -2, -3, -4, -6]
+    assert list(ref.e2m1_value(np.arange(8))) == list(E2M1_FROM_FIELDS)
+    assert list(ref.e2m1_value(np.arange(8, 16))) == list(-E2M1_FROM_FIELDS)
 
 
 def test_e2m1_ties_to_even_and_saturation():
@@ -149,7 +190,7 @@ def test_quantiser_is_nearest_value_brute_force():
                 if s == 0:
                     assert code & 7 == 0
                     continue
-                dist = [abs(abs(xe) - m * s) for m in ref.E2M1_MAGNITUDE]
+                dist = [abs(abs(xe) - m * s) for m in E2M1_FROM_FIELDS]
                 mn = min(dist)
                 ok = [c for c in range(8) if dist[c] == mn]
                 exp = ok[0] if len(ok) == 1 else [c for c in ok if c % 2 == 0][0]

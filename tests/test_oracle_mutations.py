@@ -68,7 +68,10 @@ def _merge_unnormalised(o_parts, lse_parts):
     return o * len(o_parts), lse
 
 
+_E2M1_CODE5_WRONG = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 2.5, 4.0, 6.0])
+
 MUTATIONS = {
+    "e2m1 table code 5 = 2.5": ("E2M1_MAGNITUDE", _E2M1_CODE5_WRONG),
     "scale rounds down": ("e4m3_round", _e4m3_floor),
     "element ties away from zero": ("e2m1_round", _e2m1_ties_away),
     "nibble order swapped": ("unpack_nibbles", _unpack_swapped),
@@ -83,6 +86,7 @@ MUTATIONS = {
 def _pins(golden_dir):
     return [
         lambda: tf.test_vones_probe_matches_page(golden_dir),
+        tf.test_e2m1_values_follow_the_bit_fields,
         tf.test_e2m1_ties_to_even_and_saturation,
         tf.test_e2m1_matches_brute_force,
         tf.test_e4m3_round_matches_torch_cast,
