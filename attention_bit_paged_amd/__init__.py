@@ -18,7 +18,7 @@ from ._lib import (EXPORTS, STATUS, WORK_FIELDS, KVPoolStruct, NVFP4Error, PlanI
                    check, lib)
 
 __all__ = ["KVPool", "Plan", "Prepared", "quantize_kv", "batch_decode", "batch_decode_append",
-           "batch_prefill",
+           "batch_prefill", "kv_checksum",
            "merge_partials", "merge_states", "NVFP4Error", "lib", "version", "EXPORTS"]
 
 
@@ -367,6 +367,35 @@ def batch_decode_append(plan: Plan, q: torch.Tensor, k_new: torch.Tensor, v_new:
                          out, lse))
     check(lib.nvfp4_batch_decode_append(*args))
     return out, lse
+
+
+def kv_checksum(plan: Plan, page_table: torch.Tensor, k_pool: KVPool, v_pool: KVPool,
+                workspace: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None,
+                prepare: bool = False):
+    """XOR checksum of the KV bytes a decode plan reads, streamed the way the decode
+    kernel streams them (nvfp4_kv_checksum): int32 ``[batch, Hkv]`` holding the uint32
+    words, or a ``Prepared`` call with ``prepare=True``."""
+    if page_table.dtype != torch.int32 or page_table.dim() != 2 or page_table.stride(1) != 1 \
+            or page_table.shape[0] < plan.batch or page_table.shape[1] < plan.max_pages():
+        raise ValueError(f"page_table must be int32 [>= {plan.batch}, >= {plan.max_pages()}] "
+                         "with contiguous rows")
+    _check_pools(plan, k_pool, v_pool)
+    _check_workspace(plan, workspace)
+    shape = (plan.batch, plan.num_kv_heads)
+    if out is not None and (out.dtype != torch.int32 or tuple(out.shape) != shape
+                            or not out.is_contiguous()):
+        raise ValueError(f"out must be contiguous int32 of shape {shape}")
+    dev = _device(page_table, k_pool.data, k_pool.sf, v_pool.data, v_pool.sf, workspace, out)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.int32, device=dev)
+    ks, vs = k_pool.struct(), v_pool.struct()
+    args = (plan.handle, _ptr(page_table), page_table.stride(0), ctypes.byref(ks),
+            ctypes.byref(vs), _ptr(workspace), workspace.numel(), _ptr(out), _stream(stream, dev))
+    if prepare:
+        return Prepared(lib.nvfp4_kv_checksum, args,
+                        (plan, page_table, k_pool, v_pool, ks, vs, workspace, out))
+    check(lib.nvfp4_kv_checksum(*args))
+    return out
 
 
 def batch_prefill(plan: Plan, q: torch.Tensor, page_table: torch.Tensor, k_pool: KVPool,

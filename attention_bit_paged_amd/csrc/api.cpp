@@ -647,6 +647,33 @@ nvfp4_status nvfp4_batch_prefill(const nvfp4_plan* plan, const void* q, int64_t 
              sm_scale, workspace, workspace_bytes, o, o_stride_tok, o_stride_head, lse, stream);
 }
 
+nvfp4_status nvfp4_kv_checksum(const nvfp4_plan* plan, const int32_t* page_table,
+                               int64_t pt_stride, const nvfp4_kv_pool* k_pool,
+                               const nvfp4_kv_pool* v_pool, void* workspace,
+                               size_t workspace_bytes, uint32_t* checksum, void* stream) {
+  if (plan && plan->prefill)
+    return fail(NVFP4_E_SHAPE, "the checksum streams a decode plan, got a prefill plan");
+  if (plan && plan->page_size < 16)
+    return fail(NVFP4_E_UNSUPPORTED, "page_size %d: the checksum streams through the decode "
+                "rings, which need pages of at least 16 tokens", plan->page_size);
+  if (plan && plan->batch > 0 && !checksum) return fail(NVFP4_E_INVALID, "checksum is NULL");
+  if (!aligned(checksum, 4)) return fail(NVFP4_E_SHAPE, "checksum must be 4-byte aligned");
+  // the attention checks, with stand-ins for q, o and lse (never read or written)
+  static float dummy[4] __attribute__((aligned(16)));
+  if (nvfp4_status st = check_run(plan, false, dummy, 0, 0, page_table, pt_stride, k_pool,
+                                  v_pool, 1.f, workspace, workspace_bytes, dummy, 0, 0, dummy,
+                                  stream))
+    return st;
+  AttnArgs a = make_args(plan, dummy, 0, 0, page_table, pt_stride, k_pool, v_pool, 1.f,
+                         workspace, nullptr, 0, 0, nullptr);
+  a.q = nullptr;
+  const hipError_t e = launch_kv_checksum(plan->head_dim_qk, plan->head_dim_vo, a, checksum,
+                                          plan->batch, plan->num_kv_heads,
+                                          static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(NVFP4_E_HIP, "checksum launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 nvfp4_status nvfp4_set_timing_events(void* start_event, void* stop_event) {
   LaunchEvents& ev = launch_events();
   ev.start = static_cast<hipEvent_t>(start_event);

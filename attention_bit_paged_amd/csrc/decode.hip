@@ -319,6 +319,109 @@ void decode_ring_kernel(AttnArgs a) {
                       j, it.head_valid, it.slot);
 }
 
+// XOR of the 32-bit words this lane's copies placed in a ring stage: K rows, V rows
+// (16 bytes per lane and copy) and the scale region (4 bytes per lane and copy, K's
+// scales first).  MASK: words of tokens after `tl` (step-relative) are left out.
+// dat / sf: this lane's byte address in the data and scale regions of stage 0.
+template <int DK, int DV, int WL, bool MASK>
+__device__ __forceinline__ uint32_t fold_stage(uint32_t dat, uint32_t sf, uint32_t stage_off,
+                                               int lane, int tl) {
+  using R = RingShape<DK, DV, WL>;
+  uint32_t x = 0;
+#pragma unroll
+  for (int c = 0; c < R::N_KD; ++c) {
+    if (MASK && (c * 1024 + 16 * lane) / (DK / 2) > tl) continue;
+    uint32_t w[4];
+    lds_load<16>(dat + stage_off + R::OFF_KD + c * 1024, w);
+    x ^= w[0] ^ w[1] ^ w[2] ^ w[3];
+  }
+#pragma unroll
+  for (int c = 0; c < R::N_VD; ++c) {
+    if (MASK && (c * 1024 + 16 * lane) / (DV / 2) > tl) continue;
+    uint32_t w[4];
+    lds_load<16>(dat + stage_off + R::OFF_VD + c * 1024, w);
+    x ^= w[0] ^ w[1] ^ w[2] ^ w[3];
+  }
+#pragma unroll
+  for (int c = 0; c < R::N_SF; ++c) {
+    const int byte = c * 256 + 4 * lane;
+    if (byte >= R::KS + R::VS) continue;  // padding lanes copy nothing
+    const int tok = byte < R::KS ? byte / (DK / 16) : (byte - R::KS) / (DV / 16);
+    if (MASK && tok > tl) continue;
+    uint32_t w;
+    lds_load<4>(sf + stage_off + c * 256, &w);
+    x ^= w;
+  }
+  return x;
+}
+
+// Checksum of the KV bytes a decode plan's attention reads, streamed exactly as
+// decode_ring_kernel streams them (same work items, rings, copies and waits) and folded
+// by XOR instead of attended: the access pattern's own ceiling, with a result that can
+// be checked.  out[b * Hkv + h] ^= the XOR of every 32-bit word of the packed K and V
+// rows and of their scale rows of the item's keys.  Only the first block of qo heads
+// of a row group streams (larger groups repeat the same keys for each block).
+template <int DK, int DV>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DecodeOcc<DK, DV>::WGS)))
+void kv_checksum_kernel(AttnArgs a, uint32_t* out, int num_kv_heads) {
+  constexpr int WL = DecodeOcc<DK, DV>::WAVE_LDS;
+  using R = RingShape<DK, DV, WL>;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[DecodeOcc<DK, DV>::RING_SMEM];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const DecodeItem it = decode_item(a, wave, lane & 15);
+  if (it.h0 != 0) return;  // uniform over the workgroup; no barrier follows
+  PagedView<DK, DV, true> view;
+  view.init(a, it.b, it.kvh, lane);
+  RingPlan<DK, DV, WL> rp;
+  rp.init(lane, view.k_tok, view.v_tok, view.ksf_tok, view.vsf_tok);
+  const uint32_t ring_lds =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(smem + wave * R::WAVE_BYTES));
+  const int tlast = it.w1 - 1;
+  uint32_t bad = 0;
+  // the fold's lane addresses pass through every wait, which orders the reads after it
+  RingLanes lanes;
+  lanes.k = ring_lds + 16 * lane;
+  lanes.ks = ring_lds + R::OFF_SF + 4 * lane;
+  lanes.v = lanes.vs = 0;
+  const int len = it.w1 - it.w0;
+  const int nsteps = (len + kDecodeStep - 1) / kDecodeStep;
+  const int nfull = len / kDecodeStep;
+#pragma unroll
+  for (int s = 0; s < R::NST - 1; ++s)
+    if (s < nsteps)
+      ring_issue<DK, DV, WL>(rp, ring_lds + s * R::STAGE, view, it.w0 + s * kDecodeStep, tlast,
+                             bad);
+  uint32_t x = 0;
+  for (int i0 = 0; i0 < nfull; i0 += R::NST) {
+#pragma unroll
+    for (int s = 0; s < R::NST; ++s) {
+      const int i = i0 + s;
+      if (i >= nfull) break;
+      const int ahead = i + R::NST - 1;
+      const bool more = ahead < nsteps;
+      if (more)
+        ring_issue<DK, DV, WL>(rp, ring_lds + ((s + R::NST - 1) % R::NST) * R::STAGE, view,
+                               it.w0 + ahead * kDecodeStep, tlast, bad);
+      ring_wait_sel<(R::NST - 1) * R::NDMA>(lanes, more);
+      x ^= fold_stage<DK, DV, WL, false>(lanes.k, lanes.ks, s * R::STAGE, lane, 0);
+    }
+  }
+  if (nfull < nsteps) {
+    ring_wait<0>(lanes);
+    x ^= fold_stage<DK, DV, WL, true>(lanes.k, lanes.ks, (uint32_t)(nfull % R::NST) * R::STAGE,
+                                      lane, tlast - (it.w0 + nfull * kDecodeStep));
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) x ^= (uint32_t)__shfl_xor((int)x, o);
+  if (lane == 0 && len > 0) atomicXor(out + (int64_t)it.b * num_kv_heads + it.kvh, x);
+}
+
+__global__ void zero_words_kernel(uint32_t* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
 // page_size < 16: every token is looked up on its own; the next step is held in registers.
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void decode_regs_kernel(AttnArgs a) {
@@ -419,6 +522,32 @@ size_t decode_lds_bytes(int dk, int dv, int page_size) {
   NVFP4_DECODE_CASE(512, 512)
 #undef NVFP4_DECODE_CASE
   return (size_t)-1;
+}
+
+hipError_t launch_kv_checksum(int dk, int dv, const AttnArgs& a, uint32_t* out, int batch,
+                              int num_kv_heads, hipStream_t stream) {
+  const int64_t n = (int64_t)batch * num_kv_heads;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                     out, n);
+  if (a.n_work <= 0) return hipGetLastError();
+  const dim3 grid(a.n_work);
+#define NVFP4_DECODE_CASE(K, V)                                                                \
+  if (dk == K && dv == V) {                                                                    \
+    launch_attention(kv_checksum_kernel<K, V>, grid, dim3(256), stream, a, out, num_kv_heads); \
+    return hipGetLastError();                                                                  \
+  }
+  NVFP4_DECODE_CASE(64, 64)
+  NVFP4_DECODE_CASE(128, 64)
+  NVFP4_DECODE_CASE(128, 128)
+  NVFP4_DECODE_CASE(256, 64)
+  NVFP4_DECODE_CASE(256, 128)
+  NVFP4_DECODE_CASE(256, 256)
+  NVFP4_DECODE_CASE(512, 64)
+  NVFP4_DECODE_CASE(512, 128)
+  NVFP4_DECODE_CASE(512, 256)
+#undef NVFP4_DECODE_CASE
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode(int dk, int dv, int page_shift, const AttnArgs& a, hipStream_t stream) {

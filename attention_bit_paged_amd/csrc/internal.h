@@ -93,21 +93,25 @@ struct LaunchEvents {
 };
 LaunchEvents& launch_events();
 
-// Launches an attention kernel, with the thread's timing events when they are set.
-template <typename K>
+// Launches an attention (or streaming) kernel, with the thread's timing events when
+// they are set.
+template <typename K, typename... Args>
 inline void launch_attention(K kernel, dim3 grid, dim3 block, hipStream_t stream,
-                             const AttnArgs& a) {
+                             const Args&... args) {
   const LaunchEvents& ev = launch_events();
   if (ev.start || ev.stop)
-    hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, ev.start, ev.stop, 0u, a);
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, ev.start, ev.stop, 0u, args...);
   else
-    hipLaunchKernelGGL(kernel, grid, block, 0, stream, a);
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
 }
 
 // Launchers (defined in the .hip files).  Return the hipGetLastError() status of the launch.
 hipError_t launch_quantize(const QuantArgs* k, const QuantArgs* v, int64_t n_tokens,
                            const int64_t* slots, hipStream_t stream);
 hipError_t launch_decode(int dk, int dv, int page_shift, const AttnArgs& a, hipStream_t stream);
+// Zeroes out[batch * num_kv_heads], then XORs in the KV words a decode plan streams.
+hipError_t launch_kv_checksum(int dk, int dv, const AttnArgs& a, uint32_t* out, int batch,
+                              int num_kv_heads, hipStream_t stream);
 bool decode_supported(int dk, int dv);
 // Decode workgroups (four waves each) one CU runs at once for this shape.
 int decode_wgs_per_cu(int dk, int dv);

@@ -19,6 +19,14 @@ token's rows) over its average duration, timed inside the timed steps with HIP e
 that the kernel's dispatch itself timestamps (nvfp4_set_timing_events), so that no
 event packet is added to the queue.
 
+Also in the line (default run): ``stream_ceiling``, the same plan's KV bytes streamed
+through the same rings and copies with no attention arithmetic (nvfp4_kv_checksum),
+timed the same way: what the access pattern itself sustains; ``single_decode_latency``,
+percentiles of one 128-key single-request decode (kernel and call-to-completion);
+``cpu_baseline``, the oracle on a bounded sample of the workload on one host thread and
+on the host's threads; ``other_workloads``, the long-context and 512/256 decodes and the
+two prefills, each with its own CPU baseline (and streaming ceiling for the decodes).
+
 With --workload naming a prefill workload, the timed step is that prefill's attention
 pass and merge instead (TFLOP/s; used to profile the prefill kernel).
 
@@ -65,7 +73,9 @@ def parse():
     p.add_argument("--pool-sets", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true", help="skip the other workloads' lines")
-    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    # per leg (one thread, then the host threads) and workload: about 2 x 5 x 3 s of
+    # oracle work in the default run
+    p.add_argument("--cpu-seconds", type=float, default=3.0)
     p.add_argument("--pmc-run", action="store_true")
     p.add_argument("--summarize-trace", metavar="DIR")
     p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -157,8 +167,30 @@ def decode_bytes(w, append=False):
     return w.kv_bytes(), q + o + new
 
 
-def cpu_baseline(case, budget_s):
-    """The oracle on a bounded sample of the same decode workload (one BLAS thread)."""
+def _pair_work(w, b):
+    """Algorithmic work of one (request, kv head) pair: KV bytes (decode) or flops."""
+    if w.decode:
+        return w.kv_lens[b] * (w.head_dim_qk // 2 + w.head_dim_qk // 16 + w.head_dim_vo // 2
+                               + w.head_dim_vo // 16)
+    q, l = w.qo_lens[b], w.kv_lens[b]
+    pairs = q * (l - q) + q * (q + 1) // 2 if w.causal else q * l
+    return 2 * (w.head_dim_qk + w.head_dim_vo) * w.group * pairs
+
+
+def cpu_threads():
+    """Host threads for the oracle's parallel leg: the host's cores, at most 16 (the
+    share of one GPU's host on a shared machine)."""
+    return max(1, min(os.cpu_count() or 1, 16))
+
+
+def cpu_baseline(case, budget_s, threads):
+    """The oracle (numpy float64, as it stands) on a bounded, seeded sample of the same
+    workload's (request, kv head) pairs, run from the pools' bytes.  Timed twice: on one
+    thread, and on ``threads`` host threads, each computing whole pairs (BLAS held to
+    one thread per pair, so the threads are the cores used).  Each leg stops taking new
+    pairs after ``budget_s``; its rate over the pairs done stands for the workload."""
+    import itertools
+    from concurrent.futures import FIRST_COMPLETED, ThreadPoolExecutor, wait
     from threadpoolctl import threadpool_limits
     from oracle import nvfp4_ref as ref
     from attention_bit_paged_amd import synth
@@ -167,22 +199,49 @@ def cpu_baseline(case, budget_s):
     vd, vs = case.v_pool.data.cpu().numpy(), case.v_pool.sf.cpu().numpy()
     q = case.q.float().cpu().double().numpy()
     ind = synth.indptr(w.qo_lens)
-    done, nbytes = [], 0
-    per_tok = w.num_kv_heads * (w.head_dim_qk // 2 + w.head_dim_qk // 16 + w.head_dim_vo // 2
-                                + w.head_dim_vo // 16)
-    with threadpool_limits(1):
-        t0 = time.perf_counter()
-        for b in range(w.batch):
-            ref.paged_attention(q, kd, ks, vd, vs, case.page_table_np, w.kv_lens, ind, w.page_size,
-                                w.sm_scale, False, "HND", rows=[b])
-            done.append(b)
-            nbytes += w.kv_lens[b] * per_tok
-            if time.perf_counter() - t0 > budget_s and len(done) >= 2:
-                break
-        dt = time.perf_counter() - t0
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(done)} of {w.batch} requests ({sum(w.kv_lens[b] for b in done)} "
-                      f"tokens x {w.num_kv_heads} kv heads), numpy float64, {dt:.1f} s"}
+    g = w.group
+    order = [(b, h) for b in range(w.batch) for h in range(w.num_kv_heads)]
+    order = [order[i] for i in np.random.default_rng(7).permutation(len(order))]
+    total = sum(_pair_work(w, b) for b, _ in order)
+
+    def one(pair):
+        b, h = pair
+        ref.paged_attention(q[:, g * h:g * (h + 1)], kd[:, h:h + 1], ks[:, h:h + 1],
+                            vd[:, h:h + 1], vs[:, h:h + 1], case.page_table_np, w.kv_lens, ind,
+                            w.page_size, w.sm_scale, w.causal, "HND", rows=[b])
+        return _pair_work(w, b)
+
+    def leg(n):
+        """Pairs done, their work and the elapsed time on n threads; no new pair starts
+        after budget_s."""
+        done, work = 0, 0
+        with threadpool_limits(1), ThreadPoolExecutor(n) as ex:
+            t0 = time.perf_counter()
+            pending = iter(order)
+            running = {ex.submit(one, p) for p in itertools.islice(pending, n)}
+            while running:
+                finished, running = wait(running, return_when=FIRST_COMPLETED)
+                for f in finished:
+                    work += f.result()
+                    done += 1
+                    if time.perf_counter() - t0 <= budget_s:
+                        p = next(pending, None)
+                        if p is not None:
+                            running.add(ex.submit(one, p))
+            dt = time.perf_counter() - t0
+        return done, work, dt
+
+    unit, scale = ("GB/s", 1e9) if w.decode else ("GFLOP/s", 1e9)
+    d1, w1, t1 = leg(1)
+    dn, wn, tn = leg(threads)
+    return {"workload": w.name, "unit": unit,
+            "value_1_thread": round(w1 / t1 / scale, 4),
+            "value_threads": round(wn / tn / scale, 4), "threads": threads,
+            "sample_1_thread": f"{d1} of {len(order)} (request, kv head) pairs, "
+                               f"{100 * w1 / total:.2f} % of the work, {t1:.1f} s",
+            "sample_threads": f"{dn} of {len(order)} pairs, {100 * wn / total:.2f} % of the "
+                              f"work, {tn:.1f} s",
+            "full_workload_s_extrapolated": round(total / (wn / tn), 1)}
 
 
 def timed_passes(torch, nv, run, merge, iters):
@@ -203,7 +262,7 @@ def timed_passes(torch, nv, run, merge, iters):
             float(np.mean([he.ms(e[2], e[3]) for e in ev])))
 
 
-def extra_decode(torch, nv, paged, synth, name, iters=100, warm=20):
+def extra_decode(torch, nv, paged, synth, name, iters=100, warm=20, cpu_budget=0.0):
     w = synth.workload(name)
     case = paged.build_case(w, keep_sources=False)
     plan = paged.make_plan(case)
@@ -222,16 +281,21 @@ def extra_decode(torch, nv, paged, synth, name, iters=100, warm=20):
     del run, merge
     kv, qo = decode_bytes(w)
     info = plan.info()
+    out = {"workload": name, "kv_GBs": round(kv / (run_ms + merge_ms) / 1e6, 1),
+           "kernel_GBs": round((kv + qo) / run_ms / 1e6, 1),
+           "kernel_frac_hbm": round((kv + qo) / run_ms / 1e6 / HBM_PEAK_GBS, 4),
+           "attn_ms": round(run_ms, 4), "merge_ms": round(merge_ms, 4), "kv_bytes": kv,
+           "chunk": info["kv_chunk_tokens"], "work_items": info["num_work_items"]}
+    if w.page_size >= 16:
+        out["stream_ceiling"] = stream_ceiling(torch, nv, plan, [case], ws, iters, kv, run_ms)
+    if cpu_budget > 0:
+        out["cpu_baseline"] = cpu_baseline(case, cpu_budget, cpu_threads())
     del case, ws
     torch.cuda.empty_cache()
-    return {"workload": name, "kv_GBs": round(kv / (run_ms + merge_ms) / 1e6, 1),
-            "kernel_GBs": round((kv + qo) / run_ms / 1e6, 1),
-            "kernel_frac_hbm": round((kv + qo) / run_ms / 1e6 / HBM_PEAK_GBS, 4),
-            "attn_ms": round(run_ms, 4), "merge_ms": round(merge_ms, 4), "kv_bytes": kv,
-            "chunk": info["kv_chunk_tokens"], "work_items": info["num_work_items"]}
+    return out
 
 
-def extra_prefill(torch, nv, paged, synth, name, iters=40, warm=10):
+def extra_prefill(torch, nv, paged, synth, name, iters=40, warm=10, cpu_budget=0.0):
     w = synth.workload(name)
     case = paged.build_case(w, keep_sources=False)
     plan = paged.make_plan(case)
@@ -250,13 +314,75 @@ def extra_prefill(torch, nv, paged, synth, name, iters=40, warm=10):
     del run, merge
     fl = w.flops()
     info = plan.info()
+    out = {"workload": name, "TFLOPs": round(fl / (run_ms + merge_ms) / 1e9, 2),
+           "kernel_TFLOPs": round(fl / run_ms / 1e9, 2),
+           "kernel_frac_mfma_f16": round(fl / run_ms / 1e9 / MFMA_F16_PEAK_TFLOPS, 4),
+           "attn_ms": round(run_ms, 4), "merge_ms": round(merge_ms, 4), "flops": fl,
+           "work_items": info["num_work_items"], "chunk": info["kv_chunk_tokens"]}
+    if cpu_budget > 0:
+        out["cpu_baseline"] = cpu_baseline(case, cpu_budget, cpu_threads())
     del case, ws
     torch.cuda.empty_cache()
-    return {"workload": name, "TFLOPs": round(fl / (run_ms + merge_ms) / 1e9, 2),
-            "kernel_TFLOPs": round(fl / run_ms / 1e9, 2),
-            "kernel_frac_mfma_f16": round(fl / run_ms / 1e9 / MFMA_F16_PEAK_TFLOPS, 4),
-            "attn_ms": round(run_ms, 4), "merge_ms": round(merge_ms, 4), "flops": fl,
-            "work_items": info["num_work_items"], "chunk": info["kv_chunk_tokens"]}
+    return out
+
+
+def stream_ceiling(torch, nv, plan, cases, ws, iters, kv_bytes, attn_ms):
+    """What the decode access pattern sustains without the attention arithmetic: the
+    checksum kernel (nvfp4_kv_checksum) streams the same plan's KV bytes through the same
+    rings and copies; timed like the attention kernel (events carried by its dispatch),
+    over the same rotated pool sets."""
+    w = cases[0].w
+    out = torch.empty((w.batch, w.num_kv_heads), dtype=torch.int32, device="cuda")
+    calls = [nv.kv_checksum(plan, c.page_table, c.k_pool, c.v_pool, ws, out=out, prepare=True)
+             for c in cases]
+    for i in range(10):
+        calls[i % len(calls)]()
+    he = HipEvents()
+    ev = [(he.new(), he.new()) for _ in range(iters)]
+    for i, (a, b) in enumerate(ev):
+        he.time_launches(nv, a, b)
+        calls[i % len(calls)]()
+        he.time_launches(nv, None, None)
+    torch.cuda.synchronize()
+    ms = float(np.mean([he.ms(a, b) for a, b in ev]))
+    gbs = kv_bytes / ms / 1e6
+    return {"kernel": "kv_checksum_kernel", "ms": round(ms, 5), "kv_GBs": round(gbs, 1),
+            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+            "attention_kernel_vs_ceiling": round(ms / attn_ms, 4)}
+
+
+def single_decode_latency(torch, nv, paged, synth, iters=300, warm=50):
+    """Latency of one single-request decode step (the 128-key, 4/1-head workload):
+    the kernel's own duration (events carried by its dispatch) and the host's time from
+    the call to the GPU's completion (launch + synchronize), as percentiles in us."""
+    w = synth.workload("single_decode")
+    case = paged.build_case(w, keep_sources=False)
+    plan = paged.make_plan(case)
+    ws = plan.new_workspace()
+    plan.upload(ws)
+    o = torch.empty((w.batch, w.num_qo_heads, w.head_dim_vo), device="cuda")
+    lse = torch.empty((w.batch, w.num_qo_heads), device="cuda")
+    run = nv.batch_decode(plan, case.q, case.page_table, case.k_pool, case.v_pool, w.sm_scale,
+                          ws, out=o, lse=lse, prepare=True)
+    for _ in range(warm):
+        run()
+    torch.cuda.synchronize()
+    he = HipEvents()
+    ev = [(he.new(), he.new()) for _ in range(iters)]
+    wall = []
+    for a, b in ev:
+        t0 = time.perf_counter()
+        he.time_launches(nv, a, b)
+        run()
+        he.time_launches(nv, None, None)
+        torch.cuda.synchronize()
+        wall.append((time.perf_counter() - t0) * 1e6)
+    kern = [he.ms(a, b) * 1e3 for a, b in ev]
+
+    def pct(x):
+        return {f"p{p}": round(float(np.percentile(x, p)), 2) for p in (10, 50, 90)}
+    return {"workload": w.name, "kernel_us": pct(kern), "call_to_done_us": pct(wall),
+            "iters": iters, "work_items": plan.info()["num_work_items"]}
 
 
 class Decoder:
@@ -441,7 +567,8 @@ def summarize_pmc(args):
 
 
 SIMDS = 256 * 4          # MI355X: 256 CUs of 4 SIMDs
-CLOCK_GHZ = 2.4          # nominal peak engine clock
+CLOCK_GHZ = 2.4          # nominal peak engine clock (used only without GRBM_GUI_ACTIVE)
+XCCS = 8                 # GRBM_GUI_ACTIVE is counted per XCC (dimension XCC[0:7]) and summed
 
 
 def summarize_counters(args):
@@ -449,7 +576,10 @@ def summarize_counters(args):
     its dispatches, with the figures derived from them.  Cycle counters of waves
     (SQ_WAVE_CYCLES, SQ_WAIT_*, SQ_ACTIVE_INST_*) count in units of 4 cycles;
     SQ_VALU_MFMA_BUSY_CYCLES in cycles, summed over the SIMDs.  Kernel time comes from
-    the dispatch timestamps; cycles assume the nominal 2.4 GHz clock."""
+    the dispatch timestamps.  The engine clock is measured when a pass holds
+    GRBM_GUI_ACTIVE (the cycles the graphics engine was busy, summed over the 8 XCCs:
+    clock = GRBM_GUI_ACTIVE / 8 / kernel time), else the nominal 2.4 GHz is assumed;
+    rocprofv3's own derived MfmaUtil, when a pass holds it, is reported beside ours."""
     vals, dur, waves = {}, [], None
     for d in args.summarize_counters:
         per = {}
@@ -466,14 +596,20 @@ def summarize_counters(args):
         raise SystemExit(f"no dispatch of {args.kernel} in {args.summarize_counters}")
     avg = {c: float(np.mean(v)) for c, v in vals.items()}
     t = float(np.median(dur))
-    cyc = t * CLOCK_GHZ * 1e9
+    clock_ghz, clock_src = CLOCK_GHZ, "nominal"
+    if avg.get("GRBM_GUI_ACTIVE", 0) > 0:
+        clock_ghz, clock_src = avg["GRBM_GUI_ACTIVE"] / XCCS / t / 1e9, "measured"
+    cyc = t * clock_ghz * 1e9
     lines = [f"# SQ counters of {args.kernel}, workload {args.workload}",
              f"# command: {args.command}",
              f"# {len(vals[next(iter(vals))])} dispatches per counter; kernel {t * 1e6:.1f} us "
-             f"(dispatch timestamps, median), {waves} waves", ""]
+             f"(dispatch timestamps, median), {waves} waves; engine clock {clock_ghz:.3f} GHz "
+             f"({clock_src})", ""]
     for c in sorted(avg):
         lines.append(f"{c:32s} {avg[c]:18.0f}")
-    der = {}
+    der = {"clock_ghz": clock_ghz}
+    if "MfmaUtil" in avg:
+        der["rocprof_mfma_util_share"] = avg["MfmaUtil"] / 100
     if "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
         der["mfma_busy_share"] = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (SIMDS * cyc)
     if "SQ_INSTS_VALU_MFMA_MOPS_F16" in avg:
@@ -495,6 +631,7 @@ def summarize_counters(args):
     lines += ["", "# derived (per MFMA instruction: 16 busy cycles each for 16x16x32 f16)"]
     lines += [f"{k:48s} {v:12.4f}" for k, v in der.items()]
     lines.append(json.dumps({"kernel": args.kernel, "workload": args.workload, "kernel_us": round(t * 1e6, 2),
+                             "clock": clock_src,
                              "counters": {c: round(v) for c, v in avg.items()},
                              "derived": {k: round(v, 4) for k, v in der.items()}}))
     text = "\n".join(lines) + "\n"
@@ -584,6 +721,9 @@ def main():
     # breakdown, after the timed steps
     merge_ms = d.merge_ms(max(args.steps // 2, 3))
     unfused_ms = d.unfused_step_ms(max(args.steps // 2, 3))
+    kv_only, _ = decode_bytes(w)
+    ceiling = stream_ceiling(torch, nv, d.plan, d.sets, d.ws, max(args.steps // 2, 3), kv_only,
+                             attn_ms)
 
     kv, qo = decode_bytes(w, append=True)
     value = kv / (ms_step * 1e-3) / 1e9
@@ -621,18 +761,26 @@ def main():
                               "merge": round(merge_ms, 5),
                               "unfused_step_gpu": round(unfused_ms, 5)},
         "plan_host_us": round(d.plan_us, 1),
+        "stream_ceiling": ceiling,
     }
+    budget = 0.0 if args.no_cpu_baseline else args.cpu_seconds
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(d.sets[0], budget, cpu_threads())
+        out["cpu_baseline"] = {
+            "value": cb["value_threads"], "unit": "GB/s", "cores": cb["threads"], "kind": "oracle",
+            "sample": f"{cb['sample_threads']} of the {w.name} workload on {cb['threads']} host "
+                      "threads (numpy float64, BLAS one thread each; pairs run in parallel)",
+            "value_1_thread": cb["value_1_thread"], "sample_1_thread": cb["sample_1_thread"],
+            "full_workload_s_extrapolated": cb["full_workload_s_extrapolated"]}
     if not args.no_extra:
         del d
         torch.cuda.empty_cache()
-        extras = [extra_decode(torch, nv, paged, synth, n) for n in ("long_decode", "asym_decode")]
-        extras += [extra_prefill(torch, nv, paged, synth, n) for n in ("prefill_extend", "asym_prefill")]
+        out["single_decode_latency"] = single_decode_latency(torch, nv, paged, synth)
+        extras = [extra_decode(torch, nv, paged, synth, n, cpu_budget=budget)
+                  for n in ("long_decode", "asym_decode")]
+        extras += [extra_prefill(torch, nv, paged, synth, n, cpu_budget=budget)
+                   for n in ("prefill_extend", "asym_prefill")]
         out["other_workloads"] = extras
-        case0 = paged.build_case(w, keep_sources=True)
-    else:
-        case0 = d.sets[0]
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(case0, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

@@ -234,8 +234,28 @@ nvfp4_status nvfp4_batch_decode_append(const nvfp4_plan* plan, const void* q,
                                        float* lse, void* stream);
 
 /*
- * Kernel timing for benchmarks and profilers.  While set, every decode and prefill
- * attention launch made by the calling host thread is dispatched with these HIP
+ * Checksum of the paged KV bytes that a decode plan's attention reads, streamed through
+ * the same work items, per-wave LDS rings, copies and waits as nvfp4_batch_decode, with
+ * no attention arithmetic ([XQA] walkthrough: paged decode streams packed K/V and their
+ * scale factors through the page table).  It measures what that access pattern alone
+ * sustains, and checks a cache's bytes.
+ *   checksum: device uint32 [batch, num_kv_heads]; entry (b, h) = XOR of every 32-bit
+ *     little-endian word of the packed K rows, packed V rows, K scale rows and V scale
+ *     rows (each row on its own) of tokens [0, kv_len_b) of request b, kv head h; 0 for
+ *     kv_len_b = 0.  Written in full (zeroed first) on `stream`.
+ * plan: a decode plan (NVFP4_E_SHAPE otherwise) with page_size >= 16
+ * (NVFP4_E_UNSUPPORTED otherwise), uploaded to `workspace`.  Other arguments and errors
+ * as for nvfp4_batch_decode.  A page-table entry outside [0, num_pages) reads page 0 in
+ * its place (nothing outside the pools is read); that checksum is then meaningless.
+ */
+nvfp4_status nvfp4_kv_checksum(const nvfp4_plan* plan, const int32_t* page_table,
+                               int64_t pt_stride, const nvfp4_kv_pool* k_pool,
+                               const nvfp4_kv_pool* v_pool, void* workspace,
+                               size_t workspace_bytes, uint32_t* checksum, void* stream);
+
+/*
+ * Kernel timing for benchmarks and profilers.  While set, every decode, prefill and
+ * checksum launch made by the calling host thread is dispatched with these HIP
  * events (hipEvent_t, cast to void*), which the dispatch itself timestamps when the
  * kernel starts and when it ends (hipExtLaunchKernel), so that their elapsed time is
  * the kernel's own duration without extra queue packets.  The merge and append

@@ -88,3 +88,33 @@ def test_counter_summary_derivations(tmp_path):
     assert der["sq_insts_salu_per_mfma"] == pytest.approx(2.0)
     # wave cycles count in units of four cycles
     assert der["sq_wave_cycles_cycles_per_mfma"] == pytest.approx(72.0)
+
+
+def test_counter_summary_measures_the_clock(tmp_path):
+    """With GRBM_GUI_ACTIVE in a pass (summed over 8 XCCs) the summary derives the engine
+    clock from it instead of assuming 2.4 GHz: a 1 ms kernel at 2.1 GHz whose MFMAs keep
+    the matrix units busy 40 % of the measured cycles."""
+    clock = 2.1e9
+    cyc = 1e-3 * clock
+    counters = {"SQ_VALU_MFMA_BUSY_CYCLES": 0.4 * bench.SIMDS * cyc, "SQ_INSTS_MFMA": 100.0,
+                "GRBM_GUI_ACTIVE": bench.XCCS * cyc, "MfmaUtil": 40.0}
+    d = tmp_path / "p" / "host"
+    d.mkdir(parents=True)
+    with open(d / "run_counter_collection.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name",
+                                          "Counter_Value", "Start_Timestamp", "End_Timestamp",
+                                          "Grid_Size"])
+        w.writeheader()
+        for c, v in counters.items():
+            w.writerow({"Dispatch_Id": 1, "Kernel_Name": "prefill_coop_kernel<128, 128>",
+                        "Counter_Name": c, "Counter_Value": v, "Start_Timestamp": 0,
+                        "End_Timestamp": 1_000_000, "Grid_Size": 64 * 10})
+    out = tmp_path / "s.txt"
+    args = types.SimpleNamespace(summarize_counters=[str(tmp_path / "p")], kernel="prefill_coop_kernel",
+                                 workload="w", command="synthetic", out=str(out))
+    bench.summarize_counters(args)
+    rec = __import__("json").loads(out.read_text().strip().splitlines()[-1])
+    assert rec["clock"] == "measured"
+    assert rec["derived"]["clock_ghz"] == pytest.approx(2.1, rel=1e-4)
+    assert rec["derived"]["mfma_busy_share"] == pytest.approx(0.4, rel=1e-4)
+    assert rec["derived"]["rocprof_mfma_util_share"] == pytest.approx(0.4)

@@ -246,6 +246,21 @@ def test_prefill_layouts_and_pages(layout, page_size):
     _run_case(w, layout=layout, chunk=-1)
 
 
+@pytest.mark.parametrize("dk,dv", [(512, 256), (256, 128)])
+@pytest.mark.parametrize("hkv", [2, 8])
+@pytest.mark.parametrize("page_size", [1, 16])
+def test_prefill_asymmetric_support_matrix(dk, dv, hkv, page_size):
+    """Asymmetric prefill over (512, 256) and (256, 128), page sizes 1 and 16, two and
+    eight kv heads ([PF] commit on unequal K/V strides, support half: the matrix its
+    tests cover).  Ragged causal extend, two qo heads per kv head."""
+    w = synth.custom(f"pasym{dk}x{dv}h{hkv}p{page_size}", kv_lens=[70, 161, 33],
+                     qo_lens=[70, 40, 9], num_qo_heads=2 * hkv, num_kv_heads=hkv,
+                     head_dim_qk=dk, head_dim_vo=dv, page_size=page_size, causal=True,
+                     seed=dk + hkv + page_size)
+    _run_case(w, chunk=-1)
+    _run_case(w, chunk=32)
+
+
 def test_prefill_unequal_strides():
     w = synth.custom("pstrides", kv_lens=[64, 180], qo_lens=[64, 30], num_qo_heads=8,
                      num_kv_heads=2, causal=True, seed=23)
@@ -291,6 +306,111 @@ def test_merge_states_matches_oracle():
     o_ref, lse_ref = ref.merge_states(np.moveaxis(o_parts, 1, 0), np.moveaxis(lse_parts, 1, 0))
     gh.assert_attention_close(o.cpu().double().numpy(), lse.cpu().double().numpy(), o_ref, lse_ref)
     assert np.abs(o.cpu().numpy() - o_ref).max() < 1e-5
+
+
+@pytest.mark.parametrize("d,n,heads", [(64, 9, 3), (256, 13, 2), (512, 70, 1), (4, 1, 5)])
+def test_merge_states_dims_and_many_parts(d, n, heads):
+    """Head dims 64..512 and more parts than any fixed unroll (up to 70), with -inf
+    parts, fully empty rows and one part dominating by a wide margin."""
+    rng = np.random.default_rng(d + n)
+    rows = 23
+    o_parts = rng.standard_normal((rows, n, heads, d)).astype(np.float32)
+    lse_parts = (rng.standard_normal((rows, n, heads)) * 4).astype(np.float32)
+    lse_parts[0, : max(1, n - 1)] = -np.inf        # one live part (or none when n == 1)
+    lse_parts[1] = -np.inf                          # empty row
+    lse_parts[2, 0] = 80.0                          # dominates the rest
+    o, lse = nv.merge_states(torch.from_numpy(o_parts).cuda(), torch.from_numpy(lse_parts).cuda())
+    torch.cuda.synchronize()
+    o_ref, lse_ref = ref.merge_states(np.moveaxis(o_parts, 1, 0), np.moveaxis(lse_parts, 1, 0))
+    o, lse = o.cpu().double().numpy(), lse.cpu().double().numpy()
+    assert np.array_equal(np.isinf(lse), np.isinf(lse_ref))
+    fin = np.isfinite(lse_ref)
+    assert np.abs(lse[fin] - lse_ref[fin]).max() <= 1e-5 * max(1.0, np.abs(lse_ref[fin]).max())
+    assert np.abs(o - o_ref).max() < 1e-5
+    assert np.all(o[1] == 0)
+
+
+def test_decode_more_than_64_partials():
+    """16-token chunks over long rows: up to 71 partial states per row group, past the
+    merge kernel's 8-part fast path and its 64-LSE batches."""
+    w = synth.custom("manyparts", kv_lens=[4500, 1100, 16], num_qo_heads=8, num_kv_heads=2,
+                     seed=61)
+    _, plan = _run_case(w, chunk=16)
+    assert plan.info()["num_partials"] > 64
+
+
+# ------------------------------------------------------------ bad page entries --
+
+def _new_rows(w, seed):
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    kn = torch.randn((w.batch, w.num_kv_heads, w.head_dim_qk), generator=g).to(torch.bfloat16)
+    vn = torch.randn((w.batch, w.num_kv_heads, w.head_dim_vo), generator=g).to(torch.bfloat16)
+    return kn, vn
+
+
+@pytest.mark.parametrize("kind,page_size,chunk", [
+    ("decode", 16, -1), ("decode", 16, 64), ("decode", 4, 32), ("append", 16, 64),
+    ("append", 16, -1), ("prefill", 16, -1), ("prefill", 16, 64), ("prefill", 1, -1)])
+@pytest.mark.parametrize("entry", ["num_pages", "minus_one"])
+def test_bad_page_entry_gives_nan_rows(kind, page_size, chunk, entry):
+    """A page-table entry outside [0, num_pages) is read as nothing: the rows of its
+    request come out NaN (O and LSE), every other request's rows equal the oracle, and
+    (append) nothing is written through it.  The kernels clamp the entry before forming
+    any address, so no pool byte outside the pools is touched."""
+    decode = kind != "prefill"
+    lens = [150, 300, 77]
+    w = synth.custom(f"badpage_{kind}", kv_lens=lens, qo_lens=None if decode else [30, 45, 20],
+                     num_qo_heads=8, num_kv_heads=2, page_size=page_size, causal=False, seed=71)
+    c = gh.build_oracle_case(w)
+    bad = c.k_pool.num_pages if entry == "num_pages" else -1
+    # request 1: its second page, or (append) the page its new token goes to
+    idx = (lens[1] - 1) // page_size if kind == "append" else 1
+    c.page_table[1, idx] = bad
+    plan = gh.make_plan(w, chunk)
+    ws = plan.new_workspace()
+    plan.upload(ws)
+    rows = c.q.shape[0]
+    o = torch.full((rows, w.num_qo_heads, w.head_dim_vo), 7.0, device="cuda")
+    lse = torch.full((rows, w.num_qo_heads), 7.0, device="cuda")
+    if kind == "append":
+        kn, vn = _new_rows(w, 72)
+        before = (c.k_pool.data.clone(), c.v_pool.data.clone(), c.k_pool.sf.clone(),
+                  c.v_pool.sf.clone())
+        nv.batch_decode_append(plan, c.q, kn.cuda(), vn.cuda(), c.page_table, c.k_pool,
+                               c.v_pool, w.sm_scale, ws, out=o, lse=lse)
+        # the oracle's pools get the other requests' new tokens
+        pt, P = c.pt, w.page_size
+        for b in (0, 2):
+            t = lens[b] - 1
+            pg, off = pt[b, t // P], t % P
+            for (data, sf), x in ((c.k_np, kn), (c.v_np, vn)):
+                pk, ps = ref.quantize(x[b].double().numpy())
+                data[pg, :, off], sf[pg, :, off] = pk, ps
+    elif decode:
+        nv.batch_decode(plan, c.q, c.page_table, c.k_pool, c.v_pool, w.sm_scale, ws, out=o,
+                        lse=lse)
+    else:
+        nv.batch_prefill(plan, c.q, c.page_table, c.k_pool, c.v_pool, w.sm_scale, ws, out=o,
+                         lse=lse)
+    torch.cuda.synchronize()
+    o, lse = o.cpu().double().numpy(), lse.cpu().double().numpy()
+    ind = synth.indptr(w.qo_lens)
+    r0, r1 = int(ind[1]), int(ind[2])
+    assert np.isnan(o[r0:r1]).all() and np.isnan(lse[r0:r1]).all()
+    o_ref, lse_ref = gh.oracle_reference(c, rows=[0, 2])
+    keep = np.ones(rows, dtype=bool)
+    keep[r0:r1] = False
+    gh.assert_attention_close(o[keep], lse[keep], o_ref[keep], lse_ref[keep], w.name)
+    if kind == "append":
+        # request 1's new token had no valid page: the pools hold the other two tokens'
+        # new bytes and nothing else changed
+        after = (c.k_pool.data, c.v_pool.data, c.k_pool.sf, c.v_pool.sf)
+        changed = [torch.nonzero((a != b_).reshape(a.shape[0], -1).any(1)).flatten().tolist()
+                   for a, b_ in zip(after, before)]
+        allowed = {int(c.pt[b, (lens[b] - 1) // w.page_size]) for b in (0, 2)}
+        for ch in changed:
+            assert set(ch) <= allowed, (ch, allowed)
 
 
 @pytest.mark.parametrize("decode", [True, False])
@@ -484,3 +604,44 @@ def test_timing_events_bracket_the_kernel():
     finally:
         for e in ev:
             hip.hipEventDestroy(e)
+
+
+# ------------------------------------------------------------ KV checksum ------
+
+def _host_checksum(c, b, h):
+    """XOR of every 32-bit word of request b's K/V rows and scale rows of kv head h,
+    each row taken on its own, gathered through the page table on the host."""
+    w = c.w
+    x = np.uint32(0)
+    for arr in (c.k_np[0], c.k_np[1], c.v_np[0], c.v_np[1]):
+        rows = ref.gather_pages(arr, c.pt[b], w.kv_lens[b], w.page_size, c.layout)[:, h]
+        words = np.ascontiguousarray(rows).view(np.uint32)
+        if words.size:
+            x ^= np.bitwise_xor.reduce(words.ravel())
+    return int(x)
+
+
+@pytest.mark.parametrize("dk,dv,hq,hkv,layout,chunk,pads", [
+    (128, 128, 8, 2, "HND", -1, False), (128, 128, 8, 2, "HND", 32, False),
+    (64, 64, 4, 1, "NHD", 64, False), (512, 256, 8, 1, "HND", 0, False),
+    (256, 128, 40, 2, "HND", 16, True), (128, 64, 4, 2, "NHD", -1, True)])
+def test_kv_checksum_is_exact(dk, dv, hq, hkv, layout, chunk, pads):
+    """The streaming checksum equals the XOR of the same rows' words taken on the host,
+    bit for bit: every byte the decode pattern streams arrives, each exactly once, and
+    nothing past a request's last key is folded in (pool slots there hold random bytes).
+    Group 40 runs three blocks of qo heads over the same keys; only one streams."""
+    w = synth.custom(f"cks{dk}x{dv}", kv_lens=[150, 300, 77, 0, 33, 1], num_qo_heads=hq,
+                     num_kv_heads=hkv, head_dim_qk=dk, head_dim_vo=dv, seed=dk + hq)
+    kw = dict(k_pad=(1, 1, 3, 16), v_pad=(2, 0, 1, 32)) if pads else {}
+    c = gh.build_oracle_case(w, layout=layout, **kw)
+    plan = gh.make_plan(w, chunk)
+    ws = plan.new_workspace()
+    plan.upload(ws)
+    out = torch.full((w.batch, hkv), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
+    nv.kv_checksum(plan, c.page_table, c.k_pool, c.v_pool, ws, out=out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint32)
+    for b in range(w.batch):
+        for h in range(hkv):
+            assert int(got[b, h]) == _host_checksum(c, b, h), (b, h)
+    assert got[3].tolist() == [0] * hkv
