@@ -17,7 +17,8 @@ import torch
 from ._lib import (EXPORTS, STATUS, WORK_FIELDS, KVPoolStruct, NVFP4Error, PlanInfoStruct,
                    check, lib)
 
-__all__ = ["KVPool", "Plan", "Prepared", "quantize_kv", "batch_decode", "batch_decode_append",
+__all__ = ["KVPool", "Plan", "Prepared", "quantize_kv", "batch_decode", "batch_decode_noalloc",
+           "batch_decode_append",
            "batch_prefill", "kv_checksum",
            "merge_partials", "merge_states", "NVFP4Error", "lib", "version", "EXPORTS"]
 
@@ -331,6 +332,25 @@ def batch_decode(plan: Plan, q: torch.Tensor, page_table: torch.Tensor, k_pool: 
     ``Prepared`` call with ``prepare=True``."""
     return _attn(lib.nvfp4_batch_decode, plan, q, page_table, k_pool, v_pool, sm_scale,
                  workspace, out, lse, stream, prepare)
+
+
+def batch_decode_noalloc(plan: Plan, q: torch.Tensor, page_table: torch.Tensor, k_pool: KVPool,
+                         v_pool: KVPool, sm_scale: float, out: torch.Tensor, lse: torch.Tensor,
+                         stream=None):
+    """Decode with the library's fixed per-GPU scratch in place of a workspace
+    (nvfp4_batch_decode_noalloc): allocates nothing, so ``out`` and ``lse`` must be
+    given.  Calls that overlap on one GPU race on the shared scratch."""
+    if out is None or lse is None:
+        raise ValueError("out and lse must be given: the call allocates nothing")
+    _check_rows(plan, q, page_table, out, lse)
+    _check_pools(plan, k_pool, v_pool)
+    dev = _device(q, page_table, k_pool.data, k_pool.sf, v_pool.data, v_pool.sf, out, lse)
+    ks, vs = k_pool.struct(), v_pool.struct()
+    check(lib.nvfp4_batch_decode_noalloc(
+        plan.handle, _ptr(q), q.stride(0), q.stride(1), _ptr(page_table), page_table.stride(0),
+        ctypes.byref(ks), ctypes.byref(vs), float(sm_scale), _ptr(out), out.stride(0),
+        out.stride(1), _ptr(lse), _stream(stream, dev)))
+    return out, lse
 
 
 def batch_decode_append(plan: Plan, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,

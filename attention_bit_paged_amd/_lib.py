@@ -26,6 +26,7 @@ EXPORTS = (
     "nvfp4_last_error", "nvfp4_version", "nvfp4_quantize_kv", "nvfp4_plan_create",
     "nvfp4_plan_destroy", "nvfp4_plan_workspace_bytes", "nvfp4_plan_get_info",
     "nvfp4_plan_get_work", "nvfp4_plan_upload", "nvfp4_batch_decode",
+    "nvfp4_batch_decode_noalloc",
     "nvfp4_batch_decode_append", "nvfp4_kv_checksum", "nvfp4_set_timing_events",
     "nvfp4_batch_prefill",
     "nvfp4_plan_set_deferred_merge", "nvfp4_merge_partials", "nvfp4_merge_states",
@@ -94,6 +95,8 @@ def _load():
         "nvfp4_plan_upload": (ctypes.c_int, [vp, vp, sz, vp]),
         "nvfp4_batch_decode": (ctypes.c_int, [vp, vp, i64, i64, vp, i64, pool_p, pool_p, f32, vp, sz,
                                               vp, i64, i64, vp, vp]),
+        "nvfp4_batch_decode_noalloc": (ctypes.c_int, [vp, vp, i64, i64, vp, i64, pool_p, pool_p,
+                                                      f32, vp, i64, i64, vp, vp]),
         "nvfp4_batch_decode_append": (ctypes.c_int, [vp, vp, i64, i64, vp, i64, i64, vp, i64, i64,
                                                      vp, i64, pool_p, pool_p, f32, vp, sz,
                                                      vp, i64, i64, vp, vp]),

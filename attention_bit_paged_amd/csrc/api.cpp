@@ -181,6 +181,7 @@ struct nvfp4_plan {
   // workspace layout (byte offsets)
   size_t off_work = 0, off_merge = 0, off_kvlens = 0, off_indptr = 0,
          off_part_o = 0, off_part_lse = 0, ws_bytes = 0;
+  std::vector<uint8_t> image;  // the tables as they sit at the start of the workspace
   void* uploaded_to = nullptr;
   int defer_merge = 0;  // runs leave split rows' partials for nvfp4_merge_partials
 };
@@ -402,6 +403,15 @@ nvfp4_status nvfp4_plan_create(const int32_t* kv_lens, const int32_t* qo_indptr,
   plan->off_part_lse = off;
   off = align_up(off + (size_t)plan->num_partials * plan->rows_per_slot * sizeof(float));
   plan->ws_bytes = std::max<size_t>(off, kAlign);
+  // the uploaded part of the workspace, built once
+  plan->image.assign(plan->off_part_o, 0);
+  auto put = [&](size_t at, const std::vector<int32_t>& v) {
+    if (!v.empty()) std::memcpy(plan->image.data() + at, v.data(), v.size() * sizeof(int32_t));
+  };
+  put(plan->off_work, plan->work);
+  put(plan->off_merge, plan->merges);
+  put(plan->off_kvlens, plan->kv_lens);
+  put(plan->off_indptr, plan->qo_indptr);
   *out = plan;
   return ok();
 }
@@ -440,18 +450,11 @@ nvfp4_status nvfp4_plan_upload(nvfp4_plan* plan, void* workspace, size_t workspa
     return fail(NVFP4_E_WORKSPACE, "workspace has %zu bytes, plan needs %zu", workspace_bytes,
                 plan->ws_bytes);
   if (nvfp4_status st = check_device(stream)) return st;
-  // One host staging buffer for the tables, then one copy.
-  std::vector<uint8_t> host(plan->off_part_o, 0);
-  auto put = [&](size_t off, const std::vector<int32_t>& v) {
-    if (!v.empty()) std::memcpy(host.data() + off, v.data(), v.size() * sizeof(int32_t));
-  };
-  put(plan->off_work, plan->work);
-  put(plan->off_merge, plan->merges);
-  put(plan->off_kvlens, plan->kv_lens);
-  put(plan->off_indptr, plan->qo_indptr);
+  // the plan's table image, in one copy
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (!host.empty()) {
-    hipError_t e = hipMemcpyAsync(workspace, host.data(), host.size(), hipMemcpyHostToDevice, s);
+  if (!plan->image.empty()) {
+    hipError_t e = hipMemcpyAsync(workspace, plan->image.data(), plan->image.size(),
+                                  hipMemcpyHostToDevice, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) return fail(NVFP4_E_HIP, "plan upload failed: %s", hipGetErrorString(e));
   }
@@ -467,7 +470,7 @@ nvfp4_status check_run(const nvfp4_plan* plan, bool prefill, const void* q, int6
                        int64_t q_s_head, const int32_t* page_table, int64_t pt_stride,
                        const nvfp4_kv_pool* k, const nvfp4_kv_pool* v, float sm_scale,
                        void* ws, size_t ws_bytes, float* o, int64_t o_s_row, int64_t o_s_head,
-                       float* lse, void* stream) {
+                       float* lse, void* stream, bool need_upload = true) {
   if (!plan) return fail(NVFP4_E_INVALID, "plan is NULL");
   if (plan->prefill != (int)prefill)
     return fail(NVFP4_E_SHAPE, "plan was made for %s, called for %s",
@@ -502,9 +505,44 @@ nvfp4_status check_run(const nvfp4_plan* plan, bool prefill, const void* q, int6
   if (ws_bytes < plan->ws_bytes)
     return fail(NVFP4_E_WORKSPACE, "workspace has %zu bytes, plan needs %zu", ws_bytes,
                 plan->ws_bytes);
-  if (plan->uploaded_to != ws)
+  if (need_upload && plan->uploaded_to != ws)
     return fail(NVFP4_E_WORKSPACE, "the plan was not uploaded to this workspace (nvfp4_plan_upload)");
   return check_device(stream);
+}
+
+// ---- Allocation-free decode: one fixed scratch array per GPU in place of the caller's
+// workspace.  In host code `scratch` names a host-side stand-in, never the device
+// memory: its device address is taken once per device (hipGetSymbolAddress, with that
+// device current) and only that address is used.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];
+
+nvfp4_status scratch_address(void* stream, void** out) {
+  int dev = -1;
+  if (nvfp4_status st = stream_device(stream, &dev)) return st;
+  if (dev >= 64) return fail(NVFP4_E_DEVICE, "device ordinal %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) cur = -1;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(NVFP4_E_HIP, "cannot make device %d current to find its scratch array", dev);
+    }
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev && cur >= 0) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return fail(NVFP4_E_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                  hipGetErrorString(e));
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return NVFP4_OK;
 }
 
 AttnArgs make_args(const nvfp4_plan* plan, const void* q, int64_t q_s_row, int64_t q_s_head,
@@ -582,6 +620,43 @@ nvfp4_status nvfp4_batch_decode(const nvfp4_plan* plan, const void* q, int64_t q
                                 void* stream) {
   return run(plan, false, q, q_stride_req, q_stride_head, page_table, pt_stride, k_pool, v_pool,
              sm_scale, workspace, workspace_bytes, o, o_stride_req, o_stride_head, lse, stream);
+}
+
+nvfp4_status nvfp4_batch_decode_noalloc(const nvfp4_plan* plan, const void* q,
+                                        int64_t q_stride_req, int64_t q_stride_head,
+                                        const int32_t* page_table, int64_t pt_stride,
+                                        const nvfp4_kv_pool* k_pool, const nvfp4_kv_pool* v_pool,
+                                        float sm_scale, float* o, int64_t o_stride_req,
+                                        int64_t o_stride_head, float* lse, void* stream) {
+  if (!plan) return fail(NVFP4_E_INVALID, "plan is NULL");
+  if (plan->ws_bytes > kScratchBytes)
+    return fail(NVFP4_E_WORKSPACE, "the plan needs %zu bytes of workspace; the allocation-free "
+                "entry point has a fixed %zu (use nvfp4_batch_decode with a workspace)",
+                plan->ws_bytes, kScratchBytes);
+  // every check of nvfp4_batch_decode, with the scratch array as the workspace
+  static float probe[4] __attribute__((aligned(16)));
+  if (nvfp4_status st = check_run(plan, false, q, q_stride_req, q_stride_head, page_table,
+                                  pt_stride, k_pool, v_pool, sm_scale, probe, kScratchBytes, o,
+                                  o_stride_req, o_stride_head, lse, stream, false))
+    return st;
+  void* ws = nullptr;
+  if (nvfp4_status st = scratch_address(stream, &ws)) return st;
+  if (plan->work.empty()) return ok();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // the plan's tables into the scratch array, ordered before the kernels on the stream
+  hipError_t e = hipMemcpyAsync(ws, plan->image.data(), plan->image.size(),
+                                hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return fail(NVFP4_E_HIP, "plan copy failed: %s", hipGetErrorString(e));
+  const AttnArgs a = make_args(plan, q, q_stride_req, q_stride_head, page_table, pt_stride, k_pool,
+                               v_pool, sm_scale, ws, o, o_stride_req, o_stride_head, lse);
+  e = launch_decode(plan->head_dim_qk, plan->head_dim_vo, a.page_shift, a, s);
+  if (e != hipSuccess) return fail(NVFP4_E_HIP, "decode launch failed: %s", hipGetErrorString(e));
+  const int n_merges = (int)(plan->merges.size() / kMergeFields);
+  if (n_merges > 0) {  // always merged here: the partials live in the shared scratch
+    e = launch_merge_partials(a, n_merges, plan->head_dim_vo, 0, s);
+    if (e != hipSuccess) return fail(NVFP4_E_HIP, "merge launch failed: %s", hipGetErrorString(e));
+  }
+  return ok();
 }
 
 nvfp4_status nvfp4_batch_decode_append(const nvfp4_plan* plan, const void* q,

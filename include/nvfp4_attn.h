@@ -209,6 +209,29 @@ nvfp4_status nvfp4_batch_decode(const nvfp4_plan* plan, const void* q, int64_t q
                                 void* stream);
 
 /*
+ * nvfp4_batch_decode without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  The library keeps one fixed scratch array of 32 MiB per GPU (a device
+ * global, held until the process ends) and uses it as the workspace: each call copies
+ * the plan's tables into it on `stream` (the host tables are read before the call
+ * returns), then runs the decode and the merge of the split rows.  The call allocates
+ * nothing, host or device.
+ *   plan: a decode plan whose nvfp4_plan_workspace_bytes is at most 32 MiB
+ *     (NVFP4_E_WORKSPACE otherwise); it need not be uploaded.  Its deferred-merge
+ *     setting is ignored: split rows are always merged by the call.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's contents:
+ * calls that overlap on one GPU (on different streams, or from different threads
+ * without ordering) race and must not be issued.  Other arguments, outputs and errors
+ * as for nvfp4_batch_decode.
+ */
+nvfp4_status nvfp4_batch_decode_noalloc(const nvfp4_plan* plan, const void* q,
+                                        int64_t q_stride_req, int64_t q_stride_head,
+                                        const int32_t* page_table, int64_t pt_stride,
+                                        const nvfp4_kv_pool* k_pool, const nvfp4_kv_pool* v_pool,
+                                        float sm_scale, float* o, int64_t o_stride_req,
+                                        int64_t o_stride_head, float* lse, void* stream);
+
+/*
  * Decode with the step's new token appended in the same launch.  For every request b
  * with kv_len_b >= 1, the rows k_new[b] and v_new[b] (device bf16 [batch,
  * num_kv_heads, head_dim_qk / head_dim_vo], element strides, last dim contiguous,

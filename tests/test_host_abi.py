@@ -295,3 +295,19 @@ def test_binding_checks_sources_and_merge_shapes():
         nv.merge_partials(plan, ws, torch.zeros((2, 4, 128)), torch.zeros((1, 4)))
     with pytest.raises(ValueError, match="lse must"):
         nv.merge_partials(plan, ws, torch.zeros((1, 4, 128)), torch.zeros((1, 4), dtype=torch.float64))
+
+
+def test_noalloc_decode_rejects_plans_beyond_its_scratch():
+    """The allocation-free decode has a fixed 32 MiB scratch: a plan that needs more is
+    refused, by name, before anything touches a device."""
+    big = nv.Plan([8192] * 64, num_qo_heads=64, num_kv_heads=4, head_dim_qk=256,
+                  kv_chunk_tokens=16, num_cus=256)
+    assert big.workspace_bytes > 32 << 20
+    pool = _fake_pool(head_dim=256, heads=4, pages=40000)
+    st = nv.lib.nvfp4_batch_decode_noalloc(big.handle, ctypes.c_void_p(0x1000), 64 * 256, 256,
+                                           ctypes.c_void_p(0x2000), 512, ctypes.byref(pool),
+                                           ctypes.byref(pool), 0.1, ctypes.c_void_p(0x3000),
+                                           64 * 256, 256, ctypes.c_void_p(0x4000), None)
+    assert _lib.STATUS[st] == "NVFP4_E_WORKSPACE"
+    msg = nv.lib.nvfp4_last_error().decode()
+    assert "allocation-free" in msg and str(32 << 20) in msg
