@@ -578,6 +578,9 @@ AttnArgs make_args(const nvfp4_plan* plan, const void* q, int64_t q_s_row, int64
   a.rows_per_slot = plan->rows_per_slot;
   a.causal = plan->causal;
   a.merges = reinterpret_cast<const int32_t*>(w + plan->off_merge);
+  // heads within 256 bytes of each other share cache lines / DRAM bursts: keep the
+  // heads of one key range on one XCD (decode)
+  a.xcd_group = !plan->prefill && (std::min(k->stride_head, v->stride_head) <= 256);
   return a;
 }
 

@@ -119,8 +119,21 @@ struct DecodeItem {
   bool head_valid;
 };
 
+// The work item of this workgroup.  Workgroups are dealt to the eight XCDs in turn
+// (workgroup i to XCD i % 8), and the planner puts the kv heads of one key range next
+// to each other.  With xcd_group, each full run of 64 workgroups is permuted so that
+// eight consecutive items (the heads of one key range) run on one XCD: when the pools
+// interleave heads at a short stride (NHD pages, pages of one token) those heads' rows
+// share cache lines, which that XCD's L2 then fetches once instead of eight XCDs each.
+__device__ __forceinline__ int decode_item_index(const AttnArgs& a) {
+  const int bid = blockIdx.x;
+  if (!a.xcd_group || bid >= (a.n_work & ~63)) return bid;
+  const int r = bid & 63;
+  return (bid & ~63) + ((r & 7) << 3) + (r >> 3);
+}
+
 __device__ __forceinline__ DecodeItem decode_item(const AttnArgs& a, int wave, int n) {
-  const int32_t* rec = a.work + (int64_t)blockIdx.x * kWorkFields;
+  const int32_t* rec = a.work + (int64_t)decode_item_index(a) * kWorkFields;
   DecodeItem it;
   it.b = rec[W_REQ]; it.kvh = rec[W_KVH]; it.h0 = rec[W_ROW0]; it.hn = rec[W_ROWS];
   it.kv0 = rec[W_KV0]; it.kv1 = rec[W_KV1]; it.slot = rec[W_SLOT]; it.merge = rec[W_MERGE];

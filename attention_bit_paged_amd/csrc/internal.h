@@ -60,6 +60,9 @@ struct AttnArgs {
   int32_t page_shift;       // log2(page_size)
   int32_t rows_per_slot;
   int32_t causal;
+  // Decode: deal each run of 64 work items to the XCDs in groups of eight consecutive
+  // items (see decode_item); set when the pools interleave kv heads at a short stride.
+  int32_t xcd_group;
   const int32_t* merges;    // merge records
   // Decode with append: the step's new K/V rows (bf16 [batch, kv heads, dim], element
   // strides), quantised into the slot of token kv_len-1 of their request by the work

@@ -33,16 +33,42 @@ class PagedCase:
 def poison_pool(pool: KVPool, seed: int) -> None:
     g = torch.Generator(device=pool.data.device)
     g.manual_seed(seed)
-    pool.data.copy_(torch.randint(0, 256, pool.data.shape, generator=g, dtype=torch.uint8,
+    pool.data.copy_(torch.randint(0, 256, tuple(pool.data.shape), generator=g, dtype=torch.uint8,
                                   device=pool.data.device))
     pool.sf.fill_(synth.SF_POISON)
 
 
+def padded_pool(w: synth.Workload, head_dim: int, layout: str, device, pad) -> KVPool:
+    """A pool whose tensors are views into larger parents, so that its strides differ
+    from a dense pool's: ``pad`` = extra (pages, heads, tokens, bytes per row) of the
+    parent (the scale rows get 8 extra bytes when the data rows get any)."""
+    pp, ph, pt, pb = pad
+    H, P = w.num_kv_heads, w.page_size
+    if layout == "HND":
+        lead, view = (w.pool_pages + pp, H + ph, P + pt), (w.pool_pages, H, P)
+    else:
+        lead, view = (w.pool_pages + pp, P + pt, H + ph), (w.pool_pages, P, H)
+    data = torch.empty(lead + (head_dim // 2 + pb,), dtype=torch.uint8, device=device)
+    sf = torch.empty(lead + (head_dim // 16 + (8 if pb else 0),), dtype=torch.uint8, device=device)
+    idx = tuple(slice(0, n) for n in view)
+    return KVPool(data[idx + (slice(0, head_dim // 2),)], sf[idx + (slice(0, head_dim // 16),)],
+                  head_dim=head_dim, layout=layout)
+
+
 def build_case(w: synth.Workload, device="cuda", layout="HND", poison=True,
-               keep_sources=True) -> PagedCase:
+               keep_sources=True, k_pad=None, v_pad=None) -> PagedCase:
+    """``k_pad`` / ``v_pad``: give that pool padded parents (see ``padded_pool``)."""
     q, k, v = synth.draw_qkv(w, device=device)
-    k_pool = KVPool.empty(w.pool_pages, w.num_kv_heads, w.page_size, w.head_dim_qk, layout, device)
-    v_pool = KVPool.empty(w.pool_pages, w.num_kv_heads, w.page_size, w.head_dim_vo, layout, device)
+    if k_pad is None:
+        k_pool = KVPool.empty(w.pool_pages, w.num_kv_heads, w.page_size, w.head_dim_qk, layout,
+                              device)
+    else:
+        k_pool = padded_pool(w, w.head_dim_qk, layout, device, k_pad)
+    if v_pad is None:
+        v_pool = KVPool.empty(w.pool_pages, w.num_kv_heads, w.page_size, w.head_dim_vo, layout,
+                              device)
+    else:
+        v_pool = padded_pool(w, w.head_dim_vo, layout, device, v_pad)
     if poison:
         poison_pool(k_pool, w.value_seed + 11)
         poison_pool(v_pool, w.value_seed + 12)

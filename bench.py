@@ -246,16 +246,19 @@ def cpu_baseline(case, budget_s, threads):
 
 def timed_passes(torch, nv, run, merge, iters):
     """Per-launch durations (ms) of the attention kernel (events carried by its dispatch)
-    and of the merge (events recorded around it)."""
+    and of the merge (events recorded around it).  ``run`` and ``merge`` may be lists
+    (one call per pool set), taken in turn."""
+    runs = run if isinstance(run, (list, tuple)) else [run]
+    merges = merge if isinstance(merge, (list, tuple)) else [merge]
     s = torch.cuda.current_stream()
     he = HipEvents()
     ev = [[he.new() for _ in range(4)] for _ in range(iters)]
-    for e in ev:
+    for i, e in enumerate(ev):
         he.time_launches(nv, e[0], e[1])
-        run()
+        runs[i % len(runs)]()
         he.time_launches(nv, None, None)
         he.record(e[2], s)
-        merge()
+        merges[i % len(merges)]()
         he.record(e[3], s)
     torch.cuda.synchronize()
     return (float(np.mean([he.ms(e[0], e[1]) for e in ev])),
@@ -324,6 +327,62 @@ def extra_prefill(torch, nv, paged, synth, name, iters=40, warm=10, cpu_budget=0
     del case, ws
     torch.cuda.empty_cache()
     return out
+
+
+# Layout variants of the batch decode and the prefill extend, each against the HND,
+# page size 16, dense-stride line measured the same way: (label, layout, page size,
+# K parent padding, V parent padding).  The padding makes K's and V's strides differ
+# from a dense pool's and from each other's.
+VARIANTS = (("HND_page16", "HND", 16, None, None),
+            ("NHD_page16", "NHD", 16, None, None),
+            ("HND_page16_unequal_strides", "HND", 16, (1, 1, 3, 16), (2, 0, 1, 32)),
+            ("HND_page1", "HND", 1, None, None))
+
+
+def variant_lines(torch, nv, paged, synth, name, iters=60, warm=12, pool_sets=3):
+    """Kernel throughput of one workload under each layout variant (same values, same
+    request lengths; the page size changes the pool's page count, not its bytes), over
+    ``pool_sets`` rotated pool sets like the main line."""
+    base = synth.workload(name)
+    lines, ref_rate = [], None
+    for label, layout, ps, kp, vp in VARIANTS:
+        w = synth.workload(name, page_size=ps, pool_pages=base.pool_pages * base.page_size // ps)
+        cases = [paged.build_case(w, keep_sources=False, layout=layout, k_pad=kp, v_pad=vp)
+                 for _ in range(pool_sets)]
+        case = cases[0]
+        plan = paged.make_plan(case)
+        plan.set_deferred_merge(True)
+        ws = plan.new_workspace()
+        plan.upload(ws)
+        o = torch.empty((w.total_q, w.num_qo_heads, w.head_dim_vo), device="cuda")
+        lse = torch.empty((w.total_q, w.num_qo_heads), device="cuda")
+        fn = nv.batch_decode if w.decode else nv.batch_prefill
+        run = [fn(plan, c.q, c.page_table, c.k_pool, c.v_pool, w.sm_scale, ws, out=o, lse=lse,
+                  prepare=True) for c in cases]
+        merge = nv.merge_partials(plan, ws, o, lse, prepare=True)
+        for i in range(warm):
+            run[i % len(run)]()
+            merge()
+        run_ms, _ = timed_passes(torch, nv, run, merge, iters)
+        if w.decode:
+            kv, qo = decode_bytes(w)
+            rate = (kv + qo) / run_ms / 1e6
+            line = {"variant": label, "kernel_GBs": round(rate, 1),
+                    "kernel_frac_hbm": round(rate / HBM_PEAK_GBS, 4)}
+        else:
+            rate = w.flops() / run_ms / 1e9
+            line = {"variant": label, "kernel_TFLOPs": round(rate, 2),
+                    "kernel_frac_mfma_f16": round(rate / MFMA_F16_PEAK_TFLOPS, 4)}
+        ref_rate = rate if ref_rate is None else ref_rate
+        line.update(attn_ms=round(run_ms, 4), vs_HND_page16=round(rate / ref_rate, 4),
+                    k_strides=[case.k_pool.struct().stride_page, case.k_pool.struct().stride_head,
+                               case.k_pool.struct().stride_token],
+                    v_strides=[case.v_pool.struct().stride_page, case.v_pool.struct().stride_head,
+                               case.v_pool.struct().stride_token])
+        lines.append(line)
+        del run, merge, case, cases, ws
+        torch.cuda.empty_cache()
+    return {"workload": name, "lines": lines}
 
 
 def stream_ceiling(torch, nv, plan, cases, ws, iters, kv_bytes, attn_ms):
@@ -781,6 +840,8 @@ def main():
         extras += [extra_prefill(torch, nv, paged, synth, n, cpu_budget=budget)
                    for n in ("prefill_extend", "asym_prefill")]
         out["other_workloads"] = extras
+        out["layout_variants"] = [variant_lines(torch, nv, paged, synth, n)
+                                  for n in ("batch_decode", "prefill_extend")]
     print(json.dumps(out), flush=True)
 
 

@@ -116,6 +116,17 @@ def test_decode_group_sizes(hq, hkv):
     _run_case(w, chunk=32)
 
 
+@pytest.mark.parametrize("layout,page_size", [("NHD", 16), ("HND", 4), ("NHD", 1)])
+def test_decode_xcd_grouped_items(layout, page_size):
+    """Pools whose kv heads sit at a short stride (NHD pages, small pages) run the work
+    items XCD-grouped: each full run of 64 workgroups is permuted.  Hundreds of items
+    (16-key chunks over ragged requests), so several full runs and a partial one."""
+    w = synth.custom(f"xcd{layout}{page_size}", kv_lens=[1000, 777, 1500, 64, 1203, 9],
+                     num_qo_heads=32, num_kv_heads=8, page_size=page_size, seed=81)
+    _, plan = _run_case(w, layout=layout, chunk=16)
+    assert plan.info()["num_work_items"] > 3 * 64
+
+
 @pytest.mark.parametrize("page_size", [1, 4, 8, 32, 64])
 def test_decode_page_sizes(page_size):
     w = synth.custom("pages", kv_lens=[3, 77, 130], num_qo_heads=8, num_kv_heads=2,
@@ -624,7 +635,8 @@ def _host_checksum(c, b, h):
 @pytest.mark.parametrize("dk,dv,hq,hkv,layout,chunk,pads", [
     (128, 128, 8, 2, "HND", -1, False), (128, 128, 8, 2, "HND", 32, False),
     (64, 64, 4, 1, "NHD", 64, False), (512, 256, 8, 1, "HND", 0, False),
-    (256, 128, 40, 2, "HND", 16, True), (128, 64, 4, 2, "NHD", -1, True)])
+    (256, 128, 40, 2, "HND", 16, True), (128, 64, 4, 2, "NHD", -1, True),
+    (128, 128, 32, 8, "NHD", 16, False)])
 def test_kv_checksum_is_exact(dk, dv, hq, hkv, layout, chunk, pads):
     """The streaming checksum equals the XOR of the same rows' words taken on the host,
     bit for bit: every byte the decode pattern streams arrives, each exactly once, and
