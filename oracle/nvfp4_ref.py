@@ -31,6 +31,10 @@ out the bit layouts, nibble order or rounding.  The readings taken here:
     q_b rows and L_b keys sees keys j <= i + (L_b - q_b).
   * LSE is the natural-log sum of exp of the scaled scores; a row that sees no
     key gets O = 0 and LSE = -inf.
+  * FP8 KV (the 1-byte KV type the pages run beside NVFP4): one e4m3fn byte per
+    element, code = sign | RNE_e4m3(|x| / g) saturating at 448, value = e4m3 * g.
+  * Ragged (non-paged) KV: request b's rows are rows kv_indptr[b] .. kv_indptr[b+1]-1
+    of one [rows, H, W] array.
 """
 from __future__ import annotations
 
@@ -152,6 +156,35 @@ def dequantize(packed, sf, global_scale=1.0):
 
 
 # ---------------------------------------------------------------------------
+# FP8 e4m3 KV with a per-tensor scale  ([PF] commit "Gate split-KV off...": the
+# FP8 and 16-bit KV types run the same prefill plan; dtype-aware skip commit: the
+# float8_e4m3fn KV parametrisation)
+# ---------------------------------------------------------------------------
+
+def quantize_fp8(x, global_scale=1.0):
+    """Rows x[..., D] to FP8 e4m3fn bytes: sign bit of x, magnitude RNE_e4m3(|x| / g)
+    saturating at 448 (so -0 and tiny negatives give 0x80)."""
+    x = np.asarray(x, dtype=np.float64)
+    mag = e4m3_round(np.abs(x) / float(global_scale))
+    sign = np.signbit(x).astype(np.uint8) << 7
+    return (sign | mag).astype(np.uint8)
+
+
+def dequantize_fp8(codes, global_scale=1.0):
+    """FP8 e4m3fn bytes back to float64: e4m3(code) * g."""
+    return e4m3_value(codes) * float(global_scale)
+
+
+def dequantize_kv(data, sf, global_scale, kv_dtype):
+    """Dequantised rows of either KV type (``sf`` is unused for FP8)."""
+    if kv_dtype == "nvfp4":
+        return dequantize(data, sf, global_scale)
+    if kv_dtype == "fp8":
+        return dequantize_fp8(data, global_scale)
+    raise ValueError(kv_dtype)
+
+
+# ---------------------------------------------------------------------------
 # Paged cache reads  ([XQA] walkthrough: k_cache / v_cache with a page table and
 # sequence lengths; [PF] independent K/V pools and strides)
 # ---------------------------------------------------------------------------
@@ -219,27 +252,50 @@ def attention(q, k, v, sm_scale, causal=False):
 
 def paged_attention(q, k_pool, k_sf, v_pool, v_sf, page_table, kv_lens, qo_indptr,
                     page_size, sm_scale, causal=False, layout="HND",
-                    k_global=1.0, v_global=1.0, rows=None):
-    """Batched attention over paged NVFP4 K/V (decode when every q_b is 1).
+                    k_global=1.0, v_global=1.0, rows=None, kv_dtype="nvfp4"):
+    """Batched attention over paged K/V (decode when every q_b is 1).
 
-    q [sum q_b, Hq, Dk]; pools as in ``gather_pages`` with W = D/2 (data) or
-    D/16 (scales).  ``rows`` optionally restricts the computation to a subset of
-    requests (the other outputs stay NaN).  Returns O [sum q_b, Hq, Dv] and
-    LSE [sum q_b, Hq].
+    q [sum q_b, Hq, Dk]; pools as in ``gather_pages`` with W = D/2 (NVFP4 data),
+    D/16 (NVFP4 scales) or D (FP8 data; scales None).  ``rows`` optionally restricts
+    the computation to a subset of requests (the other outputs stay NaN).  Returns
+    O [sum q_b, Hq, Dv] and LSE [sum q_b, Hq].
     """
     q = np.asarray(q, dtype=np.float64)
     nq, hq, _ = q.shape
-    dv = np.asarray(v_pool).shape[-1] * 2
+    dv = np.asarray(v_pool).shape[-1] * (2 if kv_dtype == "nvfp4" else 1)
     o = np.full((nq, hq, dv), np.nan)
     lse = np.full((nq, hq), np.nan)
     batch = len(kv_lens)
+
+    def rows_of(pool, b, L):
+        return None if pool is None else gather_pages(pool, page_table[b], L, page_size, layout)
+
     for b in (range(batch) if rows is None else rows):
         L = int(kv_lens[b])
         q0, q1 = int(qo_indptr[b]), int(qo_indptr[b + 1])
-        k = dequantize(gather_pages(k_pool, page_table[b], L, page_size, layout),
-                       gather_pages(k_sf, page_table[b], L, page_size, layout), k_global)
-        v = dequantize(gather_pages(v_pool, page_table[b], L, page_size, layout),
-                       gather_pages(v_sf, page_table[b], L, page_size, layout), v_global)
+        k = dequantize_kv(rows_of(k_pool, b, L), rows_of(k_sf, b, L), k_global, kv_dtype)
+        v = dequantize_kv(rows_of(v_pool, b, L), rows_of(v_sf, b, L), v_global, kv_dtype)
+        o[q0:q1], lse[q0:q1] = attention(q[q0:q1], k, v, sm_scale, causal)
+    return o, lse
+
+
+def ragged_attention(q, k_rows, k_sf, v_rows, v_sf, kv_indptr, qo_indptr, sm_scale,
+                     causal=False, k_global=1.0, v_global=1.0, kv_dtype="nvfp4"):
+    """Batched attention over ragged (non-paged) K/V: request b's keys are rows
+    kv_indptr[b] .. kv_indptr[b+1]-1 of k_rows / v_rows [rows, Hkv, W] (and of the
+    scale arrays for NVFP4).  Returns O [sum q_b, Hq, Dv] and LSE [sum q_b, Hq]."""
+    q = np.asarray(q, dtype=np.float64)
+    nq, hq, _ = q.shape
+    dv = np.asarray(v_rows).shape[-1] * (2 if kv_dtype == "nvfp4" else 1)
+    o = np.full((nq, hq, dv), np.nan)
+    lse = np.full((nq, hq), np.nan)
+    for b in range(len(kv_indptr) - 1):
+        a0, a1 = int(kv_indptr[b]), int(kv_indptr[b + 1])
+        q0, q1 = int(qo_indptr[b]), int(qo_indptr[b + 1])
+        k = dequantize_kv(np.asarray(k_rows)[a0:a1], None if k_sf is None else
+                          np.asarray(k_sf)[a0:a1], k_global, kv_dtype)
+        v = dequantize_kv(np.asarray(v_rows)[a0:a1], None if v_sf is None else
+                          np.asarray(v_sf)[a0:a1], v_global, kv_dtype)
         o[q0:q1], lse[q0:q1] = attention(q[q0:q1], k, v, sm_scale, causal)
     return o, lse
 
