@@ -14,12 +14,12 @@ from typing import Optional, Sequence
 import numpy as np
 import torch
 
-from ._lib import (EXPORTS, STATUS, WORK_FIELDS, KVPoolStruct, NVFP4Error, PlanInfoStruct,
-                   check, lib)
+from ._lib import (EXPORTS, KV_DTYPES, STATUS, WORK_FIELDS, KVPoolStruct, KVRaggedStruct,
+                   NVFP4Error, PlanInfoStruct, PlanOptionsStruct, check, lib)
 
-__all__ = ["KVPool", "Plan", "Prepared", "quantize_kv", "batch_decode", "batch_decode_noalloc",
-           "batch_decode_append",
-           "batch_prefill", "kv_checksum",
+__all__ = ["KVPool", "RaggedKV", "Plan", "Prepared", "quantize_kv", "batch_decode",
+           "batch_decode_noalloc", "batch_decode_append", "batch_prefill",
+           "batch_prefill_ragged", "kv_checksum",
            "merge_partials", "merge_states", "NVFP4Error", "lib", "version", "EXPORTS"]
 
 
@@ -61,29 +61,38 @@ def _stream(stream, device: Optional[torch.device] = None) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-class KVPool:
-    """One paged NVFP4 pool (K or V).
+def _row_bytes(head_dim: int, dtype: str) -> int:
+    return head_dim if dtype == "fp8" else head_dim // 2
 
-    ``data`` is uint8 ``[pages, H, P, D/2]`` (layout "HND") or ``[pages, P, H, D/2]``
-    ("NHD"); ``sf`` has the same leading dims and ``D/16`` scale bytes.  Any strides
-    are allowed as long as the last dimension is contiguous.
+
+class KVPool:
+    """One paged pool (K or V) of NVFP4 (``dtype="nvfp4"``) or FP8 e4m3 (``"fp8"``).
+
+    ``data`` is uint8 ``[pages, H, P, W]`` (layout "HND") or ``[pages, P, H, W]``
+    ("NHD") with W = D/2 (NVFP4) or D (FP8); an NVFP4 pool's ``sf`` has the same leading
+    dims and ``D/16`` scale bytes, an FP8 pool has none (``sf=None``).  Any strides are
+    allowed as long as the last dimension is contiguous.
     """
 
-    def __init__(self, data: torch.Tensor, sf: torch.Tensor, *, head_dim: int, layout="HND",
-                 global_scale: float = 1.0):
-        if data.dtype != torch.uint8 or sf.dtype != torch.uint8:
+    def __init__(self, data: torch.Tensor, sf: Optional[torch.Tensor], *, head_dim: int,
+                 layout="HND", global_scale: float = 1.0, dtype: str = "nvfp4"):
+        if dtype not in KV_DTYPES:
+            raise ValueError(f"dtype must be one of {sorted(KV_DTYPES)}, got {dtype!r}")
+        if (sf is None) != (dtype == "fp8"):
+            raise ValueError("an NVFP4 pool needs its scale tensor; an FP8 pool has none")
+        if data.dtype != torch.uint8 or (sf is not None and sf.dtype != torch.uint8):
             raise TypeError("pool data and scales must be uint8 tensors")
-        if data.dim() != 4 or sf.dim() != 4:
+        if data.dim() != 4 or (sf is not None and sf.dim() != 4):
             raise ValueError("pool tensors must be 4-D")
         if layout not in ("HND", "NHD"):
             raise ValueError(f"layout must be HND or NHD, got {layout!r}")
-        if data.stride(-1) != 1 or sf.stride(-1) != 1:
+        if data.stride(-1) != 1 or (sf is not None and sf.stride(-1) != 1):
             raise ValueError("the last pool dimension must be contiguous")
-        if tuple(data.shape[:3]) != tuple(sf.shape[:3]):
+        if sf is not None and tuple(data.shape[:3]) != tuple(sf.shape[:3]):
             raise ValueError("pool data and scales must have the same leading dims")
-        if data.device != sf.device:
+        if sf is not None and data.device != sf.device:
             raise ValueError("pool data and scales must be on one device")
-        self.data, self.sf, self.layout = data, sf, layout
+        self.data, self.sf, self.layout, self.dtype = data, sf, layout, dtype
         self.head_dim = int(head_dim)
         self.global_scale = float(global_scale)
         self.num_pages = data.shape[0]
@@ -91,19 +100,28 @@ class KVPool:
             self.num_kv_heads, self.page_size = data.shape[1], data.shape[2]
         else:
             self.page_size, self.num_kv_heads = data.shape[1], data.shape[2]
-        if data.shape[-1] != head_dim // 2 or sf.shape[-1] != head_dim // 16:
-            raise ValueError("pool last dims must be head_dim/2 (data) and head_dim/16 (scales)")
+        if data.shape[-1] != _row_bytes(head_dim, dtype) or \
+                (sf is not None and sf.shape[-1] != head_dim // 16):
+            raise ValueError("pool last dims must be head_dim/2 (NVFP4 data) or head_dim (FP8 "
+                             "data), and head_dim/16 (scales)")
+
+    def tensors(self):
+        return (self.data,) if self.sf is None else (self.data, self.sf)
 
     @classmethod
     def empty(cls, num_pages: int, num_kv_heads: int, page_size: int, head_dim: int,
-              layout="HND", device="cuda", global_scale: float = 1.0) -> "KVPool":
+              layout="HND", device="cuda", global_scale: float = 1.0,
+              dtype: str = "nvfp4") -> "KVPool":
         if layout == "HND":
             shape = (num_pages, num_kv_heads, page_size)
         else:
             shape = (num_pages, page_size, num_kv_heads)
-        data = torch.empty(shape + (head_dim // 2,), dtype=torch.uint8, device=device)
-        sf = torch.empty(shape + (head_dim // 16,), dtype=torch.uint8, device=device)
-        return cls(data, sf, head_dim=head_dim, layout=layout, global_scale=global_scale)
+        data = torch.empty(shape + (_row_bytes(head_dim, dtype),), dtype=torch.uint8,
+                           device=device)
+        sf = None if dtype == "fp8" else torch.empty(shape + (head_dim // 16,), dtype=torch.uint8,
+                                                     device=device)
+        return cls(data, sf, head_dim=head_dim, layout=layout, global_scale=global_scale,
+                   dtype=dtype)
 
     def struct(self) -> KVPoolStruct:
         """The C view of this pool (built once: the tensors of a pool never change)."""
@@ -112,16 +130,64 @@ class KVPool:
         return self._struct
 
     def _make_struct(self) -> KVPoolStruct:
-        d, s = self.data.stride(), self.sf.stride()
+        d = self.data.stride()
+        s = self.sf.stride() if self.sf is not None else (0, 0, 0, 1)
         if self.layout == "HND":
             dp, dh, dt = d[0], d[1], d[2]
             sp, sh, st = s[0], s[1], s[2]
         else:
             dp, dt, dh = d[0], d[1], d[2]
             sp, st, sh = s[0], s[1], s[2]
-        return KVPoolStruct(self.data.data_ptr(), dp, dh, dt, self.sf.data_ptr(), sp, sh, st,
+        return KVPoolStruct(self.data.data_ptr(), dp, dh, dt,
+                            self.sf.data_ptr() if self.sf is not None else None, sp, sh, st,
                             self.num_pages, self.page_size, self.num_kv_heads, self.head_dim,
-                            self.global_scale)
+                            self.global_scale, KV_DTYPES[self.dtype])
+
+
+class RaggedKV:
+    """Ragged (non-paged) K or V rows for ``batch_prefill_ragged``: ``data`` uint8
+    ``[rows, H, W]`` (W = D/2 for NVFP4, D for FP8) and, for NVFP4, ``sf`` ``[rows, H,
+    D/16]``.  Request b's keys are rows ``kv_indptr[b] .. kv_indptr[b+1]-1``; rows are
+    streamed in 16-row pages, so up to 15 rows past the last request must exist
+    (``empty`` adds them)."""
+
+    def __init__(self, data: torch.Tensor, sf: Optional[torch.Tensor], *, head_dim: int,
+                 global_scale: float = 1.0, dtype: str = "nvfp4"):
+        if dtype not in KV_DTYPES:
+            raise ValueError(f"dtype must be one of {sorted(KV_DTYPES)}, got {dtype!r}")
+        if (sf is None) != (dtype == "fp8"):
+            raise ValueError("NVFP4 rows need their scale tensor; FP8 rows have none")
+        for t in (data, sf):
+            if t is not None and (t.dtype != torch.uint8 or t.dim() != 3 or t.stride(-1) != 1):
+                raise ValueError("ragged tensors must be uint8 [rows, heads, bytes] with a "
+                                 "contiguous last dim")
+        if data.shape[-1] != _row_bytes(head_dim, dtype) or \
+                (sf is not None and (sf.shape[-1] != head_dim // 16 or sf.shape[:2] != data.shape[:2])):
+            raise ValueError("ragged rows must hold head_dim/2 (NVFP4) or head_dim (FP8) bytes "
+                             "and head_dim/16 scale bytes")
+        self.data, self.sf, self.dtype = data, sf, dtype
+        self.head_dim, self.global_scale = int(head_dim), float(global_scale)
+        self.num_rows, self.num_kv_heads = data.shape[0], data.shape[1]
+
+    @classmethod
+    def empty(cls, total_rows: int, num_kv_heads: int, head_dim: int, device="cuda",
+              global_scale: float = 1.0, dtype: str = "nvfp4") -> "RaggedKV":
+        rows = total_rows + 15
+        data = torch.empty((rows, num_kv_heads, _row_bytes(head_dim, dtype)), dtype=torch.uint8,
+                           device=device)
+        sf = None if dtype == "fp8" else torch.empty((rows, num_kv_heads, head_dim // 16),
+                                                     dtype=torch.uint8, device=device)
+        return cls(data, sf, head_dim=head_dim, global_scale=global_scale, dtype=dtype)
+
+    def tensors(self):
+        return (self.data,) if self.sf is None else (self.data, self.sf)
+
+    def struct(self) -> KVRaggedStruct:
+        s = self.sf.stride() if self.sf is not None else (0, 0, 1)
+        return KVRaggedStruct(self.data.data_ptr(), self.data.stride(0), self.data.stride(1),
+                              self.sf.data_ptr() if self.sf is not None else None, s[0], s[1],
+                              self.num_rows, self.num_kv_heads, self.head_dim, self.global_scale,
+                              KV_DTYPES[self.dtype])
 
 
 class Prepared:
@@ -159,8 +225,8 @@ def quantize_kv(k: Optional[torch.Tensor], v: Optional[torch.Tensor], slot_mappi
     if slot_mapping.dtype != torch.int64 or slot_mapping.dim() != 1 \
             or slot_mapping.numel() != n or not slot_mapping.is_contiguous():
         raise ValueError("slot_mapping must be a contiguous int64 vector with one entry per token")
-    dev = _device(k, v, slot_mapping, *(p.data for p in (k_pool, v_pool) if p is not None),
-                  *(p.sf for p in (k_pool, v_pool) if p is not None))
+    dev = _device(k, v, slot_mapping, *(t for p in (k_pool, v_pool) if p is not None
+                                        for t in p.tensors()))
     ks = k_pool.struct() if k_pool is not None else None
     vs = v_pool.struct() if v_pool is not None else None
     args = (_ptr(k), k.stride(0) if k is not None else 0, k.stride(1) if k is not None else 0,
@@ -182,10 +248,19 @@ class Plan:
     def __init__(self, kv_lens: Sequence[int], *, num_qo_heads: int, num_kv_heads: int,
                  head_dim_qk: int, head_dim_vo: Optional[int] = None, page_size: int = 16,
                  qo_indptr: Optional[Sequence[int]] = None, causal: bool = False,
-                 kv_chunk_tokens: int = 0, num_cus: int = 0, device=None):
+                 kv_chunk_tokens: int = 0, num_cus: int = 0, device=None,
+                 kv_dtype: str = "nvfp4", kv_indptr: Optional[Sequence[int]] = None):
         """``num_cus`` 0 fills the compute units of ``device`` (default: the current
-        device when a GPU is present, else the library's default of 256)."""
+        device when a GPU is present, else the library's default of 256).  ``kv_dtype``:
+        the pools' type ("nvfp4" or "fp8"); ``kv_indptr``: ragged (non-paged) prefill KV
+        rows per request (nvfp4_plan_create_ex)."""
         head_dim_vo = head_dim_qk if head_dim_vo is None else head_dim_vo
+        if kv_dtype not in KV_DTYPES:
+            raise ValueError(f"kv_dtype must be one of {sorted(KV_DTYPES)}, got {kv_dtype!r}")
+        self.kv_dtype = kv_dtype
+        self._kvind = None if kv_indptr is None else np.ascontiguousarray(
+            np.asarray(kv_indptr, dtype=np.int32))
+        self.ragged = kv_indptr is not None
         if num_cus == 0 and torch.cuda.is_available():
             num_cus = torch.cuda.get_device_properties(
                 torch.device("cuda") if device is None else torch.device(device)
@@ -201,11 +276,16 @@ class Plan:
         self.num_qo_heads, self.num_kv_heads = num_qo_heads, num_kv_heads
         self.head_dim_qk, self.head_dim_vo, self.page_size = head_dim_qk, head_dim_vo, page_size
         self.causal = causal
-        check(lib.nvfp4_plan_create(
+        opts = PlanOptionsStruct(KV_DTYPES[kv_dtype], None if self._kvind is None
+                                 else self._kvind.ctypes.data_as(ctypes.c_void_p).value)
+        check(lib.nvfp4_plan_create_ex(
             self._kv.ctypes.data_as(ctypes.c_void_p) if self.batch else None,
             self._ind.ctypes.data_as(ctypes.c_void_p) if self._ind is not None else None,
             self.batch, num_qo_heads, num_kv_heads, head_dim_qk, head_dim_vo, page_size,
-            int(bool(causal)), kv_chunk_tokens, num_cus, ctypes.byref(self._h)))
+            int(bool(causal)), kv_chunk_tokens, num_cus, ctypes.byref(opts),
+            ctypes.byref(self._h)))
+        if self.ragged:
+            self.page_size = 16
 
     def __del__(self):
         h = getattr(self, "_h", None)
@@ -294,11 +374,15 @@ def _check_rows(plan: Plan, q, page_table, out, lse):
 
 
 def _check_pools(plan: Plan, k_pool: "KVPool", v_pool: "KVPool"):
+    if plan.ragged:
+        raise ValueError("the plan was made for ragged KV rows: use batch_prefill_ragged")
     for name, p, d in (("k_pool", k_pool, plan.head_dim_qk), ("v_pool", v_pool, plan.head_dim_vo)):
         if p.head_dim != d or p.num_kv_heads != plan.num_kv_heads or p.page_size != plan.page_size:
             raise ValueError(f"{name} is (heads {p.num_kv_heads}, page {p.page_size}, dim "
                              f"{p.head_dim}); the plan needs ({plan.num_kv_heads}, "
                              f"{plan.page_size}, {d})")
+        if p.dtype != plan.kv_dtype:
+            raise ValueError(f"{name} holds {p.dtype}, the plan was made for {plan.kv_dtype}")
 
 
 def _attn(fn, plan: Plan, q, page_table, k_pool, v_pool, sm_scale, workspace, out, lse, stream,
@@ -306,8 +390,7 @@ def _attn(fn, plan: Plan, q, page_table, k_pool, v_pool, sm_scale, workspace, ou
     rows = _check_rows(plan, q, page_table, out, lse)
     _check_pools(plan, k_pool, v_pool)
     _check_workspace(plan, workspace)
-    dev = _device(q, page_table, k_pool.data, k_pool.sf, v_pool.data, v_pool.sf, workspace, out,
-                  lse)
+    dev = _device(q, page_table, *k_pool.tensors(), *v_pool.tensors(), workspace, out, lse)
     if out is None:
         out = torch.empty((rows, plan.num_qo_heads, plan.head_dim_vo), dtype=torch.float32,
                           device=dev)
@@ -344,7 +427,7 @@ def batch_decode_noalloc(plan: Plan, q: torch.Tensor, page_table: torch.Tensor, 
         raise ValueError("out and lse must be given: the call allocates nothing")
     _check_rows(plan, q, page_table, out, lse)
     _check_pools(plan, k_pool, v_pool)
-    dev = _device(q, page_table, k_pool.data, k_pool.sf, v_pool.data, v_pool.sf, out, lse)
+    dev = _device(q, page_table, *k_pool.tensors(), *v_pool.tensors(), out, lse)
     ks, vs = k_pool.struct(), v_pool.struct()
     check(lib.nvfp4_batch_decode_noalloc(
         plan.handle, _ptr(q), q.stride(0), q.stride(1), _ptr(page_table), page_table.stride(0),
@@ -368,8 +451,8 @@ def batch_decode_append(plan: Plan, q: torch.Tensor, k_new: torch.Tensor, v_new:
     rows = _check_rows(plan, q, page_table, out, lse)
     _check_pools(plan, k_pool, v_pool)
     _check_workspace(plan, workspace)
-    dev = _device(q, k_new, v_new, page_table, k_pool.data, k_pool.sf, v_pool.data, v_pool.sf,
-                  workspace, out, lse)
+    dev = _device(q, k_new, v_new, page_table, *k_pool.tensors(), *v_pool.tensors(), workspace,
+                  out, lse)
     if out is None:
         out = torch.empty((rows, plan.num_qo_heads, plan.head_dim_vo), dtype=torch.float32,
                           device=dev)
@@ -405,7 +488,7 @@ def kv_checksum(plan: Plan, page_table: torch.Tensor, k_pool: KVPool, v_pool: KV
     if out is not None and (out.dtype != torch.int32 or tuple(out.shape) != shape
                             or not out.is_contiguous()):
         raise ValueError(f"out must be contiguous int32 of shape {shape}")
-    dev = _device(page_table, k_pool.data, k_pool.sf, v_pool.data, v_pool.sf, workspace, out)
+    dev = _device(page_table, *k_pool.tensors(), *v_pool.tensors(), workspace, out)
     if out is None:
         out = torch.empty(shape, dtype=torch.int32, device=dev)
     ks, vs = k_pool.struct(), v_pool.struct()
@@ -426,6 +509,41 @@ def batch_prefill(plan: Plan, q: torch.Tensor, page_table: torch.Tensor, k_pool:
     or a ``Prepared`` call with ``prepare=True``."""
     return _attn(lib.nvfp4_batch_prefill, plan, q, page_table, k_pool, v_pool, sm_scale,
                  workspace, out, lse, stream, prepare)
+
+
+def batch_prefill_ragged(plan: Plan, q: torch.Tensor, k: RaggedKV, v: RaggedKV, sm_scale: float,
+                         workspace: torch.Tensor, out: Optional[torch.Tensor] = None,
+                         lse: Optional[torch.Tensor] = None, stream=None, prepare: bool = False):
+    """Prefill over ragged K/V rows (nvfp4_batch_prefill_ragged); the plan carries the
+    rows of each request (``kv_indptr``).  Returns (O, LSE) as ``batch_prefill``."""
+    if not plan.ragged:
+        raise ValueError("the plan was made for paged KV: create it with kv_indptr")
+    rows = plan.total_rows
+    if q.dtype != torch.bfloat16 or q.dim() != 3 or q.stride(-1) != 1 \
+            or tuple(q.shape) != (rows, plan.num_qo_heads, plan.head_dim_qk):
+        raise ValueError(f"q must be bf16 [{rows}, {plan.num_qo_heads}, {plan.head_dim_qk}] "
+                         "with a contiguous last dim")
+    _check_outputs(plan, out, lse)
+    _check_workspace(plan, workspace)
+    for name, r, d in (("k", k, plan.head_dim_qk), ("v", v, plan.head_dim_vo)):
+        if r.head_dim != d or r.num_kv_heads != plan.num_kv_heads or r.dtype != plan.kv_dtype:
+            raise ValueError(f"{name} is ({r.num_kv_heads} heads, dim {r.head_dim}, {r.dtype}); "
+                             f"the plan needs ({plan.num_kv_heads}, {d}, {plan.kv_dtype})")
+    dev = _device(q, *k.tensors(), *v.tensors(), workspace, out, lse)
+    if out is None:
+        out = torch.empty((rows, plan.num_qo_heads, plan.head_dim_vo), dtype=torch.float32,
+                          device=dev)
+    if lse is None:
+        lse = torch.empty((rows, plan.num_qo_heads), dtype=torch.float32, device=dev)
+    ks, vs = k.struct(), v.struct()
+    args = (plan.handle, _ptr(q), q.stride(0), q.stride(1), ctypes.byref(ks), ctypes.byref(vs),
+            float(sm_scale), _ptr(workspace), workspace.numel(), _ptr(out), out.stride(0),
+            out.stride(1), _ptr(lse), _stream(stream, dev))
+    if prepare:
+        return Prepared(lib.nvfp4_batch_prefill_ragged, args,
+                        (plan, q, k, v, ks, vs, workspace, out, lse))
+    check(lib.nvfp4_batch_prefill_ragged(*args))
+    return out, lse
 
 
 def merge_partials(plan: Plan, workspace: torch.Tensor, out: torch.Tensor, lse: torch.Tensor,

@@ -24,11 +24,12 @@ STATUS_CODE = {v: k for k, v in STATUS.items()}
 # Names declared in include/nvfp4_attn.h, in order.
 EXPORTS = (
     "nvfp4_last_error", "nvfp4_version", "nvfp4_quantize_kv", "nvfp4_plan_create",
+    "nvfp4_plan_create_ex",
     "nvfp4_plan_destroy", "nvfp4_plan_workspace_bytes", "nvfp4_plan_get_info",
     "nvfp4_plan_get_work", "nvfp4_plan_upload", "nvfp4_batch_decode",
     "nvfp4_batch_decode_noalloc",
     "nvfp4_batch_decode_append", "nvfp4_kv_checksum", "nvfp4_set_timing_events",
-    "nvfp4_batch_prefill",
+    "nvfp4_batch_prefill", "nvfp4_batch_prefill_ragged",
     "nvfp4_plan_set_deferred_merge", "nvfp4_merge_partials", "nvfp4_merge_states",
 )
 
@@ -51,6 +52,30 @@ class KVPoolStruct(ctypes.Structure):
         ("num_kv_heads", ctypes.c_int32),
         ("head_dim", ctypes.c_int32),
         ("global_scale", ctypes.c_float),
+        ("kv_dtype", ctypes.c_int32),
+    ]
+
+
+KV_DTYPES = {"nvfp4": 0, "fp8": 1}
+
+
+class PlanOptionsStruct(ctypes.Structure):
+    _fields_ = [("kv_dtype", ctypes.c_int32), ("kv_indptr", ctypes.c_void_p)]
+
+
+class KVRaggedStruct(ctypes.Structure):
+    _fields_ = [
+        ("data", ctypes.c_void_p),
+        ("stride_row", ctypes.c_int64),
+        ("stride_head", ctypes.c_int64),
+        ("sf", ctypes.c_void_p),
+        ("sf_stride_row", ctypes.c_int64),
+        ("sf_stride_head", ctypes.c_int64),
+        ("num_rows", ctypes.c_int64),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("global_scale", ctypes.c_float),
+        ("kv_dtype", ctypes.c_int32),
     ]
 
 
@@ -88,6 +113,9 @@ def _load():
         "nvfp4_quantize_kv": (ctypes.c_int, [vp, i64, i64, vp, i64, i64, i64, vp, pool_p, pool_p, vp]),
         "nvfp4_plan_create": (ctypes.c_int, [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32,
                                              ctypes.POINTER(vp)]),
+        "nvfp4_plan_create_ex": (ctypes.c_int, [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
+                                                i32, ctypes.POINTER(PlanOptionsStruct),
+                                                ctypes.POINTER(vp)]),
         "nvfp4_plan_destroy": (None, [vp]),
         "nvfp4_plan_workspace_bytes": (sz, [vp]),
         "nvfp4_plan_get_info": (ctypes.c_int, [vp, ctypes.POINTER(PlanInfoStruct)]),
@@ -104,6 +132,10 @@ def _load():
         "nvfp4_set_timing_events": (ctypes.c_int, [vp, vp]),
         "nvfp4_batch_prefill": (ctypes.c_int, [vp, vp, i64, i64, vp, i64, pool_p, pool_p, f32, vp, sz,
                                                vp, i64, i64, vp, vp]),
+        "nvfp4_batch_prefill_ragged": (ctypes.c_int, [vp, vp, i64, i64,
+                                                      ctypes.POINTER(KVRaggedStruct),
+                                                      ctypes.POINTER(KVRaggedStruct), f32, vp, sz,
+                                                      vp, i64, i64, vp, vp]),
         "nvfp4_plan_set_deferred_merge": (ctypes.c_int, [vp, i32]),
         "nvfp4_merge_partials": (ctypes.c_int, [vp, vp, sz, vp, i64, i64, vp, vp]),
         "nvfp4_merge_states": (ctypes.c_int, [vp, vp, i64, i32, i32, i32, vp, vp, vp]),

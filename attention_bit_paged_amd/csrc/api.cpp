@@ -106,10 +106,22 @@ bool head_dim_ok(int d) { return d == 64 || d == 128 || d == 256 || d == 512; }
 
 // Validates one pool against the expected head dim and shared page geometry.
 nvfp4_status check_pool(const nvfp4_kv_pool* p, const char* name, int head_dim,
-                        int num_kv_heads, int page_size) {
+                        int num_kv_heads, int page_size, int kv_dtype = -1) {
   if (!p) return fail(NVFP4_E_INVALID, "%s pool is NULL", name);
   if (!p->data) return fail(NVFP4_E_INVALID, "%s.data is NULL", name);
-  if (!p->sf) return fail(NVFP4_E_INVALID, "%s.sf is NULL: NVFP4 needs its scale factors", name);
+  if (p->kv_dtype != NVFP4_KV_NVFP4 && p->kv_dtype != NVFP4_KV_FP8_E4M3)
+    return fail(NVFP4_E_INVALID, "%s.kv_dtype %d is neither NVFP4 (0) nor FP8 E4M3 (1)", name,
+                p->kv_dtype);
+  if (kv_dtype >= 0 && p->kv_dtype != kv_dtype)
+    return fail(NVFP4_E_SHAPE, "%s.kv_dtype is %d, the plan was made for %d", name, p->kv_dtype,
+                kv_dtype);
+  const bool fp8 = p->kv_dtype == NVFP4_KV_FP8_E4M3;
+  // [PF] review commit: a scale tensor on a cache that is not NVFP4 is refused rather than
+  // silently changing how the cache is read
+  if (fp8 && p->sf)
+    return fail(NVFP4_E_INVALID, "%s.sf is set on an FP8 pool: FP8 KV has no block scales", name);
+  if (!fp8 && !p->sf)
+    return fail(NVFP4_E_INVALID, "%s.sf is NULL: NVFP4 needs its scale factors", name);
   if (p->head_dim != head_dim)
     return fail(NVFP4_E_SHAPE, "%s.head_dim is %d, expected %d", name, p->head_dim, head_dim);
   if (num_kv_heads >= 0 && p->num_kv_heads != num_kv_heads)
@@ -124,27 +136,27 @@ nvfp4_status check_pool(const nvfp4_kv_pool* p, const char* name, int head_dim,
   if (p->num_kv_heads < 1) return fail(NVFP4_E_INVALID, "%s.num_kv_heads must be >= 1", name);
   if (!(p->global_scale > 0.f) || !std::isfinite(p->global_scale))
     return fail(NVFP4_E_INVALID, "%s.global_scale must be finite and > 0", name);
-  const int64_t da = head_dim >= 128 ? 16 : head_dim / 8;
+  const int64_t da = fp8 ? 16 : (head_dim >= 128 ? 16 : head_dim / 8);
   const int64_t sa = std::min(head_dim / 16, 8);
   if (!aligned(p->data, da) || p->stride_page % da || p->stride_head % da || p->stride_token % da)
     return fail(NVFP4_E_SHAPE, "%s data pointer and strides must be multiples of %lld bytes", name,
                 (long long)da);
-  if (!aligned(p->sf, sa) || p->sf_stride_page % sa || p->sf_stride_head % sa ||
-      p->sf_stride_token % sa)
+  if (!fp8 && (!aligned(p->sf, sa) || p->sf_stride_page % sa || p->sf_stride_head % sa ||
+               p->sf_stride_token % sa))
     return fail(NVFP4_E_SHAPE, "%s sf pointer and strides must be multiples of %lld bytes", name,
                 (long long)sa);
-  if (p->stride_page < 0 || p->stride_head < 0 || p->stride_token < 0 || p->sf_stride_page < 0 ||
-      p->sf_stride_head < 0 || p->sf_stride_token < 0)
+  if (p->stride_page < 0 || p->stride_head < 0 || p->stride_token < 0 ||
+      (!fp8 && (p->sf_stride_page < 0 || p->sf_stride_head < 0 || p->sf_stride_token < 0)))
     return fail(NVFP4_E_SHAPE, "%s strides must be non-negative", name);
   const int64_t kMaxStride = (int64_t(1) << 31) - 1;  // kernels multiply strides in 32 bits
   if (p->stride_page > kMaxStride || p->stride_head > kMaxStride || p->stride_token > kMaxStride ||
-      p->sf_stride_page > kMaxStride || p->sf_stride_head > kMaxStride ||
-      p->sf_stride_token > kMaxStride)
+      (!fp8 && (p->sf_stride_page > kMaxStride || p->sf_stride_head > kMaxStride ||
+                p->sf_stride_token > kMaxStride)))
     return fail(NVFP4_E_SHAPE, "%s strides must be below 2^31 bytes", name);
   // the streaming copies address 16 consecutive token slots from one base with a 32-bit
   // offset per lane
   const int64_t kMaxTokStride = int64_t(1) << 27;
-  if (p->stride_token >= kMaxTokStride || p->sf_stride_token >= kMaxTokStride)
+  if (p->stride_token >= kMaxTokStride || (!fp8 && p->sf_stride_token >= kMaxTokStride))
     return fail(NVFP4_E_SHAPE, "%s token strides must be below 2^27 bytes", name);
   return NVFP4_OK;
 }
@@ -170,6 +182,11 @@ struct nvfp4_plan {
   int prefill = 0;
   int batch = 0, num_qo_heads = 0, num_kv_heads = 0, group = 0;
   int head_dim_qk = 0, head_dim_vo = 0, page_size = 0, causal = 0;
+  int kv_dtype = NVFP4_KV_NVFP4;
+  int ragged = 0;          // prefill over ragged rows (nvfp4_batch_prefill_ragged)
+  std::vector<int32_t> kv_starts;  // ragged: first row of each request
+  std::vector<int32_t> ragged_pt;  // ragged: the 16-row "pages" of each request
+  int ragged_pt_stride = 0;
   int chunk = 0;           // chunk length used when splitting (0: no split)
   int rows_per_item = 0;   // decode: 16 heads; prefill: rows of a tile
   int rows_per_slot = 0;
@@ -179,7 +196,7 @@ struct nvfp4_plan {
   std::vector<int32_t> kv_lens, qo_indptr;
   int num_partials = 0;
   // workspace layout (byte offsets)
-  size_t off_work = 0, off_merge = 0, off_kvlens = 0, off_indptr = 0,
+  size_t off_work = 0, off_merge = 0, off_kvlens = 0, off_indptr = 0, off_pt = 0,
          off_part_o = 0, off_part_lse = 0, ws_bytes = 0;
   std::vector<uint8_t> image;  // the tables as they sit at the start of the workspace
   void* uploaded_to = nullptr;
@@ -196,8 +213,28 @@ nvfp4_status nvfp4_plan_create(const int32_t* kv_lens, const int32_t* qo_indptr,
                                int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim_qk,
                                int32_t head_dim_vo, int32_t page_size, int32_t causal,
                                int32_t kv_chunk_tokens, int32_t num_cus, nvfp4_plan** out) {
+  return nvfp4_plan_create_ex(kv_lens, qo_indptr, batch, num_qo_heads, num_kv_heads, head_dim_qk,
+                              head_dim_vo, page_size, causal, kv_chunk_tokens, num_cus, nullptr,
+                              out);
+}
+
+nvfp4_status nvfp4_plan_create_ex(const int32_t* kv_lens, const int32_t* qo_indptr,
+                                  int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
+                                  int32_t head_dim_qk, int32_t head_dim_vo, int32_t page_size,
+                                  int32_t causal, int32_t kv_chunk_tokens, int32_t num_cus,
+                                  const nvfp4_plan_options* options, nvfp4_plan** out) {
   if (!out) return fail(NVFP4_E_INVALID, "out is NULL");
   *out = nullptr;
+  const int kv_dtype = options ? options->kv_dtype : NVFP4_KV_NVFP4;
+  const int32_t* kv_indptr = options ? options->kv_indptr : nullptr;
+  if (kv_dtype != NVFP4_KV_NVFP4 && kv_dtype != NVFP4_KV_FP8_E4M3)
+    return fail(NVFP4_E_INVALID, "options.kv_dtype %d is neither NVFP4 (0) nor FP8 E4M3 (1)",
+                kv_dtype);
+  if (kv_indptr && !qo_indptr)
+    return fail(NVFP4_E_SHAPE, "ragged KV (options.kv_indptr) is a prefill layout: qo_indptr "
+                "must be given");
+  // ragged rows are streamed as 16-row pages of the row array
+  if (kv_indptr) page_size = 16;
   if (batch < 0) return fail(NVFP4_E_INVALID, "batch must be >= 0");
   if (batch > 0 && !kv_lens) return fail(NVFP4_E_INVALID, "kv_lens is NULL");
   if (num_qo_heads < 1 || num_kv_heads < 1)
@@ -217,8 +254,8 @@ nvfp4_status nvfp4_plan_create(const int32_t* kv_lens, const int32_t* qo_indptr,
   // on-chip budget ([PF] commit "Re-enable split-KV...": a tile that does not fit the
   // on-chip memory is rejected at plan time): the LDS the resident workgroups of this
   // shape's kernel need, then the register file
-  const size_t lds = prefill ? prefill_lds_bytes(head_dim_qk, head_dim_vo, page_size)
-                             : decode_lds_bytes(head_dim_qk, head_dim_vo, page_size);
+  const size_t lds = prefill ? prefill_lds_bytes(head_dim_qk, head_dim_vo, page_size, kv_dtype)
+                             : decode_lds_bytes(head_dim_qk, head_dim_vo, page_size, kv_dtype);
   if (lds > kLdsBytesPerCu)
     return fail(NVFP4_E_LDS_BUDGET, "%s tile for head dims (%d, %d) needs %zu bytes of LDS per CU, "
                 "more than the %zu a CU has", prefill ? "prefill" : "decode", head_dim_qk,
@@ -226,10 +263,10 @@ nvfp4_status nvfp4_plan_create(const int32_t* kv_lens, const int32_t* qo_indptr,
   if (head_dim_qk == 512 && head_dim_vo == 512)
     return fail(NVFP4_E_LDS_BUDGET,
                 "head dims (512, 512): the per-wave decode tile does not fit the register file");
-  if (prefill ? !prefill_supported(head_dim_qk, head_dim_vo)
-              : !decode_supported(head_dim_qk, head_dim_vo))
-    return fail(NVFP4_E_UNSUPPORTED, "head dims (qk %d, vo %d) not supported", head_dim_qk,
-                head_dim_vo);
+  if (prefill ? !prefill_supported(head_dim_qk, head_dim_vo, kv_dtype)
+              : !decode_supported(head_dim_qk, head_dim_vo, kv_dtype))
+    return fail(NVFP4_E_UNSUPPORTED, "head dims (qk %d, vo %d) not supported for %s KV",
+                head_dim_qk, head_dim_vo, kv_dtype == NVFP4_KV_FP8_E4M3 ? "FP8" : "NVFP4");
   if (kv_chunk_tokens > 0 && kv_chunk_tokens % 16)
     return fail(NVFP4_E_INVALID, "kv_chunk_tokens %d is not a multiple of 16", kv_chunk_tokens);
   if (num_cus < 0) return fail(NVFP4_E_INVALID, "num_cus must be >= 0");
@@ -257,6 +294,14 @@ nvfp4_status nvfp4_plan_create(const int32_t* kv_lens, const int32_t* qo_indptr,
     }
     total_q = qo_indptr[batch];
   }
+  if (kv_indptr) {
+    if (kv_indptr[0] < 0) return fail(NVFP4_E_SHAPE, "kv_indptr[0] must be >= 0");
+    for (int b = 0; b < batch; ++b)
+      if ((int64_t)kv_indptr[b + 1] - kv_indptr[b] != kv_lens[b])
+        return fail(NVFP4_E_SHAPE, "kv_indptr[%d + 1] - kv_indptr[%d] = %lld differs from "
+                    "kv_lens[%d] = %d", b, b, (long long)kv_indptr[b + 1] - kv_indptr[b], b,
+                    kv_lens[b]);
+  }
 
   if (num_cus == 0) {
     int dev = 0, cus = 0;
@@ -279,6 +324,20 @@ nvfp4_status nvfp4_plan_create(const int32_t* kv_lens, const int32_t* qo_indptr,
   plan->head_dim_vo = head_dim_vo;
   plan->page_size = page_size;
   plan->causal = prefill ? (causal != 0) : 0;
+  plan->kv_dtype = kv_dtype;
+  if (kv_indptr) {
+    // request b's page i starts at row kv_indptr[b] + 16 i: with the page stride equal to
+    // the row stride, slot t of that page is row kv_indptr[b] + 16 i + t
+    plan->ragged = 1;
+    plan->kv_starts.assign(kv_indptr, kv_indptr + batch);
+    int maxp = 1;
+    for (int b = 0; b < batch; ++b) maxp = std::max(maxp, (kv_lens[b] + 15) / 16);
+    plan->ragged_pt_stride = maxp;
+    plan->ragged_pt.assign((size_t)batch * maxp, 0);
+    for (int b = 0; b < batch; ++b)
+      for (int i = 0; i < maxp; ++i)
+        plan->ragged_pt[(size_t)b * maxp + i] = kv_indptr[b] + 16 * std::min(i, std::max(0, (kv_lens[b] + 15) / 16 - 1));
+  }
   plan->total_q = total_q;
   plan->kv_lens.assign(kv_lens, kv_lens + batch);
   if (prefill) plan->qo_indptr.assign(qo_indptr, qo_indptr + batch + 1);
@@ -336,7 +395,7 @@ nvfp4_status nvfp4_plan_create(const int32_t* kv_lens, const int32_t* qo_indptr,
     // round is made of the short chunks
     const int64_t target =
         prefill ? (int64_t)num_cus * prefill_wgs_per_cu(head_dim_qk, head_dim_vo) * 3 / 2
-                : (int64_t)num_cus * 4 * decode_wgs_per_cu(head_dim_qk, head_dim_vo);
+                : (int64_t)num_cus * 4 * decode_wgs_per_cu(head_dim_qk, head_dim_vo, kv_dtype);
     const int64_t have = (int64_t)groups.size() * (prefill ? 1 : 4);
     if (have < target) {
       int64_t c = (total + target - 1) / std::max<int64_t>(target, 1);
@@ -398,6 +457,8 @@ nvfp4_status nvfp4_plan_create(const int32_t* kv_lens, const int32_t* qo_indptr,
   off = align_up(off + (size_t)batch * sizeof(int32_t));
   plan->off_indptr = off;
   off = align_up(off + (size_t)(batch + 1) * sizeof(int32_t));
+  plan->off_pt = off;  // ragged plans: the page table of their rows
+  off = align_up(off + plan->ragged_pt.size() * sizeof(int32_t));
   plan->off_part_o = off;
   off = align_up(off + (size_t)plan->num_partials * plan->rows_per_slot * head_dim_vo * sizeof(float));
   plan->off_part_lse = off;
@@ -412,6 +473,7 @@ nvfp4_status nvfp4_plan_create(const int32_t* kv_lens, const int32_t* qo_indptr,
   put(plan->off_merge, plan->merges);
   put(plan->off_kvlens, plan->kv_lens);
   put(plan->off_indptr, plan->qo_indptr);
+  put(plan->off_pt, plan->ragged_pt);
   *out = plan;
   return ok();
 }
@@ -476,10 +538,10 @@ nvfp4_status check_run(const nvfp4_plan* plan, bool prefill, const void* q, int6
     return fail(NVFP4_E_SHAPE, "plan was made for %s, called for %s",
                 plan->prefill ? "prefill" : "decode", prefill ? "prefill" : "decode");
   if (nvfp4_status st = check_pool(k, "k_pool", plan->head_dim_qk, plan->num_kv_heads,
-                                   plan->page_size))
+                                   plan->page_size, plan->kv_dtype))
     return st;
   if (nvfp4_status st = check_pool(v, "v_pool", plan->head_dim_vo, plan->num_kv_heads,
-                                   plan->page_size))
+                                   plan->page_size, plan->kv_dtype))
     return st;
   if (!std::isfinite(sm_scale) || !(sm_scale > 0.f))
     return fail(NVFP4_E_INVALID, "sm_scale must be finite and > 0");
@@ -596,10 +658,10 @@ nvfp4_status run(const nvfp4_plan* plan, bool prefill, const void* q, int64_t q_
   const AttnArgs a = make_args(plan, q, q_s_row, q_s_head, page_table, pt_stride, k, v, sm_scale,
                                ws, o, o_s_row, o_s_head, lse);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = prefill
-                     ? launch_prefill(plan->head_dim_qk, plan->head_dim_vo, a.page_shift, a,
-                                      plan->rows_per_item, s)
-                     : launch_decode(plan->head_dim_qk, plan->head_dim_vo, a.page_shift, a, s);
+  hipError_t e = prefill ? launch_prefill(plan->head_dim_qk, plan->head_dim_vo, plan->kv_dtype,
+                                          a.page_shift, a, s)
+                         : launch_decode(plan->head_dim_qk, plan->head_dim_vo, plan->kv_dtype,
+                                         a.page_shift, a, s);
   if (e != hipSuccess)
     return fail(NVFP4_E_HIP, "%s launch failed: %s", prefill ? "prefill" : "decode",
                 hipGetErrorString(e));
@@ -652,7 +714,7 @@ nvfp4_status nvfp4_batch_decode_noalloc(const nvfp4_plan* plan, const void* q,
   if (e != hipSuccess) return fail(NVFP4_E_HIP, "plan copy failed: %s", hipGetErrorString(e));
   const AttnArgs a = make_args(plan, q, q_stride_req, q_stride_head, page_table, pt_stride, k_pool,
                                v_pool, sm_scale, ws, o, o_stride_req, o_stride_head, lse);
-  e = launch_decode(plan->head_dim_qk, plan->head_dim_vo, a.page_shift, a, s);
+  e = launch_decode(plan->head_dim_qk, plan->head_dim_vo, plan->kv_dtype, a.page_shift, a, s);
   if (e != hipSuccess) return fail(NVFP4_E_HIP, "decode launch failed: %s", hipGetErrorString(e));
   const int n_merges = (int)(plan->merges.size() / kMergeFields);
   if (n_merges > 0) {  // always merged here: the partials live in the shared scratch
@@ -673,6 +735,9 @@ nvfp4_status nvfp4_batch_decode_append(const nvfp4_plan* plan, const void* q,
                                        float* o, int64_t o_stride_req, int64_t o_stride_head,
                                        float* lse, void* stream) {
   // the checks of the new rows come first (they need no device)
+  if (plan && plan->kv_dtype != NVFP4_KV_NVFP4)
+    return fail(NVFP4_E_UNSUPPORTED, "the in-launch append writes NVFP4; for an FP8 cache use "
+                "nvfp4_quantize_kv, then nvfp4_batch_decode");
   if (plan && !plan->prefill && plan->page_size < 16)
     return fail(NVFP4_E_UNSUPPORTED,
                 "page_size %d: the in-place append needs pages of at least 16 tokens "
@@ -705,7 +770,8 @@ nvfp4_status nvfp4_batch_decode_append(const nvfp4_plan* plan, const void* q,
     a.v_gscale = (double)v_pool->global_scale;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_decode(plan->head_dim_qk, plan->head_dim_vo, a.page_shift, a, s);
+  hipError_t e = launch_decode(plan->head_dim_qk, plan->head_dim_vo, plan->kv_dtype, a.page_shift,
+                               a, s);
   if (e != hipSuccess) return fail(NVFP4_E_HIP, "decode launch failed: %s", hipGetErrorString(e));
   const int n_merges = (int)(plan->merges.size() / kMergeFields);
   if (n_merges > 0 && !plan->defer_merge) {
@@ -721,8 +787,63 @@ nvfp4_status nvfp4_batch_prefill(const nvfp4_plan* plan, const void* q, int64_t 
                                  const nvfp4_kv_pool* v_pool, float sm_scale, void* workspace,
                                  size_t workspace_bytes, float* o, int64_t o_stride_tok,
                                  int64_t o_stride_head, float* lse, void* stream) {
+  if (plan && plan->ragged)
+    return fail(NVFP4_E_SHAPE, "the plan was made for ragged KV: use nvfp4_batch_prefill_ragged");
   return run(plan, true, q, q_stride_tok, q_stride_head, page_table, pt_stride, k_pool, v_pool,
              sm_scale, workspace, workspace_bytes, o, o_stride_tok, o_stride_head, lse, stream);
+}
+
+nvfp4_status nvfp4_batch_prefill_ragged(const nvfp4_plan* plan, const void* q,
+                                        int64_t q_stride_tok, int64_t q_stride_head,
+                                        const nvfp4_kv_ragged* k, const nvfp4_kv_ragged* v,
+                                        float sm_scale, void* workspace, size_t workspace_bytes,
+                                        float* o, int64_t o_stride_tok, int64_t o_stride_head,
+                                        float* lse, void* stream) {
+  if (!plan) return fail(NVFP4_E_INVALID, "plan is NULL");
+  if (!plan->ragged)
+    return fail(NVFP4_E_SHAPE, "the plan was made for paged KV: create it with "
+                "options.kv_indptr for ragged KV");
+  if (!k || !v) return fail(NVFP4_E_INVALID, "k and v must be set");
+  // the rows a request's last 16-row page reads past its end must exist (they are read
+  // and never used): rows up to kv_indptr[b] + 16 * ceil(kv_len_b / 16)
+  int64_t need = 0;
+  for (int b = 0; b < plan->batch; ++b)
+    need = std::max<int64_t>(need, (int64_t)plan->kv_starts[b] +
+                                       16 * (int64_t)((plan->kv_lens[b] + 15) / 16));
+  nvfp4_kv_pool pools[2];
+  const nvfp4_kv_ragged* src[2] = {k, v};
+  const char* names[2] = {"k", "v"};
+  for (int i = 0; i < 2; ++i) {
+    const nvfp4_kv_ragged* r = src[i];
+    if (r->num_rows < need)
+      return fail(NVFP4_E_SHAPE, "%s has %lld rows; the plan's requests read rows up to %lld "
+                  "(every request's rows rounded up to 16)", names[i], (long long)r->num_rows,
+                  (long long)need);
+    if (r->num_rows > INT32_MAX)
+      return fail(NVFP4_E_SHAPE, "%s has more than 2^31 - 1 rows", names[i]);
+    // the rows as a pool of one-row pages with 16 slots: page p, slot t is row p + t
+    nvfp4_kv_pool& p = pools[i];
+    p.data = r->data;
+    p.stride_page = r->stride_row;
+    p.stride_head = r->stride_head;
+    p.stride_token = r->stride_row;
+    p.sf = r->sf;
+    p.sf_stride_page = r->sf_stride_row;
+    p.sf_stride_head = r->sf_stride_head;
+    p.sf_stride_token = r->sf_stride_row;
+    p.num_pages = (int32_t)r->num_rows;
+    p.page_size = 16;
+    p.num_kv_heads = r->num_kv_heads;
+    p.head_dim = r->head_dim;
+    p.global_scale = r->global_scale;
+    p.kv_dtype = r->kv_dtype;
+  }
+  const int32_t* pt = workspace ? reinterpret_cast<const int32_t*>(
+                                      static_cast<uint8_t*>(workspace) + plan->off_pt)
+                                : nullptr;
+  return run(plan, true, q, q_stride_tok, q_stride_head, pt, plan->ragged_pt_stride, &pools[0],
+             &pools[1], sm_scale, workspace, workspace_bytes, o, o_stride_tok, o_stride_head, lse,
+             stream);
 }
 
 nvfp4_status nvfp4_kv_checksum(const nvfp4_plan* plan, const int32_t* page_table,
@@ -745,7 +866,8 @@ nvfp4_status nvfp4_kv_checksum(const nvfp4_plan* plan, const int32_t* page_table
   AttnArgs a = make_args(plan, dummy, 0, 0, page_table, pt_stride, k_pool, v_pool, 1.f,
                          workspace, nullptr, 0, 0, nullptr);
   a.q = nullptr;
-  const hipError_t e = launch_kv_checksum(plan->head_dim_qk, plan->head_dim_vo, a, checksum,
+  const hipError_t e = launch_kv_checksum(plan->head_dim_qk, plan->head_dim_vo, plan->kv_dtype, a,
+                                          checksum,
                                           plan->batch, plan->num_kv_heads,
                                           static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(NVFP4_E_HIP, "checksum launch failed: %s", hipGetErrorString(e));
@@ -836,12 +958,12 @@ nvfp4_status nvfp4_quantize_kv(const void* k_src, int64_t k_stride_token, int64_
   if (do_k && (!k_src || !k_pool)) return fail(NVFP4_E_INVALID, "k_src and k_pool must both be set");
   if (do_v && (!v_src || !v_pool)) return fail(NVFP4_E_INVALID, "v_src and v_pool must both be set");
   if (do_k) {
-    if (nvfp4_status st = check_pool(k_pool, "k_pool", k_pool->head_dim, -1, -1)) return st;
+    if (nvfp4_status st = check_pool(k_pool, "k_pool", k_pool->head_dim, -1, -1, -1)) return st;
     if (!head_dim_ok(k_pool->head_dim))
       return fail(NVFP4_E_UNSUPPORTED, "k_pool.head_dim %d unsupported", k_pool->head_dim);
   }
   if (do_v) {
-    if (nvfp4_status st = check_pool(v_pool, "v_pool", v_pool->head_dim, -1, -1)) return st;
+    if (nvfp4_status st = check_pool(v_pool, "v_pool", v_pool->head_dim, -1, -1, -1)) return st;
     if (!head_dim_ok(v_pool->head_dim))
       return fail(NVFP4_E_UNSUPPORTED, "v_pool.head_dim %d unsupported", v_pool->head_dim);
   }
@@ -858,6 +980,7 @@ nvfp4_status nvfp4_quantize_kv(const void* k_src, int64_t k_stride_token, int64_
   if (nvfp4_status st = check_device(stream)) return st;
   auto qa = [](const void* src, int64_t st, int64_t sh, const nvfp4_kv_pool* p) {
     QuantArgs a;
+    a.fp8 = p->kv_dtype == NVFP4_KV_FP8_E4M3;
     a.src = static_cast<const uint16_t*>(src);
     a.s_tok = st;
     a.s_head = sh;

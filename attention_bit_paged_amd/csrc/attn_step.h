@@ -26,24 +26,36 @@ namespace nvfp4 {
 // (base-2 units); until then exp2(x - ref) <= 2^8 and the accumulators stay untouched.
 constexpr float kRescaleSlack = 8.f;
 
-template <int DK, int DV>
+// Storage format of the K/V pools a kernel reads: NVFP4 (packed e2m1 pairs plus one
+// e4m3 scale byte per 16 elements) or FP8 (one e4m3 byte per element, no block scales;
+// the per-tensor scale is applied outside the step like NVFP4's global scale).
+enum KvFmt : int { kNvfp4 = 0, kFp8 = 1 };
+
+template <int DK, int DV, int FMT = kNvfp4>
 struct StepShape {
-  static constexpr int NS = DK / 32;     // QK k-steps; also dwords of a lane's K quarter-row
-  static constexpr int KB = DK / 8;      // K bytes per lane per token
-  static constexpr int KSF = DK / 64;    // K scale bytes per lane per token
-  static constexpr int KSFW = (KSF + 3) / 4;
+  static constexpr bool F8 = FMT == kFp8;
+  static constexpr int NS = DK / 32;     // QK k-steps (eight elements of a quarter row each)
+  static constexpr int KSTEP = F8 ? 8 : 4;         // K bytes per lane and k-step
+  static constexpr int KB = NS * KSTEP;  // K bytes per lane per token
+  static constexpr int KBW = KB / 4;
+  static constexpr int KSF = F8 ? 0 : DK / 64;     // K scale bytes per lane per token
+  static constexpr int KSFW = (KSF + 3) / 4 > 0 ? (KSF + 3) / 4 : 1;
   static constexpr int KPAIRS = (KSF + 1) / 2;
-  static constexpr int VB = DV / 32;     // V bytes per lane per token
+  static constexpr int VB = F8 ? DV / 16 : DV / 32;  // V bytes per lane per token
   static constexpr int VW = (VB + 3) / 4;
   static constexpr int NT = DV / 16;     // PV tiles
-  static constexpr int VSFB = DV >= 512 ? 2 : 1;  // V scale bytes per lane per token
+  static constexpr int VSFB = F8 ? 0 : (DV >= 512 ? 2 : 1);  // V scale bytes per lane per token
   static constexpr int QW = DK / 8;      // dwords of a lane's bf16 Q quarter-row
+  static constexpr int RBK = F8 ? DK : DK / 2;     // bytes of one K row
+  static constexpr int RBV = F8 ? DV : DV / 2;
+  static constexpr int SBK = F8 ? 0 : DK / 16;     // scale bytes of one K row
+  static constexpr int SBV = F8 ? 0 : DV / 16;
 };
 
-template <int DK, int DV>
+template <int DK, int DV, int FMT = kNvfp4>
 struct StepRaw {
-  using S = StepShape<DK, DV>;
-  uint32_t ka[S::NS], kb[S::NS];
+  using S = StepShape<DK, DV, FMT>;
+  uint32_t ka[S::KBW], kb[S::KBW];
   uint32_t ksa[S::KSFW], ksb[S::KSFW];
   uint32_t vd[8][S::VW];
   uint32_t vs[8];
@@ -55,9 +67,9 @@ struct StepRaw {
 // so a step needs two page-table entries (uniform, scalar loads); the ring kernels
 // take their copy bases from this view.  Otherwise (page_size < 16) load() looks every
 // token up on its own.
-template <int DK, int DV, bool PAGE16>
+template <int DK, int DV, bool PAGE16, int FMT = kNvfp4>
 struct PagedView {
-  using S = StepShape<DK, DV>;
+  using S = StepShape<DK, DV, FMT>;
   const int32_t* pt_row;
   int page_shift, page_mask, num_pages;
   const uint8_t* kdat;
@@ -97,22 +109,25 @@ struct PagedView {
 
   // Raw bytes of the step starting at token t0 (page_size < 16), every token looked up
   // on its own.  Keys after tlast are never used; their reads are clamped to tlast.
-  __device__ __forceinline__ void load(StepRaw<DK, DV>& r, int t0, int tlast) {
+  __device__ __forceinline__ void load(StepRaw<DK, DV, FMT>& r, int t0, int tlast) {
     static_assert(!PAGE16, "page_size >= 16 streams through the LDS rings");
     const int ta = min(t0 + 8 * (n >> 2) + (n & 3), tlast);
     const int tb = min(t0 + 8 * (n >> 2) + (n & 3) + 4, tlast);
     const int pga = page_of(ta >> page_shift), pgb = page_of(tb >> page_shift);
     load_bytes<S::KB>(kdat + pga * k_page + (int64_t)(ta & page_mask) * k_tok + j * S::KB, r.ka);
     load_bytes<S::KB>(kdat + pgb * k_page + (int64_t)(tb & page_mask) * k_tok + j * S::KB, r.kb);
-    load_bytes<S::KSF>(ksf + pga * ksf_page + (int64_t)(ta & page_mask) * ksf_tok + j * S::KSF, r.ksa);
-    load_bytes<S::KSF>(ksf + pgb * ksf_page + (int64_t)(tb & page_mask) * ksf_tok + j * S::KSF, r.ksb);
+    if constexpr (!S::F8) {
+      load_bytes<S::KSF>(ksf + pga * ksf_page + (int64_t)(ta & page_mask) * ksf_tok + j * S::KSF, r.ksa);
+      load_bytes<S::KSF>(ksf + pgb * ksf_page + (int64_t)(tb & page_mask) * ksf_tok + j * S::KSF, r.ksb);
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int t = min(t0 + 8 * j + i, tlast);
       const int pg = page_of(t >> page_shift);
       const int64_t sl = t & page_mask;
       load_bytes<S::VB>(vdat + pg * v_page + sl * v_tok + n * S::VB, r.vd[i]);
-      load_bytes<S::VSFB>(vsf + pg * vsf_page + sl * vsf_tok + (n * DV / 16) / 16, &r.vs[i]);
+      if constexpr (!S::F8)
+        load_bytes<S::VSFB>(vsf + pg * vsf_page + sl * vsf_tok + (n * DV / 16) / 16, &r.vs[i]);
     }
   }
 };
@@ -152,11 +167,24 @@ __device__ __forceinline__ float load_q_operand(const uint16_t* qrow, bool valid
   return ldexpf(1.f, qexp - 15);
 }
 
+// Eight consecutive e4m3 bytes (two dwords, element 0 in the low byte) -> exact fp16.
+__device__ __forceinline__ f16x8 fp8x8_to_f16(uint32_t w0, uint32_t w1) {
+  return pack8(fp8x2_to_f16<false>(w0), fp8x2_to_f16<true>(w0), fp8x2_to_f16<false>(w1),
+               fp8x2_to_f16<true>(w1));
+}
+
 // Dequantised K operands of the two token tiles of a step.
-template <int DK, int DV>
-__device__ __forceinline__ void k_operands(const StepRaw<DK, DV>& r, f16x8 (&ka)[DK / 32],
+template <int DK, int DV, int FMT>
+__device__ __forceinline__ void k_operands(const StepRaw<DK, DV, FMT>& r, f16x8 (&ka)[DK / 32],
                                            f16x8 (&kb)[DK / 32]) {
-  using S = StepShape<DK, DV>;
+  using S = StepShape<DK, DV, FMT>;
+  if constexpr (S::F8) {
+#pragma unroll
+    for (int s = 0; s < S::NS; ++s) {
+      ka[s] = fp8x8_to_f16(r.ka[2 * s], r.ka[2 * s + 1]);
+      kb[s] = fp8x8_to_f16(r.kb[2 * s], r.kb[2 * s + 1]);
+    }
+  } else {
   f16x2 kpa[S::KPAIRS], kpb[S::KPAIRS];
 #pragma unroll
   for (int w = 0; w < S::KPAIRS; ++w) {
@@ -172,13 +200,46 @@ __device__ __forceinline__ void k_operands(const StepRaw<DK, DV>& r, f16x8 (&ka)
     kb[s] = dequant8(r.kb[s], scb);
   }
 }
+}
 
-// Dequantised V^T operands of a step: vt[e] holds value dim m*DV/16 + e (m = lane%16)
-// for tokens 8j..8j+7.  With MASK, tokens after tlast get scale 0 (their bytes may be
-// anything, NaN scales included).
+// FP8: the byte transposition pairs the tokens of a k-slot pair: for dword q of the
+// slices of tokens 2p and 2p+1, v_perm_b32 gathers element 4q+e of both tokens into
+// one fp8 pair, which one convert turns into the fp16 pair of PV tile 4q+e.  Tokens
+// after tlast (MASK) read as zero bytes.
 template <int DK, int DV, bool MASK>
-__device__ __forceinline__ void v_operands(const StepRaw<DK, DV>& r, int t0, int tlast, int j,
+__device__ __forceinline__ void v_operands_fp8(const StepRaw<DK, DV, kFp8>& r, int t0, int tlast,
+                                               int j, f16x8 (&vt)[DV / 16]) {
+  using S = StepShape<DK, DV, kFp8>;
+  f16x2 vp[S::NT][4];
+#pragma unroll
+  for (int q = 0; q < S::VW; ++q) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      uint32_t w0 = r.vd[2 * p][q], w1 = r.vd[2 * p + 1][q];
+      if constexpr (MASK) {
+        if (t0 + 8 * j + 2 * p > tlast) w0 = 0u;
+        if (t0 + 8 * j + 2 * p + 1 > tlast) w1 = 0u;
+      }
+      // bytes {w0.b0, w1.b0, w0.b1, w1.b1} and {w0.b2, w1.b2, w0.b3, w1.b3}
+      const uint32_t lo = __builtin_amdgcn_perm(w1, w0, 0x05010400u);
+      const uint32_t hi = __builtin_amdgcn_perm(w1, w0, 0x07030602u);
+      vp[4 * q + 0][p] = fp8x2_to_f16<false>(lo);
+      vp[4 * q + 1][p] = fp8x2_to_f16<true>(lo);
+      vp[4 * q + 2][p] = fp8x2_to_f16<false>(hi);
+      vp[4 * q + 3][p] = fp8x2_to_f16<true>(hi);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < S::NT; ++e) vt[e] = pack8(vp[e][0], vp[e][1], vp[e][2], vp[e][3]);
+}
+
+template <int DK, int DV, bool MASK, int FMT>
+__device__ __forceinline__ void v_operands(const StepRaw<DK, DV, FMT>& r, int t0, int tlast, int j,
                                            f16x8 (&vt)[DV / 16]) {
+  if constexpr (FMT == kFp8) {
+    v_operands_fp8<DK, DV, MASK>(r, t0, tlast, j, vt);
+    return;
+  } else {
   using S = StepShape<DK, DV>;
   uint32_t sw[S::VSFB][2];
 #pragma unroll
@@ -214,6 +275,7 @@ __device__ __forceinline__ void v_operands(const StepRaw<DK, DV>& r, int t0, int
   }
 #pragma unroll
   for (int e = 0; e < S::NT; ++e) vt[e] = pack8(vp[e][0], vp[e][1], vp[e][2], vp[e][3]);
+  }
 }
 
 // Multiplies 16 accumulators by alpha in place.  One asm statement whose operands are

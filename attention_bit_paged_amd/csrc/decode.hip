@@ -27,9 +27,9 @@ namespace {
 // per SIMD lane are shared by the waves on a SIMD, and the kernels of each shape are
 // held to the budget of this many waves (amdgpu_waves_per_eu).  LDS: 160 KiB per CU,
 // and each wave's ring needs two stages at least.
-template <int DK, int DV>
+template <int DK, int DV, int FMT = kNvfp4>
 struct DecodeOcc {
-  static constexpr int STAGE = 16 * DK + 16 * DV + (2 * DK + 2 * DV + 255) / 256 * 256;
+  static constexpr int STAGE = RingBytes<DK, DV, FMT>::STAGE;
   static constexpr int BY_REGS = DK <= 128 ? 4 : (DK == 256 && DV <= 128 ? 3 : 2);
   static constexpr int BY_LDS = (160 * 1024) / (4 * 2 * STAGE);
   static constexpr int WGS = BY_REGS < BY_LDS ? BY_REGS : (BY_LDS > 0 ? BY_LDS : 1);
@@ -37,8 +37,8 @@ struct DecodeOcc {
   // the four waves' states exchanged at the end (accumulators, m, l, bad flag)
   static constexpr int XCH = 3 * (DV / 16 * 4 + 3) * 64 * 4;
   // LDS of one workgroup of the ring kernel: the rings, reused for the exchange
-  static constexpr int RING_SMEM = 4 * RingShape<DK, DV, WAVE_LDS>::WAVE_BYTES > XCH
-                                       ? 4 * RingShape<DK, DV, WAVE_LDS>::WAVE_BYTES
+  static constexpr int RING_SMEM = 4 * RingShape<DK, DV, WAVE_LDS, FMT>::WAVE_BYTES > XCH
+                                       ? 4 * RingShape<DK, DV, WAVE_LDS, FMT>::WAVE_BYTES
                                        : XCH;
   static_assert(RING_SMEM * WGS <= 160 * 1024, "resident workgroups exceed the LDS");
   static_assert(XCH * WGS <= 160 * 1024, "resident workgroups exceed the LDS");
@@ -94,13 +94,13 @@ __device__ __forceinline__ void decode_epilogue(const AttnArgs& a, RowState<DV /
 
 // One 32-token step: dequantise K, S^T = K Q^T, online softmax, dequantise V, O^T += V^T P^T.
 // MASK: the step may hold keys after tlast.
-template <int DK, int DV, bool MASK>
-__device__ __forceinline__ void decode_step(const StepRaw<DK, DV>& r, int t0, int tlast, int j,
+template <int DK, int DV, bool MASK, int FMT>
+__device__ __forceinline__ void decode_step(const StepRaw<DK, DV, FMT>& r, int t0, int tlast, int j,
                                             const f16x8 (&qf)[DK / 32], float score_c,
                                             RowState<DV / 16, AccForm::VGPR>& st) {
-  using S = StepShape<DK, DV>;
+  using S = StepShape<DK, DV, FMT>;
   f16x8 ka[S::NS], kb[S::NS];
-  k_operands<DK, DV>(r, ka, kb);
+  k_operands<DK, DV, FMT>(r, ka, kb);
   f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < S::NS; ++s) {
@@ -109,7 +109,7 @@ __device__ __forceinline__ void decode_step(const StepRaw<DK, DV>& r, int t0, in
   }
   const f16x8 p = st.template softmax<MASK>(sa, sb, score_c, t0, j, tlast);
   f16x8 vt[S::NT];
-  v_operands<DK, DV, MASK>(r, t0, tlast, j, vt);
+  v_operands<DK, DV, MASK, FMT>(r, t0, tlast, j, vt);
   st.pv(vt, p);
 }
 
@@ -228,29 +228,30 @@ struct NewToken {
 
 // page_size >= 16: the chunk streams through a per-wave LDS ring several steps deep.
 // APPEND: the launch also appends the step's new token (AttnArgs::k_new).
-template <int DK, int DV, bool APPEND>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DecodeOcc<DK, DV>::WGS)))
+template <int DK, int DV, bool APPEND, int FMT = kNvfp4>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DecodeOcc<DK, DV, FMT>::WGS)))
 void decode_ring_kernel(AttnArgs a) {
-  using S = StepShape<DK, DV>;
-  constexpr int WL = DecodeOcc<DK, DV>::WAVE_LDS;
-  using R = RingShape<DK, DV, WL>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[DecodeOcc<DK, DV>::RING_SMEM];
+  static_assert(!APPEND || FMT == kNvfp4, "the in-launch append writes NVFP4");
+  using S = StepShape<DK, DV, FMT>;
+  constexpr int WL = DecodeOcc<DK, DV, FMT>::WAVE_LDS;
+  using R = RingShape<DK, DV, WL, FMT>;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[DecodeOcc<DK, DV, FMT>::RING_SMEM];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int j = lane >> 4;
   const int n = lane & 15;
   const DecodeItem it = decode_item(a, wave, n);
 
-  PagedView<DK, DV, true> view;
+  PagedView<DK, DV, true, FMT> view;
   view.init(a, it.b, it.kvh, lane);
-  RingPlan<DK, DV, WL> rp;
+  RingPlan<DK, DV, WL, FMT> rp;
   rp.init(lane, view.k_tok, view.v_tok, view.ksf_tok, view.vsf_tok);
   uint8_t* ring = smem + wave * R::WAVE_BYTES;
   const uint32_t ring_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)ring);
   const int tlast = it.w1 - 1;
   uint32_t bad = 0;
 
-  RingLanes lanes = ring_lanes<DK, DV, WL>(ring_lds, j, n);
+  RingLanes lanes = ring_lanes<DK, DV, WL, FMT>(ring_lds, j, n);
   const int len = it.w1 - it.w0;
   const int nsteps = (len + kDecodeStep - 1) / kDecodeStep;
   // the wave holding the request's last key appends the step's new token; its last
@@ -268,7 +269,7 @@ void decode_ring_kernel(AttnArgs a) {
       load_q_operand<DK>(a.q + (int64_t)it.b * a.q_s_row + (int64_t)it.head * a.q_s_head,
                          it.head_valid, j, qf);
   NewToken<DK, DV> nt;
-  if (appender) {
+  if constexpr (APPEND) if (appender) {
     nt.quantise(a, it.b, it.kvh, lane);
     // Written to the pools now, overlapping the stream.  The stores join the wave's
     // vmcnt queue ahead of later copies, which only makes the ring's waits stronger;
@@ -308,23 +309,23 @@ void decode_ring_kernel(AttnArgs a) {
         ring_issue<DK, DV, WL>(rp, ring_lds + ((s + R::NST - 1) % R::NST) * R::STAGE, view,
                            it.w0 + ahead * kDecodeStep, tlast, bad);
       ring_wait_sel<(R::NST - 1) * R::NDMA>(lanes, more);
-      StepRaw<DK, DV> raw;
-      ring_read<DK, DV>(lanes, s * R::STAGE, raw);
-      decode_step<DK, DV, false>(raw, it.w0 + i * kDecodeStep, tlast, j, qf, score_c, st);
+      StepRaw<DK, DV, FMT> raw;
+      ring_read<DK, DV, FMT>(lanes, s * R::STAGE, raw);
+      decode_step<DK, DV, false, FMT>(raw, it.w0 + i * kDecodeStep, tlast, j, qf, score_c, st);
     }
   }
   if (nfull < nsteps) {  // the last step: partial, or the appender's; it was issued already
     ring_wait<0>(lanes);
     const uint32_t stage_off = (uint32_t)(nfull % R::NST) * R::STAGE;
     const int t0 = it.w0 + nfull * kDecodeStep;
-    if (appender) {
+    if constexpr (APPEND) if (appender) {
       uint32_t stage = ring_lds + stage_off;
       asm volatile("" : "+v"(stage));  // after the wait: the copies have landed
       nt.template inject<WL>(stage, tlast - t0, lane);
     }
-    StepRaw<DK, DV> raw;
-    ring_read<DK, DV>(lanes, stage_off, raw);
-    decode_step<DK, DV, true>(raw, t0, tlast, j, qf, score_c, st);
+    StepRaw<DK, DV, FMT> raw;
+    ring_read<DK, DV, FMT>(lanes, stage_off, raw);
+    decode_step<DK, DV, true, FMT>(raw, t0, tlast, j, qf, score_c, st);
   }
   const bool bad_w = __any(bad != 0);
   __syncthreads();  // every wave is done with its ring: the exchange reuses that memory
@@ -336,21 +337,21 @@ void decode_ring_kernel(AttnArgs a) {
 // (16 bytes per lane and copy) and the scale region (4 bytes per lane and copy, K's
 // scales first).  MASK: words of tokens after `tl` (step-relative) are left out.
 // dat / sf: this lane's byte address in the data and scale regions of stage 0.
-template <int DK, int DV, int WL, bool MASK>
+template <int DK, int DV, int WL, bool MASK, int FMT>
 __device__ __forceinline__ uint32_t fold_stage(uint32_t dat, uint32_t sf, uint32_t stage_off,
                                                int lane, int tl) {
-  using R = RingShape<DK, DV, WL>;
+  using R = RingShape<DK, DV, WL, FMT>;
   uint32_t x = 0;
 #pragma unroll
   for (int c = 0; c < R::N_KD; ++c) {
-    if (MASK && (c * 1024 + 16 * lane) / (DK / 2) > tl) continue;
+    if (MASK && (c * 1024 + 16 * lane) / R::RBK > tl) continue;
     uint32_t w[4];
     lds_load<16>(dat + stage_off + R::OFF_KD + c * 1024, w);
     x ^= w[0] ^ w[1] ^ w[2] ^ w[3];
   }
 #pragma unroll
   for (int c = 0; c < R::N_VD; ++c) {
-    if (MASK && (c * 1024 + 16 * lane) / (DV / 2) > tl) continue;
+    if (MASK && (c * 1024 + 16 * lane) / R::RBV > tl) continue;
     uint32_t w[4];
     lds_load<16>(dat + stage_off + R::OFF_VD + c * 1024, w);
     x ^= w[0] ^ w[1] ^ w[2] ^ w[3];
@@ -359,7 +360,7 @@ __device__ __forceinline__ uint32_t fold_stage(uint32_t dat, uint32_t sf, uint32
   for (int c = 0; c < R::N_SF; ++c) {
     const int byte = c * 256 + 4 * lane;
     if (byte >= R::KS + R::VS) continue;  // padding lanes copy nothing
-    const int tok = byte < R::KS ? byte / (DK / 16) : (byte - R::KS) / (DV / 16);
+    const int tok = byte < R::KS ? byte / R::SBK : (byte - R::KS) / R::SBV;
     if (MASK && tok > tl) continue;
     uint32_t w;
     lds_load<4>(sf + stage_off + c * 256, &w);
@@ -374,19 +375,19 @@ __device__ __forceinline__ uint32_t fold_stage(uint32_t dat, uint32_t sf, uint32
 // be checked.  out[b * Hkv + h] ^= the XOR of every 32-bit word of the packed K and V
 // rows and of their scale rows of the item's keys.  Only the first block of qo heads
 // of a row group streams (larger groups repeat the same keys for each block).
-template <int DK, int DV>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DecodeOcc<DK, DV>::WGS)))
+template <int DK, int DV, int FMT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DecodeOcc<DK, DV, FMT>::WGS)))
 void kv_checksum_kernel(AttnArgs a, uint32_t* out, int num_kv_heads) {
-  constexpr int WL = DecodeOcc<DK, DV>::WAVE_LDS;
-  using R = RingShape<DK, DV, WL>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[DecodeOcc<DK, DV>::RING_SMEM];
+  constexpr int WL = DecodeOcc<DK, DV, FMT>::WAVE_LDS;
+  using R = RingShape<DK, DV, WL, FMT>;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[DecodeOcc<DK, DV, FMT>::RING_SMEM];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const DecodeItem it = decode_item(a, wave, lane & 15);
   if (it.h0 != 0) return;  // uniform over the workgroup; no barrier follows
-  PagedView<DK, DV, true> view;
+  PagedView<DK, DV, true, FMT> view;
   view.init(a, it.b, it.kvh, lane);
-  RingPlan<DK, DV, WL> rp;
+  RingPlan<DK, DV, WL, FMT> rp;
   rp.init(lane, view.k_tok, view.v_tok, view.ksf_tok, view.vsf_tok);
   const uint32_t ring_lds =
       __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(smem + wave * R::WAVE_BYTES));
@@ -417,13 +418,14 @@ void kv_checksum_kernel(AttnArgs a, uint32_t* out, int num_kv_heads) {
         ring_issue<DK, DV, WL>(rp, ring_lds + ((s + R::NST - 1) % R::NST) * R::STAGE, view,
                                it.w0 + ahead * kDecodeStep, tlast, bad);
       ring_wait_sel<(R::NST - 1) * R::NDMA>(lanes, more);
-      x ^= fold_stage<DK, DV, WL, false>(lanes.k, lanes.ks, s * R::STAGE, lane, 0);
+      x ^= fold_stage<DK, DV, WL, false, FMT>(lanes.k, lanes.ks, s * R::STAGE, lane, 0);
     }
   }
   if (nfull < nsteps) {
     ring_wait<0>(lanes);
-    x ^= fold_stage<DK, DV, WL, true>(lanes.k, lanes.ks, (uint32_t)(nfull % R::NST) * R::STAGE,
-                                      lane, tlast - (it.w0 + nfull * kDecodeStep));
+    x ^= fold_stage<DK, DV, WL, true, FMT>(lanes.k, lanes.ks,
+                                           (uint32_t)(nfull % R::NST) * R::STAGE, lane,
+                                           tlast - (it.w0 + nfull * kDecodeStep));
   }
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) x ^= (uint32_t)__shfl_xor((int)x, o);
@@ -436,10 +438,10 @@ __global__ void zero_words_kernel(uint32_t* p, int64_t n) {
 }
 
 // page_size < 16: every token is looked up on its own; the next step is held in registers.
-template <int DK, int DV>
+template <int DK, int DV, int FMT = kNvfp4>
 __global__ __launch_bounds__(256) void decode_regs_kernel(AttnArgs a) {
-  using S = StepShape<DK, DV>;
-  __shared__ float xch[DecodeOcc<DK, DV>::XCH / 4];
+  using S = StepShape<DK, DV, FMT>;
+  __shared__ float xch[DecodeOcc<DK, DV, FMT>::XCH / 4];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int j = lane >> 4;
@@ -450,7 +452,7 @@ __global__ __launch_bounds__(256) void decode_regs_kernel(AttnArgs a) {
   const float score_c = a.score_scale *
       load_q_operand<DK>(a.q + (int64_t)it.b * a.q_s_row + (int64_t)it.head * a.q_s_head,
                          it.head_valid, j, qf);
-  PagedView<DK, DV, false> view;
+  PagedView<DK, DV, false, FMT> view;
   view.init(a, it.b, it.kvh, lane);
   const int tlast = it.w1 - 1;
   RowState<S::NT, AccForm::VGPR> st;
@@ -460,124 +462,113 @@ __global__ __launch_bounds__(256) void decode_regs_kernel(AttnArgs a) {
   const int nfull = len / kDecodeStep;
   auto t_of = [&](int i) { return it.w0 + i * kDecodeStep; };
   // r0 holds step i at the top of every iteration; full steps in pairs, unmasked
-  StepRaw<DK, DV> r0, r1;
+  StepRaw<DK, DV, FMT> r0, r1;
   if (nsteps > 0) view.load(r0, t_of(0), tlast);
   int i = 0;
   for (; i + 1 < nfull; i += 2) {
     view.load(r1, t_of(i + 1), tlast);
-    decode_step<DK, DV, false>(r0, t_of(i), tlast, j, qf, score_c, st);
+    decode_step<DK, DV, false, FMT>(r0, t_of(i), tlast, j, qf, score_c, st);
     if (i + 2 < nsteps) view.load(r0, t_of(i + 2), tlast);
-    decode_step<DK, DV, false>(r1, t_of(i + 1), tlast, j, qf, score_c, st);
+    decode_step<DK, DV, false, FMT>(r1, t_of(i + 1), tlast, j, qf, score_c, st);
   }
   // at most two steps are left, the second one partial
   if (i < nsteps) {
     if (i + 1 < nsteps) view.load(r1, t_of(i + 1), tlast);
-    decode_step<DK, DV, true>(r0, t_of(i), tlast, j, qf, score_c, st);
-    if (i + 1 < nsteps) decode_step<DK, DV, true>(r1, t_of(i + 1), tlast, j, qf, score_c, st);
+    decode_step<DK, DV, true, FMT>(r0, t_of(i), tlast, j, qf, score_c, st);
+    if (i + 1 < nsteps) decode_step<DK, DV, true, FMT>(r1, t_of(i + 1), tlast, j, qf, score_c, st);
   }
   const bool bad_w = __any(view.bad != 0);
   decode_epilogue<DV>(a, st, xch, bad_w, wave, lane, it.b, it.head, n, j, it.head_valid, it.slot);
 }
 
-template <int DK, int DV>
+template <int DK, int DV, int FMT>
 hipError_t launch_dk_dv(int page_shift, const AttnArgs& a, hipStream_t stream) {
   const dim3 grid(a.n_work);
-  if (page_shift >= 4 && a.k_new)
-    launch_attention(decode_ring_kernel<DK, DV, true>, grid, dim3(256), stream, a);
-  else if (page_shift >= 4)
-    launch_attention(decode_ring_kernel<DK, DV, false>, grid, dim3(256), stream, a);
-  else if (!a.k_new)
-    launch_attention(decode_regs_kernel<DK, DV>, grid, dim3(256), stream, a);
+  if constexpr (FMT == kNvfp4) {
+    if (page_shift >= 4 && a.k_new) {
+      launch_attention(decode_ring_kernel<DK, DV, true>, grid, dim3(256), stream, a);
+      return hipGetLastError();
+    }
+  }
+  if (a.k_new) return hipErrorInvalidValue;  // the append: NVFP4 with page_size >= 16 only
+  if (page_shift >= 4)
+    launch_attention(decode_ring_kernel<DK, DV, false, FMT>, grid, dim3(256), stream, a);
   else
-    return hipErrorInvalidValue;  // the append needs the ring kernel (page_size >= 16)
+    launch_attention(decode_regs_kernel<DK, DV, FMT>, grid, dim3(256), stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-bool decode_supported(int dk, int dv) {
-  const bool okk = dk == 64 || dk == 128 || dk == 256 || dk == 512;
-  const bool okv = dv == 64 || dv == 128 || dv == 256 || dv == 512;
-  return okk && okv && dv <= dk && !(dk == 512 && dv == 512);
+// Shapes with kernels: NVFP4 at every (qk, vo) pair of 64..512 with vo <= qk except
+// 512/512; FP8 at head dims up to 256 (a 512-dim FP8 ring does not fit two stages of
+// four waves in LDS at 256 value dims, and is not built for the narrower ones).
+#define NVFP4_DECODE_SHAPES(X)                                                      \
+  X(64, 64, kNvfp4) X(128, 64, kNvfp4) X(128, 128, kNvfp4) X(256, 64, kNvfp4)      \
+  X(256, 128, kNvfp4) X(256, 256, kNvfp4) X(512, 64, kNvfp4) X(512, 128, kNvfp4)   \
+  X(512, 256, kNvfp4) X(64, 64, kFp8) X(128, 64, kFp8) X(128, 128, kFp8)           \
+  X(256, 64, kFp8) X(256, 128, kFp8) X(256, 256, kFp8)
+
+bool decode_supported(int dk, int dv, int fmt) {
+#define NVFP4_DECODE_CASE(K, V, F) \
+  if (dk == K && dv == V && fmt == F) return true;
+  NVFP4_DECODE_SHAPES(NVFP4_DECODE_CASE)
+#undef NVFP4_DECODE_CASE
+  return false;
 }
 
-int decode_wgs_per_cu(int dk, int dv) {
-#define NVFP4_DECODE_CASE(K, V) \
-  if (dk == K && dv == V) return DecodeOcc<K, V>::WGS;
-  NVFP4_DECODE_CASE(64, 64)
-  NVFP4_DECODE_CASE(128, 64)
-  NVFP4_DECODE_CASE(128, 128)
-  NVFP4_DECODE_CASE(256, 64)
-  NVFP4_DECODE_CASE(256, 128)
-  NVFP4_DECODE_CASE(256, 256)
-  NVFP4_DECODE_CASE(512, 64)
-  NVFP4_DECODE_CASE(512, 128)
-  NVFP4_DECODE_CASE(512, 256)
+int decode_wgs_per_cu(int dk, int dv, int fmt) {
+#define NVFP4_DECODE_CASE(K, V, F) \
+  if (dk == K && dv == V && fmt == F) return DecodeOcc<K, V, F>::WGS;
+  NVFP4_DECODE_SHAPES(NVFP4_DECODE_CASE)
 #undef NVFP4_DECODE_CASE
   return 2;
 }
 
-size_t decode_lds_bytes(int dk, int dv, int page_size) {
+size_t decode_lds_bytes(int dk, int dv, int page_size, int fmt) {
   // per CU: the resident workgroups' rings (page_size >= 16) or exchange buffers
-#define NVFP4_DECODE_CASE(K, V)                                                      \
-  if (dk == K && dv == V)                                                            \
-    return (size_t)DecodeOcc<K, V>::WGS *                                            \
-           (page_size >= 16 ? DecodeOcc<K, V>::RING_SMEM : DecodeOcc<K, V>::XCH);
-  NVFP4_DECODE_CASE(64, 64)
-  NVFP4_DECODE_CASE(128, 64)
-  NVFP4_DECODE_CASE(128, 128)
-  NVFP4_DECODE_CASE(256, 64)
-  NVFP4_DECODE_CASE(256, 128)
-  NVFP4_DECODE_CASE(256, 256)
-  NVFP4_DECODE_CASE(512, 64)
-  NVFP4_DECODE_CASE(512, 128)
-  NVFP4_DECODE_CASE(512, 256)
-  NVFP4_DECODE_CASE(512, 512)
+#define NVFP4_DECODE_CASE(K, V, F)                                                   \
+  if (dk == K && dv == V && fmt == F)                                                \
+    return (size_t)DecodeOcc<K, V, F>::WGS *                                         \
+           (page_size >= 16 ? DecodeOcc<K, V, F>::RING_SMEM : DecodeOcc<K, V, F>::XCH);
+  NVFP4_DECODE_SHAPES(NVFP4_DECODE_CASE)
 #undef NVFP4_DECODE_CASE
-  return (size_t)-1;
+  // shapes without a kernel: the least a ring workgroup needs (four waves, two stages)
+  const int rbk = fmt == kFp8 ? dk : dk / 2, rbv = fmt == kFp8 ? dv : dv / 2;
+  const int sf = fmt == kFp8 ? 0 : (2 * dk + 2 * dv + 255) / 256 * 256;
+  const size_t stage = (size_t)32 * (rbk + rbv) + sf;
+  return page_size >= 16 ? 8 * stage : (size_t)3 * (dv / 16 * 4 + 3) * 64 * 4;
 }
 
-hipError_t launch_kv_checksum(int dk, int dv, const AttnArgs& a, uint32_t* out, int batch,
-                              int num_kv_heads, hipStream_t stream) {
+hipError_t launch_kv_checksum(int dk, int dv, int fmt, const AttnArgs& a, uint32_t* out,
+                              int batch, int num_kv_heads, hipStream_t stream) {
   const int64_t n = (int64_t)batch * num_kv_heads;
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
                      out, n);
   if (a.n_work <= 0) return hipGetLastError();
   const dim3 grid(a.n_work);
-#define NVFP4_DECODE_CASE(K, V)                                                                \
-  if (dk == K && dv == V) {                                                                    \
-    launch_attention(kv_checksum_kernel<K, V>, grid, dim3(256), stream, a, out, num_kv_heads); \
-    return hipGetLastError();                                                                  \
+#define NVFP4_DECODE_CASE(K, V, F)                                                       \
+  if (dk == K && dv == V && fmt == F) {                                                  \
+    launch_attention(kv_checksum_kernel<K, V, F>, grid, dim3(256), stream, a, out,       \
+                     num_kv_heads);                                                      \
+    return hipGetLastError();                                                            \
   }
-  NVFP4_DECODE_CASE(64, 64)
-  NVFP4_DECODE_CASE(128, 64)
-  NVFP4_DECODE_CASE(128, 128)
-  NVFP4_DECODE_CASE(256, 64)
-  NVFP4_DECODE_CASE(256, 128)
-  NVFP4_DECODE_CASE(256, 256)
-  NVFP4_DECODE_CASE(512, 64)
-  NVFP4_DECODE_CASE(512, 128)
-  NVFP4_DECODE_CASE(512, 256)
+  NVFP4_DECODE_SHAPES(NVFP4_DECODE_CASE)
 #undef NVFP4_DECODE_CASE
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_decode(int dk, int dv, int page_shift, const AttnArgs& a, hipStream_t stream) {
+hipError_t launch_decode(int dk, int dv, int fmt, int page_shift, const AttnArgs& a,
+                         hipStream_t stream) {
   if (a.n_work <= 0) return hipSuccess;
-#define NVFP4_DECODE_CASE(K, V) \
-  if (dk == K && dv == V) return launch_dk_dv<K, V>(page_shift, a, stream);
-  NVFP4_DECODE_CASE(64, 64)
-  NVFP4_DECODE_CASE(128, 64)
-  NVFP4_DECODE_CASE(128, 128)
-  NVFP4_DECODE_CASE(256, 64)
-  NVFP4_DECODE_CASE(256, 128)
-  NVFP4_DECODE_CASE(256, 256)
-  NVFP4_DECODE_CASE(512, 64)
-  NVFP4_DECODE_CASE(512, 128)
-  NVFP4_DECODE_CASE(512, 256)
+#define NVFP4_DECODE_CASE(K, V, F) \
+  if (dk == K && dv == V && fmt == F) return launch_dk_dv<K, V, F>(page_shift, a, stream);
+  NVFP4_DECODE_SHAPES(NVFP4_DECODE_CASE)
 #undef NVFP4_DECODE_CASE
   return hipErrorInvalidValue;
 }
+
+#undef NVFP4_DECODE_SHAPES
 
 }  // namespace nvfp4

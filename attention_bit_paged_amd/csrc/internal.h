@@ -75,6 +75,7 @@ struct AttnArgs {
 };
 
 struct QuantArgs {
+  int32_t fp8;              // the pool stores FP8 e4m3 bytes (else NVFP4)
   const uint16_t* src;      // bf16 bits
   int64_t s_tok, s_head;    // elements
   uint8_t* data;
@@ -111,23 +112,25 @@ inline void launch_attention(K kernel, dim3 grid, dim3 block, hipStream_t stream
 // Launchers (defined in the .hip files).  Return the hipGetLastError() status of the launch.
 hipError_t launch_quantize(const QuantArgs* k, const QuantArgs* v, int64_t n_tokens,
                            const int64_t* slots, hipStream_t stream);
-hipError_t launch_decode(int dk, int dv, int page_shift, const AttnArgs& a, hipStream_t stream);
+// `fmt` below: the pools' storage format, 0 = NVFP4, 1 = FP8 e4m3 (KvFmt).
+hipError_t launch_decode(int dk, int dv, int fmt, int page_shift, const AttnArgs& a,
+                         hipStream_t stream);
 // Zeroes out[batch * num_kv_heads], then XORs in the KV words a decode plan streams.
-hipError_t launch_kv_checksum(int dk, int dv, const AttnArgs& a, uint32_t* out, int batch,
-                              int num_kv_heads, hipStream_t stream);
-bool decode_supported(int dk, int dv);
+hipError_t launch_kv_checksum(int dk, int dv, int fmt, const AttnArgs& a, uint32_t* out,
+                              int batch, int num_kv_heads, hipStream_t stream);
+bool decode_supported(int dk, int dv, int fmt);
 // Decode workgroups (four waves each) one CU runs at once for this shape.
-int decode_wgs_per_cu(int dk, int dv);
+int decode_wgs_per_cu(int dk, int dv, int fmt);
 // LDS one CU's resident decode workgroups use (any head dims of the set 64..512).
-size_t decode_lds_bytes(int dk, int dv, int page_size);
-hipError_t launch_prefill(int dk, int dv, int page_shift, const AttnArgs& a, int rows_per_item,
+size_t decode_lds_bytes(int dk, int dv, int page_size, int fmt);
+hipError_t launch_prefill(int dk, int dv, int fmt, int page_shift, const AttnArgs& a,
                           hipStream_t stream);
-bool prefill_supported(int dk, int dv);
+bool prefill_supported(int dk, int dv, int fmt);
 int prefill_rows_per_item(int dk, int dv, int group, int page_size);
 // Prefill workgroups one CU runs at once for this shape.
 int prefill_wgs_per_cu(int dk, int dv);
 // LDS one CU's resident prefill workgroups use (any head dims of the set 64..512).
-size_t prefill_lds_bytes(int dk, int dv, int page_size);
+size_t prefill_lds_bytes(int dk, int dv, int page_size, int fmt);
 hipError_t launch_merge_partials(const AttnArgs& a, int n_merges, int dv, int prefill,
                                  hipStream_t stream);
 hipError_t launch_merge_states(const float* o_parts, const float* lse_parts, int64_t rows,

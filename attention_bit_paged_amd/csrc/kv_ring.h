@@ -22,12 +22,29 @@
 namespace nvfp4 {
 
 // WAVE_LDS: LDS bytes available to one wave's ring; the ring is 2..4 stages deep.
-template <int DK, int DV, int WAVE_LDS>
+// FMT: the pools' storage format (FP8 rows are twice as long and have no scale rows).
+template <int DK, int DV, int FMT = kNvfp4>
+struct RingBytes {
+  using S = StepShape<DK, DV, FMT>;
+  static constexpr int KD = 32 * S::RBK;  // 32 tokens of K rows
+  static constexpr int VD = 32 * S::RBV;
+  static constexpr int KS = 32 * S::SBK;  // 32 tokens of K scale rows (0 for FP8)
+  static constexpr int VS = 32 * S::SBV;
+  static constexpr int SFP = (KS + VS + 255) / 256 * 256;  // scale region, padded
+  static constexpr int STAGE = KD + VD + SFP;
+};
+
+template <int DK, int DV, int WAVE_LDS, int FMT = kNvfp4>
 struct RingShape {
-  static constexpr int KD = 16 * DK;  // 32 tokens x DK/2 bytes
-  static constexpr int VD = 16 * DV;
-  static constexpr int KS = 2 * DK;   // 32 tokens x DK/16 scale bytes
-  static constexpr int VS = 2 * DV;
+  using S = StepShape<DK, DV, FMT>;
+  static constexpr int RBK = S::RBK, RBV = S::RBV;
+  // scale row bytes (FP8 has none: every scale branch below is then unreachable, and the
+  // divisor is kept nonzero)
+  static constexpr int SBK = S::SBK > 0 ? S::SBK : 1, SBV = S::SBV > 0 ? S::SBV : 1;
+  static constexpr int KD = 32 * RBK;
+  static constexpr int VD = 32 * RBV;
+  static constexpr int KS = 32 * S::SBK;
+  static constexpr int VS = 32 * S::SBV;
   static constexpr int OFF_KD = 0;
   static constexpr int OFF_VD = KD;
   static constexpr int OFF_SF = KD + VD;  // K scales, then V scales
@@ -42,13 +59,13 @@ struct RingShape {
   // Group of the bytes lane `lane` moves in copy c: 0/1 K rows of token half 0/1,
   // 2/3 V rows, 4/5 K scales, 6/7 V scales; -1 for padding lanes (not issued).
   static constexpr int group(int c, int lane) {
-    if (c < N_KD) return (c * 1024 + lane * 16) / (DK / 2) >= 16 ? 1 : 0;
-    if (c < N_KD + N_VD) return ((c - N_KD) * 1024 + lane * 16) / (DV / 2) >= 16 ? 3 : 2;
+    if (c < N_KD) return (c * 1024 + lane * 16) / RBK >= 16 ? 1 : 0;
+    if (c < N_KD + N_VD) return ((c - N_KD) * 1024 + lane * 16) / RBV >= 16 ? 3 : 2;
     int byte = (c - N_KD - N_VD) * 256 + lane * 4;
     if (byte >= KS + VS) return -1;
-    if (byte < KS) return byte / (DK / 16) >= 16 ? 5 : 4;
+    if (byte < KS) return byte / SBK >= 16 ? 5 : 4;
     byte -= KS;
-    return byte / (DV / 16) >= 16 ? 7 : 6;
+    return byte / SBV >= 16 ? 7 : 6;
   }
   static constexpr uint64_t mask(int c, int g) {
     uint64_t m = 0;
@@ -128,9 +145,9 @@ __device__ __forceinline__ void ring_wait_sel(RingLanes& b, uint32_t newer) {
 }
 
 // Per-lane copy offsets of one stage, relative to the lane's group base.
-template <int DK, int DV, int WAVE_LDS>
+template <int DK, int DV, int WAVE_LDS, int FMT = kNvfp4>
 struct RingPlan {
-  using R = RingShape<DK, DV, WAVE_LDS>;
+  using R = RingShape<DK, DV, WAVE_LDS, FMT>;
   uint32_t off[R::NCOPY];
 
   // token strides in bytes: k_tok/v_tok (data), ks_tok/vs_tok (scales); the host
@@ -140,13 +157,13 @@ struct RingPlan {
 #pragma unroll
     for (int i = 0; i < R::N_KD; ++i) {
       const int byte = i * 1024 + lane * 16;
-      const int t = byte / (DK / 2), in_row = byte % (DK / 2);
+      const int t = byte / R::RBK, in_row = byte % R::RBK;
       off[i] = (uint32_t)(t & 15) * (uint32_t)k_tok + in_row;
     }
 #pragma unroll
     for (int i = 0; i < R::N_VD; ++i) {
       const int byte = i * 1024 + lane * 16;
-      const int t = byte / (DV / 2), in_row = byte % (DV / 2);
+      const int t = byte / R::RBV, in_row = byte % R::RBV;
       off[R::N_KD + i] = (uint32_t)(t & 15) * (uint32_t)v_tok + in_row;
     }
 #pragma unroll
@@ -154,10 +171,10 @@ struct RingPlan {
       int byte = i * 256 + lane * 4;
       uint32_t o = 0;
       if (byte < R::KS) {
-        o = (uint32_t)((byte / (DK / 16)) & 15) * (uint32_t)ks_tok + byte % (DK / 16);
+        o = (uint32_t)((byte / R::SBK) & 15) * (uint32_t)ks_tok + byte % R::SBK;
       } else if (byte < R::KS + R::VS) {
         byte -= R::KS;
-        o = (uint32_t)((byte / (DV / 16)) & 15) * (uint32_t)vs_tok + byte % (DV / 16);
+        o = (uint32_t)((byte / R::SBV) & 15) * (uint32_t)vs_tok + byte % R::SBV;
       }
       off[R::N_KD + R::N_VD + i] = o;
     }
@@ -166,10 +183,10 @@ struct RingPlan {
 
 namespace ring_detail {
 
-template <int DK, int DV, int WL, int POOLS, int C, int G>
+template <int DK, int DV, int WL, int FMT, int POOLS, int C, int G>
 __device__ __forceinline__ void issue_group(uint32_t m0, uint32_t voff,
                                             const uint8_t* const (&base)[8]) {
-  using R = RingShape<DK, DV, WL>;
+  using R = RingShape<DK, DV, WL, FMT>;
   constexpr uint64_t M = ((POOLS >> (G / 2)) & 1) ? R::mask(C, G) : 0;
   constexpr bool X4 = C < R::N_KD + R::N_VD;
   if constexpr (M == ~uint64_t(0)) {
@@ -179,26 +196,26 @@ __device__ __forceinline__ void issue_group(uint32_t m0, uint32_t voff,
   }
 }
 
-template <int DK, int DV, int WL, int POOLS, int C>
-__device__ __forceinline__ void issue_copy(uint32_t stage_lds, const RingPlan<DK, DV, WL>& rp,
+template <int DK, int DV, int WL, int FMT, int POOLS, int C>
+__device__ __forceinline__ void issue_copy(uint32_t stage_lds, const RingPlan<DK, DV, WL, FMT>& rp,
                                            const uint8_t* const (&base)[8]) {
-  using R = RingShape<DK, DV, WL>;
+  using R = RingShape<DK, DV, WL, FMT>;
   const uint32_t m0 = stage_lds + R::lds_off(C);
-  issue_group<DK, DV, WL, POOLS, C, 0>(m0, rp.off[C], base);
-  issue_group<DK, DV, WL, POOLS, C, 1>(m0, rp.off[C], base);
-  issue_group<DK, DV, WL, POOLS, C, 2>(m0, rp.off[C], base);
-  issue_group<DK, DV, WL, POOLS, C, 3>(m0, rp.off[C], base);
-  issue_group<DK, DV, WL, POOLS, C, 4>(m0, rp.off[C], base);
-  issue_group<DK, DV, WL, POOLS, C, 5>(m0, rp.off[C], base);
-  issue_group<DK, DV, WL, POOLS, C, 6>(m0, rp.off[C], base);
-  issue_group<DK, DV, WL, POOLS, C, 7>(m0, rp.off[C], base);
+  issue_group<DK, DV, WL, FMT, POOLS, C, 0>(m0, rp.off[C], base);
+  issue_group<DK, DV, WL, FMT, POOLS, C, 1>(m0, rp.off[C], base);
+  issue_group<DK, DV, WL, FMT, POOLS, C, 2>(m0, rp.off[C], base);
+  issue_group<DK, DV, WL, FMT, POOLS, C, 3>(m0, rp.off[C], base);
+  issue_group<DK, DV, WL, FMT, POOLS, C, 4>(m0, rp.off[C], base);
+  issue_group<DK, DV, WL, FMT, POOLS, C, 5>(m0, rp.off[C], base);
+  issue_group<DK, DV, WL, FMT, POOLS, C, 6>(m0, rp.off[C], base);
+  issue_group<DK, DV, WL, FMT, POOLS, C, 7>(m0, rp.off[C], base);
 }
 
-template <int DK, int DV, int WL, int POOLS, int... Cs>
+template <int DK, int DV, int WL, int FMT, int POOLS, int... Cs>
 __device__ __forceinline__ void issue_all(std::integer_sequence<int, Cs...>, uint32_t stage_lds,
-                                          const RingPlan<DK, DV, WL>& rp,
+                                          const RingPlan<DK, DV, WL, FMT>& rp,
                                           const uint8_t* const (&base)[8]) {
-  (issue_copy<DK, DV, WL, POOLS, Cs>(stage_lds, rp, base), ...);
+  (issue_copy<DK, DV, WL, FMT, POOLS, Cs>(stage_lds, rp, base), ...);
 }
 
 }  // namespace ring_detail
@@ -207,11 +224,11 @@ __device__ __forceinline__ void issue_all(std::integer_sequence<int, Cs...>, uin
 // the pools in the bit set POOLS (see RingShape::ndma).  Bases of the two 16-token
 // halves come from two page-table entries; a half that starts after tlast reuses the
 // first half's page (its bytes are never used).
-template <int DK, int DV, int WL, int POOLS = 0xF>
-__device__ __forceinline__ void ring_issue(const RingPlan<DK, DV, WL>& rp, uint32_t lds_stage,
-                                           const PagedView<DK, DV, true>& pv, int t0, int tlast,
-                                           uint32_t& bad) {
-  using R = RingShape<DK, DV, WL>;
+template <int DK, int DV, int WL, int POOLS = 0xF, int FMT = kNvfp4>
+__device__ __forceinline__ void ring_issue(const RingPlan<DK, DV, WL, FMT>& rp, uint32_t lds_stage,
+                                           const PagedView<DK, DV, true, FMT>& pv, int t0,
+                                           int tlast, uint32_t& bad) {
+  using R = RingShape<DK, DV, WL, FMT>;
   // The page table is read-only while the kernel runs: reading it through the
   // constant address space keeps these uniform reads scalar loads.
   const __attribute__((address_space(4))) int32_t* pt =
@@ -240,21 +257,21 @@ __device__ __forceinline__ void ring_issue(const RingPlan<DK, DV, WL>& rp, uint3
       at(pv.vsf, pg0, s0, pv.vsf_page, pv.vsf_tok),  at(pv.vsf, pg1, s1, pv.vsf_page, pv.vsf_tok)};
   // the previous reads of this stage were consumed already; make sure they completed
   asm volatile("s_waitcnt lgkmcnt(0)");
-  ring_detail::issue_all<DK, DV, WL, POOLS>(std::make_integer_sequence<int, R::NCOPY>{},
-                                             lds_stage, rp, base);
+  ring_detail::issue_all<DK, DV, WL, FMT, POOLS>(std::make_integer_sequence<int, R::NCOPY>{},
+                                                  lds_stage, rp, base);
 }
 
 // LDS addresses of this lane's reads in stage 0 of the ring at ring_lds.
-template <int DK, int DV, int WL>
+template <int DK, int DV, int WL, int FMT = kNvfp4>
 __device__ __forceinline__ RingLanes ring_lanes(uint32_t ring_lds, int j, int n) {
-  using R = RingShape<DK, DV, WL>;
-  using S = StepShape<DK, DV>;
+  using R = RingShape<DK, DV, WL, FMT>;
+  using S = StepShape<DK, DV, FMT>;
   const int ta = 8 * (n >> 2) + (n & 3);
   RingLanes b;
-  b.k = ring_lds + R::OFF_KD + ta * (DK / 2) + j * S::KB;
-  b.ks = ring_lds + R::OFF_SF + ta * (DK / 16) + j * S::KSF;
-  b.v = ring_lds + R::OFF_VD + 8 * j * (DV / 2) + n * S::VB;
-  b.vs = ring_lds + R::OFF_SF + R::KS + 8 * j * (DV / 16) + (n * DV / 16) / 16;
+  b.k = ring_lds + R::OFF_KD + ta * S::RBK + j * S::KB;
+  b.ks = ring_lds + R::OFF_SF + ta * S::SBK + j * S::KSF;
+  b.v = ring_lds + R::OFF_VD + 8 * j * S::RBV + n * S::VB;
+  b.vs = ring_lds + R::OFF_SF + R::KS + 8 * j * S::SBV + (n * DV / 16) / 16;
   return b;
 }
 
@@ -292,18 +309,20 @@ __device__ __forceinline__ void lds_load(uint32_t addr, uint32_t* out) {
 // Reads a step's raw bytes for this lane from the stage `stage_off` bytes past the
 // lane addresses, in the register layout the step helpers expect (the same as a
 // direct load from the pool).
-template <int DK, int DV>
+template <int DK, int DV, int FMT = kNvfp4>
 __device__ __forceinline__ void ring_read(const RingLanes& b, uint32_t stage_off,
-                                          StepRaw<DK, DV>& r) {
-  using S = StepShape<DK, DV>;
+                                          StepRaw<DK, DV, FMT>& r) {
+  using S = StepShape<DK, DV, FMT>;
   lds_load<S::KB>(b.k + stage_off, r.ka);
-  lds_load<S::KB>(b.k + stage_off + 4 * (DK / 2), r.kb);
-  lds_load<S::KSF>(b.ks + stage_off, r.ksa);
-  lds_load<S::KSF>(b.ks + stage_off + 4 * (DK / 16), r.ksb);
+  lds_load<S::KB>(b.k + stage_off + 4 * S::RBK, r.kb);
+  if constexpr (!S::F8) {
+    lds_load<S::KSF>(b.ks + stage_off, r.ksa);
+    lds_load<S::KSF>(b.ks + stage_off + 4 * S::SBK, r.ksb);
+  }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    lds_load<S::VB>(b.v + stage_off + i * (DV / 2), r.vd[i]);
-    lds_load<S::VSFB>(b.vs + stage_off + i * (DV / 16), &r.vs[i]);
+    lds_load<S::VB>(b.v + stage_off + i * S::RBV, r.vd[i]);
+    if constexpr (!S::F8) lds_load<S::VSFB>(b.vs + stage_off + i * S::SBV, &r.vs[i]);
   }
 }
 

@@ -44,9 +44,9 @@ constexpr int prefill_nr() {
 }
 
 // page_size < 16: every token is looked up on its own (PagedView::load).
-template <int DK, int DV>
+template <int DK, int DV, int FMT = kNvfp4>
 __global__ __launch_bounds__(256) void prefill_regs_kernel(AttnArgs a) {
-  using S = StepShape<DK, DV>;
+  using S = StepShape<DK, DV, FMT>;
   constexpr int NR = prefill_nr<DK>();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256) void prefill_regs_kernel(AttnArgs a) {
   int mask_from = kv1 - kDecodeStep;
   if (a.causal) mask_from = min(mask_from, q0 + row_base / G + off + 1 - kDecodeStep);
 
-  PagedView<DK, DV, false> view;
+  PagedView<DK, DV, false, FMT> view;
   view.init(a, b, kvh, lane);
   const int tlast = kv1 - 1;
 
@@ -102,9 +102,9 @@ __global__ __launch_bounds__(256) void prefill_regs_kernel(AttnArgs a) {
 #pragma unroll
   for (int rg = 0; rg < NR; ++rg) st[rg].init();
 
-  auto step = [&](const StepRaw<DK, DV>& r, int t0) {
+  auto step = [&](const StepRaw<DK, DV, FMT>& r, int t0) {
     f16x8 ka[S::NS], kb[S::NS];
-    k_operands<DK, DV>(r, ka, kb);
+    k_operands<DK, DV, FMT>(r, ka, kb);
     const bool masked = t0 > mask_from;
     f16x8 p[NR];
 #pragma unroll
@@ -120,14 +120,14 @@ __global__ __launch_bounds__(256) void prefill_regs_kernel(AttnArgs a) {
     }
     f16x8 vt[S::NT];
     if (t0 + kDecodeStep > kv1)
-      v_operands<DK, DV, true>(r, t0, tlast, j, vt);
+      v_operands<DK, DV, true, FMT>(r, t0, tlast, j, vt);
     else
-      v_operands<DK, DV, false>(r, t0, tlast, j, vt);
+      v_operands<DK, DV, false, FMT>(r, t0, tlast, j, vt);
 #pragma unroll
     for (int rg = 0; rg < NR; ++rg) st[rg].pv(vt, p[rg]);
   };
 
-  StepRaw<DK, DV> r0, r1;
+  StepRaw<DK, DV, FMT> r0, r1;
   if (kv0 < wave_end) view.load(r0, kv0, tlast);
   for (int t0 = kv0; t0 < wave_end; t0 += 2 * kDecodeStep) {
     const int t1 = t0 + kDecodeStep;
@@ -160,9 +160,9 @@ __global__ __launch_bounds__(256) void prefill_regs_kernel(AttnArgs a) {
 
 // ------------------------------------------------------------------ cooperative --
 
-template <int DK, int DV>
+template <int DK, int DV, int FMT = kNvfp4>
 struct CoopShape {
-  using S = StepShape<DK, DV>;
+  using S = StepShape<DK, DV, FMT>;
   static constexpr bool OK = (DK <= 256 && DV <= 256) || (DK == 512 && DV <= 256);
   // Head dims up to 128: four waves of three row groups, two workgroups per CU (two
   // waves per SIMD hide each other's latencies, and the two workgroups' barriers are
@@ -178,8 +178,8 @@ struct CoopShape {
   static constexpr int ROWS = NW * NR * 16;       // rows per work item
   static constexpr int NOP = 2 * S::NS + S::NT;   // operand vectors per step
   static constexpr int OPB = NOP * 64 * 16;       // bytes of one operand buffer
-  static constexpr int RAW_STAGE = 16 * DK + 16 * DV + (2 * DK + 2 * DV + 255) / 256 * 256;
-  using R = RingShape<DK, DV, 3 * RAW_STAGE>;     // three raw stages
+  static constexpr int RAW_STAGE = RingBytes<DK, DV, FMT>::STAGE;
+  using R = RingShape<DK, DV, 3 * RAW_STAGE, FMT>;  // three raw stages
   static constexpr int LDS = 3 * RAW_STAGE + 2 * OPB;
   static constexpr int KE = (2 * S::NS + NW - 1) / NW;  // K operand entries per lane
   static constexpr int VH = NW / 4;               // V tiles split in this many parts
@@ -190,26 +190,38 @@ struct CoopShape {
 
 constexpr int kLdsPerCu = 160 * 1024;
 
+// LDS of one cooperative workgroup: three raw stages of 32 tokens (rows and, for NVFP4,
+// scale rows) and two fp16 operand buffers (2 NS K entries and NT V tiles of 64 lanes x
+// 16 bytes).  A formula, so that shapes without a kernel can be priced too.
+constexpr int coop_lds_formula(int dk, int dv, int fmt) {
+  const int rbk = fmt == kFp8 ? dk : dk / 2, rbv = fmt == kFp8 ? dv : dv / 2;
+  const int sf = fmt == kFp8 ? 0 : (2 * dk + 2 * dv + 255) / 256 * 256;
+  const int raw = 32 * (rbk + rbv) + sf;
+  const int opb = (2 * (dk / 32) + dv / 16) * 64 * 16;
+  return 3 * raw + 2 * opb;
+}
+constexpr int coop_wgs_per_cu(int dk, int dv) { return dk <= 128 && dv <= 128 ? 2 : 1; }
+
 // Per-lane LDS offsets of the cooperative dequantisation (constant for the kernel).
 // Operand o < 2*NS is K tile o/NS (token tile A or B), k-step o%NS; operand 2*NS + e is
 // V^T tile e.  Entry (o, lane) is the 16 bytes lane `lane` loads for operand o.  K
 // entries: wave w makes entries (w + NW*r, lane).  V: lane L of the workgroup makes,
 // for the operand lane c = L / (4*VH), the token pair p = L%4 of the V tiles of part
 // (L/4)%VH.
-template <int DK, int DV>
+template <int DK, int DV, int FMT = kNvfp4>
 struct CoopLanes {
-  using S = StepShape<DK, DV>;
-  using C = CoopShape<DK, DV>;
+  using S = StepShape<DK, DV, FMT>;
+  using C = CoopShape<DK, DV, FMT>;
   using R = typename C::R;
   // Entry r of a lane is operand wave + NW*r.  NW divides NS (or a lane has one entry),
   // so entry r lies a fixed distance from entry 0 in the raw stage and in the operand
   // buffer: one per-lane base per pool, the rest immediate offsets of the LDS accesses.
   static_assert(S::NS % C::NW == 0 || C::KE == 1, "K entry spacing");
   static constexpr uint32_t k_raw_off(int r) {
-    return (C::NW * r) / S::NS * 4 * (DK / 2) + 4 * ((C::NW * r) % S::NS);
+    return (C::NW * r) / S::NS * 4 * S::RBK + S::KSTEP * ((C::NW * r) % S::NS);
   }
   static constexpr uint32_t k_sc_off(int r) {
-    return (C::NW * r) / S::NS * 4 * (DK / 16) + ((C::NW * r) % S::NS) / 2;
+    return (C::NW * r) / S::NS * 4 * S::SBK + ((C::NW * r) % S::NS) / 2;
   }
   static constexpr uint32_t k_dst_off(int r) { return C::NW * r * 64 * 16; }
   uint32_t k_raw, k_sc, k_dst;  // entry 0
@@ -221,16 +233,16 @@ struct CoopLanes {
     const int o = min(wave, 2 * S::NS - 1);  // clamped: unused when past the end
     const int tile = o / S::NS, s = o % S::NS;
     const int k_tok = 8 * (n >> 2) + (n & 3) + 4 * tile;
-    k_raw = R::OFF_KD + k_tok * (DK / 2) + j * S::KB + 4 * s;
-    k_sc = R::OFF_SF + k_tok * (DK / 16) + j * S::KSF + (s >> 1);
+    k_raw = R::OFF_KD + k_tok * S::RBK + j * S::KB + S::KSTEP * s;
+    k_sc = R::OFF_SF + k_tok * S::SBK + j * S::KSF + (s >> 1);
     k_dst = (o * 64 + lane) * 16;
     const int L = wave * 64 + lane;
     const int c = L / (4 * C::VH), p = L & 3;
     part = (L >> 2) % C::VH;
     const int jj = c >> 4, m = c & 15;
     v_tok = 8 * jj + 2 * p;
-    v_raw = R::OFF_VD + v_tok * (DV / 2) + m * S::VB;
-    v_sc = R::OFF_SF + R::KS + v_tok * (DV / 16) + (m * (DV / 16)) / 16;
+    v_raw = R::OFF_VD + v_tok * S::RBV + m * S::VB;
+    v_sc = R::OFF_SF + R::KS + v_tok * S::SBV + (m * (DV / 16)) / 16;
     v_dst = (2 * S::NS * 64 + c) * 16 + 4 * p;
   }
 };
@@ -242,54 +254,85 @@ struct CoopLanes {
 // would reach every output through its zero probability.  Key rows past the end are
 // left as they are: a bad key row only spoils its own scores, which the softmax of a
 // step that holds such keys replaces by -inf.
-template <int DK, int DV>
+template <int DK, int DV, int FMT = kNvfp4>
 struct CoopRaw {
-  using S = StepShape<DK, DV>;
-  using C = CoopShape<DK, DV>;
+  using S = StepShape<DK, DV, FMT>;
+  using C = CoopShape<DK, DV, FMT>;
   static constexpr int NB = S::VB < 4 ? S::VB : 4;   // bytes of the V slice per dword
-  static constexpr int EPD = 2 * NB;                 // V tiles per slice dword
-  uint32_t kw[C::KE], ksc[C::KE], sa, sb, vw0[S::VW], vw1[S::VW];
+  static constexpr int EPD = S::F8 ? NB : 2 * NB;    // V tiles per slice dword
+  static constexpr int KW = S::KSTEP / 4;            // dwords of one K entry
+  uint32_t kw[C::KE][KW], ksc[C::KE], sa, sb, vw0[S::VW], vw1[S::VW];
 
-  __device__ __forceinline__ void load(uint32_t raw, int wave, const CoopLanes<DK, DV>& cl) {
+  __device__ __forceinline__ void load(uint32_t raw, int wave, const CoopLanes<DK, DV, FMT>& cl) {
 #pragma unroll
     for (int r = 0; r < C::KE; ++r) {
       // wave-uniform; always true when the K entries divide evenly among the waves
       if ((2 * S::NS) % C::NW == 0 || wave + C::NW * r < 2 * S::NS) {
-        lds_load<4>(raw + cl.k_raw + cl.k_raw_off(r), &kw[r]);
-        lds_load<1>(raw + cl.k_sc + cl.k_sc_off(r), &ksc[r]);
+        lds_load<S::KSTEP>(raw + cl.k_raw + cl.k_raw_off(r), kw[r]);
+        if constexpr (!S::F8) lds_load<1>(raw + cl.k_sc + cl.k_sc_off(r), &ksc[r]);
       }
     }
-    const uint32_t vs = raw + cl.v_sc;
-    lds_load<1>(vs, &sa);
-    lds_load<1>(vs + DV / 16, &sb);
+    if constexpr (!S::F8) {
+      const uint32_t vs = raw + cl.v_sc;
+      lds_load<1>(vs, &sa);
+      lds_load<1>(vs + DV / 16, &sb);
+    }
     const uint32_t vr = raw + cl.v_raw;
 #pragma unroll
     for (int q = 0; q < S::VW; ++q) {
       if (C::VH > 1 && C::VPART >= EPD && (q * EPD) / C::VPART != cl.part) continue;
       lds_load<NB>(vr + 4 * q, &vw0[q]);
-      lds_load<NB>(vr + DV / 2 + 4 * q, &vw1[q]);
+      lds_load<NB>(vr + S::RBV + 4 * q, &vw1[q]);
     }
   }
   template <bool MASK>
-  __device__ __forceinline__ void store(uint32_t opb, int wave, const CoopLanes<DK, DV>& cl, int kleft);
+  __device__ __forceinline__ void store(uint32_t opb, int wave, const CoopLanes<DK, DV, FMT>& cl,
+                                        int kleft);
 };
 
-template <int DK, int DV>
+template <int DK, int DV, int FMT>
 template <bool MASK>
-__device__ __forceinline__ void CoopRaw<DK, DV>::store(uint32_t opb, int wave,
-                                                       const CoopLanes<DK, DV>& cl, int kleft) {
+__device__ __forceinline__ void CoopRaw<DK, DV, FMT>::store(uint32_t opb, int wave,
+                                                            const CoopLanes<DK, DV, FMT>& cl,
+                                                            int kleft) {
   typedef __attribute__((address_space(3))) uint8_t* lds_p;
 #pragma unroll
   for (int r = 0; r < C::KE; ++r) {
     if ((2 * S::NS) % C::NW == 0 || wave + C::NW * r < 2 * S::NS) {
-      const f16x8 v = dequant8(kw[r], splat_lo(fp8x2_to_f16<false>(ksc[r])));
+      f16x8 v;
+      if constexpr (S::F8)
+        v = fp8x8_to_f16(kw[r][0], kw[r][1]);
+      else
+        v = dequant8(kw[r][0], splat_lo(fp8x2_to_f16<false>(ksc[r])));
       *(__attribute__((address_space(3))) f16x8*)(lds_p)(size_t)(opb + cl.k_dst + cl.k_dst_off(r)) = v;
     }
   }
+  const uint32_t vd = opb + cl.v_dst;
+  if constexpr (S::F8) {
+    // value rows past the chunk's last key read as zero bytes; the byte transposition
+    // pairs tokens v_tok and v_tok + 1 for each element (see v_operands_fp8)
+#pragma unroll
+    for (int q = 0; q < S::VW; ++q) {
+      if (C::VH > 1 && C::VPART >= EPD && (q * EPD) / C::VPART != cl.part) continue;
+      const uint32_t w0 = MASK && cl.v_tok > kleft ? 0u : vw0[q];
+      const uint32_t w1 = MASK && cl.v_tok + 1 > kleft ? 0u : vw1[q];
+      const uint32_t lo = __builtin_amdgcn_perm(w1, w0, 0x05010400u);
+      const uint32_t hi = __builtin_amdgcn_perm(w1, w0, 0x07030602u);
+#pragma unroll
+      for (int k = 0; k < EPD; ++k) {
+        if (C::VH > 1 && C::VPART < EPD && k / C::VPART != cl.part) continue;
+        const f16x2 v = k == 0 ? fp8x2_to_f16<false>(lo)
+                               : (k == 1 ? fp8x2_to_f16<true>(lo)
+                                         : (k == 2 ? fp8x2_to_f16<false>(hi) : fp8x2_to_f16<true>(hi)));
+        *(__attribute__((address_space(3))) uint32_t*)(lds_p)(size_t)(vd + (EPD * q + k) * 1024) =
+            f16x2_bits(v);
+      }
+    }
+    return;
+  } else {
   if (MASK && cl.v_tok > kleft) sa = 0;
   if (MASK && cl.v_tok + 1 > kleft) sb = 0;
   const f16x2 sp = fp8x2_to_f16<false>(sa | (sb << 8));
-  const uint32_t vd = opb + cl.v_dst;
 #pragma unroll
   for (int q = 0; q < S::VW; ++q) {
     // a part covers VPART consecutive tiles: whole dwords, or a share of one
@@ -314,24 +357,25 @@ __device__ __forceinline__ void CoopRaw<DK, DV>::store(uint32_t opb, int wave,
       *(__attribute__((address_space(3))) uint32_t*)(lds_p)(size_t)(vd + e * 1024) = f16x2_bits(v);
     }
   }
+  }
 }
 
 // Dequantises the raw stage at `raw` into the operand buffer at `opb`.  MASK: value rows
 // past `kleft` get scale 0.  Every raw read first: the operand stores may not move above
 // them (the compiler cannot tell the raw stage from the operand buffer).
-template <int DK, int DV, bool MASK>
+template <int DK, int DV, bool MASK, int FMT>
 __device__ __forceinline__ void coop_dequant(uint32_t raw, uint32_t opb, int wave,
-                                             const CoopLanes<DK, DV>& cl, int kleft) {
-  CoopRaw<DK, DV> r;
+                                             const CoopLanes<DK, DV, FMT>& cl, int kleft) {
+  CoopRaw<DK, DV, FMT> r;
   r.load(raw, wave, cl);
   r.template store<MASK>(opb, wave, cl, kleft);
 }
 
 // Waits until this wave's copies of all but the newest issued step are done (or all
 // of them).  Waves 0..3 each copy one pool; the others copy nothing.
-template <int DK, int DV>
+template <int DK, int DV, int FMT>
 __device__ __forceinline__ void coop_wait(int wave, bool one_newer) {
-  using R = typename CoopShape<DK, DV>::R;
+  using R = typename CoopShape<DK, DV, FMT>::R;
   constexpr int N0 = R::ndma(1), N1 = R::ndma(2), N2 = R::ndma(4), N3 = R::ndma(8);
   if (wave > 3) return;
   if (!one_newer) {
@@ -350,13 +394,13 @@ __device__ __forceinline__ void coop_wait(int wave, bool one_newer) {
 // The copy offsets of the one pool this wave issues (wave 0: K data, 1: V data, 2 and 3:
 // the scale bytes, whose copies carry both pools' lanes).  The full plan holds every
 // pool's offsets; kept whole in each wave they cost registers the loop needs.
-template <int DK, int DV>
+template <int DK, int DV, int FMT = kNvfp4>
 struct CoopCopies {
-  using R = RingShape<DK, DV, 3 * CoopShape<DK, DV>::RAW_STAGE>;
-  using Plan = RingPlan<DK, DV, 3 * CoopShape<DK, DV>::RAW_STAGE>;
+  using R = RingShape<DK, DV, 3 * CoopShape<DK, DV, FMT>::RAW_STAGE, FMT>;
+  using Plan = RingPlan<DK, DV, 3 * CoopShape<DK, DV, FMT>::RAW_STAGE, FMT>;
   static constexpr int MAXC = R::N_KD > R::N_VD ? (R::N_KD > R::N_SF ? R::N_KD : R::N_SF)
                                                 : (R::N_VD > R::N_SF ? R::N_VD : R::N_SF);
-  uint32_t mine[MAXC];
+  uint32_t mine[MAXC > 0 ? MAXC : 1];
 
   __device__ __forceinline__ void init(const Plan& rp, int wave) {
 #pragma unroll
@@ -381,15 +425,17 @@ struct CoopCopies {
   }
 };
 
-template <int DK, int DV>
-__device__ __forceinline__ void coop_issue(int wave, const CoopCopies<DK, DV>& cc, uint32_t stage,
-                                           const PagedView<DK, DV, true>& view, int t0, int tlast,
-                                           uint32_t& bad) {
-  constexpr int WL = 3 * CoopShape<DK, DV>::RAW_STAGE;
+template <int DK, int DV, int FMT>
+__device__ __forceinline__ void coop_issue(int wave, const CoopCopies<DK, DV, FMT>& cc,
+                                           uint32_t stage, const PagedView<DK, DV, true, FMT>& view,
+                                           int t0, int tlast, uint32_t& bad) {
+  constexpr int WL = 3 * CoopShape<DK, DV, FMT>::RAW_STAGE;
   if (wave == 0) ring_issue<DK, DV, WL, 1>(cc.template expand<1>(), stage, view, t0, tlast, bad);
   else if (wave == 1) ring_issue<DK, DV, WL, 2>(cc.template expand<2>(), stage, view, t0, tlast, bad);
-  else if (wave == 2) ring_issue<DK, DV, WL, 4>(cc.template expand<4>(), stage, view, t0, tlast, bad);
-  else if (wave == 3) ring_issue<DK, DV, WL, 8>(cc.template expand<8>(), stage, view, t0, tlast, bad);
+  else if constexpr (!StepShape<DK, DV, FMT>::F8) {  // FP8 has no scale pools
+    if (wave == 2) ring_issue<DK, DV, WL, 4>(cc.template expand<4>(), stage, view, t0, tlast, bad);
+    else if (wave == 3) ring_issue<DK, DV, WL, 8>(cc.template expand<8>(), stage, view, t0, tlast, bad);
+  }
 }
 
 // Q quarter-row multiplied by the score factor c (the scores then leave the product in
@@ -473,15 +519,17 @@ __device__ __forceinline__ f16x8 probs_shifted(RowState<NT, AccForm::VGPR>& st, 
   return pack8(pp[0], pp[1], pp[2], pp[3]);
 }
 
-template <int DK, int DV>
-__global__ __launch_bounds__((CoopShape<DK, DV>::NW * 64))
-__attribute__((amdgpu_waves_per_eu(CoopShape<DK, DV>::WGS_PER_CU)))
+template <int DK, int DV, int FMT = kNvfp4>
+__global__ __launch_bounds__((CoopShape<DK, DV, FMT>::NW * 64))
+__attribute__((amdgpu_waves_per_eu(CoopShape<DK, DV, FMT>::WGS_PER_CU)))
 void prefill_coop_kernel(AttnArgs a) {
-  using S = StepShape<DK, DV>;
-  using C = CoopShape<DK, DV>;
+  using S = StepShape<DK, DV, FMT>;
+  using C = CoopShape<DK, DV, FMT>;
   constexpr int NR = C::NR;
   constexpr int WL = 3 * C::RAW_STAGE;
   static_assert(C::OK, "shape has no cooperative kernel");
+  static_assert(C::LDS == coop_lds_formula(DK, DV, FMT) &&
+                C::WGS_PER_CU == coop_wgs_per_cu(DK, DV), "LDS formula");
   static_assert(C::LDS * C::WGS_PER_CU <= kLdsPerCu, "resident workgroups exceed the LDS");
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -508,24 +556,25 @@ void prefill_coop_kernel(AttnArgs a) {
   const int tlast = kv1 - 1;
   const int nsteps = tile_end > kv0 ? (tile_end - kv0 + kDecodeStep - 1) / kDecodeStep : 0;
 
-  PagedView<DK, DV, true> view;
+  PagedView<DK, DV, true, FMT> view;
   view.init(a, b, kvh, lane);
-  CoopCopies<DK, DV> cc;
+  CoopCopies<DK, DV, FMT> cc;
   {
-    RingPlan<DK, DV, WL> rp;
+    RingPlan<DK, DV, WL, FMT> rp;
     rp.init(lane, view.k_tok, view.v_tok, view.ksf_tok, view.vsf_tok);
     cc.init(rp, wave);
   }
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
   const uint32_t raw0 = lds0, opb0 = lds0 + 3 * C::RAW_STAGE;
-  CoopLanes<DK, DV> cl;
+  CoopLanes<DK, DV, FMT> cl;
   cl.init(wave, lane);
   uint32_t bad = 0;
 
   // The first three steps' copies go out before Q is read, so that the two memory
   // latencies of a work item's start overlap.
   for (int i = 0; i < 3 && i < nsteps; ++i)
-    coop_issue<DK, DV>(wave, cc, raw0 + i * C::RAW_STAGE, view, kv0 + i * kDecodeStep, tlast, bad);
+    coop_issue<DK, DV, FMT>(wave, cc, raw0 + i * C::RAW_STAGE, view, kv0 + i * kDecodeStep, tlast,
+                            bad);
   // Head dims up to 256: Q carries the score factor (see ShiftRef) unless some row of
   // the wave could overflow fp16; that wave then takes the exact prescaled Q.
   bool safe = true;
@@ -586,10 +635,11 @@ void prefill_coop_kernel(AttnArgs a) {
     const bool next = i + 1 < nsteps;
     // raw step i+1 landed (only step i+2 may still be in flight); operands of step i
     // are visible; nobody reads operand buffer (i+1)%2 or raw stage i%3 any more
-    if (next) coop_wait<DK, DV>(wave, i + 2 < nsteps);
+    if (next) coop_wait<DK, DV, FMT>(wave, i + 2 < nsteps);
     __syncthreads();
     if (i + 3 < nsteps)
-      coop_issue<DK, DV>(wave, cc, raw0 + (i % 3) * C::RAW_STAGE, view, t_of(i + 3), tlast, bad);
+      coop_issue<DK, DV, FMT>(wave, cc, raw0 + (i % 3) * C::RAW_STAGE, view, t_of(i + 3), tlast,
+                              bad);
     // Stage and buffer bases as single scalars: left to itself the compiler folds the
     // modulo's parts into every lane address separately (two vector adds per address).
     const uint32_t ob = __builtin_amdgcn_readfirstlane(opb0 + (i & 1) * C::OPB);
@@ -600,9 +650,9 @@ void prefill_coop_kernel(AttnArgs a) {
     if constexpr (C::WIDE) {
       if (next) {
         if (t_of(i + 1) + kDecodeStep - 1 > tlast)
-          coop_dequant<DK, DV, true>(rs, ob1, wave, cl, tlast - t_of(i + 1));
+          coop_dequant<DK, DV, true, FMT>(rs, ob1, wave, cl, tlast - t_of(i + 1));
         else
-          coop_dequant<DK, DV, false>(rs, ob1, wave, cl, 0);
+          coop_dequant<DK, DV, false, FMT>(rs, ob1, wave, cl, 0);
       }
       f32x4 sa[NR], sb[NR];
 #pragma unroll
@@ -674,7 +724,7 @@ void prefill_coop_kernel(AttnArgs a) {
       lds_load<16>(obl + s * 1024, reinterpret_cast<uint32_t*>(&ka[s]));
       lds_load<16>(obl + (S::NS + s) * 1024, reinterpret_cast<uint32_t*>(&kb[s]));
     }
-    CoopRaw<DK, DV> raw;
+    CoopRaw<DK, DV, FMT> raw;
     raw.load(rs, wave, cl);
     f32x4 sa[NR], sb[NR];
 #pragma unroll
@@ -738,9 +788,9 @@ void prefill_coop_kernel(AttnArgs a) {
   };
   // prologue: three steps in flight (issued above), step 0 dequantised
   if (nsteps > 0) {
-    coop_wait<DK, DV>(wave, false);
+    coop_wait<DK, DV, FMT>(wave, false);
     __syncthreads();
-    coop_dequant<DK, DV, true>(raw0, opb0, wave, cl, tlast - t_of(0));
+    coop_dequant<DK, DV, true, FMT>(raw0, opb0, wave, cl, tlast - t_of(0));
   }
   // steps whose 32 keys are visible to every row of the tile, then the rest
   const int tile_min_last = a.causal ? min(kv1 - 1, q0 + off) : kv1 - 1;
@@ -776,22 +826,34 @@ void prefill_coop_kernel(AttnArgs a) {
   }
 }
 
-template <int DK, int DV>
+template <int DK, int DV, int FMT>
 hipError_t launch_dk_dv(int page_shift, const AttnArgs& a, hipStream_t stream) {
   const dim3 grid(a.n_work);
   if (page_shift >= 4)
-    launch_attention(prefill_coop_kernel<DK, DV>, grid, dim3(CoopShape<DK, DV>::NW * 64), stream, a);
+    launch_attention(prefill_coop_kernel<DK, DV, FMT>, grid,
+                     dim3(CoopShape<DK, DV, FMT>::NW * 64), stream, a);
   else
-    launch_attention(prefill_regs_kernel<DK, DV>, grid, dim3(256), stream, a);
+    launch_attention(prefill_regs_kernel<DK, DV, FMT>, grid, dim3(256), stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-bool prefill_supported(int dk, int dv) {
-  const bool okk = dk == 64 || dk == 128 || dk == 256 || dk == 512;
-  const bool okv = dv == 64 || dv == 128 || dv == 256 || dv == 512;
-  return okk && okv && dv <= dk && !(dk == 512 && dv == 512);
+// Shapes with kernels: NVFP4 at every (qk, vo) pair of 64..512 with vo <= qk except
+// 512/512; FP8 at head dims up to 256 (the 512/256 FP8 tile needs more LDS than a CU
+// has, and the narrower 512-dim FP8 shapes are not built).
+#define NVFP4_PREFILL_SHAPES(X)                                                     \
+  X(64, 64, kNvfp4) X(128, 64, kNvfp4) X(128, 128, kNvfp4) X(256, 64, kNvfp4)      \
+  X(256, 128, kNvfp4) X(256, 256, kNvfp4) X(512, 64, kNvfp4) X(512, 128, kNvfp4)   \
+  X(512, 256, kNvfp4) X(64, 64, kFp8) X(128, 64, kFp8) X(128, 128, kFp8)           \
+  X(256, 64, kFp8) X(256, 128, kFp8) X(256, 256, kFp8)
+
+bool prefill_supported(int dk, int dv, int fmt) {
+#define NVFP4_PREFILL_CASE(K, V, F) \
+  if (dk == K && dv == V && fmt == F) return true;
+  NVFP4_PREFILL_SHAPES(NVFP4_PREFILL_CASE)
+#undef NVFP4_PREFILL_CASE
+  return false;
 }
 
 int prefill_wgs_per_cu(int dk, int dv) { return dk <= 128 && dv <= 128 ? 2 : 1; }
@@ -802,42 +864,22 @@ int prefill_rows_per_item(int dk, int dv, int /*group*/, int page_size) {
   return 64 * (dk >= 512 ? 1 : 2);
 }
 
-size_t prefill_lds_bytes(int dk, int dv, int page_size) {
+size_t prefill_lds_bytes(int dk, int dv, int page_size, int fmt) {
   if (page_size < 16) return 0;  // the register kernel uses no LDS
-  // one CU holds WGS_PER_CU workgroups of the cooperative kernel; formula for every
-  // pair of head dims, including those the planner then rejects for it
-#define NVFP4_PREFILL_LDS(K, V) \
-  if (dk == K && dv == V) return (size_t)CoopShape<K, V>::LDS * CoopShape<K, V>::WGS_PER_CU;
-  NVFP4_PREFILL_LDS(64, 64)
-  NVFP4_PREFILL_LDS(128, 64)
-  NVFP4_PREFILL_LDS(128, 128)
-  NVFP4_PREFILL_LDS(256, 64)
-  NVFP4_PREFILL_LDS(256, 128)
-  NVFP4_PREFILL_LDS(256, 256)
-  NVFP4_PREFILL_LDS(512, 64)
-  NVFP4_PREFILL_LDS(512, 128)
-  NVFP4_PREFILL_LDS(512, 256)
-  NVFP4_PREFILL_LDS(512, 512)
-#undef NVFP4_PREFILL_LDS
-  return (size_t)-1;
+  // the resident workgroups of the cooperative kernel, also for shapes without one
+  return (size_t)coop_lds_formula(dk, dv, fmt) * coop_wgs_per_cu(dk, dv);
 }
 
-hipError_t launch_prefill(int dk, int dv, int page_shift, const AttnArgs& a, int /*rows*/,
+hipError_t launch_prefill(int dk, int dv, int fmt, int page_shift, const AttnArgs& a,
                           hipStream_t stream) {
   if (a.n_work <= 0) return hipSuccess;
-#define NVFP4_PREFILL_CASE(K, V) \
-  if (dk == K && dv == V) return launch_dk_dv<K, V>(page_shift, a, stream);
-  NVFP4_PREFILL_CASE(64, 64)
-  NVFP4_PREFILL_CASE(128, 64)
-  NVFP4_PREFILL_CASE(128, 128)
-  NVFP4_PREFILL_CASE(256, 64)
-  NVFP4_PREFILL_CASE(256, 128)
-  NVFP4_PREFILL_CASE(256, 256)
-  NVFP4_PREFILL_CASE(512, 64)
-  NVFP4_PREFILL_CASE(512, 128)
-  NVFP4_PREFILL_CASE(512, 256)
+#define NVFP4_PREFILL_CASE(K, V, F) \
+  if (dk == K && dv == V && fmt == F) return launch_dk_dv<K, V, F>(page_shift, a, stream);
+  NVFP4_PREFILL_SHAPES(NVFP4_PREFILL_CASE)
 #undef NVFP4_PREFILL_CASE
   return hipErrorInvalidValue;
 }
+
+#undef NVFP4_PREFILL_SHAPES
 
 }  // namespace nvfp4

@@ -1,5 +1,5 @@
-// NVFP4 quantisation of bf16 K/V rows into a paged pool (the per-block arithmetic
-// and its exactness argument are in fp4_quant.h).
+// Quantisation of bf16 K/V rows into a paged pool: NVFP4 (the per-block arithmetic
+// and its exactness argument are in fp4_quant.h) or FP8 e4m3 with a per-tensor scale.
 #include <algorithm>
 
 #include "fp4_quant.h"
@@ -32,13 +32,27 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs ka, QuantArgs v
     const uint4 u1 = src[1];
     if (slot < 0 || slot >= a.num_slots) continue;
     const uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-    uint32_t p0, p1, sc;
-    quant::block16(w, a.gscale, p0, p1, sc);
     const int64_t page = slot >> a.page_shift;
     const int64_t off = slot & (((int64_t)1 << a.page_shift) - 1);
-    uint2* dst = reinterpret_cast<uint2*>(a.data + page * a.d_page + head * a.d_head +
-                                          off * a.d_tok + blk * 8);
-    *dst = make_uint2(p0, p1);
+    uint8_t* row = a.data + page * a.d_page + head * a.d_head + off * a.d_tok;
+    if (a.fp8) {
+      // FP8: every element on its own, sign | RNE_e4m3(|x| / g) saturated (exact: see
+      // fp4_quant.h, the quotient of a bf16 value by a float cannot land on a midpoint
+      // it is not exactly on)
+      uint32_t c[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const uint32_t bits = (w[e >> 1] >> (16 * (e & 1))) & 0xFFFF;
+        const double ax = (double)fabsf(quant::bf16_to_float(bits));
+        const uint32_t code = quant::e4m3_code(ax / a.gscale) | ((bits >> 8) & 0x80);
+        c[e >> 2] |= code << (8 * (e & 3));
+      }
+      *reinterpret_cast<uint4*>(row + blk * 16) = make_uint4(c[0], c[1], c[2], c[3]);
+      continue;
+    }
+    uint32_t p0, p1, sc;
+    quant::block16(w, a.gscale, p0, p1, sc);
+    *reinterpret_cast<uint2*>(row + blk * 8) = make_uint2(p0, p1);
     a.sf[page * a.sf_page + head * a.sf_head + off * a.sf_tok + blk] = (uint8_t)sc;
   }
 }

@@ -35,10 +35,12 @@ def poison_pool(pool: KVPool, seed: int) -> None:
     g.manual_seed(seed)
     pool.data.copy_(torch.randint(0, 256, tuple(pool.data.shape), generator=g, dtype=torch.uint8,
                                   device=pool.data.device))
-    pool.sf.fill_(synth.SF_POISON)
+    if pool.sf is not None:
+        pool.sf.fill_(synth.SF_POISON)
 
 
-def padded_pool(w: synth.Workload, head_dim: int, layout: str, device, pad) -> KVPool:
+def padded_pool(w: synth.Workload, head_dim: int, layout: str, device, pad,
+                dtype: str = "nvfp4") -> KVPool:
     """A pool whose tensors are views into larger parents, so that its strides differ
     from a dense pool's: ``pad`` = extra (pages, heads, tokens, bytes per row) of the
     parent (the scale rows get 8 extra bytes when the data rows get any)."""
@@ -48,27 +50,31 @@ def padded_pool(w: synth.Workload, head_dim: int, layout: str, device, pad) -> K
         lead, view = (w.pool_pages + pp, H + ph, P + pt), (w.pool_pages, H, P)
     else:
         lead, view = (w.pool_pages + pp, P + pt, H + ph), (w.pool_pages, P, H)
-    data = torch.empty(lead + (head_dim // 2 + pb,), dtype=torch.uint8, device=device)
-    sf = torch.empty(lead + (head_dim // 16 + (8 if pb else 0),), dtype=torch.uint8, device=device)
+    row = head_dim if dtype == "fp8" else head_dim // 2
+    data = torch.empty(lead + (row + pb,), dtype=torch.uint8, device=device)
     idx = tuple(slice(0, n) for n in view)
-    return KVPool(data[idx + (slice(0, head_dim // 2),)], sf[idx + (slice(0, head_dim // 16),)],
-                  head_dim=head_dim, layout=layout)
+    sf = None
+    if dtype != "fp8":
+        sf = torch.empty(lead + (head_dim // 16 + (8 if pb else 0),), dtype=torch.uint8,
+                         device=device)[idx + (slice(0, head_dim // 16),)]
+    return KVPool(data[idx + (slice(0, row),)], sf, head_dim=head_dim, layout=layout, dtype=dtype)
 
 
 def build_case(w: synth.Workload, device="cuda", layout="HND", poison=True,
-               keep_sources=True, k_pad=None, v_pad=None) -> PagedCase:
-    """``k_pad`` / ``v_pad``: give that pool padded parents (see ``padded_pool``)."""
+               keep_sources=True, k_pad=None, v_pad=None, dtype: str = "nvfp4") -> PagedCase:
+    """``k_pad`` / ``v_pad``: give that pool padded parents (see ``padded_pool``);
+    ``dtype``: the pools' KV type ("nvfp4" or "fp8")."""
     q, k, v = synth.draw_qkv(w, device=device)
     if k_pad is None:
         k_pool = KVPool.empty(w.pool_pages, w.num_kv_heads, w.page_size, w.head_dim_qk, layout,
-                              device)
+                              device, dtype=dtype)
     else:
-        k_pool = padded_pool(w, w.head_dim_qk, layout, device, k_pad)
+        k_pool = padded_pool(w, w.head_dim_qk, layout, device, k_pad, dtype)
     if v_pad is None:
         v_pool = KVPool.empty(w.pool_pages, w.num_kv_heads, w.page_size, w.head_dim_vo, layout,
-                              device)
+                              device, dtype=dtype)
     else:
-        v_pool = padded_pool(w, w.head_dim_vo, layout, device, v_pad)
+        v_pool = padded_pool(w, w.head_dim_vo, layout, device, v_pad, dtype)
     if poison:
         poison_pool(k_pool, w.value_seed + 11)
         poison_pool(v_pool, w.value_seed + 12)
@@ -87,4 +93,4 @@ def make_plan(case: PagedCase, num_cus: int = 0, kv_chunk_tokens: Optional[int] 
     return Plan(w.kv_lens, num_qo_heads=w.num_qo_heads, num_kv_heads=w.num_kv_heads,
                 head_dim_qk=w.head_dim_qk, head_dim_vo=w.head_dim_vo, page_size=w.page_size,
                 qo_indptr=None if w.decode else case.qo_indptr.tolist(), causal=w.causal,
-                kv_chunk_tokens=chunk, num_cus=num_cus)
+                kv_chunk_tokens=chunk, num_cus=num_cus, kv_dtype=case.k_pool.dtype)

@@ -15,6 +15,10 @@
  * uint8, two e2m1 values per byte (element 2j in the low nibble of byte j,
  * element 2j+1 in the high nibble), with one FP8 e4m3fn scale byte per 16
  * consecutive head-dim elements.  dequantised value = e2m1 * e4m3 * global_scale.
+ * The other 1-byte KV type the same plan serves ([PF] commit "Gate split-KV off...":
+ * FP8 and 16-bit KV run the same prefill plan; dtype-aware-skip commit: the
+ * float8_e4m3fn KV cache) is FP8: one e4m3fn byte per element, no block scales,
+ * dequantised value = e4m3 * global_scale (NVFP4_KV_FP8_E4M3).
  *
  * Conventions shared by every entry point:
  *   - Pointers named "device" are device memory the caller owns (for example
@@ -57,6 +61,12 @@ typedef enum {
   NVFP4_E_HIP = 7          /* a HIP runtime call failed */
 } nvfp4_status;
 
+/* Storage type of a K or V pool. */
+typedef enum {
+  NVFP4_KV_NVFP4 = 0,    /* packed e2m1 pairs + one e4m3 scale byte per 16 elements */
+  NVFP4_KV_FP8_E4M3 = 1  /* one e4m3fn byte per element; no scale pool (sf must be NULL) */
+} nvfp4_kv_dtype;
+
 /* Text of the last error on the calling thread ("" if none).  Never NULL. */
 const char* nvfp4_last_error(void);
 
@@ -73,9 +83,10 @@ const char* nvfp4_version(void);
  * HND and NHD layouts are both expressed through these strides ([XQA] changelog:
  * scale tensors follow the data layout; container strides count bytes).
  * Alignment: data and every data stride must be multiples of 16 bytes when
- * head_dim >= 128, of head_dim/8 bytes otherwise; sf and every sf stride multiples
- * of min(head_dim/16, 8) bytes.  Strides are non-negative and below 2^31 bytes;
- * token strides (data and sf) below 2^27 bytes.
+ * head_dim >= 128 or the pool is FP8, of head_dim/8 bytes otherwise; sf and every sf
+ * stride multiples of min(head_dim/16, 8) bytes.  Strides are non-negative and below
+ * 2^31 bytes; token strides (data and sf) below 2^27 bytes.  An FP8 pool's rows hold
+ * head_dim bytes and it has no scale pool.
  */
 typedef struct {
   void* data;              /* device, packed e2m1 pairs (uint8) */
@@ -92,6 +103,7 @@ typedef struct {
   int32_t num_kv_heads;
   int32_t head_dim;        /* 64, 128, 256 or 512 */
   float global_scale;      /* > 0; multiplies every dequantised value */
+  int32_t kv_dtype;        /* nvfp4_kv_dtype; NVFP4 pools need sf, FP8 pools must not have it */
 } nvfp4_kv_pool;
 
 /*
@@ -106,8 +118,9 @@ typedef struct {
  *     past num_pages*page_size is skipped too.
  * Per 16-element block: s = RNE_e4m3(amax / (6*g)) saturated to 448; element code =
  * RNE_e2m1(|x| / (s*g)), ties to the even code, saturated to 6, sign bit copied
- * from x; s == 0 gives magnitude code 0.  Decisions are exact (no rounding of the
- * quotients affects them).  Inputs must be finite.
+ * from x; s == 0 gives magnitude code 0.  An FP8 pool gets, per element, the sign
+ * bit of x and RNE_e4m3(|x| / g) saturated to 448.  Decisions are exact (no rounding
+ * of the quotients affects them).  Inputs must be finite.
  */
 nvfp4_status nvfp4_quantize_kv(const void* k_src, int64_t k_stride_token, int64_t k_stride_head,
                                const void* v_src, int64_t v_stride_token, int64_t v_stride_head,
@@ -146,6 +159,31 @@ nvfp4_status nvfp4_plan_create(const int32_t* kv_lens, const int32_t* qo_indptr,
                                int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim_qk,
                                int32_t head_dim_vo, int32_t page_size, int32_t causal,
                                int32_t kv_chunk_tokens, int32_t num_cus, nvfp4_plan** out);
+
+/*
+ * Options of nvfp4_plan_create_ex ([PF] commit "Gate split-KV off...": one plan()
+ * serves the paged and the ragged prefill, over NVFP4 and the other KV types).
+ *   kv_dtype:  nvfp4_kv_dtype of the pools the runs read (their kv_dtype must match).
+ *              FP8 has kernels for head dims up to 256; the 512/256 FP8 prefill tile
+ *              is refused with NVFP4_E_LDS_BUDGET.
+ *   kv_indptr: NULL (paged KV), or host int32 [batch+1] for ragged (non-paged) prefill
+ *              KV: request b's keys are rows kv_indptr[b] .. kv_indptr[b+1]-1 of one
+ *              row array (nvfp4_kv_ragged); kv_indptr[b+1] - kv_indptr[b] must equal
+ *              kv_lens[b].  Needs qo_indptr; the page_size argument is then ignored
+ *              (the rows stream as 16-row pages), and runs use
+ *              nvfp4_batch_prefill_ragged.
+ */
+typedef struct {
+  int32_t kv_dtype;
+  const int32_t* kv_indptr;
+} nvfp4_plan_options;
+
+/* nvfp4_plan_create with options (NULL options = nvfp4_plan_create). */
+nvfp4_status nvfp4_plan_create_ex(const int32_t* kv_lens, const int32_t* qo_indptr,
+                                  int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
+                                  int32_t head_dim_qk, int32_t head_dim_vo, int32_t page_size,
+                                  int32_t causal, int32_t kv_chunk_tokens, int32_t num_cus,
+                                  const nvfp4_plan_options* options, nvfp4_plan** out);
 
 void nvfp4_plan_destroy(nvfp4_plan* plan);
 
@@ -301,6 +339,44 @@ nvfp4_status nvfp4_batch_prefill(const nvfp4_plan* plan, const void* q, int64_t 
                                  const nvfp4_kv_pool* v_pool, float sm_scale, void* workspace,
                                  size_t workspace_bytes, float* o, int64_t o_stride_tok,
                                  int64_t o_stride_head, float* lse, void* stream);
+
+/*
+ * Ragged (non-paged) K or V rows for nvfp4_batch_prefill_ragged: row r of kv head h
+ * starts at data + r*stride_row + h*stride_head (head_dim/2 bytes for NVFP4, head_dim
+ * for FP8); NVFP4 scale rows at sf + r*sf_stride_row + h*sf_stride_head.  Strides
+ * and alignment as for nvfp4_kv_pool's token and head strides.
+ *   num_rows: rows the arrays hold.  Every request's rows are read in 16-row pages,
+ *     so the arrays must hold rows up to kv_indptr[b] + 16*ceil(kv_len_b/16) for
+ *     every request b (at most 15 rows past the last request, read and never used);
+ *     NVFP4_E_SHAPE otherwise.
+ */
+typedef struct {
+  void* data;
+  int64_t stride_row;
+  int64_t stride_head;
+  void* sf;
+  int64_t sf_stride_row;
+  int64_t sf_stride_head;
+  int64_t num_rows;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  float global_scale;
+  int32_t kv_dtype;
+} nvfp4_kv_ragged;
+
+/*
+ * Prefill / extend over ragged K/V rows ([PF] commit "Gate split-KV off...": the
+ * ragged prefill plan beside the paged one).  plan: made with options.kv_indptr
+ * (NVFP4_E_SHAPE otherwise; a ragged plan is refused by nvfp4_batch_prefill).  The
+ * plan's uploaded workspace holds the rows' page table.  Other arguments, outputs and
+ * errors as for nvfp4_batch_prefill.
+ */
+nvfp4_status nvfp4_batch_prefill_ragged(const nvfp4_plan* plan, const void* q,
+                                        int64_t q_stride_tok, int64_t q_stride_head,
+                                        const nvfp4_kv_ragged* k, const nvfp4_kv_ragged* v,
+                                        float sm_scale, void* workspace, size_t workspace_bytes,
+                                        float* o, int64_t o_stride_tok, int64_t o_stride_head,
+                                        float* lse, void* stream);
 
 /*
  * Deferred merge ([XQA] changelog: the split-KV partial tiles are merged after the

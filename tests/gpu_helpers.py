@@ -34,35 +34,38 @@ class OracleCase:
     page_table: torch.Tensor
     k_global: float
     v_global: float
+    kv_dtype: str = "nvfp4"
 
 
 def _pool_arrays(w, layout, packed, sf, slots, head_dim, pad, seed):
     """numpy pool (data, sf) with random bytes / NaN scales everywhere, rows at their slots.
-    ``pad`` = (pages, heads, tokens, bytes) of extra parent padding -> unequal strides."""
+    ``pad`` = (pages, heads, tokens, bytes) of extra parent padding -> unequal strides.
+    ``sf`` None: an FP8 pool (rows of head_dim bytes, no scale pool)."""
     P, H = w.page_size, w.num_kv_heads
     rng = np.random.default_rng(seed)
     pp, ph, pt_, pb = pad
+    row = head_dim // 2 if sf is not None else head_dim
     if layout == "HND":
-        dshape = (w.pool_pages + pp, H + ph, P + pt_, head_dim // 2 + pb)
+        dshape = (w.pool_pages + pp, H + ph, P + pt_, row + pb)
         sshape = (w.pool_pages + pp, H + ph, P + pt_, head_dim // 16 + (8 if pb else 0))
     else:
-        dshape = (w.pool_pages + pp, P + pt_, H + ph, head_dim // 2 + pb)
+        dshape = (w.pool_pages + pp, P + pt_, H + ph, row + pb)
         sshape = (w.pool_pages + pp, P + pt_, H + ph, head_dim // 16 + (8 if pb else 0))
     dpar = rng.integers(0, 256, dshape, dtype=np.uint8)
-    spar = np.full(sshape, synth.SF_POISON, dtype=np.uint8)
-    if layout == "HND":
-        d = dpar[:w.pool_pages, :H, :P, :head_dim // 2]
-        s = spar[:w.pool_pages, :H, :P, :head_dim // 16]
-    else:
-        d = dpar[:w.pool_pages, :P, :H, :head_dim // 2]
-        s = spar[:w.pool_pages, :P, :H, :head_dim // 16]
+    spar = np.full(sshape, synth.SF_POISON, dtype=np.uint8) if sf is not None else None
+    lead = (slice(0, w.pool_pages), slice(0, H), slice(0, P)) if layout == "HND" else \
+        (slice(0, w.pool_pages), slice(0, P), slice(0, H))
+    d = dpar[lead + (slice(0, row),)]
+    s = spar[lead + (slice(0, head_dim // 16),)] if sf is not None else None
     pages, offs = slots // P, slots % P
     if layout == "HND":
         d[pages, :, offs, :] = packed
-        s[pages, :, offs, :] = sf
+        if s is not None:
+            s[pages, :, offs, :] = sf
     else:
         d[pages, offs, :, :] = packed
-        s[pages, offs, :, :] = sf
+        if s is not None:
+            s[pages, offs, :, :] = sf
     return dpar, spar, d, s
 
 
@@ -74,35 +77,42 @@ def _to_device_view(parent, view, device):
 
 def build_oracle_case(w: synth.Workload, layout="HND", device="cuda", k_global=1.0,
                       v_global=1.0, k_pad=(0, 0, 0, 0), v_pad=(0, 0, 0, 0),
-                      pad_page: Optional[int] = None) -> OracleCase:
+                      pad_page: Optional[int] = None, kv_dtype: str = "nvfp4") -> OracleCase:
     q, k, v = synth.draw_qkv(w, device="cpu")
-    kq, ks = ref.quantize(k.double().numpy(), k_global)
-    vq, vs = ref.quantize(v.double().numpy(), v_global)
+    if kv_dtype == "fp8":
+        kq, ks = ref.quantize_fp8(k.double().numpy(), k_global), None
+        vq, vs = ref.quantize_fp8(v.double().numpy(), v_global), None
+    else:
+        kq, ks = ref.quantize(k.double().numpy(), k_global)
+        vq, vs = ref.quantize(v.double().numpy(), v_global)
     pt = synth.page_table(w, pad_page)
     slots = synth.token_slots(w, pt)
     kd_par, ks_par, kd, ksf = _pool_arrays(w, layout, kq, ks, slots, w.head_dim_qk, k_pad, 1)
     vd_par, vs_par, vd, vsf = _pool_arrays(w, layout, vq, vs, slots, w.head_dim_vo, v_pad, 2)
-    k_pool = nv.KVPool(_to_device_view(kd_par, kd, device), _to_device_view(ks_par, ksf, device),
-                       head_dim=w.head_dim_qk, layout=layout, global_scale=k_global)
-    v_pool = nv.KVPool(_to_device_view(vd_par, vd, device), _to_device_view(vs_par, vsf, device),
-                       head_dim=w.head_dim_vo, layout=layout, global_scale=v_global)
+    dv = lambda par, view: None if par is None else _to_device_view(par, view, device)
+    k_pool = nv.KVPool(dv(kd_par, kd), dv(ks_par, ksf), head_dim=w.head_dim_qk, layout=layout,
+                       global_scale=k_global, dtype=kv_dtype)
+    v_pool = nv.KVPool(dv(vd_par, vd), dv(vs_par, vsf), head_dim=w.head_dim_vo, layout=layout,
+                       global_scale=v_global, dtype=kv_dtype)
     return OracleCase(w, layout, q.double().numpy(), (kd, ksf), (vd, vsf), pt, q.to(device),
-                      k_pool, v_pool, torch.from_numpy(pt).to(device), k_global, v_global)
+                      k_pool, v_pool, torch.from_numpy(pt).to(device), k_global, v_global,
+                      kv_dtype)
 
 
 def oracle_reference(c: OracleCase, rows=None):
     w = c.w
     return ref.paged_attention(c.q_np, c.k_np[0], c.k_np[1], c.v_np[0], c.v_np[1], c.pt,
                                w.kv_lens, synth.indptr(w.qo_lens), w.page_size, w.sm_scale,
-                               w.causal, c.layout, c.k_global, c.v_global, rows=rows)
+                               w.causal, c.layout, c.k_global, c.v_global, rows=rows,
+                               kv_dtype=c.kv_dtype)
 
 
-def make_plan(w: synth.Workload, chunk=None, num_cus=256):
+def make_plan(w: synth.Workload, chunk=None, num_cus=256, kv_dtype="nvfp4"):
     return nv.Plan(w.kv_lens, num_qo_heads=w.num_qo_heads, num_kv_heads=w.num_kv_heads,
                    head_dim_qk=w.head_dim_qk, head_dim_vo=w.head_dim_vo, page_size=w.page_size,
                    qo_indptr=None if w.decode else synth.indptr(w.qo_lens).tolist(),
                    causal=w.causal, kv_chunk_tokens=w.kv_chunk_tokens if chunk is None else chunk,
-                   num_cus=num_cus)
+                   num_cus=num_cus, kv_dtype=kv_dtype)
 
 
 def run_gpu(c: OracleCase, plan: nv.Plan):

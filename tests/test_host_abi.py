@@ -311,3 +311,100 @@ def test_noalloc_decode_rejects_plans_beyond_its_scratch():
     assert _lib.STATUS[st] == "NVFP4_E_WORKSPACE"
     msg = nv.lib.nvfp4_last_error().decode()
     assert "allocation-free" in msg and str(32 << 20) in msg
+
+
+def _plan_ex_status(kv_dtype=0, kv_indptr=None, **kw):
+    args = dict(kv_lens=[64], qo_indptr=[0, 8], num_qo_heads=8, num_kv_heads=1, head_dim_qk=128,
+                head_dim_vo=128, num_cus=256, kv_dtype=["nvfp4", "fp8"][kv_dtype],
+                kv_indptr=kv_indptr)
+    args.update(kw)
+    try:
+        nv.Plan(**args)
+    except nv.NVFP4Error as e:
+        return e.status, str(e)
+    return "NVFP4_OK", ""
+
+
+def test_fp8_plans_price_the_tile_in_lds():
+    """FP8 rows are twice as long: the 512/256 FP8 prefill tile (and the decode ring)
+    needs more LDS than a CU has and is refused by the computed budget; FP8 kernels
+    exist for head dims up to 256."""
+    st, msg = _plan_ex_status(1, head_dim_qk=512, head_dim_vo=256)
+    assert st == "NVFP4_E_LDS_BUDGET" and "LDS" in msg, msg
+    st, msg = _plan_ex_status(1, qo_indptr=None, head_dim_qk=512, head_dim_vo=256)
+    assert st == "NVFP4_E_LDS_BUDGET", msg
+    st, msg = _plan_ex_status(1, qo_indptr=None, head_dim_qk=512, head_dim_vo=128)
+    assert st == "NVFP4_E_UNSUPPORTED" and "FP8" in msg, msg
+    for dk, dv in ((64, 64), (128, 64), (128, 128), (256, 64), (256, 128), (256, 256)):
+        for ind in (None, [0, 8]):
+            for ps in (1, 16):
+                st, msg = _plan_ex_status(1, qo_indptr=ind, head_dim_qk=dk, head_dim_vo=dv,
+                                          page_size=ps)
+                assert st == "NVFP4_OK", (dk, dv, ind, ps, msg)
+
+
+def test_fp8_pool_rules_and_dtype_mismatch():
+    plan8 = nv.Plan([100], num_qo_heads=4, num_kv_heads=1, head_dim_qk=128, num_cus=256,
+                    kv_dtype="fp8")
+    plan4 = nv.Plan([100], num_qo_heads=4, num_kv_heads=1, head_dim_qk=128, num_cus=256)
+    fp8 = _fake_pool()
+    fp8.kv_dtype = 1
+    fp8.stride_page, fp8.stride_token = 16 * 128, 128
+    st, msg = _decode(plan8, k=fp8, v=fp8)       # a stray scale pointer on an FP8 pool
+    assert st == "NVFP4_E_INVALID" and "FP8 pool" in msg, msg
+    fp8.sf = None
+    st, msg = _decode(plan4, k=fp8, v=fp8)       # an FP8 pool under an NVFP4 plan
+    assert st == "NVFP4_E_SHAPE" and "kv_dtype" in msg, msg
+    st, msg = _decode(plan8, k=_fake_pool(), v=_fake_pool())   # NVFP4 pools, FP8 plan
+    assert st == "NVFP4_E_SHAPE", msg
+    # the in-launch append writes NVFP4 only
+    st = nv.lib.nvfp4_batch_decode_append(plan8.handle, ctypes.c_void_p(0x10000), 512, 128,
+                                          ctypes.c_void_p(0x10000), 128, 128,
+                                          ctypes.c_void_p(0x10000), 128, 128,
+                                          ctypes.c_void_p(0x20000), 8, ctypes.byref(fp8),
+                                          ctypes.byref(fp8), 0.1, ctypes.c_void_p(0x40000),
+                                          plan8.workspace_bytes, ctypes.c_void_p(0x80000), 512,
+                                          128, ctypes.c_void_p(0x90000), None)
+    assert _lib.STATUS[st] == "NVFP4_E_UNSUPPORTED" and "FP8" in nv.lib.nvfp4_last_error().decode()
+
+
+def test_ragged_plan_rules():
+    st, msg = _plan_ex_status(kv_indptr=[0, 64], qo_indptr=None)
+    assert st == "NVFP4_E_SHAPE" and "qo_indptr" in msg
+    st, msg = _plan_ex_status(kv_indptr=[3, 60])          # 57 rows, kv_lens says 64
+    assert st == "NVFP4_E_SHAPE" and "kv_indptr" in msg
+    assert _plan_ex_status(kv_indptr=[5, 69])[0] == "NVFP4_OK"
+    import torch
+    ragged = nv.Plan([64, 20], qo_indptr=[0, 8, 28], kv_indptr=[5, 69, 89], num_qo_heads=8,
+                     num_kv_heads=1, head_dim_qk=128, num_cus=256)
+    paged = nv.Plan([64, 20], qo_indptr=[0, 8, 28], num_qo_heads=8, num_kv_heads=1,
+                    head_dim_qk=128, num_cus=256)
+    # a ragged plan through the paged entry point and the reverse, before any launch
+    st = nv.lib.nvfp4_batch_prefill(ragged.handle, ctypes.c_void_p(0x10000), 1024, 128,
+                                    ctypes.c_void_p(0x20000), 8, ctypes.byref(_fake_pool()),
+                                    ctypes.byref(_fake_pool()), 0.1, ctypes.c_void_p(0x40000),
+                                    ragged.workspace_bytes, ctypes.c_void_p(0x80000), 1024, 128,
+                                    ctypes.c_void_p(0x90000), None)
+    assert _lib.STATUS[st] == "NVFP4_E_SHAPE" and "ragged" in nv.lib.nvfp4_last_error().decode()
+
+    def rows(n, dtype=0):
+        return _lib.KVRaggedStruct(0x100000, 64, 64, 0x200000, 8, 8, n, 1, 128, 1.0, dtype)
+    call = lambda plan, k, v: nv.lib.nvfp4_batch_prefill_ragged(
+        plan.handle, ctypes.c_void_p(0x10000), 1024, 128, ctypes.byref(k), ctypes.byref(v), 0.1,
+        ctypes.c_void_p(0x40000), plan.workspace_bytes, ctypes.c_void_p(0x80000), 1024, 128,
+        ctypes.c_void_p(0x90000), None)
+    st = call(paged, rows(200), rows(200))
+    assert _lib.STATUS[st] == "NVFP4_E_SHAPE" and "paged" in nv.lib.nvfp4_last_error().decode()
+    # request 1 ends at row 89; its 16-row pages read rows up to 69 + 32 = 101
+    st = call(ragged, rows(100), rows(200))
+    assert _lib.STATUS[st] == "NVFP4_E_SHAPE" and "101" in nv.lib.nvfp4_last_error().decode()
+    st = call(ragged, rows(101), rows(101, dtype=1))      # V says FP8, the plan NVFP4
+    assert _lib.STATUS[st] in ("NVFP4_E_SHAPE", "NVFP4_E_INVALID")
+    # the binding refuses host tensors and a paged plan
+    k = nv.RaggedKV.empty(89, 1, 128, device="cpu")
+    q = torch.zeros((28, 8, 128), dtype=torch.bfloat16)
+    ws = torch.zeros(ragged.workspace_bytes, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        nv.batch_prefill_ragged(ragged, q, k, k, 0.1, ws)
+    with pytest.raises(ValueError, match="paged"):
+        nv.batch_prefill_ragged(paged, q, k, k, 0.1, ws)
