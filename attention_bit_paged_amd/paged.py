@@ -13,7 +13,7 @@ from typing import Optional
 import numpy as np
 import torch
 
-from . import KVPool, Plan, quantize_kv, synth
+from . import KVPool, Plan, RaggedKV, quantize_kv, synth
 
 
 @dataclasses.dataclass
@@ -94,3 +94,47 @@ def make_plan(case: PagedCase, num_cus: int = 0, kv_chunk_tokens: Optional[int] 
                 head_dim_qk=w.head_dim_qk, head_dim_vo=w.head_dim_vo, page_size=w.page_size,
                 qo_indptr=None if w.decode else case.qo_indptr.tolist(), causal=w.causal,
                 kv_chunk_tokens=chunk, num_cus=num_cus, kv_dtype=case.k_pool.dtype)
+
+
+@dataclasses.dataclass
+class RaggedCase:
+    w: synth.Workload
+    q: torch.Tensor
+    k: RaggedKV
+    v: RaggedKV
+    kv_indptr: np.ndarray
+    qo_indptr: np.ndarray
+
+
+def build_ragged_case(w: synth.Workload, device="cuda", dtype: str = "nvfp4",
+                      start: int = 0) -> RaggedCase:
+    """The workload's K/V as ragged rows (requests back to back from row ``start``),
+    quantised by ``quantize_kv`` through a one-row-per-page view of the same tensors;
+    the rows around them hold random bytes (and NaN scales)."""
+    q, k, v = synth.draw_qkv(w, device=device)
+    rows = []
+    for x, d, seed in ((k, w.head_dim_qk, 21), (v, w.head_dim_vo, 22)):
+        r = RaggedKV.empty(start + w.total_kv, w.num_kv_heads, d, device=device, dtype=dtype)
+        g = torch.Generator(device=r.data.device)
+        g.manual_seed(w.value_seed + seed)
+        r.data.copy_(torch.randint(0, 256, tuple(r.data.shape), generator=g, dtype=torch.uint8,
+                                   device=r.data.device))
+        if r.sf is not None:
+            r.sf.fill_(synth.SF_POISON)
+        rows.append(r)
+    views = [KVPool(r.data.unsqueeze(2), None if r.sf is None else r.sf.unsqueeze(2),
+                    head_dim=r.head_dim, layout="HND", dtype=dtype) for r in rows]
+    slots = torch.arange(start, start + w.total_kv, dtype=torch.int64, device=q.device)
+    quantize_kv(k, v, slots, views[0], views[1])
+    kv_ind = synth.indptr(w.kv_lens) + start
+    return RaggedCase(w, q, rows[0], rows[1], kv_ind, synth.indptr(w.qo_lens))
+
+
+def make_ragged_plan(case: RaggedCase, num_cus: int = 0,
+                     kv_chunk_tokens: Optional[int] = None) -> Plan:
+    w = case.w
+    chunk = w.kv_chunk_tokens if kv_chunk_tokens is None else kv_chunk_tokens
+    return Plan(w.kv_lens, num_qo_heads=w.num_qo_heads, num_kv_heads=w.num_kv_heads,
+                head_dim_qk=w.head_dim_qk, head_dim_vo=w.head_dim_vo,
+                qo_indptr=case.qo_indptr.tolist(), kv_indptr=case.kv_indptr.tolist(),
+                causal=w.causal, kv_chunk_tokens=chunk, num_cus=num_cus, kv_dtype=case.k.dtype)

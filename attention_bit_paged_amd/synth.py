@@ -65,10 +65,14 @@ class Workload:
     def pages_needed(self) -> int:
         return int(sum(-(-l // self.page_size) for l in self.kv_lens))
 
-    def kv_bytes(self) -> int:
-        """Packed e2m1 bytes plus e4m3 scale bytes of every visible K and V row."""
-        per_tok = (self.head_dim_qk // 2 + self.head_dim_qk // 16
-                   + self.head_dim_vo // 2 + self.head_dim_vo // 16)
+    def kv_bytes(self, dtype: str = "nvfp4") -> int:
+        """Bytes of every visible K and V row: packed e2m1 bytes plus e4m3 scale bytes
+        (NVFP4), or one byte per element (FP8)."""
+        if dtype == "fp8":
+            per_tok = self.head_dim_qk + self.head_dim_vo
+        else:
+            per_tok = (self.head_dim_qk // 2 + self.head_dim_qk // 16
+                       + self.head_dim_vo // 2 + self.head_dim_vo // 16)
         return self.total_kv * self.num_kv_heads * per_tok
 
     def unmasked_pairs(self) -> int:

@@ -385,6 +385,65 @@ def variant_lines(torch, nv, paged, synth, name, iters=60, warm=12, pool_sets=3)
     return {"workload": name, "lines": lines}
 
 
+def kv_type_lines(torch, nv, paged, synth, iters=60, warm=12, pool_sets=3):
+    """The FP8 e4m3 cache beside NVFP4 (batch decode, prefill extend), and the prefill
+    extend over ragged (non-paged) rows of either type; kernel figures as in the main
+    lines (decode: the type's own KV bytes + Q + O + LSE; prefill: visible-pair flops),
+    each with its ratio to the NVFP4 paged figure measured the same way."""
+    out = []
+    for name in ("batch_decode", "prefill_extend"):
+        w = synth.workload(name)
+        ref_rate = None
+        for dtype, layout in (("nvfp4", "paged"), ("fp8", "paged"), ("nvfp4", "ragged"),
+                              ("fp8", "ragged")):
+            if layout == "ragged" and w.decode:
+                continue
+            if layout == "paged":
+                cases = [paged.build_case(w, keep_sources=False, dtype=dtype)
+                         for _ in range(pool_sets)]
+                plan = paged.make_plan(cases[0])
+            else:
+                cases = [paged.build_ragged_case(w, dtype=dtype) for _ in range(pool_sets)]
+                plan = paged.make_ragged_plan(cases[0])
+            plan.set_deferred_merge(True)
+            ws = plan.new_workspace()
+            plan.upload(ws)
+            o = torch.empty((w.total_q, w.num_qo_heads, w.head_dim_vo), device="cuda")
+            lse = torch.empty((w.total_q, w.num_qo_heads), device="cuda")
+            if layout == "ragged":
+                run = [nv.batch_prefill_ragged(plan, c.q, c.k, c.v, w.sm_scale, ws, out=o, lse=lse,
+                                               prepare=True) for c in cases]
+            else:
+                fn = nv.batch_decode if w.decode else nv.batch_prefill
+                run = [fn(plan, c.q, c.page_table, c.k_pool, c.v_pool, w.sm_scale, ws, out=o,
+                          lse=lse, prepare=True) for c in cases]
+            merge = nv.merge_partials(plan, ws, o, lse, prepare=True)
+            for i in range(warm):
+                run[i % len(run)]()
+                merge()
+            run_ms, merge_ms = timed_passes(torch, nv, run, merge, iters)
+            if w.decode:
+                q = w.batch * w.num_qo_heads * w.head_dim_qk * 2
+                o_b = w.batch * w.num_qo_heads * (w.head_dim_vo * 4 + 4)
+                rate = (w.kv_bytes(dtype) + q + o_b) / run_ms / 1e6
+                line = {"workload": name, "kv_dtype": dtype, "layout": layout,
+                        "kernel_GBs": round(rate, 1),
+                        "kernel_frac_hbm": round(rate / HBM_PEAK_GBS, 4),
+                        "kv_bytes": w.kv_bytes(dtype)}
+            else:
+                rate = w.flops() / run_ms / 1e9
+                line = {"workload": name, "kv_dtype": dtype, "layout": layout,
+                        "kernel_TFLOPs": round(rate, 2),
+                        "kernel_frac_mfma_f16": round(rate / MFMA_F16_PEAK_TFLOPS, 4)}
+            ref_rate = rate if ref_rate is None else ref_rate
+            line.update(attn_ms=round(run_ms, 4), merge_ms=round(merge_ms, 4),
+                        vs_nvfp4_paged=round(rate / ref_rate, 4))
+            out.append(line)
+            del run, merge, cases, ws
+            torch.cuda.empty_cache()
+    return out
+
+
 def stream_ceiling(torch, nv, plan, cases, ws, iters, kv_bytes, attn_ms):
     """What the decode access pattern sustains without the attention arithmetic: the
     checksum kernel (nvfp4_kv_checksum) streams the same plan's KV bytes through the same
@@ -842,6 +901,7 @@ def main():
         out["other_workloads"] = extras
         out["layout_variants"] = [variant_lines(torch, nv, paged, synth, n)
                                   for n in ("batch_decode", "prefill_extend")]
+        out["kv_types"] = kv_type_lines(torch, nv, paged, synth)
     print(json.dumps(out), flush=True)
 
 

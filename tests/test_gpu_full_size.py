@@ -45,8 +45,10 @@ def _oracle_pairs(case, o, lse, samples, record, causal=False):
     """Compare O/LSE of the sampled (request, kv head) pairs with the oracle; returns
     the largest O error over them."""
     w = case.w
-    kd, ks = case.k_pool.data.cpu().numpy(), case.k_pool.sf.cpu().numpy()
-    vd, vs = case.v_pool.data.cpu().numpy(), case.v_pool.sf.cpu().numpy()
+    host = lambda t: None if t is None else t.cpu().numpy()
+    kd, ks = host(case.k_pool.data), host(case.k_pool.sf)
+    vd, vs = host(case.v_pool.data), host(case.v_pool.sf)
+    head = lambda a, h: None if a is None else a[:, h:h + 1]
     q = case.q.float().cpu().double().numpy()
     g = w.group
     ind = synth.indptr(w.qo_lens)
@@ -55,9 +57,9 @@ def _oracle_pairs(case, o, lse, samples, record, causal=False):
         q0, q1 = int(ind[b]), int(ind[b + 1])
         qs = q[:, g * h:g * (h + 1)]
         o_ref, lse_ref = ref.paged_attention(
-            qs, kd[:, h:h + 1], ks[:, h:h + 1], vd[:, h:h + 1], vs[:, h:h + 1],
+            qs, head(kd, h), head(ks, h), head(vd, h), head(vs, h),
             case.page_table_np, w.kv_lens, ind, w.page_size, w.sm_scale, causal, "HND",
-            rows=[b])
+            rows=[b], kv_dtype=case.k_pool.dtype)
         og, lg = o[q0:q1, g * h:g * (h + 1)], lse[q0:q1, g * h:g * (h + 1)]
         err = gh.assert_attention_close(og, lg, o_ref[q0:q1], lse_ref[q0:q1],
                                         f"{w.name} b={b} h={h}")
@@ -73,9 +75,9 @@ def _oracle_pairs(case, o, lse, samples, record, causal=False):
     return worst
 
 
-def _decode(name, fused):
+def _decode(name, fused, dtype="nvfp4"):
     w = synth.workload(name)
-    case = paged.build_case(w, keep_sources=False)
+    case = paged.build_case(w, keep_sources=False, dtype=dtype)
     plan = paged.make_plan(case)
     ws = plan.new_workspace()
     plan.upload(ws)
@@ -95,9 +97,9 @@ def _decode(name, fused):
     return case, o.cpu().double().numpy(), lse.cpu().double().numpy()
 
 
-def _prefill(name):
+def _prefill(name, dtype="nvfp4"):
     w = synth.workload(name)
-    case = paged.build_case(w, keep_sources=False)
+    case = paged.build_case(w, keep_sources=False, dtype=dtype)
     plan = paged.make_plan(case)
     ws = plan.new_workspace()
     plan.upload(ws)
@@ -148,3 +150,19 @@ def test_asym_prefill_full_size(record_property):
     case, o, lse = _prefill("asym_prefill")
     assert not np.isnan(o).any() and not np.isnan(lse).any()
     _oracle_pairs(case, o, lse, sample_pairs(case.w, 55, frac=1.0), record_property, causal=True)
+
+
+@pytest.mark.timeout(600)
+def test_batch_decode_full_size_fp8(record_property):
+    """The batch decode workload over an FP8 cache (quantised on the GPU by the FP8
+    append kernel, whose bytes are pinned to the oracle by the bit-exact test)."""
+    case, o, lse = _decode("batch_decode", fused=False, dtype="fp8")
+    assert not np.isnan(o).any() and not np.isnan(lse).any()
+    _oracle_pairs(case, o, lse, sample_pairs(case.w, 57), record_property)
+
+
+@pytest.mark.timeout(600)
+def test_prefill_extend_full_size_fp8(record_property):
+    case, o, lse = _prefill("prefill_extend", dtype="fp8")
+    assert not np.isnan(o).any() and not np.isnan(lse).any()
+    _oracle_pairs(case, o, lse, sample_pairs(case.w, 58), record_property, causal=True)
