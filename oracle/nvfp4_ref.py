@@ -35,6 +35,10 @@ out the bit layouts, nibble order or rounding.  The readings taken here:
     element, code = sign | RNE_e4m3(|x| / g) saturating at 448, value = e4m3 * g.
   * Ragged (non-paged) KV: request b's rows are rows kv_indptr[b] .. kv_indptr[b+1]-1
     of one [rows, H, W] array.
+  * Packed custom masks: request b's mask is a [q_b, L_b] boolean array, row-major,
+    1 = visible; each request's bits are packed on their own (little-endian bits within
+    a byte, padded to a whole byte), so its bits start at byte sum of ceil(q_b' L_b' / 8)
+    over the requests before it; a custom mask replaces the causal rule.
 """
 from __future__ import annotations
 
@@ -212,11 +216,12 @@ def gather_pages(pool, page_table_row, kv_len, page_size, layout="HND"):
 # decode and prefix-cache extend, qo_len << kv_len)
 # ---------------------------------------------------------------------------
 
-def attention(q, k, v, sm_scale, causal=False):
+def attention(q, k, v, sm_scale, causal=False, mask=None):
     """Exact softmax attention of one request.
 
     q [n, Hq, Dk], k [L, Hkv, Dk], v [L, Hkv, Dv] (float64, already dequantised).
-    Query row i sees keys j < L, and with ``causal`` only j <= i + (L - n).
+    Query row i sees keys j < L, and with ``causal`` only j <= i + (L - n); a boolean
+    ``mask`` [n, L] (True = visible) replaces both rules.
     Returns O [n, Hq, Dv] and LSE [n, Hq] (natural log).
     """
     q = np.asarray(q, dtype=np.float64)
@@ -233,6 +238,8 @@ def attention(q, k, v, sm_scale, causal=False):
     visible = np.ones((n, L), dtype=bool)
     if causal:
         visible = np.arange(L)[None, :] <= (np.arange(n)[:, None] + (L - n))
+    if mask is not None:
+        visible = np.asarray(mask, dtype=bool).reshape(n, L)
     for h in range(hq):
         g = h // group
         s = sm_scale * (q[:, h, :] @ k[:, g, :].T)          # [n, L]
@@ -250,19 +257,53 @@ def attention(q, k, v, sm_scale, causal=False):
     return o, lse
 
 
+def mask_segments(qo_lens, kv_lens):
+    """Byte offset of each request's packed mask bits, and the total bytes."""
+    sizes = [-(-int(q) * int(l) // 8) for q, l in zip(qo_lens, kv_lens)]
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    return off[:-1], int(off[-1])
+
+
+def unpack_mask_segment(packed, byte_offset, q, L):
+    """Request mask [q, L] from its packed bits: element e = i*L + j is bit e % 8 of
+    byte byte_offset + e // 8."""
+    e = np.arange(q * L, dtype=np.int64)
+    byte = np.asarray(packed, dtype=np.uint8)[byte_offset + e // 8]
+    return ((byte >> (e % 8).astype(np.uint8)) & 1).astype(bool).reshape(q, L)
+
+
+def pack_masks(masks):
+    """Boolean masks [q_b, L_b] of the requests -> packed bytes (each request's bits on
+    their own, little-endian within a byte, padded to a byte)."""
+    out = []
+    for m in masks:
+        bits = np.asarray(m, dtype=bool).ravel()
+        nbytes = -(-bits.size // 8)
+        buf = np.zeros(nbytes, dtype=np.uint8)
+        for e in np.flatnonzero(bits):
+            buf[e // 8] |= np.uint8(1 << (e % 8))
+        out.append(buf)
+    return np.concatenate(out) if out else np.zeros(0, dtype=np.uint8)
+
+
 def paged_attention(q, k_pool, k_sf, v_pool, v_sf, page_table, kv_lens, qo_indptr,
                     page_size, sm_scale, causal=False, layout="HND",
-                    k_global=1.0, v_global=1.0, rows=None, kv_dtype="nvfp4"):
+                    k_global=1.0, v_global=1.0, rows=None, kv_dtype="nvfp4",
+                    custom_mask=None):
     """Batched attention over paged K/V (decode when every q_b is 1).
 
     q [sum q_b, Hq, Dk]; pools as in ``gather_pages`` with W = D/2 (NVFP4 data),
     D/16 (NVFP4 scales) or D (FP8 data; scales None).  ``rows`` optionally restricts
-    the computation to a subset of requests (the other outputs stay NaN).  Returns
-    O [sum q_b, Hq, Dv] and LSE [sum q_b, Hq].
+    the computation to a subset of requests (the other outputs stay NaN).
+    ``custom_mask``: packed mask bytes of all requests (see ``mask_segments``), which
+    then decide visibility in place of ``causal``.  Returns O [sum q_b, Hq, Dv] and
+    LSE [sum q_b, Hq].
     """
     q = np.asarray(q, dtype=np.float64)
     nq, hq, _ = q.shape
     dv = np.asarray(v_pool).shape[-1] * (2 if kv_dtype == "nvfp4" else 1)
+    qo_lens = [int(qo_indptr[b + 1]) - int(qo_indptr[b]) for b in range(len(kv_lens))]
+    seg = mask_segments(qo_lens, kv_lens)[0] if custom_mask is not None else None
     o = np.full((nq, hq, dv), np.nan)
     lse = np.full((nq, hq), np.nan)
     batch = len(kv_lens)
@@ -275,7 +316,8 @@ def paged_attention(q, k_pool, k_sf, v_pool, v_sf, page_table, kv_lens, qo_indpt
         q0, q1 = int(qo_indptr[b]), int(qo_indptr[b + 1])
         k = dequantize_kv(rows_of(k_pool, b, L), rows_of(k_sf, b, L), k_global, kv_dtype)
         v = dequantize_kv(rows_of(v_pool, b, L), rows_of(v_sf, b, L), v_global, kv_dtype)
-        o[q0:q1], lse[q0:q1] = attention(q[q0:q1], k, v, sm_scale, causal)
+        m = None if seg is None else unpack_mask_segment(custom_mask, seg[b], q1 - q0, L)
+        o[q0:q1], lse[q0:q1] = attention(q[q0:q1], k, v, sm_scale, causal, m)
     return o, lse
 
 
