@@ -18,7 +18,7 @@ from ._lib import (EXPORTS, KV_DTYPES, STATUS, WORK_FIELDS, KVPoolStruct, KVRagg
                    NVFP4Error, PlanInfoStruct, PlanOptionsStruct, check, lib)
 
 __all__ = ["KVPool", "RaggedKV", "Plan", "Prepared", "quantize_kv", "batch_decode",
-           "batch_decode_noalloc", "batch_decode_append", "batch_prefill",
+           "batch_decode_noalloc", "batch_decode_append", "batch_prefill", "batch_prefill_masked",
            "batch_prefill_ragged", "kv_checksum",
            "merge_partials", "merge_states", "NVFP4Error", "lib", "version", "EXPORTS"]
 
@@ -249,11 +249,13 @@ class Plan:
                  head_dim_qk: int, head_dim_vo: Optional[int] = None, page_size: int = 16,
                  qo_indptr: Optional[Sequence[int]] = None, causal: bool = False,
                  kv_chunk_tokens: int = 0, num_cus: int = 0, device=None,
-                 kv_dtype: str = "nvfp4", kv_indptr: Optional[Sequence[int]] = None):
+                 kv_dtype: str = "nvfp4", kv_indptr: Optional[Sequence[int]] = None,
+                 custom_mask: bool = False):
         """``num_cus`` 0 fills the compute units of ``device`` (default: the current
         device when a GPU is present, else the library's default of 256).  ``kv_dtype``:
         the pools' type ("nvfp4" or "fp8"); ``kv_indptr``: ragged (non-paged) prefill KV
-        rows per request (nvfp4_plan_create_ex)."""
+        rows per request; ``custom_mask``: runs take a packed mask in place of the causal
+        rule (nvfp4_plan_create_ex)."""
         head_dim_vo = head_dim_qk if head_dim_vo is None else head_dim_vo
         if kv_dtype not in KV_DTYPES:
             raise ValueError(f"kv_dtype must be one of {sorted(KV_DTYPES)}, got {kv_dtype!r}")
@@ -261,6 +263,7 @@ class Plan:
         self._kvind = None if kv_indptr is None else np.ascontiguousarray(
             np.asarray(kv_indptr, dtype=np.int32))
         self.ragged = kv_indptr is not None
+        self.custom_mask = bool(custom_mask)
         if num_cus == 0 and torch.cuda.is_available():
             num_cus = torch.cuda.get_device_properties(
                 torch.device("cuda") if device is None else torch.device(device)
@@ -277,7 +280,8 @@ class Plan:
         self.head_dim_qk, self.head_dim_vo, self.page_size = head_dim_qk, head_dim_vo, page_size
         self.causal = causal
         opts = PlanOptionsStruct(KV_DTYPES[kv_dtype], None if self._kvind is None
-                                 else self._kvind.ctypes.data_as(ctypes.c_void_p).value)
+                                 else self._kvind.ctypes.data_as(ctypes.c_void_p).value,
+                                 int(self.custom_mask))
         check(lib.nvfp4_plan_create_ex(
             self._kv.ctypes.data_as(ctypes.c_void_p) if self.batch else None,
             self._ind.ctypes.data_as(ctypes.c_void_p) if self._ind is not None else None,
@@ -320,6 +324,12 @@ class Plan:
         _check_workspace(self, workspace)
         check(lib.nvfp4_plan_upload(self._h, _ptr(workspace), workspace.numel(),
                                     _stream(stream, _device(workspace))))
+
+    @property
+    def mask_bytes(self) -> int:
+        """Bytes of the packed custom mask of this plan's requests (without the 8 bytes
+        of read-ahead the buffer must also hold)."""
+        return int(lib.nvfp4_plan_mask_bytes(self._h))
 
     @property
     def total_rows(self) -> int:
@@ -387,6 +397,8 @@ def _check_pools(plan: Plan, k_pool: "KVPool", v_pool: "KVPool"):
 
 def _attn(fn, plan: Plan, q, page_table, k_pool, v_pool, sm_scale, workspace, out, lse, stream,
           prepare=False):
+    if plan.custom_mask:
+        raise ValueError("the plan was made for a custom mask: use batch_prefill_masked")
     rows = _check_rows(plan, q, page_table, out, lse)
     _check_pools(plan, k_pool, v_pool)
     _check_workspace(plan, workspace)
@@ -509,6 +521,40 @@ def batch_prefill(plan: Plan, q: torch.Tensor, page_table: torch.Tensor, k_pool:
     or a ``Prepared`` call with ``prepare=True``."""
     return _attn(lib.nvfp4_batch_prefill, plan, q, page_table, k_pool, v_pool, sm_scale,
                  workspace, out, lse, stream, prepare)
+
+
+def batch_prefill_masked(plan: Plan, q: torch.Tensor, page_table: torch.Tensor, k_pool: KVPool,
+                         v_pool: KVPool, mask: torch.Tensor, sm_scale: float,
+                         workspace: torch.Tensor, out: Optional[torch.Tensor] = None,
+                         lse: Optional[torch.Tensor] = None, stream=None, prepare: bool = False):
+    """Prefill over the paged cache with a packed custom mask (nvfp4_batch_prefill_masked):
+    ``mask`` uint8, the requests' bits one segment after the other, little-endian, each
+    segment padded to a byte, and 8 more readable bytes at the end."""
+    if not plan.custom_mask:
+        raise ValueError("the plan was made without custom_mask")
+    if mask.dtype != torch.uint8 or mask.dim() != 1 or not mask.is_contiguous() \
+            or mask.numel() < plan.mask_bytes + 8:
+        raise ValueError(f"mask must be a contiguous uint8 vector of at least "
+                         f"{plan.mask_bytes} + 8 bytes")
+    rows = _check_rows(plan, q, page_table, out, lse)
+    _check_pools(plan, k_pool, v_pool)
+    _check_workspace(plan, workspace)
+    dev = _device(q, page_table, *k_pool.tensors(), *v_pool.tensors(), mask, workspace, out, lse)
+    if out is None:
+        out = torch.empty((rows, plan.num_qo_heads, plan.head_dim_vo), dtype=torch.float32,
+                          device=dev)
+    if lse is None:
+        lse = torch.empty((rows, plan.num_qo_heads), dtype=torch.float32, device=dev)
+    ks, vs = k_pool.struct(), v_pool.struct()
+    args = (plan.handle, _ptr(q), q.stride(0), q.stride(1), _ptr(page_table), page_table.stride(0),
+            ctypes.byref(ks), ctypes.byref(vs), _ptr(mask), float(sm_scale), _ptr(workspace),
+            workspace.numel(), _ptr(out), out.stride(0), out.stride(1), _ptr(lse),
+            _stream(stream, dev))
+    if prepare:
+        return Prepared(lib.nvfp4_batch_prefill_masked, args,
+                        (plan, q, page_table, k_pool, v_pool, ks, vs, mask, workspace, out, lse))
+    check(lib.nvfp4_batch_prefill_masked(*args))
+    return out, lse
 
 
 def batch_prefill_ragged(plan: Plan, q: torch.Tensor, k: RaggedKV, v: RaggedKV, sm_scale: float,

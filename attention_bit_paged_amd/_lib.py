@@ -29,7 +29,8 @@ EXPORTS = (
     "nvfp4_plan_get_work", "nvfp4_plan_upload", "nvfp4_batch_decode",
     "nvfp4_batch_decode_noalloc",
     "nvfp4_batch_decode_append", "nvfp4_kv_checksum", "nvfp4_set_timing_events",
-    "nvfp4_batch_prefill", "nvfp4_batch_prefill_ragged",
+    "nvfp4_batch_prefill", "nvfp4_plan_mask_bytes", "nvfp4_batch_prefill_masked",
+    "nvfp4_batch_prefill_ragged",
     "nvfp4_plan_set_deferred_merge", "nvfp4_merge_partials", "nvfp4_merge_states",
 )
 
@@ -60,7 +61,8 @@ KV_DTYPES = {"nvfp4": 0, "fp8": 1}
 
 
 class PlanOptionsStruct(ctypes.Structure):
-    _fields_ = [("kv_dtype", ctypes.c_int32), ("kv_indptr", ctypes.c_void_p)]
+    _fields_ = [("kv_dtype", ctypes.c_int32), ("kv_indptr", ctypes.c_void_p),
+                ("custom_mask", ctypes.c_int32)]
 
 
 class KVRaggedStruct(ctypes.Structure):
@@ -132,6 +134,9 @@ def _load():
         "nvfp4_set_timing_events": (ctypes.c_int, [vp, vp]),
         "nvfp4_batch_prefill": (ctypes.c_int, [vp, vp, i64, i64, vp, i64, pool_p, pool_p, f32, vp, sz,
                                                vp, i64, i64, vp, vp]),
+        "nvfp4_plan_mask_bytes": (i64, [vp]),
+        "nvfp4_batch_prefill_masked": (ctypes.c_int, [vp, vp, i64, i64, vp, i64, pool_p, pool_p,
+                                                      vp, f32, vp, sz, vp, i64, i64, vp, vp]),
         "nvfp4_batch_prefill_ragged": (ctypes.c_int, [vp, vp, i64, i64,
                                                       ctypes.POINTER(KVRaggedStruct),
                                                       ctypes.POINTER(KVRaggedStruct), f32, vp, sz,

@@ -183,6 +183,9 @@ struct nvfp4_plan {
   int batch = 0, num_qo_heads = 0, num_kv_heads = 0, group = 0;
   int head_dim_qk = 0, head_dim_vo = 0, page_size = 0, causal = 0;
   int kv_dtype = NVFP4_KV_NVFP4;
+  int custom_mask = 0;     // prefill with a packed custom mask (nvfp4_batch_prefill_masked)
+  std::vector<int64_t> mask_off;  // byte offset of each request's mask segment
+  int64_t mask_bytes = 0;
   int ragged = 0;          // prefill over ragged rows (nvfp4_batch_prefill_ragged)
   std::vector<int32_t> kv_starts;  // ragged: first row of each request
   std::vector<int32_t> ragged_pt;  // ragged: the 16-row "pages" of each request
@@ -196,7 +199,7 @@ struct nvfp4_plan {
   std::vector<int32_t> kv_lens, qo_indptr;
   int num_partials = 0;
   // workspace layout (byte offsets)
-  size_t off_work = 0, off_merge = 0, off_kvlens = 0, off_indptr = 0, off_pt = 0,
+  size_t off_work = 0, off_merge = 0, off_kvlens = 0, off_indptr = 0, off_pt = 0, off_mask = 0,
          off_part_o = 0, off_part_lse = 0, ws_bytes = 0;
   std::vector<uint8_t> image;  // the tables as they sit at the start of the workspace
   void* uploaded_to = nullptr;
@@ -227,6 +230,13 @@ nvfp4_status nvfp4_plan_create_ex(const int32_t* kv_lens, const int32_t* qo_indp
   *out = nullptr;
   const int kv_dtype = options ? options->kv_dtype : NVFP4_KV_NVFP4;
   const int32_t* kv_indptr = options ? options->kv_indptr : nullptr;
+  const bool custom_mask = options && options->custom_mask;
+  if (custom_mask && !qo_indptr)
+    return fail(NVFP4_E_SHAPE, "a custom mask is a prefill mask: qo_indptr must be given");
+  if (custom_mask && kv_indptr)
+    return fail(NVFP4_E_UNSUPPORTED, "custom masks run over paged KV only, not ragged rows");
+  // the mask decides visibility: every tile covers its request's whole key range
+  if (custom_mask) causal = 0;
   if (kv_dtype != NVFP4_KV_NVFP4 && kv_dtype != NVFP4_KV_FP8_E4M3)
     return fail(NVFP4_E_INVALID, "options.kv_dtype %d is neither NVFP4 (0) nor FP8 E4M3 (1)",
                 kv_dtype);
@@ -325,6 +335,22 @@ nvfp4_status nvfp4_plan_create_ex(const int32_t* kv_lens, const int32_t* qo_indp
   plan->page_size = page_size;
   plan->causal = prefill ? (causal != 0) : 0;
   plan->kv_dtype = kv_dtype;
+  if (custom_mask) {
+    // each request's bits packed on their own, padded to a byte
+    plan->custom_mask = 1;
+    plan->mask_off.resize(batch);
+    int64_t at = 0;
+    for (int b = 0; b < batch; ++b) {
+      plan->mask_off[b] = at;
+      at += ((int64_t)(qo_indptr[b + 1] - qo_indptr[b]) * kv_lens[b] + 7) / 8;
+    }
+    plan->mask_bytes = at;
+    if (at >= (int64_t(1) << 31) - 64) {
+      delete plan;
+      return fail(NVFP4_E_UNSUPPORTED, "the packed mask would hold %lld bytes; the kernels "
+                  "address it with 32-bit offsets", (long long)at);
+    }
+  }
   if (kv_indptr) {
     // request b's page i starts at row kv_indptr[b] + 16 i: with the page stride equal to
     // the row stride, slot t of that page is row kv_indptr[b] + 16 i + t
@@ -459,6 +485,8 @@ nvfp4_status nvfp4_plan_create_ex(const int32_t* kv_lens, const int32_t* qo_indp
   off = align_up(off + (size_t)(batch + 1) * sizeof(int32_t));
   plan->off_pt = off;  // ragged plans: the page table of their rows
   off = align_up(off + plan->ragged_pt.size() * sizeof(int32_t));
+  plan->off_mask = off;  // custom-mask plans: the requests' segment offsets
+  off = align_up(off + plan->mask_off.size() * sizeof(int64_t));
   plan->off_part_o = off;
   off = align_up(off + (size_t)plan->num_partials * plan->rows_per_slot * head_dim_vo * sizeof(float));
   plan->off_part_lse = off;
@@ -474,6 +502,9 @@ nvfp4_status nvfp4_plan_create_ex(const int32_t* kv_lens, const int32_t* qo_indp
   put(plan->off_kvlens, plan->kv_lens);
   put(plan->off_indptr, plan->qo_indptr);
   put(plan->off_pt, plan->ragged_pt);
+  if (!plan->mask_off.empty())
+    std::memcpy(plan->image.data() + plan->off_mask, plan->mask_off.data(),
+                plan->mask_off.size() * sizeof(int64_t));
   *out = plan;
   return ok();
 }
@@ -650,13 +681,17 @@ nvfp4_status run(const nvfp4_plan* plan, bool prefill, const void* q, int64_t q_
                  int64_t q_s_head, const int32_t* page_table, int64_t pt_stride,
                  const nvfp4_kv_pool* k, const nvfp4_kv_pool* v, float sm_scale, void* ws,
                  size_t ws_bytes, float* o, int64_t o_s_row, int64_t o_s_head, float* lse,
-                 void* stream) {
+                 void* stream, const uint8_t* mask = nullptr) {
   if (nvfp4_status st = check_run(plan, prefill, q, q_s_row, q_s_head, page_table, pt_stride, k,
                                   v, sm_scale, ws, ws_bytes, o, o_s_row, o_s_head, lse, stream))
     return st;
   if (plan->work.empty()) return ok();
-  const AttnArgs a = make_args(plan, q, q_s_row, q_s_head, page_table, pt_stride, k, v, sm_scale,
-                               ws, o, o_s_row, o_s_head, lse);
+  AttnArgs a = make_args(plan, q, q_s_row, q_s_head, page_table, pt_stride, k, v, sm_scale, ws, o,
+                         o_s_row, o_s_head, lse);
+  if (mask) {
+    a.mask = mask;
+    a.mask_off = reinterpret_cast<const int64_t*>(static_cast<uint8_t*>(ws) + plan->off_mask);
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = prefill ? launch_prefill(plan->head_dim_qk, plan->head_dim_vo, plan->kv_dtype,
                                           a.page_shift, a, s)
@@ -789,8 +824,31 @@ nvfp4_status nvfp4_batch_prefill(const nvfp4_plan* plan, const void* q, int64_t 
                                  int64_t o_stride_head, float* lse, void* stream) {
   if (plan && plan->ragged)
     return fail(NVFP4_E_SHAPE, "the plan was made for ragged KV: use nvfp4_batch_prefill_ragged");
+  if (plan && plan->custom_mask)
+    return fail(NVFP4_E_SHAPE, "the plan was made for a custom mask: use "
+                "nvfp4_batch_prefill_masked");
   return run(plan, true, q, q_stride_tok, q_stride_head, page_table, pt_stride, k_pool, v_pool,
              sm_scale, workspace, workspace_bytes, o, o_stride_tok, o_stride_head, lse, stream);
+}
+
+int64_t nvfp4_plan_mask_bytes(const nvfp4_plan* plan) { return plan ? plan->mask_bytes : 0; }
+
+nvfp4_status nvfp4_batch_prefill_masked(const nvfp4_plan* plan, const void* q,
+                                        int64_t q_stride_tok, int64_t q_stride_head,
+                                        const int32_t* page_table, int64_t pt_stride,
+                                        const nvfp4_kv_pool* k_pool, const nvfp4_kv_pool* v_pool,
+                                        const uint8_t* mask, float sm_scale, void* workspace,
+                                        size_t workspace_bytes, float* o, int64_t o_stride_tok,
+                                        int64_t o_stride_head, float* lse, void* stream) {
+  if (!plan) return fail(NVFP4_E_INVALID, "plan is NULL");
+  if (!plan->custom_mask)
+    return fail(NVFP4_E_SHAPE, "the plan was made without a custom mask: create it with "
+                "options.custom_mask");
+  // a plan with work has queries, and then keys (q_b <= kv_len_b), so mask bits
+  if (!plan->work.empty() && !mask) return fail(NVFP4_E_INVALID, "mask is NULL");
+  return run(plan, true, q, q_stride_tok, q_stride_head, page_table, pt_stride, k_pool, v_pool,
+             sm_scale, workspace, workspace_bytes, o, o_stride_tok, o_stride_head, lse, stream,
+             mask);
 }
 
 nvfp4_status nvfp4_batch_prefill_ragged(const nvfp4_plan* plan, const void* q,

@@ -278,6 +278,21 @@ __device__ __forceinline__ void v_operands(const StepRaw<DK, DV, FMT>& r, int t0
   }
 }
 
+// Custom masks (packed bits, 1 = visible; element i*L + j of a request's [q, L] mask is
+// bit (e % 8) of byte e / 8 of its segment).  The visibility of the lane's eight keys
+// key0 .. key0 + 7 for query row `qpos`: only the first `nvalid` of them exist (the
+// rest read as hidden), and only the bytes holding those bits are read.
+__device__ __forceinline__ uint32_t mask_bits8(const uint8_t* seg, int64_t L, int qpos, int key0,
+                                               int nvalid) {
+  if (nvalid <= 0) return 0u;
+  nvalid = nvalid > 8 ? 8 : nvalid;
+  const int64_t bit = (int64_t)qpos * L + key0;
+  const int sh = (int)(bit & 7);
+  uint32_t w = seg[bit >> 3];
+  if (sh + nvalid > 8) w |= (uint32_t)seg[(bit >> 3) + 1] << 8;
+  return (w >> sh) & ((1u << nvalid) - 1u);
+}
+
 // Multiplies 16 accumulators by alpha in place.  One asm statement whose operands are
 // the accumulators themselves: under a branch, the registers stay where they are (as
 // C++ arithmetic, the join of the two paths copies every accumulator).  The leading
@@ -358,6 +373,28 @@ struct RowState {
     const float b2 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(x[3], x[4]), x[5]);
     const float b3 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(x[6], x[7]), b1);
     return __builtin_elementwise_maximum(b3, b2);
+  }
+  // The same with visibility given bit by bit (a custom mask): key t0 + 8j + i is
+  // visible when bit i of `vis` is set.
+  __device__ __forceinline__ float scores_vis(f32x4 sa, f32x4 sb, uint32_t vis, float (&x)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = sa[i];
+      x[4 + i] = sb[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (!((vis >> i) & 1u)) x[i] = -INFINITY;
+    const float b1 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(x[0], x[1]), x[2]);
+    const float b2 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(x[3], x[4]), x[5]);
+    const float b3 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(x[6], x[7]), b1);
+    return __builtin_elementwise_maximum(b3, b2);
+  }
+  __device__ __forceinline__ f16x8 softmax_vis(f32x4 sa, f32x4 sb, float c, uint32_t vis) {
+    float x[8];
+    const float bm = scores_vis(sa, sb, vis, x);
+    if (__ballot(wants(bm, c)) != 0) raise(bm, c);
+    return probs<true>(x, c);
   }
   // This lane's largest passes the reference by more than the slack.  bm * c - m is
   // +inf while m is -inf (any key raises) and NaN when both are -inf (the lane has no

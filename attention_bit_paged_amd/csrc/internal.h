@@ -64,6 +64,10 @@ struct AttnArgs {
   // items (see decode_item); set when the pools interleave kv heads at a short stride.
   int32_t xcd_group;
   const int32_t* merges;    // merge records
+  // Prefill with a custom mask (else null): packed bits, and each request's byte offset
+  // into them (device, from the workspace).
+  const uint8_t* mask;
+  const int64_t* mask_off;
   // Decode with append: the step's new K/V rows (bf16 [batch, kv heads, dim], element
   // strides), quantised into the slot of token kv_len-1 of their request by the work
   // item that ends there; k_new is null when the call appends nothing.

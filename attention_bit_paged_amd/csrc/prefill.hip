@@ -90,9 +90,13 @@ __global__ __launch_bounds__(256) void prefill_regs_kernel(AttnArgs a) {
     wave_end = min(kv1, q0 + r_last / G + off + 1);
   }
   // steps that may hold a masked key: the chunk's tail and, for causal rows, any step
-  // past the first visible-key limit of the wave's first row
+  // past the first visible-key limit of the wave's first row (every step with a custom
+  // mask)
   int mask_from = kv1 - kDecodeStep;
   if (a.causal) mask_from = min(mask_from, q0 + row_base / G + off + 1 - kDecodeStep);
+  const bool custom = a.mask != nullptr;  // uniform
+  const uint8_t* mseg = custom ? a.mask + a.mask_off[b] : nullptr;
+  const int64_t kv_len = a.kv_lens[b];
 
   PagedView<DK, DV, false, FMT> view;
   view.init(a, b, kvh, lane);
@@ -115,8 +119,15 @@ __global__ __launch_bounds__(256) void prefill_regs_kernel(AttnArgs a) {
         sa = mfma16x16x32(ka[s], qf[rg][s], sa);
         sb = mfma16x16x32(kb[s], qf[rg][s], sb);
       }
-      p[rg] = masked ? st[rg].template softmax<true>(sa, sb, sc[rg], t0, j, last[rg])
-                     : st[rg].template softmax<false>(sa, sb, sc[rg], t0, j, last[rg]);
+      if (custom) {
+        const int key0 = t0 + 8 * j;
+        const int qpos = q0 + (row_base + rg * 16 + n) / G;
+        const uint32_t vis = rv[rg] ? mask_bits8(mseg, kv_len, qpos, key0, tlast - key0 + 1) : 0u;
+        p[rg] = st[rg].softmax_vis(sa, sb, sc[rg], vis);
+      } else {
+        p[rg] = masked ? st[rg].template softmax<true>(sa, sb, sc[rg], t0, j, last[rg])
+                       : st[rg].template softmax<false>(sa, sb, sc[rg], t0, j, last[rg]);
+      }
     }
     f16x8 vt[S::NT];
     if (t0 + kDecodeStep > kv1)
@@ -178,9 +189,16 @@ struct CoopShape {
   static constexpr int ROWS = NW * NR * 16;       // rows per work item
   static constexpr int NOP = 2 * S::NS + S::NT;   // operand vectors per step
   static constexpr int OPB = NOP * 64 * 16;       // bytes of one operand buffer
-  static constexpr int RAW_STAGE = RingBytes<DK, DV, FMT>::STAGE;
-  using R = RingShape<DK, DV, 3 * RAW_STAGE, FMT>;  // three raw stages
-  static constexpr int LDS = 3 * RAW_STAGE + 2 * OPB;
+  static constexpr int RAW_STAGE = RingBytes<DK, DV, FMT>::STAGE;  // a step's K/V bytes
+  static constexpr int WL = 3 * RAW_STAGE;
+  using R = RingShape<DK, DV, WL, FMT>;           // three raw stages
+  // A step's custom-mask bytes: 8 per tile query (two 4-byte copies of 64 lanes per
+  // block of 64 queries; a tile has at most ROWS queries), in a ring of four slots of
+  // their own: the copies of step s land in slot s % 4 three steps ahead, and that slot
+  // is written again only after step s's softmax, so the step reads its bits directly.
+  static constexpr int MASK_BLOCKS = (ROWS + 63) / 64;
+  static constexpr int MASK_SLOT = MASK_BLOCKS * 512;
+  static constexpr int LDS = 3 * RAW_STAGE + 2 * OPB + 4 * MASK_SLOT;
   static constexpr int KE = (2 * S::NS + NW - 1) / NW;  // K operand entries per lane
   static constexpr int VH = NW / 4;               // V tiles split in this many parts
   static constexpr int VPART = S::NT / VH;        // V tiles per part
@@ -196,9 +214,10 @@ constexpr int kLdsPerCu = 160 * 1024;
 constexpr int coop_lds_formula(int dk, int dv, int fmt) {
   const int rbk = fmt == kFp8 ? dk : dk / 2, rbv = fmt == kFp8 ? dv : dv / 2;
   const int sf = fmt == kFp8 ? 0 : (2 * dk + 2 * dv + 255) / 256 * 256;
+  const int rows = dk <= 128 && dv <= 128 ? 192 : 128;  // tile rows (queries at most)
   const int raw = 32 * (rbk + rbv) + sf;
   const int opb = (2 * (dk / 32) + dv / 16) * 64 * 16;
-  return 3 * raw + 2 * opb;
+  return 3 * raw + 2 * opb + 4 * ((rows + 63) / 64 * 512);
 }
 constexpr int coop_wgs_per_cu(int dk, int dv) { return dk <= 128 && dv <= 128 ? 2 : 1; }
 
@@ -373,8 +392,10 @@ __device__ __forceinline__ void coop_dequant(uint32_t raw, uint32_t opb, int wav
 
 // Waits until this wave's copies of all but the newest issued step are done (or all
 // of them).  Waves 0..3 each copy one pool; the others copy nothing.
+// Wave 3 also copies the custom-mask bytes, two copies per block of 64 tile queries:
+// `mask_copies` of them per step (0, 2, 4 or 6; wave-uniform).
 template <int DK, int DV, int FMT>
-__device__ __forceinline__ void coop_wait(int wave, bool one_newer) {
+__device__ __forceinline__ void coop_wait(int wave, bool one_newer, int mask_copies) {
   using R = typename CoopShape<DK, DV, FMT>::R;
   constexpr int N0 = R::ndma(1), N1 = R::ndma(2), N2 = R::ndma(4), N3 = R::ndma(8);
   if (wave > 3) return;
@@ -386,18 +407,36 @@ __device__ __forceinline__ void coop_wait(int wave, bool one_newer) {
     asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N1));
   } else if (wave == 2) {
     asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N2));
-  } else {
+  } else if (mask_copies == 0) {
     asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N3));
+  } else if (mask_copies == 2) {
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N3 + 2));
+  } else if (mask_copies == 4) {
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N3 + 4));
+  } else {
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N3 + 6));
   }
 }
+
+// The custom-mask copies of a tile: lane l of block qb carries tile query 64 qb + l.
+// A query's bits of the keys of a step start 4 bytes further on in every step (32 keys),
+// at a fixed bit shift, so its copies take the step's base (scalar) plus a fixed
+// per-lane byte offset; lanes past the tile's queries copy the tile's first query's
+// bytes instead (unused).
+struct CoopMask {
+  const uint8_t* seg;  // the request's mask segment; null without a custom mask
+  uint32_t voff[3];    // byte offset of this lane's query at the chunk's first key
+  int blocks;          // blocks of 64 tile queries (uniform)
+  uint32_t ring;       // LDS address of the mask ring (uniform)
+};
 
 // The copy offsets of the one pool this wave issues (wave 0: K data, 1: V data, 2 and 3:
 // the scale bytes, whose copies carry both pools' lanes).  The full plan holds every
 // pool's offsets; kept whole in each wave they cost registers the loop needs.
 template <int DK, int DV, int FMT = kNvfp4>
 struct CoopCopies {
-  using R = RingShape<DK, DV, 3 * CoopShape<DK, DV, FMT>::RAW_STAGE, FMT>;
-  using Plan = RingPlan<DK, DV, 3 * CoopShape<DK, DV, FMT>::RAW_STAGE, FMT>;
+  using R = RingShape<DK, DV, CoopShape<DK, DV, FMT>::WL, FMT>;
+  using Plan = RingPlan<DK, DV, CoopShape<DK, DV, FMT>::WL, FMT>;
   static constexpr int MAXC = R::N_KD > R::N_VD ? (R::N_KD > R::N_SF ? R::N_KD : R::N_SF)
                                                 : (R::N_VD > R::N_SF ? R::N_VD : R::N_SF);
   uint32_t mine[MAXC > 0 ? MAXC : 1];
@@ -428,14 +467,47 @@ struct CoopCopies {
 template <int DK, int DV, int FMT>
 __device__ __forceinline__ void coop_issue(int wave, const CoopCopies<DK, DV, FMT>& cc,
                                            uint32_t stage, const PagedView<DK, DV, true, FMT>& view,
-                                           int t0, int tlast, uint32_t& bad) {
-  constexpr int WL = 3 * CoopShape<DK, DV, FMT>::RAW_STAGE;
+                                           int t0, int tlast, uint32_t& bad, const CoopMask& cm,
+                                           int kv0) {
+  using C = CoopShape<DK, DV, FMT>;
+  constexpr int WL = C::WL;
   if (wave == 0) ring_issue<DK, DV, WL, 1>(cc.template expand<1>(), stage, view, t0, tlast, bad);
   else if (wave == 1) ring_issue<DK, DV, WL, 2>(cc.template expand<2>(), stage, view, t0, tlast, bad);
   else if constexpr (!StepShape<DK, DV, FMT>::F8) {  // FP8 has no scale pools
     if (wave == 2) ring_issue<DK, DV, WL, 4>(cc.template expand<4>(), stage, view, t0, tlast, bad);
     else if (wave == 3) ring_issue<DK, DV, WL, 8>(cc.template expand<8>(), stage, view, t0, tlast, bad);
   }
+  if (wave == 3 && cm.blocks > 0) {
+    const uint8_t* base = cm.seg + ((t0 - kv0) >> 3);  // 4 bytes per 32-key step
+    const uint32_t slot = cm.ring + (((t0 - kv0) >> 5) & 3) * C::MASK_SLOT;
+#pragma unroll
+    for (int qb = 0; qb < C::MASK_BLOCKS; ++qb) {
+      if (qb < cm.blocks) {
+        dma<false>(slot + qb * 512, cm.voff[qb], base);
+        dma<false>(slot + qb * 512 + 256, cm.voff[qb] + 4, base);
+      }
+    }
+  }
+}
+
+// This lane's visibility bits of keys t0 + 8j .. t0 + 8j + 7 for the query of its row
+// `row` (tile-local), from the step's slot of the mask ring; keys after tlast hidden.
+template <int DK, int DV, int FMT>
+__device__ __forceinline__ uint32_t coop_mask_bits(const CoopMask& cm, int row, int j, int G,
+                                                   int q0, int64_t kv_len, int kv0, int t0,
+                                                   int tlast) {
+  using C = CoopShape<DK, DV, FMT>;
+  const int nvalid = tlast - (t0 + 8 * j) + 1;
+  const uint32_t keep = nvalid <= 0 ? 0u : (nvalid >= 8 ? 0xFFu : (1u << nvalid) - 1u);
+  const int ql = min(row / G, C::MASK_BLOCKS * 64 - 1);  // rows past the tile are not stored
+  const uint32_t at = cm.ring + (((t0 - kv0) >> 5) & 3) * C::MASK_SLOT + (ql >> 6) * 512 +
+                      (ql & 63) * 4;
+  uint32_t lo, hi;
+  lds_load<4>(at, &lo);
+  lds_load<4>(at + 256, &hi);
+  const int sh = (int)(((int64_t)(q0 + ql) * kv_len + kv0) & 7) + 8 * j;
+  const uint64_t v = ((uint64_t)hi << 32) | lo;
+  return ((uint32_t)(v >> sh) & 0xFFu) & keep;
 }
 
 // Q quarter-row multiplied by the score factor c (the scores then leave the product in
@@ -566,6 +638,22 @@ void prefill_coop_kernel(AttnArgs a) {
   }
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
   const uint32_t raw0 = lds0, opb0 = lds0 + 3 * C::RAW_STAGE;
+  // custom mask (the plan tiles the whole key range then: every step is masked)
+  const bool custom = a.mask != nullptr;  // uniform
+  const int64_t kv_len = a.kv_lens[b];
+  CoopMask cm;
+  cm.seg = nullptr;
+  cm.blocks = 0;
+  cm.ring = opb0 + 2 * C::OPB;
+  if (custom) {
+    cm.seg = a.mask + a.mask_off[b];
+    cm.blocks = (qn + 63) / 64;
+#pragma unroll
+    for (int qb = 0; qb < C::MASK_BLOCKS; ++qb) {
+      const int ql = qb * 64 + lane < qn ? qb * 64 + lane : 0;
+      cm.voff[qb] = (uint32_t)(((int64_t)(q0 + ql) * kv_len + kv0) >> 3);
+    }
+  }
   CoopLanes<DK, DV, FMT> cl;
   cl.init(wave, lane);
   uint32_t bad = 0;
@@ -574,7 +662,7 @@ void prefill_coop_kernel(AttnArgs a) {
   // latencies of a work item's start overlap.
   for (int i = 0; i < 3 && i < nsteps; ++i)
     coop_issue<DK, DV, FMT>(wave, cc, raw0 + i * C::RAW_STAGE, view, kv0 + i * kDecodeStep, tlast,
-                            bad);
+                            bad, cm, kv0);
   // Head dims up to 256: Q carries the score factor (see ShiftRef) unless some row of
   // the wave could overflow fp16; that wave then takes the exact prescaled Q.
   bool safe = true;
@@ -635,11 +723,11 @@ void prefill_coop_kernel(AttnArgs a) {
     const bool next = i + 1 < nsteps;
     // raw step i+1 landed (only step i+2 may still be in flight); operands of step i
     // are visible; nobody reads operand buffer (i+1)%2 or raw stage i%3 any more
-    if (next) coop_wait<DK, DV, FMT>(wave, i + 2 < nsteps);
+    if (next) coop_wait<DK, DV, FMT>(wave, i + 2 < nsteps, 2 * cm.blocks);
     __syncthreads();
     if (i + 3 < nsteps)
       coop_issue<DK, DV, FMT>(wave, cc, raw0 + (i % 3) * C::RAW_STAGE, view, t_of(i + 3), tlast,
-                              bad);
+                              bad, cm, kv0);
     // Stage and buffer bases as single scalars: left to itself the compiler folds the
     // modulo's parts into every lane address separately (two vector adds per address).
     const uint32_t ob = __builtin_amdgcn_readfirstlane(opb0 + (i & 1) * C::OPB);
@@ -687,7 +775,13 @@ void prefill_coop_kernel(AttnArgs a) {
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       }
       __builtin_amdgcn_s_setprio(0);
-      const f16x8 p = st[0].template softmax<MASK>(sa[0], sb[0], sc[0], t0, j, MASK ? last_of(0) : 0);
+      f16x8 p;
+      if (MASK && custom)
+        p = st[0].softmax_vis(sa[0], sb[0], sc[0],
+                              coop_mask_bits<DK, DV, FMT>(cm, row_base + n, j, G, q0, kv_len, kv0,
+                                                          t0, tlast));
+      else
+        p = st[0].template softmax<MASK>(sa[0], sb[0], sc[0], t0, j, MASK ? last_of(0) : 0);
       f16x8 vt[PF];
       auto vload = [&](int e) {
         lds_load<16>(obl + (2 * S::NS + e) * 1024, reinterpret_cast<uint32_t*>(&vt[e % PF]));
@@ -753,7 +847,13 @@ void prefill_coop_kernel(AttnArgs a) {
     uint64_t want = 0;  // the groups' votes, combined as wave masks on the scalar unit
 #pragma unroll
     for (int rg = 0; rg < NR; ++rg) {
-      bm[rg] = st[rg].template scores<MASK>(sa[rg], sb[rg], t0, j, MASK ? last_of(rg) : 0, x[rg]);
+      if (MASK && custom)
+        bm[rg] = st[rg].scores_vis(sa[rg], sb[rg],
+                                   coop_mask_bits<DK, DV, FMT>(cm, row_base + rg * 16 + n, j, G, q0,
+                                                               kv_len, kv0, t0, tlast),
+                                   x[rg]);
+      else
+        bm[rg] = st[rg].template scores<MASK>(sa[rg], sb[rg], t0, j, MASK ? last_of(rg) : 0, x[rg]);
       want |= __ballot(vote(rg));
     }
     if (want != 0) {
@@ -788,13 +888,13 @@ void prefill_coop_kernel(AttnArgs a) {
   };
   // prologue: three steps in flight (issued above), step 0 dequantised
   if (nsteps > 0) {
-    coop_wait<DK, DV, FMT>(wave, false);
+    coop_wait<DK, DV, FMT>(wave, false, 2 * cm.blocks);
     __syncthreads();
     coop_dequant<DK, DV, true, FMT>(raw0, opb0, wave, cl, tlast - t_of(0));
   }
   // steps whose 32 keys are visible to every row of the tile, then the rest
   const int tile_min_last = a.causal ? min(kv1 - 1, q0 + off) : kv1 - 1;
-  const int n_full = min(nsteps, max(0, (tile_min_last - kv0 + 1) / kDecodeStep));
+  const int n_full = custom ? 0 : min(nsteps, max(0, (tile_min_last - kv0 + 1) / kDecodeStep));
   int i = 0;
   if (shifted) {
     for (; i < n_full; ++i) step(i, std::false_type{}, std::true_type{});

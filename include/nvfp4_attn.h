@@ -172,10 +172,14 @@ nvfp4_status nvfp4_plan_create(const int32_t* kv_lens, const int32_t* qo_indptr,
  *              kv_lens[b].  Needs qo_indptr; the page_size argument is then ignored
  *              (the rows stream as 16-row pages), and runs use
  *              nvfp4_batch_prefill_ragged.
+ *   custom_mask: prefill (paged KV) whose visibility a packed custom mask decides in
+ *              place of the causal rule (nvfp4_batch_prefill_masked); the plan then
+ *              tiles every request's whole key range.
  */
 typedef struct {
   int32_t kv_dtype;
   const int32_t* kv_indptr;
+  int32_t custom_mask;  /* nonzero: runs take a packed custom mask (nvfp4_batch_prefill_masked) */
 } nvfp4_plan_options;
 
 /* nvfp4_plan_create with options (NULL options = nvfp4_plan_create). */
@@ -339,6 +343,31 @@ nvfp4_status nvfp4_batch_prefill(const nvfp4_plan* plan, const void* q, int64_t 
                                  const nvfp4_kv_pool* v_pool, float sm_scale, void* workspace,
                                  size_t workspace_bytes, float* o, int64_t o_stride_tok,
                                  int64_t o_stride_head, float* lse, void* stream);
+
+/*
+ * Prefill with a packed custom mask ([PF] commits on segment_packbits: packed custom
+ * masks for bidirectional, multimodal-prefix attention, built per request segment).
+ *   mask: device uint8, the requests' masks packed one after the other: request b's
+ *     mask is [q_b, kv_len_b], row-major (query i, key j), bit set = visible; element
+ *     e = i*kv_len_b + j is bit e % 8 (little-endian) of byte e / 8 of its segment, and
+ *     each segment is padded to a whole byte, so segment b starts at the sum over the
+ *     requests before it of ceil(q * kv_len / 8) bytes.  The buffer must be readable 8
+ *     bytes past its last segment (nvfp4_plan_mask_bytes() + 8 bytes in all): the
+ *     kernels read each query's bits 8 bytes at a time.
+ * The mask replaces the causal rule; a query row that sees no key gets O = 0 and
+ * LSE = -inf.  plan: made with options.custom_mask (NVFP4_E_SHAPE otherwise; such a
+ * plan is refused by nvfp4_batch_prefill).  Other arguments and errors as for
+ * nvfp4_batch_prefill.
+ */
+int64_t nvfp4_plan_mask_bytes(const nvfp4_plan* plan);
+
+nvfp4_status nvfp4_batch_prefill_masked(const nvfp4_plan* plan, const void* q,
+                                        int64_t q_stride_tok, int64_t q_stride_head,
+                                        const int32_t* page_table, int64_t pt_stride,
+                                        const nvfp4_kv_pool* k_pool, const nvfp4_kv_pool* v_pool,
+                                        const uint8_t* mask, float sm_scale, void* workspace,
+                                        size_t workspace_bytes, float* o, int64_t o_stride_tok,
+                                        int64_t o_stride_head, float* lse, void* stream);
 
 /*
  * Ragged (non-paged) K or V rows for nvfp4_batch_prefill_ragged: row r of kv head h

@@ -313,10 +313,10 @@ def test_noalloc_decode_rejects_plans_beyond_its_scratch():
     assert "allocation-free" in msg and str(32 << 20) in msg
 
 
-def _plan_ex_status(kv_dtype=0, kv_indptr=None, **kw):
+def _plan_ex_status(kv_dtype=0, kv_indptr=None, custom_mask=False, **kw):
     args = dict(kv_lens=[64], qo_indptr=[0, 8], num_qo_heads=8, num_kv_heads=1, head_dim_qk=128,
                 head_dim_vo=128, num_cus=256, kv_dtype=["nvfp4", "fp8"][kv_dtype],
-                kv_indptr=kv_indptr)
+                kv_indptr=kv_indptr, custom_mask=custom_mask)
     args.update(kw)
     try:
         nv.Plan(**args)
@@ -408,3 +408,48 @@ def test_ragged_plan_rules():
         nv.batch_prefill_ragged(ragged, q, k, k, 0.1, ws)
     with pytest.raises(ValueError, match="paged"):
         nv.batch_prefill_ragged(paged, q, k, k, 0.1, ws)
+
+
+def test_custom_mask_plan_rules():
+    st, msg = _plan_ex_status(custom_mask=True, qo_indptr=None)
+    assert st == "NVFP4_E_SHAPE" and "prefill" in msg, msg
+    st, msg = _plan_ex_status(custom_mask=True, kv_indptr=[0, 64])
+    assert st == "NVFP4_E_UNSUPPORTED" and "ragged" in msg, msg
+    import torch
+    plan = nv.Plan([64, 20, 5], qo_indptr=[0, 8, 28, 28], num_qo_heads=8, num_kv_heads=1,
+                   head_dim_qk=128, num_cus=256, custom_mask=True, causal=True)
+    assert plan.mask_bytes == (8 * 64 + 7) // 8 + (20 * 20 + 7) // 8 + 0
+    # a mask plan through the unmasked entry point, and no mask given
+    st = nv.lib.nvfp4_batch_prefill(plan.handle, ctypes.c_void_p(0x10000), 1024, 128,
+                                    ctypes.c_void_p(0x20000), 8, ctypes.byref(_fake_pool()),
+                                    ctypes.byref(_fake_pool()), 0.1, ctypes.c_void_p(0x40000),
+                                    plan.workspace_bytes, ctypes.c_void_p(0x80000), 1024, 128,
+                                    ctypes.c_void_p(0x90000), None)
+    assert _lib.STATUS[st] == "NVFP4_E_SHAPE" and "custom mask" in nv.lib.nvfp4_last_error().decode()
+    st = nv.lib.nvfp4_batch_prefill_masked(plan.handle, ctypes.c_void_p(0x10000), 1024, 128,
+                                           ctypes.c_void_p(0x20000), 8,
+                                           ctypes.byref(_fake_pool()), ctypes.byref(_fake_pool()),
+                                           None, 0.1, ctypes.c_void_p(0x40000),
+                                           plan.workspace_bytes, ctypes.c_void_p(0x80000), 1024,
+                                           128, ctypes.c_void_p(0x90000), None)
+    assert _lib.STATUS[st] == "NVFP4_E_INVALID" and "mask" in nv.lib.nvfp4_last_error().decode()
+    unmasked = nv.Plan([64], qo_indptr=[0, 8], num_qo_heads=8, num_kv_heads=1, head_dim_qk=128,
+                       num_cus=256)
+    st = nv.lib.nvfp4_batch_prefill_masked(unmasked.handle, ctypes.c_void_p(0x10000), 1024, 128,
+                                           ctypes.c_void_p(0x20000), 8,
+                                           ctypes.byref(_fake_pool()), ctypes.byref(_fake_pool()),
+                                           ctypes.c_void_p(0x50000), 0.1,
+                                           ctypes.c_void_p(0x40000), unmasked.workspace_bytes,
+                                           ctypes.c_void_p(0x80000), 1024, 128,
+                                           ctypes.c_void_p(0x90000), None)
+    assert _lib.STATUS[st] == "NVFP4_E_SHAPE"
+    # the binding checks the buffer holds the bits plus 8 bytes of read-ahead
+    q = torch.zeros((28, 8, 128), dtype=torch.bfloat16)
+    pt = torch.zeros((3, 4), dtype=torch.int32)
+    pool = nv.KVPool.empty(16, 1, 16, 128, device="cpu")
+    ws = torch.zeros(plan.workspace_bytes, dtype=torch.uint8)
+    short = torch.zeros(plan.mask_bytes + 7, dtype=torch.uint8)
+    with pytest.raises(ValueError, match=r"\+ 8"):
+        nv.batch_prefill_masked(plan, q, pt, pool, pool, short, 0.1, ws)
+    with pytest.raises(ValueError, match="custom mask"):
+        nv.batch_prefill(plan, q, pt, pool, pool, 0.1, ws)
