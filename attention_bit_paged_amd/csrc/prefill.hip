@@ -198,7 +198,8 @@ struct CoopShape {
   // is written again only after step s's softmax, so the step reads its bits directly.
   static constexpr int MASK_BLOCKS = (ROWS + 63) / 64;
   static constexpr int MASK_SLOT = MASK_BLOCKS * 512;
-  static constexpr int LDS = 3 * RAW_STAGE + 2 * OPB + 4 * MASK_SLOT;
+  static constexpr int LDS = 3 * RAW_STAGE + 2 * OPB;  // without the mask ring
+  static constexpr int LDS_MASKED = LDS + 4 * MASK_SLOT;
   static constexpr int KE = (2 * S::NS + NW - 1) / NW;  // K operand entries per lane
   static constexpr int VH = NW / 4;               // V tiles split in this many parts
   static constexpr int VPART = S::NT / VH;        // V tiles per part
@@ -211,13 +212,13 @@ constexpr int kLdsPerCu = 160 * 1024;
 // LDS of one cooperative workgroup: three raw stages of 32 tokens (rows and, for NVFP4,
 // scale rows) and two fp16 operand buffers (2 NS K entries and NT V tiles of 64 lanes x
 // 16 bytes).  A formula, so that shapes without a kernel can be priced too.
-constexpr int coop_lds_formula(int dk, int dv, int fmt) {
+constexpr int coop_lds_formula(int dk, int dv, int fmt, bool masked) {
   const int rbk = fmt == kFp8 ? dk : dk / 2, rbv = fmt == kFp8 ? dv : dv / 2;
   const int sf = fmt == kFp8 ? 0 : (2 * dk + 2 * dv + 255) / 256 * 256;
   const int rows = dk <= 128 && dv <= 128 ? 192 : 128;  // tile rows (queries at most)
   const int raw = 32 * (rbk + rbv) + sf;
   const int opb = (2 * (dk / 32) + dv / 16) * 64 * 16;
-  return 3 * raw + 2 * opb + 4 * ((rows + 63) / 64 * 512);
+  return 3 * raw + 2 * opb + (masked ? 4 * ((rows + 63) / 64 * 512) : 0);
 }
 constexpr int coop_wgs_per_cu(int dk, int dv) { return dk <= 128 && dv <= 128 ? 2 : 1; }
 
@@ -424,7 +425,7 @@ __device__ __forceinline__ void coop_wait(int wave, bool one_newer, int mask_cop
 // per-lane byte offset; lanes past the tile's queries copy the tile's first query's
 // bytes instead (unused).
 struct CoopMask {
-  const uint8_t* seg;  // the request's mask segment; null without a custom mask
+  const uint8_t* seg;  // the request's mask segment
   uint32_t voff[3];    // byte offset of this lane's query at the chunk's first key
   int blocks;          // blocks of 64 tile queries (uniform)
   uint32_t ring;       // LDS address of the mask ring (uniform)
@@ -464,7 +465,7 @@ struct CoopCopies {
   }
 };
 
-template <int DK, int DV, int FMT>
+template <int DK, int DV, int FMT, bool CMASK>
 __device__ __forceinline__ void coop_issue(int wave, const CoopCopies<DK, DV, FMT>& cc,
                                            uint32_t stage, const PagedView<DK, DV, true, FMT>& view,
                                            int t0, int tlast, uint32_t& bad, const CoopMask& cm,
@@ -477,7 +478,7 @@ __device__ __forceinline__ void coop_issue(int wave, const CoopCopies<DK, DV, FM
     if (wave == 2) ring_issue<DK, DV, WL, 4>(cc.template expand<4>(), stage, view, t0, tlast, bad);
     else if (wave == 3) ring_issue<DK, DV, WL, 8>(cc.template expand<8>(), stage, view, t0, tlast, bad);
   }
-  if (wave == 3 && cm.blocks > 0) {
+  if (CMASK && wave == 3) {
     const uint8_t* base = cm.seg + ((t0 - kv0) >> 3);  // 4 bytes per 32-key step
     const uint32_t slot = cm.ring + (((t0 - kv0) >> 5) & 3) * C::MASK_SLOT;
 #pragma unroll
@@ -591,7 +592,9 @@ __device__ __forceinline__ f16x8 probs_shifted(RowState<NT, AccForm::VGPR>& st, 
   return pack8(pp[0], pp[1], pp[2], pp[3]);
 }
 
-template <int DK, int DV, int FMT = kNvfp4>
+// CMASK: the launch carries a custom mask (AttnArgs::mask); a separate instantiation,
+// so that the unmasked kernel holds none of its state.
+template <int DK, int DV, int FMT, bool CMASK>
 __global__ __launch_bounds__((CoopShape<DK, DV, FMT>::NW * 64))
 __attribute__((amdgpu_waves_per_eu(CoopShape<DK, DV, FMT>::WGS_PER_CU)))
 void prefill_coop_kernel(AttnArgs a) {
@@ -600,10 +603,11 @@ void prefill_coop_kernel(AttnArgs a) {
   constexpr int NR = C::NR;
   constexpr int WL = 3 * C::RAW_STAGE;
   static_assert(C::OK, "shape has no cooperative kernel");
-  static_assert(C::LDS == coop_lds_formula(DK, DV, FMT) &&
+  constexpr int LDS = CMASK ? C::LDS_MASKED : C::LDS;
+  static_assert(LDS == coop_lds_formula(DK, DV, FMT, CMASK) &&
                 C::WGS_PER_CU == coop_wgs_per_cu(DK, DV), "LDS formula");
-  static_assert(C::LDS * C::WGS_PER_CU <= kLdsPerCu, "resident workgroups exceed the LDS");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
+  static_assert(LDS * C::WGS_PER_CU <= kLdsPerCu, "resident workgroups exceed the LDS");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int j = lane >> 4;
@@ -639,13 +643,13 @@ void prefill_coop_kernel(AttnArgs a) {
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
   const uint32_t raw0 = lds0, opb0 = lds0 + 3 * C::RAW_STAGE;
   // custom mask (the plan tiles the whole key range then: every step is masked)
-  const bool custom = a.mask != nullptr;  // uniform
+  constexpr bool custom = CMASK;
   const int64_t kv_len = a.kv_lens[b];
   CoopMask cm;
   cm.seg = nullptr;
   cm.blocks = 0;
   cm.ring = opb0 + 2 * C::OPB;
-  if (custom) {
+  if constexpr (CMASK) {
     cm.seg = a.mask + a.mask_off[b];
     cm.blocks = (qn + 63) / 64;
 #pragma unroll
@@ -661,8 +665,8 @@ void prefill_coop_kernel(AttnArgs a) {
   // The first three steps' copies go out before Q is read, so that the two memory
   // latencies of a work item's start overlap.
   for (int i = 0; i < 3 && i < nsteps; ++i)
-    coop_issue<DK, DV, FMT>(wave, cc, raw0 + i * C::RAW_STAGE, view, kv0 + i * kDecodeStep, tlast,
-                            bad, cm, kv0);
+    coop_issue<DK, DV, FMT, CMASK>(wave, cc, raw0 + i * C::RAW_STAGE, view, kv0 + i * kDecodeStep,
+                                   tlast, bad, cm, kv0);
   // Head dims up to 256: Q carries the score factor (see ShiftRef) unless some row of
   // the wave could overflow fp16; that wave then takes the exact prescaled Q.
   bool safe = true;
@@ -726,8 +730,8 @@ void prefill_coop_kernel(AttnArgs a) {
     if (next) coop_wait<DK, DV, FMT>(wave, i + 2 < nsteps, 2 * cm.blocks);
     __syncthreads();
     if (i + 3 < nsteps)
-      coop_issue<DK, DV, FMT>(wave, cc, raw0 + (i % 3) * C::RAW_STAGE, view, t_of(i + 3), tlast,
-                              bad, cm, kv0);
+      coop_issue<DK, DV, FMT, CMASK>(wave, cc, raw0 + (i % 3) * C::RAW_STAGE, view, t_of(i + 3),
+                                     tlast, bad, cm, kv0);
     // Stage and buffer bases as single scalars: left to itself the compiler folds the
     // modulo's parts into every lane address separately (two vector adds per address).
     const uint32_t ob = __builtin_amdgcn_readfirstlane(opb0 + (i & 1) * C::OPB);
@@ -929,8 +933,11 @@ void prefill_coop_kernel(AttnArgs a) {
 template <int DK, int DV, int FMT>
 hipError_t launch_dk_dv(int page_shift, const AttnArgs& a, hipStream_t stream) {
   const dim3 grid(a.n_work);
-  if (page_shift >= 4)
-    launch_attention(prefill_coop_kernel<DK, DV, FMT>, grid,
+  if (page_shift >= 4 && a.mask)
+    launch_attention(prefill_coop_kernel<DK, DV, FMT, true>, grid,
+                     dim3(CoopShape<DK, DV, FMT>::NW * 64), stream, a);
+  else if (page_shift >= 4)
+    launch_attention(prefill_coop_kernel<DK, DV, FMT, false>, grid,
                      dim3(CoopShape<DK, DV, FMT>::NW * 64), stream, a);
   else
     launch_attention(prefill_regs_kernel<DK, DV, FMT>, grid, dim3(256), stream, a);
@@ -966,8 +973,9 @@ int prefill_rows_per_item(int dk, int dv, int /*group*/, int page_size) {
 
 size_t prefill_lds_bytes(int dk, int dv, int page_size, int fmt) {
   if (page_size < 16) return 0;  // the register kernel uses no LDS
-  // the resident workgroups of the cooperative kernel, also for shapes without one
-  return (size_t)coop_lds_formula(dk, dv, fmt) * coop_wgs_per_cu(dk, dv);
+  // the resident workgroups of the cooperative kernel (its custom-mask form, the larger),
+  // also for shapes without one
+  return (size_t)coop_lds_formula(dk, dv, fmt, true) * coop_wgs_per_cu(dk, dv);
 }
 
 hipError_t launch_prefill(int dk, int dv, int fmt, int page_shift, const AttnArgs& a,

@@ -444,6 +444,66 @@ def kv_type_lines(torch, nv, paged, synth, iters=60, warm=12, pool_sets=3):
     return out
 
 
+def prefix_masks(w):
+    """Multimodal-prefix masks of a prefill workload: the first third of each request's
+    new tokens (an image) attend to each other bidirectionally, every row also sees the
+    cached prefix and, causally, the tokens up to itself."""
+    out = []
+    for q, L in zip(w.qo_lens, w.kv_lens):
+        prefix, img = L - q, max(1, q // 3)
+        i = np.arange(q)[:, None]
+        j = np.arange(L)[None, :]
+        out.append((j <= i + prefix) | ((i < img) & (j >= prefix) & (j < prefix + img)))
+    return out
+
+
+def masked_prefill_line(torch, nv, paged, synth, iters=60, warm=12, pool_sets=3):
+    """The prefill extend under multimodal-prefix masks (nvfp4_batch_prefill_masked),
+    beside the same workload's causal run measured the same way.  Flops count the
+    pairs the mask leaves visible."""
+    w = synth.workload("prefill_extend")
+    masks = prefix_masks(w)
+    packed = np.concatenate([np.packbits(m.ravel(), bitorder="little") for m in masks] +
+                            [np.zeros(8, dtype=np.uint8)])
+    visible = int(sum(int(m.sum()) for m in masks))
+    flops = 2 * (w.head_dim_qk + w.head_dim_vo) * w.num_qo_heads * visible
+    cases = [paged.build_case(w, keep_sources=False) for _ in range(pool_sets)]
+    out = {"workload": w.name, "mask": "first third of each request's new tokens "
+           "bidirectional, the rest causal", "visible_pairs_per_head": visible,
+           "causal_pairs_per_head": w.unmasked_pairs(), "flops": flops}
+    for label, custom in (("causal", False), ("masked", True)):
+        plan = nv.Plan(w.kv_lens, num_qo_heads=w.num_qo_heads, num_kv_heads=w.num_kv_heads,
+                       head_dim_qk=w.head_dim_qk, head_dim_vo=w.head_dim_vo,
+                       qo_indptr=cases[0].qo_indptr.tolist(), causal=True, custom_mask=custom)
+        plan.set_deferred_merge(True)
+        ws = plan.new_workspace()
+        plan.upload(ws)
+        o = torch.empty((w.total_q, w.num_qo_heads, w.head_dim_vo), device="cuda")
+        lse = torch.empty((w.total_q, w.num_qo_heads), device="cuda")
+        if custom:
+            mask = torch.from_numpy(packed).cuda()
+            run = [nv.batch_prefill_masked(plan, c.q, c.page_table, c.k_pool, c.v_pool, mask,
+                                           w.sm_scale, ws, out=o, lse=lse, prepare=True)
+                   for c in cases]
+        else:
+            run = [nv.batch_prefill(plan, c.q, c.page_table, c.k_pool, c.v_pool, w.sm_scale, ws,
+                                    out=o, lse=lse, prepare=True) for c in cases]
+        merge = nv.merge_partials(plan, ws, o, lse, prepare=True)
+        for i in range(warm):
+            run[i % len(run)]()
+            merge()
+        run_ms, merge_ms = timed_passes(torch, nv, run, merge, iters)
+        fl = flops if custom else w.flops()
+        out[label] = {"kernel_TFLOPs": round(fl / run_ms / 1e9, 2),
+                      "kernel_frac_mfma_f16": round(fl / run_ms / 1e9 / MFMA_F16_PEAK_TFLOPS, 4),
+                      "attn_ms": round(run_ms, 4), "merge_ms": round(merge_ms, 4),
+                      "work_items": plan.info()["num_work_items"]}
+        del run, merge, ws
+    del cases
+    torch.cuda.empty_cache()
+    return out
+
+
 def stream_ceiling(torch, nv, plan, cases, ws, iters, kv_bytes, attn_ms):
     """What the decode access pattern sustains without the attention arithmetic: the
     checksum kernel (nvfp4_kv_checksum) streams the same plan's KV bytes through the same
@@ -902,6 +962,7 @@ def main():
         out["layout_variants"] = [variant_lines(torch, nv, paged, synth, n)
                                   for n in ("batch_decode", "prefill_extend")]
         out["kv_types"] = kv_type_lines(torch, nv, paged, synth)
+        out["masked_prefill"] = masked_prefill_line(torch, nv, paged, synth)
     print(json.dumps(out), flush=True)
 
 
