@@ -39,6 +39,14 @@ out the bit layouts, nibble order or rounding.  The readings taken here:
     1 = visible; each request's bits are packed on their own (little-endian bits within
     a byte, padded to a whole byte), so its bits start at byte sum of ceil(q_b' L_b' / 8)
     over the requests before it; a custom mask replaces the causal rule.
+  * Rotary position embedding (in-kernel RoPE): the pages give no formula.  Reading:
+    the rotary embedding of RoFormer in its rotate-half arrangement, where element i
+    and element i + Dk/2 of a Q or K row form a pair rotated by pos * w_i, with
+    w_i = theta^(-2i/Dk) / scale for i < Dk/2 (theta 1e4 by default; scale > 1
+    stretches positions linearly).  Half the QK head dim of frequencies, as the pages'
+    frequency table holds, spanning Dk also when Dv is smaller.  Key j of a request
+    sits at position j (the cache holds un-rotated keys); query row i of a request
+    with q_b rows and L_b keys at L_b - q_b + i, the causal rule's alignment.
 """
 from __future__ import annotations
 
@@ -286,18 +294,61 @@ def pack_masks(masks):
     return np.concatenate(out) if out else np.zeros(0, dtype=np.uint8)
 
 
+# ---------------------------------------------------------------------------
+# Rotary position embedding  ([PF] commit "Address CodeRabbit review on
+# flashinfer-ai#3684 (5 findings)", item init_rope_freq: the in-kernel rotary's
+# frequency table has one entry per pair of QK head-dim elements, NUM_MMA_D_QK/2
+# MMA tiles of them, and must span the QK dim also where the VO dim is smaller;
+# pos_encoding_mode of the prefill paths)
+# ---------------------------------------------------------------------------
+
+def rope_frequencies(head_dim, theta=1e4, scale=1.0):
+    """Angular frequency of each of the head_dim/2 element pairs:
+    w_i = theta^(-2i / head_dim) / scale (radians per position)."""
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    return np.power(float(theta), -2.0 * i / head_dim) / float(scale)
+
+
+def apply_rope(x, positions, theta=1e4, scale=1.0):
+    """Rotate rows x [n, H, D] (float64) at integer ``positions`` [n]: the pair
+    (x_i, x_{i+D/2}) becomes (x_i cos a - x_{i+D/2} sin a, x_{i+D/2} cos a + x_i sin a)
+    with a = pos * w_i, i < D/2."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    h = d // 2
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * rope_frequencies(d, theta, scale)[None, :]
+    c, s = np.cos(ang)[:, None, :], np.sin(ang)[:, None, :]
+    x1, x2 = x[..., :h], x[..., h:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+def query_positions(q_len, kv_len):
+    """Positions of a request's query rows: the last q_len of its kv_len positions."""
+    return np.arange(q_len, dtype=np.int64) + (int(kv_len) - int(q_len))
+
+
+def _rotate(q, k, kv_len, rope):
+    """Q and K of one request rotated at their positions (rope = (theta, scale))."""
+    if rope is None:
+        return q, k
+    theta, scale = rope
+    return (apply_rope(q, query_positions(q.shape[0], kv_len), theta, scale),
+            apply_rope(k, np.arange(k.shape[0]), theta, scale))
+
+
 def paged_attention(q, k_pool, k_sf, v_pool, v_sf, page_table, kv_lens, qo_indptr,
                     page_size, sm_scale, causal=False, layout="HND",
                     k_global=1.0, v_global=1.0, rows=None, kv_dtype="nvfp4",
-                    custom_mask=None):
+                    custom_mask=None, rope=None):
     """Batched attention over paged K/V (decode when every q_b is 1).
 
     q [sum q_b, Hq, Dk]; pools as in ``gather_pages`` with W = D/2 (NVFP4 data),
     D/16 (NVFP4 scales) or D (FP8 data; scales None).  ``rows`` optionally restricts
     the computation to a subset of requests (the other outputs stay NaN).
     ``custom_mask``: packed mask bytes of all requests (see ``mask_segments``), which
-    then decide visibility in place of ``causal``.  Returns O [sum q_b, Hq, Dv] and
-    LSE [sum q_b, Hq].
+    then decide visibility in place of ``causal``.  ``rope`` = (theta, scale) rotates
+    Q and the dequantised K at their positions first (``apply_rope``).  Returns
+    O [sum q_b, Hq, Dv] and LSE [sum q_b, Hq].
     """
     q = np.asarray(q, dtype=np.float64)
     nq, hq, _ = q.shape
@@ -317,15 +368,17 @@ def paged_attention(q, k_pool, k_sf, v_pool, v_sf, page_table, kv_lens, qo_indpt
         k = dequantize_kv(rows_of(k_pool, b, L), rows_of(k_sf, b, L), k_global, kv_dtype)
         v = dequantize_kv(rows_of(v_pool, b, L), rows_of(v_sf, b, L), v_global, kv_dtype)
         m = None if seg is None else unpack_mask_segment(custom_mask, seg[b], q1 - q0, L)
-        o[q0:q1], lse[q0:q1] = attention(q[q0:q1], k, v, sm_scale, causal, m)
+        qb, k = _rotate(q[q0:q1], k, L, rope)
+        o[q0:q1], lse[q0:q1] = attention(qb, k, v, sm_scale, causal, m)
     return o, lse
 
 
 def ragged_attention(q, k_rows, k_sf, v_rows, v_sf, kv_indptr, qo_indptr, sm_scale,
-                     causal=False, k_global=1.0, v_global=1.0, kv_dtype="nvfp4"):
+                     causal=False, k_global=1.0, v_global=1.0, kv_dtype="nvfp4", rope=None):
     """Batched attention over ragged (non-paged) K/V: request b's keys are rows
     kv_indptr[b] .. kv_indptr[b+1]-1 of k_rows / v_rows [rows, Hkv, W] (and of the
-    scale arrays for NVFP4).  Returns O [sum q_b, Hq, Dv] and LSE [sum q_b, Hq]."""
+    scale arrays for NVFP4); ``rope`` as in ``paged_attention``.  Returns
+    O [sum q_b, Hq, Dv] and LSE [sum q_b, Hq]."""
     q = np.asarray(q, dtype=np.float64)
     nq, hq, _ = q.shape
     dv = np.asarray(v_rows).shape[-1] * (2 if kv_dtype == "nvfp4" else 1)
@@ -338,7 +391,8 @@ def ragged_attention(q, k_rows, k_sf, v_rows, v_sf, kv_indptr, qo_indptr, sm_sca
                           np.asarray(k_sf)[a0:a1], k_global, kv_dtype)
         v = dequantize_kv(np.asarray(v_rows)[a0:a1], None if v_sf is None else
                           np.asarray(v_sf)[a0:a1], v_global, kv_dtype)
-        o[q0:q1], lse[q0:q1] = attention(q[q0:q1], k, v, sm_scale, causal)
+        qb, k = _rotate(q[q0:q1], k, a1 - a0, rope)
+        o[q0:q1], lse[q0:q1] = attention(qb, k, v, sm_scale, causal)
     return o, lse
 
 
