@@ -15,7 +15,7 @@ import numpy as np
 import torch
 
 from ._lib import (EXPORTS, KV_DTYPES, STATUS, WORK_FIELDS, KVPoolStruct, KVRaggedStruct,
-                   NVFP4Error, PlanInfoStruct, PlanOptionsStruct, check, lib)
+                   POS_ENCODINGS, NVFP4Error, PlanInfoStruct, PlanOptionsStruct, check, lib)
 
 __all__ = ["KVPool", "RaggedKV", "Plan", "Prepared", "quantize_kv", "batch_decode",
            "batch_decode_noalloc", "batch_decode_append", "batch_prefill", "batch_prefill_masked",
@@ -250,12 +250,15 @@ class Plan:
                  qo_indptr: Optional[Sequence[int]] = None, causal: bool = False,
                  kv_chunk_tokens: int = 0, num_cus: int = 0, device=None,
                  kv_dtype: str = "nvfp4", kv_indptr: Optional[Sequence[int]] = None,
-                 custom_mask: bool = False):
+                 custom_mask: bool = False, rope_theta: Optional[float] = None,
+                 rope_scale: float = 1.0):
         """``num_cus`` 0 fills the compute units of ``device`` (default: the current
         device when a GPU is present, else the library's default of 256).  ``kv_dtype``:
         the pools' type ("nvfp4" or "fp8"); ``kv_indptr``: ragged (non-paged) prefill KV
         rows per request; ``custom_mask``: runs take a packed mask in place of the causal
-        rule (nvfp4_plan_create_ex)."""
+        rule; ``rope_theta``: the prefill kernels apply the rotary embedding (base
+        ``rope_theta``, positions divided by ``rope_scale``) to Q and K
+        (nvfp4_plan_create_ex)."""
         head_dim_vo = head_dim_qk if head_dim_vo is None else head_dim_vo
         if kv_dtype not in KV_DTYPES:
             raise ValueError(f"kv_dtype must be one of {sorted(KV_DTYPES)}, got {kv_dtype!r}")
@@ -264,6 +267,7 @@ class Plan:
             np.asarray(kv_indptr, dtype=np.int32))
         self.ragged = kv_indptr is not None
         self.custom_mask = bool(custom_mask)
+        self.rope = None if rope_theta is None else (float(rope_theta), float(rope_scale))
         if num_cus == 0 and torch.cuda.is_available():
             num_cus = torch.cuda.get_device_properties(
                 torch.device("cuda") if device is None else torch.device(device)
@@ -281,7 +285,9 @@ class Plan:
         self.causal = causal
         opts = PlanOptionsStruct(KV_DTYPES[kv_dtype], None if self._kvind is None
                                  else self._kvind.ctypes.data_as(ctypes.c_void_p).value,
-                                 int(self.custom_mask))
+                                 int(self.custom_mask),
+                                 POS_ENCODINGS["none" if self.rope is None else "rope"],
+                                 *(self.rope or (0.0, 0.0)))
         check(lib.nvfp4_plan_create_ex(
             self._kv.ctypes.data_as(ctypes.c_void_p) if self.batch else None,
             self._ind.ctypes.data_as(ctypes.c_void_p) if self._ind is not None else None,

@@ -62,7 +62,11 @@ KV_DTYPES = {"nvfp4": 0, "fp8": 1}
 
 class PlanOptionsStruct(ctypes.Structure):
     _fields_ = [("kv_dtype", ctypes.c_int32), ("kv_indptr", ctypes.c_void_p),
-                ("custom_mask", ctypes.c_int32)]
+                ("custom_mask", ctypes.c_int32), ("pos_encoding", ctypes.c_int32),
+                ("rope_theta", ctypes.c_float), ("rope_scale", ctypes.c_float)]
+
+
+POS_ENCODINGS = {"none": 0, "rope": 1}  # nvfp4_pos_encoding
 
 
 class KVRaggedStruct(ctypes.Structure):

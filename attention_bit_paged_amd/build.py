@@ -16,7 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libnvfp4_attn.so")
-SOURCES = ["api.cpp", "quantize.hip", "merge.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "merge.hip", "decode.hip", "prefill.hip",
+           "prefill_rope.hip"]
 ARCH = "gfx950"
 
 
@@ -36,7 +37,8 @@ def flags():
 # Per-file extras.  MFMA accumulators in ordinary VGPRs, so the softmax can rescale
 # them in place instead of copying them out of AGPRs every step.
 EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-         "prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+         "prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+         "prefill_rope.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str) -> str:

@@ -190,6 +190,8 @@ struct nvfp4_plan {
   std::vector<int32_t> kv_starts;  // ragged: first row of each request
   std::vector<int32_t> ragged_pt;  // ragged: the 16-row "pages" of each request
   int ragged_pt_stride = 0;
+  int rope = 0;            // prefill with in-kernel RoPE
+  std::vector<float> rope_freq;  // (hi, lo) of w_i / (2 pi) per pair i < Dk/2
   int chunk = 0;           // chunk length used when splitting (0: no split)
   int rows_per_item = 0;   // decode: 16 heads; prefill: rows of a tile
   int rows_per_slot = 0;
@@ -200,7 +202,7 @@ struct nvfp4_plan {
   int num_partials = 0;
   // workspace layout (byte offsets)
   size_t off_work = 0, off_merge = 0, off_kvlens = 0, off_indptr = 0, off_pt = 0, off_mask = 0,
-         off_part_o = 0, off_part_lse = 0, ws_bytes = 0;
+         off_rope = 0, off_part_o = 0, off_part_lse = 0, ws_bytes = 0;
   std::vector<uint8_t> image;  // the tables as they sit at the start of the workspace
   void* uploaded_to = nullptr;
   int defer_merge = 0;  // runs leave split rows' partials for nvfp4_merge_partials
@@ -231,6 +233,22 @@ nvfp4_status nvfp4_plan_create_ex(const int32_t* kv_lens, const int32_t* qo_indp
   const int kv_dtype = options ? options->kv_dtype : NVFP4_KV_NVFP4;
   const int32_t* kv_indptr = options ? options->kv_indptr : nullptr;
   const bool custom_mask = options && options->custom_mask;
+  const int pos_encoding = options ? options->pos_encoding : NVFP4_POS_NONE;
+  if (pos_encoding != NVFP4_POS_NONE && pos_encoding != NVFP4_POS_ROPE)
+    return fail(NVFP4_E_INVALID, "options.pos_encoding %d is neither none (0) nor RoPE (1)",
+                pos_encoding);
+  const bool rope = pos_encoding == NVFP4_POS_ROPE;
+  if (rope) {
+    if (!qo_indptr)
+      return fail(NVFP4_E_UNSUPPORTED, "in-kernel RoPE runs in the prefill kernels: qo_indptr "
+                  "must be given");
+    if (custom_mask)
+      return fail(NVFP4_E_UNSUPPORTED, "in-kernel RoPE is not combined with custom masks");
+    if (!(options->rope_theta > 0.f) || !std::isfinite(options->rope_theta) ||
+        !(options->rope_scale > 0.f) || !std::isfinite(options->rope_scale))
+      return fail(NVFP4_E_INVALID, "rope_theta %g and rope_scale %g must be positive and finite",
+                  (double)options->rope_theta, (double)options->rope_scale);
+  }
   if (custom_mask && !qo_indptr)
     return fail(NVFP4_E_SHAPE, "a custom mask is a prefill mask: qo_indptr must be given");
   if (custom_mask && kv_indptr)
@@ -292,6 +310,9 @@ nvfp4_status nvfp4_plan_create_ex(const int32_t* kv_lens, const int32_t* qo_indp
 
   for (int b = 0; b < batch; ++b) {
     if (kv_lens[b] < 0) return fail(NVFP4_E_INVALID, "kv_lens[%d] = %d is negative", b, kv_lens[b]);
+    if (rope && kv_lens[b] > (1 << 24))
+      return fail(NVFP4_E_UNSUPPORTED, "kv_lens[%d] = %d: in-kernel RoPE takes positions below "
+                  "2^24", b, kv_lens[b]);
   }
   int64_t total_q = batch;
   if (prefill) {
@@ -363,6 +384,23 @@ nvfp4_status nvfp4_plan_create_ex(const int32_t* kv_lens, const int32_t* qo_indp
     for (int b = 0; b < batch; ++b)
       for (int i = 0; i < maxp; ++i)
         plan->ragged_pt[(size_t)b * maxp + i] = kv_indptr[b] + 16 * std::min(i, std::max(0, (kv_lens[b] + 15) / 16 - 1));
+  }
+  if (rope) {
+    // w_i = theta^(-2i/Dk) / scale, in turns per position, split into a float pair
+    // whose sum carries it to about 48 bits (the kernels reduce pos * w_i to a fraction
+    // of a turn with it)
+    plan->rope = 1;
+    const int half = head_dim_qk / 2;
+    plan->rope_freq.resize(2 * (size_t)half);
+    const double two_pi = 6.283185307179586476925286766559;
+    for (int i = 0; i < half; ++i) {
+      const double w = std::pow((double)options->rope_theta, -2.0 * i / head_dim_qk) /
+                       (double)options->rope_scale;
+      const double f = w / two_pi;
+      const float hi = (float)f;
+      plan->rope_freq[2 * i] = hi;
+      plan->rope_freq[2 * i + 1] = (float)(f - (double)hi);
+    }
   }
   plan->total_q = total_q;
   plan->kv_lens.assign(kv_lens, kv_lens + batch);
@@ -487,6 +525,8 @@ nvfp4_status nvfp4_plan_create_ex(const int32_t* kv_lens, const int32_t* qo_indp
   off = align_up(off + plan->ragged_pt.size() * sizeof(int32_t));
   plan->off_mask = off;  // custom-mask plans: the requests' segment offsets
   off = align_up(off + plan->mask_off.size() * sizeof(int64_t));
+  plan->off_rope = off;  // RoPE plans: the frequency pairs
+  off = align_up(off + plan->rope_freq.size() * sizeof(float));
   plan->off_part_o = off;
   off = align_up(off + (size_t)plan->num_partials * plan->rows_per_slot * head_dim_vo * sizeof(float));
   plan->off_part_lse = off;
@@ -505,6 +545,9 @@ nvfp4_status nvfp4_plan_create_ex(const int32_t* kv_lens, const int32_t* qo_indp
   if (!plan->mask_off.empty())
     std::memcpy(plan->image.data() + plan->off_mask, plan->mask_off.data(),
                 plan->mask_off.size() * sizeof(int64_t));
+  if (!plan->rope_freq.empty())
+    std::memcpy(plan->image.data() + plan->off_rope, plan->rope_freq.data(),
+                plan->rope_freq.size() * sizeof(float));
   *out = plan;
   return ok();
 }
@@ -674,6 +717,7 @@ AttnArgs make_args(const nvfp4_plan* plan, const void* q, int64_t q_s_row, int64
   // heads within 256 bytes of each other share cache lines / DRAM bursts: keep the
   // heads of one key range on one XCD (decode)
   a.xcd_group = !plan->prefill && (std::min(k->stride_head, v->stride_head) <= 256);
+  a.rope = plan->rope ? reinterpret_cast<const float*>(w + plan->off_rope) : nullptr;
   return a;
 }
 

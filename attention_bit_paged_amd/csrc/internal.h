@@ -68,6 +68,10 @@ struct AttnArgs {
   // into them (device, from the workspace).
   const uint8_t* mask;
   const int64_t* mask_off;
+  // Prefill with in-kernel RoPE (else null): per pair i < Dk/2 of head-dim elements
+  // (i, i + Dk/2), the float pair (hi, lo) with hi + lo = w_i / (2 pi) (device, from
+  // the workspace).
+  const float* rope;
   // Decode with append: the step's new K/V rows (bf16 [batch, kv heads, dim], element
   // strides), quantised into the slot of token kv_len-1 of their request by the work
   // item that ends there; k_new is null when the call appends nothing.
@@ -129,6 +133,9 @@ int decode_wgs_per_cu(int dk, int dv, int fmt);
 size_t decode_lds_bytes(int dk, int dv, int page_size, int fmt);
 hipError_t launch_prefill(int dk, int dv, int fmt, int page_shift, const AttnArgs& a,
                           hipStream_t stream);
+// The rotary (a.rope) instantiations of launch_prefill's kernels.
+hipError_t launch_prefill_rope(int dk, int dv, int fmt, int page_shift, const AttnArgs& a,
+                               hipStream_t stream);
 bool prefill_supported(int dk, int dv, int fmt);
 int prefill_rows_per_item(int dk, int dv, int group, int page_size);
 // Prefill workgroups one CU runs at once for this shape.

@@ -1,960 +1,10 @@
-// Paged NVFP4 prefill / extend: causal or full attention of a tile of query rows
-// against a chunk of the paged cache.
-//
-// [PF] "Re-enable split-KV for NVFP4 KV cache in prefill path": the paged prefill
-// path with in-kernel NVFP4 dequantisation, asymmetric head dims (commit on
-// (qk, vo) = (512, 256): output sized by VO), causal runs, and prefix-cache extend
-// where a short query attends a long cached prefix (commit "Gate split-KV off...").
-// The causal mask is aligned to the end of the keys: query row i of a request with
-// q_b queries and L_b keys sees keys j <= i + L_b - q_b.
-//
-// A work item is one workgroup of four waves: (request b, kv head g, query tile,
-// chunk [kv0, kv1)).  The tile's rows are (query, qo head of the group) pairs, query
-// major, so the heads that share a kv head share every K/V byte read.
-//
-// Cooperative kernel (page_size >= 16, head dims up to 256): the workgroup streams
-// the chunk in 32-token steps.  The raw packed bytes of a step arrive in a shared LDS
-// ring by direct global-to-LDS copies (each wave issues one pool's copies, three
-// steps deep); the four waves then dequantise the step together into fp16 MFMA
-// operands, stored lane-major in an LDS operand buffer (double-buffered, one barrier
-// per step), and every wave computes its groups of 16 rows from those operands, held
-// in registers for the step (three groups per wave for head dims up to 128).  The K/V
-// dequantisation and the LDS reads are thus shared by all rows of the tile.
-//
-// Register kernel (any page size, any head dims): each wave owns its rows and loads
-// and dequantises every step itself, the next step's bytes held in registers.
-//
-// A split tile's partial states are merged by a separate kernel.
-#include <type_traits>
+// Host side of the paged prefill: the shapes with kernels, their LDS and tile sizes,
+// and the launch (RoPE launches are built in prefill_rope.hip).
+#include <algorithm>
 
-#include "kv_ring.h"
+#include "prefill_kernels.h"
 
 namespace nvfp4 {
-
-namespace {
-
-// Operand registers of the wide-head (DK = 512) cooperative kernel's LDS read pipeline:
-// reads run this many k-steps (V tiles) less one ahead of their products (3 and 5
-// measured alike, 7 slower).
-constexpr int kWidePrefetch = 3;
-
-template <int DK>
-constexpr int prefill_nr() {
-  return DK >= 512 ? 1 : 2;
-}
-
-// page_size < 16: every token is looked up on its own (PagedView::load).
-template <int DK, int DV, int FMT = kNvfp4>
-__global__ __launch_bounds__(256) void prefill_regs_kernel(AttnArgs a) {
-  using S = StepShape<DK, DV, FMT>;
-  constexpr int NR = prefill_nr<DK>();
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int j = lane >> 4;
-  const int n = lane & 15;
-  const int32_t* rec = a.work + (int64_t)blockIdx.x * kWorkFields;
-  const int b = rec[W_REQ], kvh = rec[W_KVH], q0 = rec[W_ROW0], qn = rec[W_ROWS];
-  const int kv0 = rec[W_KV0], kv1 = rec[W_KV1], slot = rec[W_SLOT];
-  const int G = a.group;
-  const int R = qn * G;
-  const int row_base = wave * NR * 16;
-  const bool wave_has_rows = row_base < R;  // uniform; rowless waves still meet the barriers
-  const int qstart = a.qo_indptr[b];
-  const int qlen = a.qo_indptr[b + 1] - qstart;
-  const int off = a.kv_lens[b] - qlen;
-
-  f16x8 qf[NR][S::NS];
-  float sc[NR];
-  int last[NR];
-  bool rv[NR];
-  int64_t tokrow[NR];
-  int headi[NR];
-#pragma unroll
-  for (int rg = 0; rg < NR; ++rg) {
-    const int r = row_base + rg * 16 + n;
-    rv[rg] = r < R;
-    const int qi = r / G;
-    const int gh = r - qi * G;
-    const int qpos = q0 + qi;
-    tokrow[rg] = (int64_t)qstart + qpos;
-    headi[rg] = kvh * G + gh;
-    last[rg] = a.causal ? min(kv1 - 1, qpos + off) : kv1 - 1;
-    sc[rg] = a.score_scale *
-             load_q_operand<DK>(a.q + tokrow[rg] * a.q_s_row + (int64_t)headi[rg] * a.q_s_head,
-                                rv[rg], j, qf[rg]);
-  }
-  // keys this wave needs: up to the last visible key of its last valid row
-  int wave_end = wave_has_rows ? kv1 : kv0;
-  if (a.causal && wave_has_rows) {
-    const int r_last = min(R - 1, row_base + NR * 16 - 1);
-    wave_end = min(kv1, q0 + r_last / G + off + 1);
-  }
-  // steps that may hold a masked key: the chunk's tail and, for causal rows, any step
-  // past the first visible-key limit of the wave's first row (every step with a custom
-  // mask)
-  int mask_from = kv1 - kDecodeStep;
-  if (a.causal) mask_from = min(mask_from, q0 + row_base / G + off + 1 - kDecodeStep);
-  const bool custom = a.mask != nullptr;  // uniform
-  const uint8_t* mseg = custom ? a.mask + a.mask_off[b] : nullptr;
-  const int64_t kv_len = a.kv_lens[b];
-
-  PagedView<DK, DV, false, FMT> view;
-  view.init(a, b, kvh, lane);
-  const int tlast = kv1 - 1;
-
-  RowState<S::NT, AccForm::PLAIN> st[NR];
-#pragma unroll
-  for (int rg = 0; rg < NR; ++rg) st[rg].init();
-
-  auto step = [&](const StepRaw<DK, DV, FMT>& r, int t0) {
-    f16x8 ka[S::NS], kb[S::NS];
-    k_operands<DK, DV, FMT>(r, ka, kb);
-    const bool masked = t0 > mask_from;
-    f16x8 p[NR];
-#pragma unroll
-    for (int rg = 0; rg < NR; ++rg) {
-      f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < S::NS; ++s) {
-        sa = mfma16x16x32(ka[s], qf[rg][s], sa);
-        sb = mfma16x16x32(kb[s], qf[rg][s], sb);
-      }
-      if (custom) {
-        const int key0 = t0 + 8 * j;
-        const int qpos = q0 + (row_base + rg * 16 + n) / G;
-        const uint32_t vis = rv[rg] ? mask_bits8(mseg, kv_len, qpos, key0, tlast - key0 + 1) : 0u;
-        p[rg] = st[rg].softmax_vis(sa, sb, sc[rg], vis);
-      } else {
-        p[rg] = masked ? st[rg].template softmax<true>(sa, sb, sc[rg], t0, j, last[rg])
-                       : st[rg].template softmax<false>(sa, sb, sc[rg], t0, j, last[rg]);
-      }
-    }
-    f16x8 vt[S::NT];
-    if (t0 + kDecodeStep > kv1)
-      v_operands<DK, DV, true, FMT>(r, t0, tlast, j, vt);
-    else
-      v_operands<DK, DV, false, FMT>(r, t0, tlast, j, vt);
-#pragma unroll
-    for (int rg = 0; rg < NR; ++rg) st[rg].pv(vt, p[rg]);
-  };
-
-  StepRaw<DK, DV, FMT> r0, r1;
-  if (kv0 < wave_end) view.load(r0, kv0, tlast);
-  for (int t0 = kv0; t0 < wave_end; t0 += 2 * kDecodeStep) {
-    const int t1 = t0 + kDecodeStep;
-    if (t1 < wave_end) view.load(r1, t1, tlast);
-    step(r0, t0);
-    if (t1 >= wave_end) break;
-    if (t1 + kDecodeStep < wave_end) view.load(r0, t1 + kDecodeStep, tlast);
-    step(r1, t1);
-  }
-
-  const bool bad = __any(view.bad != 0);
-  if (slot < 0) {
-    if (wave_has_rows) {
-#pragma unroll
-      for (int rg = 0; rg < NR; ++rg)
-        st[rg].store(a.o + tokrow[rg] * a.o_s_row + (int64_t)headi[rg] * a.o_s_head,
-                     a.lse + tokrow[rg] * a.num_qo_heads + headi[rg], rv[rg], bad, a.out_scale, j);
-    }
-    return;
-  }
-  if (wave_has_rows) {
-#pragma unroll
-    for (int rg = 0; rg < NR; ++rg) {
-      const int r = row_base + rg * 16 + n;
-      st[rg].store(a.part_o + ((int64_t)slot * a.rows_per_slot + r) * DV,
-                   a.part_lse + (int64_t)slot * a.rows_per_slot + r, rv[rg], bad, a.out_scale, j);
-    }
-  }
-}
-
-// ------------------------------------------------------------------ cooperative --
-
-template <int DK, int DV, int FMT = kNvfp4>
-struct CoopShape {
-  using S = StepShape<DK, DV, FMT>;
-  static constexpr bool OK = (DK <= 256 && DV <= 256) || (DK == 512 && DV <= 256);
-  // Head dims up to 128: four waves of three row groups, two workgroups per CU (two
-  // waves per SIMD hide each other's latencies, and the two workgroups' barriers are
-  // independent); up to 256: four waves of two row groups, one wave per SIMD.
-  static constexpr bool SMALL = DK <= 128 && DV <= 128;
-  // DK = 512: the K operands of a step (a quarter of the register file) are read one
-  // k-step at a time and the V operands one tile at a time; eight waves of one row
-  // group each, two per SIMD, so that one wave's LDS reads overlap the other's products.
-  static constexpr bool WIDE = DK > 256;
-  static constexpr int NW = WIDE ? 8 : 4;
-  static constexpr int NR = SMALL ? 3 : (WIDE ? 1 : 2);  // row groups of 16 per wave
-  static constexpr int WGS_PER_CU = SMALL ? 2 : 1;
-  static constexpr int ROWS = NW * NR * 16;       // rows per work item
-  static constexpr int NOP = 2 * S::NS + S::NT;   // operand vectors per step
-  static constexpr int OPB = NOP * 64 * 16;       // bytes of one operand buffer
-  static constexpr int RAW_STAGE = RingBytes<DK, DV, FMT>::STAGE;  // a step's K/V bytes
-  static constexpr int WL = 3 * RAW_STAGE;
-  using R = RingShape<DK, DV, WL, FMT>;           // three raw stages
-  // A step's custom-mask bytes: 8 per tile query (two 4-byte copies of 64 lanes per
-  // block of 64 queries; a tile has at most ROWS queries), in a ring of four slots of
-  // their own: the copies of step s land in slot s % 4 three steps ahead, and that slot
-  // is written again only after step s's softmax, so the step reads its bits directly.
-  static constexpr int MASK_BLOCKS = (ROWS + 63) / 64;
-  static constexpr int MASK_SLOT = MASK_BLOCKS * 512;
-  static constexpr int LDS = 3 * RAW_STAGE + 2 * OPB;  // without the mask ring
-  static constexpr int LDS_MASKED = LDS + 4 * MASK_SLOT;
-  static constexpr int KE = (2 * S::NS + NW - 1) / NW;  // K operand entries per lane
-  static constexpr int VH = NW / 4;               // V tiles split in this many parts
-  static constexpr int VPART = S::NT / VH;        // V tiles per part
-  static_assert(R::NST == 3, "raw ring depth");
-  static_assert(S::NT % VH == 0, "V split");
-};
-
-constexpr int kLdsPerCu = 160 * 1024;
-
-// LDS of one cooperative workgroup: three raw stages of 32 tokens (rows and, for NVFP4,
-// scale rows) and two fp16 operand buffers (2 NS K entries and NT V tiles of 64 lanes x
-// 16 bytes).  A formula, so that shapes without a kernel can be priced too.
-constexpr int coop_lds_formula(int dk, int dv, int fmt, bool masked) {
-  const int rbk = fmt == kFp8 ? dk : dk / 2, rbv = fmt == kFp8 ? dv : dv / 2;
-  const int sf = fmt == kFp8 ? 0 : (2 * dk + 2 * dv + 255) / 256 * 256;
-  const int rows = dk <= 128 && dv <= 128 ? 192 : 128;  // tile rows (queries at most)
-  const int raw = 32 * (rbk + rbv) + sf;
-  const int opb = (2 * (dk / 32) + dv / 16) * 64 * 16;
-  return 3 * raw + 2 * opb + (masked ? 4 * ((rows + 63) / 64 * 512) : 0);
-}
-constexpr int coop_wgs_per_cu(int dk, int dv) { return dk <= 128 && dv <= 128 ? 2 : 1; }
-
-// Per-lane LDS offsets of the cooperative dequantisation (constant for the kernel).
-// Operand o < 2*NS is K tile o/NS (token tile A or B), k-step o%NS; operand 2*NS + e is
-// V^T tile e.  Entry (o, lane) is the 16 bytes lane `lane` loads for operand o.  K
-// entries: wave w makes entries (w + NW*r, lane).  V: lane L of the workgroup makes,
-// for the operand lane c = L / (4*VH), the token pair p = L%4 of the V tiles of part
-// (L/4)%VH.
-template <int DK, int DV, int FMT = kNvfp4>
-struct CoopLanes {
-  using S = StepShape<DK, DV, FMT>;
-  using C = CoopShape<DK, DV, FMT>;
-  using R = typename C::R;
-  // Entry r of a lane is operand wave + NW*r.  NW divides NS (or a lane has one entry),
-  // so entry r lies a fixed distance from entry 0 in the raw stage and in the operand
-  // buffer: one per-lane base per pool, the rest immediate offsets of the LDS accesses.
-  static_assert(S::NS % C::NW == 0 || C::KE == 1, "K entry spacing");
-  static constexpr uint32_t k_raw_off(int r) {
-    return (C::NW * r) / S::NS * 4 * S::RBK + S::KSTEP * ((C::NW * r) % S::NS);
-  }
-  static constexpr uint32_t k_sc_off(int r) {
-    return (C::NW * r) / S::NS * 4 * S::SBK + ((C::NW * r) % S::NS) / 2;
-  }
-  static constexpr uint32_t k_dst_off(int r) { return C::NW * r * 64 * 16; }
-  uint32_t k_raw, k_sc, k_dst;  // entry 0
-  uint32_t v_raw, v_sc, v_dst;
-  int v_tok, part;
-
-  __device__ __forceinline__ void init(int wave, int lane) {
-    const int j = lane >> 4, n = lane & 15;
-    const int o = min(wave, 2 * S::NS - 1);  // clamped: unused when past the end
-    const int tile = o / S::NS, s = o % S::NS;
-    const int k_tok = 8 * (n >> 2) + (n & 3) + 4 * tile;
-    k_raw = R::OFF_KD + k_tok * S::RBK + j * S::KB + S::KSTEP * s;
-    k_sc = R::OFF_SF + k_tok * S::SBK + j * S::KSF + (s >> 1);
-    k_dst = (o * 64 + lane) * 16;
-    const int L = wave * 64 + lane;
-    const int c = L / (4 * C::VH), p = L & 3;
-    part = (L >> 2) % C::VH;
-    const int jj = c >> 4, m = c & 15;
-    v_tok = 8 * jj + 2 * p;
-    v_raw = R::OFF_VD + v_tok * S::RBV + m * S::VB;
-    v_sc = R::OFF_SF + R::KS + v_tok * S::SBV + (m * (DV / 16)) / 16;
-    v_dst = (2 * S::NS * 64 + c) * 16 + 4 * p;
-  }
-};
-
-// The cooperative dequantisation of one raw stage: load() reads this lane's raw bytes
-// and scales, store() writes its fp16 operand entries.  MASK: value rows past `kleft`
-// (tokens of the step after the chunk's last key) get scale 0, so that their bytes,
-// whatever they hold (NaN scales included), dequantise to finite zeros: a NaN there
-// would reach every output through its zero probability.  Key rows past the end are
-// left as they are: a bad key row only spoils its own scores, which the softmax of a
-// step that holds such keys replaces by -inf.
-template <int DK, int DV, int FMT = kNvfp4>
-struct CoopRaw {
-  using S = StepShape<DK, DV, FMT>;
-  using C = CoopShape<DK, DV, FMT>;
-  static constexpr int NB = S::VB < 4 ? S::VB : 4;   // bytes of the V slice per dword
-  static constexpr int EPD = S::F8 ? NB : 2 * NB;    // V tiles per slice dword
-  static constexpr int KW = S::KSTEP / 4;            // dwords of one K entry
-  uint32_t kw[C::KE][KW], ksc[C::KE], sa, sb, vw0[S::VW], vw1[S::VW];
-
-  __device__ __forceinline__ void load(uint32_t raw, int wave, const CoopLanes<DK, DV, FMT>& cl) {
-#pragma unroll
-    for (int r = 0; r < C::KE; ++r) {
-      // wave-uniform; always true when the K entries divide evenly among the waves
-      if ((2 * S::NS) % C::NW == 0 || wave + C::NW * r < 2 * S::NS) {
-        lds_load<S::KSTEP>(raw + cl.k_raw + cl.k_raw_off(r), kw[r]);
-        if constexpr (!S::F8) lds_load<1>(raw + cl.k_sc + cl.k_sc_off(r), &ksc[r]);
-      }
-    }
-    if constexpr (!S::F8) {
-      const uint32_t vs = raw + cl.v_sc;
-      lds_load<1>(vs, &sa);
-      lds_load<1>(vs + DV / 16, &sb);
-    }
-    const uint32_t vr = raw + cl.v_raw;
-#pragma unroll
-    for (int q = 0; q < S::VW; ++q) {
-      if (C::VH > 1 && C::VPART >= EPD && (q * EPD) / C::VPART != cl.part) continue;
-      lds_load<NB>(vr + 4 * q, &vw0[q]);
-      lds_load<NB>(vr + S::RBV + 4 * q, &vw1[q]);
-    }
-  }
-  template <bool MASK>
-  __device__ __forceinline__ void store(uint32_t opb, int wave, const CoopLanes<DK, DV, FMT>& cl,
-                                        int kleft);
-};
-
-template <int DK, int DV, int FMT>
-template <bool MASK>
-__device__ __forceinline__ void CoopRaw<DK, DV, FMT>::store(uint32_t opb, int wave,
-                                                            const CoopLanes<DK, DV, FMT>& cl,
-                                                            int kleft) {
-  typedef __attribute__((address_space(3))) uint8_t* lds_p;
-#pragma unroll
-  for (int r = 0; r < C::KE; ++r) {
-    if ((2 * S::NS) % C::NW == 0 || wave + C::NW * r < 2 * S::NS) {
-      f16x8 v;
-      if constexpr (S::F8)
-        v = fp8x8_to_f16(kw[r][0], kw[r][1]);
-      else
-        v = dequant8(kw[r][0], splat_lo(fp8x2_to_f16<false>(ksc[r])));
-      *(__attribute__((address_space(3))) f16x8*)(lds_p)(size_t)(opb + cl.k_dst + cl.k_dst_off(r)) = v;
-    }
-  }
-  const uint32_t vd = opb + cl.v_dst;
-  if constexpr (S::F8) {
-    // value rows past the chunk's last key read as zero bytes; the byte transposition
-    // pairs tokens v_tok and v_tok + 1 for each element (see v_operands_fp8)
-#pragma unroll
-    for (int q = 0; q < S::VW; ++q) {
-      if (C::VH > 1 && C::VPART >= EPD && (q * EPD) / C::VPART != cl.part) continue;
-      const uint32_t w0 = MASK && cl.v_tok > kleft ? 0u : vw0[q];
-      const uint32_t w1 = MASK && cl.v_tok + 1 > kleft ? 0u : vw1[q];
-      const uint32_t lo = __builtin_amdgcn_perm(w1, w0, 0x05010400u);
-      const uint32_t hi = __builtin_amdgcn_perm(w1, w0, 0x07030602u);
-#pragma unroll
-      for (int k = 0; k < EPD; ++k) {
-        if (C::VH > 1 && C::VPART < EPD && k / C::VPART != cl.part) continue;
-        const f16x2 v = k == 0 ? fp8x2_to_f16<false>(lo)
-                               : (k == 1 ? fp8x2_to_f16<true>(lo)
-                                         : (k == 2 ? fp8x2_to_f16<false>(hi) : fp8x2_to_f16<true>(hi)));
-        *(__attribute__((address_space(3))) uint32_t*)(lds_p)(size_t)(vd + (EPD * q + k) * 1024) =
-            f16x2_bits(v);
-      }
-    }
-    return;
-  } else {
-  if (MASK && cl.v_tok > kleft) sa = 0;
-  if (MASK && cl.v_tok + 1 > kleft) sb = 0;
-  const f16x2 sp = fp8x2_to_f16<false>(sa | (sb << 8));
-#pragma unroll
-  for (int q = 0; q < S::VW; ++q) {
-    // a part covers VPART consecutive tiles: whole dwords, or a share of one
-    if (C::VH > 1 && C::VPART >= EPD && (q * EPD) / C::VPART != cl.part) continue;
-    const uint32_t w0 = vw0[q], w1 = vw1[q];
-    // byte k of lo: nibble 2k of token ta (low) and of token ta+1 (high); hi: nibble 2k+1
-    const uint32_t lo = (w0 & 0x0F0F0F0Fu) | ((w1 << 4) & 0xF0F0F0F0u);
-    const uint32_t hi = ((w0 >> 4) & 0x0F0F0F0Fu) | (w1 & 0xF0F0F0F0u);
-#pragma unroll
-    for (int k = 0; k < EPD; ++k) {
-      const int e = EPD * q + k;
-      if (C::VH > 1 && C::VPART < EPD && k / C::VPART != cl.part) continue;
-      const uint32_t src = (k & 1) ? hi : lo;
-      f16x2 v;
-      switch (k >> 1) {
-        case 0: v = fp4x2_to_f16<0>(src); break;
-        case 1: v = fp4x2_to_f16<1>(src); break;
-        case 2: v = fp4x2_to_f16<2>(src); break;
-        default: v = fp4x2_to_f16<3>(src); break;
-      }
-      v = v * sp;
-      *(__attribute__((address_space(3))) uint32_t*)(lds_p)(size_t)(vd + e * 1024) = f16x2_bits(v);
-    }
-  }
-  }
-}
-
-// Dequantises the raw stage at `raw` into the operand buffer at `opb`.  MASK: value rows
-// past `kleft` get scale 0.  Every raw read first: the operand stores may not move above
-// them (the compiler cannot tell the raw stage from the operand buffer).
-template <int DK, int DV, bool MASK, int FMT>
-__device__ __forceinline__ void coop_dequant(uint32_t raw, uint32_t opb, int wave,
-                                             const CoopLanes<DK, DV, FMT>& cl, int kleft) {
-  CoopRaw<DK, DV, FMT> r;
-  r.load(raw, wave, cl);
-  r.template store<MASK>(opb, wave, cl, kleft);
-}
-
-// Waits until this wave's copies of all but the newest issued step are done (or all
-// of them).  Waves 0..3 each copy one pool; the others copy nothing.
-// Wave 3 also copies the custom-mask bytes, two copies per block of 64 tile queries:
-// `mask_copies` of them per step (0, 2, 4 or 6; wave-uniform).
-template <int DK, int DV, int FMT>
-__device__ __forceinline__ void coop_wait(int wave, bool one_newer, int mask_copies) {
-  using R = typename CoopShape<DK, DV, FMT>::R;
-  constexpr int N0 = R::ndma(1), N1 = R::ndma(2), N2 = R::ndma(4), N3 = R::ndma(8);
-  if (wave > 3) return;
-  if (!one_newer) {
-    asm volatile("s_waitcnt vmcnt(0)");
-  } else if (wave == 0) {
-    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N0));
-  } else if (wave == 1) {
-    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N1));
-  } else if (wave == 2) {
-    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N2));
-  } else if (mask_copies == 0) {
-    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N3));
-  } else if (mask_copies == 2) {
-    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N3 + 2));
-  } else if (mask_copies == 4) {
-    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N3 + 4));
-  } else {
-    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N3 + 6));
-  }
-}
-
-// The custom-mask copies of a tile: lane l of block qb carries tile query 64 qb + l.
-// A query's bits of the keys of a step start 4 bytes further on in every step (32 keys),
-// at a fixed bit shift, so its copies take the step's base (scalar) plus a fixed
-// per-lane byte offset; lanes past the tile's queries copy the tile's first query's
-// bytes instead (unused).
-struct CoopMask {
-  const uint8_t* seg;  // the request's mask segment
-  uint32_t voff[3];    // byte offset of this lane's query at the chunk's first key
-  int blocks;          // blocks of 64 tile queries (uniform)
-  uint32_t ring;       // LDS address of the mask ring (uniform)
-};
-
-// The copy offsets of the one pool this wave issues (wave 0: K data, 1: V data, 2 and 3:
-// the scale bytes, whose copies carry both pools' lanes).  The full plan holds every
-// pool's offsets; kept whole in each wave they cost registers the loop needs.
-template <int DK, int DV, int FMT = kNvfp4>
-struct CoopCopies {
-  using R = RingShape<DK, DV, CoopShape<DK, DV, FMT>::WL, FMT>;
-  using Plan = RingPlan<DK, DV, CoopShape<DK, DV, FMT>::WL, FMT>;
-  static constexpr int MAXC = R::N_KD > R::N_VD ? (R::N_KD > R::N_SF ? R::N_KD : R::N_SF)
-                                                : (R::N_VD > R::N_SF ? R::N_VD : R::N_SF);
-  uint32_t mine[MAXC > 0 ? MAXC : 1];
-
-  __device__ __forceinline__ void init(const Plan& rp, int wave) {
-#pragma unroll
-    for (int c = 0; c < MAXC; ++c) {
-      const uint32_t kd = c < R::N_KD ? rp.off[c] : 0u;
-      const uint32_t vd = c < R::N_VD ? rp.off[R::N_KD + c] : 0u;
-      const uint32_t sf = c < R::N_SF ? rp.off[R::N_KD + R::N_VD + c] : 0u;
-      mine[c] = wave == 0 ? kd : (wave == 1 ? vd : sf);
-    }
-  }
-  // a plan holding this wave's offsets in the places of pool P (1, 2, 4 or 8) and zeros
-  // (never read for P) elsewhere
-  template <int P>
-  __device__ __forceinline__ Plan expand() const {
-    Plan r;
-    constexpr int first = P == 1 ? 0 : (P == 2 ? R::N_KD : R::N_KD + R::N_VD);
-    constexpr int count = P == 1 ? R::N_KD : (P == 2 ? R::N_VD : R::N_SF);
-#pragma unroll
-    for (int c = 0; c < R::NCOPY; ++c)
-      r.off[c] = (c >= first && c < first + count) ? mine[c - first] : 0u;
-    return r;
-  }
-};
-
-template <int DK, int DV, int FMT, bool CMASK>
-__device__ __forceinline__ void coop_issue(int wave, const CoopCopies<DK, DV, FMT>& cc,
-                                           uint32_t stage, const PagedView<DK, DV, true, FMT>& view,
-                                           int t0, int tlast, uint32_t& bad, const CoopMask& cm,
-                                           int kv0) {
-  using C = CoopShape<DK, DV, FMT>;
-  constexpr int WL = C::WL;
-  if (wave == 0) ring_issue<DK, DV, WL, 1>(cc.template expand<1>(), stage, view, t0, tlast, bad);
-  else if (wave == 1) ring_issue<DK, DV, WL, 2>(cc.template expand<2>(), stage, view, t0, tlast, bad);
-  else if constexpr (!StepShape<DK, DV, FMT>::F8) {  // FP8 has no scale pools
-    if (wave == 2) ring_issue<DK, DV, WL, 4>(cc.template expand<4>(), stage, view, t0, tlast, bad);
-    else if (wave == 3) ring_issue<DK, DV, WL, 8>(cc.template expand<8>(), stage, view, t0, tlast, bad);
-  }
-  if (CMASK && wave == 3) {
-    const uint8_t* base = cm.seg + ((t0 - kv0) >> 3);  // 4 bytes per 32-key step
-    const uint32_t slot = cm.ring + (((t0 - kv0) >> 5) & 3) * C::MASK_SLOT;
-#pragma unroll
-    for (int qb = 0; qb < C::MASK_BLOCKS; ++qb) {
-      if (qb < cm.blocks) {
-        dma<false>(slot + qb * 512, cm.voff[qb], base);
-        dma<false>(slot + qb * 512 + 256, cm.voff[qb] + 4, base);
-      }
-    }
-  }
-}
-
-// This lane's visibility bits of keys t0 + 8j .. t0 + 8j + 7 for the query of its row
-// `row` (tile-local), from the step's slot of the mask ring; keys after tlast hidden.
-template <int DK, int DV, int FMT>
-__device__ __forceinline__ uint32_t coop_mask_bits(const CoopMask& cm, int row, int j, int G,
-                                                   int q0, int64_t kv_len, int kv0, int t0,
-                                                   int tlast) {
-  using C = CoopShape<DK, DV, FMT>;
-  const int nvalid = tlast - (t0 + 8 * j) + 1;
-  const uint32_t keep = nvalid <= 0 ? 0u : (nvalid >= 8 ? 0xFFu : (1u << nvalid) - 1u);
-  const int ql = min(row / G, C::MASK_BLOCKS * 64 - 1);  // rows past the tile are not stored
-  const uint32_t at = cm.ring + (((t0 - kv0) >> 5) & 3) * C::MASK_SLOT + (ql >> 6) * 512 +
-                      (ql & 63) * 4;
-  uint32_t lo, hi;
-  lds_load<4>(at, &lo);
-  lds_load<4>(at + 256, &hi);
-  const int sh = (int)(((int64_t)(q0 + ql) * kv_len + kv0) & 7) + 8 * j;
-  const uint64_t v = ((uint64_t)hi << 32) | lo;
-  return ((uint32_t)(v >> sh) & 0xFFu) & keep;
-}
-
-// Q quarter-row multiplied by the score factor c (the scores then leave the product in
-// base-2 exponent units) and rounded to fp16, relative error at most 2^-12 per
-// element.  Returns false when the row could overflow fp16 (|q c| >= 2^15, or not
-// finite): the caller then takes the exact prescaled form of load_q_operand.
-template <int DK>
-__device__ __forceinline__ bool load_q_scaled(const uint16_t* qrow, bool valid, int j, float c,
-                                              f16x8 (&qf)[DK / 32]) {
-  constexpr int QW = DK / 8;
-  uint32_t qraw[QW];
-  if (valid) {
-    load_bytes<DK / 2>(reinterpret_cast<const uint8_t*>(qrow + j * (DK / 4)), qraw);
-  } else {
-#pragma unroll
-    for (int i = 0; i < QW; ++i) qraw[i] = 0u;
-  }
-  float qmax = 0.f;
-#pragma unroll
-  for (int i = 0; i < QW; ++i)
-    qmax = fmaxf(qmax, fmaxf(fabsf(bf16f(qraw[i] & 0xFFFF)), fabsf(bf16f(qraw[i] >> 16))));
-#pragma unroll
-  for (int s = 0; s < DK / 32; ++s) {
-    f16x2 p[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const uint32_t w = qraw[4 * s + t];
-      p[t] = f16x2{(_Float16)(bf16f(w & 0xFFFF) * c), (_Float16)(bf16f(w >> 16) * c)};
-    }
-    qf[s] = pack8(p[0], p[1], p[2], p[3]);
-  }
-  return qmax * c < 32768.f;
-}
-
-// Softmax with the reference point inside the product (head dims up to 256).  Q carries
-// the score factor, and each row group's QK accumulators start at -r, where r is the
-// row's reference point (0 while the row has seen no key): the products then give
-// x = c s - r directly and p = exp2(x), without a multiply-add per score.  A row moves
-// its reference when its largest x passes the slack, and at its first visible key: in
-// a step whose keys every row sees (no mask) that can only be the item's first step,
-// where every row moves; a masked step also moves rows that have no reference yet.
-struct ShiftRef {
-  f32x4 negr;
-  __device__ __forceinline__ void init() { negr = f32x4{0.f, 0.f, 0.f, 0.f}; }
-};
-
-// Under a wave-uniform branch taken when some lane of the group voted (see ShiftRef):
-// moves the reference of the rows whose largest score passed the slack, or that had
-// none, rescales their accumulators and row sums, and shifts this step's x to the new
-// reference.
-template <int NT>
-__device__ __forceinline__ void raise_shifted(RowState<NT, AccForm::VGPR>& st, ShiftRef& sr,
-                                              float bm, float (&x)[8]) {
-  const float r = -sr.negr[0];
-  const float bmr = max_over_groups(bm) + r;  // the row's largest c s
-  const bool up = bmr > st.m + kRescaleSlack;
-  const float m_new = up ? bmr : st.m;
-  const float alpha = up ? fast_exp2(st.m - m_new) : 1.f;  // 0 when m was -inf
-#pragma unroll
-  for (int e = 0; e < NT; e += 4)
-    scale16(st.acc[e], st.acc[e + 1], st.acc[e + 2], st.acc[e + 3], alpha);
-  st.l *= alpha;
-  st.m = m_new;
-  const float r_new = m_new == -INFINITY ? 0.f : m_new;
-  const float d = r_new - r;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) x[i] -= d;
-  sr.negr = f32x4{-r_new, -r_new, -r_new, -r_new};
-}
-
-// P = exp2(x) in fp16 and the lane's row sum of those fp16 values.
-template <int NT>
-__device__ __forceinline__ f16x8 probs_shifted(RowState<NT, AccForm::VGPR>& st, const float (&x)[8]) {
-  f16x2 pp[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    pp[i] = f16x2{(_Float16)fast_exp2(x[2 * i]), (_Float16)fast_exp2(x[2 * i + 1])};
-  const f16x2 one2 = {(_Float16)1.f, (_Float16)1.f};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) st.l = __builtin_amdgcn_fdot2(pp[i], one2, st.l, false);
-  return pack8(pp[0], pp[1], pp[2], pp[3]);
-}
-
-// CMASK: the launch carries a custom mask (AttnArgs::mask); a separate instantiation,
-// so that the unmasked kernel holds none of its state.
-template <int DK, int DV, int FMT, bool CMASK>
-__global__ __launch_bounds__((CoopShape<DK, DV, FMT>::NW * 64))
-__attribute__((amdgpu_waves_per_eu(CoopShape<DK, DV, FMT>::WGS_PER_CU)))
-void prefill_coop_kernel(AttnArgs a) {
-  using S = StepShape<DK, DV, FMT>;
-  using C = CoopShape<DK, DV, FMT>;
-  constexpr int NR = C::NR;
-  constexpr int WL = 3 * C::RAW_STAGE;
-  static_assert(C::OK, "shape has no cooperative kernel");
-  constexpr int LDS = CMASK ? C::LDS_MASKED : C::LDS;
-  static_assert(LDS == coop_lds_formula(DK, DV, FMT, CMASK) &&
-                C::WGS_PER_CU == coop_wgs_per_cu(DK, DV), "LDS formula");
-  static_assert(LDS * C::WGS_PER_CU <= kLdsPerCu, "resident workgroups exceed the LDS");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS];
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int j = lane >> 4;
-  const int n = lane & 15;
-  const int32_t* rec = a.work + (int64_t)blockIdx.x * kWorkFields;
-  const int b = rec[W_REQ], kvh = rec[W_KVH], q0 = rec[W_ROW0], qn = rec[W_ROWS];
-  const int kv0 = rec[W_KV0], kv1 = rec[W_KV1], slot = rec[W_SLOT];
-  const int G = a.group;
-  const int Rn = qn * G;
-  const int row_base = wave * NR * 16;
-  const int qstart = a.qo_indptr[b];
-  const int qlen = a.qo_indptr[b + 1] - qstart;
-  const int off = a.kv_lens[b] - qlen;
-
-  f16x8 qf[NR][S::NS];
-  float sc[NR];
-  bool rv[NR];
-  int64_t tokrow[NR];
-  int headi[NR];
-  // keys the tile needs: up to the last visible key of its last row
-  const int tile_end = a.causal ? min(kv1, q0 + (Rn - 1) / G + off + 1) : kv1;
-  const int tlast = kv1 - 1;
-  const int nsteps = tile_end > kv0 ? (tile_end - kv0 + kDecodeStep - 1) / kDecodeStep : 0;
-
-  PagedView<DK, DV, true, FMT> view;
-  view.init(a, b, kvh, lane);
-  CoopCopies<DK, DV, FMT> cc;
-  {
-    RingPlan<DK, DV, WL, FMT> rp;
-    rp.init(lane, view.k_tok, view.v_tok, view.ksf_tok, view.vsf_tok);
-    cc.init(rp, wave);
-  }
-  const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
-  const uint32_t raw0 = lds0, opb0 = lds0 + 3 * C::RAW_STAGE;
-  // custom mask (the plan tiles the whole key range then: every step is masked)
-  constexpr bool custom = CMASK;
-  const int64_t kv_len = a.kv_lens[b];
-  CoopMask cm;
-  cm.seg = nullptr;
-  cm.blocks = 0;
-  cm.ring = opb0 + 2 * C::OPB;
-  if constexpr (CMASK) {
-    cm.seg = a.mask + a.mask_off[b];
-    cm.blocks = (qn + 63) / 64;
-#pragma unroll
-    for (int qb = 0; qb < C::MASK_BLOCKS; ++qb) {
-      const int ql = qb * 64 + lane < qn ? qb * 64 + lane : 0;
-      cm.voff[qb] = (uint32_t)(((int64_t)(q0 + ql) * kv_len + kv0) >> 3);
-    }
-  }
-  CoopLanes<DK, DV, FMT> cl;
-  cl.init(wave, lane);
-  uint32_t bad = 0;
-
-  // The first three steps' copies go out before Q is read, so that the two memory
-  // latencies of a work item's start overlap.
-  for (int i = 0; i < 3 && i < nsteps; ++i)
-    coop_issue<DK, DV, FMT, CMASK>(wave, cc, raw0 + i * C::RAW_STAGE, view, kv0 + i * kDecodeStep,
-                                   tlast, bad, cm, kv0);
-  // Head dims up to 256: Q carries the score factor (see ShiftRef) unless some row of
-  // the wave could overflow fp16; that wave then takes the exact prescaled Q.
-  bool safe = true;
-#pragma unroll
-  for (int rg = 0; rg < NR; ++rg) {
-    const int r = row_base + rg * 16 + n;
-    rv[rg] = r < Rn;
-    const int qi = r / G;
-    const int gh = r - qi * G;
-    const int qpos = q0 + qi;
-    tokrow[rg] = (int64_t)qstart + qpos;
-    headi[rg] = kvh * G + gh;
-    const uint16_t* qrow = a.q + tokrow[rg] * a.q_s_row + (int64_t)headi[rg] * a.q_s_head;
-    if constexpr (C::WIDE)
-      sc[rg] = a.score_scale * load_q_operand<DK>(qrow, rv[rg], j, qf[rg]);
-    else
-      safe = load_q_scaled<DK>(qrow, rv[rg], j, a.score_scale, qf[rg]) && safe;
-  }
-  const bool shifted = !C::WIDE && __all(safe);
-  if (!C::WIDE && !shifted) {
-#pragma unroll
-    for (int rg = 0; rg < NR; ++rg)
-      sc[rg] = a.score_scale *
-               load_q_operand<DK>(a.q + tokrow[rg] * a.q_s_row + (int64_t)headi[rg] * a.q_s_head,
-                                  rv[rg], j, qf[rg]);
-  }
-
-  // One wave per SIMD (wide heads): the Q operands are only ever MFMA sources, so they
-  // are kept in AGPRs, leaving the VGPRs to the accumulators and the step's operands.
-  // Two waves per SIMD: everything fits the 256 VGPRs of a wave.
-  if constexpr (C::WGS_PER_CU == 1) {
-#pragma unroll
-    for (int rg = 0; rg < NR; ++rg)
-#pragma unroll
-      for (int s = 0; s < S::NS; ++s) asm volatile("" : "+a"(qf[rg][s]));
-  }
-
-  RowState<S::NT, AccForm::VGPR> st[NR];
-  ShiftRef sr[NR];
-#pragma unroll
-  for (int rg = 0; rg < NR; ++rg) {
-    st[rg].init();
-    sr[rg].init();
-  }
-
-  auto t_of = [&](int i) { return kv0 + i * kDecodeStep; };
-  // the last key row group rg may see; recomputed in the (few) masked steps rather than
-  // held in registers for the whole loop
-  auto last_of = [&](int rg) {
-    const int qpos = q0 + (row_base + rg * 16 + n) / G;
-    return a.causal ? min(kv1 - 1, qpos + off) : kv1 - 1;
-  };
-  // One step: wait for the next raw step, refill the ring, dequantise the next step
-  // and compute this one.  MASK: some key of the step is past some row's limit.
-  auto step = [&](int i, auto mask_tag, auto shift_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    constexpr bool SHIFT = decltype(shift_tag)::value && !C::WIDE;
-    const bool next = i + 1 < nsteps;
-    // raw step i+1 landed (only step i+2 may still be in flight); operands of step i
-    // are visible; nobody reads operand buffer (i+1)%2 or raw stage i%3 any more
-    if (next) coop_wait<DK, DV, FMT>(wave, i + 2 < nsteps, 2 * cm.blocks);
-    __syncthreads();
-    if (i + 3 < nsteps)
-      coop_issue<DK, DV, FMT, CMASK>(wave, cc, raw0 + (i % 3) * C::RAW_STAGE, view, t_of(i + 3),
-                                     tlast, bad, cm, kv0);
-    // Stage and buffer bases as single scalars: left to itself the compiler folds the
-    // modulo's parts into every lane address separately (two vector adds per address).
-    const uint32_t ob = __builtin_amdgcn_readfirstlane(opb0 + (i & 1) * C::OPB);
-    const int t0 = t_of(i);
-    const uint32_t obl = ob + lane * 16;  // this lane's entry of operand 0
-    const uint32_t rs = __builtin_amdgcn_readfirstlane(raw0 + ((i + 1) % 3) * C::RAW_STAGE);
-    const uint32_t ob1 = __builtin_amdgcn_readfirstlane(opb0 + ((i + 1) & 1) * C::OPB);
-    if constexpr (C::WIDE) {
-      if (next) {
-        if (t_of(i + 1) + kDecodeStep - 1 > tlast)
-          coop_dequant<DK, DV, true, FMT>(rs, ob1, wave, cl, tlast - t_of(i + 1));
-        else
-          coop_dequant<DK, DV, false, FMT>(rs, ob1, wave, cl, 0);
-      }
-      f32x4 sa[NR], sb[NR];
-#pragma unroll
-      for (int rg = 0; rg < NR; ++rg) {
-        sa[rg] = f32x4{0.f, 0.f, 0.f, 0.f};
-        sb[rg] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-      // K operands PF - 1 k-steps ahead of their products, the order pinned by
-      // scheduling groups: left to itself the compiler moves every read next to its
-      // product (three operand registers instead of PF) and each pair of products
-      // then waits for the LDS.
-      constexpr int PF = kWidePrefetch;
-      static_assert(NR == 1, "one row group per wave");
-      f16x8 ka[PF], kb[PF];
-      auto kload = [&](int s) {
-        lds_load<16>(obl + s * 1024, reinterpret_cast<uint32_t*>(&ka[s % PF]));
-        lds_load<16>(obl + (S::NS + s) * 1024, reinterpret_cast<uint32_t*>(&kb[s % PF]));
-      };
-      __builtin_amdgcn_s_setprio(1);  // the QK products first, as below
-#pragma unroll
-      for (int s = 0; s < PF - 1; ++s) kload(s);
-#pragma unroll
-      for (int s = 0; s < S::NS; ++s) {
-        if (s + PF - 1 < S::NS) kload(s + PF - 1);
-        sa[0] = mfma16x16x32(ka[s % PF], qf[0][s], sa[0]);
-        sb[0] = mfma16x16x32(kb[s % PF], qf[0][s], sb[0]);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (PF - 1), 0);
-#pragma unroll
-      for (int s = 0; s < S::NS; ++s) {
-        if (s + PF - 1 < S::NS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      }
-      __builtin_amdgcn_s_setprio(0);
-      f16x8 p;
-      if (MASK && custom)
-        p = st[0].softmax_vis(sa[0], sb[0], sc[0],
-                              coop_mask_bits<DK, DV, FMT>(cm, row_base + n, j, G, q0, kv_len, kv0,
-                                                          t0, tlast));
-      else
-        p = st[0].template softmax<MASK>(sa[0], sb[0], sc[0], t0, j, MASK ? last_of(0) : 0);
-      f16x8 vt[PF];
-      auto vload = [&](int e) {
-        lds_load<16>(obl + (2 * S::NS + e) * 1024, reinterpret_cast<uint32_t*>(&vt[e % PF]));
-      };
-#pragma unroll
-      for (int e = 0; e < PF - 1; ++e) vload(e);
-#pragma unroll
-      for (int e = 0; e < S::NT; ++e) {
-        if (e + PF - 1 < S::NT) vload(e + PF - 1);
-        st[0].acc[e] = mfma16x16x32(vt[e % PF], p, st[0].acc[e]);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, PF - 1, 0);
-#pragma unroll
-      for (int e = 0; e < S::NT; ++e) {
-        if (e + PF - 1 < S::NT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      }
-      return;
-    }
-    // Two straight-line blocks.  The first reads this step's K operands and the next
-    // step's raw bytes, forms S = K Q^T for every row group and dequantises the next
-    // step beside those products (on the last step: a stale stage, into the operand
-    // buffer nobody reads any more), then takes each row group's largest score.  The
-    // rare rescale sits between the blocks; the second forms P and O^T += V^T P^T for
-    // every row group, each group's PV products beside the next group's exponentials.
-    f16x8 ka[S::NS], kb[S::NS], vt[S::NT];
-    // This block at raised wave priority: of the two workgroups sharing a SIMD, the
-    // wave that is issuing its QK products goes first and the other wave's softmax and
-    // PV work fills the matrix unit's gaps (about 4 % faster than equal priorities;
-    // raising the PV block as well, or the barrier and copy issue, gained nothing).
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int s = 0; s < S::NS; ++s) {
-      lds_load<16>(obl + s * 1024, reinterpret_cast<uint32_t*>(&ka[s]));
-      lds_load<16>(obl + (S::NS + s) * 1024, reinterpret_cast<uint32_t*>(&kb[s]));
-    }
-    CoopRaw<DK, DV, FMT> raw;
-    raw.load(rs, wave, cl);
-    f32x4 sa[NR], sb[NR];
-#pragma unroll
-    for (int rg = 0; rg < NR; ++rg) {
-      sa[rg] = SHIFT ? sr[rg].negr : f32x4{0.f, 0.f, 0.f, 0.f};
-      sb[rg] = sa[rg];
-#pragma unroll
-      for (int s = 0; s < S::NS; ++s) {
-        sa[rg] = mfma16x16x32(ka[s], qf[rg][s], sa[rg]);
-        sb[rg] = mfma16x16x32(kb[s], qf[rg][s], sb[rg]);
-      }
-    }
-    raw.template store<true>(ob1, wave, cl, tlast - t_of(i + 1));
-    __builtin_amdgcn_s_setprio(0);
-#pragma unroll
-    for (int e = 0; e < S::NT; ++e)
-      lds_load<16>(obl + (2 * S::NS + e) * 1024, reinterpret_cast<uint32_t*>(&vt[e]));
-    float x[NR][8], bm[NR];
-    const bool first = i == 0;  // uniform
-    auto vote = [&](int rg) -> bool {
-      if constexpr (SHIFT)
-        return first || bm[rg] > kRescaleSlack || (MASK && st[rg].m == -INFINITY);
-      else
-        return st[rg].wants(bm[rg], sc[rg]);
-    };
-    uint64_t want = 0;  // the groups' votes, combined as wave masks on the scalar unit
-#pragma unroll
-    for (int rg = 0; rg < NR; ++rg) {
-      if (MASK && custom)
-        bm[rg] = st[rg].scores_vis(sa[rg], sb[rg],
-                                   coop_mask_bits<DK, DV, FMT>(cm, row_base + rg * 16 + n, j, G, q0,
-                                                               kv_len, kv0, t0, tlast),
-                                   x[rg]);
-      else
-        bm[rg] = st[rg].template scores<MASK>(sa[rg], sb[rg], t0, j, MASK ? last_of(rg) : 0, x[rg]);
-      want |= __ballot(vote(rg));
-    }
-    if (want != 0) {
-#pragma unroll
-      for (int rg = 0; rg < NR; ++rg) {
-        if (__ballot(vote(rg)) != 0) {
-          if constexpr (SHIFT)
-            raise_shifted(st[rg], sr[rg], bm[rg], x[rg]);
-          else
-            st[rg].raise(bm[rg], sc[rg]);
-        }
-      }
-    }
-#pragma unroll
-    for (int rg = 0; rg < NR; ++rg) {
-      const f16x8 p = SHIFT ? probs_shifted(st[rg], x[rg]) : st[rg].template probs<MASK>(x[rg], sc[rg]);
-      st[rg].pv(vt, p);
-    }
-    // order of the second block: group 0's P, then one PV product of group g to a share
-    // of group g+1's P (16 VALU instructions a group shifted, 24 otherwise), then the
-    // last group's products
-    constexpr int PV_VALU = SHIFT ? 2 : 3;
-    __builtin_amdgcn_sched_group_barrier(0x002, SHIFT ? 16 : 20, 0);
-#pragma unroll
-    for (int rg = 1; rg < NR; ++rg)
-#pragma unroll
-      for (int e = 0; e < S::NT; ++e) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, PV_VALU, 0);
-      }
-    __builtin_amdgcn_sched_group_barrier(0x008, S::NT, 0);
-  };
-  // prologue: three steps in flight (issued above), step 0 dequantised
-  if (nsteps > 0) {
-    coop_wait<DK, DV, FMT>(wave, false, 2 * cm.blocks);
-    __syncthreads();
-    coop_dequant<DK, DV, true, FMT>(raw0, opb0, wave, cl, tlast - t_of(0));
-  }
-  // steps whose 32 keys are visible to every row of the tile, then the rest
-  const int tile_min_last = a.causal ? min(kv1 - 1, q0 + off) : kv1 - 1;
-  const int n_full = custom ? 0 : min(nsteps, max(0, (tile_min_last - kv0 + 1) / kDecodeStep));
-  int i = 0;
-  if (shifted) {
-    for (; i < n_full; ++i) step(i, std::false_type{}, std::true_type{});
-    for (; i < nsteps; ++i) step(i, std::true_type{}, std::true_type{});
-  } else {
-    for (; i < n_full; ++i) step(i, std::false_type{}, std::false_type{});
-    for (; i < nsteps; ++i) step(i, std::true_type{}, std::false_type{});
-  }
-
-  const bool badw = __any(bad != 0);
-  // the four waves saw different copies: any bad page poisons the whole tile
-  __shared__ uint32_t bad_flag;
-  if (threadIdx.x == 0) bad_flag = 0;
-  __syncthreads();
-  if (badw && lane == 0) atomicOr(&bad_flag, 1u);
-  __syncthreads();
-  const bool bad_any = bad_flag != 0;
-  if (row_base >= Rn) return;
-#pragma unroll
-  for (int rg = 0; rg < NR; ++rg) {
-    if (slot < 0) {
-      st[rg].store(a.o + tokrow[rg] * a.o_s_row + (int64_t)headi[rg] * a.o_s_head,
-                   a.lse + tokrow[rg] * a.num_qo_heads + headi[rg], rv[rg], bad_any, a.out_scale, j);
-    } else {
-      const int r = row_base + rg * 16 + n;
-      st[rg].store(a.part_o + ((int64_t)slot * a.rows_per_slot + r) * DV,
-                   a.part_lse + (int64_t)slot * a.rows_per_slot + r, rv[rg], bad_any, a.out_scale, j);
-    }
-  }
-}
-
-template <int DK, int DV, int FMT>
-hipError_t launch_dk_dv(int page_shift, const AttnArgs& a, hipStream_t stream) {
-  const dim3 grid(a.n_work);
-  if (page_shift >= 4 && a.mask)
-    launch_attention(prefill_coop_kernel<DK, DV, FMT, true>, grid,
-                     dim3(CoopShape<DK, DV, FMT>::NW * 64), stream, a);
-  else if (page_shift >= 4)
-    launch_attention(prefill_coop_kernel<DK, DV, FMT, false>, grid,
-                     dim3(CoopShape<DK, DV, FMT>::NW * 64), stream, a);
-  else
-    launch_attention(prefill_regs_kernel<DK, DV, FMT>, grid, dim3(256), stream, a);
-  return hipGetLastError();
-}
-
-}  // namespace
-
-// Shapes with kernels: NVFP4 at every (qk, vo) pair of 64..512 with vo <= qk except
-// 512/512; FP8 at head dims up to 256 (the 512/256 FP8 tile needs more LDS than a CU
-// has, and the narrower 512-dim FP8 shapes are not built).
-#define NVFP4_PREFILL_SHAPES(X)                                                     \
-  X(64, 64, kNvfp4) X(128, 64, kNvfp4) X(128, 128, kNvfp4) X(256, 64, kNvfp4)      \
-  X(256, 128, kNvfp4) X(256, 256, kNvfp4) X(512, 64, kNvfp4) X(512, 128, kNvfp4)   \
-  X(512, 256, kNvfp4) X(64, 64, kFp8) X(128, 64, kFp8) X(128, 128, kFp8)           \
-  X(256, 64, kFp8) X(256, 128, kFp8) X(256, 256, kFp8)
-
 bool prefill_supported(int dk, int dv, int fmt) {
 #define NVFP4_PREFILL_CASE(K, V, F) \
   if (dk == K && dv == V && fmt == F) return true;
@@ -972,22 +22,23 @@ int prefill_rows_per_item(int dk, int dv, int /*group*/, int page_size) {
 }
 
 size_t prefill_lds_bytes(int dk, int dv, int page_size, int fmt) {
-  if (page_size < 16) return 0;  // the register kernel uses no LDS
-  // the resident workgroups of the cooperative kernel (its custom-mask form, the larger),
-  // also for shapes without one
-  return (size_t)coop_lds_formula(dk, dv, fmt, true) * coop_wgs_per_cu(dk, dv);
+  // the register kernel's only LDS is the RoPE frequency table
+  if (page_size < 16) return (size_t)4 * dk;
+  // the resident workgroups of the cooperative kernel (its larger form: custom-mask or
+  // RoPE), also for shapes without one
+  const int most = std::max(coop_lds_formula(dk, dv, fmt, true), coop_lds_formula(dk, dv, fmt, false, true));
+  return (size_t)most * coop_wgs_per_cu(dk, dv);
 }
 
 hipError_t launch_prefill(int dk, int dv, int fmt, int page_shift, const AttnArgs& a,
                           hipStream_t stream) {
   if (a.n_work <= 0) return hipSuccess;
+  if (a.rope) return launch_prefill_rope(dk, dv, fmt, page_shift, a, stream);
 #define NVFP4_PREFILL_CASE(K, V, F) \
-  if (dk == K && dv == V && fmt == F) return launch_dk_dv<K, V, F>(page_shift, a, stream);
+  if (dk == K && dv == V && fmt == F) return launch_dk_dv<K, V, F, false>(page_shift, a, stream);
   NVFP4_PREFILL_SHAPES(NVFP4_PREFILL_CASE)
 #undef NVFP4_PREFILL_CASE
   return hipErrorInvalidValue;
 }
-
-#undef NVFP4_PREFILL_SHAPES
 
 }  // namespace nvfp4

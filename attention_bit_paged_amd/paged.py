@@ -87,13 +87,17 @@ def build_case(w: synth.Workload, device="cuda", layout="HND", poison=True,
     return PagedCase(w, q, k, v, k_pool, v_pool, torch.from_numpy(pt).to(device), pt, slots, ind)
 
 
-def make_plan(case: PagedCase, num_cus: int = 0, kv_chunk_tokens: Optional[int] = None) -> Plan:
+def make_plan(case: PagedCase, num_cus: int = 0, kv_chunk_tokens: Optional[int] = None,
+              rope: Optional[tuple] = None) -> Plan:
+    """The case's plan; ``rope`` = (theta, scale) turns on the in-kernel rotary (prefill)."""
     w = case.w
     chunk = w.kv_chunk_tokens if kv_chunk_tokens is None else kv_chunk_tokens
+    theta, scale = rope if rope is not None else (None, 1.0)
     return Plan(w.kv_lens, num_qo_heads=w.num_qo_heads, num_kv_heads=w.num_kv_heads,
                 head_dim_qk=w.head_dim_qk, head_dim_vo=w.head_dim_vo, page_size=w.page_size,
                 qo_indptr=None if w.decode else case.qo_indptr.tolist(), causal=w.causal,
-                kv_chunk_tokens=chunk, num_cus=num_cus, kv_dtype=case.k_pool.dtype)
+                kv_chunk_tokens=chunk, num_cus=num_cus, kv_dtype=case.k_pool.dtype,
+                rope_theta=theta, rope_scale=scale)
 
 
 @dataclasses.dataclass
@@ -131,10 +135,12 @@ def build_ragged_case(w: synth.Workload, device="cuda", dtype: str = "nvfp4",
 
 
 def make_ragged_plan(case: RaggedCase, num_cus: int = 0,
-                     kv_chunk_tokens: Optional[int] = None) -> Plan:
+                     kv_chunk_tokens: Optional[int] = None, rope: Optional[tuple] = None) -> Plan:
     w = case.w
     chunk = w.kv_chunk_tokens if kv_chunk_tokens is None else kv_chunk_tokens
+    theta, scale = rope if rope is not None else (None, 1.0)
     return Plan(w.kv_lens, num_qo_heads=w.num_qo_heads, num_kv_heads=w.num_kv_heads,
                 head_dim_qk=w.head_dim_qk, head_dim_vo=w.head_dim_vo,
                 qo_indptr=case.qo_indptr.tolist(), kv_indptr=case.kv_indptr.tolist(),
-                causal=w.causal, kv_chunk_tokens=chunk, num_cus=num_cus, kv_dtype=case.k.dtype)
+                causal=w.causal, kv_chunk_tokens=chunk, num_cus=num_cus, kv_dtype=case.k.dtype,
+                rope_theta=theta, rope_scale=scale)

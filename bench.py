@@ -504,6 +504,41 @@ def masked_prefill_line(torch, nv, paged, synth, iters=60, warm=12, pool_sets=3)
     return out
 
 
+def rope_prefill_lines(torch, nv, paged, synth, iters=40, warm=10, pool_sets=3):
+    """Prefill with in-kernel RoPE (base 1e4) beside the same workload without it, both
+    measured the same way; flops count the QK and PV products of the visible pairs only
+    (the rotations are extra vector work on the same pairs)."""
+    out = []
+    for name in ("prefill_extend", "asym_prefill"):
+        w = synth.workload(name)
+        cases = [paged.build_case(w, keep_sources=False) for _ in range(pool_sets)]
+        line = {"workload": name, "rope_theta": 1e4, "flops": w.flops()}
+        for label, rope in (("plain", None), ("rope", (1e4, 1.0))):
+            plan = paged.make_plan(cases[0], rope=rope)
+            plan.set_deferred_merge(True)
+            ws = plan.new_workspace()
+            plan.upload(ws)
+            o = torch.empty((w.total_q, w.num_qo_heads, w.head_dim_vo), device="cuda")
+            lse = torch.empty((w.total_q, w.num_qo_heads), device="cuda")
+            run = [nv.batch_prefill(plan, c.q, c.page_table, c.k_pool, c.v_pool, w.sm_scale, ws,
+                                    out=o, lse=lse, prepare=True) for c in cases]
+            merge = nv.merge_partials(plan, ws, o, lse, prepare=True)
+            for i in range(warm):
+                run[i % len(run)]()
+                merge()
+            run_ms, merge_ms = timed_passes(torch, nv, run, merge, iters)
+            rate = w.flops() / run_ms / 1e9
+            line[label] = {"kernel_TFLOPs": round(rate, 2),
+                           "kernel_frac_mfma_f16": round(rate / MFMA_F16_PEAK_TFLOPS, 4),
+                           "attn_ms": round(run_ms, 4), "merge_ms": round(merge_ms, 4)}
+            del run, merge, ws
+        line["rope_vs_plain"] = round(line["plain"]["attn_ms"] / line["rope"]["attn_ms"], 4)
+        out.append(line)
+        del cases
+        torch.cuda.empty_cache()
+    return out
+
+
 def stream_ceiling(torch, nv, plan, cases, ws, iters, kv_bytes, attn_ms):
     """What the decode access pattern sustains without the attention arithmetic: the
     checksum kernel (nvfp4_kv_checksum) streams the same plan's KV bytes through the same
@@ -963,6 +998,7 @@ def main():
                                   for n in ("batch_decode", "prefill_extend")]
         out["kv_types"] = kv_type_lines(torch, nv, paged, synth)
         out["masked_prefill"] = masked_prefill_line(torch, nv, paged, synth)
+        out["rope_prefill"] = rope_prefill_lines(torch, nv, paged, synth)
     print(json.dumps(out), flush=True)
 
 

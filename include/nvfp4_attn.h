@@ -175,11 +175,31 @@ nvfp4_status nvfp4_plan_create(const int32_t* kv_lens, const int32_t* qo_indptr,
  *   custom_mask: prefill (paged KV) whose visibility a packed custom mask decides in
  *              place of the causal rule (nvfp4_batch_prefill_masked); the plan then
  *              tiles every request's whole key range.
+ *   pos_encoding: nvfp4_pos_encoding.  NVFP4_POS_ROPE: the prefill kernels rotate Q and
+ *              the dequantised K in registers before the QK product ([PF] commit
+ *              "Address CodeRabbit review on flashinfer-ai#3684 (5 findings)", item
+ *              init_rope_freq: in-kernel RoPE whose frequency table spans half the QK
+ *              head dim, also where the VO head dim is smaller).  Rotate-half form:
+ *              element i < Dk/2 of a row and element i + Dk/2 turn together by
+ *              pos * w_i, w_i = rope_theta^(-2i/Dk) / rope_scale.  Key j of a request
+ *              sits at position j (the cache holds un-rotated keys), query row i of a
+ *              request with q_b queries and L_b keys at L_b - q_b + i.  Prefill plans
+ *              (paged or ragged) only; not with custom_mask (NVFP4_E_UNSUPPORTED for
+ *              either), and every kv_len must be at most 2^24 (positions are exact
+ *              floats).  V is never rotated.
+ *   rope_theta, rope_scale: > 0 and finite when pos_encoding is NVFP4_POS_ROPE
+ *              (NVFP4_E_INVALID otherwise); ignored else.
+ * A zero-initialised options struct is the plain paged NVFP4 plan.
  */
+typedef enum { NVFP4_POS_NONE = 0, NVFP4_POS_ROPE = 1 } nvfp4_pos_encoding;
+
 typedef struct {
   int32_t kv_dtype;
   const int32_t* kv_indptr;
   int32_t custom_mask;  /* nonzero: runs take a packed custom mask (nvfp4_batch_prefill_masked) */
+  int32_t pos_encoding; /* nvfp4_pos_encoding */
+  float rope_theta;
+  float rope_scale;
 } nvfp4_plan_options;
 
 /* nvfp4_plan_create with options (NULL options = nvfp4_plan_create). */
@@ -335,6 +355,9 @@ nvfp4_status nvfp4_set_timing_events(void* start_event, void* stop_event);
  *   q: device bf16 [total_q, num_qo_heads, head_dim_qk] ragged by the plan's
  *      qo_indptr; o: device fp32 [total_q, num_qo_heads, head_dim_vo];
  *   lse: device fp32 [total_q, num_qo_heads] contiguous.
+ * A plan made with options.pos_encoding = NVFP4_POS_ROPE applies the rotary embedding
+ * to Q and K in the kernels (also nvfp4_batch_prefill_ragged); the rotated rows are
+ * never stored.
  * Other arguments as for nvfp4_batch_decode.
  */
 nvfp4_status nvfp4_batch_prefill(const nvfp4_plan* plan, const void* q, int64_t q_stride_tok,

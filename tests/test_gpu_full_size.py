@@ -41,7 +41,7 @@ def sample_pairs(w: synth.Workload, seed: int, frac: float = SAMPLE_FRACTION):
     return sorted(pick)
 
 
-def _oracle_pairs(case, o, lse, samples, record, causal=False):
+def _oracle_pairs(case, o, lse, samples, record, causal=False, rope=None):
     """Compare O/LSE of the sampled (request, kv head) pairs with the oracle; returns
     the largest O error over them."""
     w = case.w
@@ -59,7 +59,7 @@ def _oracle_pairs(case, o, lse, samples, record, causal=False):
         o_ref, lse_ref = ref.paged_attention(
             qs, head(kd, h), head(ks, h), head(vd, h), head(vs, h),
             case.page_table_np, w.kv_lens, ind, w.page_size, w.sm_scale, causal, "HND",
-            rows=[b], kv_dtype=case.k_pool.dtype)
+            rows=[b], kv_dtype=case.k_pool.dtype, rope=rope)
         og, lg = o[q0:q1, g * h:g * (h + 1)], lse[q0:q1, g * h:g * (h + 1)]
         err = gh.assert_attention_close(og, lg, o_ref[q0:q1], lse_ref[q0:q1],
                                         f"{w.name} b={b} h={h}")
@@ -97,10 +97,10 @@ def _decode(name, fused, dtype="nvfp4"):
     return case, o.cpu().double().numpy(), lse.cpu().double().numpy()
 
 
-def _prefill(name, dtype="nvfp4"):
+def _prefill(name, dtype="nvfp4", rope=None):
     w = synth.workload(name)
     case = paged.build_case(w, keep_sources=False, dtype=dtype)
-    plan = paged.make_plan(case)
+    plan = paged.make_plan(case, rope=rope)
     ws = plan.new_workspace()
     plan.upload(ws)
     o = torch.full((w.total_q, w.num_qo_heads, w.head_dim_vo), float("nan"), device="cuda")
@@ -166,3 +166,22 @@ def test_prefill_extend_full_size_fp8(record_property):
     case, o, lse = _prefill("prefill_extend", dtype="fp8")
     assert not np.isnan(o).any() and not np.isnan(lse).any()
     _oracle_pairs(case, o, lse, sample_pairs(case.w, 58), record_property, causal=True)
+
+
+@pytest.mark.timeout(600)
+def test_prefill_extend_full_size_rope(record_property):
+    """The prefill extend with in-kernel RoPE (base 1e4), in the benchmark's launch."""
+    case, o, lse = _prefill("prefill_extend", rope=(1e4, 1.0))
+    assert not np.isnan(o).any() and not np.isnan(lse).any()
+    _oracle_pairs(case, o, lse, sample_pairs(case.w, 59), record_property, causal=True,
+                  rope=(1e4, 1.0))
+
+
+@pytest.mark.timeout(600)
+def test_asym_prefill_full_size_rope(record_property):
+    """4 causal requests of 1024 queries, head dims 512/256, RoPE over the 512-dim QK
+    rows: every pair."""
+    case, o, lse = _prefill("asym_prefill", rope=(1e4, 1.0))
+    assert not np.isnan(o).any() and not np.isnan(lse).any()
+    _oracle_pairs(case, o, lse, sample_pairs(case.w, 60, frac=1.0), record_property, causal=True,
+                  rope=(1e4, 1.0))

@@ -453,3 +453,44 @@ def test_custom_mask_plan_rules():
         nv.batch_prefill_masked(plan, q, pt, pool, pool, short, 0.1, ws)
     with pytest.raises(ValueError, match="custom mask"):
         nv.batch_prefill(plan, q, pt, pool, pool, 0.1, ws)
+
+
+def test_rope_plan_rules():
+    """In-kernel RoPE: prefill plans only (paged or ragged), not with a custom mask, a
+    positive finite base and scale, positions below 2^24; every supported shape's rotary
+    tile fits the LDS budget."""
+    st, msg = _plan_ex_status(qo_indptr=None, rope_theta=1e4)
+    assert st == "NVFP4_E_UNSUPPORTED" and "prefill" in msg, msg
+    st, msg = _plan_ex_status(custom_mask=True, rope_theta=1e4)
+    assert st == "NVFP4_E_UNSUPPORTED" and "custom mask" in msg, msg
+    for theta, scale in ((0.0, 1.0), (-5.0, 1.0), (float("nan"), 1.0), (float("inf"), 1.0),
+                         (1e4, 0.0), (1e4, float("inf"))):
+        st, msg = _plan_ex_status(rope_theta=theta, rope_scale=scale)
+        assert st == "NVFP4_E_INVALID" and "rope_theta" in msg, (theta, scale, msg)
+    st, msg = _plan_ex_status(kv_lens=[(1 << 24) + 1], qo_indptr=[0, 4], rope_theta=1e4)
+    assert st == "NVFP4_E_UNSUPPORTED" and "2^24" in msg, msg
+    assert _plan_ex_status(kv_lens=[1 << 24], qo_indptr=[0, 4], rope_theta=1e4)[0] == "NVFP4_OK"
+    assert _plan_ex_status(kv_indptr=[0, 64], rope_theta=1e4, kv_dtype=1)[0] == "NVFP4_OK"
+    # an unknown position encoding through the C struct
+    opts = _lib.PlanOptionsStruct(0, None, 0, 7, 1e4, 1.0)
+    kv = np.array([64], dtype=np.int32)
+    ind = np.array([0, 8], dtype=np.int32)
+    h = ctypes.c_void_p()
+    st = nv.lib.nvfp4_plan_create_ex(kv.ctypes.data_as(ctypes.c_void_p),
+                                     ind.ctypes.data_as(ctypes.c_void_p), 1, 8, 1, 128, 128, 16,
+                                     1, 0, 256, ctypes.byref(opts), ctypes.byref(h))
+    assert _lib.STATUS[st] == "NVFP4_E_INVALID" and "pos_encoding" in nv.lib.nvfp4_last_error().decode()
+    # the frequency table rides in the uploaded part of the workspace: DK/2 float pairs
+    plain = nv.Plan([64], qo_indptr=[0, 8], num_qo_heads=8, num_kv_heads=1, head_dim_qk=512,
+                    head_dim_vo=256, num_cus=256)
+    rope = nv.Plan([64], qo_indptr=[0, 8], num_qo_heads=8, num_kv_heads=1, head_dim_qk=512,
+                   head_dim_vo=256, num_cus=256, rope_theta=1e4)
+    assert rope.workspace_bytes == plain.workspace_bytes + 512 * 4
+    for dk in (64, 128, 256, 512):
+        for dv in (64, 128, 256):
+            if dv > dk:
+                continue
+            for ps in (1, 16):
+                st, msg = _plan_ex_status(page_size=ps, head_dim_qk=dk, head_dim_vo=dv,
+                                          rope_theta=5e5, rope_scale=8.0)
+                assert st == "NVFP4_OK", (dk, dv, ps, msg)
