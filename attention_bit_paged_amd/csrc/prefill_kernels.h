@@ -30,6 +30,7 @@
 #include <type_traits>
 
 #include "kv_ring.h"
+#include "rope.h"
 
 namespace nvfp4 {
 
@@ -39,6 +40,10 @@ namespace {
 // reads run this many k-steps (V tiles) less one ahead of their products (3 and 5
 // measured alike, 7 slower).
 constexpr int kWidePrefetch = 3;
+// Row groups of 16 per wave of the wide-head kernel (waves: 8 / groups).  Two groups
+// (four waves, one per SIMD, half the operand reads per product) measured 8 % slower:
+// with one wave per SIMD the LDS and barrier latencies are exposed.
+constexpr int kWideGroups = 1;
 
 template <int DK>
 constexpr int prefill_nr() {
@@ -214,8 +219,8 @@ struct CoopShape {
   // k-step at a time and the V operands one tile at a time; eight waves of one row
   // group each, two per SIMD, so that one wave's LDS reads overlap the other's products.
   static constexpr bool WIDE = DK > 256;
-  static constexpr int NW = WIDE ? 8 : 4;
-  static constexpr int NR = SMALL ? 3 : (WIDE ? 1 : 2);  // row groups of 16 per wave
+  static constexpr int NW = WIDE ? 8 / kWideGroups : 4;
+  static constexpr int NR = SMALL ? 3 : (WIDE ? kWideGroups : 2);  // row groups of 16 per wave
   static constexpr int WGS_PER_CU = SMALL ? 2 : 1;
   static constexpr int ROWS = NW * NR * 16;       // rows per work item
   static constexpr int NOP = 2 * S::NS + S::NT;   // operand vectors per step
@@ -861,6 +866,8 @@ void prefill_coop_kernel(AttnArgs a) {
     const uint32_t rs = __builtin_amdgcn_readfirstlane(raw0 + ((i + 1) % 3) * C::RAW_STAGE);
     const uint32_t ob1 = __builtin_amdgcn_readfirstlane(opb0 + ((i + 1) & 1) * C::OPB);
     if constexpr (C::WIDE) {
+      // the next step's operands first: placed beside the products (raw bytes read
+      // before them, operands written after) the kernel measured 8 % slower
       if (next) {
         if (t_of(i + 1) + kDecodeStep - 1 > tlast)
           coop_dequant<DK, DV, true, FMT, ROPE>(rs, ob1, wave, cl, tlast - t_of(i + 1),
@@ -879,7 +886,6 @@ void prefill_coop_kernel(AttnArgs a) {
       // product (three operand registers instead of PF) and each pair of products
       // then waits for the LDS.
       constexpr int PF = kWidePrefetch;
-      static_assert(NR == 1, "one row group per wave");
       f16x8 ka[PF], kb[PF];
       auto kload = [&](int s) {
         lds_load<16>(obl + s * 1024, reinterpret_cast<uint32_t*>(&ka[s % PF]));
@@ -891,23 +897,30 @@ void prefill_coop_kernel(AttnArgs a) {
 #pragma unroll
       for (int s = 0; s < S::NS; ++s) {
         if (s + PF - 1 < S::NS) kload(s + PF - 1);
-        sa[0] = mfma16x16x32(ka[s % PF], qf[0][s], sa[0]);
-        sb[0] = mfma16x16x32(kb[s % PF], qf[0][s], sb[0]);
+#pragma unroll
+        for (int rg = 0; rg < NR; ++rg) {
+          sa[rg] = mfma16x16x32(ka[s % PF], qf[rg][s], sa[rg]);
+          sb[rg] = mfma16x16x32(kb[s % PF], qf[rg][s], sb[rg]);
+        }
       }
       __builtin_amdgcn_sched_group_barrier(0x100, 2 * (PF - 1), 0);
 #pragma unroll
       for (int s = 0; s < S::NS; ++s) {
         if (s + PF - 1 < S::NS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * NR, 0);
       }
       __builtin_amdgcn_s_setprio(0);
-      f16x8 p;
-      if (MASK && custom)
-        p = st[0].softmax_vis(sa[0], sb[0], sc[0],
-                              coop_mask_bits<DK, DV, FMT>(cm, row_base + n, j, G, q0, kv_len, kv0,
-                                                          t0, tlast));
-      else
-        p = st[0].template softmax<MASK>(sa[0], sb[0], sc[0], t0, j, MASK ? last_of(0) : 0);
+      f16x8 p[NR];
+#pragma unroll
+      for (int rg = 0; rg < NR; ++rg) {
+        if (MASK && custom)
+          p[rg] = st[rg].softmax_vis(sa[rg], sb[rg], sc[rg],
+                                     coop_mask_bits<DK, DV, FMT>(cm, row_base + rg * 16 + n, j, G,
+                                                                 q0, kv_len, kv0, t0, tlast));
+        else
+          p[rg] = st[rg].template softmax<MASK>(sa[rg], sb[rg], sc[rg], t0, j,
+                                                MASK ? last_of(rg) : 0);
+      }
       f16x8 vt[PF];
       auto vload = [&](int e) {
         lds_load<16>(obl + (2 * S::NS + e) * 1024, reinterpret_cast<uint32_t*>(&vt[e % PF]));
@@ -917,13 +930,15 @@ void prefill_coop_kernel(AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < S::NT; ++e) {
         if (e + PF - 1 < S::NT) vload(e + PF - 1);
-        st[0].acc[e] = mfma16x16x32(vt[e % PF], p, st[0].acc[e]);
+#pragma unroll
+        for (int rg = 0; rg < NR; ++rg)
+          st[rg].acc[e] = mfma16x16x32(vt[e % PF], p[rg], st[rg].acc[e]);
       }
       __builtin_amdgcn_sched_group_barrier(0x100, PF - 1, 0);
 #pragma unroll
       for (int e = 0; e < S::NT; ++e) {
         if (e + PF - 1 < S::NT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, NR, 0);
       }
       return;
     }

@@ -32,7 +32,8 @@ pass and merge instead (TFLOP/s; used to profile the prefill kernel).
 
 Other modes (profiling support):
   --pmc-run                a short program for rocprofv3 counter passes: a 1 GiB copy
-                           (counter calibration) and a few steps of the workload;
+                           (counter calibration) and a few steps of the workload (with
+                           --variant: a few plain decode launches of that layout variant);
   --summarize-trace DIR    summarise a rocprofv3 --kernel-trace --stats output dir;
   --summarize-pmc DIR ...  summarise FETCH_SIZE / WRITE_SIZE counter dirs into the
                            traffic record read back by the benchmark;
@@ -77,6 +78,7 @@ def parse():
     # oracle work in the default run
     p.add_argument("--cpu-seconds", type=float, default=3.0)
     p.add_argument("--pmc-run", action="store_true")
+    p.add_argument("--variant", default="", help="layout variant of --pmc-run (a VARIANTS label)")
     p.add_argument("--summarize-trace", metavar="DIR")
     p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     p.add_argument("--summarize-counters", nargs="+", metavar="DIR")
@@ -339,14 +341,30 @@ VARIANTS = (("HND_page16", "HND", 16, None, None),
             ("HND_page1", "HND", 1, None, None))
 
 
+def variant_workload(synth, name, label):
+    """The workload under layout variant ``label`` and its (layout, K, V padding)."""
+    base = synth.workload(name)
+    for lab, layout, ps, kp, vp in VARIANTS:
+        if lab == label:
+            w = synth.workload(name, page_size=ps,
+                               pool_pages=base.pool_pages * base.page_size // ps)
+            return w, layout, kp, vp
+    raise SystemExit(f"unknown variant {label!r}; one of {[v[0] for v in VARIANTS]}")
+
+
+def variant_case(paged, synth, name, label):
+    w, layout, kp, vp = variant_workload(synth, name, label)
+    case = paged.build_case(w, keep_sources=False, layout=layout, k_pad=kp, v_pad=vp)
+    return w, case, paged.make_plan(case)
+
+
 def variant_lines(torch, nv, paged, synth, name, iters=60, warm=12, pool_sets=3):
     """Kernel throughput of one workload under each layout variant (same values, same
     request lengths; the page size changes the pool's page count, not its bytes), over
     ``pool_sets`` rotated pool sets like the main line."""
-    base = synth.workload(name)
     lines, ref_rate = [], None
-    for label, layout, ps, kp, vp in VARIANTS:
-        w = synth.workload(name, page_size=ps, pool_pages=base.pool_pages * base.page_size // ps)
+    for label, *_ in VARIANTS:
+        w, layout, kp, vp = variant_workload(synth, name, label)
         cases = [paged.build_case(w, keep_sources=False, layout=layout, k_pad=kp, v_pad=vp)
                  for _ in range(pool_sets)]
         case = cases[0]
@@ -683,6 +701,13 @@ class Decoder:
         return float(np.mean([he.ms(a, b) for a, b in ev]))
 
 
+def synth_module():
+    """The input-recipe module (no torch device work), for the summaries."""
+    sys.path.insert(0, ROOT)
+    from attention_bit_paged_amd import synth
+    return synth
+
+
 def pmc_run(args):
     """Short program for counter passes: calibration copy, then a few decode steps."""
     import torch
@@ -695,6 +720,19 @@ def pmc_run(args):
         y.copy_(x)
     torch.cuda.synchronize()
     del x, y
+    if args.variant:
+        w, case, plan = variant_case(paged, synth, args.workload, args.variant)
+        ws = plan.new_workspace()
+        plan.upload(ws)
+        o = torch.empty((w.total_q, w.num_qo_heads, w.head_dim_vo), device="cuda")
+        lse = torch.empty((w.total_q, w.num_qo_heads), device="cuda")
+        for _ in range(5):
+            nv.batch_decode(plan, case.q, case.page_table, case.k_pool, case.v_pool, w.sm_scale,
+                            ws, out=o, lse=lse)
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_run": args.workload, "variant": args.variant,
+                          "info": plan.info()}), flush=True)
+        return
     d = Decoder(torch, nv, paged, synth, args.workload, 1)
     for i in range(5):
         d.step(i)
@@ -746,7 +784,10 @@ def summarize_pmc(args):
         return out
 
     fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
-    dec = [k for k in fetch if "decode_ring_kernel" in k and "true" in k]
+    # the decode launch with the append (the benchmark's step), else the plain decode
+    # kernel of a --variant run
+    dec = ([k for k in fetch if "decode_ring_kernel" in k and "true" in k] or
+           [k for k in fetch if "decode_ring_kernel" in k or "decode_regs_kernel" in k])
     cpy = [k for k in fetch if "copyBuffer" in k]
     if not dec or not cpy:
         raise SystemExit(f"kernels not found: {list(fetch)}")
@@ -757,21 +798,32 @@ def summarize_pmc(args):
     w_scale = kib / float(np.mean(write[ck][:3]))
     f_dec, w_dec = float(np.mean(fetch[dk])), float(np.mean(write[dk]))
     nbytes = (f_dec * f_scale + w_dec * w_scale) * 1024
-    rec = {"kernel": _short(dk), "workload": args.workload,
+    variant = getattr(args, "variant", "")
+    if variant:
+        w = variant_workload(synth_module(), args.workload, variant)[0]
+        kv, qo = decode_bytes(w)
+    else:
+        kv, qo = decode_bytes(synth_module().workload(args.workload), append=True)
+    rec = {"kernel": _short(dk), "workload": args.workload, "variant": variant or None,
+           "algorithmic_bytes": kv + qo,
            "fetch_kib_per_dispatch": round(f_dec, 1), "write_kib_per_dispatch": round(w_dec, 1),
            "copy_fetch_kib": round(float(np.mean(fetch[ck][:3])), 1),
            "copy_write_kib": round(float(np.mean(write[ck][:3])), 1),
            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
-           "bytes_per_launch": round(nbytes), "source_digest": sources_digest()}
+           "bytes_per_launch": round(nbytes),
+           "traffic_over_algorithmic": round(nbytes / (kv + qo), 4),
+           "source_digest": sources_digest()}
     text = "\n".join([
         f"# HBM traffic of the decode kernel, workload {args.workload}",
         f"# commands: {args.command}",
         f"# calibration: {_short(ck)} copies {CALIB_BYTES} bytes; FETCH_SIZE reads "
         f"{rec['copy_fetch_kib']} KiB and WRITE_SIZE {rec['copy_write_kib']} KiB for it, so the "
         f"scales are {rec['fetch_scale']} and {rec['write_scale']}",
-        f"# decode kernel {rec['kernel']}: FETCH_SIZE {rec['fetch_kib_per_dispatch']} KiB, "
+        f"# decode kernel {rec['kernel']}{' (' + variant + ')' if variant else ''}: "
+        f"FETCH_SIZE {rec['fetch_kib_per_dispatch']} KiB, "
         f"WRITE_SIZE {rec['write_kib_per_dispatch']} KiB per dispatch "
-        f"({len(fetch[dk])} dispatches) -> {rec['bytes_per_launch']} bytes per launch",
+        f"({len(fetch[dk])} dispatches) -> {rec['bytes_per_launch']} bytes per launch, "
+        f"{rec['traffic_over_algorithmic']} x the {rec['algorithmic_bytes']} algorithmic bytes",
         json.dumps(rec)]) + "\n"
     if args.out:
         with open(args.out, "w") as f:
@@ -959,7 +1011,12 @@ def main():
                               else f"{min(w.kv_lens)}..{max(w.kv_lens)} (seeded uniform)"),
                    "num_qo_heads": w.num_qo_heads, "num_kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim_qk, "page_size": w.page_size, "pool_pages": w.pool_pages,
-                   "kv_chunk_tokens": info["kv_chunk_tokens"], "work_items": info["num_work_items"],
+                   "kv_chunk_tokens": info["kv_chunk_tokens"],
+                   "kv_chunk_tokens_meaning": "keys per wave part; a work item (workgroup of "
+                   "four waves) covers four consecutive parts, and split rows are merged per "
+                   "work item",
+                   "keys_per_work_item": 4 * info["kv_chunk_tokens"],
+                   "work_items": info["num_work_items"],
                    "total_kv_tokens": w.total_kv, "pool_sets_rotated": len(d.sets)},
         "frac_hbm": round(value / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,

@@ -118,3 +118,22 @@ def test_counter_summary_measures_the_clock(tmp_path):
     assert rec["derived"]["clock_ghz"] == pytest.approx(2.1, rel=1e-4)
     assert rec["derived"]["mfma_busy_share"] == pytest.approx(0.4, rel=1e-4)
     assert rec["derived"]["rocprof_mfma_util_share"] == pytest.approx(0.4)
+
+
+def test_variant_traffic_record_names_the_plain_kernel(tmp_path):
+    """A --variant counter run has no append launch: the record takes the plain decode
+    kernel and prices it against the variant's own algorithmic bytes."""
+    kib = bench.CALIB_BYTES / 1024
+    plain = "decode_ring_kernel<128, 128, false, 0>(nvfp4::AttnArgs)"
+    fetch = _counter_dir(tmp_path, "f", "FETCH_SIZE", [(COPY, kib)] * 3 + [(plain, 500.0)] * 2)
+    write = _counter_dir(tmp_path, "w", "WRITE_SIZE", [(COPY, kib)] * 3 + [(plain, 8.0)] * 2)
+    out = tmp_path / "summary.txt"
+    args = types.SimpleNamespace(summarize_pmc=[fetch, write], workload="batch_decode",
+                                 command="synthetic", out=str(out), variant="NHD_page16")
+    bench.summarize_pmc(args)
+    rec = __import__("json").loads(out.read_text().strip().splitlines()[-1])
+    assert rec["variant"] == "NHD_page16" and rec["kernel"].startswith("decode_ring_kernel")
+    w = bench.variant_workload(bench.synth_module(), "batch_decode", "NHD_page16")[0]
+    kv, qo = bench.decode_bytes(w)
+    assert rec["algorithmic_bytes"] == kv + qo
+    assert rec["traffic_over_algorithmic"] == pytest.approx(508.0 * 1024 / (kv + qo), abs=1e-4)
