@@ -735,6 +735,8 @@ void prefill_coop_kernel(AttnArgs a) {
   bool rv[NR];
   int64_t tokrow[NR];
   int headi[NR];
+  const uint16_t* qrows[NR];
+  float qpos_f[NR];
   // keys the tile needs: up to the last visible key of its last row
   const int tile_end = a.causal ? min(kv1, q0 + (Rn - 1) / G + off + 1) : kv1;
   const int tlast = kv1 - 1;
@@ -796,27 +798,49 @@ void prefill_coop_kernel(AttnArgs a) {
     tokrow[rg] = (int64_t)qstart + qpos;
     headi[rg] = kvh * G + gh;
     const uint16_t* qrow = a.q + tokrow[rg] * a.q_s_row + (int64_t)headi[rg] * a.q_s_head;
-    const float qp = (float)(qpos + off);  // the query's position (RoPE)
-    if constexpr (C::WIDE && ROPE)
-      sc[rg] = a.score_scale * load_q_rope_prescaled<DK>(qrow, rv[rg], j, qp, a.rope, qf[rg]);
-    else if constexpr (C::WIDE)
+    if constexpr (ROPE) {
+      qrows[rg] = qrow;
+      qpos_f[rg] = (float)(qpos + off);  // the query's position
+    } else if constexpr (C::WIDE) {
       sc[rg] = a.score_scale * load_q_operand<DK>(qrow, rv[rg], j, qf[rg]);
-    else if constexpr (ROPE)
-      safe = load_q_rope<DK>(qrow, rv[rg], j, qp, a.rope, a.score_scale, qf[rg]) < 32768.f && safe;
-    else
+    } else {
       safe = load_q_scaled<DK>(qrow, rv[rg], j, a.score_scale, qf[rg]) && safe;
+    }
+  }
+  // RoPE: all rows rotated together (scaled by the score factor, as load_q_scaled, unless
+  // the wide kernel, which takes the exact prescaled form)
+  auto rope_prescaled = [&]() {
+    float mul[NR], amax[NR];
+#pragma unroll
+    for (int rg = 0; rg < NR; ++rg) {
+      int qexp = 0;
+      const float qmax = q_row_absmax<DK>(qrows[rg], rv[rg], j);
+      if (qmax > 0.f) (void)frexpf(qmax, &qexp);
+      mul[rg] = ldexpf(1.f, 15 - qexp);
+      sc[rg] = a.score_scale * ldexpf(1.f, qexp - 15);
+    }
+    load_q_rope_rows<DK, NR, C::WGS_PER_CU == 1>(qrows, rv, j, qpos_f, a.rope, mul, qf, amax);
+  };
+  if constexpr (ROPE && C::WIDE) {
+    rope_prescaled();
+  } else if constexpr (ROPE) {
+    float mul[NR], amax[NR];
+#pragma unroll
+    for (int rg = 0; rg < NR; ++rg) mul[rg] = a.score_scale;
+    load_q_rope_rows<DK, NR, C::WGS_PER_CU == 1>(qrows, rv, j, qpos_f, a.rope, mul, qf, amax);
+#pragma unroll
+    for (int rg = 0; rg < NR; ++rg) safe = amax[rg] < 32768.f && safe;
   }
   const bool shifted = !C::WIDE && __all(safe);
   if (!C::WIDE && !shifted) {
+    if constexpr (ROPE) {
+      rope_prescaled();
+    } else {
 #pragma unroll
-    for (int rg = 0; rg < NR; ++rg) {
-      const uint16_t* qrow = a.q + tokrow[rg] * a.q_s_row + (int64_t)headi[rg] * a.q_s_head;
-      if constexpr (ROPE)
+      for (int rg = 0; rg < NR; ++rg)
         sc[rg] = a.score_scale *
-                 load_q_rope_prescaled<DK>(qrow, rv[rg], j,
-                                           (float)(tokrow[rg] - qstart + off), a.rope, qf[rg]);
-      else
-        sc[rg] = a.score_scale * load_q_operand<DK>(qrow, rv[rg], j, qf[rg]);
+                 load_q_operand<DK>(a.q + tokrow[rg] * a.q_s_row + (int64_t)headi[rg] * a.q_s_head,
+                                    rv[rg], j, qf[rg]);
     }
   }
 

@@ -104,6 +104,57 @@ __device__ __forceinline__ float load_q_rope_prescaled(const uint16_t* qrow, boo
   return ldexpf(1.f, qexp - 15);
 }
 
+// The Q quarter-rows of a wave's NR row groups rotated, k-step by k-step: a k-step's
+// eight frequency pairs are read once for all rows, and a row's own and partner loads
+// are issued one k-step at a time (all of them at once held every row's quarter-rows
+// beside the kernel's state and spilled it).  Row rg is scaled by mul[rg]; amax[rg]
+// returns its largest |rotated q * mul| (NaN when an input is NaN).  AGPR: each operand
+// moves to the accumulation registers as soon as it is made (kernels that keep Q there).
+template <int DK, int NR, bool AGPR = false>
+__device__ __forceinline__ void load_q_rope_rows(const uint16_t* const (&qrow)[NR],
+                                                 const bool (&valid)[NR], int j,
+                                                 const float (&pos)[NR], const float* freq,
+                                                 const float (&mul)[NR], f16x8 (&qf)[NR][DK / 32],
+                                                 float (&amax)[NR]) {
+  const float* fr = freq + 2 * ((j & 1) * (DK / 4));
+  const float sgn = j < 2 ? -1.f : 1.f;  // first half: x cos - y sin; second: x cos + y sin
+#pragma unroll
+  for (int rg = 0; rg < NR; ++rg) amax[rg] = 0.f;
+#pragma unroll
+  for (int s = 0; s < DK / 32; ++s) {
+    uint32_t fw[16];
+    load_bytes<64>(reinterpret_cast<const uint8_t*>(fr + 16 * s), fw);
+#pragma unroll
+    for (int rg = 0; rg < NR; ++rg) {
+      uint32_t xo[4] = {0u, 0u, 0u, 0u}, xp[4] = {0u, 0u, 0u, 0u};
+      if (valid[rg]) {
+        load_bytes<16>(reinterpret_cast<const uint8_t*>(qrow[rg] + j * (DK / 4)) + 16 * s, xo);
+        load_bytes<16>(reinterpret_cast<const uint8_t*>(qrow[rg] + (j ^ 2) * (DK / 4)) + 16 * s,
+                       xp);
+      }
+      f16x2 p[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        float r[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float x = bf16f(h ? xo[t] >> 16 : xo[t] & 0xFFFF);
+          const float y = bf16f(h ? xp[t] >> 16 : xp[t] & 0xFFFF);
+          float c, sn;
+          rope_cs(pos[rg], __builtin_bit_cast(float, fw[2 * (2 * t + h)]),
+                  __builtin_bit_cast(float, fw[2 * (2 * t + h) + 1]), c, sn);
+          r[h] = fmaf(x, c, sgn * (y * sn)) * mul[rg];
+          amax[rg] = __builtin_elementwise_maximum(amax[rg], fabsf(r[h]));
+        }
+        p[t] = f16x2{(_Float16)r[0], (_Float16)r[1]};
+      }
+      qf[rg][s] = pack8(p[0], p[1], p[2], p[3]);
+      if constexpr (AGPR) asm volatile("" : "+a"(qf[rg][s]));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // Rotates one pair of K operand vectors in place: lo holds elements i .. i+7 of a key
 // row (pair indices i0 .. i0+7), hi the partner elements i + D/2 ...; `tab` the LDS
 // address of the pairs' eight frequencies.
