@@ -526,13 +526,15 @@ __device__ __forceinline__ void coop_wait(int wave, bool one_newer, int mask_cop
 }
 
 // The custom-mask copies of a tile: lane l of block qb carries tile query 64 qb + l.
-// A query's bits of the keys of a step start 4 bytes further on in every step (32 keys),
-// at a fixed bit shift, so its copies take the step's base (scalar) plus a fixed
-// per-lane byte offset; lanes past the tile's queries copy the tile's first query's
-// bytes instead (unused).
+// A query's bits of the keys of a step start at byte ((q0 + l') L + t0) / 8 of the
+// segment (t0 a multiple of 32), at a fixed bit shift; lanes past the tile's queries
+// copy the tile's first query's bytes instead (unused).  The per-lane offsets are formed
+// at each issue from scalars: held for the whole loop they were spilled, and a reload
+// there waits for every copy in flight.
 struct CoopMask {
   const uint8_t* seg;  // the request's mask segment
-  uint32_t voff[3];    // byte offset of this lane's query at the chunk's first key
+  int64_t q0, kv_len;  // the tile's first query (within the request), the request's keys
+  int qn;              // the tile's queries
   int blocks;          // blocks of 64 tile queries (uniform)
   uint32_t ring;       // LDS address of the mask ring (uniform)
 };
@@ -585,13 +587,18 @@ __device__ __forceinline__ void coop_issue(int wave, const CoopCopies<DK, DV, FM
     else if (wave == 3) ring_issue<DK, DV, WL, 8>(cc.template expand<8>(), stage, view, t0, tlast, bad);
   }
   if (CMASK && wave == 3) {
-    const uint8_t* base = cm.seg + ((t0 - kv0) >> 3);  // 4 bytes per 32-key step
     const uint32_t slot = cm.ring + (((t0 - kv0) >> 5) & 3) * C::MASK_SLOT;
+    int lane = threadIdx.x & 63;
+    // opaque at each issue, so that the offsets below are formed here and not hoisted
+    // out of the loop (and spilled)
+    asm volatile("" : "+v"(lane));
 #pragma unroll
     for (int qb = 0; qb < C::MASK_BLOCKS; ++qb) {
       if (qb < cm.blocks) {
-        dma<false>(slot + qb * 512, cm.voff[qb], base);
-        dma<false>(slot + qb * 512 + 256, cm.voff[qb] + 4, base);
+        const int ql = qb * 64 + lane < cm.qn ? qb * 64 + lane : 0;
+        const uint32_t voff = (uint32_t)(((cm.q0 + ql) * cm.kv_len + t0) >> 3);
+        dma<false>(slot + qb * 512, voff, cm.seg);
+        dma<false>(slot + qb * 512 + 256, voff + 4, cm.seg);
       }
     }
   }
@@ -759,14 +766,12 @@ void prefill_coop_kernel(AttnArgs a) {
   cm.seg = nullptr;
   cm.blocks = 0;
   cm.ring = opb0 + 2 * C::OPB;
+  cm.q0 = q0;
+  cm.kv_len = kv_len;
+  cm.qn = qn;
   if constexpr (CMASK) {
     cm.seg = a.mask + a.mask_off[b];
     cm.blocks = (qn + 63) / 64;
-#pragma unroll
-    for (int qb = 0; qb < C::MASK_BLOCKS; ++qb) {
-      const int ql = qb * 64 + lane < qn ? qb * 64 + lane : 0;
-      cm.voff[qb] = (uint32_t)(((int64_t)(q0 + ql) * kv_len + kv0) >> 3);
-    }
   }
   // RoPE: the frequency table after the operand buffers (visible to the dequantisation
   // after the prologue's barrier)
