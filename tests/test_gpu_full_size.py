@@ -185,3 +185,93 @@ def test_asym_prefill_full_size_rope(record_property):
     assert not np.isnan(o).any() and not np.isnan(lse).any()
     _oracle_pairs(case, o, lse, sample_pairs(case.w, 60, frac=1.0), record_property, causal=True,
                   rope=(1e4, 1.0))
+
+
+def _prefix_masks(w):
+    """The benchmark's multimodal-prefix masks: the first third of each request's new
+    tokens attend to each other bidirectionally, the rest causal over the prefix."""
+    out = []
+    for q, L in zip(w.qo_lens, w.kv_lens):
+        prefix, img = L - q, max(1, q // 3)
+        i = np.arange(q)[:, None]
+        j = np.arange(L)[None, :]
+        out.append((j <= i + prefix) | ((i < img) & (j >= prefix) & (j < prefix + img)))
+    return out
+
+
+@pytest.mark.timeout(600)
+def test_prefill_extend_full_size_masked(record_property):
+    """The prefill extend under the benchmark's multimodal-prefix masks, in its launch
+    (nvfp4_batch_prefill_masked, whole-key-range tiles)."""
+    w = synth.workload("prefill_extend")
+    case = paged.build_case(w, keep_sources=False)
+    plan = nv.Plan(w.kv_lens, num_qo_heads=w.num_qo_heads, num_kv_heads=w.num_kv_heads,
+                   head_dim_qk=w.head_dim_qk, head_dim_vo=w.head_dim_vo,
+                   qo_indptr=case.qo_indptr.tolist(), causal=True, custom_mask=True)
+    packed = ref.pack_masks(_prefix_masks(w))
+    assert packed.size == plan.mask_bytes
+    mask = torch.from_numpy(np.concatenate([packed, np.full(8, 0xFF, np.uint8)])).cuda()
+    ws = plan.new_workspace()
+    plan.upload(ws)
+    o = torch.full((w.total_q, w.num_qo_heads, w.head_dim_vo), float("nan"), device="cuda")
+    lse = torch.full((w.total_q, w.num_qo_heads), float("nan"), device="cuda")
+    nv.batch_prefill_masked(plan, case.q, case.page_table, case.k_pool, case.v_pool, mask,
+                            w.sm_scale, ws, out=o, lse=lse)
+    torch.cuda.synchronize()
+    o, lse = o.cpu().double().numpy(), lse.cpu().double().numpy()
+    assert not np.isnan(o).any() and not np.isnan(lse).any()
+    host = lambda t: None if t is None else t.cpu().numpy()
+    kd, ks, vd, vs = (host(case.k_pool.data), host(case.k_pool.sf), host(case.v_pool.data),
+                      host(case.v_pool.sf))
+    q = case.q.float().cpu().double().numpy()
+    g, ind = w.group, synth.indptr(w.qo_lens)
+    worst = 0.0
+    samples = sample_pairs(w, 61)
+    for b, h in samples:
+        q0, q1 = int(ind[b]), int(ind[b + 1])
+        o_ref, lse_ref = ref.paged_attention(
+            q[:, g * h:g * (h + 1)], kd[:, h:h + 1], ks[:, h:h + 1], vd[:, h:h + 1],
+            vs[:, h:h + 1], case.page_table_np, w.kv_lens, ind, w.page_size, w.sm_scale, False,
+            "HND", rows=[b], custom_mask=packed)
+        err = gh.assert_attention_close(o[q0:q1, g * h:g * (h + 1)], lse[q0:q1, g * h:g * (h + 1)],
+                                        o_ref[q0:q1], lse_ref[q0:q1], f"masked b={b} h={h}")
+        worst = max(worst, float(err))
+    record_property("pairs_checked", len(samples))
+    record_property("max_abs_err_O", worst)
+    print(f"masked prefill_extend: {len(samples)} pairs, max |O err| {worst:.3e}", flush=True)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("dtype", ["nvfp4", "fp8"])
+def test_prefill_extend_full_size_ragged(dtype, record_property):
+    """The prefill extend over ragged (non-paged) rows, in the benchmark's launch."""
+    w = synth.workload("prefill_extend")
+    case = paged.build_ragged_case(w, dtype=dtype)
+    plan = paged.make_ragged_plan(case)
+    ws = plan.new_workspace()
+    plan.upload(ws)
+    o, lse = nv.batch_prefill_ragged(plan, case.q, case.k, case.v, w.sm_scale, ws)
+    torch.cuda.synchronize()
+    o, lse = o.cpu().double().numpy(), lse.cpu().double().numpy()
+    assert not np.isnan(o).any() and not np.isnan(lse).any()
+    host = lambda t: None if t is None else t.cpu().numpy()
+    kd, ks, vd, vs = host(case.k.data), host(case.k.sf), host(case.v.data), host(case.v.sf)
+    q = case.q.float().cpu().double().numpy()
+    g, ind = w.group, synth.indptr(w.qo_lens)
+    worst = 0.0
+    samples = sample_pairs(w, 62)
+    head = lambda a, h: None if a is None else a[:, h:h + 1]
+    for b, h in samples:
+        q0, q1 = int(ind[b]), int(ind[b + 1])
+        a0, a1 = int(case.kv_indptr[b]), int(case.kv_indptr[b + 1])
+        o_ref, lse_ref = ref.ragged_attention(
+            q[q0:q1, g * h:g * (h + 1)], head(kd, h)[a0:a1], None if ks is None else
+            head(ks, h)[a0:a1], head(vd, h)[a0:a1], None if vs is None else head(vs, h)[a0:a1],
+            [0, a1 - a0], [0, q1 - q0], w.sm_scale, True, kv_dtype=dtype)
+        err = gh.assert_attention_close(o[q0:q1, g * h:g * (h + 1)], lse[q0:q1, g * h:g * (h + 1)],
+                                        o_ref, lse_ref, f"ragged {dtype} b={b} h={h}")
+        worst = max(worst, float(err))
+    record_property("pairs_checked", len(samples))
+    record_property("max_abs_err_O", worst)
+    print(f"ragged {dtype} prefill_extend: {len(samples)} pairs, max |O err| {worst:.3e}",
+          flush=True)
