@@ -107,13 +107,35 @@ struct PagedView {
     return pg;
   }
 
-  // Raw bytes of the step starting at token t0 (page_size < 16), every token looked up
-  // on its own.  Keys after tlast are never used; their reads are clamped to tlast.
-  __device__ __forceinline__ void load(StepRaw<DK, DV, FMT>& r, int t0, int tlast) {
+  // The page-table entries of a step's tokens for this lane (page_size < 16): the K
+  // tiles' two tokens and the eight value tokens.  Read a step ahead of the step's data
+  // (load below), so that a data load never waits for its page-table load.
+  struct Pages {
+    int ka, kb, v[8];
+  };
+  __device__ __forceinline__ void lookup(Pages& p, int t0, int tlast) const {
     static_assert(!PAGE16, "page_size >= 16 streams through the LDS rings");
     const int ta = min(t0 + 8 * (n >> 2) + (n & 3), tlast);
     const int tb = min(t0 + 8 * (n >> 2) + (n & 3) + 4, tlast);
-    const int pga = page_of(ta >> page_shift), pgb = page_of(tb >> page_shift);
+    p.ka = pt_row[ta >> page_shift];
+    p.kb = pt_row[tb >> page_shift];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p.v[i] = pt_row[min(t0 + 8 * j + i, tlast) >> page_shift];
+  }
+  // Raw bytes of the step starting at token t0 from its looked-up pages.  Keys after
+  // tlast are never used; their reads are clamped to tlast.  An entry outside
+  // [0, num_pages) marks the view bad and reads page 0 instead.
+  __device__ __forceinline__ void load(StepRaw<DK, DV, FMT>& r, const Pages& p, int t0, int tlast) {
+    auto valid = [&](int pg) {
+      if ((unsigned)pg >= (unsigned)num_pages) {
+        bad = 1;
+        return 0;
+      }
+      return pg;
+    };
+    const int ta = min(t0 + 8 * (n >> 2) + (n & 3), tlast);
+    const int tb = min(t0 + 8 * (n >> 2) + (n & 3) + 4, tlast);
+    const int pga = valid(p.ka), pgb = valid(p.kb);
     load_bytes<S::KB>(kdat + pga * k_page + (int64_t)(ta & page_mask) * k_tok + j * S::KB, r.ka);
     load_bytes<S::KB>(kdat + pgb * k_page + (int64_t)(tb & page_mask) * k_tok + j * S::KB, r.kb);
     if constexpr (!S::F8) {
@@ -123,12 +145,18 @@ struct PagedView {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int t = min(t0 + 8 * j + i, tlast);
-      const int pg = page_of(t >> page_shift);
+      const int pg = valid(p.v[i]);
       const int64_t sl = t & page_mask;
       load_bytes<S::VB>(vdat + pg * v_page + sl * v_tok + n * S::VB, r.vd[i]);
       if constexpr (!S::F8)
         load_bytes<S::VSFB>(vsf + pg * vsf_page + sl * vsf_tok + (n * DV / 16) / 16, &r.vs[i]);
     }
+  }
+  // Both at once (a step whose pages were not looked up ahead).
+  __device__ __forceinline__ void load(StepRaw<DK, DV, FMT>& r, int t0, int tlast) {
+    Pages p;
+    lookup(p, t0, tlast);
+    load(r, p, t0, tlast);
   }
 };
 

@@ -461,19 +461,26 @@ __global__ __launch_bounds__(256) void decode_regs_kernel(AttnArgs a) {
   const int nsteps = (len + kDecodeStep - 1) / kDecodeStep;
   const int nfull = len / kDecodeStep;
   auto t_of = [&](int i) { return it.w0 + i * kDecodeStep; };
-  // r0 holds step i at the top of every iteration; full steps in pairs, unmasked
+  using View = PagedView<DK, DV, false, FMT>;
+  // r0 holds step i at the top of every iteration, p1 the pages of step i + 1; full
+  // steps in pairs, unmasked.  A step's page-table entries are read one step before its
+  // bytes, its bytes one step before its compute.
   StepRaw<DK, DV, FMT> r0, r1;
+  typename View::Pages p0, p1;
   if (nsteps > 0) view.load(r0, t_of(0), tlast);
+  if (nsteps > 1) view.lookup(p1, t_of(1), tlast);
   int i = 0;
   for (; i + 1 < nfull; i += 2) {
-    view.load(r1, t_of(i + 1), tlast);
+    if (i + 2 < nsteps) view.lookup(p0, t_of(i + 2), tlast);
+    view.load(r1, p1, t_of(i + 1), tlast);
     decode_step<DK, DV, false, FMT>(r0, t_of(i), tlast, j, qf, score_c, st);
-    if (i + 2 < nsteps) view.load(r0, t_of(i + 2), tlast);
+    if (i + 3 < nsteps) view.lookup(p1, t_of(i + 3), tlast);
+    if (i + 2 < nsteps) view.load(r0, p0, t_of(i + 2), tlast);
     decode_step<DK, DV, false, FMT>(r1, t_of(i + 1), tlast, j, qf, score_c, st);
   }
-  // at most two steps are left, the second one partial
+  // at most two steps are left, the second one partial (its pages are in p1)
   if (i < nsteps) {
-    if (i + 1 < nsteps) view.load(r1, t_of(i + 1), tlast);
+    if (i + 1 < nsteps) view.load(r1, p1, t_of(i + 1), tlast);
     decode_step<DK, DV, true, FMT>(r0, t_of(i), tlast, j, qf, score_c, st);
     if (i + 1 < nsteps) decode_step<DK, DV, true, FMT>(r1, t_of(i + 1), tlast, j, qf, score_c, st);
   }

@@ -174,14 +174,22 @@ __global__ __launch_bounds__(256) void prefill_regs_kernel(AttnArgs a) {
     for (int rg = 0; rg < NR; ++rg) st[rg].pv(vt, p[rg]);
   };
 
+  // r0 holds the step at t0 at the top of every iteration, p1 the pages of the next: a
+  // step's page-table entries are read one step before its bytes, its bytes one step
+  // before its compute
+  using View = PagedView<DK, DV, false, FMT>;
   StepRaw<DK, DV, FMT> r0, r1;
+  typename View::Pages p0, p1;
   if (kv0 < wave_end) view.load(r0, kv0, tlast);
+  if (kv0 + kDecodeStep < wave_end) view.lookup(p1, kv0 + kDecodeStep, tlast);
   for (int t0 = kv0; t0 < wave_end; t0 += 2 * kDecodeStep) {
     const int t1 = t0 + kDecodeStep;
-    if (t1 < wave_end) view.load(r1, t1, tlast);
+    if (t1 + kDecodeStep < wave_end) view.lookup(p0, t1 + kDecodeStep, tlast);
+    if (t1 < wave_end) view.load(r1, p1, t1, tlast);
     step(r0, t0);
     if (t1 >= wave_end) break;
-    if (t1 + kDecodeStep < wave_end) view.load(r0, t1 + kDecodeStep, tlast);
+    if (t1 + 2 * kDecodeStep < wave_end) view.lookup(p1, t1 + 2 * kDecodeStep, tlast);
+    if (t1 + kDecodeStep < wave_end) view.load(r0, p0, t1 + kDecodeStep, tlast);
     step(r1, t1);
   }
 
