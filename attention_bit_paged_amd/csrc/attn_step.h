@@ -174,10 +174,15 @@ __device__ __forceinline__ float load_q_operand(const uint16_t* qrow, bool valid
 #pragma unroll
     for (int i = 0; i < QW; ++i) qraw[i] = 0u;
   }
-  float qmax = 0.f;
+  // The largest magnitude, as the largest sign-cleared bf16 bit pattern: for finite
+  // values the unsigned order of those patterns is the order of the magnitudes (a row
+  // holding a NaN or an infinity gives non-finite scores whatever its scale).
+  typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+  u16x2 mb = {0, 0};
 #pragma unroll
   for (int i = 0; i < QW; ++i)
-    qmax = fmaxf(qmax, fmaxf(fabsf(bf16f(qraw[i] & 0xFFFF)), fabsf(bf16f(qraw[i] >> 16))));
+    mb = __builtin_elementwise_max(mb, __builtin_bit_cast(u16x2, qraw[i] & 0x7FFF7FFFu));
+  float qmax = __uint_as_float((uint32_t)(mb[0] > mb[1] ? mb[0] : mb[1]) << 16);
   qmax = max_over_groups(qmax);
   int qexp = 0;
   if (qmax > 0.f) (void)frexpf(qmax, &qexp);

@@ -247,6 +247,9 @@ struct CoopShape {
   static constexpr int ROPE_TAB = DK * 4;          // RoPE: DK/2 frequency pairs of floats
   static constexpr int LDS_ROPE = LDS + ROPE_TAB;
   static constexpr int KE = (2 * S::NS + NW - 1) / NW;  // K operand entries per lane
+  // 512-dim heads (without RoPE): a lane dequantises one 16-byte piece of a key row into
+  // four K entries (see CoopLanes); the ring holds each key row's pieces rotated
+  static constexpr bool piece(bool rope) { return WIDE && !rope && FMT == kNvfp4; }
   static constexpr int VH = NW / 4;               // V tiles split in this many parts
   static constexpr int VPART = S::NT / VH;        // V tiles per part
   static_assert(R::NST == 3, "raw ring depth");
@@ -321,6 +324,20 @@ struct CoopLanes {
       k_sc = R::OFF_SF + k_tok * S::SBK + jj * S::KSF + (s >> 1);
       k_dst = (o * 64 + 16 * jj + n) * 16;
       k_tab = tab + 8 * (jj * (DK / 4) + 8 * s);
+    } else if constexpr (C::piece(ROPE)) {
+      // Wave w covers k-steps 4(w%4)..4(w%4)+3 of token tile w/4; lane (j, n) reads the
+      // 16-byte piece 4j + w%4 of its token's row (the lane's dwords of those four
+      // k-steps) and its two scale bytes, and writes entry (j, n) of the four operands.
+      // Key row t's piece p sits in LDS slot (p + n) % 16 of the row (n: the token's
+      // column), so that each quarter-wave's 16 reads cover all banks.
+      static_assert(S::NS == 16 && S::RBK == 256 && C::NW == 8, "piece layout");
+      const int tile = wave >> 2, g = wave & 3, p = 4 * j + g;
+      k_tok = 8 * (n >> 2) + (n & 3) + 4 * tile;
+      k_raw = R::OFF_KD + k_tok * S::RBK + 16 * ((p + n) & 15);
+      k_sc = R::OFF_SF + k_tok * S::SBK + 2 * p;
+      k_dst = ((tile * S::NS + 4 * g) * 64 + lane) * 16;
+      k_tab = 0;
+      k_live = true;
     } else {
       const int o = min(wave, 2 * S::NS - 1);  // clamped: unused when past the end
       const int tile = o / S::NS, s = o % S::NS;
@@ -357,10 +374,17 @@ struct CoopRaw {
   static constexpr int NB = S::VB < 4 ? S::VB : 4;   // bytes of the V slice per dword
   static constexpr int EPD = S::F8 ? NB : 2 * NB;    // V tiles per slice dword
   static constexpr int KW = S::KSTEP / 4;            // dwords of one K entry
-  static constexpr int KSLOT = ROPE ? 2 * L::KJ : C::KE;  // RoPE: both halves of each pair
-  uint32_t kw[KSLOT][KW], ksc[KSLOT], sa, sb, vw0[S::VW], vw1[S::VW];
+  static constexpr bool PIECE = C::piece(ROPE);
+  // RoPE: both halves of each pair; pieces: the piece's four dwords in kw[0]
+  static constexpr int KSLOT = ROPE ? 2 * L::KJ : (PIECE ? 1 : C::KE);
+  static constexpr int KWP = PIECE ? 4 : KW;
+  uint32_t kw[KSLOT][KWP], ksc[KSLOT], sa, sb, vw0[S::VW], vw1[S::VW];
 
   __device__ __forceinline__ void load(uint32_t raw, int wave, const L& cl) {
+    if constexpr (PIECE) {
+      lds_load<16>(raw + cl.k_raw, kw[0]);
+      lds_load<2>(raw + cl.k_sc, &ksc[0]);
+    }
     if constexpr (ROPE) {
       // both halves of each of the lane's entries (its address clamped in range when
       // the entry does not exist)
@@ -377,7 +401,7 @@ struct CoopRaw {
       }
     }
 #pragma unroll
-    for (int r = 0; r < (ROPE ? 0 : C::KE); ++r) {
+    for (int r = 0; r < (ROPE || PIECE ? 0 : C::KE); ++r) {
       // wave-uniform; always true when the K entries divide evenly among the waves
       if ((2 * S::NS) % C::NW == 0 || wave + C::NW * r < 2 * S::NS) {
         lds_load<S::KSTEP>(raw + cl.k_raw + cl.k_raw_off(r), kw[r]);
@@ -429,8 +453,17 @@ __device__ __forceinline__ void CoopRaw<DK, DV, FMT, ROPE>::store(uint32_t opb, 
       }
     }
   }
+  if constexpr (PIECE) {
+    // dword q of the piece is k-step 4(w%4) + q; the two scales cover dwords 0-1 and 2-3
+    const f16x2 sc2 = fp8x2_to_f16<false>(ksc[0]);
 #pragma unroll
-  for (int r = 0; r < (ROPE ? 0 : C::KE); ++r) {
+    for (int q = 0; q < 4; ++q) {
+      const f16x8 v = dequant8(kw[0][q], q < 2 ? splat_lo(sc2) : splat_hi(sc2));
+      *(__attribute__((address_space(3))) f16x8*)(lds_p)(size_t)(opb + cl.k_dst + q * 1024) = v;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < (ROPE || PIECE ? 0 : C::KE); ++r) {
     if ((2 * S::NS) % C::NW == 0 || wave + C::NW * r < 2 * S::NS) {
       f16x8 v;
       if constexpr (S::F8)
@@ -558,6 +591,19 @@ struct CoopCopies {
                                                 : (R::N_VD > R::N_SF ? R::N_VD : R::N_SF);
   uint32_t mine[MAXC > 0 ? MAXC : 1];
 
+  // Pieces: the K copies place piece p of step token t in slot (p + n(t)) % 16 of its
+  // row, n(t) the token's column in its 16-token tile; so the copy lane that lands in
+  // slot q fetches piece (q - n(t)) % 16.  Only the offset inside the row changes.
+  __device__ __forceinline__ void rotate_k(Plan& rp, int lane) {
+    static_assert(R::RBK == 256, "rotation of 16-piece rows");
+#pragma unroll
+    for (int c = 0; c < R::N_KD; ++c) {
+      const int byte = c * 1024 + lane * 16;
+      const int t = byte / R::RBK, q = (byte % R::RBK) / 16;
+      const int nt = ((t >> 3) << 2) | (t & 3);
+      rp.off[c] = rp.off[c] - (uint32_t)(16 * q) + (uint32_t)(16 * ((q - nt) & 15));
+    }
+  }
   __device__ __forceinline__ void init(const Plan& rp, int wave) {
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) {
@@ -763,6 +809,7 @@ void prefill_coop_kernel(AttnArgs a) {
   {
     RingPlan<DK, DV, WL, FMT> rp;
     rp.init(lane, view.k_tok, view.v_tok, view.ksf_tok, view.vsf_tok);
+    if constexpr (C::piece(ROPE)) cc.rotate_k(rp, lane);
     cc.init(rp, wave);
   }
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
@@ -903,15 +950,22 @@ void prefill_coop_kernel(AttnArgs a) {
     const uint32_t rs = __builtin_amdgcn_readfirstlane(raw0 + ((i + 1) % 3) * C::RAW_STAGE);
     const uint32_t ob1 = __builtin_amdgcn_readfirstlane(opb0 + ((i + 1) & 1) * C::OPB);
     if constexpr (C::WIDE) {
-      // the next step's operands first: placed beside the products (raw bytes read
-      // before them, operands written after) the kernel measured 8 % slower
-      if (next) {
+      // The two waves of a SIMD take the step's two parts in opposite orders: one
+      // dequantises its share of the next step and then computes this one, the other
+      // computes first, so that one wave's vector and LDS work runs beside the other's
+      // products.  The one barrier a step covers both orders.  Waves w and w + 4 share a
+      // SIMD when waves are placed round robin, w and w + 1 when in pairs: this split
+      // separates both.
+      const bool late = ((wave ^ (wave >> 2)) & 1) != 0;  // uniform
+      auto dequant_next = [&]() {
+        if (!next) return;
         if (t_of(i + 1) + kDecodeStep - 1 > tlast)
           coop_dequant<DK, DV, true, FMT, ROPE>(rs, ob1, wave, cl, tlast - t_of(i + 1),
                                                 (float)t_of(i + 1));
         else
           coop_dequant<DK, DV, false, FMT, ROPE>(rs, ob1, wave, cl, 0, (float)t_of(i + 1));
-      }
+      };
+      if (!late) dequant_next();
       f32x4 sa[NR], sb[NR];
 #pragma unroll
       for (int rg = 0; rg < NR; ++rg) {
@@ -977,6 +1031,7 @@ void prefill_coop_kernel(AttnArgs a) {
         if (e + PF - 1 < S::NT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, NR, 0);
       }
+      if (late) dequant_next();
       return;
     }
     // Two straight-line blocks.  The first reads this step's K operands and the next
