@@ -693,10 +693,13 @@ __device__ __forceinline__ bool load_q_scaled(const uint16_t* qrow, bool valid, 
 #pragma unroll
     for (int i = 0; i < QW; ++i) qraw[i] = 0u;
   }
-  float qmax = 0.f;
+  // the largest magnitude as the largest sign-cleared bit pattern (see load_q_operand)
+  typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+  u16x2 mb = {0, 0};
 #pragma unroll
   for (int i = 0; i < QW; ++i)
-    qmax = fmaxf(qmax, fmaxf(fabsf(bf16f(qraw[i] & 0xFFFF)), fabsf(bf16f(qraw[i] >> 16))));
+    mb = __builtin_elementwise_max(mb, __builtin_bit_cast(u16x2, qraw[i] & 0x7FFF7FFFu));
+  const float qmax = __uint_as_float((uint32_t)(mb[0] > mb[1] ? mb[0] : mb[1]) << 16);
 #pragma unroll
   for (int s = 0; s < DK / 32; ++s) {
     f16x2 p[4];
@@ -861,8 +864,6 @@ void prefill_coop_kernel(AttnArgs a) {
     if constexpr (ROPE) {
       qrows[rg] = qrow;
       qpos_f[rg] = (float)(qpos + off);  // the query's position
-    } else if constexpr (C::WIDE) {
-      sc[rg] = a.score_scale * load_q_operand<DK>(qrow, rv[rg], j, qf[rg]);
     } else {
       safe = load_q_scaled<DK>(qrow, rv[rg], j, a.score_scale, qf[rg]) && safe;
     }
@@ -891,8 +892,10 @@ void prefill_coop_kernel(AttnArgs a) {
 #pragma unroll
     for (int rg = 0; rg < NR; ++rg) safe = amax[rg] < 32768.f && safe;
   }
-  const bool shifted = !C::WIDE && __all(safe);
-  if (!C::WIDE && !shifted) {
+  // (the rotary wide kernel keeps the exact prescaled Q and the plain softmax)
+  constexpr bool SHIFTABLE = !(ROPE && C::WIDE);
+  const bool shifted = SHIFTABLE && __all(safe);
+  if (SHIFTABLE && !shifted) {
     if constexpr (ROPE) {
       rope_prescaled();
     } else {
@@ -933,7 +936,7 @@ void prefill_coop_kernel(AttnArgs a) {
   // and compute this one.  MASK: some key of the step is past some row's limit.
   auto step = [&](int i, auto mask_tag, auto shift_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    constexpr bool SHIFT = decltype(shift_tag)::value && !C::WIDE;
+    constexpr bool SHIFT = decltype(shift_tag)::value && SHIFTABLE;
     const bool next = i + 1 < nsteps;
     // raw step i+1 landed (only step i+2 may still be in flight); operands of step i
     // are visible; nobody reads operand buffer (i+1)%2 or raw stage i%3 any more
@@ -969,8 +972,8 @@ void prefill_coop_kernel(AttnArgs a) {
       f32x4 sa[NR], sb[NR];
 #pragma unroll
       for (int rg = 0; rg < NR; ++rg) {
-        sa[rg] = f32x4{0.f, 0.f, 0.f, 0.f};
-        sb[rg] = f32x4{0.f, 0.f, 0.f, 0.f};
+        sa[rg] = SHIFT ? sr[rg].negr : f32x4{0.f, 0.f, 0.f, 0.f};
+        sb[rg] = sa[rg];
       }
       // K operands PF - 1 k-steps ahead of their products, the order pinned by
       // scheduling groups: left to itself the compiler moves every read next to its
@@ -1001,17 +1004,42 @@ void prefill_coop_kernel(AttnArgs a) {
         __builtin_amdgcn_sched_group_barrier(0x008, 2 * NR, 0);
       }
       __builtin_amdgcn_s_setprio(0);
-      f16x8 p[NR];
+      // softmax as in the narrower kernels: scores, the rare reference move, then P
+      float x[NR][8], bm[NR];
+      const bool first = i == 0;  // uniform
+      auto vote = [&](int rg) -> bool {
+        if constexpr (SHIFT)
+          return first || bm[rg] > kRescaleSlack || (MASK && st[rg].m == -INFINITY);
+        else
+          return st[rg].wants(bm[rg], sc[rg]);
+      };
+      uint64_t want = 0;
 #pragma unroll
       for (int rg = 0; rg < NR; ++rg) {
         if (MASK && custom)
-          p[rg] = st[rg].softmax_vis(sa[rg], sb[rg], sc[rg],
-                                     coop_mask_bits<DK, DV, FMT>(cm, row_base + rg * 16 + n, j, G,
-                                                                 q0, kv_len, kv0, t0, tlast));
+          bm[rg] = st[rg].scores_vis(sa[rg], sb[rg],
+                                     coop_mask_bits<DK, DV, FMT>(cm, row_base + rg * 16 + n, j, G, q0,
+                                                                 kv_len, kv0, t0, tlast),
+                                     x[rg]);
         else
-          p[rg] = st[rg].template softmax<MASK>(sa[rg], sb[rg], sc[rg], t0, j,
-                                                MASK ? last_of(rg) : 0);
+          bm[rg] = st[rg].template scores<MASK>(sa[rg], sb[rg], t0, j, MASK ? last_of(rg) : 0, x[rg]);
+        want |= __ballot(vote(rg));
       }
+      if (want != 0) {
+#pragma unroll
+        for (int rg = 0; rg < NR; ++rg) {
+          if (__ballot(vote(rg)) != 0) {
+            if constexpr (SHIFT)
+              raise_shifted(st[rg], sr[rg], bm[rg], x[rg]);
+            else
+              st[rg].raise(bm[rg], sc[rg]);
+          }
+        }
+      }
+      f16x8 p[NR];
+#pragma unroll
+      for (int rg = 0; rg < NR; ++rg)
+        p[rg] = SHIFT ? probs_shifted(st[rg], x[rg]) : st[rg].template probs<MASK>(x[rg], sc[rg]);
       f16x8 vt[PF];
       auto vload = [&](int e) {
         lds_load<16>(obl + (2 * S::NS + e) * 1024, reinterpret_cast<uint32_t*>(&vt[e % PF]));

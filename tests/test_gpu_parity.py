@@ -278,7 +278,7 @@ def test_prefill_unequal_strides():
     _run_case(w, k_pad=(1, 1, 3, 16), v_pad=(2, 0, 1, 32), chunk=-1)
 
 
-@pytest.mark.parametrize("dk,dv", [(128, 128), (256, 256), (64, 64)])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (256, 256), (64, 64), (512, 256)])
 def test_prefill_extreme_q_magnitudes(dk, dv):
     """Query rows scaled by 2^18 (|q sm_scale log2 e| far above fp16's range: those waves
     take the exactly prescaled Q) next to rows scaled by 2^-20 (fp16 subnormals once
