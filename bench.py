@@ -267,20 +267,24 @@ def timed_passes(torch, nv, run, merge, iters):
             float(np.mean([he.ms(e[2], e[3]) for e in ev])))
 
 
-def extra_decode(torch, nv, paged, synth, name, iters=100, warm=20, cpu_budget=0.0):
+def extra_decode(torch, nv, paged, synth, name, iters=100, warm=20, cpu_budget=0.0,
+                 pool_sets=3):
+    """One decode workload's line, over ``pool_sets`` rotated pool sets like the main line
+    (a workload smaller than the 256 MB Infinity Cache would otherwise be read from it)."""
     w = synth.workload(name)
-    case = paged.build_case(w, keep_sources=False)
+    cases = [paged.build_case(w, keep_sources=False) for _ in range(pool_sets)]
+    case = cases[0]
     plan = paged.make_plan(case)
     plan.set_deferred_merge(True)
     ws = plan.new_workspace()
     plan.upload(ws)
     o = torch.empty((w.batch, w.num_qo_heads, w.head_dim_vo), device="cuda")
     lse = torch.empty((w.batch, w.num_qo_heads), device="cuda")
-    run = nv.batch_decode(plan, case.q, case.page_table, case.k_pool, case.v_pool, w.sm_scale,
-                          ws, out=o, lse=lse, prepare=True)
+    run = [nv.batch_decode(plan, c.q, c.page_table, c.k_pool, c.v_pool, w.sm_scale, ws, out=o,
+                           lse=lse, prepare=True) for c in cases]
     merge = nv.merge_partials(plan, ws, o, lse, prepare=True)
-    for _ in range(warm):
-        run()
+    for i in range(warm):
+        run[i % pool_sets]()
         merge()
     run_ms, merge_ms = timed_passes(torch, nv, run, merge, iters)
     del run, merge
@@ -290,30 +294,33 @@ def extra_decode(torch, nv, paged, synth, name, iters=100, warm=20, cpu_budget=0
            "kernel_GBs": round((kv + qo) / run_ms / 1e6, 1),
            "kernel_frac_hbm": round((kv + qo) / run_ms / 1e6 / HBM_PEAK_GBS, 4),
            "attn_ms": round(run_ms, 4), "merge_ms": round(merge_ms, 4), "kv_bytes": kv,
-           "chunk": info["kv_chunk_tokens"], "work_items": info["num_work_items"]}
+           "chunk": info["kv_chunk_tokens"], "work_items": info["num_work_items"],
+           "pool_sets_rotated": pool_sets}
     if w.page_size >= 16:
-        out["stream_ceiling"] = stream_ceiling(torch, nv, plan, [case], ws, iters, kv, run_ms)
+        out["stream_ceiling"] = stream_ceiling(torch, nv, plan, cases, ws, iters, kv, run_ms)
     if cpu_budget > 0:
         out["cpu_baseline"] = cpu_baseline(case, cpu_budget, cpu_threads())
-    del case, ws
+    del case, cases, ws
     torch.cuda.empty_cache()
     return out
 
 
-def extra_prefill(torch, nv, paged, synth, name, iters=40, warm=10, cpu_budget=0.0):
+def extra_prefill(torch, nv, paged, synth, name, iters=40, warm=10, cpu_budget=0.0,
+                  pool_sets=3):
     w = synth.workload(name)
-    case = paged.build_case(w, keep_sources=False)
+    cases = [paged.build_case(w, keep_sources=False) for _ in range(pool_sets)]
+    case = cases[0]
     plan = paged.make_plan(case)
     plan.set_deferred_merge(True)
     ws = plan.new_workspace()
     plan.upload(ws)
     o = torch.empty((w.total_q, w.num_qo_heads, w.head_dim_vo), device="cuda")
     lse = torch.empty((w.total_q, w.num_qo_heads), device="cuda")
-    run = nv.batch_prefill(plan, case.q, case.page_table, case.k_pool, case.v_pool, w.sm_scale,
-                           ws, out=o, lse=lse, prepare=True)
+    run = [nv.batch_prefill(plan, c.q, c.page_table, c.k_pool, c.v_pool, w.sm_scale, ws, out=o,
+                            lse=lse, prepare=True) for c in cases]
     merge = nv.merge_partials(plan, ws, o, lse, prepare=True)
-    for _ in range(warm):
-        run()
+    for i in range(warm):
+        run[i % pool_sets]()
         merge()
     run_ms, merge_ms = timed_passes(torch, nv, run, merge, iters)
     del run, merge
@@ -323,10 +330,11 @@ def extra_prefill(torch, nv, paged, synth, name, iters=40, warm=10, cpu_budget=0
            "kernel_TFLOPs": round(fl / run_ms / 1e9, 2),
            "kernel_frac_mfma_f16": round(fl / run_ms / 1e9 / MFMA_F16_PEAK_TFLOPS, 4),
            "attn_ms": round(run_ms, 4), "merge_ms": round(merge_ms, 4), "flops": fl,
-           "work_items": info["num_work_items"], "chunk": info["kv_chunk_tokens"]}
+           "work_items": info["num_work_items"], "chunk": info["kv_chunk_tokens"],
+           "pool_sets_rotated": pool_sets}
     if cpu_budget > 0:
         out["cpu_baseline"] = cpu_baseline(case, cpu_budget, cpu_threads())
-    del case, ws
+    del case, cases, ws
     torch.cuda.empty_cache()
     return out
 
