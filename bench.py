@@ -305,8 +305,11 @@ def extra_decode(torch, nv, paged, synth, name, iters=100, warm=20, cpu_budget=0
     return out
 
 
-def extra_prefill(torch, nv, paged, synth, name, iters=40, warm=10, cpu_budget=0.0,
+def extra_prefill(torch, nv, paged, synth, name, iters=40, warm=40, cpu_budget=0.0,
                   pool_sets=3):
+    """One prefill workload's line.  The first prefill line of a run follows the decode
+    lines; with ten warm-up passes it measured about 8 % below the same kernel timed
+    later in the run, so the warm-up is forty passes."""
     w = synth.workload(name)
     cases = [paged.build_case(w, keep_sources=False) for _ in range(pool_sets)]
     case = cases[0]
