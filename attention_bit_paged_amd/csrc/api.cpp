@@ -202,7 +202,7 @@ struct nvfp4_plan {
   int num_partials = 0;
   // workspace layout (byte offsets)
   size_t off_work = 0, off_merge = 0, off_kvlens = 0, off_indptr = 0, off_pt = 0, off_mask = 0,
-         off_rope = 0, off_part_o = 0, off_part_lse = 0, ws_bytes = 0;
+         off_rope = 0, off_part_o = 0, off_part_lse = 0, off_part_scale = 0, ws_bytes = 0;
   std::vector<uint8_t> image;  // the tables as they sit at the start of the workspace
   void* uploaded_to = nullptr;
   int defer_merge = 0;  // runs leave split rows' partials for nvfp4_merge_partials
@@ -528,9 +528,11 @@ nvfp4_status nvfp4_plan_create_ex(const int32_t* kv_lens, const int32_t* qo_indp
   plan->off_rope = off;  // RoPE plans: the frequency pairs
   off = align_up(off + plan->rope_freq.size() * sizeof(float));
   plan->off_part_o = off;
-  off = align_up(off + (size_t)plan->num_partials * plan->rows_per_slot * head_dim_vo * sizeof(float));
+  off = align_up(off + (size_t)plan->num_partials * plan->rows_per_slot * head_dim_vo * sizeof(_Float16));
   plan->off_part_lse = off;
   off = align_up(off + (size_t)plan->num_partials * plan->rows_per_slot * sizeof(float));
+  plan->off_part_scale = off;
+  off = align_up(off + sizeof(float));
   plan->ws_bytes = std::max<size_t>(off, kAlign);
   // the uploaded part of the workspace, built once
   plan->image.assign(plan->off_part_o, 0);
@@ -706,8 +708,9 @@ AttnArgs make_args(const nvfp4_plan* plan, const void* q, int64_t q_s_row, int64
   a.o_s_row = o_s_row;
   a.o_s_head = o_s_head;
   a.lse = lse;
-  a.part_o = reinterpret_cast<float*>(w + plan->off_part_o);
+  a.part_o = reinterpret_cast<_Float16*>(w + plan->off_part_o);
   a.part_lse = reinterpret_cast<float*>(w + plan->off_part_lse);
+  a.part_scale = reinterpret_cast<float*>(w + plan->off_part_scale);
   a.num_qo_heads = plan->num_qo_heads;
   a.group = plan->group;
   a.page_shift = log2i(plan->page_size);
@@ -1016,8 +1019,9 @@ nvfp4_status nvfp4_merge_partials(const nvfp4_plan* plan, void* workspace, size_
   a.o_s_row = o_stride_row;
   a.o_s_head = o_stride_head;
   a.lse = lse;
-  a.part_o = reinterpret_cast<float*>(w + plan->off_part_o);
+  a.part_o = reinterpret_cast<_Float16*>(w + plan->off_part_o);
   a.part_lse = reinterpret_cast<float*>(w + plan->off_part_lse);
+  a.part_scale = reinterpret_cast<float*>(w + plan->off_part_scale);
   a.num_qo_heads = plan->num_qo_heads;
   a.group = plan->group;
   a.rows_per_slot = plan->rows_per_slot;

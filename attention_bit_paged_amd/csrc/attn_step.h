@@ -475,6 +475,31 @@ struct RowState {
     for (int e = 0; e < NT; ++e) acc[e] = mfma16x16x32(vt[e], p, acc[e]);
   }
 
+  // A split work item's partial state: this lane's part of the row normalised by its own
+  // row sum, in fp16 (the layout of store), and its LSE.  The global V scale is left to
+  // the merge, so the values stay within fp16's range: a normalised row is a convex
+  // combination of dequantised values (|v| <= 6 x 448).  Each value is rounded once, a
+  // relative error of at most 2^-11.
+  __device__ __forceinline__ void store_partial(_Float16* dst, float* lse_dst, bool valid, bool bad,
+                                                int j) {
+    typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+    const float l_tot = sum_over_groups(l);
+    const bool empty = !(l_tot > 0.f);
+    const float inv = bad ? NAN : (empty ? 0.f : 1.f / l_tot);
+    const float lse_v =
+        bad ? NAN : (empty ? -INFINITY : (m + fast_log2(l_tot)) * 0.69314718055994531f);
+    if (!valid) return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f16x4* row = reinterpret_cast<f16x4*>(dst + (4 * j + i) * NT);
+#pragma unroll
+      for (int e = 0; e < NT; e += 4)
+        row[e / 4] = f16x4{(_Float16)(acc[e][i] * inv), (_Float16)(acc[e + 1][i] * inv),
+                           (_Float16)(acc[e + 2][i] * inv), (_Float16)(acc[e + 3][i] * inv)};
+    }
+    if (j == 0) *lse_dst = lse_v;
+  }
+
   // Normalise and store this lane's part of the row: value dims (4j+i)*NT + e.  The row
   // sum is first completed over the four lanes of the row.
   __device__ __forceinline__ void store(float* dst, float* lse_dst, bool valid, bool bad,

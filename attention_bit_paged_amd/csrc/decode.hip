@@ -87,8 +87,8 @@ __device__ __forceinline__ void decode_epilogue(const AttnArgs& a, RowState<DV /
   if (slot < 0) {
     st.store(o_dst, lse_dst, head_valid, bad, a.out_scale, j);
   } else {
-    st.store(a.part_o + ((int64_t)slot * a.rows_per_slot + n) * DV,
-             a.part_lse + (int64_t)slot * a.rows_per_slot + n, head_valid, bad, a.out_scale, j);
+    st.store_partial(a.part_o + ((int64_t)slot * a.rows_per_slot + n) * DV,
+                     a.part_lse + (int64_t)slot * a.rows_per_slot + n, head_valid, bad, j);
   }
 }
 
@@ -241,6 +241,7 @@ void decode_ring_kernel(AttnArgs a) {
   const int j = lane >> 4;
   const int n = lane & 15;
   const DecodeItem it = decode_item(a, wave, n);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *a.part_scale = a.out_scale;  // for the merge
 
   PagedView<DK, DV, true, FMT> view;
   view.init(a, it.b, it.kvh, lane);
@@ -447,6 +448,7 @@ __global__ __launch_bounds__(256) void decode_regs_kernel(AttnArgs a) {
   const int j = lane >> 4;
   const int n = lane & 15;
   const DecodeItem it = decode_item(a, wave, n);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *a.part_scale = a.out_scale;  // for the merge
 
   f16x8 qf[S::NS];
   const float score_c = a.score_scale *

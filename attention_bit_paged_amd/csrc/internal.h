@@ -53,8 +53,13 @@ struct AttnArgs {
   float* o;
   int64_t o_s_row, o_s_head;
   float* lse;               // [rows, num_qo_heads]
-  float* part_o;            // [slots, rows_per_slot, head_dim_vo]
+  // [slots, rows_per_slot, head_dim_vo] in fp16, without the global V scale (the merge
+  // applies it)
+  _Float16* part_o;
   float* part_lse;          // [slots, rows_per_slot]
+  // one float of the workspace: the global V scale of the last attention launch, which
+  // the merge applies to the partials (written by the first workgroup of every launch)
+  float* part_scale;
   int32_t num_qo_heads;
   int32_t group;            // qo heads per kv head
   int32_t page_shift;       // log2(page_size)

@@ -25,7 +25,8 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 // Partials of split row groups, after the attention kernel: one wave per (merge
 // record, row).  A row is one qo head of the group (decode) or one (query, qo head) pair
-// of a query tile (prefill); each partial holds a normalised O row and its LSE.  Lane
+// of a query tile (prefill); each partial holds a normalised O row (fp16, without the
+// global V scale, which is applied here) and its LSE.  Lane
 // p reads partial p's LSE; each lane sums its DV/64 value dims over the partials.  With
 // at most FAST partials every load is issued at once, before any weight is known, so
 // the merge costs one memory round trip after the record; more partials are taken 64
@@ -63,26 +64,15 @@ __global__ __launch_bounds__(256) void merge_partials_kernel(AttnArgs a, int n_m
   constexpr int PER = DV / 64;  // lane covers value dims [lane * PER, (lane + 1) * PER)
   const int64_t rps = a.rows_per_slot;
   const int64_t row_of_first = (int64_t)first * rps + r;  // partial p: row_of_first + p * rps
-  const float* src = a.part_o + row_of_first * DV + lane * PER;
+  const _Float16* src = a.part_o + row_of_first * DV + lane * PER;
   const int64_t step = rps * DV;
   auto lse_of = [&](int p) { return p < np ? a.part_lse[row_of_first + (int64_t)p * rps] : -INFINITY; };
-  auto load_row = [&](const float* s, float (&v)[PER]) {
-    if constexpr (PER == 1) {
-      v[0] = s[0];
-    } else if constexpr (PER == 2) {
-      const float2 x = *reinterpret_cast<const float2*>(s);
-      v[0] = x.x;
-      v[1] = x.y;
-    } else {
+  // PER consecutive fp16 values in one load (2, 4, 8 or 16 bytes)
+  auto load_row = [&](const _Float16* s, float (&v)[PER]) {
+    typedef _Float16 hv __attribute__((ext_vector_type(PER)));
+    const hv x = *reinterpret_cast<const hv*>(s);
 #pragma unroll
-      for (int k = 0; k < PER; k += 4) {
-        const float4 x = *reinterpret_cast<const float4*>(s + k);
-        v[k] = x.x;
-        v[k + 1] = x.y;
-        v[k + 2] = x.z;
-        v[k + 3] = x.w;
-      }
-    }
+    for (int k = 0; k < PER; ++k) v[k] = (float)x[k];
   };
   auto lane_weight = [&](float w, int q) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), q));
@@ -131,7 +121,7 @@ __global__ __launch_bounds__(256) void merge_partials_kernel(AttnArgs a, int n_m
         const float w = lp > -INFINITY ? __expf(lp - mx) : 0.f;  // weight of partial p0 + lane
         wsum += w;
         const int cnt = min(64, np - p0);
-        const float* base = src + (int64_t)p0 * step;
+        const _Float16* base = src + (int64_t)p0 * step;
         auto add = [&](int q) {
           const float wq = lane_weight(w, q);
           float v[PER];
@@ -149,7 +139,7 @@ __global__ __launch_bounds__(256) void merge_partials_kernel(AttnArgs a, int n_m
       wsum = wave_sum(wsum);
     }
   }
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  const float inv = wsum > 0.f ? *a.part_scale / wsum : 0.f;
   float* dst = a.o + orow * a.o_s_row + (int64_t)head * a.o_s_head + lane * PER;
 #pragma unroll
   for (int k = 0; k < PER; ++k) dst[k] = any_nan ? NAN : acc[k] * inv;

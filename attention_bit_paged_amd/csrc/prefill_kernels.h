@@ -60,6 +60,7 @@ __global__ __launch_bounds__(256) void prefill_regs_kernel(AttnArgs a) {
   const int j = lane >> 4;
   const int n = lane & 15;
   const int32_t* rec = a.work + (int64_t)blockIdx.x * kWorkFields;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *a.part_scale = a.out_scale;  // for the merge
   const int b = rec[W_REQ], kvh = rec[W_KVH], q0 = rec[W_ROW0], qn = rec[W_ROWS];
   const int kv0 = rec[W_KV0], kv1 = rec[W_KV1], slot = rec[W_SLOT];
   const int G = a.group;
@@ -207,8 +208,8 @@ __global__ __launch_bounds__(256) void prefill_regs_kernel(AttnArgs a) {
 #pragma unroll
     for (int rg = 0; rg < NR; ++rg) {
       const int r = row_base + rg * 16 + n;
-      st[rg].store(a.part_o + ((int64_t)slot * a.rows_per_slot + r) * DV,
-                   a.part_lse + (int64_t)slot * a.rows_per_slot + r, rv[rg], bad, a.out_scale, j);
+      st[rg].store_partial(a.part_o + ((int64_t)slot * a.rows_per_slot + r) * DV,
+                   a.part_lse + (int64_t)slot * a.rows_per_slot + r, rv[rg], bad, j);
     }
   }
 }
@@ -785,6 +786,7 @@ void prefill_coop_kernel(AttnArgs a) {
   const int j = lane >> 4;
   const int n = lane & 15;
   const int32_t* rec = a.work + (int64_t)blockIdx.x * kWorkFields;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *a.part_scale = a.out_scale;  // for the merge
   const int b = rec[W_REQ], kvh = rec[W_KVH], q0 = rec[W_ROW0], qn = rec[W_ROWS];
   const int kv0 = rec[W_KV0], kv1 = rec[W_KV1], slot = rec[W_SLOT];
   const int G = a.group;
@@ -1181,8 +1183,8 @@ void prefill_coop_kernel(AttnArgs a) {
                    a.lse + tokrow[rg] * a.num_qo_heads + headi[rg], rv[rg], bad_any, a.out_scale, j);
     } else {
       const int r = row_base + rg * 16 + n;
-      st[rg].store(a.part_o + ((int64_t)slot * a.rows_per_slot + r) * DV,
-                   a.part_lse + (int64_t)slot * a.rows_per_slot + r, rv[rg], bad_any, a.out_scale, j);
+      st[rg].store_partial(a.part_o + ((int64_t)slot * a.rows_per_slot + r) * DV,
+                   a.part_lse + (int64_t)slot * a.rows_per_slot + r, rv[rg], bad_any, j);
     }
   }
 }

@@ -259,9 +259,11 @@ nvfp4_status nvfp4_plan_upload(nvfp4_plan* plan, void* workspace, size_t workspa
  *      scores).  A request with kv_len 0 gets O = 0 and LSE = -inf.
  *   sm_scale: finite and > 0; scores are sm_scale * q.k (times the K pool's
  *      global scale).
- * Split work items write partial states into the workspace; a merge kernel on the
- * same stream then combines them by LSE ([XQA] changelog: mergeAndSaveOutTile),
- * unless the plan defers it (nvfp4_plan_set_deferred_merge).
+ * Split work items write partial states into the workspace (each row normalised by its
+ * own sum, in fp16, and its LSE; the run also records v_pool's global scale there); a
+ * merge kernel on the same stream then combines them by LSE ([XQA] changelog:
+ * mergeAndSaveOutTile) and applies the scale, unless the plan defers it
+ * (nvfp4_plan_set_deferred_merge).
  */
 nvfp4_status nvfp4_batch_decode(const nvfp4_plan* plan, const void* q, int64_t q_stride_req,
                                 int64_t q_stride_head, const int32_t* page_table, int64_t pt_stride,
