@@ -720,6 +720,7 @@ AttnArgs make_args(const nvfp4_plan* plan, const void* q, int64_t q_s_row, int64
   // heads within 256 bytes of each other share cache lines / DRAM bursts: keep the
   // heads of one key range on one XCD (decode)
   a.xcd_group = !plan->prefill && (std::min(k->stride_head, v->stride_head) <= 256);
+  a.stream_kv = !plan->prefill && !a.xcd_group;
   a.rope = plan->rope ? reinterpret_cast<const float*>(w + plan->off_rope) : nullptr;
   return a;
 }

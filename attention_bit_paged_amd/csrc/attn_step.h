@@ -79,6 +79,7 @@ struct PagedView {
   int64_t k_page, k_tok, ksf_page, ksf_tok, v_page, v_tok, vsf_page, vsf_tok;
   int j, n;
   uint32_t bad;
+  int stream;  // the ring copies may take the non-temporal policy (AttnArgs::stream_kv)
 
   __device__ __forceinline__ void init(const AttnArgs& a, int b, int kvh, int lane) {
     j = lane >> 4;
@@ -94,6 +95,7 @@ struct PagedView {
     k_page = a.k.s_page; k_tok = a.k.s_tok; ksf_page = a.k.sf_page; ksf_tok = a.k.sf_tok;
     v_page = a.v.s_page; v_tok = a.v.s_tok; vsf_page = a.v.sf_page; vsf_tok = a.v.sf_tok;
     bad = 0;
+    stream = a.stream_kv;
   }
 
   // A page-table entry; one outside [0, num_pages) marks the view bad and reads page 0

@@ -23,6 +23,10 @@ namespace nvfp4 {
 
 namespace {
 
+// Decode reads each K/V byte once per launch: every pool's copies, non-temporal (the
+// work records, page table and split partials stay cached; 5-10 % faster measured).
+constexpr int kDecodePools = 0xF | kStreamCopies;
+
 // Workgroups (of four waves) one CU holds at once, by design.  Registers: 512 VGPRs
 // per SIMD lane are shared by the waves on a SIMD, and the kernels of each shape are
 // held to the budget of this many waves (amdgpu_waves_per_eu).  LDS: 160 KiB per CU,
@@ -262,8 +266,8 @@ void decode_ring_kernel(AttnArgs a) {
 #pragma unroll
   for (int s = 0; s < R::NST - 1; ++s)
     if (s < nsteps)
-      ring_issue<DK, DV, WL>(rp, ring_lds + s * R::STAGE, view, it.w0 + s * kDecodeStep, tlast,
-                             bad);
+      ring_issue<DK, DV, WL, kDecodePools>(rp, ring_lds + s * R::STAGE, view,
+                                            it.w0 + s * kDecodeStep, tlast, bad);
   // Q (and the new token's rows) after the first copies, so that their loads overlap
   f16x8 qf[S::NS];
   const float score_c = a.score_scale *
@@ -307,8 +311,8 @@ void decode_ring_kernel(AttnArgs a) {
       const int ahead = i + R::NST - 1;
       const bool more = ahead < nsteps;
       if (more)
-        ring_issue<DK, DV, WL>(rp, ring_lds + ((s + R::NST - 1) % R::NST) * R::STAGE, view,
-                           it.w0 + ahead * kDecodeStep, tlast, bad);
+        ring_issue<DK, DV, WL, kDecodePools>(rp, ring_lds + ((s + R::NST - 1) % R::NST) * R::STAGE,
+                                            view, it.w0 + ahead * kDecodeStep, tlast, bad);
       ring_wait_sel<(R::NST - 1) * R::NDMA>(lanes, more);
       StepRaw<DK, DV, FMT> raw;
       ring_read<DK, DV, FMT>(lanes, s * R::STAGE, raw);
@@ -405,8 +409,8 @@ void kv_checksum_kernel(AttnArgs a, uint32_t* out, int num_kv_heads) {
 #pragma unroll
   for (int s = 0; s < R::NST - 1; ++s)
     if (s < nsteps)
-      ring_issue<DK, DV, WL>(rp, ring_lds + s * R::STAGE, view, it.w0 + s * kDecodeStep, tlast,
-                             bad);
+      ring_issue<DK, DV, WL, kDecodePools>(rp, ring_lds + s * R::STAGE, view,
+                                            it.w0 + s * kDecodeStep, tlast, bad);
   uint32_t x = 0;
   for (int i0 = 0; i0 < nfull; i0 += R::NST) {
 #pragma unroll
@@ -416,8 +420,8 @@ void kv_checksum_kernel(AttnArgs a, uint32_t* out, int num_kv_heads) {
       const int ahead = i + R::NST - 1;
       const bool more = ahead < nsteps;
       if (more)
-        ring_issue<DK, DV, WL>(rp, ring_lds + ((s + R::NST - 1) % R::NST) * R::STAGE, view,
-                               it.w0 + ahead * kDecodeStep, tlast, bad);
+        ring_issue<DK, DV, WL, kDecodePools>(rp, ring_lds + ((s + R::NST - 1) % R::NST) * R::STAGE,
+                                              view, it.w0 + ahead * kDecodeStep, tlast, bad);
       ring_wait_sel<(R::NST - 1) * R::NDMA>(lanes, more);
       x ^= fold_stage<DK, DV, WL, false, FMT>(lanes.k, lanes.ks, s * R::STAGE, lane, 0);
     }

@@ -68,6 +68,10 @@ struct AttnArgs {
   // Decode: deal each run of 64 work items to the XCDs in groups of eight consecutive
   // items (see decode_item); set when the pools interleave kv heads at a short stride.
   int32_t xcd_group;
+  // Decode: the K/V copies take the non-temporal cache policy (kStreamCopies), since
+  // each byte is read by one work item; clear when the heads share cache lines
+  // (xcd_group), whose other head's item reads them again.
+  int32_t stream_kv;
   const int32_t* merges;    // merge records
   // Prefill with a custom mask (else null): packed bits, and each request's byte offset
   // into them (device, from the workspace).

@@ -98,30 +98,48 @@ struct RingShape {
 // not declared to touch memory: they only write this wave's ring, whose reads take
 // their addresses from the wait below, so the compiler cannot move them above it.
 // Keeping the global view unclobbered lets the page-table reads stay scalar loads.
-template <bool X4>
+// NT: the copy carries the non-temporal cache policy, for bytes that one launch reads
+// once (decode): they then do not displace from the caches what is read again, the
+// work records, the page table and the partial rows.
+// A flag beside the pool bits of ring_issue: the step's copies take the non-temporal
+// policy.
+constexpr int kStreamCopies = 0x10;
+#define NVFP4_DMA_X4(nt) "s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" nt
+#define NVFP4_DMA_X1(nt) "s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" nt
+template <bool X4, bool NT = false>
 __device__ __forceinline__ void dma(uint32_t m0, uint32_t voff, const uint8_t* sbase) {
-  if constexpr (X4)
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-                 :: "s"(m0), "v"(voff), "s"(sbase));
+  if constexpr (X4 && NT)
+    asm volatile(NVFP4_DMA_X4(" nt") :: "s"(m0), "v"(voff), "s"(sbase));
+  else if constexpr (X4)
+    asm volatile(NVFP4_DMA_X4("") :: "s"(m0), "v"(voff), "s"(sbase));
+  else if constexpr (NT)
+    asm volatile(NVFP4_DMA_X1(" nt") :: "s"(m0), "v"(voff), "s"(sbase));
   else
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
-                 :: "s"(m0), "v"(voff), "s"(sbase));
+    asm volatile(NVFP4_DMA_X1("") :: "s"(m0), "v"(voff), "s"(sbase));
 }
 // The same copy for the lanes in (LO, HI) only; exec is restored inside the statement.
-template <bool X4, int LO, int HI>
+#define NVFP4_DMA_MASKED(op, nt)                                                        \
+  "s_mov_b64 %0, exec\n\ts_mov_b32 exec_lo, %4\n\ts_mov_b32 exec_hi, %5\n\t"            \
+  "s_mov_b32 m0, %1\n\ts_nop 0\n\t" op " %2, %3" nt "\n\ts_mov_b64 exec, %0"
+template <bool X4, int LO, int HI, bool NT = false>
 __device__ __forceinline__ void dma_masked(uint32_t m0, uint32_t voff, const uint8_t* sbase) {
   uint64_t save;
-  if constexpr (X4)
-    asm volatile("s_mov_b64 %0, exec\n\ts_mov_b32 exec_lo, %4\n\ts_mov_b32 exec_hi, %5\n\t"
-                 "s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3\n\t"
-                 "s_mov_b64 exec, %0"
+  if constexpr (X4 && NT)
+    asm volatile(NVFP4_DMA_MASKED("global_load_lds_dwordx4", " nt")
+                 : "=&s"(save) : "s"(m0), "v"(voff), "s"(sbase), "n"(LO), "n"(HI));
+  else if constexpr (X4)
+    asm volatile(NVFP4_DMA_MASKED("global_load_lds_dwordx4", "")
+                 : "=&s"(save) : "s"(m0), "v"(voff), "s"(sbase), "n"(LO), "n"(HI));
+  else if constexpr (NT)
+    asm volatile(NVFP4_DMA_MASKED("global_load_lds_dword", " nt")
                  : "=&s"(save) : "s"(m0), "v"(voff), "s"(sbase), "n"(LO), "n"(HI));
   else
-    asm volatile("s_mov_b64 %0, exec\n\ts_mov_b32 exec_lo, %4\n\ts_mov_b32 exec_hi, %5\n\t"
-                 "s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, %3\n\t"
-                 "s_mov_b64 exec, %0"
+    asm volatile(NVFP4_DMA_MASKED("global_load_lds_dword", "")
                  : "=&s"(save) : "s"(m0), "v"(voff), "s"(sbase), "n"(LO), "n"(HI));
 }
+#undef NVFP4_DMA_X4
+#undef NVFP4_DMA_X1
+#undef NVFP4_DMA_MASKED
 
 // LDS byte addresses of this lane's reads in stage 0 of its wave's ring.  They pass
 // through every wait (tied asm operands), which both orders the reads after the wait
@@ -189,10 +207,11 @@ __device__ __forceinline__ void issue_group(uint32_t m0, uint32_t voff,
   using R = RingShape<DK, DV, WL, FMT>;
   constexpr uint64_t M = ((POOLS >> (G / 2)) & 1) ? R::mask(C, G) : 0;
   constexpr bool X4 = C < R::N_KD + R::N_VD;
+  constexpr bool NT = (POOLS & kStreamCopies) != 0;
   if constexpr (M == ~uint64_t(0)) {
-    dma<X4>(m0, voff, base[G]);
+    dma<X4, NT>(m0, voff, base[G]);
   } else if constexpr (M != 0) {
-    dma_masked<X4, (int)(uint32_t)M, (int)(uint32_t)(M >> 32)>(m0, voff, base[G]);
+    dma_masked<X4, (int)(uint32_t)M, (int)(uint32_t)(M >> 32), NT>(m0, voff, base[G]);
   }
 }
 
@@ -221,9 +240,10 @@ __device__ __forceinline__ void issue_all(std::integer_sequence<int, Cs...>, uin
 }  // namespace ring_detail
 
 // Issues the copies of the step starting at token t0 into the stage at lds_stage, for
-// the pools in the bit set POOLS (see RingShape::ndma).  Bases of the two 16-token
-// halves come from two page-table entries; a half that starts after tlast reuses the
-// first half's page (its bytes are never used).
+// the pools in the bit set POOLS (see RingShape::ndma), with the non-temporal policy
+// when POOLS holds kStreamCopies and the view allows it (a uniform branch).  Bases of
+// the two 16-token halves come from two page-table entries; a half that starts after
+// tlast reuses the first half's page (its bytes are never used).
 template <int DK, int DV, int WL, int POOLS = 0xF, int FMT = kNvfp4>
 __device__ __forceinline__ void ring_issue(const RingPlan<DK, DV, WL, FMT>& rp, uint32_t lds_stage,
                                            const PagedView<DK, DV, true, FMT>& pv, int t0,
@@ -257,7 +277,15 @@ __device__ __forceinline__ void ring_issue(const RingPlan<DK, DV, WL, FMT>& rp, 
       at(pv.vsf, pg0, s0, pv.vsf_page, pv.vsf_tok),  at(pv.vsf, pg1, s1, pv.vsf_page, pv.vsf_tok)};
   // the previous reads of this stage were consumed already; make sure they completed
   asm volatile("s_waitcnt lgkmcnt(0)");
-  ring_detail::issue_all<DK, DV, WL, FMT, POOLS>(std::make_integer_sequence<int, R::NCOPY>{},
+  constexpr int PLAIN = POOLS & ~kStreamCopies;
+  if constexpr (PLAIN != POOLS) {
+    if (pv.stream) {
+      ring_detail::issue_all<DK, DV, WL, FMT, POOLS>(std::make_integer_sequence<int, R::NCOPY>{},
+                                                      lds_stage, rp, base);
+      return;
+    }
+  }
+  ring_detail::issue_all<DK, DV, WL, FMT, PLAIN>(std::make_integer_sequence<int, R::NCOPY>{},
                                                   lds_stage, rp, base);
 }
 
