@@ -584,12 +584,16 @@ struct CoopMask {
 // The copy offsets of the one pool this wave issues (wave 0: K data, 1: V data, 2 and 3:
 // the scale bytes, whose copies carry both pools' lanes).  The full plan holds every
 // pool's offsets; kept whole in each wave they cost registers the loop needs.
+// RECOMPUTE (FP8 rows at two workgroups per CU, four offsets a wave): the offsets are
+// formed from the lane at each issue instead; held for the loop they were spilled, and
+// the reload before its copy waited for every copy in flight.
 template <int DK, int DV, int FMT = kNvfp4>
 struct CoopCopies {
   using R = RingShape<DK, DV, CoopShape<DK, DV, FMT>::WL, FMT>;
   using Plan = RingPlan<DK, DV, CoopShape<DK, DV, FMT>::WL, FMT>;
   static constexpr int MAXC = R::N_KD > R::N_VD ? (R::N_KD > R::N_SF ? R::N_KD : R::N_SF)
                                                 : (R::N_VD > R::N_SF ? R::N_VD : R::N_SF);
+  static constexpr bool RECOMPUTE = FMT == kFp8 && CoopShape<DK, DV, FMT>::WGS_PER_CU == 2;
   uint32_t mine[MAXC > 0 ? MAXC : 1];
 
   // Pieces: the K copies place piece p of step token t in slot (p + n(t)) % 16 of its
@@ -606,6 +610,7 @@ struct CoopCopies {
     }
   }
   __device__ __forceinline__ void init(const Plan& rp, int wave) {
+    if constexpr (RECOMPUTE) return;
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) {
       const uint32_t kd = c < R::N_KD ? rp.off[c] : 0u;
@@ -635,11 +640,22 @@ __device__ __forceinline__ void coop_issue(int wave, const CoopCopies<DK, DV, FM
                                            int kv0) {
   using C = CoopShape<DK, DV, FMT>;
   constexpr int WL = C::WL;
-  if (wave == 0) ring_issue<DK, DV, WL, 1>(cc.template expand<1>(), stage, view, t0, tlast, bad);
-  else if (wave == 1) ring_issue<DK, DV, WL, 2>(cc.template expand<2>(), stage, view, t0, tlast, bad);
-  else if constexpr (!StepShape<DK, DV, FMT>::F8) {  // FP8 has no scale pools
-    if (wave == 2) ring_issue<DK, DV, WL, 4>(cc.template expand<4>(), stage, view, t0, tlast, bad);
-    else if (wave == 3) ring_issue<DK, DV, WL, 8>(cc.template expand<8>(), stage, view, t0, tlast, bad);
+  if constexpr (CoopCopies<DK, DV, FMT>::RECOMPUTE) {
+    static_assert(StepShape<DK, DV, FMT>::F8, "FP8 only: no scale pools");
+    // opaque at each issue, so that the offsets are formed here (see CoopCopies)
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
+    typename CoopCopies<DK, DV, FMT>::Plan rp;
+    rp.init(lane, view.k_tok, view.v_tok, view.ksf_tok, view.vsf_tok);
+    if (wave == 0) ring_issue<DK, DV, WL, 1>(rp, stage, view, t0, tlast, bad);
+    else if (wave == 1) ring_issue<DK, DV, WL, 2>(rp, stage, view, t0, tlast, bad);
+  } else {
+    if (wave == 0) ring_issue<DK, DV, WL, 1>(cc.template expand<1>(), stage, view, t0, tlast, bad);
+    else if (wave == 1) ring_issue<DK, DV, WL, 2>(cc.template expand<2>(), stage, view, t0, tlast, bad);
+    else if constexpr (!StepShape<DK, DV, FMT>::F8) {  // FP8 has no scale pools
+      if (wave == 2) ring_issue<DK, DV, WL, 4>(cc.template expand<4>(), stage, view, t0, tlast, bad);
+      else if (wave == 3) ring_issue<DK, DV, WL, 8>(cc.template expand<8>(), stage, view, t0, tlast, bad);
+    }
   }
   if (CMASK && wave == 3) {
     const uint32_t slot = cm.ring + (((t0 - kv0) >> 5) & 3) * C::MASK_SLOT;
