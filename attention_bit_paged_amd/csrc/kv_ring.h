@@ -334,6 +334,166 @@ __device__ __forceinline__ void lds_load(uint32_t addr, uint32_t* out) {
   }
 }
 
+// ---- pages smaller than a step's 16-token halves (page_size 1..8) ----
+//
+// A step's 32 tokens then lie on up to 32 pages, so every copy lane forms its own
+// 64-bit address from its token's page.  The step's page-table entries reach LDS by a
+// copy of their own (one 4-byte entry per lane into a 256-byte slot, some steps before
+// the step's data copies need them), so the loop holds no page numbers in registers
+// and every vector-memory operation of the stream is still a counted copy.  Each step
+// then issues its data copies, one per ring copy and without exec masks (lanes past the
+// scale rows fetch token 0's scales into the stage's padding), and one entry copy.
+// Per lane and ring copy C (a constant): the copy's token within the step (t), whether
+// it carries a V row or V scale row (isv; scale copies hold both pools' lanes) and the
+// byte within the token's row.
+template <int DK, int DV, int WL, int FMT, int C>
+struct SmallCopy {
+  using R = RingShape<DK, DV, WL, FMT>;
+  static constexpr bool KD = C < R::N_KD, VD = !KD && C < R::N_KD + R::N_VD;
+  int t, in_row;
+  bool isv;
+  __device__ __forceinline__ explicit SmallCopy(int lane) {
+    if constexpr (KD) {
+      const int b = C * 1024 + 16 * lane;
+      t = b / R::RBK; in_row = b % R::RBK; isv = false;
+    } else if constexpr (VD) {
+      const int b = (C - R::N_KD) * 1024 + 16 * lane;
+      t = b / R::RBV; in_row = b % R::RBV; isv = true;
+    } else {
+      const int b = (C - R::N_KD - R::N_VD) * 256 + 4 * lane;
+      isv = b >= R::KS;
+      const int bv = b - R::KS;
+      // padding lanes (past both scale regions): token 0's K scales, bytes never read
+      const bool pad = bv >= R::VS;
+      t = pad ? 0 : (isv ? bv / R::SBV : b / R::SBK);
+      in_row = pad ? 0 : (isv ? bv % R::SBV : b % R::SBK);
+      isv = isv && !pad;
+    }
+  }
+};
+
+// Loop-invariant part of each copy lane's address: (t mod page_size) * token stride +
+// byte in the row (a step starts on a page boundary: its first token is a multiple of
+// 16).  Strides are below 2^31 and a page holds at most 8 tokens, so it fits 32 bits
+// as the host keeps 16 token strides plus a row there.
+template <int DK, int DV, int WL, int FMT = kNvfp4>
+struct SmallPlan {
+  using R = RingShape<DK, DV, WL, FMT>;
+  uint32_t off[R::NCOPY];
+  template <int C>
+  __device__ __forceinline__ void init_one(int lane, const PagedView<DK, DV, true, FMT>& pv) {
+    const SmallCopy<DK, DV, WL, FMT, C> x(lane);
+    uint32_t ts;
+    if constexpr (SmallCopy<DK, DV, WL, FMT, C>::KD) ts = (uint32_t)pv.k_tok;
+    else if constexpr (SmallCopy<DK, DV, WL, FMT, C>::VD) ts = (uint32_t)pv.v_tok;
+    else ts = x.isv ? (uint32_t)pv.vsf_tok : (uint32_t)pv.ksf_tok;
+    off[C] = (uint32_t)(x.t & pv.page_mask) * ts + (uint32_t)x.in_row;
+  }
+  template <int... Cs>
+  __device__ __forceinline__ void init_all(std::integer_sequence<int, Cs...>, int lane,
+                                           const PagedView<DK, DV, true, FMT>& pv) {
+    (init_one<Cs>(lane, pv), ...);
+  }
+  __device__ __forceinline__ void init(int lane, const PagedView<DK, DV, true, FMT>& pv) {
+    init_all(std::make_integer_sequence<int, R::NCOPY>{}, lane, pv);
+  }
+};
+
+// The entry copy of the step at t0 into the slot at LDS `slot`: lane l carries entry
+// (t0 >> page_shift) + l, clamped to the entry of key tlast (tlast >= t0).
+__device__ __forceinline__ void small_entries(uint32_t slot, const int32_t* pt_row, int t0,
+                                              int tlast, int page_shift, int lane) {
+  const int e = min((t0 >> page_shift) + lane, tlast >> page_shift);
+  dma<false>(slot, (uint32_t)(4 * e), reinterpret_cast<const uint8_t*>(pt_row));
+}
+
+// Waits until at most N of the wave's vector-memory operations are in flight; `ids`
+// (the entry slot read next) passes through the wait, so the reads follow it.
+template <int N>
+__device__ __forceinline__ void small_wait(uint32_t& ids) {
+  asm volatile("s_waitcnt vmcnt(%1)" : "+s"(ids) : "n"(N));
+}
+
+namespace ring_detail {
+template <int DK, int DV, int WL, bool NT, int FMT, int POOLS, int C>
+__device__ __forceinline__ void issue_small_copy(const SmallPlan<DK, DV, WL, FMT>& sp,
+                                                 uint32_t stage, uint32_t ids,
+                                                 const PagedView<DK, DV, true, FMT>& pv,
+                                                 int lane, uint32_t& bad) {
+  using R = RingShape<DK, DV, WL, FMT>;
+  constexpr int MINE = C < R::N_KD ? 1 : (C < R::N_KD + R::N_VD ? 2 : 0xC);
+  if constexpr ((POOLS & MINE) == 0) return;
+  using X = SmallCopy<DK, DV, WL, FMT, C>;
+  const X x(lane);
+  uint32_t pg;
+  lds_load<4>(ids + 4 * (uint32_t)(x.t >> pv.page_shift), &pg);
+  if (pg >= (uint32_t)pv.num_pages) {
+    bad = 1;
+    pg = 0;
+  }
+  uint64_t base;
+  uint32_t ps;
+  if constexpr (X::KD) {
+    base = (uint64_t)(uintptr_t)pv.kdat; ps = (uint32_t)pv.k_page;
+  } else if constexpr (X::VD) {
+    base = (uint64_t)(uintptr_t)pv.vdat; ps = (uint32_t)pv.v_page;
+  } else {
+    // two-way selects on the lane's pool (a wider select became a table in memory)
+    base = x.isv ? (uint64_t)(uintptr_t)pv.vsf : (uint64_t)(uintptr_t)pv.ksf;
+    ps = x.isv ? (uint32_t)pv.vsf_page : (uint32_t)pv.ksf_page;
+  }
+  const uint64_t at = base + (uint64_t)pg * ps + sp.off[C];
+  const uint32_t m0 = stage + R::lds_off(C);
+  constexpr bool X4 = C < R::N_KD + R::N_VD;
+  if constexpr (X4 && NT)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
+                 :: "s"(m0), "v"(at));
+  else if constexpr (X4)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :: "s"(m0), "v"(at));
+  else if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off nt"
+                 :: "s"(m0), "v"(at));
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+                 :: "s"(m0), "v"(at));
+  // one copy's entry read, address and copy before the next copy's: hoisted together
+  // they hold an entry and a 64-bit address per copy at once, which the kernels'
+  // registers do not have
+  __builtin_amdgcn_sched_barrier(0);
+}
+template <int DK, int DV, int WL, bool NT, int FMT, int POOLS, int... Cs>
+__device__ __forceinline__ void issue_small_all(std::integer_sequence<int, Cs...>,
+                                                const SmallPlan<DK, DV, WL, FMT>& sp,
+                                                uint32_t stage, uint32_t ids,
+                                                const PagedView<DK, DV, true, FMT>& pv,
+                                                int lane, uint32_t& bad) {
+  (issue_small_copy<DK, DV, WL, NT, FMT, POOLS, Cs>(sp, stage, ids, pv, lane, bad), ...);
+}
+}  // namespace ring_detail
+
+// The data copies of one step into `stage` from the entries in the slot at `ids`, for
+// the pools in POOLS (bit 0 K rows, 1 V rows; either scale bit: every scale copy, whose
+// lanes carry both pools' rows).  An entry outside [0, num_pages) sets `bad` and reads
+// page 0.  STREAM: the copies take the non-temporal policy when the view allows it (a
+// uniform branch; see ring_issue).
+template <int DK, int DV, int WL, bool STREAM, int POOLS = 0xF, int FMT = kNvfp4>
+__device__ __forceinline__ void ring_issue_small(const SmallPlan<DK, DV, WL, FMT>& sp,
+                                                 uint32_t stage, uint32_t ids,
+                                                 const PagedView<DK, DV, true, FMT>& pv,
+                                                 int lane, uint32_t& bad) {
+  using R = RingShape<DK, DV, WL, FMT>;
+  if constexpr (STREAM) {
+    if (pv.stream) {
+      ring_detail::issue_small_all<DK, DV, WL, true, FMT, POOLS>(
+          std::make_integer_sequence<int, R::NCOPY>{}, sp, stage, ids, pv, lane, bad);
+      return;
+    }
+  }
+  ring_detail::issue_small_all<DK, DV, WL, false, FMT, POOLS>(
+      std::make_integer_sequence<int, R::NCOPY>{}, sp, stage, ids, pv, lane, bad);
+}
+
 // Reads a step's raw bytes for this lane from the stage `stage_off` bytes past the
 // lane addresses, in the register layout the step helpers expect (the same as a
 // direct load from the pool).

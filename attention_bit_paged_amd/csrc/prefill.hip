@@ -15,18 +15,18 @@ bool prefill_supported(int dk, int dv, int fmt) {
 
 int prefill_wgs_per_cu(int dk, int dv) { return dk <= 128 && dv <= 128 ? 2 : 1; }
 
-int prefill_rows_per_item(int dk, int dv, int /*group*/, int page_size) {
-  if (page_size >= 16 && ((dk <= 256 && dv <= 256) || (dk == 512 && dv <= 256)))
+int prefill_rows_per_item(int dk, int dv, int /*group*/, int /*page_size*/) {
+  if ((dk <= 256 && dv <= 256) || (dk == 512 && dv <= 256))
     return dk <= 128 && dv <= 128 ? 192 : 128;  // cooperative kernel: 4 waves x NR x 16 rows
   return 64 * (dk >= 512 ? 1 : 2);
 }
 
 size_t prefill_lds_bytes(int dk, int dv, int page_size, int fmt) {
-  // the register kernel's only LDS is the RoPE frequency table
-  if (page_size < 16) return (size_t)4 * dk;
   // the resident workgroups of the cooperative kernel (its larger form: custom-mask or
-  // RoPE), also for shapes without one
-  const int most = std::max(coop_lds_formula(dk, dv, fmt, true), coop_lds_formula(dk, dv, fmt, false, true));
+  // RoPE; pages below 16 tokens add the entry slots), also for shapes without one
+  const bool small = page_size < 16;
+  const int most = std::max(coop_lds_formula(dk, dv, fmt, true, false, small),
+                            coop_lds_formula(dk, dv, fmt, false, true, small));
   return (size_t)most * coop_wgs_per_cu(dk, dv);
 }
 

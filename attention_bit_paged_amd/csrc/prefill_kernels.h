@@ -12,17 +12,16 @@
 // chunk [kv0, kv1)).  The tile's rows are (query, qo head of the group) pairs, query
 // major, so the heads that share a kv head share every K/V byte read.
 //
-// Cooperative kernel (page_size >= 16, head dims up to 256): the workgroup streams
-// the chunk in 32-token steps.  The raw packed bytes of a step arrive in a shared LDS
-// ring by direct global-to-LDS copies (each wave issues one pool's copies, three
-// steps deep); the four waves then dequantise the step together into fp16 MFMA
-// operands, stored lane-major in an LDS operand buffer (double-buffered, one barrier
-// per step), and every wave computes its groups of 16 rows from those operands, held
-// in registers for the step (three groups per wave for head dims up to 128).  The K/V
-// dequantisation and the LDS reads are thus shared by all rows of the tile.
-//
-// Register kernel (any page size, any head dims): each wave owns its rows and loads
-// and dequantises every step itself, the next step's bytes held in registers.
+// Cooperative kernel: the workgroup streams the chunk in 32-token steps.  The raw
+// packed bytes of a step arrive in a shared LDS ring by direct global-to-LDS copies
+// (each wave issues one pool's copies, three steps deep); the four waves then
+// dequantise the step together into fp16 MFMA operands, stored lane-major in an LDS
+// operand buffer (double-buffered, one barrier per step), and every wave computes its
+// groups of 16 rows from those operands, held in registers for the step (three groups
+// per wave for head dims up to 128).  The K/V dequantisation and the LDS reads are thus
+// shared by all rows of the tile.  Pages of 16 tokens or more give each copy a base per
+// 16-token half; smaller pages (SMALL) give each copy lane its own address, from the
+// step's page-table entries that stream into LDS with the copies.
 //
 // A split tile's partial states are merged by a separate kernel.
 #pragma once
@@ -44,175 +43,6 @@ constexpr int kWidePrefetch = 3;
 // (four waves, one per SIMD, half the operand reads per product) measured 8 % slower:
 // with one wave per SIMD the LDS and barrier latencies are exposed.
 constexpr int kWideGroups = 1;
-
-template <int DK>
-constexpr int prefill_nr() {
-  return DK >= 512 ? 1 : 2;
-}
-
-// page_size < 16: every token is looked up on its own (PagedView::load).
-template <int DK, int DV, int FMT = kNvfp4, bool ROPE = false>
-__global__ __launch_bounds__(256) void prefill_regs_kernel(AttnArgs a) {
-  using S = StepShape<DK, DV, FMT>;
-  constexpr int NR = prefill_nr<DK>();
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int j = lane >> 4;
-  const int n = lane & 15;
-  const int32_t* rec = a.work + (int64_t)blockIdx.x * kWorkFields;
-  if (blockIdx.x == 0 && threadIdx.x == 0) *a.part_scale = a.out_scale;  // for the merge
-  const int b = rec[W_REQ], kvh = rec[W_KVH], q0 = rec[W_ROW0], qn = rec[W_ROWS];
-  const int kv0 = rec[W_KV0], kv1 = rec[W_KV1], slot = rec[W_SLOT];
-  const int G = a.group;
-  const int R = qn * G;
-  const int row_base = wave * NR * 16;
-  const bool wave_has_rows = row_base < R;  // uniform; rowless waves still meet the barriers
-  const int qstart = a.qo_indptr[b];
-  const int qlen = a.qo_indptr[b + 1] - qstart;
-  const int off = a.kv_lens[b] - qlen;
-
-  f16x8 qf[NR][S::NS];
-  float sc[NR];
-  int last[NR];
-  bool rv[NR];
-  int64_t tokrow[NR];
-  int headi[NR];
-#pragma unroll
-  for (int rg = 0; rg < NR; ++rg) {
-    const int r = row_base + rg * 16 + n;
-    rv[rg] = r < R;
-    const int qi = r / G;
-    const int gh = r - qi * G;
-    const int qpos = q0 + qi;
-    tokrow[rg] = (int64_t)qstart + qpos;
-    headi[rg] = kvh * G + gh;
-    last[rg] = a.causal ? min(kv1 - 1, qpos + off) : kv1 - 1;
-    const uint16_t* qrow = a.q + tokrow[rg] * a.q_s_row + (int64_t)headi[rg] * a.q_s_head;
-    if constexpr (ROPE)
-      sc[rg] = a.score_scale *
-               load_q_rope_prescaled<DK>(qrow, rv[rg], j, (float)(qpos + off), a.rope, qf[rg]);
-    else
-      sc[rg] = a.score_scale * load_q_operand<DK>(qrow, rv[rg], j, qf[rg]);
-  }
-  // RoPE: the frequency pairs in LDS, read by every step
-  __shared__ __attribute__((aligned(16))) float rope_tab[ROPE ? DK : 4];
-  if constexpr (ROPE) {
-    for (int t = threadIdx.x; t < DK; t += 256) rope_tab[t] = a.rope[t];
-    __syncthreads();
-  }
-  const uint32_t tab0 = (uint32_t)(uintptr_t)rope_tab + 8 * ((j & 1) * (DK / 4));
-  // keys this wave needs: up to the last visible key of its last valid row
-  int wave_end = wave_has_rows ? kv1 : kv0;
-  if (a.causal && wave_has_rows) {
-    const int r_last = min(R - 1, row_base + NR * 16 - 1);
-    wave_end = min(kv1, q0 + r_last / G + off + 1);
-  }
-  // steps that may hold a masked key: the chunk's tail and, for causal rows, any step
-  // past the first visible-key limit of the wave's first row (every step with a custom
-  // mask)
-  int mask_from = kv1 - kDecodeStep;
-  if (a.causal) mask_from = min(mask_from, q0 + row_base / G + off + 1 - kDecodeStep);
-  const bool custom = a.mask != nullptr;  // uniform
-  const uint8_t* mseg = custom ? a.mask + a.mask_off[b] : nullptr;
-  const int64_t kv_len = a.kv_lens[b];
-
-  PagedView<DK, DV, false, FMT> view;
-  view.init(a, b, kvh, lane);
-  const int tlast = kv1 - 1;
-
-  RowState<S::NT, AccForm::PLAIN> st[NR];
-#pragma unroll
-  for (int rg = 0; rg < NR; ++rg) st[rg].init();
-
-  auto step = [&](const StepRaw<DK, DV, FMT>& r, int t0) {
-    f16x8 ka[S::NS], kb[S::NS];
-    k_operands<DK, DV, FMT>(r, ka, kb);
-    if constexpr (ROPE) {
-      // each element's partner (head-dim index +- DK/2) sits in lane l ^ 32
-      const float pa = (float)(t0 + 8 * (n >> 2) + (n & 3));
-#pragma unroll
-      for (int s = 0; s < S::NS; ++s) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          f16x8& own = t ? kb[s] : ka[s];
-          u32x4 w = __builtin_bit_cast(u32x4, own);
-          u32x4 pw;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) pw[i] = (uint32_t)__shfl_xor((int)w[i], 32, 64);
-          f16x8 par = __builtin_bit_cast(f16x8, pw);
-          f16x8 lo = j < 2 ? own : par, hi = j < 2 ? par : own;
-          rope_k_pair(lo, hi, pa + 4.f * t, tab0 + 64 * s);
-          own = j < 2 ? lo : hi;
-        }
-      }
-    }
-    const bool masked = t0 > mask_from;
-    f16x8 p[NR];
-#pragma unroll
-    for (int rg = 0; rg < NR; ++rg) {
-      f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < S::NS; ++s) {
-        sa = mfma16x16x32(ka[s], qf[rg][s], sa);
-        sb = mfma16x16x32(kb[s], qf[rg][s], sb);
-      }
-      if (custom) {
-        const int key0 = t0 + 8 * j;
-        const int qpos = q0 + (row_base + rg * 16 + n) / G;
-        const uint32_t vis = rv[rg] ? mask_bits8(mseg, kv_len, qpos, key0, tlast - key0 + 1) : 0u;
-        p[rg] = st[rg].softmax_vis(sa, sb, sc[rg], vis);
-      } else {
-        p[rg] = masked ? st[rg].template softmax<true>(sa, sb, sc[rg], t0, j, last[rg])
-                       : st[rg].template softmax<false>(sa, sb, sc[rg], t0, j, last[rg]);
-      }
-    }
-    f16x8 vt[S::NT];
-    if (t0 + kDecodeStep > kv1)
-      v_operands<DK, DV, true, FMT>(r, t0, tlast, j, vt);
-    else
-      v_operands<DK, DV, false, FMT>(r, t0, tlast, j, vt);
-#pragma unroll
-    for (int rg = 0; rg < NR; ++rg) st[rg].pv(vt, p[rg]);
-  };
-
-  // r0 holds the step at t0 at the top of every iteration, p1 the pages of the next: a
-  // step's page-table entries are read one step before its bytes, its bytes one step
-  // before its compute
-  using View = PagedView<DK, DV, false, FMT>;
-  StepRaw<DK, DV, FMT> r0, r1;
-  typename View::Pages p0, p1;
-  if (kv0 < wave_end) view.load(r0, kv0, tlast);
-  if (kv0 + kDecodeStep < wave_end) view.lookup(p1, kv0 + kDecodeStep, tlast);
-  for (int t0 = kv0; t0 < wave_end; t0 += 2 * kDecodeStep) {
-    const int t1 = t0 + kDecodeStep;
-    if (t1 + kDecodeStep < wave_end) view.lookup(p0, t1 + kDecodeStep, tlast);
-    if (t1 < wave_end) view.load(r1, p1, t1, tlast);
-    step(r0, t0);
-    if (t1 >= wave_end) break;
-    if (t1 + 2 * kDecodeStep < wave_end) view.lookup(p1, t1 + 2 * kDecodeStep, tlast);
-    if (t1 + kDecodeStep < wave_end) view.load(r0, p0, t1 + kDecodeStep, tlast);
-    step(r1, t1);
-  }
-
-  const bool bad = __any(view.bad != 0);
-  if (slot < 0) {
-    if (wave_has_rows) {
-#pragma unroll
-      for (int rg = 0; rg < NR; ++rg)
-        st[rg].store(a.o + tokrow[rg] * a.o_s_row + (int64_t)headi[rg] * a.o_s_head,
-                     a.lse + tokrow[rg] * a.num_qo_heads + headi[rg], rv[rg], bad, a.out_scale, j);
-    }
-    return;
-  }
-  if (wave_has_rows) {
-#pragma unroll
-    for (int rg = 0; rg < NR; ++rg) {
-      const int r = row_base + rg * 16 + n;
-      st[rg].store_partial(a.part_o + ((int64_t)slot * a.rows_per_slot + r) * DV,
-                   a.part_lse + (int64_t)slot * a.rows_per_slot + r, rv[rg], bad, j);
-    }
-  }
-}
 
 // ------------------------------------------------------------------ cooperative --
 
@@ -262,13 +92,17 @@ constexpr int kLdsPerCu = 160 * 1024;
 // LDS of one cooperative workgroup: three raw stages of 32 tokens (rows and, for NVFP4,
 // scale rows) and two fp16 operand buffers (2 NS K entries and NT V tiles of 64 lanes x
 // 16 bytes).  A formula, so that shapes without a kernel can be priced too.
-constexpr int coop_lds_formula(int dk, int dv, int fmt, bool masked, bool rope = false) {
+// SMALL (pages below 16 tokens): four copy roles' page-table entry slots (4 x 256 bytes each).
+constexpr int kCoopEntryBytes = 4 * 4 * 256;
+constexpr int coop_lds_formula(int dk, int dv, int fmt, bool masked, bool rope = false,
+                               bool small = false) {
   const int rbk = fmt == kFp8 ? dk : dk / 2, rbv = fmt == kFp8 ? dv : dv / 2;
   const int sf = fmt == kFp8 ? 0 : (2 * dk + 2 * dv + 255) / 256 * 256;
   const int rows = dk <= 128 && dv <= 128 ? 192 : 128;  // tile rows (queries at most)
   const int raw = 32 * (rbk + rbv) + sf;
   const int opb = (2 * (dk / 32) + dv / 16) * 64 * 16;
-  return 3 * raw + 2 * opb + (masked ? 4 * ((rows + 63) / 64 * 512) : 0) + (rope ? 4 * dk : 0);
+  return 3 * raw + 2 * opb + (masked ? 4 * ((rows + 63) / 64 * 512) : 0) + (rope ? 4 * dk : 0) +
+         (small ? kCoopEntryBytes : 0);
 }
 constexpr int coop_wgs_per_cu(int dk, int dv) { return dk <= 128 && dv <= 128 ? 2 : 1; }
 
@@ -543,10 +377,17 @@ __device__ __forceinline__ void coop_dequant(uint32_t raw, uint32_t opb, int wav
 // of them).  Waves 0..3 each copy one pool; the others copy nothing.
 // Wave 3 also copies the custom-mask bytes, two copies per block of 64 tile queries:
 // `mask_copies` of them per step (0, 2, 4 or 6; wave-uniform).
-template <int DK, int DV, int FMT>
+// SMALL: roles 0, 1 and 2 copy the K rows, the V rows and every scale row (R::N_KD,
+// R::N_VD and R::N_SF copies, each whole) plus one entry copy a step; role 3 copies only
+// the mask bytes.
+template <int DK, int DV, int FMT, bool SMALL = false>
 __device__ __forceinline__ void coop_wait(int wave, bool one_newer, int mask_copies) {
   using R = typename CoopShape<DK, DV, FMT>::R;
-  constexpr int N0 = R::ndma(1), N1 = R::ndma(2), N2 = R::ndma(4), N3 = R::ndma(8);
+  constexpr bool F8 = StepShape<DK, DV, FMT>::F8;
+  constexpr int N0 = SMALL ? R::N_KD + 1 : R::ndma(1);
+  constexpr int N1 = SMALL ? R::N_VD + 1 : R::ndma(2);
+  constexpr int N2 = SMALL ? (F8 ? 0 : R::N_SF + 1) : R::ndma(4);
+  constexpr int N3 = SMALL ? 0 : R::ndma(8);
   if (wave > 3) return;
   if (!one_newer) {
     asm volatile("s_waitcnt vmcnt(0)");
@@ -599,7 +440,8 @@ struct CoopCopies {
   // Pieces: the K copies place piece p of step token t in slot (p + n(t)) % 16 of its
   // row, n(t) the token's column in its 16-token tile; so the copy lane that lands in
   // slot q fetches piece (q - n(t)) % 16.  Only the offset inside the row changes.
-  __device__ __forceinline__ void rotate_k(Plan& rp, int lane) {
+  template <class P>
+  __device__ __forceinline__ static void rotate_k(P& rp, int lane) {
     static_assert(R::RBK == 256, "rotation of 16-piece rows");
 #pragma unroll
     for (int c = 0; c < R::N_KD; ++c) {
@@ -633,14 +475,40 @@ struct CoopCopies {
   }
 };
 
-template <int DK, int DV, int FMT, bool CMASK>
+// SMALL: this role's copies of the step at t0 take their pages from the entry slot of
+// that step (slots at `ids`, four of 256 bytes, the step's index mod 4), and the entry
+// copy of the step three later goes out with them (see coop_wait).
+template <int DK, int DV, int FMT, bool CMASK, bool SMALL = false, bool PIECE = false>
 __device__ __forceinline__ void coop_issue(int wave, const CoopCopies<DK, DV, FMT>& cc,
                                            uint32_t stage, const PagedView<DK, DV, true, FMT>& view,
                                            int t0, int tlast, uint32_t& bad, const CoopMask& cm,
-                                           int kv0) {
+                                           int kv0, uint32_t ids = 0) {
   using C = CoopShape<DK, DV, FMT>;
   constexpr int WL = C::WL;
-  if constexpr (CoopCopies<DK, DV, FMT>::RECOMPUTE) {
+  if constexpr (SMALL) {
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));  // the offsets are formed here, at each issue
+    SmallPlan<DK, DV, WL, FMT> sp;
+    sp.init(lane, view);
+    if constexpr (PIECE) CoopCopies<DK, DV, FMT>::rotate_k(sp, lane);
+    const int m = (t0 - kv0) / kDecodeStep;
+    const uint32_t slot = ids + (uint32_t)(m & 3) * 256, next = ids + (uint32_t)((m + 3) & 3) * 256;
+    auto entries = [&]() {
+      small_entries(next, view.pt_row, t0 + 3 * kDecodeStep, tlast, view.page_shift, lane);
+    };
+    if (wave == 0) {
+      ring_issue_small<DK, DV, WL, false, 1, FMT>(sp, stage, slot, view, lane, bad);
+      entries();
+    } else if (wave == 1) {
+      ring_issue_small<DK, DV, WL, false, 2, FMT>(sp, stage, slot, view, lane, bad);
+      entries();
+    } else if constexpr (!StepShape<DK, DV, FMT>::F8) {
+      if (wave == 2) {
+        ring_issue_small<DK, DV, WL, false, 0xC, FMT>(sp, stage, slot, view, lane, bad);
+        entries();
+      }
+    }
+  } else if constexpr (CoopCopies<DK, DV, FMT>::RECOMPUTE) {
     static_assert(StepShape<DK, DV, FMT>::F8, "FP8 only: no scale pools");
     // opaque at each issue, so that the offsets are formed here (see CoopCopies)
     int lane = threadIdx.x & 63;
@@ -780,9 +648,10 @@ __device__ __forceinline__ f16x8 probs_shifted(RowState<NT, AccForm::VGPR>& st, 
 }
 
 // CMASK: the launch carries a custom mask (AttnArgs::mask); ROPE: Q and K are rotated
-// (AttnArgs::rope).  Separate instantiations, so that the plain kernel holds none of
-// their state.
-template <int DK, int DV, int FMT, bool CMASK, bool ROPE>
+// (AttnArgs::rope); SMALL: pages of 1..8 tokens (per-lane copy addresses from page-table
+// entries streamed into LDS slots, see ring_issue_small).  Separate instantiations, so
+// that the plain kernel holds none of their state.
+template <int DK, int DV, int FMT, bool CMASK, bool ROPE, bool SMALL = false>
 __global__ __launch_bounds__((CoopShape<DK, DV, FMT>::NW * 64))
 __attribute__((amdgpu_waves_per_eu(CoopShape<DK, DV, FMT>::WGS_PER_CU)))
 void prefill_coop_kernel(AttnArgs a) {
@@ -792,9 +661,11 @@ void prefill_coop_kernel(AttnArgs a) {
   constexpr int WL = 3 * C::RAW_STAGE;
   static_assert(C::OK, "shape has no cooperative kernel");
   static_assert(!(CMASK && ROPE), "RoPE is not combined with custom masks");
-  constexpr int LDS = CMASK ? C::LDS_MASKED : (ROPE ? C::LDS_ROPE : C::LDS);
-  static_assert(LDS == coop_lds_formula(DK, DV, FMT, CMASK, ROPE) &&
+  constexpr int LDS_BASE = CMASK ? C::LDS_MASKED : (ROPE ? C::LDS_ROPE : C::LDS);
+  constexpr int LDS = LDS_BASE + (SMALL ? kCoopEntryBytes : 0);
+  static_assert(LDS == coop_lds_formula(DK, DV, FMT, CMASK, ROPE, SMALL) &&
                 C::WGS_PER_CU == coop_wgs_per_cu(DK, DV), "LDS formula");
+  constexpr bool PIECE = C::piece(ROPE);
   static_assert(LDS * C::WGS_PER_CU <= kLdsPerCu, "resident workgroups exceed the LDS");
   __shared__ __attribute__((aligned(16))) uint8_t smem[LDS];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -830,7 +701,7 @@ void prefill_coop_kernel(AttnArgs a) {
   {
     RingPlan<DK, DV, WL, FMT> rp;
     rp.init(lane, view.k_tok, view.v_tok, view.ksf_tok, view.vsf_tok);
-    if constexpr (C::piece(ROPE)) cc.rotate_k(rp, lane);
+    if constexpr (PIECE) cc.rotate_k(rp, lane);
     cc.init(rp, wave);
   }
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
@@ -861,11 +732,23 @@ void prefill_coop_kernel(AttnArgs a) {
   cl.init(wave, lane, rope_tab);
   uint32_t bad = 0;
 
+  // SMALL: the page-table entries of a wave's copies, four slots per copy role after the
+  // rest of the LDS; the first three steps' entries are read here, at once (the later
+  // ones go out with the copies, three steps ahead).
+  uint32_t ids = lds0 + LDS_BASE + (uint32_t)(wave & 3) * 1024;
+  if constexpr (SMALL) {
+    if (wave < 3 && nsteps > 0) {
+      for (int m = 0; m < 3; ++m)
+        small_entries(ids + (uint32_t)m * 256, view.pt_row, kv0 + m * kDecodeStep, tlast,
+                      view.page_shift, lane);
+      small_wait<0>(ids);
+    }
+  }
   // The first three steps' copies go out before Q is read, so that the two memory
   // latencies of a work item's start overlap.
   for (int i = 0; i < 3 && i < nsteps; ++i)
-    coop_issue<DK, DV, FMT, CMASK>(wave, cc, raw0 + i * C::RAW_STAGE, view, kv0 + i * kDecodeStep,
-                                   tlast, bad, cm, kv0);
+    coop_issue<DK, DV, FMT, CMASK, SMALL, PIECE>(wave, cc, raw0 + i * C::RAW_STAGE, view,
+                                                 kv0 + i * kDecodeStep, tlast, bad, cm, kv0, ids);
   // Head dims up to 256: Q carries the score factor (see ShiftRef) unless some row of
   // the wave could overflow fp16; that wave then takes the exact prescaled Q.
   bool safe = true;
@@ -958,11 +841,11 @@ void prefill_coop_kernel(AttnArgs a) {
     const bool next = i + 1 < nsteps;
     // raw step i+1 landed (only step i+2 may still be in flight); operands of step i
     // are visible; nobody reads operand buffer (i+1)%2 or raw stage i%3 any more
-    if (next) coop_wait<DK, DV, FMT>(wave, i + 2 < nsteps, 2 * cm.blocks);
+    if (next) coop_wait<DK, DV, FMT, SMALL>(wave, i + 2 < nsteps, 2 * cm.blocks);
     __syncthreads();
     if (i + 3 < nsteps)
-      coop_issue<DK, DV, FMT, CMASK>(wave, cc, raw0 + (i % 3) * C::RAW_STAGE, view, t_of(i + 3),
-                                     tlast, bad, cm, kv0);
+      coop_issue<DK, DV, FMT, CMASK, SMALL, PIECE>(wave, cc, raw0 + (i % 3) * C::RAW_STAGE, view,
+                                                   t_of(i + 3), tlast, bad, cm, kv0, ids);
     // Stage and buffer bases as single scalars: left to itself the compiler folds the
     // modulo's parts into every lane address separately (two vector adds per address).
     const uint32_t ob = __builtin_amdgcn_readfirstlane(opb0 + (i & 1) * C::OPB);
@@ -1167,7 +1050,7 @@ void prefill_coop_kernel(AttnArgs a) {
   };
   // prologue: three steps in flight (issued above), step 0 dequantised
   if (nsteps > 0) {
-    coop_wait<DK, DV, FMT>(wave, false, 2 * cm.blocks);
+    coop_wait<DK, DV, FMT, SMALL>(wave, false, 2 * cm.blocks);
     __syncthreads();
     coop_dequant<DK, DV, true, FMT, ROPE>(raw0, opb0, wave, cl, tlast - t_of(0), (float)t_of(0));
   }
@@ -1211,18 +1094,21 @@ template <int DK, int DV, int FMT, bool ROPE>
 hipError_t launch_dk_dv(int page_shift, const AttnArgs& a, hipStream_t stream) {
   const dim3 grid(a.n_work);
   const dim3 block(CoopShape<DK, DV, FMT>::NW * 64);
+  // pages of 16 tokens or more, or fewer (SMALL)
   if constexpr (ROPE) {
     if (page_shift >= 4)
       launch_attention(prefill_coop_kernel<DK, DV, FMT, false, true>, grid, block, stream, a);
     else
-      launch_attention(prefill_regs_kernel<DK, DV, FMT, true>, grid, dim3(256), stream, a);
+      launch_attention(prefill_coop_kernel<DK, DV, FMT, false, true, true>, grid, block, stream, a);
   } else {
     if (page_shift >= 4 && a.mask)
       launch_attention(prefill_coop_kernel<DK, DV, FMT, true, false>, grid, block, stream, a);
     else if (page_shift >= 4)
       launch_attention(prefill_coop_kernel<DK, DV, FMT, false, false>, grid, block, stream, a);
+    else if (a.mask)
+      launch_attention(prefill_coop_kernel<DK, DV, FMT, true, false, true>, grid, block, stream, a);
     else
-      launch_attention(prefill_regs_kernel<DK, DV, FMT, false>, grid, dim3(256), stream, a);
+      launch_attention(prefill_coop_kernel<DK, DV, FMT, false, false, true>, grid, block, stream, a);
   }
   return hipGetLastError();
 }

@@ -43,67 +43,6 @@ __device__ __forceinline__ float q_row_absmax(const uint16_t* qrow, bool valid, 
   return max_over_groups(qmax);
 }
 
-// The lane's Q quarter-row rotated at position `pos`, times `mul`, as fp16 operands
-// (the layout of load_q_operand).  Element m of lane group j (head-dim index
-// j*DK/4 + m) pairs with the same element of lane group j ^ 2, which this lane reads
-// from the row as well; the pair's index is (j & 1)*DK/4 + m.  The rotation runs in
-// fp32 and rounds once.  `freq`: the frequency pairs (device, DK/2 of them).  Returns
-// the largest |rotated q * mul| of the lane (NaN when some input is NaN).
-template <int DK>
-__device__ __forceinline__ float load_q_rope(const uint16_t* qrow, bool valid, int j, float pos,
-                                             const float* freq, float mul, f16x8 (&qf)[DK / 32]) {
-  const uint8_t* own = reinterpret_cast<const uint8_t*>(qrow + j * (DK / 4));
-  const uint8_t* par = reinterpret_cast<const uint8_t*>(qrow + (j ^ 2) * (DK / 4));
-  const float* fr = freq + 2 * ((j & 1) * (DK / 4));
-  const float sgn = j < 2 ? -1.f : 1.f;  // first half: x cos - y sin; second: x cos + y sin
-  float amax = 0.f;
-#pragma unroll
-  for (int s = 0; s < DK / 32; ++s) {
-    uint32_t xo[4] = {0u, 0u, 0u, 0u}, xp[4] = {0u, 0u, 0u, 0u}, fw[16];
-    if (valid) {
-      load_bytes<16>(own + 16 * s, xo);
-      load_bytes<16>(par + 16 * s, xp);
-    }
-    load_bytes<64>(reinterpret_cast<const uint8_t*>(fr + 16 * s), fw);
-    f16x2 p[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      float r[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const float x = bf16f(h ? xo[t] >> 16 : xo[t] & 0xFFFF);
-        const float y = bf16f(h ? xp[t] >> 16 : xp[t] & 0xFFFF);
-        float c, sn;
-        rope_cs(pos, __builtin_bit_cast(float, fw[2 * (2 * t + h)]),
-                __builtin_bit_cast(float, fw[2 * (2 * t + h) + 1]), c, sn);
-        r[h] = fmaf(x, c, sgn * (y * sn)) * mul;
-        amax = __builtin_elementwise_maximum(amax, fabsf(r[h]));
-      }
-      p[t] = f16x2{(_Float16)r[0], (_Float16)r[1]};
-    }
-    qf[s] = pack8(p[0], p[1], p[2], p[3]);
-    // one k-step's loads at a time: hoisted together they would hold 48 dwords per
-    // k-step beside the kernel's state
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  return amax;
-}
-
-// The exact-range form for RoPE (as load_q_operand): Q rotated and scaled by the power
-// of two that puts the row's largest unrotated magnitude in [2^14, 2^15); a rotated
-// element is at most sqrt(2) times that, so below 46341 and inside fp16.  Returns the
-// factor that undoes the prescale on the scores.
-template <int DK>
-__device__ __forceinline__ float load_q_rope_prescaled(const uint16_t* qrow, bool valid, int j,
-                                                       float pos, const float* freq,
-                                                       f16x8 (&qf)[DK / 32]) {
-  const float qmax = q_row_absmax<DK>(qrow, valid, j);
-  int qexp = 0;
-  if (qmax > 0.f) (void)frexpf(qmax, &qexp);
-  (void)load_q_rope<DK>(qrow, valid, j, pos, freq, ldexpf(1.f, 15 - qexp), qf);
-  return ldexpf(1.f, qexp - 15);
-}
-
 // The Q quarter-rows of a wave's NR row groups rotated, k-step by k-step: a k-step's
 // eight frequency pairs are read once for all rows, and a row's own and partner loads
 // are issued one k-step at a time (all of them at once held every row's quarter-rows

@@ -1,6 +1,6 @@
 """GPU parity of prefill with in-kernel RoPE against the oracle: the cooperative
 kernel at every shape family (one, two and four K entries per lane and wave, the
-512-dim wide kernel), the register kernel (page sizes 4 and 1), NVFP4 and FP8, causal
+512-dim wide kernel), pages of 4 and 1 tokens (per-lane copy addresses), NVFP4 and FP8, causal
 and full, unsplit and split, ragged KV, a base and position scale other than the
 defaults, and positions up to 70000 (where a plain float product pos * w would
 already miss the angle by about 1e-2 rad)."""
@@ -56,7 +56,7 @@ def test_rope_prefill_extend(kv_dtype, causal, chunk):
     (128, 64, "nvfp4", 16, 8, 8),     # 192-query tiles
     (64, 64, "fp8", 16, 16, 4),       # one K entry per wave: half the lanes idle
     (64, 64, "nvfp4", 16, 4, 4),
-    (128, 128, "nvfp4", 4, 8, 2),     # register kernel
+    (128, 128, "nvfp4", 4, 8, 2),     # pages of 4 tokens
     (512, 256, "nvfp4", 1, 8, 1),
     (256, 128, "fp8", 1, 4, 2),
 ])
