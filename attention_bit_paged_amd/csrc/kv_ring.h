@@ -457,10 +457,6 @@ __device__ __forceinline__ void issue_small_copy(const SmallPlan<DK, DV, WL, FMT
   else
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
                  :: "s"(m0), "v"(at));
-  // one copy's entry read, address and copy before the next copy's: hoisted together
-  // they hold an entry and a 64-bit address per copy at once, which the kernels'
-  // registers do not have
-  __builtin_amdgcn_sched_barrier(0);
 }
 template <int DK, int DV, int WL, bool NT, int FMT, int POOLS, int... Cs>
 __device__ __forceinline__ void issue_small_all(std::integer_sequence<int, Cs...>,
