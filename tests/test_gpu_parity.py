@@ -250,11 +250,16 @@ def test_prefill_head_dims(dk, dv, hq, hkv):
     _run_case(w, chunk=-1)
 
 
-@pytest.mark.parametrize("layout,page_size", [("NHD", 16), ("HND", 4), ("HND", 32)])
+@pytest.mark.parametrize("layout,page_size", [("NHD", 16), ("HND", 4), ("HND", 32), ("HND", 8),
+                                              ("NHD", 2), ("NHD", 1)])
 def test_prefill_layouts_and_pages(layout, page_size):
+    """Every page size takes the cooperative kernel; below 16 tokens its copy lanes form
+    their own addresses from the page-table entries streamed beside the copies."""
     w = synth.custom("playout", kv_lens=[60, 150], qo_lens=[20, 50], num_qo_heads=8,
                      num_kv_heads=2, page_size=page_size, causal=True, seed=22)
     _run_case(w, layout=layout, chunk=-1)
+    if page_size < 16:
+        _run_case(w, layout=layout, chunk=32)  # split items: chunks starting mid-request
 
 
 @pytest.mark.parametrize("dk,dv", [(512, 256), (256, 128)])
