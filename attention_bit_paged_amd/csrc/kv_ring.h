@@ -343,6 +343,9 @@ __device__ __forceinline__ void lds_load(uint32_t addr, uint32_t* out) {
 // and every vector-memory operation of the stream is still a counted copy.  Each step
 // then issues its data copies, one per ring copy and without exec masks (lanes past the
 // scale rows fetch token 0's scales into the stage's padding), and one entry copy.
+// The copies keep the default cache policy: the prefill kernel that streams them reads
+// each request's rows for every query tile.
+
 // Per lane and ring copy C (a constant): the copy's token within the step (t), whether
 // it carries a V row or V scale row (isv; scale copies hold both pools' lanes) and the
 // byte within the token's row.
@@ -415,7 +418,7 @@ __device__ __forceinline__ void small_wait(uint32_t& ids) {
 }
 
 namespace ring_detail {
-template <int DK, int DV, int WL, bool NT, int FMT, int POOLS, int C>
+template <int DK, int DV, int WL, int FMT, int POOLS, int C>
 __device__ __forceinline__ void issue_small_copy(const SmallPlan<DK, DV, WL, FMT>& sp,
                                                  uint32_t stage, uint32_t ids,
                                                  const PagedView<DK, DV, true, FMT>& pv,
@@ -444,50 +447,35 @@ __device__ __forceinline__ void issue_small_copy(const SmallPlan<DK, DV, WL, FMT
   }
   const uint64_t at = base + (uint64_t)pg * ps + sp.off[C];
   const uint32_t m0 = stage + R::lds_off(C);
-  constexpr bool X4 = C < R::N_KD + R::N_VD;
-  if constexpr (X4 && NT)
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
-                 :: "s"(m0), "v"(at));
-  else if constexpr (X4)
+  if constexpr (C < R::N_KD + R::N_VD)
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-                 :: "s"(m0), "v"(at));
-  else if constexpr (NT)
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off nt"
                  :: "s"(m0), "v"(at));
   else
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
                  :: "s"(m0), "v"(at));
 }
-template <int DK, int DV, int WL, bool NT, int FMT, int POOLS, int... Cs>
+template <int DK, int DV, int WL, int FMT, int POOLS, int... Cs>
 __device__ __forceinline__ void issue_small_all(std::integer_sequence<int, Cs...>,
                                                 const SmallPlan<DK, DV, WL, FMT>& sp,
                                                 uint32_t stage, uint32_t ids,
                                                 const PagedView<DK, DV, true, FMT>& pv,
                                                 int lane, uint32_t& bad) {
-  (issue_small_copy<DK, DV, WL, NT, FMT, POOLS, Cs>(sp, stage, ids, pv, lane, bad), ...);
+  (issue_small_copy<DK, DV, WL, FMT, POOLS, Cs>(sp, stage, ids, pv, lane, bad), ...);
 }
 }  // namespace ring_detail
 
 // The data copies of one step into `stage` from the entries in the slot at `ids`, for
 // the pools in POOLS (bit 0 K rows, 1 V rows; either scale bit: every scale copy, whose
 // lanes carry both pools' rows).  An entry outside [0, num_pages) sets `bad` and reads
-// page 0.  STREAM: the copies take the non-temporal policy when the view allows it (a
-// uniform branch; see ring_issue).
-template <int DK, int DV, int WL, bool STREAM, int POOLS = 0xF, int FMT = kNvfp4>
+// page 0.
+template <int DK, int DV, int WL, int POOLS = 0xF, int FMT = kNvfp4>
 __device__ __forceinline__ void ring_issue_small(const SmallPlan<DK, DV, WL, FMT>& sp,
                                                  uint32_t stage, uint32_t ids,
                                                  const PagedView<DK, DV, true, FMT>& pv,
                                                  int lane, uint32_t& bad) {
   using R = RingShape<DK, DV, WL, FMT>;
-  if constexpr (STREAM) {
-    if (pv.stream) {
-      ring_detail::issue_small_all<DK, DV, WL, true, FMT, POOLS>(
-          std::make_integer_sequence<int, R::NCOPY>{}, sp, stage, ids, pv, lane, bad);
-      return;
-    }
-  }
-  ring_detail::issue_small_all<DK, DV, WL, false, FMT, POOLS>(
-      std::make_integer_sequence<int, R::NCOPY>{}, sp, stage, ids, pv, lane, bad);
+  ring_detail::issue_small_all<DK, DV, WL, FMT, POOLS>(std::make_integer_sequence<int, R::NCOPY>{},
+                                                      sp, stage, ids, pv, lane, bad);
 }
 
 // Reads a step's raw bytes for this lane from the stage `stage_off` bytes past the

@@ -497,14 +497,14 @@ __device__ __forceinline__ void coop_issue(int wave, const CoopCopies<DK, DV, FM
       small_entries(next, view.pt_row, t0 + 3 * kDecodeStep, tlast, view.page_shift, lane);
     };
     if (wave == 0) {
-      ring_issue_small<DK, DV, WL, false, 1, FMT>(sp, stage, slot, view, lane, bad);
+      ring_issue_small<DK, DV, WL, 1, FMT>(sp, stage, slot, view, lane, bad);
       entries();
     } else if (wave == 1) {
-      ring_issue_small<DK, DV, WL, false, 2, FMT>(sp, stage, slot, view, lane, bad);
+      ring_issue_small<DK, DV, WL, 2, FMT>(sp, stage, slot, view, lane, bad);
       entries();
     } else if constexpr (!StepShape<DK, DV, FMT>::F8) {
       if (wave == 2) {
-        ring_issue_small<DK, DV, WL, false, 0xC, FMT>(sp, stage, slot, view, lane, bad);
+        ring_issue_small<DK, DV, WL, 0xC, FMT>(sp, stage, slot, view, lane, bad);
         entries();
       }
     }
