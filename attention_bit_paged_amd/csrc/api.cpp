@@ -961,6 +961,10 @@ nvfp4_status nvfp4_kv_checksum(const nvfp4_plan* plan, const int32_t* page_table
   if (plan && plan->page_size < 16)
     return fail(NVFP4_E_UNSUPPORTED, "page_size %d: the checksum streams through the decode "
                 "rings, which need pages of at least 16 tokens", plan->page_size);
+  if (plan && !decode_ring_supported(plan->head_dim_qk, plan->head_dim_vo, plan->kv_dtype))
+    return fail(NVFP4_E_UNSUPPORTED, "head dims (%d, %d) %s: the checksum streams through the "
+                "decode rings, which this shape has none of", plan->head_dim_qk,
+                plan->head_dim_vo, plan->kv_dtype == NVFP4_KV_FP8_E4M3 ? "FP8" : "NVFP4");
   if (plan && plan->batch > 0 && !checksum) return fail(NVFP4_E_INVALID, "checksum is NULL");
   if (!aligned(checksum, 4)) return fail(NVFP4_E_SHAPE, "checksum must be 4-byte aligned");
   // the attention checks, with stand-ins for q, o and lse (never read or written)

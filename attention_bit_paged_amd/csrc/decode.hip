@@ -27,23 +27,37 @@ namespace {
 // work records, page table and split partials stay cached; 5-10 % faster measured).
 constexpr int kDecodePools = 0xF | kStreamCopies;
 
+// Bytes of one ring workgroup's four rings (0 for shapes without a ring kernel).
+template <bool RING, int DK, int DV, int WL, int FMT>
+struct RingSmem {
+  static constexpr int BYTES = 4 * RingShape<DK, DV, WL, FMT>::WAVE_BYTES;
+};
+template <int DK, int DV, int WL, int FMT>
+struct RingSmem<false, DK, DV, WL, FMT> {
+  static constexpr int BYTES = 0;
+};
+
 // Workgroups (of four waves) one CU holds at once, by design.  Registers: 512 VGPRs
 // per SIMD lane are shared by the waves on a SIMD, and the kernels of each shape are
 // held to the budget of this many waves (amdgpu_waves_per_eu).  LDS: 160 KiB per CU,
-// and each wave's ring needs two stages at least.
+// and each wave's ring needs two stages at least; a shape whose four waves' rings of
+// two stages exceed the LDS (FP8 at 512 dims) has no ring kernel (RING false) and runs
+// the register kernel, which needs only the exchange buffer, at every page size.
 template <int DK, int DV, int FMT = kNvfp4>
 struct DecodeOcc {
   static constexpr int STAGE = RingBytes<DK, DV, FMT>::STAGE;
   static constexpr int BY_REGS = DK <= 128 ? 4 : (DK == 256 && DV <= 128 ? 3 : 2);
   static constexpr int BY_LDS = (160 * 1024) / (4 * 2 * STAGE);
-  static constexpr int WGS = BY_REGS < BY_LDS ? BY_REGS : (BY_LDS > 0 ? BY_LDS : 1);
-  static constexpr int WAVE_LDS = (160 * 1024) / (4 * WGS);  // one wave's ring budget
+  static constexpr bool RING = BY_LDS > 0;
   // the four waves' states exchanged at the end (accumulators, m, l, bad flag)
   static constexpr int XCH = 3 * (DV / 16 * 4 + 3) * 64 * 4;
+  static constexpr int BY_XCH = (160 * 1024) / XCH;
+  static constexpr int WGS = RING ? (BY_REGS < BY_LDS ? BY_REGS : BY_LDS)
+                                  : (BY_REGS < BY_XCH ? BY_REGS : BY_XCH);
+  static constexpr int WAVE_LDS = (160 * 1024) / (4 * WGS);  // one wave's ring budget
   // LDS of one workgroup of the ring kernel: the rings, reused for the exchange
-  static constexpr int RING_SMEM = 4 * RingShape<DK, DV, WAVE_LDS, FMT>::WAVE_BYTES > XCH
-                                       ? 4 * RingShape<DK, DV, WAVE_LDS, FMT>::WAVE_BYTES
-                                       : XCH;
+  static constexpr int RING_BYTES = RingSmem<RING, DK, DV, WAVE_LDS, FMT>::BYTES;
+  static constexpr int RING_SMEM = RING_BYTES > XCH ? RING_BYTES : XCH;
   static_assert(RING_SMEM * WGS <= 160 * 1024, "resident workgroups exceed the LDS");
   static_assert(XCH * WGS <= 160 * 1024, "resident workgroups exceed the LDS");
 };
@@ -504,27 +518,39 @@ hipError_t launch_dk_dv(int page_shift, const AttnArgs& a, hipStream_t stream) {
     }
   }
   if (a.k_new) return hipErrorInvalidValue;  // the append: NVFP4 with page_size >= 16 only
-  if (page_shift >= 4)
-    launch_attention(decode_ring_kernel<DK, DV, false, FMT>, grid, dim3(256), stream, a);
-  else
-    launch_attention(decode_regs_kernel<DK, DV, FMT>, grid, dim3(256), stream, a);
+  if constexpr (DecodeOcc<DK, DV, FMT>::RING) {
+    if (page_shift >= 4) {
+      launch_attention(decode_ring_kernel<DK, DV, false, FMT>, grid, dim3(256), stream, a);
+      return hipGetLastError();
+    }
+  }
+  launch_attention(decode_regs_kernel<DK, DV, FMT>, grid, dim3(256), stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 // Shapes with kernels: NVFP4 at every (qk, vo) pair of 64..512 with vo <= qk except
-// 512/512; FP8 at head dims up to 256 (a 512-dim FP8 ring does not fit two stages of
-// four waves in LDS at 256 value dims, and is not built for the narrower ones).
+// 512/512; FP8 at the same pairs.  A 512-dim FP8 ring does not fit two stages of four
+// waves in LDS, so those shapes run the register kernel at every page size.
 #define NVFP4_DECODE_SHAPES(X)                                                      \
   X(64, 64, kNvfp4) X(128, 64, kNvfp4) X(128, 128, kNvfp4) X(256, 64, kNvfp4)      \
   X(256, 128, kNvfp4) X(256, 256, kNvfp4) X(512, 64, kNvfp4) X(512, 128, kNvfp4)   \
   X(512, 256, kNvfp4) X(64, 64, kFp8) X(128, 64, kFp8) X(128, 128, kFp8)           \
-  X(256, 64, kFp8) X(256, 128, kFp8) X(256, 256, kFp8)
+  X(256, 64, kFp8) X(256, 128, kFp8) X(256, 256, kFp8) X(512, 64, kFp8)            \
+  X(512, 128, kFp8) X(512, 256, kFp8)
 
 bool decode_supported(int dk, int dv, int fmt) {
 #define NVFP4_DECODE_CASE(K, V, F) \
   if (dk == K && dv == V && fmt == F) return true;
+  NVFP4_DECODE_SHAPES(NVFP4_DECODE_CASE)
+#undef NVFP4_DECODE_CASE
+  return false;
+}
+
+bool decode_ring_supported(int dk, int dv, int fmt) {
+#define NVFP4_DECODE_CASE(K, V, F) \
+  if (dk == K && dv == V && fmt == F) return DecodeOcc<K, V, F>::RING;
   NVFP4_DECODE_SHAPES(NVFP4_DECODE_CASE)
 #undef NVFP4_DECODE_CASE
   return false;
@@ -563,9 +589,12 @@ hipError_t launch_kv_checksum(int dk, int dv, int fmt, const AttnArgs& a, uint32
   const dim3 grid(a.n_work);
 #define NVFP4_DECODE_CASE(K, V, F)                                                       \
   if (dk == K && dv == V && fmt == F) {                                                  \
-    launch_attention(kv_checksum_kernel<K, V, F>, grid, dim3(256), stream, a, out,       \
-                     num_kv_heads);                                                      \
-    return hipGetLastError();                                                            \
+    if constexpr (DecodeOcc<K, V, F>::RING) {                                            \
+      launch_attention(kv_checksum_kernel<K, V, F>, grid, dim3(256), stream, a, out,     \
+                       num_kv_heads);                                                    \
+      return hipGetLastError();                                                          \
+    }                                                                                    \
+    return hipErrorInvalidValue;                                                         \
   }
   NVFP4_DECODE_SHAPES(NVFP4_DECODE_CASE)
 #undef NVFP4_DECODE_CASE

@@ -136,6 +136,8 @@ hipError_t launch_decode(int dk, int dv, int fmt, int page_shift, const AttnArgs
 hipError_t launch_kv_checksum(int dk, int dv, int fmt, const AttnArgs& a, uint32_t* out,
                               int batch, int num_kv_heads, hipStream_t stream);
 bool decode_supported(int dk, int dv, int fmt);
+// The shape has the ring kernel (pages of 16+ tokens; the checksum streams through it).
+bool decode_ring_supported(int dk, int dv, int fmt);
 // Decode workgroups (four waves each) one CU runs at once for this shape.
 int decode_wgs_per_cu(int dk, int dv, int fmt);
 // LDS one CU's resident decode workgroups use (any head dims of the set 64..512).

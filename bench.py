@@ -415,12 +415,12 @@ def variant_lines(torch, nv, paged, synth, name, iters=60, warm=12, pool_sets=3)
 
 
 def kv_type_lines(torch, nv, paged, synth, iters=60, warm=12, pool_sets=3):
-    """The FP8 e4m3 cache beside NVFP4 (batch decode, prefill extend), and the prefill
-    extend over ragged (non-paged) rows of either type; kernel figures as in the main
-    lines (decode: the type's own KV bytes + Q + O + LSE; prefill: visible-pair flops),
-    each with its ratio to the NVFP4 paged figure measured the same way."""
+    """The FP8 e4m3 cache beside NVFP4 (batch decode, 512/256 decode, prefill extend), and
+    the prefill extend over ragged (non-paged) rows of either type; kernel figures as in
+    the main lines (decode: the type's own KV bytes + Q + O + LSE; prefill: visible-pair
+    flops), each with its ratio to the NVFP4 paged figure measured the same way."""
     out = []
-    for name in ("batch_decode", "prefill_extend"):
+    for name in ("batch_decode", "asym_decode", "prefill_extend"):
         w = synth.workload(name)
         ref_rate = None
         for dtype, layout in (("nvfp4", "paged"), ("fp8", "paged"), ("nvfp4", "ragged"),

@@ -164,8 +164,9 @@ nvfp4_status nvfp4_plan_create(const int32_t* kv_lens, const int32_t* qo_indptr,
  * Options of nvfp4_plan_create_ex ([PF] commit "Gate split-KV off...": one plan()
  * serves the paged and the ragged prefill, over NVFP4 and the other KV types).
  *   kv_dtype:  nvfp4_kv_dtype of the pools the runs read (their kv_dtype must match).
- *              FP8 has kernels for head dims up to 256; the 512/256 FP8 prefill tile
- *              is refused with NVFP4_E_LDS_BUDGET.
+ *              FP8 decode has kernels at every head-dim pair NVFP4 has (512-dim heads
+ *              with per-token reads, their rings exceeding the LDS); FP8 prefill up to
+ *              256, the 512/256 FP8 prefill tile refused with NVFP4_E_LDS_BUDGET.
  *   kv_indptr: NULL (paged KV), or host int32 [batch+1] for ragged (non-paged) prefill
  *              KV: request b's keys are rows kv_indptr[b] .. kv_indptr[b+1]-1 of one
  *              row array (nvfp4_kv_ragged); kv_indptr[b+1] - kv_indptr[b] must equal
@@ -330,8 +331,9 @@ nvfp4_status nvfp4_batch_decode_append(const nvfp4_plan* plan, const void* q,
  *     little-endian word of the packed K rows, packed V rows, K scale rows and V scale
  *     rows (each row on its own) of tokens [0, kv_len_b) of request b, kv head h; 0 for
  *     kv_len_b = 0.  Written in full (zeroed first) on `stream`.
- * plan: a decode plan (NVFP4_E_SHAPE otherwise) with page_size >= 16
- * (NVFP4_E_UNSUPPORTED otherwise), uploaded to `workspace`.  Other arguments and errors
+ * plan: a decode plan (NVFP4_E_SHAPE otherwise) with page_size >= 16 whose head dims
+ * have a ring kernel (NVFP4_E_UNSUPPORTED otherwise: FP8 at 512-dim heads decodes with
+ * per-token reads instead), uploaded to `workspace`.  Other arguments and errors
  * as for nvfp4_batch_decode.  A page-table entry outside [0, num_pages) reads page 0 in
  * its place (nothing outside the pools is read); that checksum is then meaningless.
  */

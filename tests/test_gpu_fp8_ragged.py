@@ -75,8 +75,11 @@ def test_fp8_decode_ragged_and_split(chunk):
 
 
 @pytest.mark.parametrize("dk,dv,hq,hkv", [(64, 64, 4, 1), (128, 64, 8, 2), (256, 128, 8, 2),
-                                          (256, 256, 16, 1), (256, 64, 4, 4), (128, 128, 40, 2)])
+                                          (256, 256, 16, 1), (256, 64, 4, 4), (128, 128, 40, 2),
+                                          (512, 256, 8, 1), (512, 128, 8, 2), (512, 64, 4, 1)])
 def test_fp8_decode_head_dims_and_groups(dk, dv, hq, hkv):
+    """FP8 decode at every head-dim pair; the 512-dim pairs run the register kernel at
+    pages of 16 tokens (their rings do not fit the LDS)."""
     w = synth.custom(f"d8dims{dk}x{dv}", kv_lens=[150, 513, 40], num_qo_heads=hq,
                      num_kv_heads=hkv, head_dim_qk=dk, head_dim_vo=dv, seed=dk + hq)
     _run(w, chunk=64)
@@ -87,6 +90,13 @@ def test_fp8_decode_layouts_and_pages(layout, page_size):
     w = synth.custom("d8layout", kv_lens=[200, 31, 1030], num_qo_heads=32, num_kv_heads=8,
                      page_size=page_size, seed=151)
     _run(w, layout=layout, chunk=32)
+
+
+@pytest.mark.parametrize("layout,page_size", [("HND", 16), ("NHD", 1)])
+def test_fp8_decode_512_layouts_and_pages(layout, page_size):
+    w = synth.custom("d8w512", kv_lens=[700, 17, 1500], num_qo_heads=8, num_kv_heads=1,
+                     head_dim_qk=512, head_dim_vo=256, page_size=page_size, seed=153)
+    _run(w, layout=layout, chunk=64)
 
 
 def test_fp8_decode_global_scales_and_unequal_strides():

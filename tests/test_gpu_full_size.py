@@ -169,6 +169,14 @@ def test_prefill_extend_full_size_fp8(record_property):
 
 
 @pytest.mark.timeout(600)
+def test_asym_decode_full_size_fp8(record_property):
+    """The 512/256 decode workload over an FP8 cache (the per-token register kernel)."""
+    case, o, lse = _decode("asym_decode", fused=False, dtype="fp8")
+    assert not np.isnan(o).any() and not np.isnan(lse).any()
+    _oracle_pairs(case, o, lse, sample_pairs(case.w, 61), record_property)
+
+
+@pytest.mark.timeout(600)
 def test_prefill_extend_full_size_rope(record_property):
     """The prefill extend with in-kernel RoPE (base 1e4), in the benchmark's launch."""
     case, o, lse = _prefill("prefill_extend", rope=(1e4, 1.0))

@@ -326,15 +326,27 @@ def _plan_ex_status(kv_dtype=0, kv_indptr=None, custom_mask=False, **kw):
 
 
 def test_fp8_plans_price_the_tile_in_lds():
-    """FP8 rows are twice as long: the 512/256 FP8 prefill tile (and the decode ring)
-    needs more LDS than a CU has and is refused by the computed budget; FP8 kernels
-    exist for head dims up to 256."""
+    """FP8 rows are twice as long: the 512/256 FP8 prefill tile needs more LDS than a CU
+    has and is refused by the computed budget; FP8 prefill kernels exist for head dims
+    up to 256.  FP8 decode covers the 512-dim pairs with the register kernel (priced by
+    its exchange buffer), and the checksum, which streams through the rings, refuses
+    them."""
     st, msg = _plan_ex_status(1, head_dim_qk=512, head_dim_vo=256)
     assert st == "NVFP4_E_LDS_BUDGET" and "LDS" in msg, msg
-    st, msg = _plan_ex_status(1, qo_indptr=None, head_dim_qk=512, head_dim_vo=256)
-    assert st == "NVFP4_E_LDS_BUDGET", msg
-    st, msg = _plan_ex_status(1, qo_indptr=None, head_dim_qk=512, head_dim_vo=128)
+    st, msg = _plan_ex_status(1, head_dim_qk=512, head_dim_vo=128)
     assert st == "NVFP4_E_UNSUPPORTED" and "FP8" in msg, msg
+    for dv in (64, 128, 256):
+        for ps in (1, 16):
+            st, msg = _plan_ex_status(1, qo_indptr=None, head_dim_qk=512, head_dim_vo=dv,
+                                      page_size=ps)
+            assert st == "NVFP4_OK", (dv, ps, msg)
+    plan = nv.Plan([64], num_qo_heads=8, num_kv_heads=1, head_dim_qk=512, head_dim_vo=256,
+                   num_cus=256, kv_dtype="fp8")
+    st = nv.lib.nvfp4_kv_checksum(plan.handle, ctypes.c_void_p(0x4000), 64, None, None,
+                                  ctypes.c_void_p(0x8000), 1 << 20, ctypes.c_void_p(0x9000),
+                                  None)
+    assert _lib.STATUS[st] == "NVFP4_E_UNSUPPORTED", nv.lib.nvfp4_last_error().decode()
+    assert "rings" in nv.lib.nvfp4_last_error().decode()
     for dk, dv in ((64, 64), (128, 64), (128, 128), (256, 64), (256, 128), (256, 256)):
         for ind in (None, [0, 8]):
             for ps in (1, 16):
